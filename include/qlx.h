@@ -1,0 +1,240 @@
+/*
+ * qlx.h — C ABI of libqlx: the hot path of layer-streamed QLoRA fine-tuning
+ * (a frozen NF4-quantized Llama-style decoder stack with trainable LoRA
+ * adapters; the base weights stay in pinned host RAM and reach the GPU one
+ * decoder layer at a time) on AMD Instinct MI355X (gfx950).
+ *
+ * What the method is (cited by page title and section):
+ *  - rug.gal, "Soup: fine-tune an 8B model on a 4 GB laptop GPU (layer
+ *    streaming)", intro and "En detalle": the frozen base is kept off the GPU
+ *    and fed to it one decoder layer at a time (load, compute, unload); only the
+ *    LoRA adapters and the batch stay resident; the result is bit-exact with a
+ *    non-streamed run; DPO's reference model is the same layer stream with the
+ *    adapters switched off.
+ *  - guillermodelpino.com, "Soup: afinar un modelo de 8.000 millones de
+ *    parámetros en un portátil con 4 GB de gráfica", "Qué es exactamente"
+ *    (LoRA r 64, alpha 16, quantization 4bit) and "El streaming de capas".
+ *  - imasters.com.br, "Soup promete fine-tuning de modelo 8B em GPU de notebook
+ *    com 4 GB", "Como cabe um 8B em 4 GB" (NF4; base in host RAM) and "Do SFT
+ *    para os métodos de preferência" (DPO reference with adapters off).
+ *  - NF4 as defined by QLoRA (Dettmers et al., 2023); LoRA (Hu et al., 2021);
+ *    the Llama decoder (RMSNorm, rotate-half RoPE, grouped-query causal
+ *    attention, SwiGLU); DPO (Rafailov et al., 2023, eq. 7).
+ *
+ * Conventions for every call
+ *  - Pointers are DEVICE pointers unless marked HOST. bf16 and fp16 values
+ *    travel as uint16_t bit patterns. Matrices are row-major.
+ *  - The caller owns every buffer. No call allocates device memory; scratch
+ *    space comes from a caller-provided workspace whose size the matching
+ *    qlx_*_workspace_bytes() call reports. Pass ws = NULL with ws_bytes = 0
+ *    only when that size is 0.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Calls are
+ *    asynchronous on it: outputs are valid once the stream reaches that
+ *    point. Streaming steps fork to the context's side stream and join back
+ *    with events before returning.
+ *  - Return value: qlx_status. Arguments are validated on the host before
+ *    any launch; on a non-OK return nothing was launched (except QLX_EHIP,
+ *    which reports a launch or runtime failure). qlx_last_error() gives a
+ *    thread-local message. No exception crosses the ABI.
+ *  - Results are deterministic: no floating-point atomics anywhere, fixed
+ *    reduction orders, and kernel choice depends only on shapes (never on
+ *    pointer values), so the same inputs give the same bits whether the
+ *    layer bytes sit in a streaming slot or stay resident.
+ */
+#ifndef QLX_H
+#define QLX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QLX_OK = 0,
+    QLX_EINVAL = 1,        /* null pointer, negative size, inconsistent shapes */
+    QLX_EUNSUPPORTED = 2,  /* valid request this build does not handle */
+    QLX_EWORKSPACE = 3,    /* ws_bytes smaller than the reported requirement */
+    QLX_ENOTPINNED = 4,    /* a streamed layer blob is not pinned host memory */
+    QLX_EHIP = 5           /* the HIP runtime reported an error */
+} qlx_status;
+
+enum { QLX_F32 = 0, QLX_BF16 = 1 };                /* nf4_dequant output type */
+enum { QLX_STREAMED = 0, QLX_RESIDENT = 1 };       /* where layer blobs live */
+enum { QLX_DPO_REF_FUSED = 0, QLX_DPO_REF_SEPARATE = 1 };
+
+/* Thread-local text of the last non-OK status (never NULL). */
+const char* qlx_last_error(void);
+/* Library version string. */
+const char* qlx_version(void);
+
+/* Decoder dimensions. rms_eps 1e-5 and rope_theta 5e5 for the Llama-3.1
+ * shape; lora_alpha / lora_r is the LoRA scale s. */
+typedef struct {
+    int32_t hidden, n_heads, n_kv_heads, head_dim, inter, vocab, n_layers, lora_r;
+    float lora_alpha, rms_eps, rope_theta;
+} qlx_dims;
+
+/* ---------------------------------------------------------------------------
+ * NF4 (QLoRA's 4-bit NormalFloat), blocksize 64, fp32 absmax.
+ * Source: rug.gal article "En detalle" and imasters article "Como cabe um 8B
+ * em 4 GB" name NF4; the values and rounding follow QLoRA's NF4 definition.
+ * Layout ("canonical NF4 tensor"): the tensor is flattened row-major; block b
+ * covers elements [64b, 64b+64) (blocks may straddle rows); absmax[b] =
+ * max |w| over the block (fp32); each element's code is the nearest of the 16
+ * NF4 values to w / absmax[b] (fp32 division; an exact midpoint goes to the
+ * lower code; an all-zero block has absmax 0 and codes 7); packed[j] holds
+ * element 2j in its high nibble and 2j+1 in its low nibble (an odd count pads
+ * the last low nibble with code 7).
+ * ------------------------------------------------------------------------- */
+
+/* Quantize w (bf16, n = rows*cols elements) into packed (ceil(n/2) bytes)
+ * and absmax (ceil(n/64) floats). n = 0 is a no-op. */
+int nf4_quantize(const uint16_t* w_bf16, int64_t rows, int64_t cols,
+                 uint8_t* packed, float* absmax, void* stream);
+
+/* out[i] = fl32(code_value[code_i] * absmax[i/64]) as fp32 (QLX_F32) or that
+ * value rounded to nearest-even bf16 (QLX_BF16), for i < rows*cols. */
+int nf4_dequant(const uint8_t* packed, const float* absmax, int64_t rows, int64_t cols,
+                int out_dtype, void* out, void* stream);
+
+/* A canonical NF4 matrix W [rows = out_features, cols = in_features]. */
+typedef struct {
+    const uint8_t* packed;
+    const float* absmax;
+    int64_t rows, cols;
+} qlx_nf4;
+
+/* ---------------------------------------------------------------------------
+ * QLoRA linear (LoRA, Hu et al. 2021, section 4.1, on an NF4 base).
+ *   y = x W'^T + s (x A^T) B^T,  W' = bf16(dequant(W)),  s = scale
+ * x bf16 [T, in]; A fp32 [r, in]; B fp32 [out, r]; y bf16 [T, out].
+ * A = B = NULL switches LoRA off (y = x W'^T exactly; B = 0 gives the same
+ * bits). The base GEMM runs on bf16 MFMA with fp32 accumulation and the
+ * dequantization fused into its weight-operand load.
+ * ------------------------------------------------------------------------- */
+size_t qlx_linear_workspace_bytes(int64_t T, int64_t in_f, int64_t out_f, int r);
+
+int qlora_linear_fwd(const uint16_t* x, int64_t T, qlx_nf4 W, const float* A, const float* B,
+                     int r, float scale, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward with W frozen. dy bf16 [T, out], x bf16 [T, in] (the forward input).
+ *   du = s dy B;  dx = dy W' + du A (bf16 [T, in], NULL = skip);
+ *   dB = s dy^T (x A^T) (fp32 [out, r]);  dA = du^T x (fp32 [r, in]).
+ * accumulate = 1 adds into dA/dB instead of overwriting them. With LoRA off
+ * (A = B = NULL) only dx is produced. */
+int qlora_linear_bwd(const uint16_t* dy, const uint16_t* x, int64_t T, qlx_nf4 W,
+                     const float* A, const float* B, int r, float scale,
+                     uint16_t* dx, float* dA, float* dB, int accumulate,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Decoder layer blob: one contiguous region per layer holding
+ *   packed q,k,v,o,gate,up,down (back to back, in that order)
+ *   absmax q,k,v,o,gate,up,down (back to back, in that order)
+ *   g_attn fp32 [hidden], g_mlp fp32 [hidden] (RMSNorm gains)
+ * with each region 256-byte aligned. Projection shapes [out, in]:
+ *   q [nH*hd, H], k/v [nKV*hd, H], o [H, nH*hd], gate/up [I, H], down [H, I].
+ * Every projection must hold a multiple of 64 elements (true for all Llama
+ * shapes), so q|k|v and gate|up are each one canonical NF4 matrix.
+ * offsets[0..6] = packed q..down, [7..13] = absmax q..down, [14] = g_attn,
+ * [15] = g_mlp; *total_bytes = blob size (a multiple of 256).
+ * ------------------------------------------------------------------------- */
+#define QLX_BLOB_NSEG 16
+int qlx_layer_blob_layout(const qlx_dims* d, uint64_t offsets[QLX_BLOB_NSEG], uint64_t* total_bytes);
+
+/* LoRA adapters of one layer (fp32, device): A[p] [r, in_p], B[p] [out_p, r]
+ * for p = q,k,v,o,gate,up,down. */
+typedef struct { const float* A[7]; const float* B[7]; } qlx_lora;
+typedef struct { float* dA[7]; float* dB[7]; } qlx_lora_grad;
+
+/* One decoder layer (Llama: RMSNorm, q/k/v QLoRA, RoPE, causal GQA attention,
+ * o QLoRA + residual, RMSNorm, SwiGLU QLoRA MLP + residual).
+ * h_in / h_out: the fp32 residual stream [batch*seq, hidden] (row b*seq + t).
+ * blob: DEVICE layer blob (layout above). lora = NULL runs the base only.
+ * Positions restart at 0 for every sequence; attention is causal. */
+size_t qlx_layer_workspace_bytes(const qlx_dims* d, int batch, int seq);
+int layer_fwd(const qlx_dims* d, const void* blob, const qlx_lora* lora, const float* h_in,
+              int batch, int seq, float* h_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of layer_fwd: recomputes the layer forward from h_in first, then
+ * returns dh_in (fp32, NULL = skip the input gradient) and overwrites the 14
+ * LoRA gradients in `grads` (fp32). lora must be non-NULL. */
+int layer_bwd(const qlx_dims* d, const void* blob, const qlx_lora* lora, const float* h_in,
+              const float* dh_out, int batch, int seq, float* dh_in, const qlx_lora_grad* grads,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Streaming context: owns a side stream (default priority, non-blocking),
+ * the slot events and the step statistics. Nothing else.
+ * ------------------------------------------------------------------------- */
+typedef struct qlx_ctx qlx_ctx;
+
+typedef struct {
+    int64_t layer_reads;   /* layer blobs copied host -> device in the last step */
+    int64_t h2d_bytes;     /* bytes those copies moved */
+    int64_t layer_passes;  /* layer computations (fwd, recompute+bwd, reference) */
+    float step_ms;         /* first to last event of the last step */
+    float h2d_ms;          /* sum of the copies' durations (side stream) */
+} qlx_stats;
+
+int qlx_ctx_create(qlx_ctx** out, int device);
+int qlx_ctx_destroy(qlx_ctx* ctx);
+/* Waits for all work of the last step and fills *stats (HOST) if non-NULL. */
+int qlx_ctx_sync(qlx_ctx* ctx, qlx_stats* stats);
+
+/* The model a step runs on.
+ * layer_blobs: HOST array of n_layers pointers to layer blobs; in
+ *   QLX_STREAMED mode they must be pinned host memory (hipHostMalloc or
+ *   registered by the runtime's pinned allocator); in QLX_RESIDENT mode they
+ *   are device memory and no copy happens.
+ * embed_f16, lm_head_f16: DEVICE fp16 [vocab, hidden] (untied, frozen).
+ * final_norm: DEVICE fp32 [hidden]. lora: HOST array of n_layers qlx_lora. */
+typedef struct {
+    qlx_dims dims;
+    const void* const* layer_blobs;
+    const uint16_t* embed_f16;
+    const uint16_t* lm_head_f16;
+    const float* final_norm;
+    const qlx_lora* lora;
+} qlx_model;
+
+/* Workspace of a step: two device slots of one layer blob each (streamed
+ * mode), n_layers+1 fp32 layer-boundary checkpoints, one layer's workspace
+ * and the LM-head logits [T, vocab] fp32. kind: 0 = SFT, 1 = DPO (T = 2*pairs*seq). */
+size_t qlx_step_workspace_bytes(const qlx_dims* d, int kind, int batch, int seq);
+
+/* One SFT step: embedding, n_layers decoder layers streamed one at a time
+ * (double-buffered: the copy of layer i+1 overlaps compute on layer i; in
+ * backward the layers are re-streamed in reverse and recomputed from the
+ * layer-boundary checkpoints; the two layers still in the slots at the turn
+ * are not copied again), final RMSNorm, fp16 LM head, next-token
+ * cross-entropy averaged over batch*(seq-1) positions.
+ * tokens: DEVICE int32 [batch, seq]. loss: DEVICE fp32 scalar.
+ * grads: HOST array of n_layers qlx_lora_grad (device fp32 buffers, overwritten).
+ * Streamed and resident modes give bit-identical loss and gradients. */
+int stream_step_sft(qlx_ctx* ctx, const qlx_model* model, const int32_t* tokens, int batch,
+                    int seq, int mode, float* loss, const qlx_lora_grad* grads,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* One DPO step (Rafailov et al. 2023, eq. 7; reference = the same layer
+ * stream with LoRA off). chosen/rejected: DEVICE int32 [pairs, seq]; the
+ * response of each sequence is positions prompt_len..seq-1. The batch is
+ * [chosen_1..chosen_P, rejected_1..rejected_P].
+ * ref_schedule = QLX_DPO_REF_FUSED computes the reference forward on each
+ *   layer while it is resident for the policy forward (layer reads as SFT);
+ *   QLX_DPO_REF_SEPARATE runs a separate reference pass first (3L-2 reads).
+ *   Both give identical bits.
+ * loss: DEVICE fp32 scalar = mean over pairs of -log sigmoid(beta*Delta).
+ * logps: DEVICE fp32 [4*pairs] = policy chosen, policy rejected, reference
+ *   chosen, reference rejected (summed response-token log-probs). */
+int stream_step_dpo(qlx_ctx* ctx, const qlx_model* model, const int32_t* chosen,
+                    const int32_t* rejected, int pairs, int seq, int prompt_len, float beta,
+                    int mode, int ref_schedule, float* loss, float* logps,
+                    const qlx_lora_grad* grads, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QLX_H */

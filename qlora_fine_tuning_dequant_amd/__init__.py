@@ -1,0 +1,12 @@
+"""MI355X-native layer-streamed QLoRA training step (NF4 base + LoRA).
+
+The compute lives in libqlx.so (hand-written HIP kernels for gfx950 behind
+the C ABI in include/qlx.h); ``binding`` marshals torch tensors to it."""
+from . import binding
+from .binding import (Context, LoraGrads, LoraLayer, NF4Matrix, QlxError, StreamModel, layer_bwd, layer_fwd,
+                      nf4_dequant, nf4_quantize, qlora_linear_bwd, qlora_linear_fwd, stream_step_dpo,
+                      stream_step_sft)
+
+__all__ = ["binding", "Context", "LoraGrads", "LoraLayer", "NF4Matrix", "QlxError", "StreamModel", "layer_bwd",
+           "layer_fwd", "nf4_dequant", "nf4_quantize", "qlora_linear_bwd", "qlora_linear_fwd", "stream_step_dpo",
+           "stream_step_sft"]

@@ -1,0 +1,351 @@
+"""ctypes binding of libqlx (include/qlx.h). Argument marshalling only: every
+step of the path runs in the library's HIP kernels. torch supplies device and
+pinned host memory and the current HIP stream; it does no math here.
+
+The functions keep the C names: nf4_quantize, nf4_dequant, qlora_linear_fwd,
+qlora_linear_bwd, layer_fwd, layer_bwd, stream_step_sft, stream_step_dpo.
+A missing or unloadable library raises immediately; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Sequence
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlx.so")
+
+QLX_OK, QLX_EINVAL, QLX_EUNSUPPORTED, QLX_EWORKSPACE, QLX_ENOTPINNED, QLX_EHIP = range(6)
+QLX_F32, QLX_BF16 = 0, 1
+QLX_STREAMED, QLX_RESIDENT = 0, 1
+QLX_DPO_REF_FUSED, QLX_DPO_REF_SEPARATE = 0, 1
+BLOB_NSEG = 16
+PROJ = ("q", "k", "v", "o", "gate", "up", "down")
+
+EXPORTED = (
+    "qlx_last_error", "qlx_version", "nf4_quantize", "nf4_dequant", "qlx_linear_workspace_bytes",
+    "qlora_linear_fwd", "qlora_linear_bwd", "qlx_layer_blob_layout", "qlx_layer_workspace_bytes",
+    "layer_fwd", "layer_bwd", "qlx_ctx_create", "qlx_ctx_destroy", "qlx_ctx_sync",
+    "qlx_step_workspace_bytes", "stream_step_sft", "stream_step_dpo",
+)
+
+
+class QlxError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"qlx error {code}: {msg}")
+        self.code = code
+
+
+class Dims(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("n_heads", C.c_int32), ("n_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("inter", C.c_int32), ("vocab", C.c_int32),
+                ("n_layers", C.c_int32), ("lora_r", C.c_int32), ("lora_alpha", C.c_float),
+                ("rms_eps", C.c_float), ("rope_theta", C.c_float)]
+
+    @classmethod
+    def of(cls, d) -> "Dims":
+        if isinstance(d, Dims):
+            return d
+        return cls(d.hidden, d.n_heads, d.n_kv_heads, d.head_dim, d.inter, d.vocab, d.n_layers,
+                   d.lora_r, float(d.lora_alpha), float(d.rms_eps), float(d.rope_theta))
+
+
+class NF4(C.Structure):
+    _fields_ = [("packed", C.c_void_p), ("absmax", C.c_void_p), ("rows", C.c_int64), ("cols", C.c_int64)]
+
+
+class Lora(C.Structure):
+    _fields_ = [("A", C.c_void_p * 7), ("B", C.c_void_p * 7)]
+
+
+class LoraGrad(C.Structure):
+    _fields_ = [("dA", C.c_void_p * 7), ("dB", C.c_void_p * 7)]
+
+
+class Stats(C.Structure):
+    _fields_ = [("layer_reads", C.c_int64), ("h2d_bytes", C.c_int64), ("layer_passes", C.c_int64),
+                ("step_ms", C.c_float), ("h2d_ms", C.c_float)]
+
+
+class Model(C.Structure):
+    _fields_ = [("dims", Dims), ("layer_blobs", C.POINTER(C.c_void_p)), ("embed_f16", C.c_void_p),
+                ("lm_head_f16", C.c_void_p), ("final_norm", C.c_void_p), ("lora", C.POINTER(Lora))]
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """The loaded libqlx; raises if it was not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libqlx.so not built at {LIB_PATH}: run __graft_entry__.build()")
+    L = C.CDLL(LIB_PATH)
+    vp, i64, i32, f32, sz = C.c_void_p, C.c_int64, C.c_int, C.c_float, C.c_size_t
+    sig = {
+        "qlx_last_error": (C.c_char_p, []),
+        "qlx_version": (C.c_char_p, []),
+        "nf4_quantize": (i32, [vp, i64, i64, vp, vp, vp]),
+        "nf4_dequant": (i32, [vp, vp, i64, i64, i32, vp, vp]),
+        "qlx_linear_workspace_bytes": (sz, [i64, i64, i64, i32]),
+        "qlora_linear_fwd": (i32, [vp, i64, NF4, vp, vp, i32, f32, vp, vp, sz, vp]),
+        "qlora_linear_bwd": (i32, [vp, vp, i64, NF4, vp, vp, i32, f32, vp, vp, vp, i32, vp, sz, vp]),
+        "qlx_layer_blob_layout": (i32, [C.POINTER(Dims), C.POINTER(C.c_uint64), C.POINTER(C.c_uint64)]),
+        "qlx_layer_workspace_bytes": (sz, [C.POINTER(Dims), i32, i32]),
+        "layer_fwd": (i32, [C.POINTER(Dims), vp, C.POINTER(Lora), vp, i32, i32, vp, vp, sz, vp]),
+        "layer_bwd": (i32, [C.POINTER(Dims), vp, C.POINTER(Lora), vp, vp, i32, i32, vp, C.POINTER(LoraGrad),
+                            vp, sz, vp]),
+        "qlx_ctx_create": (i32, [C.POINTER(vp), i32]),
+        "qlx_ctx_destroy": (i32, [vp]),
+        "qlx_ctx_sync": (i32, [vp, C.POINTER(Stats)]),
+        "qlx_step_workspace_bytes": (sz, [C.POINTER(Dims), i32, i32, i32]),
+        "stream_step_sft": (i32, [vp, C.POINTER(Model), vp, i32, i32, i32, vp, C.POINTER(LoraGrad), vp, sz, vp]),
+        "stream_step_dpo": (i32, [vp, C.POINTER(Model), vp, vp, i32, i32, i32, f32, i32, i32, vp, vp,
+                                  C.POINTER(LoraGrad), vp, sz, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(code: int) -> None:
+    if code != QLX_OK:
+        raise QlxError(code, lib().qlx_last_error().decode())
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _bits16(t: torch.Tensor) -> torch.Tensor:
+    assert t.dtype in (torch.bfloat16, torch.float16, torch.int16, torch.uint16), t.dtype
+    return t
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------------- NF4
+def nf4_quantize(w: torch.Tensor, packed: torch.Tensor, absmax: torch.Tensor, stream=None) -> None:
+    """w bf16 [rows, cols] (any shape, flattened) -> packed uint8 [ceil(n/2)], absmax fp32 [ceil(n/64)]."""
+    _bits16(w)
+    rows = w.shape[0] if w.dim() > 0 else 1
+    cols = w.numel() // rows if rows else 0
+    _check(lib().nf4_quantize(_ptr(w), rows, cols, _ptr(packed), _ptr(absmax), _stream(stream)))
+
+
+def nf4_dequant(packed: torch.Tensor, absmax: torch.Tensor, rows: int, cols: int, out: torch.Tensor,
+                stream=None) -> None:
+    dt = QLX_BF16 if out.dtype == torch.bfloat16 else QLX_F32
+    assert out.dtype in (torch.bfloat16, torch.float32)
+    _check(lib().nf4_dequant(_ptr(packed), _ptr(absmax), rows, cols, dt, _ptr(out), _stream(stream)))
+
+
+class NF4Matrix:
+    """A canonical NF4 matrix [rows = out_features, cols = in_features] on the device."""
+
+    def __init__(self, packed: torch.Tensor, absmax: torch.Tensor, rows: int, cols: int):
+        self.packed, self.absmax, self.rows, self.cols = packed, absmax, int(rows), int(cols)
+
+    @classmethod
+    def quantize(cls, w: torch.Tensor, stream=None) -> "NF4Matrix":
+        rows, cols = w.shape
+        n = rows * cols
+        packed = torch.empty((n + 1) // 2, dtype=torch.uint8, device=w.device)
+        absmax = torch.empty((n + 63) // 64, dtype=torch.float32, device=w.device)
+        nf4_quantize(w, packed, absmax, stream)
+        return cls(packed, absmax, rows, cols)
+
+    def c(self) -> NF4:
+        return NF4(_ptr(self.packed), _ptr(self.absmax), self.rows, self.cols)
+
+
+# -------------------------------------------------------------- QLoRA linear
+def linear_workspace_bytes(T: int, in_f: int, out_f: int, r: int) -> int:
+    return int(lib().qlx_linear_workspace_bytes(T, in_f, out_f, r))
+
+
+def qlora_linear_fwd(x: torch.Tensor, W: NF4Matrix, A, B, scale: float, y: torch.Tensor,
+                     ws: torch.Tensor | None = None, stream=None) -> None:
+    T = x.shape[0]
+    r = A.shape[0] if A is not None else 0
+    if ws is None:
+        ws = workspace(linear_workspace_bytes(T, W.cols, W.rows, r), x.device)
+    _check(lib().qlora_linear_fwd(_ptr(x), T, W.c(), _ptr(A), _ptr(B), r, float(scale), _ptr(y), _ptr(ws),
+                                  ws.numel(), _stream(stream)))
+
+
+def qlora_linear_bwd(dy: torch.Tensor, x: torch.Tensor, W: NF4Matrix, A, B, scale: float, dx, dA, dB,
+                     accumulate: bool = False, ws: torch.Tensor | None = None, stream=None) -> None:
+    T = x.shape[0]
+    r = A.shape[0] if A is not None else 0
+    if ws is None:
+        ws = workspace(linear_workspace_bytes(T, W.cols, W.rows, r), x.device)
+    _check(lib().qlora_linear_bwd(_ptr(dy), _ptr(x), T, W.c(), _ptr(A), _ptr(B), r, float(scale), _ptr(dx),
+                                  _ptr(dA), _ptr(dB), int(accumulate), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+# ------------------------------------------------------------------- layers
+def blob_layout(dims) -> tuple[list[int], int]:
+    d = Dims.of(dims)
+    offs = (C.c_uint64 * BLOB_NSEG)()
+    total = C.c_uint64()
+    _check(lib().qlx_layer_blob_layout(C.byref(d), offs, C.byref(total)))
+    return list(offs), int(total.value)
+
+
+def fill_blob(dims, blob: torch.Tensor, weights_bf16: dict, g1: torch.Tensor, g2: torch.Tensor,
+              stream=None) -> None:
+    """Quantize each projection's bf16 weight (device tensors [out, in]) with
+    nf4_quantize straight into a device blob, and copy the RMSNorm gains."""
+    offs, total = blob_layout(dims)
+    assert blob.numel() >= total and blob.is_cuda
+    base = blob.data_ptr()
+    for p, name in enumerate(PROJ):
+        w = weights_bf16[name]
+        rows, cols = w.shape
+        _check(lib().nf4_quantize(_ptr(w), rows, cols, base + offs[p], base + offs[7 + p], _stream(stream)))
+    H = g1.numel()
+    blob[offs[14]: offs[14] + 4 * H].copy_(g1.to(torch.float32).view(torch.uint8))
+    blob[offs[15]: offs[15] + 4 * H].copy_(g2.to(torch.float32).view(torch.uint8))
+
+
+class LoraLayer:
+    """The 7 adapters of one layer: A [r, in], B [out, r] fp32 device tensors."""
+
+    def __init__(self, A: Sequence[torch.Tensor], B: Sequence[torch.Tensor]):
+        self.A, self.B = list(A), list(B)
+
+    def c(self) -> Lora:
+        return Lora((C.c_void_p * 7)(*[_ptr(a) for a in self.A]), (C.c_void_p * 7)(*[_ptr(b) for b in self.B]))
+
+
+class LoraGrads:
+    """Gradient buffers matching a LoraLayer (fp32, device)."""
+
+    def __init__(self, like: LoraLayer):
+        self.dA = [torch.empty_like(a) for a in like.A]
+        self.dB = [torch.empty_like(b) for b in like.B]
+
+    def c(self) -> LoraGrad:
+        return LoraGrad((C.c_void_p * 7)(*[_ptr(a) for a in self.dA]), (C.c_void_p * 7)(*[_ptr(b) for b in self.dB]))
+
+
+def layer_workspace_bytes(dims, batch: int, seq: int) -> int:
+    d = Dims.of(dims)
+    return int(lib().qlx_layer_workspace_bytes(C.byref(d), batch, seq))
+
+
+def layer_fwd(dims, blob: torch.Tensor, lora: LoraLayer | None, h_in: torch.Tensor, batch: int, seq: int,
+              h_out: torch.Tensor, ws: torch.Tensor | None = None, stream=None) -> None:
+    d = Dims.of(dims)
+    if ws is None:
+        ws = workspace(layer_workspace_bytes(d, batch, seq), h_in.device)
+    lo = C.byref(lora.c()) if lora is not None else None
+    _check(lib().layer_fwd(C.byref(d), _ptr(blob), lo, _ptr(h_in), batch, seq, _ptr(h_out), _ptr(ws),
+                           ws.numel(), _stream(stream)))
+
+
+def layer_bwd(dims, blob: torch.Tensor, lora: LoraLayer, h_in: torch.Tensor, dh_out: torch.Tensor, batch: int,
+              seq: int, dh_in: torch.Tensor | None, grads: LoraGrads, ws: torch.Tensor | None = None,
+              stream=None) -> None:
+    d = Dims.of(dims)
+    if ws is None:
+        ws = workspace(layer_workspace_bytes(d, batch, seq), h_in.device)
+    lc, gc = lora.c(), grads.c()
+    _check(lib().layer_bwd(C.byref(d), _ptr(blob), C.byref(lc), _ptr(h_in), _ptr(dh_out), batch, seq,
+                           _ptr(dh_in), C.byref(gc), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+# ------------------------------------------------------------------ streaming
+class Context:
+    """Streaming context (side stream, slot events, statistics)."""
+
+    def __init__(self, device: int = 0):
+        h = C.c_void_p()
+        _check(lib().qlx_ctx_create(C.byref(h), device))
+        self.h = h
+
+    def sync(self) -> dict:
+        st = Stats()
+        _check(lib().qlx_ctx_sync(self.h, C.byref(st)))
+        return {k: getattr(st, k) for k, _ in Stats._fields_}
+
+    def close(self) -> None:
+        if self.h:
+            lib().qlx_ctx_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class StreamModel:
+    """Holds the tensors of a model and the C struct pointing at them.
+    blobs: pinned host uint8 tensors (streamed) or device uint8 tensors (resident)."""
+
+    def __init__(self, dims, blobs: Sequence[torch.Tensor], embed_f16: torch.Tensor, head_f16: torch.Tensor,
+                 final_norm: torch.Tensor, lora: Sequence[LoraLayer]):
+        self.dims = Dims.of(dims)
+        _, total = blob_layout(self.dims)
+        for bl in blobs:
+            if bl.numel() * bl.element_size() < total:
+                raise ValueError(f"layer blob holds {bl.numel() * bl.element_size()} bytes, layout needs {total}")
+        self.blobs, self.embed, self.head, self.final_norm, self.lora = list(blobs), embed_f16, head_f16, final_norm, list(lora)
+        n = len(self.blobs)
+        self._blob_arr = (C.c_void_p * n)(*[_ptr(b) for b in self.blobs])
+        self._lora_arr = (Lora * n)(*[l.c() for l in self.lora])
+        self.c = Model(self.dims, C.cast(self._blob_arr, C.POINTER(C.c_void_p)), _ptr(embed_f16), _ptr(head_f16),
+                       _ptr(final_norm), C.cast(self._lora_arr, C.POINTER(Lora)))
+
+    def with_blobs(self, blobs: Sequence[torch.Tensor]) -> "StreamModel":
+        return StreamModel(self.dims, blobs, self.embed, self.head, self.final_norm, self.lora)
+
+
+def step_workspace_bytes(dims, kind: int, batch: int, seq: int) -> int:
+    d = Dims.of(dims)
+    return int(lib().qlx_step_workspace_bytes(C.byref(d), kind, batch, seq))
+
+
+def _grad_arr(grads: Sequence[LoraGrads]):
+    return (LoraGrad * len(grads))(*[g.c() for g in grads])
+
+
+def stream_step_sft(ctx: Context, model: StreamModel, tokens: torch.Tensor, mode: int, loss: torch.Tensor,
+                    grads: Sequence[LoraGrads], ws: torch.Tensor, stream=None) -> None:
+    B, S = tokens.shape
+    ga = _grad_arr(grads)
+    _check(lib().stream_step_sft(ctx.h, C.byref(model.c), _ptr(tokens), B, S, mode, _ptr(loss), ga, _ptr(ws),
+                                 ws.numel(), _stream(stream)))
+
+
+def stream_step_dpo(ctx: Context, model: StreamModel, chosen: torch.Tensor, rejected: torch.Tensor,
+                    prompt_len: int, beta: float, mode: int, ref_schedule: int, loss: torch.Tensor,
+                    logps: torch.Tensor, grads: Sequence[LoraGrads], ws: torch.Tensor, stream=None) -> None:
+    P, S = chosen.shape
+    ga = _grad_arr(grads)
+    _check(lib().stream_step_dpo(ctx.h, C.byref(model.c), _ptr(chosen), _ptr(rejected), P, S, prompt_len,
+                                 float(beta), mode, ref_schedule, _ptr(loss), _ptr(logps), ga, _ptr(ws),
+                                 ws.numel(), _stream(stream)))

@@ -1,0 +1,773 @@
+// C ABI of libqlx: argument validation, workspace carving, the layer
+// streamer and the SFT / DPO steps.
+//
+// Layer streaming (rug.gal article, intro and "En detalle"; guillermodelpino.com
+// article, "El streaming de capas"; imasters article, "Como cabe um 8B em
+// 4 GB"): the frozen NF4 base stays in pinned host RAM; one decoder layer at a
+// time is copied to the GPU, computed, and its slot reused. Here the copy runs
+// on a side stream into two device slots (double buffering): the copy of layer
+// i+1 overlaps compute on layer i, ordered only by events (copy_done[slot] on
+// the side stream, compute_done[slot] on the compute stream). The backward
+// re-streams the layers in reverse from layer-boundary checkpoints; the two
+// layers still in the slots when the forward ends are used directly.
+// DPO (same pages, "Do SFT para os métodos de preferência"): the reference
+// model is the same layer stream with the adapters off. With
+// QLX_DPO_REF_FUSED the reference forward of each layer runs while that layer
+// is resident for the policy forward, so DPO reads the stack as often as SFT;
+// QLX_DPO_REF_SEPARATE streams a separate reference pass first.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "layer.h"
+
+namespace qlx {
+
+static thread_local std::string g_err;
+void set_error(const std::string& msg) { g_err = msg; }
+void check_launch(const char* what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) throw Error{QLX_EHIP, std::string(what) + ": " + hipGetErrorString(e)};
+}
+
+template <typename F>
+static int guarded(F&& f) {
+    try {
+        f();
+        return QLX_OK;
+    } catch (const Error& e) {
+        set_error(e.msg);
+        return e.code;
+    } catch (const std::exception& e) {
+        set_error(std::string("internal error: ") + e.what());
+        return QLX_EHIP;
+    } catch (...) {
+        set_error("internal error");
+        return QLX_EHIP;
+    }
+}
+
+static inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+#define REQ_PTR(p, name) QLX_REQUIRE((p) != nullptr, QLX_EINVAL, std::string(name) + " is NULL")
+#define REQ_AL(p, name) QLX_REQUIRE(al16(p), QLX_EINVAL, std::string(name) + " must be 16-byte aligned")
+
+static void check_ws(void* ws, size_t ws_bytes, size_t need) {
+    QLX_REQUIRE(ws_bytes >= need, QLX_EWORKSPACE,
+                "workspace too small: need " + std::to_string(need) + " bytes, got " + std::to_string(ws_bytes));
+    QLX_REQUIRE(need == 0 || ws != nullptr, QLX_EINVAL, "workspace is NULL");
+    QLX_REQUIRE(al16(ws), QLX_EINVAL, "workspace must be 16-byte aligned");
+}
+
+// ------------------------------------------------------------ QLoRA linear
+struct LinearWs {
+    uint16_t *Ab, *Bb, *u, *du;
+    float* partial;
+};
+static LinearWs carve_linear(Carver& c, int64_t T, int64_t in_f, int64_t out_f, int r) {
+    LinearWs w;
+    w.Ab = c.take<uint16_t>(size_t(r) * in_f);
+    w.Bb = c.take<uint16_t>(size_t(out_f) * r);
+    w.u = c.take<uint16_t>(size_t(T) * r);
+    w.du = c.take<uint16_t>(size_t(T) * r);
+    w.partial = c.take<float>(kGemmPartialFloats);
+    return w;
+}
+
+static void validate_linear(int64_t T, const qlx_nf4& W, const float* A, const float* B, int r) {
+    QLX_REQUIRE(T >= 0 && W.rows > 0 && W.cols > 0, QLX_EINVAL, "linear: T >= 0, W.rows > 0, W.cols > 0");
+    QLX_REQUIRE(T <= INT32_MAX && W.rows <= INT32_MAX && W.cols <= INT32_MAX, QLX_EUNSUPPORTED, "linear: sizes exceed int32");
+    REQ_PTR(W.packed, "W.packed");
+    REQ_PTR(W.absmax, "W.absmax");
+    REQ_AL(W.packed, "W.packed");
+    QLX_REQUIRE((A == nullptr) == (B == nullptr), QLX_EINVAL, "linear: A and B must both be set or both NULL");
+    if (A) QLX_REQUIRE(r > 0, QLX_EINVAL, "linear: r must be positive with LoRA on");
+    QLX_REQUIRE(W.cols % 4 == 0, QLX_EUNSUPPORTED, "linear: in_features must be a multiple of 4");
+}
+
+}  // namespace qlx
+
+using namespace qlx;
+
+extern "C" {
+
+const char* qlx_last_error(void) { return g_err.c_str(); }
+const char* qlx_version(void) { return "qlx 0.1 (gfx950)"; }
+
+int nf4_quantize(const uint16_t* w, int64_t rows, int64_t cols, uint8_t* packed, float* absmax, void* stream) {
+    return guarded([&] {
+        QLX_REQUIRE(rows >= 0 && cols >= 0, QLX_EINVAL, "nf4_quantize: negative size");
+        const int64_t n = rows * cols;
+        if (n == 0) return;
+        REQ_PTR(w, "w");
+        REQ_PTR(packed, "packed");
+        REQ_PTR(absmax, "absmax");
+        launch_nf4_quantize(w, n, packed, absmax, static_cast<hipStream_t>(stream));
+    });
+}
+
+int nf4_dequant(const uint8_t* packed, const float* absmax, int64_t rows, int64_t cols, int out_dtype, void* out,
+                void* stream) {
+    return guarded([&] {
+        QLX_REQUIRE(rows >= 0 && cols >= 0, QLX_EINVAL, "nf4_dequant: negative size");
+        QLX_REQUIRE(out_dtype == QLX_F32 || out_dtype == QLX_BF16, QLX_EINVAL, "nf4_dequant: out_dtype");
+        const int64_t n = rows * cols;
+        if (n == 0) return;
+        REQ_PTR(packed, "packed");
+        REQ_PTR(absmax, "absmax");
+        REQ_PTR(out, "out");
+        QLX_REQUIRE((reinterpret_cast<uintptr_t>(packed) & 3) == 0, QLX_EINVAL, "packed must be 4-byte aligned");
+        REQ_AL(out, "out");
+        launch_nf4_dequant(packed, absmax, n, out_dtype, out, static_cast<hipStream_t>(stream));
+    });
+}
+
+size_t qlx_linear_workspace_bytes(int64_t T, int64_t in_f, int64_t out_f, int r) {
+    if (T < 0 || in_f <= 0 || out_f <= 0 || r < 0) return 0;
+    Carver c(nullptr);
+    carve_linear(c, T, in_f, out_f, std::max(r, 0));
+    return c.size();
+}
+
+int qlora_linear_fwd(const uint16_t* x, int64_t T, qlx_nf4 W, const float* A, const float* B, int r, float scale,
+                     uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
+    return guarded([&] {
+        validate_linear(T, W, A, B, r);
+        if (T == 0) return;
+        REQ_PTR(x, "x");
+        REQ_PTR(y, "y");
+        const int rr = A ? r : 0;
+        check_ws(ws, ws_bytes, qlx_linear_workspace_bytes(T, W.cols, W.rows, rr));
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        Carver c(ws);
+        LinearWs w = carve_linear(c, T, W.cols, W.rows, rr);
+        const int M = int(T), N = int(W.rows), K = int(W.cols);
+        GemmParams p;
+        p.M = M;
+        p.N = N;
+        p.K = K;
+        p.A = x;
+        p.lda = K;
+        p.B = W.packed;
+        p.absmax = W.absmax;
+        p.nf4_cols = K;
+        if (A) {
+            LoraSeg seg{A, B, N};
+            launch_lora_pack(&seg, 1, r, K, scale, w.Ab, w.Bb, s);
+            GemmParams pu;
+            pu.M = M;
+            pu.N = r;
+            pu.K = K;
+            pu.A = x;
+            pu.lda = K;
+            pu.B = w.Ab;
+            pu.ldb = K;
+            pu.C = w.u;
+            pu.ldc = r;
+            pu.c_type = C_BF16;
+            gemm(pu, A_ROW, B_DENSE_NT, TE_BF16, w.partial, s);
+            p.K2 = r;
+            p.A2 = w.u;
+            p.lda2 = r;
+            p.B2 = w.Bb;
+            p.ldb2 = r;
+        }
+        p.C = y;
+        p.ldc = N;
+        p.c_type = C_BF16;
+        gemm(p, A_ROW, B_NF4_NT, TE_BF16, w.partial, s);
+    });
+}
+
+int qlora_linear_bwd(const uint16_t* dy, const uint16_t* x, int64_t T, qlx_nf4 W, const float* A, const float* B,
+                     int r, float scale, uint16_t* dx, float* dA, float* dB, int accumulate, void* ws,
+                     size_t ws_bytes, void* stream) {
+    return guarded([&] {
+        validate_linear(T, W, A, B, r);
+        if (A) {
+            REQ_PTR(dA, "dA");
+            REQ_PTR(dB, "dB");
+        }
+        if (T == 0) return;
+        REQ_PTR(dy, "dy");
+        REQ_PTR(x, "x");
+        const int rr = A ? r : 0;
+        check_ws(ws, ws_bytes, qlx_linear_workspace_bytes(T, W.cols, W.rows, rr));
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        Carver c(ws);
+        LinearWs w = carve_linear(c, T, W.cols, W.rows, rr);
+        const int M = int(T), N = int(W.rows), K = int(W.cols);  // forward: y [T, N] = x [T, K] W^T
+        if (A) {
+            LoraSeg seg{A, B, N};
+            launch_lora_pack(&seg, 1, r, K, scale, w.Ab, w.Bb, s);
+            GemmParams pu;  // u = x A^T
+            pu.M = M;
+            pu.N = r;
+            pu.K = K;
+            pu.A = x;
+            pu.lda = K;
+            pu.B = w.Ab;
+            pu.ldb = K;
+            pu.C = w.u;
+            pu.ldc = r;
+            pu.c_type = C_BF16;
+            gemm(pu, A_ROW, B_DENSE_NT, TE_BF16, w.partial, s);
+            GemmParams pd;  // du = dy (sB)
+            pd.M = M;
+            pd.N = r;
+            pd.K = N;
+            pd.A = dy;
+            pd.lda = N;
+            pd.B = w.Bb;
+            pd.ldb = r;
+            pd.C = w.du;
+            pd.ldc = r;
+            pd.c_type = C_BF16;
+            gemm(pd, A_ROW, B_DENSE_NN, TE_BF16, w.partial, s);
+        }
+        if (dx) {
+            GemmParams p;
+            p.M = M;
+            p.N = K;
+            p.K = N;
+            p.A = dy;
+            p.lda = N;
+            p.B = W.packed;
+            p.absmax = W.absmax;
+            p.nf4_cols = K;
+            if (A) {
+                p.K2 = r;
+                p.A2 = w.du;
+                p.lda2 = r;
+                p.B2 = w.Ab;
+                p.ldb2 = K;
+            }
+            p.C = dx;
+            p.ldc = K;
+            p.c_type = C_BF16;
+            gemm(p, A_ROW, B_NF4_NN, TE_BF16, w.partial, s);
+        }
+        if (A) {
+            GemmParams pb;  // dB = s dy^T u
+            pb.M = N;
+            pb.N = r;
+            pb.K = M;
+            pb.A = dy;
+            pb.lda = N;
+            pb.B = w.u;
+            pb.ldb = r;
+            pb.C = dB;
+            pb.ldc = r;
+            pb.c_type = C_F32;
+            pb.alpha = scale;
+            pb.accumulate = accumulate;
+            gemm(pb, A_TRANS, B_DENSE_NN, TE_BF16, w.partial, s);
+            GemmParams pa;  // dA = du^T x
+            pa.M = r;
+            pa.N = K;
+            pa.K = M;
+            pa.A = w.du;
+            pa.lda = r;
+            pa.B = x;
+            pa.ldb = K;
+            pa.C = dA;
+            pa.ldc = K;
+            pa.c_type = C_F32;
+            pa.accumulate = accumulate;
+            gemm(pa, A_TRANS, B_DENSE_NN, TE_BF16, w.partial, s);
+        }
+    });
+}
+
+int qlx_layer_blob_layout(const qlx_dims* d, uint64_t offsets[QLX_BLOB_NSEG], uint64_t* total_bytes) {
+    return guarded([&] {
+        validate_dims(d);
+        REQ_PTR(offsets, "offsets");
+        REQ_PTR(total_bytes, "total_bytes");
+        blob_layout(*d, offsets, total_bytes);
+    });
+}
+
+size_t qlx_layer_workspace_bytes(const qlx_dims* d, int batch, int seq) {
+    if (!d || batch <= 0 || seq <= 0) return 0;
+    return layer_ws_bytes(make_geom(*d, batch, seq));
+}
+
+static void validate_lora(const qlx_lora* l) {
+    for (int p = 0; p < 7; ++p) {
+        QLX_REQUIRE(l->A[p] && l->B[p], QLX_EINVAL, "lora: every A[p] and B[p] must be set");
+    }
+}
+static void validate_grads(const qlx_lora_grad* g) {
+    REQ_PTR(g, "grads");
+    for (int p = 0; p < 7; ++p) QLX_REQUIRE(g->dA[p] && g->dB[p], QLX_EINVAL, "grads: every dA[p], dB[p] must be set");
+}
+static void validate_bs(int batch, int seq) {
+    QLX_REQUIRE(batch > 0 && seq > 0, QLX_EINVAL, "batch and seq must be positive");
+    QLX_REQUIRE(int64_t(batch) * seq <= (1 << 24), QLX_EUNSUPPORTED, "batch*seq too large");
+}
+
+int layer_fwd(const qlx_dims* d, const void* blob, const qlx_lora* lora, const float* h_in, int batch, int seq,
+              float* h_out, void* ws, size_t ws_bytes, void* stream) {
+    return guarded([&] {
+        validate_dims(d);
+        validate_bs(batch, seq);
+        REQ_PTR(blob, "blob");
+        REQ_AL(blob, "blob");
+        REQ_PTR(h_in, "h_in");
+        REQ_PTR(h_out, "h_out");
+        if (lora) validate_lora(lora);
+        const LayerGeom g = make_geom(*d, batch, seq);
+        check_ws(ws, ws_bytes, layer_ws_bytes(g));
+        Carver c(ws);
+        LayerWs w = carve_layer(c, g);
+        layer_forward(g, blob_ptrs(*d, blob), lora, false, h_in, h_out, w, static_cast<hipStream_t>(stream));
+    });
+}
+
+int layer_bwd(const qlx_dims* d, const void* blob, const qlx_lora* lora, const float* h_in, const float* dh_out,
+              int batch, int seq, float* dh_in, const qlx_lora_grad* grads, void* ws, size_t ws_bytes, void* stream) {
+    return guarded([&] {
+        validate_dims(d);
+        validate_bs(batch, seq);
+        REQ_PTR(blob, "blob");
+        REQ_AL(blob, "blob");
+        REQ_PTR(lora, "lora");
+        validate_lora(lora);
+        validate_grads(grads);
+        REQ_PTR(h_in, "h_in");
+        REQ_PTR(dh_out, "dh_out");
+        const LayerGeom g = make_geom(*d, batch, seq);
+        check_ws(ws, ws_bytes, layer_ws_bytes(g));
+        Carver c(ws);
+        LayerWs w = carve_layer(c, g);
+        layer_backward(g, blob_ptrs(*d, blob), lora, h_in, dh_out, dh_in, grads, w, static_cast<hipStream_t>(stream));
+    });
+}
+
+}  // extern "C"
+
+// ===================================================================== streamer
+struct qlx_ctx {
+    int device = 0;
+    hipStream_t side = nullptr;
+    hipEvent_t copy_done[2] = {nullptr, nullptr};
+    hipEvent_t compute_done[2] = {nullptr, nullptr};
+    hipEvent_t step_begin = nullptr, step_end = nullptr;
+    std::vector<hipEvent_t> copy_ev;  // timing pairs for copies (begin, end)
+    size_t copies_used = 0;
+    qlx_stats stats{};
+};
+
+namespace qlx {
+
+struct StepWs {
+    char* slot[2];
+    float* ckpt;     // (L+1) x [T, H]
+    float* href[2];  // reference stream (DPO)
+    int32_t* toks;   // [T]
+    LayerWs lw;
+    uint16_t* nf;  // fp16 [T, H]
+    float* rstd_f;
+    float* logits;  // [T, V]
+    uint16_t* dz;   // fp16 [T, V]
+    float *lse, *picked, *lse_ref, *pk_ref;
+    float* dnf;  // [T, H]
+    float* dh[2];
+    float* gseq;
+};
+
+static StepWs carve_step(Carver& c, const qlx_dims& d, int T, int kind, uint64_t blob_bytes) {
+    StepWs w{};
+    const LayerGeom g = make_geom(d, 1, T);  // only H, V needed here
+    const size_t H = size_t(d.hidden), V = size_t(d.vocab), L = size_t(d.n_layers), Tz = size_t(T);
+    w.slot[0] = c.take<char>(blob_bytes);
+    w.slot[1] = c.take<char>(blob_bytes);
+    w.ckpt = c.take<float>((L + 1) * Tz * H);
+    if (kind == 1) {
+        w.href[0] = c.take<float>(Tz * H);
+        w.href[1] = c.take<float>(Tz * H);
+        w.toks = c.take<int32_t>(Tz);
+        w.lse_ref = c.take<float>(Tz);
+        w.pk_ref = c.take<float>(Tz);
+        w.gseq = c.take<float>(64);
+    }
+    w.nf = c.take<uint16_t>(Tz * H);
+    w.rstd_f = c.take<float>(Tz);
+    w.logits = c.take<float>(Tz * V);
+    w.dz = c.take<uint16_t>(Tz * V);
+    w.lse = c.take<float>(Tz);
+    w.picked = c.take<float>(Tz);
+    w.dnf = c.take<float>(Tz * H);
+    w.dh[0] = c.take<float>(Tz * H);
+    w.dh[1] = c.take<float>(Tz * H);
+    (void)g;
+    return w;
+}
+
+static size_t step_ws_bytes(const qlx_dims& d, int kind, int batch, int seq) {
+    uint64_t off[QLX_BLOB_NSEG], blob_bytes;
+    blob_layout(d, off, &blob_bytes);
+    const int T = batch * seq;
+    Carver c(nullptr);
+    carve_step(c, d, T, kind, blob_bytes);
+    carve_layer(c, make_geom(d, batch, seq));
+    return c.size();
+}
+
+// Streams layers through the two slots and hands each resident layer to `use`.
+class Streamer {
+   public:
+    Streamer(qlx_ctx* ctx, const qlx_model* m, int mode, const StepWs& w, uint64_t blob_bytes, hipStream_t main)
+        : ctx_(ctx), m_(m), mode_(mode), w_(w), bytes_(blob_bytes), main_(main) {
+        held_[0] = held_[1] = -1;
+    }
+    // Make layer i resident (if not already), wait for it on the main stream,
+    // and return its device pointer. prefetch_next >= 0 also starts the copy
+    // of that layer into the other slot once its previous user is done.
+    const void* acquire(int i) {
+        if (mode_ == QLX_RESIDENT) return m_->layer_blobs[i];
+        const int sl = slot_of(i);
+        if (held_[sl] != i) issue_copy(i, sl);
+        QLX_CHECK_HIP(hipStreamWaitEvent(main_, ctx_->copy_done[sl], 0));
+        return w_.slot[sl];
+    }
+    void prefetch(int i) {
+        if (mode_ == QLX_RESIDENT || i < 0 || i >= m_->dims.n_layers) return;
+        const int sl = slot_of(i);
+        if (held_[sl] == i) return;
+        issue_copy(i, sl);
+    }
+    void release(int i) {
+        if (mode_ == QLX_RESIDENT) return;
+        QLX_CHECK_HIP(hipEventRecord(ctx_->compute_done[slot_of(i)], main_));
+    }
+    void forget() { held_[0] = held_[1] = -1; }
+
+   private:
+    int slot_of(int i) const { return i & 1; }
+    void issue_copy(int i, int sl) {
+        // the slot's previous contents must be finished with on the main stream
+        QLX_CHECK_HIP(hipStreamWaitEvent(ctx_->side, ctx_->compute_done[sl], 0));
+        hipEvent_t* ev = next_timing_pair();
+        if (ev) QLX_CHECK_HIP(hipEventRecord(ev[0], ctx_->side));
+        QLX_CHECK_HIP(hipMemcpyAsync(w_.slot[sl], m_->layer_blobs[i], bytes_, hipMemcpyHostToDevice, ctx_->side));
+        if (ev) QLX_CHECK_HIP(hipEventRecord(ev[1], ctx_->side));
+        QLX_CHECK_HIP(hipEventRecord(ctx_->copy_done[sl], ctx_->side));
+        held_[sl] = i;
+        ctx_->stats.layer_reads += 1;
+        ctx_->stats.h2d_bytes += int64_t(bytes_);
+    }
+    hipEvent_t* next_timing_pair() {
+        if (ctx_->copies_used + 2 > ctx_->copy_ev.size()) return nullptr;
+        hipEvent_t* e = &ctx_->copy_ev[ctx_->copies_used];
+        ctx_->copies_used += 2;
+        return e;
+    }
+    qlx_ctx* ctx_;
+    const qlx_model* m_;
+    int mode_;
+    const StepWs& w_;
+    uint64_t bytes_;
+    hipStream_t main_;
+    int held_[2];
+};
+
+static void validate_model(qlx_ctx* ctx, const qlx_model* m, int mode) {
+    REQ_PTR(ctx, "ctx");
+    REQ_PTR(m, "model");
+    validate_dims(&m->dims);
+    QLX_REQUIRE(mode == QLX_STREAMED || mode == QLX_RESIDENT, QLX_EINVAL, "mode must be QLX_STREAMED or QLX_RESIDENT");
+    REQ_PTR(m->layer_blobs, "model.layer_blobs");
+    REQ_PTR(m->embed_f16, "model.embed_f16");
+    REQ_PTR(m->lm_head_f16, "model.lm_head_f16");
+    REQ_PTR(m->final_norm, "model.final_norm");
+    REQ_PTR(m->lora, "model.lora");
+    REQ_AL(m->lm_head_f16, "model.lm_head_f16");
+    for (int i = 0; i < m->dims.n_layers; ++i) {
+        const void* b = m->layer_blobs[i];
+        QLX_REQUIRE(b != nullptr, QLX_EINVAL, "model.layer_blobs[" + std::to_string(i) + "] is NULL");
+        REQ_AL(b, "layer blob");
+        validate_lora(&m->lora[i]);
+        if (mode == QLX_STREAMED) {
+            hipPointerAttribute_t attr;
+            const hipError_t e = hipPointerGetAttributes(&attr, b);
+            if (e != hipSuccess) (void)hipGetLastError();
+            QLX_REQUIRE(e == hipSuccess && attr.type == hipMemoryTypeHost, QLX_ENOTPINNED,
+                        "layer blob " + std::to_string(i) + " is not pinned host memory");
+        }
+    }
+}
+
+static void begin_step(qlx_ctx* ctx, hipStream_t main) {
+    QLX_CHECK_HIP(hipSetDevice(ctx->device));
+    ctx->stats = qlx_stats{};
+    ctx->copies_used = 0;
+    QLX_CHECK_HIP(hipEventRecord(ctx->step_begin, main));
+    // the side stream starts after everything already queued on main
+    QLX_CHECK_HIP(hipEventRecord(ctx->compute_done[0], main));
+    QLX_CHECK_HIP(hipEventRecord(ctx->compute_done[1], main));
+}
+static void end_step(qlx_ctx* ctx, hipStream_t main) {
+    hipEvent_t join;
+    QLX_CHECK_HIP(hipEventCreateWithFlags(&join, hipEventDisableTiming));
+    QLX_CHECK_HIP(hipEventRecord(join, ctx->side));
+    QLX_CHECK_HIP(hipStreamWaitEvent(main, join, 0));
+    QLX_CHECK_HIP(hipEventDestroy(join));
+    QLX_CHECK_HIP(hipEventRecord(ctx->step_end, main));
+}
+
+// Final RMSNorm (fp16 out) + LM head logits [T, V] (fp32).
+static void head_logits(const qlx_model* m, const float* hL, int T, StepWs& w, float* partial, hipStream_t s) {
+    const qlx_dims& d = m->dims;
+    launch_rmsnorm_fwd(hL, m->final_norm, T, d.hidden, d.rms_eps, w.nf, 1, w.rstd_f, s);
+    GemmParams p;
+    p.M = T;
+    p.N = d.vocab;
+    p.K = d.hidden;
+    p.A = w.nf;
+    p.lda = d.hidden;
+    p.B = m->lm_head_f16;
+    p.ldb = d.hidden;
+    p.C = w.logits;
+    p.ldc = d.vocab;
+    p.c_type = C_F32;
+    gemm(p, A_ROW, B_DENSE_NT, TE_F16, partial, s);
+}
+// dh = RMSNorm^T( (dz . head) * alpha )
+static void head_backward(const qlx_model* m, const float* hL, int T, float alpha, StepWs& w, float* dh_out,
+                          float* partial, hipStream_t s) {
+    const qlx_dims& d = m->dims;
+    GemmParams p;
+    p.M = T;
+    p.N = d.hidden;
+    p.K = d.vocab;
+    p.A = w.dz;
+    p.lda = d.vocab;
+    p.B = m->lm_head_f16;
+    p.ldb = d.hidden;
+    p.C = w.dnf;
+    p.ldc = d.hidden;
+    p.c_type = C_F32;
+    p.alpha = alpha;
+    gemm(p, A_ROW, B_DENSE_NN, TE_F16, partial, s);
+    launch_rmsnorm_bwd(w.dnf, hL, m->final_norm, w.rstd_f, nullptr, T, d.hidden, dh_out, s);
+}
+
+// dz is stored in fp16 scaled by 2^12 so that softmax values ~1/V stay normal.
+constexpr float kDzScale = 4096.f;
+
+static void backward_layers(Streamer& st, const qlx_model* m, const LayerGeom& g, StepWs& w, float* dh,
+                            const qlx_lora_grad* grads, hipStream_t s) {
+    const int L = m->dims.n_layers;
+    const size_t TH = size_t(g.T) * g.H;
+    float* cur = dh;
+    float* nxt = (dh == w.dh[0]) ? w.dh[1] : w.dh[0];
+    for (int i = L - 1; i >= 0; --i) {
+        const void* blob = st.acquire(i);
+        st.prefetch(i - 1);
+        layer_backward(g, blob_ptrs(m->dims, blob), &m->lora[i], w.ckpt + size_t(i) * TH, cur, i > 0 ? nxt : nullptr,
+                       &grads[i], w.lw, s);
+        st.release(i);
+        std::swap(cur, nxt);
+    }
+}
+
+}  // namespace qlx
+
+extern "C" {
+
+int qlx_ctx_create(qlx_ctx** out, int device) {
+    return guarded([&] {
+        REQ_PTR(out, "out");
+        int n = 0;
+        QLX_CHECK_HIP(hipGetDeviceCount(&n));
+        QLX_REQUIRE(device >= 0 && device < n, QLX_EINVAL, "device out of range");
+        QLX_CHECK_HIP(hipSetDevice(device));
+        qlx_ctx* c = new qlx_ctx();
+        c->device = device;
+        QLX_CHECK_HIP(hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking));
+        for (int i = 0; i < 2; ++i) {
+            QLX_CHECK_HIP(hipEventCreateWithFlags(&c->copy_done[i], hipEventDisableTiming));
+            QLX_CHECK_HIP(hipEventCreateWithFlags(&c->compute_done[i], hipEventDisableTiming));
+        }
+        QLX_CHECK_HIP(hipEventCreate(&c->step_begin));
+        QLX_CHECK_HIP(hipEventCreate(&c->step_end));
+        c->copy_ev.resize(512);
+        for (auto& e : c->copy_ev) QLX_CHECK_HIP(hipEventCreate(&e));
+        *out = c;
+    });
+}
+
+int qlx_ctx_destroy(qlx_ctx* ctx) {
+    return guarded([&] {
+        if (!ctx) return;
+        (void)hipSetDevice(ctx->device);
+        (void)hipStreamSynchronize(ctx->side);
+        for (auto& e : ctx->copy_ev) (void)hipEventDestroy(e);
+        for (int i = 0; i < 2; ++i) {
+            (void)hipEventDestroy(ctx->copy_done[i]);
+            (void)hipEventDestroy(ctx->compute_done[i]);
+        }
+        (void)hipEventDestroy(ctx->step_begin);
+        (void)hipEventDestroy(ctx->step_end);
+        (void)hipStreamDestroy(ctx->side);
+        delete ctx;
+    });
+}
+
+int qlx_ctx_sync(qlx_ctx* ctx, qlx_stats* stats) {
+    return guarded([&] {
+        REQ_PTR(ctx, "ctx");
+        QLX_CHECK_HIP(hipSetDevice(ctx->device));
+        QLX_CHECK_HIP(hipStreamSynchronize(ctx->side));
+        QLX_CHECK_HIP(hipEventSynchronize(ctx->step_end));
+        float ms = 0.f;
+        QLX_CHECK_HIP(hipEventElapsedTime(&ms, ctx->step_begin, ctx->step_end));
+        ctx->stats.step_ms = ms;
+        float h2d = 0.f;
+        for (size_t i = 0; i + 1 < ctx->copies_used; i += 2) {
+            float t = 0.f;
+            QLX_CHECK_HIP(hipEventElapsedTime(&t, ctx->copy_ev[i], ctx->copy_ev[i + 1]));
+            h2d += t;
+        }
+        ctx->stats.h2d_ms = h2d;
+        if (stats) *stats = ctx->stats;
+    });
+}
+
+size_t qlx_step_workspace_bytes(const qlx_dims* d, int kind, int batch, int seq) {
+    if (!d || batch <= 0 || seq <= 0 || (kind != 0 && kind != 1)) return 0;
+    return step_ws_bytes(*d, kind, kind == 1 ? 2 * batch : batch, seq);
+}
+
+int stream_step_sft(qlx_ctx* ctx, const qlx_model* m, const int32_t* tokens, int batch, int seq, int mode,
+                    float* loss, const qlx_lora_grad* grads, void* ws, size_t ws_bytes, void* stream) {
+    return guarded([&] {
+        validate_model(ctx, m, mode);
+        validate_bs(batch, seq);
+        QLX_REQUIRE(seq >= 2, QLX_EINVAL, "seq must be >= 2 for next-token loss");
+        REQ_PTR(tokens, "tokens");
+        REQ_PTR(loss, "loss");
+        REQ_PTR(grads, "grads");
+        for (int i = 0; i < m->dims.n_layers; ++i) validate_grads(&grads[i]);
+        const qlx_dims& d = m->dims;
+        check_ws(ws, ws_bytes, step_ws_bytes(d, 0, batch, seq));
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        uint64_t off[QLX_BLOB_NSEG], blob_bytes;
+        blob_layout(d, off, &blob_bytes);
+        const int T = batch * seq;
+        Carver c(ws);
+        StepWs w = carve_step(c, d, T, 0, blob_bytes);
+        const LayerGeom g = make_geom(d, batch, seq);
+        w.lw = carve_layer(c, g);
+        const size_t TH = size_t(T) * d.hidden;
+        const int L = d.n_layers;
+
+        begin_step(ctx, s);
+        Streamer st(ctx, m, mode, w, blob_bytes, s);
+        launch_embed(tokens, m->embed_f16, T, d.hidden, d.vocab, w.ckpt, s);
+        st.prefetch(0);
+        for (int i = 0; i < L; ++i) {
+            const void* blob = st.acquire(i);
+            st.prefetch(i + 1);
+            layer_forward(g, blob_ptrs(d, blob), &m->lora[i], false, w.ckpt + size_t(i) * TH,
+                          w.ckpt + size_t(i + 1) * TH, w.lw, s);
+            st.release(i);
+        }
+        const float* hL = w.ckpt + size_t(L) * TH;
+        head_logits(m, hL, T, w, w.lw.partial, s);
+        launch_ce_stats(w.logits, T, d.vocab, tokens, seq, 0, w.lse, w.picked, s);
+        launch_sft_loss(w.lse, w.picked, T, seq, loss, s);
+        launch_ce_grad(w.logits, w.lse, T, d.vocab, tokens, seq, 0, 0, kDzScale, nullptr, w.dz, s);
+        const float alpha = 1.0f / (kDzScale * float(batch) * float(seq - 1));
+        head_backward(m, hL, T, alpha, w, w.dh[0], w.lw.partial, s);
+        ctx->stats.layer_passes = 2 * L;
+        backward_layers(st, m, g, w, w.dh[0], grads, s);
+        end_step(ctx, s);
+    });
+}
+
+int stream_step_dpo(qlx_ctx* ctx, const qlx_model* m, const int32_t* chosen, const int32_t* rejected, int pairs,
+                    int seq, int prompt_len, float beta, int mode, int ref_schedule, float* loss, float* logps,
+                    const qlx_lora_grad* grads, void* ws, size_t ws_bytes, void* stream) {
+    return guarded([&] {
+        validate_model(ctx, m, mode);
+        QLX_REQUIRE(pairs > 0 && pairs <= 32, QLX_EINVAL, "pairs must be in 1..32");
+        validate_bs(2 * pairs, seq);
+        QLX_REQUIRE(prompt_len >= 1 && prompt_len < seq, QLX_EINVAL, "prompt_len must be in [1, seq)");
+        QLX_REQUIRE(ref_schedule == QLX_DPO_REF_FUSED || ref_schedule == QLX_DPO_REF_SEPARATE, QLX_EINVAL,
+                    "ref_schedule");
+        QLX_REQUIRE(beta == beta, QLX_EINVAL, "beta is NaN");
+        REQ_PTR(chosen, "chosen");
+        REQ_PTR(rejected, "rejected");
+        REQ_PTR(loss, "loss");
+        REQ_PTR(logps, "logps");
+        REQ_PTR(grads, "grads");
+        for (int i = 0; i < m->dims.n_layers; ++i) validate_grads(&grads[i]);
+        const qlx_dims& d = m->dims;
+        const int B = 2 * pairs;
+        check_ws(ws, ws_bytes, step_ws_bytes(d, 1, B, seq));
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        uint64_t off[QLX_BLOB_NSEG], blob_bytes;
+        blob_layout(d, off, &blob_bytes);
+        const int T = B * seq;
+        Carver c(ws);
+        StepWs w = carve_step(c, d, T, 1, blob_bytes);
+        const LayerGeom g = make_geom(d, B, seq);
+        w.lw = carve_layer(c, g);
+        const size_t TH = size_t(T) * d.hidden;
+        const int L = d.n_layers;
+
+        begin_step(ctx, s);
+        const size_t half = size_t(pairs) * seq * sizeof(int32_t);
+        QLX_CHECK_HIP(hipMemcpyAsync(w.toks, chosen, half, hipMemcpyDeviceToDevice, s));
+        QLX_CHECK_HIP(hipMemcpyAsync(w.toks + size_t(pairs) * seq, rejected, half, hipMemcpyDeviceToDevice, s));
+        Streamer st(ctx, m, mode, w, blob_bytes, s);
+        launch_embed(w.toks, m->embed_f16, T, d.hidden, d.vocab, w.ckpt, s);
+        const int start = prompt_len - 1;
+        float* ref_cur = w.ckpt;  // reference and policy share h_0
+        float* ref_nxt = w.href[0];
+        if (ref_schedule == QLX_DPO_REF_SEPARATE) {
+            st.prefetch(0);
+            for (int i = 0; i < L; ++i) {
+                const void* blob = st.acquire(i);
+                st.prefetch(i + 1);
+                layer_forward(g, blob_ptrs(d, blob), nullptr, false, ref_cur, ref_nxt, w.lw, s);
+                st.release(i);
+                ref_cur = ref_nxt;
+                ref_nxt = (ref_cur == w.href[0]) ? w.href[1] : w.href[0];
+            }
+            st.forget();  // the policy pass streams the stack again from layer 0
+        }
+        st.prefetch(0);
+        for (int i = 0; i < L; ++i) {
+            const void* blob = st.acquire(i);
+            st.prefetch(i + 1);
+            const BlobPtrs wt = blob_ptrs(d, blob);
+            if (ref_schedule == QLX_DPO_REF_FUSED) {
+                layer_forward(g, wt, nullptr, false, ref_cur, ref_nxt, w.lw, s);
+                ref_cur = ref_nxt;
+                ref_nxt = (ref_cur == w.href[0]) ? w.href[1] : w.href[0];
+            }
+            layer_forward(g, wt, &m->lora[i], false, w.ckpt + size_t(i) * TH, w.ckpt + size_t(i + 1) * TH, w.lw, s);
+            st.release(i);
+        }
+        // reference log-probs
+        head_logits(m, ref_cur, T, w, w.lw.partial, s);
+        launch_ce_stats(w.logits, T, d.vocab, w.toks, seq, start, w.lse_ref, w.pk_ref, s);
+        // policy log-probs, loss, and dL/dlp
+        const float* hL = w.ckpt + size_t(L) * TH;
+        head_logits(m, hL, T, w, w.lw.partial, s);
+        launch_ce_stats(w.logits, T, d.vocab, w.toks, seq, start, w.lse, w.picked, s);
+        launch_dpo_loss(w.lse, w.picked, w.lse_ref, w.pk_ref, pairs, seq, prompt_len, beta, loss, logps, w.gseq, s);
+        // dz = g_seq (onehot - softmax) = (softmax - onehot) * (-g_seq)
+        launch_ce_grad(w.logits, w.lse, T, d.vocab, w.toks, seq, start, 1, -kDzScale, w.gseq, w.dz, s);
+        head_backward(m, hL, T, 1.0f / kDzScale, w, w.dh[0], w.lw.partial, s);
+        ctx->stats.layer_passes = 3 * L;
+        backward_layers(st, m, g, w, w.dh[0], grads, s);
+        end_step(ctx, s);
+    });
+}
+
+}  // extern "C"

@@ -1,0 +1,464 @@
+// Memory-bound kernels of the decoder layer and the loss: RMSNorm fwd/bwd,
+// rotate-half RoPE, SwiGLU fwd/bwd, embedding gather, LoRA operand staging,
+// causal-softmax fwd/bwd for attention, grouped-query gradient reduction,
+// cross-entropy statistics and gradients, SFT and DPO loss reductions.
+//
+// The layer is the Llama decoder the pages fine-tune (Llama-3.1-8B-Instruct:
+// rug.gal article intro; guillermodelpino.com article, "Qué es exactamente").
+// Every reduction runs in a fixed order (per-thread strided partial sums,
+// xor-shuffle wavefront trees, then the waves in index order), so results
+// never depend on scheduling.
+#include <cmath>
+
+#include "nf4_codes.h"
+#include "qlx_internal.h"
+
+namespace qlx {
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+__device__ inline float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+// Block-wide sum over 256 threads in a fixed order; every thread gets the result.
+__device__ inline float block_sum256(float v, float* red) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    return (red[0] + red[1]) + (red[2] + red[3]);
+}
+__device__ inline float block_max256(float v, float* red) {
+    v = wave_max(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// ------------------------------------------------------------------ RMSNorm
+// y = x * rstd * g, rstd = 1 / sqrt(mean(x^2) + eps). One workgroup per row.
+__global__ __launch_bounds__(256) void k_rmsnorm_fwd(const float* __restrict__ x, const float* __restrict__ g, int H,
+                                                     float eps, void* __restrict__ out, int out_f16,
+                                                     float* __restrict__ rstd) {
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const float* xr = x + row * H;
+    float ss = 0.f;
+    for (int j = threadIdx.x; j < H; j += 256) ss += xr[j] * xr[j];
+    ss = block_sum256(ss, red);
+    const float r = 1.0f / sqrtf(ss / float(H) + eps);
+    if (threadIdx.x == 0 && rstd) rstd[row] = r;
+    uint16_t* o = static_cast<uint16_t*>(out) + row * H;
+    for (int j = threadIdx.x; j < H; j += 256) {
+        const float y = xr[j] * r * g[j];
+        o[j] = out_f16 ? f32_to_f16_bits(y) : f32_to_bf16_bits(y);
+    }
+}
+
+// dx = dres + rstd * (dy*g - xhat * mean(dy*g*xhat)), xhat = x*rstd (g frozen).
+__global__ __launch_bounds__(256) void k_rmsnorm_bwd(const float* __restrict__ dy, const float* __restrict__ x,
+                                                     const float* __restrict__ g, const float* __restrict__ rstd,
+                                                     const float* __restrict__ dres, int H, float* __restrict__ dx) {
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const float* dyr = dy + row * H;
+    const float* xr = x + row * H;
+    const float r = rstd[row];
+    float dot = 0.f;
+    for (int j = threadIdx.x; j < H; j += 256) dot += (dyr[j] * g[j]) * (xr[j] * r);
+    dot = block_sum256(dot, red) / float(H);
+    for (int j = threadIdx.x; j < H; j += 256) {
+        const float xhat = xr[j] * r;
+        float v = r * (dyr[j] * g[j] - xhat * dot);
+        if (dres) v += dres[row * H + j];
+        dx[row * H + j] = v;
+    }
+}
+
+void launch_rmsnorm_fwd(const float* x, const float* g, int T, int H, float eps, void* out, int out_f16, float* rstd,
+                        hipStream_t s) {
+    if (T <= 0) return;
+    hipLaunchKernelGGL(k_rmsnorm_fwd, dim3(T), dim3(256), 0, s, x, g, H, eps, out, out_f16, rstd);
+    check_launch("rmsnorm_fwd");
+}
+void launch_rmsnorm_bwd(const float* dy, const float* x, const float* g, const float* rstd, const float* dres, int T,
+                        int H, float* dx, hipStream_t s) {
+    if (T <= 0) return;
+    hipLaunchKernelGGL(k_rmsnorm_bwd, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx);
+    check_launch("rmsnorm_bwd");
+}
+
+// ------------------------------------------------------------------ RoPE
+// Table cs[pos][j] = (cos, sin)(pos * theta^(-2j/hd)), angles in fp64.
+__global__ void k_rope_table(int seq, int hd, double theta, float2* cs) {
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    const int half = hd / 2;
+    if (idx >= seq * half) return;
+    const int pos = idx / half, j = idx % half;
+    const double inv = pow(theta, -2.0 * double(j) / double(hd));
+    const double ang = double(pos) * inv;
+    cs[idx] = make_float2(float(cos(ang)), float(sin(ang)));
+}
+
+// Rotate pairs (j, j + hd/2) of every head in columns [col0, col0 + nheads*hd)
+// of a bf16 [T, ld] buffer; row t has position t % seq. inverse = transpose.
+__global__ void k_rope(uint16_t* __restrict__ buf, int64_t ld, int T, int seq, int col0, int nheads, int hd,
+                       const float2* __restrict__ cs, int inverse) {
+    const int half = hd / 2;
+    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t total = int64_t(T) * nheads * half;
+    if (idx >= total) return;
+    const int j = int(idx % half);
+    const int h = int((idx / half) % nheads);
+    const int t = int(idx / (int64_t(half) * nheads));
+    const float2 c = cs[(t % seq) * half + j];
+    uint16_t* p = buf + int64_t(t) * ld + col0 + h * hd + j;
+    const float x1 = bf16_bits_to_f32(p[0]), x2 = bf16_bits_to_f32(p[half]);
+    float y1, y2;
+    if (!inverse) {
+        y1 = x1 * c.x - x2 * c.y;
+        y2 = x2 * c.x + x1 * c.y;
+    } else {
+        y1 = x1 * c.x + x2 * c.y;
+        y2 = x2 * c.x - x1 * c.y;
+    }
+    p[0] = f32_to_bf16_bits(y1);
+    p[half] = f32_to_bf16_bits(y2);
+}
+
+void launch_rope_table(int seq, int hd, float theta, float* cs, hipStream_t s) {
+    const int n = seq * (hd / 2);
+    hipLaunchKernelGGL(k_rope_table, dim3((n + 255) / 256), dim3(256), 0, s, seq, hd, double(theta),
+                       reinterpret_cast<float2*>(cs));
+    check_launch("rope_table");
+}
+void launch_rope(uint16_t* buf, int64_t ld, int T, int seq, int col0, int nheads, int hd, const float* cs, int inverse,
+                 hipStream_t s) {
+    const int64_t total = int64_t(T) * nheads * (hd / 2);
+    if (total <= 0) return;
+    hipLaunchKernelGGL(k_rope, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, buf, ld, T, seq, col0, nheads,
+                       hd, reinterpret_cast<const float2*>(cs), inverse);
+    check_launch("rope");
+}
+
+// ------------------------------------------------------------------ SwiGLU
+// gu = [gate | up] bf16 [T, 2I]; act = silu(gate) * up.
+__global__ void k_swiglu_fwd(const uint16_t* __restrict__ gu, int T, int I, uint16_t* __restrict__ act) {
+    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= int64_t(T) * I) return;
+    const int64_t t = idx / I, i = idx % I;
+    const float g = bf16_bits_to_f32(gu[t * 2 * I + i]);
+    const float u = bf16_bits_to_f32(gu[t * 2 * I + I + i]);
+    const float sg = 1.0f / (1.0f + expf(-g));
+    act[idx] = f32_to_bf16_bits(g * sg * u);
+}
+// dgate = da * up * silu'(gate), dup = da * silu(gate); silu' = s (1 + g (1 - s)).
+__global__ void k_swiglu_bwd(const uint16_t* __restrict__ dact, const uint16_t* __restrict__ gu, int T, int I,
+                             uint16_t* __restrict__ dgu) {
+    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= int64_t(T) * I) return;
+    const int64_t t = idx / I, i = idx % I;
+    const float g = bf16_bits_to_f32(gu[t * 2 * I + i]);
+    const float u = bf16_bits_to_f32(gu[t * 2 * I + I + i]);
+    const float da = bf16_bits_to_f32(dact[idx]);
+    const float sg = 1.0f / (1.0f + expf(-g));
+    dgu[t * 2 * I + i] = f32_to_bf16_bits(da * u * (sg * (1.0f + g * (1.0f - sg))));
+    dgu[t * 2 * I + I + i] = f32_to_bf16_bits(da * g * sg);
+}
+void launch_swiglu_fwd(const uint16_t* gu, int T, int I, uint16_t* act, hipStream_t s) {
+    const int64_t n = int64_t(T) * I;
+    if (n <= 0) return;
+    hipLaunchKernelGGL(k_swiglu_fwd, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, gu, T, I, act);
+    check_launch("swiglu_fwd");
+}
+void launch_swiglu_bwd(const uint16_t* dact, const uint16_t* gu, int T, int I, uint16_t* dgu, hipStream_t s) {
+    const int64_t n = int64_t(T) * I;
+    if (n <= 0) return;
+    hipLaunchKernelGGL(k_swiglu_bwd, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, dact, gu, T, I, dgu);
+    check_launch("swiglu_bwd");
+}
+
+// ------------------------------------------------------------------ embedding
+// h[t] = fp32(E[tok[t]]); an out-of-range id yields NaN (never an out-of-bounds read).
+__global__ void k_embed(const int32_t* __restrict__ tok, const uint16_t* __restrict__ E, int T, int H, int V,
+                        float* __restrict__ h) {
+    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx >= int64_t(T) * H) return;
+    const int64_t t = idx / H, j = idx % H;
+    const int id = tok[t];
+    h[idx] = (id >= 0 && id < V) ? f16_bits_to_f32(E[int64_t(id) * H + j]) : __int_as_float(0x7fc00000);
+}
+void launch_embed(const int32_t* tok, const uint16_t* E, int T, int H, int V, float* h, hipStream_t s) {
+    const int64_t n = int64_t(T) * H;
+    if (n <= 0) return;
+    hipLaunchKernelGGL(k_embed, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, tok, E, T, H, V, h);
+    check_launch("embed");
+}
+
+__global__ void k_f32_to_bf16(const float* __restrict__ x, int64_t n, uint16_t* __restrict__ y) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) y[i] = f32_to_bf16_bits(x[i]);
+}
+void launch_f32_to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s) {
+    if (n <= 0) return;
+    hipLaunchKernelGGL(k_f32_to_bf16, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, x, n, y);
+    check_launch("f32_to_bf16");
+}
+
+// ------------------------------------------------------------------ LoRA staging
+// Acat [nseg*r, in] = bf16(A_p) stacked; Bbd [sum out_p, nseg*r] block-diagonal
+// with block p = bf16(scale * B_p), zeros elsewhere. The zeros contribute
+// exact +0 products, so a projection only sees its own adapter.
+struct LoraSegs {
+    const float* A[3];
+    const float* B[3];
+    int out[3];
+    int nseg;
+};
+__global__ void k_lora_pack(const LoraSegs sg, int r, int in_f, float scale, uint16_t* __restrict__ Acat,
+                            uint16_t* __restrict__ Bbd, int64_t nA, int64_t nB, int ntot) {
+    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (idx < nA) {
+        const int64_t row = idx / in_f, k = idx % in_f;
+        const int p = int(row / r), i = int(row % r);
+        Acat[idx] = f32_to_bf16_bits(sg.A[p][int64_t(i) * in_f + k]);
+        return;
+    }
+    const int64_t jdx = idx - nA;
+    if (jdx >= nB) return;
+    const int rr = sg.nseg * r;
+    const int n = int(jdx / rr), c = int(jdx % rr);
+    const int q = c / r, j = c % r;
+    int off = 0, p = 0;
+    while (p < sg.nseg - 1 && n >= off + sg.out[p]) off += sg.out[p++];
+    Bbd[jdx] = (p == q) ? f32_to_bf16_bits(scale * sg.B[p][int64_t(n - off) * r + j]) : uint16_t(0);
+}
+void launch_lora_pack(const LoraSeg* segs, int nseg, int r, int in_f, float scale, uint16_t* Acat, uint16_t* Bbd,
+                      hipStream_t s) {
+    LoraSegs sg{};
+    int ntot = 0;
+    for (int p = 0; p < nseg; ++p) {
+        sg.A[p] = segs[p].A;
+        sg.B[p] = segs[p].B;
+        sg.out[p] = segs[p].out_p;
+        ntot += segs[p].out_p;
+    }
+    sg.nseg = nseg;
+    const int64_t nA = int64_t(nseg) * r * in_f, nB = int64_t(ntot) * nseg * r;
+    const int64_t n = nA + nB;
+    hipLaunchKernelGGL(k_lora_pack, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, sg, r, in_f, scale, Acat, Bbd,
+                       nA, nB, ntot);
+    check_launch("lora_pack");
+}
+
+// ------------------------------------------------------------------ attention softmax
+// scores [Z, S, S] (already scaled by 1/sqrt(hd)); P[i][j] = softmax over j <= i,
+// 0 for j > i. One wavefront per row; only j <= i is read.
+__global__ __launch_bounds__(256) void k_attn_softmax_fwd(const float* __restrict__ sc, int Z, int S,
+                                                          uint16_t* __restrict__ P) {
+    const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (row >= int64_t(Z) * S) return;
+    const int lane = threadIdx.x & 63;
+    const int i = int(row % S);
+    const float* s = sc + row * S;
+    float m = -INFINITY;
+    for (int j = lane; j <= i; j += 64) m = fmaxf(m, s[j]);
+    m = wave_max(m);
+    float sum = 0.f;
+    for (int j = lane; j <= i; j += 64) sum += expf(s[j] - m);
+    sum = wave_sum(sum);
+    uint16_t* p = P + row * S;
+    for (int j = lane; j < S; j += 64) p[j] = (j <= i) ? f32_to_bf16_bits(expf(s[j] - m) / sum) : uint16_t(0);
+}
+// dS = P * (dP - sum_j P dP), zeros above the diagonal.
+__global__ __launch_bounds__(256) void k_attn_softmax_bwd(const uint16_t* __restrict__ P, const float* __restrict__ dP,
+                                                          int Z, int S, uint16_t* __restrict__ dS) {
+    const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (row >= int64_t(Z) * S) return;
+    const int lane = threadIdx.x & 63;
+    const int i = int(row % S);
+    const uint16_t* p = P + row * S;
+    const float* d = dP + row * S;
+    float D = 0.f;
+    for (int j = lane; j <= i; j += 64) D += bf16_bits_to_f32(p[j]) * d[j];
+    D = wave_sum(D);
+    uint16_t* o = dS + row * S;
+    for (int j = lane; j < S; j += 64)
+        o[j] = (j <= i) ? f32_to_bf16_bits(bf16_bits_to_f32(p[j]) * (d[j] - D)) : uint16_t(0);
+}
+void launch_attn_softmax_fwd(const float* scores, int Z, int S, uint16_t* P, hipStream_t s) {
+    const int64_t rows = int64_t(Z) * S;
+    hipLaunchKernelGGL(k_attn_softmax_fwd, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, scores, Z, S, P);
+    check_launch("attn_softmax_fwd");
+}
+void launch_attn_softmax_bwd(const uint16_t* P, const float* dP, int Z, int S, uint16_t* dS, hipStream_t s) {
+    const int64_t rows = int64_t(Z) * S;
+    hipLaunchKernelGGL(k_attn_softmax_bwd, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, P, dP, Z, S, dS);
+    check_launch("attn_softmax_bwd");
+}
+
+// Per-query-head gradients dh [B*nH, S, hd] -> per-KV-head sums written as bf16
+// into out[(b*S + t)*ldo + col0 + kvh*hd + d]; group members summed in order.
+__global__ void k_gqa_reduce(const float* __restrict__ dh, int B, int nH, int nKV, int S, int hd,
+                             uint16_t* __restrict__ out, int64_t ldo, int col0) {
+    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t total = int64_t(B) * nKV * S * hd;
+    if (idx >= total) return;
+    const int d = int(idx % hd);
+    const int t = int((idx / hd) % S);
+    const int kvh = int((idx / (int64_t(hd) * S)) % nKV);
+    const int b = int(idx / (int64_t(hd) * S * nKV));
+    const int grp = nH / nKV;
+    float v = 0.f;
+    for (int g = 0; g < grp; ++g) v += dh[((int64_t(b) * nH + kvh * grp + g) * S + t) * hd + d];
+    out[(int64_t(b) * S + t) * ldo + col0 + kvh * hd + d] = f32_to_bf16_bits(v);
+}
+void launch_gqa_reduce(const float* dh, int B, int nH, int nKV, int S, int hd, uint16_t* out, int64_t ldo, int col0,
+                       hipStream_t s) {
+    const int64_t total = int64_t(B) * nKV * S * hd;
+    hipLaunchKernelGGL(k_gqa_reduce, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, dh, B, nH, nKV, S, hd, out,
+                       ldo, col0);
+    check_launch("gqa_reduce");
+}
+
+// ------------------------------------------------------------------ cross-entropy
+// Row t (position s = t % seq) has a target iff start <= s < seq-1; target = tokens[t+1].
+__device__ inline int row_target(const int32_t* tokens, int t, int seq, int start) {
+    const int s = t % seq;
+    if (s < start || s >= seq - 1) return -1;
+    return tokens[t + 1];
+}
+
+__global__ __launch_bounds__(256) void k_ce_stats(const float* __restrict__ z, int T, int V,
+                                                  const int32_t* __restrict__ tokens, int seq, int start,
+                                                  float* __restrict__ lse, float* __restrict__ picked) {
+    __shared__ float red[4];
+    const int t = blockIdx.x;
+    const int tgt = row_target(tokens, t, seq, start);
+    if (tgt < 0) {  // uniform across the workgroup
+        if (threadIdx.x == 0) {
+            lse[t] = 0.f;
+            picked[t] = 0.f;
+        }
+        return;
+    }
+    const float* zr = z + int64_t(t) * V;
+    float m = -INFINITY;
+    for (int j = threadIdx.x; j < V; j += 256) m = fmaxf(m, zr[j]);
+    m = block_max256(m, red);
+    float sum = 0.f;
+    for (int j = threadIdx.x; j < V; j += 256) sum += expf(zr[j] - m);
+    sum = block_sum256(sum, red);
+    if (threadIdx.x == 0) {
+        const bool ok = tgt < V;
+        lse[t] = ok ? m + logf(sum) : __int_as_float(0x7fc00000);
+        picked[t] = ok ? zr[tgt] : __int_as_float(0x7fc00000);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_ce_grad(const float* __restrict__ z, const float* __restrict__ lse, int T,
+                                                 int V, const int32_t* __restrict__ tokens, int seq, int start,
+                                                 int mode, float sc, const float* __restrict__ gseq,
+                                                 uint16_t* __restrict__ dz) {
+    const int t = blockIdx.y;
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= V) return;
+    const int tgt = row_target(tokens, t, seq, start);
+    uint16_t* o = dz + int64_t(t) * V;
+    if (tgt < 0) {
+        o[j] = 0;
+        return;
+    }
+    const float scale = (mode == 1) ? sc * gseq[t / seq] : sc;
+    const float p = expf(z[int64_t(t) * V + j] - lse[t]);
+    o[j] = f32_to_f16_bits((p - (j == tgt ? 1.f : 0.f)) * scale);
+}
+
+void launch_ce_stats(const float* logits, int T, int V, const int32_t* tokens, int seq, int start, float* lse,
+                     float* picked, hipStream_t s) {
+    hipLaunchKernelGGL(k_ce_stats, dim3(T), dim3(256), 0, s, logits, T, V, tokens, seq, start, lse, picked);
+    check_launch("ce_stats");
+}
+void launch_ce_grad(const float* logits, const float* lse, int T, int V, const int32_t* tokens, int seq, int start,
+                    int mode, float sc, const float* gseq, uint16_t* dz, hipStream_t s) {
+    hipLaunchKernelGGL(k_ce_grad, dim3((V + 255) / 256, T), dim3(256), 0, s, logits, lse, T, V, tokens, seq, start,
+                       mode, sc, gseq, dz);
+    check_launch("ce_grad");
+}
+
+// SFT loss = sum over target rows of (lse - picked) / (#rows with a target).
+__global__ __launch_bounds__(256) void k_sft_loss(const float* __restrict__ lse, const float* __restrict__ picked,
+                                                  int T, int seq, float* __restrict__ loss) {
+    __shared__ float red[4];
+    float acc = 0.f;
+    for (int t = threadIdx.x; t < T; t += 256) acc += lse[t] - picked[t];
+    acc = block_sum256(acc, red);
+    if (threadIdx.x == 0) {
+        const int nseq = T / seq;
+        loss[0] = acc / float(nseq * (seq - 1));
+    }
+}
+void launch_sft_loss(const float* lse, const float* picked, int T, int seq, float* loss, hipStream_t s) {
+    hipLaunchKernelGGL(k_sft_loss, dim3(1), dim3(256), 0, s, lse, picked, T, seq, loss);
+    check_launch("sft_loss");
+}
+
+// DPO (Rafailov et al. 2023, eq. 7). lp[b] = sum over response rows of
+// (picked - lse); Delta_i = (pol_c - ref_c) - (pol_r - ref_r);
+// loss = mean_i softplus(-beta Delta_i); gseq = dloss/dlp_pol.
+__global__ __launch_bounds__(256) void k_dpo_loss(const float* __restrict__ lse_p, const float* __restrict__ pk_p,
+                                                  const float* __restrict__ lse_r, const float* __restrict__ pk_r,
+                                                  int pairs, int seq, float beta, float* __restrict__ loss,
+                                                  float* __restrict__ logps, float* __restrict__ gseq) {
+    __shared__ float red[4];
+    __shared__ float lp[2][64];
+    const int nseq = 2 * pairs;
+    for (int b = 0; b < nseq; ++b) {
+        float a = 0.f, c = 0.f;
+        for (int s = threadIdx.x; s < seq; s += 256) {
+            const int64_t t = int64_t(b) * seq + s;
+            a += pk_p[t] - lse_p[t];
+            c += pk_r[t] - lse_r[t];
+        }
+        a = block_sum256(a, red);
+        c = block_sum256(c, red);
+        if (threadIdx.x == 0) {
+            lp[0][b] = a;
+            lp[1][b] = c;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double tot = 0.0;
+        for (int i = 0; i < pairs; ++i) {
+            const float delta = (lp[0][i] - lp[1][i]) - (lp[0][pairs + i] - lp[1][pairs + i]);
+            const double x = double(beta) * double(delta);
+            tot += (x >= 0.0) ? log1p(exp(-x)) : (-x + log1p(exp(x)));
+            const double g = -double(beta) / (1.0 + exp(x)) / double(pairs);
+            gseq[i] = float(g);
+            gseq[pairs + i] = float(-g);
+        }
+        loss[0] = float(tot / double(pairs));
+        for (int b = 0; b < nseq; ++b) {
+            logps[b] = lp[0][b];
+            logps[nseq + b] = lp[1][b];
+        }
+    }
+}
+void launch_dpo_loss(const float* lse_pol, const float* pk_pol, const float* lse_ref, const float* pk_ref, int pairs,
+                     int seq, int prompt_len, float beta, float* loss, float* logps, float* gseq, hipStream_t s) {
+    (void)prompt_len;
+    hipLaunchKernelGGL(k_dpo_loss, dim3(1), dim3(256), 0, s, lse_pol, pk_pol, lse_ref, pk_ref, pairs, seq, beta, loss,
+                       logps, gseq);
+    check_launch("dpo_loss");
+}
+
+}  // namespace qlx

@@ -1,0 +1,52 @@
+// Decoder-layer geometry, blob addressing, workspace and orchestration.
+#pragma once
+#include "qlx_internal.h"
+
+namespace qlx {
+
+struct LayerGeom {
+    int H, nH, nKV, hd, I, r;
+    float s, eps, theta;
+    int B, S, T;
+    int qdim, kvdim, nqkv;
+    int out[7], in[7];
+    int64_t nel[7];
+    bool hidden_ok() const { return H % 4 == 0 && qdim % 4 == 0 && I % 4 == 0 && kvdim % 4 == 0; }
+};
+
+struct BlobPtrs {
+    const uint8_t* packed[7];
+    const float* absmax[7];
+    const float* g1;
+    const float* g2;
+};
+
+// Every intermediate of one layer's forward and backward (bf16 activations,
+// fp32 residual-stream values, fp32 attention scores, LoRA staging, split-K
+// scratch). Carved from the caller's workspace.
+struct LayerWs {
+    uint16_t *n1, *qkv, *oattn, *n2, *gu, *act;
+    float *h1, *rstd1, *rstd2, *scores;
+    uint16_t* P;
+    uint16_t *u_qkv, *u_o, *u_gu, *u_d;
+    uint16_t *A_qkv, *B_qkv, *A_o, *B_o, *A_gu, *B_gu, *A_d, *B_d;
+    float* rope_cs;
+    float* partial;
+    uint16_t *dy16, *dact, *dgu, *doattn, *dqkv, *dS;
+    uint16_t *du_d, *du_gu, *du_o, *du_qkv;
+    float *dn2, *dh1, *dKh, *dVh, *dn1;
+};
+
+LayerGeom make_geom(const qlx_dims& d, int batch, int seq);
+void validate_dims(const qlx_dims* d);
+void blob_layout(const qlx_dims& d, uint64_t off[QLX_BLOB_NSEG], uint64_t* total);
+BlobPtrs blob_ptrs(const qlx_dims& d, const void* blob);
+LayerWs carve_layer(Carver& c, const LayerGeom& g);
+size_t layer_ws_bytes(const LayerGeom& g);
+void stage_lora(const LayerGeom& g, const qlx_lora* lora, LayerWs& w, hipStream_t s);
+void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora, bool lora_staged, const float* h_in,
+                   float* h_out, LayerWs& w, hipStream_t s);
+void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora, const float* h_in,
+                    const float* dh_out, float* dh_in, const qlx_lora_grad* grads, LayerWs& w, hipStream_t s);
+
+}  // namespace qlx

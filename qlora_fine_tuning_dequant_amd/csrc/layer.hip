@@ -1,0 +1,520 @@
+// Decoder-layer orchestration on one HIP stream: the Llama decoder layer with
+// a frozen NF4 base and LoRA adapters, forward and backward (the backward
+// recomputes the forward from the layer's input first).
+//
+// Pages: the frozen base is fed to the GPU one decoder layer at a time and
+// only the LoRA adapters train (rug.gal article, "En detalle";
+// guillermodelpino.com article, "El streaming de capas"); the layer is
+// Llama-3.1-8B's (all pages' intros), so: RMSNorm, q/k/v projections, RoPE,
+// causal grouped-query attention, o projection + residual, RMSNorm, SwiGLU
+// MLP + residual.
+//
+// Fusions: q|k|v is one NF4 GEMM over the concatenated rows (N = (nH+2nKV)hd),
+// gate|up likewise (N = 2I); each LoRA term rides in its base GEMM as a short
+// second K phase against block-diagonal staged adapters; residual adds happen
+// in the o/down GEMM epilogues; the backward dX GEMMs read the NF4 weight in
+// its stored [out][in] layout (no transposed copy) and fold the LoRA dX term
+// (du . A) in the same way.
+#include <algorithm>
+#include <cmath>
+
+#include "layer.h"
+
+namespace qlx {
+
+LayerGeom make_geom(const qlx_dims& d, int batch, int seq) {
+    LayerGeom g;
+    g.H = d.hidden;
+    g.nH = d.n_heads;
+    g.nKV = d.n_kv_heads;
+    g.hd = d.head_dim;
+    g.I = d.inter;
+    g.r = d.lora_r;
+    g.s = d.lora_alpha / float(d.lora_r);
+    g.eps = d.rms_eps;
+    g.theta = d.rope_theta;
+    g.B = batch;
+    g.S = seq;
+    g.T = batch * seq;
+    g.qdim = g.nH * g.hd;
+    g.kvdim = g.nKV * g.hd;
+    g.nqkv = g.qdim + 2 * g.kvdim;
+    const int outs[7] = {g.qdim, g.kvdim, g.kvdim, g.H, g.I, g.I, g.H};
+    const int ins[7] = {g.H, g.H, g.H, g.qdim, g.H, g.H, g.I};
+    for (int p = 0; p < 7; ++p) {
+        g.out[p] = outs[p];
+        g.in[p] = ins[p];
+        g.nel[p] = int64_t(outs[p]) * ins[p];
+    }
+    return g;
+}
+
+void validate_dims(const qlx_dims* d) {
+    QLX_REQUIRE(d, QLX_EINVAL, "dims is NULL");
+    QLX_REQUIRE(d->hidden > 0 && d->n_heads > 0 && d->n_kv_heads > 0 && d->head_dim > 0 && d->inter > 0 &&
+                    d->vocab > 0 && d->n_layers > 0 && d->lora_r > 0,
+                QLX_EINVAL, "dims: every size must be positive");
+    QLX_REQUIRE(d->n_heads % d->n_kv_heads == 0, QLX_EINVAL, "dims: n_heads must be a multiple of n_kv_heads");
+    QLX_REQUIRE(d->head_dim % 2 == 0, QLX_EINVAL, "dims: head_dim must be even (rotate-half RoPE)");
+    QLX_REQUIRE(d->lora_alpha == d->lora_alpha && d->rms_eps > 0 && d->rope_theta > 0, QLX_EINVAL,
+                "dims: lora_alpha, rms_eps, rope_theta must be finite and positive");
+    const LayerGeom g = make_geom(*d, 1, 1);
+    for (int p = 0; p < 7; ++p)
+        QLX_REQUIRE(g.nel[p] % 64 == 0, QLX_EUNSUPPORTED,
+                    "dims: every projection must hold a multiple of 64 elements (NF4 blocks may not straddle projections)");
+    QLX_REQUIRE(g.hidden_ok(), QLX_EUNSUPPORTED, "dims: hidden, heads*head_dim and inter must be multiples of 4");
+}
+
+void blob_layout(const qlx_dims& d, uint64_t off[QLX_BLOB_NSEG], uint64_t* total) {
+    const LayerGeom g = make_geom(d, 1, 1);
+    auto al = [](uint64_t x) { return (x + 255) & ~uint64_t(255); };
+    uint64_t o = 0;
+    for (int p = 0; p < 7; ++p) {
+        off[p] = o;
+        o += uint64_t(g.nel[p] / 2);  // packed regions back to back (each a multiple of 32 bytes)
+    }
+    o = al(o);
+    for (int p = 0; p < 7; ++p) {
+        off[7 + p] = o;
+        o += uint64_t(g.nel[p] / 64) * 4;
+    }
+    o = al(o);
+    off[14] = o;
+    o = al(o + uint64_t(g.H) * 4);
+    off[15] = o;
+    o = al(o + uint64_t(g.H) * 4);
+    *total = o;
+}
+
+BlobPtrs blob_ptrs(const qlx_dims& d, const void* blob) {
+    uint64_t off[QLX_BLOB_NSEG], total;
+    blob_layout(d, off, &total);
+    const char* b = static_cast<const char*>(blob);
+    BlobPtrs w;
+    for (int p = 0; p < 7; ++p) {
+        w.packed[p] = reinterpret_cast<const uint8_t*>(b + off[p]);
+        w.absmax[p] = reinterpret_cast<const float*>(b + off[7 + p]);
+    }
+    w.g1 = reinterpret_cast<const float*>(b + off[14]);
+    w.g2 = reinterpret_cast<const float*>(b + off[15]);
+    return w;
+}
+
+LayerWs carve_layer(Carver& c, const LayerGeom& g) {
+    LayerWs w;
+    const size_t T = size_t(g.T), H = size_t(g.H), r = size_t(g.r);
+    const size_t Z = size_t(g.B) * g.nH, SS = size_t(g.S) * g.S;
+    w.n1 = c.take<uint16_t>(T * H);
+    w.qkv = c.take<uint16_t>(T * g.nqkv);
+    w.oattn = c.take<uint16_t>(T * g.qdim);
+    w.n2 = c.take<uint16_t>(T * H);
+    w.gu = c.take<uint16_t>(T * 2 * g.I);
+    w.act = c.take<uint16_t>(T * g.I);
+    w.h1 = c.take<float>(T * H);
+    w.rstd1 = c.take<float>(T);
+    w.rstd2 = c.take<float>(T);
+    w.scores = c.take<float>(Z * SS);
+    w.P = c.take<uint16_t>(Z * SS);
+    w.u_qkv = c.take<uint16_t>(T * 3 * r);
+    w.u_o = c.take<uint16_t>(T * r);
+    w.u_gu = c.take<uint16_t>(T * 2 * r);
+    w.u_d = c.take<uint16_t>(T * r);
+    w.A_qkv = c.take<uint16_t>(3 * r * H);
+    w.B_qkv = c.take<uint16_t>(size_t(g.nqkv) * 3 * r);
+    w.A_o = c.take<uint16_t>(r * g.qdim);
+    w.B_o = c.take<uint16_t>(H * r);
+    w.A_gu = c.take<uint16_t>(2 * r * H);
+    w.B_gu = c.take<uint16_t>(size_t(2) * g.I * 2 * r);
+    w.A_d = c.take<uint16_t>(r * g.I);
+    w.B_d = c.take<uint16_t>(H * r);
+    w.rope_cs = c.take<float>(size_t(g.S) * g.hd);
+    w.partial = c.take<float>(kGemmPartialFloats);
+    // backward
+    w.dy16 = c.take<uint16_t>(T * std::max(H, size_t(g.qdim)));
+    w.dact = c.take<uint16_t>(T * g.I);
+    w.dgu = c.take<uint16_t>(T * 2 * g.I);
+    w.doattn = c.take<uint16_t>(T * g.qdim);
+    w.dqkv = c.take<uint16_t>(T * g.nqkv);
+    w.dS = c.take<uint16_t>(Z * SS);
+    w.du_d = c.take<uint16_t>(T * r);
+    w.du_gu = c.take<uint16_t>(T * 2 * r);
+    w.du_o = c.take<uint16_t>(T * r);
+    w.du_qkv = c.take<uint16_t>(T * 3 * r);
+    w.dn2 = c.take<float>(T * H);
+    w.dh1 = c.take<float>(T * H);
+    w.dKh = c.take<float>(Z * g.S * g.hd);
+    w.dVh = c.take<float>(Z * g.S * g.hd);
+    w.dn1 = c.take<float>(T * H);
+    return w;
+}
+
+size_t layer_ws_bytes(const LayerGeom& g) {
+    Carver c(nullptr);
+    carve_layer(c, g);
+    return c.size();
+}
+
+// ---------------------------------------------------------------- helpers
+static GemmParams nf4_gemm(int M, int N, int K, const uint16_t* A, int64_t lda, const uint8_t* packed,
+                           const float* absmax, int64_t cols) {
+    GemmParams p;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.A = A;
+    p.lda = lda;
+    p.B = packed;
+    p.absmax = absmax;
+    p.nf4_cols = cols;
+    return p;
+}
+static GemmParams dense_gemm(int M, int N, int K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb) {
+    GemmParams p;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.A = A;
+    p.lda = lda;
+    p.B = B;
+    p.ldb = ldb;
+    return p;
+}
+static void out_bf16(GemmParams& p, uint16_t* C, int64_t ldc) {
+    p.C = C;
+    p.ldc = ldc;
+    p.c_type = C_BF16;
+}
+static void out_f32(GemmParams& p, float* C, int64_t ldc) {
+    p.C = C;
+    p.ldc = ldc;
+    p.c_type = C_F32;
+}
+
+void stage_lora(const LayerGeom& g, const qlx_lora* lora, LayerWs& w, hipStream_t s) {
+    const int r = g.r;
+    LoraSeg qkv[3] = {{lora->A[0], lora->B[0], g.qdim}, {lora->A[1], lora->B[1], g.kvdim},
+                      {lora->A[2], lora->B[2], g.kvdim}};
+    launch_lora_pack(qkv, 3, r, g.H, g.s, w.A_qkv, w.B_qkv, s);
+    LoraSeg o[1] = {{lora->A[3], lora->B[3], g.H}};
+    launch_lora_pack(o, 1, r, g.qdim, g.s, w.A_o, w.B_o, s);
+    LoraSeg gu[2] = {{lora->A[4], lora->B[4], g.I}, {lora->A[5], lora->B[5], g.I}};
+    launch_lora_pack(gu, 2, r, g.H, g.s, w.A_gu, w.B_gu, s);
+    LoraSeg dn[1] = {{lora->A[6], lora->B[6], g.H}};
+    launch_lora_pack(dn, 1, r, g.I, g.s, w.A_d, w.B_d, s);
+}
+
+// Forward. h_out == nullptr skips the down projection (the backward does not
+// need the layer output). lora_staged: adapters already staged in w.
+void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora, bool lora_staged, const float* h_in,
+                   float* h_out, LayerWs& w, hipStream_t s) {
+    const int T = g.T, H = g.H, r = g.r;
+    const bool L = lora != nullptr;
+    if (L && !lora_staged) stage_lora(g, lora, w, s);
+    launch_rope_table(g.S, g.hd, g.theta, w.rope_cs, s);
+
+    // attention block
+    launch_rmsnorm_fwd(h_in, wt.g1, T, H, g.eps, w.n1, 0, w.rstd1, s);
+    if (L) {
+        GemmParams pu = dense_gemm(T, 3 * r, H, w.n1, H, w.A_qkv, H);
+        out_bf16(pu, w.u_qkv, 3 * r);
+        gemm(pu, A_ROW, B_DENSE_NT, TE_BF16, w.partial, s);
+    }
+    {
+        GemmParams p = nf4_gemm(T, g.nqkv, H, w.n1, H, wt.packed[0], wt.absmax[0], H);
+        if (L) {
+            p.K2 = 3 * r;
+            p.A2 = w.u_qkv;
+            p.lda2 = 3 * r;
+            p.B2 = w.B_qkv;
+            p.ldb2 = 3 * r;
+        }
+        out_bf16(p, w.qkv, g.nqkv);
+        gemm(p, A_ROW, B_NF4_NT, TE_BF16, w.partial, s);
+    }
+    launch_rope(w.qkv, g.nqkv, T, g.S, 0, g.nH, g.hd, w.rope_cs, 0, s);
+    launch_rope(w.qkv, g.nqkv, T, g.S, g.qdim, g.nKV, g.hd, w.rope_cs, 0, s);
+    const int S = g.S, grp = g.nH / g.nKV;
+    const float scale = 1.0f / sqrtf(float(g.hd));
+    {  // scores = scale * q k^T, causal tiles only
+        GemmParams p = dense_gemm(S, S, g.hd, w.qkv, g.nqkv, w.qkv + g.qdim, g.nqkv);
+        p.batch = g.B * g.nH;
+        p.zdiv = g.nH;
+        p.a_so = int64_t(S) * g.nqkv;
+        p.a_si = g.hd;
+        p.b_so = int64_t(S) * g.nqkv;
+        p.b_si = g.hd;
+        p.b_grp = grp;
+        out_f32(p, w.scores, S);
+        p.c_so = int64_t(g.nH) * S * S;
+        p.c_si = int64_t(S) * S;
+        p.alpha = scale;
+        p.causal = CAUSAL_SKIP_UPPER;
+        gemm(p, A_ROW, B_DENSE_NT, TE_BF16, nullptr, s);
+    }
+    launch_attn_softmax_fwd(w.scores, g.B * g.nH, S, w.P, s);
+    {  // o = P v
+        GemmParams p = dense_gemm(S, g.hd, S, w.P, S, w.qkv + g.qdim + g.kvdim, g.nqkv);
+        p.batch = g.B * g.nH;
+        p.zdiv = g.nH;
+        p.a_so = int64_t(g.nH) * S * S;
+        p.a_si = int64_t(S) * S;
+        p.b_so = int64_t(S) * g.nqkv;
+        p.b_si = g.hd;
+        p.b_grp = grp;
+        out_bf16(p, w.oattn, g.qdim);
+        p.c_so = int64_t(S) * g.qdim;
+        p.c_si = g.hd;
+        p.causal = CAUSAL_K_LE_M;
+        gemm(p, A_ROW, B_DENSE_NN, TE_BF16, nullptr, s);
+    }
+    if (L) {
+        GemmParams pu = dense_gemm(T, r, g.qdim, w.oattn, g.qdim, w.A_o, g.qdim);
+        out_bf16(pu, w.u_o, r);
+        gemm(pu, A_ROW, B_DENSE_NT, TE_BF16, w.partial, s);
+    }
+    {  // h1 = h_in + o_proj(o)
+        GemmParams p = nf4_gemm(T, H, g.qdim, w.oattn, g.qdim, wt.packed[3], wt.absmax[3], g.qdim);
+        if (L) {
+            p.K2 = r;
+            p.A2 = w.u_o;
+            p.lda2 = r;
+            p.B2 = w.B_o;
+            p.ldb2 = r;
+        }
+        out_f32(p, w.h1, H);
+        p.R = h_in;
+        p.ldr = H;
+        gemm(p, A_ROW, B_NF4_NT, TE_BF16, w.partial, s);
+    }
+    // MLP block
+    launch_rmsnorm_fwd(w.h1, wt.g2, T, H, g.eps, w.n2, 0, w.rstd2, s);
+    if (L) {
+        GemmParams pu = dense_gemm(T, 2 * r, H, w.n2, H, w.A_gu, H);
+        out_bf16(pu, w.u_gu, 2 * r);
+        gemm(pu, A_ROW, B_DENSE_NT, TE_BF16, w.partial, s);
+    }
+    {
+        GemmParams p = nf4_gemm(T, 2 * g.I, H, w.n2, H, wt.packed[4], wt.absmax[4], H);
+        if (L) {
+            p.K2 = 2 * r;
+            p.A2 = w.u_gu;
+            p.lda2 = 2 * r;
+            p.B2 = w.B_gu;
+            p.ldb2 = 2 * r;
+        }
+        out_bf16(p, w.gu, 2 * g.I);
+        gemm(p, A_ROW, B_NF4_NT, TE_BF16, w.partial, s);
+    }
+    launch_swiglu_fwd(w.gu, T, g.I, w.act, s);
+    if (L) {
+        GemmParams pu = dense_gemm(T, r, g.I, w.act, g.I, w.A_d, g.I);
+        out_bf16(pu, w.u_d, r);
+        gemm(pu, A_ROW, B_DENSE_NT, TE_BF16, w.partial, s);
+    }
+    if (h_out) {
+        GemmParams p = nf4_gemm(T, H, g.I, w.act, g.I, wt.packed[6], wt.absmax[6], g.I);
+        if (L) {
+            p.K2 = r;
+            p.A2 = w.u_d;
+            p.lda2 = r;
+            p.B2 = w.B_d;
+            p.ldb2 = r;
+        }
+        out_f32(p, h_out, H);
+        p.R = w.h1;
+        p.ldr = H;
+        gemm(p, A_ROW, B_NF4_NT, TE_BF16, w.partial, s);
+    }
+}
+
+// dB = s * dy^T u  (M = out, N = r, K = T): dy [T, ld_dy] column slice, u [T, ld_u] slice.
+static void grad_B(const LayerGeom& g, const uint16_t* dy, int64_t ld_dy, int out, const uint16_t* u, int64_t ld_u,
+                   float* dB, LayerWs& w, hipStream_t s) {
+    GemmParams p = dense_gemm(out, g.r, g.T, dy, ld_dy, u, ld_u);
+    out_f32(p, dB, g.r);
+    p.alpha = g.s;
+    gemm(p, A_TRANS, B_DENSE_NN, TE_BF16, w.partial, s);
+}
+// dA (stacked over nseg segments of r rows) = du^T x  (M = nseg*r, N = in, K = T).
+static void grad_A(const LayerGeom& g, const uint16_t* du, int nseg, const uint16_t* x, int in_f, float* const* dA,
+                   LayerWs& w, hipStream_t s) {
+    GemmParams p = dense_gemm(nseg * g.r, in_f, g.T, du, int64_t(nseg) * g.r, x, in_f);
+    p.c_type = C_F32;
+    p.ldc = in_f;
+    p.seg_rows = g.r;
+    for (int i = 0; i < nseg; ++i) p.Cseg[i] = dA[i];
+    p.C = dA[0];
+    gemm(p, A_TRANS, B_DENSE_NN, TE_BF16, w.partial, s);
+}
+
+void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora, const float* h_in,
+                    const float* dh_out, float* dh_in, const qlx_lora_grad* grads, LayerWs& w, hipStream_t s) {
+    const int T = g.T, H = g.H, r = g.r, S = g.S, grp = g.nH / g.nKV;
+    const float scale = 1.0f / sqrtf(float(g.hd));
+    layer_forward(g, wt, lora, false, h_in, nullptr, w, s);
+
+    // ---- down projection: out = h1 + down(act)
+    launch_f32_to_bf16(dh_out, int64_t(T) * H, w.dy16, s);
+    {
+        GemmParams p = dense_gemm(T, r, H, w.dy16, H, w.B_d, r);
+        out_bf16(p, w.du_d, r);
+        gemm(p, A_ROW, B_DENSE_NN, TE_BF16, w.partial, s);
+    }
+    {
+        GemmParams p = nf4_gemm(T, g.I, H, w.dy16, H, wt.packed[6], wt.absmax[6], g.I);
+        p.K2 = r;
+        p.A2 = w.du_d;
+        p.lda2 = r;
+        p.B2 = w.A_d;
+        p.ldb2 = g.I;
+        out_bf16(p, w.dact, g.I);
+        gemm(p, A_ROW, B_NF4_NN, TE_BF16, w.partial, s);
+    }
+    grad_B(g, w.dy16, H, H, w.u_d, r, grads->dB[6], w, s);
+    {
+        float* dA[1] = {grads->dA[6]};
+        grad_A(g, w.du_d, 1, w.act, g.I, dA, w, s);
+    }
+    // ---- SwiGLU and gate/up
+    launch_swiglu_bwd(w.dact, w.gu, T, g.I, w.dgu, s);
+    {
+        GemmParams p = dense_gemm(T, 2 * r, 2 * g.I, w.dgu, 2 * g.I, w.B_gu, 2 * r);
+        out_bf16(p, w.du_gu, 2 * r);
+        gemm(p, A_ROW, B_DENSE_NN, TE_BF16, w.partial, s);
+    }
+    {
+        GemmParams p = nf4_gemm(T, H, 2 * g.I, w.dgu, 2 * g.I, wt.packed[4], wt.absmax[4], H);
+        p.K2 = 2 * r;
+        p.A2 = w.du_gu;
+        p.lda2 = 2 * r;
+        p.B2 = w.A_gu;
+        p.ldb2 = H;
+        out_f32(p, w.dn2, H);
+        gemm(p, A_ROW, B_NF4_NN, TE_BF16, w.partial, s);
+    }
+    grad_B(g, w.dgu, 2 * g.I, g.I, w.u_gu, 2 * r, grads->dB[4], w, s);
+    grad_B(g, w.dgu + g.I, 2 * g.I, g.I, w.u_gu + r, 2 * r, grads->dB[5], w, s);
+    {
+        float* dA[2] = {grads->dA[4], grads->dA[5]};
+        grad_A(g, w.du_gu, 2, w.n2, H, dA, w, s);
+    }
+    launch_rmsnorm_bwd(w.dn2, w.h1, wt.g2, w.rstd2, dh_out, T, H, w.dh1, s);
+
+    // ---- o projection: h1 = h + o(oattn)
+    launch_f32_to_bf16(w.dh1, int64_t(T) * H, w.dy16, s);
+    {
+        GemmParams p = dense_gemm(T, r, H, w.dy16, H, w.B_o, r);
+        out_bf16(p, w.du_o, r);
+        gemm(p, A_ROW, B_DENSE_NN, TE_BF16, w.partial, s);
+    }
+    {
+        GemmParams p = nf4_gemm(T, g.qdim, H, w.dy16, H, wt.packed[3], wt.absmax[3], g.qdim);
+        p.K2 = r;
+        p.A2 = w.du_o;
+        p.lda2 = r;
+        p.B2 = w.A_o;
+        p.ldb2 = g.qdim;
+        out_bf16(p, w.doattn, g.qdim);
+        gemm(p, A_ROW, B_NF4_NN, TE_BF16, w.partial, s);
+    }
+    grad_B(g, w.dy16, H, H, w.u_o, r, grads->dB[3], w, s);
+    {
+        float* dA[1] = {grads->dA[3]};
+        grad_A(g, w.du_o, 1, w.oattn, g.qdim, dA, w, s);
+    }
+
+    // ---- attention
+    const int Z = g.B * g.nH;
+    {  // dV_h = P^T dO (keys >= ... causal: query >= key)
+        GemmParams p = dense_gemm(S, g.hd, S, w.P, S, w.doattn, g.qdim);
+        p.batch = Z;
+        p.zdiv = g.nH;
+        p.a_so = int64_t(g.nH) * S * S;
+        p.a_si = int64_t(S) * S;
+        p.b_so = int64_t(S) * g.qdim;
+        p.b_si = g.hd;
+        out_f32(p, w.dVh, g.hd);
+        p.c_so = int64_t(g.nH) * S * g.hd;
+        p.c_si = int64_t(S) * g.hd;
+        p.causal = CAUSAL_K_GE_M;
+        gemm(p, A_TRANS, B_DENSE_NN, TE_BF16, nullptr, s);
+    }
+    {  // dP = dO v^T (into the scores buffer)
+        GemmParams p = dense_gemm(S, S, g.hd, w.doattn, g.qdim, w.qkv + g.qdim + g.kvdim, g.nqkv);
+        p.batch = Z;
+        p.zdiv = g.nH;
+        p.a_so = int64_t(S) * g.qdim;
+        p.a_si = g.hd;
+        p.b_so = int64_t(S) * g.nqkv;
+        p.b_si = g.hd;
+        p.b_grp = grp;
+        out_f32(p, w.scores, S);
+        p.c_so = int64_t(g.nH) * S * S;
+        p.c_si = int64_t(S) * S;
+        p.causal = CAUSAL_SKIP_UPPER;
+        gemm(p, A_ROW, B_DENSE_NT, TE_BF16, nullptr, s);
+    }
+    launch_attn_softmax_bwd(w.P, w.scores, Z, S, w.dS, s);
+    {  // dq = scale dS k  -> dqkv q columns
+        GemmParams p = dense_gemm(S, g.hd, S, w.dS, S, w.qkv + g.qdim, g.nqkv);
+        p.batch = Z;
+        p.zdiv = g.nH;
+        p.a_so = int64_t(g.nH) * S * S;
+        p.a_si = int64_t(S) * S;
+        p.b_so = int64_t(S) * g.nqkv;
+        p.b_si = g.hd;
+        p.b_grp = grp;
+        out_bf16(p, w.dqkv, g.nqkv);
+        p.c_so = int64_t(S) * g.nqkv;
+        p.c_si = g.hd;
+        p.alpha = scale;
+        p.causal = CAUSAL_K_LE_M;
+        gemm(p, A_ROW, B_DENSE_NN, TE_BF16, nullptr, s);
+    }
+    {  // dK_h = scale dS^T q
+        GemmParams p = dense_gemm(S, g.hd, S, w.dS, S, w.qkv, g.nqkv);
+        p.batch = Z;
+        p.zdiv = g.nH;
+        p.a_so = int64_t(g.nH) * S * S;
+        p.a_si = int64_t(S) * S;
+        p.b_so = int64_t(S) * g.nqkv;
+        p.b_si = g.hd;
+        out_f32(p, w.dKh, g.hd);
+        p.c_so = int64_t(g.nH) * S * g.hd;
+        p.c_si = int64_t(S) * g.hd;
+        p.alpha = scale;
+        p.causal = CAUSAL_K_GE_M;
+        gemm(p, A_TRANS, B_DENSE_NN, TE_BF16, nullptr, s);
+    }
+    launch_gqa_reduce(w.dKh, g.B, g.nH, g.nKV, S, g.hd, w.dqkv, g.nqkv, g.qdim, s);
+    launch_gqa_reduce(w.dVh, g.B, g.nH, g.nKV, S, g.hd, w.dqkv, g.nqkv, g.qdim + g.kvdim, s);
+    launch_rope(w.dqkv, g.nqkv, T, S, 0, g.nH, g.hd, w.rope_cs, 1, s);
+    launch_rope(w.dqkv, g.nqkv, T, S, g.qdim, g.nKV, g.hd, w.rope_cs, 1, s);
+
+    // ---- q/k/v projections
+    {
+        GemmParams p = dense_gemm(T, 3 * r, g.nqkv, w.dqkv, g.nqkv, w.B_qkv, 3 * r);
+        out_bf16(p, w.du_qkv, 3 * r);
+        gemm(p, A_ROW, B_DENSE_NN, TE_BF16, w.partial, s);
+    }
+    if (dh_in) {
+        GemmParams p = nf4_gemm(T, H, g.nqkv, w.dqkv, g.nqkv, wt.packed[0], wt.absmax[0], H);
+        p.K2 = 3 * r;
+        p.A2 = w.du_qkv;
+        p.lda2 = 3 * r;
+        p.B2 = w.A_qkv;
+        p.ldb2 = H;
+        out_f32(p, w.dn1, H);
+        gemm(p, A_ROW, B_NF4_NN, TE_BF16, w.partial, s);
+        launch_rmsnorm_bwd(w.dn1, h_in, wt.g1, w.rstd1, w.dh1, T, H, dh_in, s);
+    }
+    grad_B(g, w.dqkv, g.nqkv, g.qdim, w.u_qkv, 3 * r, grads->dB[0], w, s);
+    grad_B(g, w.dqkv + g.qdim, g.nqkv, g.kvdim, w.u_qkv + r, 3 * r, grads->dB[1], w, s);
+    grad_B(g, w.dqkv + g.qdim + g.kvdim, g.nqkv, g.kvdim, w.u_qkv + 2 * r, 3 * r, grads->dB[2], w, s);
+    {
+        float* dA[3] = {grads->dA[0], grads->dA[1], grads->dA[2]};
+        grad_A(g, w.du_qkv, 3, w.n1, H, dA, w, s);
+    }
+}
+
+}  // namespace qlx

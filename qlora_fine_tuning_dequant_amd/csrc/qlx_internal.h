@@ -1,0 +1,140 @@
+// Internal interfaces of libqlx (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "qlx.h"
+
+namespace qlx {
+
+// ---------------------------------------------------------------- errors
+void set_error(const std::string& msg);
+struct Error {
+    int code;
+    std::string msg;
+};
+#define QLX_CHECK_HIP(expr)                                                          \
+    do {                                                                             \
+        hipError_t e_ = (expr);                                                      \
+        if (e_ != hipSuccess)                                                        \
+            throw ::qlx::Error{QLX_EHIP, std::string(#expr) + ": " + hipGetErrorString(e_)}; \
+    } while (0)
+#define QLX_REQUIRE(cond, code, msg)                                                 \
+    do {                                                                             \
+        if (!(cond)) throw ::qlx::Error{(code), (msg)};                              \
+    } while (0)
+void check_launch(const char* what);
+
+// ---------------------------------------------------------- workspace carving
+// Hands out 256-byte aligned sub-buffers of a caller workspace. With a null
+// base it only measures (every take() returns nullptr and bumps the size).
+struct Carver {
+    char* base;
+    size_t off = 0;
+    explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+    template <typename T>
+    T* take(size_t count) {
+        off = (off + 255) & ~size_t(255);
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off += count * sizeof(T);
+        return p;
+    }
+    size_t size() const { return (off + 255) & ~size_t(255); }
+};
+
+// ---------------------------------------------------------------- NF4
+void launch_nf4_quantize(const uint16_t* w, int64_t n, uint8_t* packed, float* absmax, hipStream_t s);
+void launch_nf4_dequant(const uint8_t* packed, const float* absmax, int64_t n, int out_dtype, void* out,
+                        hipStream_t s);
+
+// ---------------------------------------------------------------- GEMM
+// C[M,N] = alpha * (A . op(B) [+ A2 . op(B2)]) [+ R] [+ C_old], fp32 accumulation.
+// Element types: bf16 (TE_BF16) or fp16 (TE_F16) for A and dense B.
+enum AKind { A_ROW = 0, A_TRANS = 1 };  // A_ROW: A[m*lda+k]; A_TRANS: A[k*lda+m]
+enum BKind { B_NF4_NT = 0, B_NF4_NN = 1, B_DENSE_NT = 2, B_DENSE_NN = 3 };
+// B_*_NT: stored [N][K] (element (n,k) at n*ldb+k, NF4: flat n*nf4_cols+k)
+// B_*_NN: stored [K][N] (element (n,k) at k*ldb+n, NF4: flat k*nf4_cols+n)
+enum TElem { TE_BF16 = 0, TE_F16 = 1 };
+enum CType { C_F32 = 0, C_BF16 = 1, C_F16 = 2 };
+enum Causal { CAUSAL_NONE = 0, CAUSAL_SKIP_UPPER = 1, CAUSAL_K_LE_M = 2, CAUSAL_K_GE_M = 3 };
+
+struct GemmParams {
+    int M = 0, N = 0, K = 0;
+    const uint16_t* A = nullptr;
+    int64_t lda = 0;
+    const void* B = nullptr;  // dense: uint16 elements; NF4: packed bytes
+    int64_t ldb = 0;
+    const float* absmax = nullptr;  // NF4 only
+    int64_t nf4_cols = 0;           // NF4: row length of the stored matrix
+    // second K phase ("slab"): A2 [M, K2] row-major, B2 dense with the
+    // orientation of B (NT for B_NF4_NT, NN for B_NF4_NN)
+    int K2 = 0;
+    const uint16_t* A2 = nullptr;
+    int64_t lda2 = 0;
+    const uint16_t* B2 = nullptr;
+    int64_t ldb2 = 0;
+    // batching over grid.z: z -> (bo = z / zdiv, bi = z % zdiv)
+    int batch = 1, zdiv = 1, a_grp = 1, b_grp = 1;
+    int64_t a_so = 0, a_si = 0, b_so = 0, b_si = 0, c_so = 0, c_si = 0;
+    // split-K (chosen by the launcher; shapes only)
+    int splits = 1, kchunk = 0;
+    float* partial = nullptr;
+    // epilogue
+    void* C = nullptr;
+    int64_t ldc = 0;
+    int c_type = C_F32;
+    float alpha = 1.f;
+    const float* R = nullptr;  // residual added after alpha (fp32, ldr), no batching
+    int64_t ldr = 0;
+    int accumulate = 0;        // C (fp32) += result
+    int seg_rows = 0;          // >0: row m goes to Cseg[m / seg_rows] row m % seg_rows
+    void* Cseg[4] = {nullptr, nullptr, nullptr, nullptr};
+    int causal = CAUSAL_NONE;
+    // set by the launcher
+    int a_vec = 0, b_vec = 0, a2_vec = 0, b2_vec = 0;
+};
+
+// Floats of split-K scratch the launcher may use for any one GEMM.
+constexpr size_t kGemmPartialFloats = size_t(1024) * 128 * 128;
+void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStream_t s);
+
+// ---------------------------------------------------------------- elementwise
+void launch_rmsnorm_fwd(const float* x, const float* g, int T, int H, float eps, void* out, int out_f16,
+                        float* rstd, hipStream_t s);
+void launch_rmsnorm_bwd(const float* dy, const float* x, const float* g, const float* rstd, const float* dres,
+                        int T, int H, float* dx, hipStream_t s);
+void launch_rope_table(int seq, int hd, float theta, float* cs, hipStream_t s);
+void launch_rope(uint16_t* buf, int64_t ld, int T, int seq, int col0, int nheads, int hd, const float* cs,
+                 int inverse, hipStream_t s);
+void launch_swiglu_fwd(const uint16_t* gu, int T, int I, uint16_t* act, hipStream_t s);
+void launch_swiglu_bwd(const uint16_t* dact, const uint16_t* gu, int T, int I, uint16_t* dgu, hipStream_t s);
+void launch_embed(const int32_t* tok, const uint16_t* E, int T, int H, int V, float* h, hipStream_t s);
+void launch_f32_to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s);
+struct LoraSeg {
+    const float* A;  // [r, in]
+    const float* B;  // [out_p, r]
+    int out_p;
+};
+void launch_lora_pack(const LoraSeg* segs, int nseg, int r, int in_f, float scale, uint16_t* Acat,
+                      uint16_t* Bbd, hipStream_t s);
+void launch_attn_softmax_fwd(const float* scores, int Z, int S, uint16_t* P, hipStream_t s);
+void launch_attn_softmax_bwd(const uint16_t* P, const float* dP, int Z, int S, uint16_t* dS, hipStream_t s);
+void launch_gqa_reduce(const float* dh, int B, int nH, int nKV, int S, int hd, uint16_t* out, int64_t ldo,
+                       int col0, hipStream_t s);
+// Cross-entropy pieces over logits [T, V] (fp32).
+// target[t] < 0 marks a row with no loss. lse[t], picked[t] = z[t, target].
+void launch_ce_stats(const float* logits, int T, int V, const int32_t* tokens, int seq, int prompt_len,
+                     float* lse, float* picked, hipStream_t s);
+// dz[t, j] = f16((softmax_j - [j == target]) * rowscale[t]); rows without a target -> 0.
+// rowscale: mode 0 = scalar `sc`; mode 1 = sc * gseq[t / seq]
+void launch_ce_grad(const float* logits, const float* lse, int T, int V, const int32_t* tokens, int seq,
+                    int prompt_len, int mode, float sc, const float* gseq, uint16_t* dz, hipStream_t s);
+void launch_sft_loss(const float* lse, const float* picked, int T, int seq, float* loss, hipStream_t s);
+void launch_dpo_loss(const float* lse_pol, const float* pk_pol, const float* lse_ref, const float* pk_ref,
+                     int pairs, int seq, int prompt_len, float beta, float* loss, float* logps, float* gseq,
+                     hipStream_t s);
+
+}  // namespace qlx

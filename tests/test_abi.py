@@ -1,0 +1,111 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point the
+header declares, and rejects bad arguments before touching the GPU."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import qlora_fine_tuning_dequant_amd as q
+from qlora_fine_tuning_dequant_amd import binding as b
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qlx.h")
+
+
+def _declared():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while", "sizeof")))
+
+
+def test_library_exports_every_declared_symbol():
+    L = b.lib()
+    declared = _declared()
+    assert {"nf4_quantize", "nf4_dequant", "qlora_linear_fwd", "qlora_linear_bwd", "layer_fwd", "layer_bwd",
+            "stream_step_sft", "stream_step_dpo"} <= set(declared)
+    for n in declared:
+        assert hasattr(L, n), n
+    assert set(b.EXPORTED) == set(declared)
+
+
+def test_version_and_error_codes():
+    L = b.lib()
+    assert L.qlx_version().startswith(b"qlx")
+    assert L.nf4_quantize(None, -1, 4, None, None, None) == b.QLX_EINVAL
+    assert b"negative" in L.qlx_last_error()
+    assert L.nf4_quantize(None, 0, 4, None, None, None) == b.QLX_OK  # empty input is a no-op
+    assert L.nf4_dequant(None, None, 2, 2, 7, None, None) == b.QLX_EINVAL
+
+
+def _dims(**kw):
+    base = dict(hidden=256, n_heads=4, n_kv_heads=2, head_dim=64, inter=688, vocab=1024, n_layers=2, lora_r=8,
+                lora_alpha=16.0, rms_eps=1e-5, rope_theta=5e5)
+    base.update(kw)
+    return b.Dims(**base)
+
+
+def test_blob_layout_is_aligned_and_complete():
+    for d in (_dims(), _dims(hidden=4096, n_heads=32, n_kv_heads=8, head_dim=128, inter=14336, vocab=128256,
+                             n_layers=32, lora_r=64)):
+        offs, total = b.blob_layout(d)
+        H, I, q_, kv = d.hidden, d.inter, d.n_heads * d.head_dim, d.n_kv_heads * d.head_dim
+        nel = [q_ * H, kv * H, kv * H, H * q_, I * H, I * H, H * I]
+        # packed regions back to back, then absmax back to back
+        for p in range(6):
+            assert offs[p + 1] - offs[p] == nel[p] // 2
+            assert offs[8 + p] - offs[7 + p] == nel[p] // 64 * 4
+        assert offs[7] % 256 == 0 and offs[14] % 256 == 0 and offs[15] % 256 == 0 and total % 256 == 0
+        assert offs[7] >= offs[6] + nel[6] // 2 and offs[14] >= offs[13] + nel[6] // 16
+        assert total >= offs[15] + 4 * H
+    big = b.blob_layout(_dims(hidden=4096, n_heads=32, n_kv_heads=8, head_dim=128, inter=14336, vocab=128256,
+                              n_layers=32, lora_r=64))[1]
+    # 218,103,808 NF4 weights: 4 bits each + one fp32 absmax per 64, plus two fp32 gains
+    assert big == 218103808 // 2 + 218103808 // 16 + 2 * 4096 * 4
+
+
+def test_dims_validation():
+    offs = (C.c_uint64 * 16)()
+    tot = C.c_uint64()
+    L = b.lib()
+    assert L.qlx_layer_blob_layout(C.byref(_dims(n_heads=3)), offs, C.byref(tot)) == b.QLX_EINVAL
+    assert L.qlx_layer_blob_layout(C.byref(_dims(head_dim=63)), offs, C.byref(tot)) == b.QLX_EINVAL
+    # 10 x 10 projections cannot be cut into whole 64-element blocks
+    assert L.qlx_layer_blob_layout(C.byref(_dims(hidden=10, n_heads=2, n_kv_heads=1, head_dim=4, inter=12)), offs,
+                                   C.byref(tot)) == b.QLX_EUNSUPPORTED
+    assert L.qlx_layer_blob_layout(None, offs, C.byref(tot)) == b.QLX_EINVAL
+
+
+def test_linear_and_layer_argument_checks_run_before_any_launch():
+    L = b.lib()
+    W = b.NF4(None, None, 16, 16)
+    assert L.qlora_linear_fwd(None, 4, W, None, None, 0, 1.0, None, None, 0, None) == b.QLX_EINVAL
+    W = b.NF4(256, 512, 16, 16)  # fake but aligned addresses; nothing is launched
+    assert L.qlora_linear_fwd(1024, 4, W, 2048, None, 4, 1.0, 4096, None, 0, None) == b.QLX_EINVAL  # A without B
+    need = L.qlx_linear_workspace_bytes(4, 16, 16, 4)
+    assert need > 0
+    assert L.qlora_linear_fwd(1024, 4, W, 2048, 3072, 4, 1.0, 4096, 8192, need - 1, None) == b.QLX_EWORKSPACE
+    d = _dims()
+    need = L.qlx_layer_workspace_bytes(C.byref(d), 1, 64)
+    assert L.layer_fwd(C.byref(d), 256, None, 512, 1, 64, 1024, 4096, need - 256, None) == b.QLX_EWORKSPACE
+    assert L.layer_fwd(C.byref(d), 256, None, 512, 0, 64, 1024, 4096, need, None) == b.QLX_EINVAL
+    assert L.layer_bwd(C.byref(d), 256, None, 512, 512, 1, 64, None, None, 4096, need, None) == b.QLX_EINVAL
+
+
+def test_workspace_sizes_scale_with_tokens():
+    L = b.lib()
+    d = _dims()
+    w1 = L.qlx_layer_workspace_bytes(C.byref(d), 1, 64)
+    w2 = L.qlx_layer_workspace_bytes(C.byref(d), 2, 64)
+    assert 0 < w1 < w2
+    s1 = L.qlx_step_workspace_bytes(C.byref(d), 0, 1, 64)
+    s_dpo = L.qlx_step_workspace_bytes(C.byref(d), 1, 1, 64)
+    assert s1 > w1 and s_dpo > s1
+    assert L.qlx_step_workspace_bytes(C.byref(d), 2, 1, 64) == 0
+
+
+def test_product_path_fails_loudly_without_the_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(b, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(b, "_lib", None)
+    with pytest.raises(ImportError):
+        b.lib()

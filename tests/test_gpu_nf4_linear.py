@@ -1,0 +1,143 @@
+"""GPU parity of NF4 quantize/dequant (bit-exact) and the QLoRA linear
+(fused NF4-dequant MFMA GEMM + LoRA slab) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import DEV, bf16_dev, f32_dev, to_np
+from helpers import rel_l2
+
+pytestmark = pytest.mark.gpu
+q = pytest.importorskip("qlora_fine_tuning_dequant_amd")
+
+TOL = 2e-2
+
+
+def _w_bits(rows, cols, seed, std=0.02):
+    return synth.to_bf16_bits(synth._normal_f32(rows * cols, std, seed, 99, rows, cols)).reshape(rows, cols)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 64), (3, 40), (5, 13), (256, 688), (688, 256), (1, 1), (7, 64 * 5 + 3),
+                                       (1024, 4096), (4096, 14336)])
+def test_nf4_quantize_and_dequant_bit_exact(rows, cols):
+    wb = _w_bits(rows, cols, rows * 31 + cols)
+    w = bf16_dev(wb)
+    n = rows * cols
+    packed = torch.empty((n + 1) // 2, dtype=torch.uint8, device=DEV)
+    absmax = torch.empty((n + 63) // 64, dtype=torch.float32, device=DEV)
+    q.nf4_quantize(w, packed, absmax)
+    p_ref, a_ref = oracle.nf4_quantize(synth.bf16_bits_to_f32(wb))
+    assert np.array_equal(to_np(packed), p_ref)
+    assert np.array_equal(to_np(absmax).view(np.uint32), a_ref.view(np.uint32))
+    out32 = torch.empty(n, dtype=torch.float32, device=DEV)
+    out16 = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    q.nf4_dequant(packed, absmax, rows, cols, out32)
+    q.nf4_dequant(packed, absmax, rows, cols, out16)
+    d_ref = oracle.nf4_dequant(p_ref, a_ref, n)
+    assert np.array_equal(to_np(out32).view(np.uint32), d_ref.view(np.uint32))
+    assert np.array_equal(out16.view(torch.int16).cpu().numpy().view(np.uint16), oracle.bf16_rne_bits(d_ref))
+
+
+def test_nf4_special_blocks_bit_exact():
+    c = oracle.nf4_codebook()
+    rows = []
+    for k in (-20, 0, 7):  # every code at a power-of-two scale round-trips exactly
+        blk = np.full(64, c[3], np.float32)
+        blk[:16] = c
+        rows.append(blk * np.float32(2.0 ** k))
+    rows.append(np.zeros(64, np.float32))                     # all-zero block
+    rows.append(np.concatenate([np.full(32, 0.5, np.float32), np.full(32, -1e-30, np.float32)]))
+    mids = oracle.nf4_midpoints()
+    blk = np.zeros(64, np.float32)
+    blk[0] = 1.0
+    blk[1:16] = mids                                          # exact midpoints go to the lower code
+    rows.append(blk)
+    w = np.concatenate(rows)
+    wb = oracle.bf16_rne_bits(w)
+    # keep exact bf16 representability for the midpoint case by comparing on the rounded values
+    wf = synth.bf16_bits_to_f32(wb)
+    packed = torch.empty(w.size // 2, dtype=torch.uint8, device=DEV)
+    absmax = torch.empty(w.size // 64, dtype=torch.float32, device=DEV)
+    q.nf4_quantize(bf16_dev(wb).view(1, -1), packed, absmax)
+    p_ref, a_ref = oracle.nf4_quantize(wf)
+    assert np.array_equal(to_np(packed), p_ref) and np.array_equal(to_np(absmax), a_ref)
+
+
+def _oracle_linear(xb, W_deq, A, B, s):
+    return oracle.qlora_linear_fwd(synth.bf16_bits_to_f32(xb), W_deq, A, B, s)
+
+
+# (T, in, out, r): ragged tails in every dimension, the tiny workload's down
+# projection (blocks straddle rows), and 8B-shaped q / down projections.
+SHAPES = [(64, 256, 512, 8), (37, 688, 256, 8), (200, 256, 1376, 16), (130, 96, 200, 4),
+          (512, 4096, 4096, 64), (512, 14336, 4096, 64)]
+
+
+@pytest.mark.parametrize("T,in_f,out_f,r", SHAPES)
+def test_qlora_linear_fwd_bwd_vs_oracle(T, in_f, out_f, r):
+    seed = T + in_f + out_f
+    wb = _w_bits(out_f, in_f, seed)
+    W = q.NF4Matrix.quantize(bf16_dev(wb))
+    p_ref, a_ref = oracle.nf4_quantize(synth.bf16_bits_to_f32(wb))
+    Wd = oracle.nf4_dequant(p_ref, a_ref, out_f * in_f).reshape(out_f, in_f)
+    xb = synth.activations_bf16(seed, T, in_f, 0)
+    dyb = synth.activations_bf16(seed, T, out_f, 1)
+    g = np.random.default_rng(seed)
+    A = (g.uniform(-1, 1, (r, in_f)) / np.sqrt(in_f)).astype(np.float32)
+    B = (g.standard_normal((out_f, r)) * 0.05).astype(np.float32)
+    s = 16.0 / r
+    x, dy = bf16_dev(xb), bf16_dev(dyb)
+    y = torch.empty(T, out_f, dtype=torch.bfloat16, device=DEV)
+    q.qlora_linear_fwd(x, W, f32_dev(A), f32_dev(B), s, y)
+    y_ref, u_ref = _oracle_linear(xb, Wd, A, B, s)
+    assert rel_l2(to_np(y), y_ref) < TOL
+    dx = torch.empty(T, in_f, dtype=torch.bfloat16, device=DEV)
+    dA = torch.empty(r, in_f, dtype=torch.float32, device=DEV)
+    dB = torch.empty(out_f, r, dtype=torch.float32, device=DEV)
+    q.qlora_linear_bwd(dy, x, W, f32_dev(A), f32_dev(B), s, dx, dA, dB)
+    dx_ref, dA_ref, dB_ref = oracle.qlora_linear_bwd(synth.bf16_bits_to_f32(dyb), synth.bf16_bits_to_f32(xb), u_ref,
+                                                     Wd, A, B, s)
+    assert rel_l2(to_np(dx), dx_ref) < TOL
+    assert rel_l2(to_np(dA), dA_ref) < TOL
+    assert rel_l2(to_np(dB), dB_ref) < TOL
+    # accumulate adds onto what is there
+    q.qlora_linear_bwd(dy, x, W, f32_dev(A), f32_dev(B), s, None, dA, dB, accumulate=True)
+    assert rel_l2(to_np(dA), 2 * dA_ref) < TOL and rel_l2(to_np(dB), 2 * dB_ref) < TOL
+
+
+@pytest.mark.parametrize("T,in_f,out_f,r", [(64, 256, 512, 8), (512, 4096, 4096, 64)])
+def test_lora_zero_B_is_bit_exact_base_and_lora_off(T, in_f, out_f, r):
+    wb = _w_bits(out_f, in_f, 5)
+    W = q.NF4Matrix.quantize(bf16_dev(wb))
+    x = bf16_dev(synth.activations_bf16(5, T, in_f, 0))
+    A = f32_dev(np.random.default_rng(0).standard_normal((r, in_f)).astype(np.float32))
+    B0 = torch.zeros(out_f, r, dtype=torch.float32, device=DEV)
+    y0 = torch.empty(T, out_f, dtype=torch.bfloat16, device=DEV)
+    y_off = torch.empty_like(y0)
+    q.qlora_linear_fwd(x, W, A, B0, 2.0, y0)
+    q.qlora_linear_fwd(x, W, None, None, 2.0, y_off)
+    assert torch.equal(y0.view(torch.int16), y_off.view(torch.int16))
+    # and the base itself matches the oracle
+    p_ref, a_ref = oracle.nf4_quantize(synth.bf16_bits_to_f32(wb))
+    Wd = oracle.nf4_dequant(p_ref, a_ref, out_f * in_f).reshape(out_f, in_f)
+    y_ref = synth.bf16_bits_to_f32(synth.activations_bf16(5, T, in_f, 0)) @ Wd.T
+    assert rel_l2(to_np(y_off), y_ref) < TOL
+
+
+def test_linear_dequant_operand_is_exactly_bf16_of_dequant():
+    """A one-hot input row selects a weight column, so y = bf16(W'[:, j]) exactly."""
+    out_f, in_f = 256, 512
+    wb = _w_bits(out_f, in_f, 9)
+    W = q.NF4Matrix.quantize(bf16_dev(wb))
+    xb = np.zeros((16, in_f), np.float32)
+    for i in range(16):
+        xb[i, i * 31] = 1.0
+    x = bf16_dev(oracle.bf16_rne_bits(xb))
+    y = torch.empty(16, out_f, dtype=torch.bfloat16, device=DEV)
+    q.qlora_linear_fwd(x, W, None, None, 1.0, y)
+    p_ref, a_ref = oracle.nf4_quantize(synth.bf16_bits_to_f32(wb))
+    Wd = oracle.nf4_dequant(p_ref, a_ref, out_f * in_f).reshape(out_f, in_f)
+    expect = oracle.bf16_rne_bits(np.stack([Wd[:, i * 31] for i in range(16)]))
+    assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), expect)
