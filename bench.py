@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Throughput of the layer-streamed QLoRA training step on one MI355X.
+
+Default workload: one streamed SFT step of a 32-layer Llama-3.1-8B-shaped
+model (hidden 4096, 32/8 heads, head_dim 128, SwiGLU 14336, vocab 128256),
+NF4 base layers in pinned host RAM fed to the GPU one decoder layer at a time,
+LoRA r 64 / alpha 16 on all 7 projections resident, batch 1, sequence 512,
+seeded synthetic weights and uniform random tokens (seed 1). Other workloads:
+--workload sft8b_b4 (batch 4) and dpo8b (2 preference pairs, 128-token
+prompts, beta 0.1).
+
+Prints ONE JSON line. `value` is tokens/s over the timed steps (inputs
+resident: weights in pinned host RAM as the method keeps them, tokens on the
+device). `roofline` reports the dominant kernel (the fused NF4-dequant MFMA
+GEMM) from HIP events recorded around every launch during the timed steps;
+`cpu_baseline` times the oracle on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import threading
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "train tokens/s, streamed NF4+LoRA Llama-8B-shape step; % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBPS = 8000.0
+SEED = 1
+
+WORKLOADS = {
+    "sft8b_b1": dict(kind="sft", batch=1, seq=512,
+                     name="streamed SFT step, 32-layer Llama-3.1-8B-shaped NF4 base + LoRA r64, batch 1, seq 512"),
+    "sft8b_b4": dict(kind="sft", batch=4, seq=512,
+                     name="streamed SFT step, 32-layer Llama-3.1-8B-shaped NF4 base + LoRA r64, batch 4, seq 512"),
+    "dpo8b": dict(kind="dpo", batch=2, seq=512, prompt=128, beta=0.1,
+                  name="streamed DPO step, 32-layer Llama-3.1-8B-shaped NF4 base + LoRA r64, 2 pairs x seq 512"),
+}
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def build_model(q, d, seed: int, want_device_blobs: bool = False):
+    """Quantize every layer's seeded bf16 weights on the GPU (nf4_quantize)
+    into a device blob and keep a pinned host copy. Host-side generation of
+    layer i+1 overlaps the GPU work of layer i."""
+    import numpy as np
+    import torch
+
+    import synth
+    dev = "cuda:0"
+    _, total = q.binding.blob_layout(d)
+    host, dev_blobs = [], []
+    staging = torch.empty(total, dtype=torch.uint8, device=dev)
+
+    def gen(layer):
+        return {p: synth.proj_weight_bf16(d, seed, layer, p) for p in synth.PROJ_NAMES}
+
+    nxt = {}
+    th = None
+
+    def start(layer):
+        nonlocal th
+        def run():
+            nxt[layer] = gen(layer)
+        th = threading.Thread(target=run)
+        th.start()
+
+    start(0)
+    for layer in range(d.n_layers):
+        th.join()
+        w_np = nxt.pop(layer)
+        if layer + 1 < d.n_layers:
+            start(layer + 1)
+        w = {p: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev) for p, a in w_np.items()}
+        g1, g2 = synth.norm_weights(d, seed, layer)
+        blob = torch.empty(total, dtype=torch.uint8, device=dev) if want_device_blobs else staging
+        q.binding.fill_blob(d, blob, w, torch.from_numpy(g1).to(dev), torch.from_numpy(g2).to(dev))
+        h = torch.empty(total, dtype=torch.uint8, pin_memory=True)
+        h.copy_(blob)
+        host.append(h)
+        if want_device_blobs:
+            dev_blobs.append(blob)
+        del w
+        if layer % 8 == 7:
+            log(f"  layers quantized: {layer + 1}/{d.n_layers}")
+    loras = []
+    for layer in range(d.n_layers):
+        lp = synth.lora_params(d, seed, layer, "kaiming")
+        loras.append(q.LoraLayer([torch.from_numpy(lp[p][0]).to(dev) for p in synth.PROJ_NAMES],
+                                 [torch.from_numpy(lp[p][1]).to(dev) for p in synth.PROJ_NAMES]))
+    emb = torch.from_numpy(synth.embedding_f16(d, seed).view(np.int16)).view(torch.float16).to(dev)
+    head = torch.from_numpy(synth.lm_head_f16(d, seed).view(np.int16)).view(torch.float16).to(dev)
+    gf = torch.from_numpy(synth.final_norm_weight(d, seed)).to(dev)
+    m = q.StreamModel(d, host, emb, head, gf, loras)
+    return m, dev_blobs
+
+
+def cpu_baseline(d, batch: int, seq: int) -> dict:
+    """The oracle on a bounded sample of the step: one of the 32 decoder
+    layers (dequantize, forward, recompute, backward) and the final norm +
+    LM head + cross-entropy, both at the full batch x seq shape; the step time
+    is extrapolated as n_layers x layer + head."""
+    import numpy as np
+
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    T = batch * seq
+    nf4 = {p: oracle.nf4_quantize(synth.bf16_bits_to_f32(synth.proj_weight_bf16(d, SEED, 0, p)))
+           for p in synth.PROJ_NAMES}
+    lp = synth.lora_params(d, SEED, 0, "kaiming")
+    g1, g2 = synth.norm_weights(d, SEED, 0)
+    toks = synth.tokens(SEED, batch, seq, d.vocab)
+    h = oracle.embed(toks, synth.embedding_f16(d, SEED))
+    dh = synth.activations_f32(SEED, T, d.hidden, 1) * np.float32(1e-4)
+    t0 = time.perf_counter()
+    W = oracle.dequant_layer(nf4, d)                                       # forward pass dequant
+    out = oracle.layer_fwd(h, W, g1, g2, lp, d, batch, seq)
+    W = oracle.dequant_layer(nf4, d)                                       # backward pass dequant
+    _, cache = oracle.layer_fwd(h, W, g1, g2, lp, d, batch, seq, keep=True)  # recompute
+    oracle.layer_bwd(dh, W, g1, g2, lp, d, batch, seq, cache)
+    t_layer = time.perf_counter() - t0
+    del W, cache
+    head = synth.lm_head_f16(d, SEED)
+    t0 = time.perf_counter()
+    oracle.head_ce(out, synth.final_norm_weight(d, SEED), head, toks, d.rms_eps)
+    t_head = time.perf_counter() - t0
+    step_s = d.n_layers * t_layer + t_head
+    return {"value": round(T / step_s, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"1 of {d.n_layers} decoder layers (dequant + fwd + recompute + bwd, {t_layer:.2f} s) and "
+                      f"the LM head + cross-entropy ({t_head:.2f} s) at batch {batch} x seq {seq}; "
+                      f"step = {d.n_layers} x layer + head = {step_s:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="sft8b_b1", choices=sorted(WORKLOADS))
+    ap.add_argument("--mode", default="streamed", choices=["streamed", "resident"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timing")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import qlora_fine_tuning_dequant_amd as q
+    import synth
+    B_ = q.binding
+    wl = WORKLOADS[args.workload]
+    d = synth.LLAMA8B
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    log(f"workload {args.workload}: {wl['name']} ({args.mode})")
+    t0 = time.perf_counter()
+    m, dev_blobs = build_model(q, d, SEED, want_device_blobs=(args.mode == "resident"))
+    if args.mode == "resident":
+        m = m.with_blobs(dev_blobs)
+    log(f"model ready in {time.perf_counter() - t0:.1f} s")
+    mode = B_.QLX_STREAMED if args.mode == "streamed" else B_.QLX_RESIDENT
+    ctx = q.Context(0)
+    grads = [q.LoraGrads(l) for l in m.lora]
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    batch, seq = wl["batch"], wl["seq"]
+    if wl["kind"] == "sft":
+        toks = torch.from_numpy(synth.tokens(SEED, batch, seq, d.vocab)).to(dev)
+        ws = B_.workspace(B_.step_workspace_bytes(d, 0, batch, seq))
+        tokens_per_step = batch * seq
+
+        def step():
+            q.stream_step_sft(ctx, m, toks, mode, loss, grads, ws)
+    else:
+        pairs = batch
+        ch, rj = synth.dpo_pairs(SEED, pairs, seq, wl["prompt"], d.vocab)
+        ch, rj = torch.from_numpy(ch).to(dev), torch.from_numpy(rj).to(dev)
+        logps = torch.empty(4 * pairs, dtype=torch.float32, device=dev)
+        ws = B_.workspace(B_.step_workspace_bytes(d, 1, pairs, seq))
+        tokens_per_step = 2 * pairs * seq
+
+        def step():
+            q.stream_step_dpo(ctx, m, ch, rj, wl["prompt"], wl["beta"], mode, B_.QLX_DPO_REF_FUSED, loss, logps,
+                              grads, ws)
+
+    for i in range(args.warmup):
+        step()
+        st = ctx.sync()
+        log(f"warmup {i + 1}/{args.warmup}: {st['step_ms']:.1f} ms, loss {loss.item():.4f}")
+    torch.cuda.synchronize()
+    if not args.no_profile:
+        B_.profile_begin()
+    stats = []
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step()
+        stats.append(ctx.sync())
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    prof = B_.profile_end() if not args.no_profile else {}
+    ms_step = 1000.0 * elapsed / args.steps
+    value = tokens_per_step * args.steps / elapsed
+    log(f"timed {args.steps} steps: {ms_step:.1f} ms/step, {value:.1f} tokens/s, loss {loss.item():.4f}")
+
+    reads = stats[-1]["layer_reads"]
+    h2d_ms = float(np.mean([s["h2d_ms"] for s in stats]))
+    h2d_bytes = stats[-1]["h2d_bytes"]
+    gemm_ms = sum(v["ms"] for k, v in prof.items() if k.startswith("gemm")) / max(args.steps, 1)
+    gemm_tf = sum(v["flops"] for k, v in prof.items() if k.startswith("gemm")) / max(args.steps, 1)
+    all_kernel_ms = sum(v["ms"] for v in prof.values()) / max(args.steps, 1)
+    roofline = None
+    if prof:
+        dom = max((k for k in prof if k.startswith("gemm_nf4")), key=lambda k: prof[k]["ms"])
+        p = prof[dom]
+        ach = p["flops"] / (p["ms"] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "launches": p["launches"], "avg_launch_us": round(1000.0 * p["ms"] / p["launches"], 2),
+                    "flops_per_launch": p["flops"] / p["launches"]}
+    kernels = {k: {"launches_per_step": v["launches"] // args.steps, "ms_per_step": round(v["ms"] / args.steps, 3),
+                   "TFLOP/s": round(v["flops"] / max(v["ms"], 1e-9) / 1e9, 2),
+                   "GB/s": round(v["bytes"] / max(v["ms"], 1e-9) / 1e6, 1)}
+               for k, v in sorted(prof.items(), key=lambda kv: -kv[1]["ms"])}
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl["name"], "global_batch": batch if wl["kind"] == "sft" else 2 * batch,
+                   "seq_len": seq, "mode": args.mode, "layers": d.n_layers, "lora_r": d.lora_r},
+        "roofline": roofline,
+        "stream": {"layer_reads_per_step": reads, "h2d_GB_per_step": round(h2d_bytes / 1e9, 3),
+                   "h2d_ms_per_step": round(h2d_ms, 2),
+                   "h2d_GBps": round(h2d_bytes / max(h2d_ms, 1e-9) / 1e6, 1) if h2d_ms else None},
+        "gpu_time": {"kernels_ms_per_step": round(all_kernel_ms, 2), "gemm_ms_per_step": round(gemm_ms, 2),
+                     "gemm_TFLOP_per_step": round(gemm_tf / 1e12, 3),
+                     "gemm_TFLOPs_avg": round(gemm_tf / max(gemm_ms, 1e-9) / 1e9, 1)},
+        "peak_vram_GB": round(torch.cuda.max_memory_allocated() / 1e9, 3),
+        "kernels": kernels,
+        "loss": float(loss.item()),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        del ws
+        out["cpu_baseline"] = cpu_baseline(d, wl["batch"] if wl["kind"] == "sft" else 2 * wl["batch"], seq)
+        log(f"cpu baseline: {out['cpu_baseline']['value']} tokens/s")
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    ctx.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

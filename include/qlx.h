@@ -234,6 +234,26 @@ int stream_step_dpo(qlx_ctx* ctx, const qlx_model* model, const int32_t* chosen,
                     int mode, int ref_schedule, float* loss, float* logps,
                     const qlx_lora_grad* grads, void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Per-kernel timing (observability). Between qlx_profile_begin() and
+ * qlx_profile_end() every kernel the library launches is bracketed by a pair
+ * of HIP events on its own stream; qlx_profile_end() waits for them and
+ * returns one row per kernel: launches, summed event time, and the summed
+ * algorithmic flops and HBM bytes of those launches (operands read once,
+ * outputs written once). Process-wide; not for concurrent use from several
+ * threads. `out` may be NULL to only count rows.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    char name[48];
+    int64_t launches;
+    double ms;
+    double flops;
+    double bytes;
+} qlx_kernel_prof;
+
+int qlx_profile_begin(void);
+int qlx_profile_end(qlx_kernel_prof* out, int max_out, int* count);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,7 @@ EXPORTED = (
     "qlx_last_error", "qlx_version", "nf4_quantize", "nf4_dequant", "qlx_linear_workspace_bytes",
     "qlora_linear_fwd", "qlora_linear_bwd", "qlx_layer_blob_layout", "qlx_layer_workspace_bytes",
     "layer_fwd", "layer_bwd", "qlx_ctx_create", "qlx_ctx_destroy", "qlx_ctx_sync",
-    "qlx_step_workspace_bytes", "stream_step_sft", "stream_step_dpo",
+    "qlx_step_workspace_bytes", "stream_step_sft", "stream_step_dpo", "qlx_profile_begin", "qlx_profile_end",
 )
 
 
@@ -68,6 +68,11 @@ class Stats(C.Structure):
                 ("step_ms", C.c_float), ("h2d_ms", C.c_float)]
 
 
+class KernelProf(C.Structure):
+    _fields_ = [("name", C.c_char * 48), ("launches", C.c_int64), ("ms", C.c_double), ("flops", C.c_double),
+                ("bytes", C.c_double)]
+
+
 class Model(C.Structure):
     _fields_ = [("dims", Dims), ("layer_blobs", C.POINTER(C.c_void_p)), ("embed_f16", C.c_void_p),
                 ("lm_head_f16", C.c_void_p), ("final_norm", C.c_void_p), ("lora", C.POINTER(Lora))]
@@ -105,6 +110,8 @@ def lib() -> C.CDLL:
         "stream_step_sft": (i32, [vp, C.POINTER(Model), vp, i32, i32, i32, vp, C.POINTER(LoraGrad), vp, sz, vp]),
         "stream_step_dpo": (i32, [vp, C.POINTER(Model), vp, vp, i32, i32, i32, f32, i32, i32, vp, vp,
                                   C.POINTER(LoraGrad), vp, sz, vp]),
+        "qlx_profile_begin": (i32, []),
+        "qlx_profile_end": (i32, [C.POINTER(KernelProf), i32, C.POINTER(C.c_int)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -349,3 +356,17 @@ def stream_step_dpo(ctx: Context, model: StreamModel, chosen: torch.Tensor, reje
     _check(lib().stream_step_dpo(ctx.h, C.byref(model.c), _ptr(chosen), _ptr(rejected), P, S, prompt_len,
                                  float(beta), mode, ref_schedule, _ptr(loss), _ptr(logps), ga, _ptr(ws),
                                  ws.numel(), _stream(stream)))
+
+
+# ------------------------------------------------------------------ profiling
+def profile_begin() -> None:
+    _check(lib().qlx_profile_begin())
+
+
+def profile_end() -> dict:
+    """{kernel name: {launches, ms, flops, bytes}} summed since profile_begin()."""
+    n = C.c_int()
+    out = (KernelProf * 64)()
+    _check(lib().qlx_profile_end(out, 64, C.byref(n)))
+    return {out[i].name.decode(): {"launches": out[i].launches, "ms": out[i].ms, "flops": out[i].flops,
+                                   "bytes": out[i].bytes} for i in range(min(n.value, 64))}

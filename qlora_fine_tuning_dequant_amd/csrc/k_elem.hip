@@ -86,12 +86,14 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const float* __restrict__ d
 void launch_rmsnorm_fwd(const float* x, const float* g, int T, int H, float eps, void* out, int out_f16, float* rstd,
                         hipStream_t s) {
     if (T <= 0) return;
+    ProfScope prof("rmsnorm_fwd", 4.0 * T * H, double(T) * H * (4.0 + (out_f16 ? 2 : 2)) + 4.0 * H, s);
     hipLaunchKernelGGL(k_rmsnorm_fwd, dim3(T), dim3(256), 0, s, x, g, H, eps, out, out_f16, rstd);
     check_launch("rmsnorm_fwd");
 }
 void launch_rmsnorm_bwd(const float* dy, const float* x, const float* g, const float* rstd, const float* dres, int T,
                         int H, float* dx, hipStream_t s) {
     if (T <= 0) return;
+    ProfScope prof("rmsnorm_bwd", 8.0 * T * H, double(T) * H * (12.0 + (dres ? 4 : 0)), s);
     hipLaunchKernelGGL(k_rmsnorm_bwd, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx);
     check_launch("rmsnorm_bwd");
 }
@@ -136,6 +138,7 @@ __global__ void k_rope(uint16_t* __restrict__ buf, int64_t ld, int T, int seq, i
 
 void launch_rope_table(int seq, int hd, float theta, float* cs, hipStream_t s) {
     const int n = seq * (hd / 2);
+    ProfScope prof("rope_table", 0.0, 8.0 * n, s);
     hipLaunchKernelGGL(k_rope_table, dim3((n + 255) / 256), dim3(256), 0, s, seq, hd, double(theta),
                        reinterpret_cast<float2*>(cs));
     check_launch("rope_table");
@@ -144,6 +147,7 @@ void launch_rope(uint16_t* buf, int64_t ld, int T, int seq, int col0, int nheads
                  hipStream_t s) {
     const int64_t total = int64_t(T) * nheads * (hd / 2);
     if (total <= 0) return;
+    ProfScope prof("rope", 6.0 * total, 8.0 * total, s);
     hipLaunchKernelGGL(k_rope, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, buf, ld, T, seq, col0, nheads,
                        hd, reinterpret_cast<const float2*>(cs), inverse);
     check_launch("rope");
@@ -176,12 +180,14 @@ __global__ void k_swiglu_bwd(const uint16_t* __restrict__ dact, const uint16_t* 
 void launch_swiglu_fwd(const uint16_t* gu, int T, int I, uint16_t* act, hipStream_t s) {
     const int64_t n = int64_t(T) * I;
     if (n <= 0) return;
+    ProfScope prof("swiglu_fwd", 5.0 * n, 6.0 * n, s);
     hipLaunchKernelGGL(k_swiglu_fwd, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, gu, T, I, act);
     check_launch("swiglu_fwd");
 }
 void launch_swiglu_bwd(const uint16_t* dact, const uint16_t* gu, int T, int I, uint16_t* dgu, hipStream_t s) {
     const int64_t n = int64_t(T) * I;
     if (n <= 0) return;
+    ProfScope prof("swiglu_bwd", 10.0 * n, 10.0 * n, s);
     hipLaunchKernelGGL(k_swiglu_bwd, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, dact, gu, T, I, dgu);
     check_launch("swiglu_bwd");
 }
@@ -199,6 +205,7 @@ __global__ void k_embed(const int32_t* __restrict__ tok, const uint16_t* __restr
 void launch_embed(const int32_t* tok, const uint16_t* E, int T, int H, int V, float* h, hipStream_t s) {
     const int64_t n = int64_t(T) * H;
     if (n <= 0) return;
+    ProfScope prof("embed", 0.0, 6.0 * n, s);
     hipLaunchKernelGGL(k_embed, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, tok, E, T, H, V, h);
     check_launch("embed");
 }
@@ -209,6 +216,7 @@ __global__ void k_f32_to_bf16(const float* __restrict__ x, int64_t n, uint16_t* 
 }
 void launch_f32_to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s) {
     if (n <= 0) return;
+    ProfScope prof("f32_to_bf16", 0.0, 6.0 * n, s);
     hipLaunchKernelGGL(k_f32_to_bf16, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, x, n, y);
     check_launch("f32_to_bf16");
 }
@@ -254,6 +262,7 @@ void launch_lora_pack(const LoraSeg* segs, int nseg, int r, int in_f, float scal
     sg.nseg = nseg;
     const int64_t nA = int64_t(nseg) * r * in_f, nB = int64_t(ntot) * nseg * r;
     const int64_t n = nA + nB;
+    ProfScope prof("lora_pack", double(nB), 4.0 * nA + 2.0 * nA + 2.0 * nB + 4.0 * (nB / nseg), s);
     hipLaunchKernelGGL(k_lora_pack, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, sg, r, in_f, scale, Acat, Bbd,
                        nA, nB, ntot);
     check_launch("lora_pack");
@@ -296,11 +305,13 @@ __global__ __launch_bounds__(256) void k_attn_softmax_bwd(const uint16_t* __rest
 }
 void launch_attn_softmax_fwd(const float* scores, int Z, int S, uint16_t* P, hipStream_t s) {
     const int64_t rows = int64_t(Z) * S;
+    ProfScope prof("attn_softmax_fwd", 5.0 * Z * (S * (S + 1.0) / 2), Z * (4.0 * (S * (S + 1.0) / 2) + 2.0 * S * S), s);
     hipLaunchKernelGGL(k_attn_softmax_fwd, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, scores, Z, S, P);
     check_launch("attn_softmax_fwd");
 }
 void launch_attn_softmax_bwd(const uint16_t* P, const float* dP, int Z, int S, uint16_t* dS, hipStream_t s) {
     const int64_t rows = int64_t(Z) * S;
+    ProfScope prof("attn_softmax_bwd", 4.0 * Z * (S * (S + 1.0) / 2), Z * (6.0 * (S * (S + 1.0) / 2) + 2.0 * S * S), s);
     hipLaunchKernelGGL(k_attn_softmax_bwd, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, P, dP, Z, S, dS);
     check_launch("attn_softmax_bwd");
 }
@@ -324,6 +335,7 @@ __global__ void k_gqa_reduce(const float* __restrict__ dh, int B, int nH, int nK
 void launch_gqa_reduce(const float* dh, int B, int nH, int nKV, int S, int hd, uint16_t* out, int64_t ldo, int col0,
                        hipStream_t s) {
     const int64_t total = int64_t(B) * nKV * S * hd;
+    ProfScope prof("gqa_reduce", double(total) * (nH / nKV), double(total) * (4.0 * (nH / nKV) + 2.0), s);
     hipLaunchKernelGGL(k_gqa_reduce, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, dh, B, nH, nKV, S, hd, out,
                        ldo, col0);
     check_launch("gqa_reduce");
@@ -384,11 +396,13 @@ __global__ __launch_bounds__(256) void k_ce_grad(const float* __restrict__ z, co
 
 void launch_ce_stats(const float* logits, int T, int V, const int32_t* tokens, int seq, int start, float* lse,
                      float* picked, hipStream_t s) {
+    ProfScope prof("ce_stats", 3.0 * T * V, 4.0 * T * V, s);
     hipLaunchKernelGGL(k_ce_stats, dim3(T), dim3(256), 0, s, logits, T, V, tokens, seq, start, lse, picked);
     check_launch("ce_stats");
 }
 void launch_ce_grad(const float* logits, const float* lse, int T, int V, const int32_t* tokens, int seq, int start,
                     int mode, float sc, const float* gseq, uint16_t* dz, hipStream_t s) {
+    ProfScope prof("ce_grad", 4.0 * T * V, 6.0 * T * V, s);
     hipLaunchKernelGGL(k_ce_grad, dim3((V + 255) / 256, T), dim3(256), 0, s, logits, lse, T, V, tokens, seq, start,
                        mode, sc, gseq, dz);
     check_launch("ce_grad");
@@ -407,6 +421,7 @@ __global__ __launch_bounds__(256) void k_sft_loss(const float* __restrict__ lse,
     }
 }
 void launch_sft_loss(const float* lse, const float* picked, int T, int seq, float* loss, hipStream_t s) {
+    ProfScope prof("loss_reduce", 2.0 * T, 8.0 * T, s);
     hipLaunchKernelGGL(k_sft_loss, dim3(1), dim3(256), 0, s, lse, picked, T, seq, loss);
     check_launch("sft_loss");
 }
@@ -456,6 +471,7 @@ __global__ __launch_bounds__(256) void k_dpo_loss(const float* __restrict__ lse_
 void launch_dpo_loss(const float* lse_pol, const float* pk_pol, const float* lse_ref, const float* pk_ref, int pairs,
                      int seq, int prompt_len, float beta, float* loss, float* logps, float* gseq, hipStream_t s) {
     (void)prompt_len;
+    ProfScope prof("loss_reduce", 4.0 * seq * pairs * 2, 16.0 * seq * pairs * 2, s);
     hipLaunchKernelGGL(k_dpo_loss, dim3(1), dim3(256), 0, s, lse_pol, pk_pol, lse_ref, pk_ref, pairs, seq, beta, loss,
                        logps, gseq);
     check_launch("dpo_loss");

@@ -349,6 +349,24 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
     QLX_REQUIRE(p.batch >= 1 && p.batch * p.splits <= 65535, QLX_EUNSUPPORTED, "gemm: grid.z too large");
     dim3 grid(gx, gy, p.batch * p.splits);
     const int key = akind * 100 + bkind * 10 + te;
+    // algorithmic work: multiply-adds actually needed (causal halves, no zero blocks)
+    double pairs_k;
+    const double M = p.M, N = p.N, K = p.K;
+    if (p.causal == CAUSAL_SKIP_UPPER) pairs_k = (M * (M + 1) / 2) * K;
+    else if (p.causal == CAUSAL_K_LE_M || p.causal == CAUSAL_K_GE_M) pairs_k = N * (M * (M + 1) / 2);
+    else pairs_k = M * N * K;
+    const double k2 = p.K2 > 0 ? (p.slab_alg_k >= 0 ? p.slab_alg_k : p.K2) : 0;
+    const double flops = 2.0 * p.batch * (pairs_k + M * N * k2);
+    const double belt = (te == TE_F16 || !nf4) ? 2.0 : 0.5 + 4.0 / 64.0;
+    const double cb = p.c_type == C_F32 ? 4.0 : 2.0;
+    const double bytes = p.batch * (M * K * 2 + N * K * belt + M * N * cb * (p.accumulate ? 2 : 1) +
+                                    (p.R ? M * N * 4 : 0) + (p.K2 ? (M + N) * p.K2 * 2.0 : 0));
+    static const char* kNames[] = {"gemm_nf4_nt", "gemm_nf4_nn", "gemm_bf16_nt", "gemm_bf16_nn",
+                                   "gemm_bf16_tn", "gemm_f16_nt", "gemm_f16_nn", "gemm_other"};
+    const int ni = key == 0 ? 0 : key == 10 ? 1 : key == 20 ? 2 : key == 30 ? 3 : key == 130 ? 4
+                 : key == 21 ? 5 : key == 31 ? 6 : 7;
+    {
+    ProfScope prof(kNames[ni], flops, bytes, s);
     switch (key) {
         case A_ROW * 100 + B_NF4_NT * 10 + TE_BF16: launch<A_ROW, B_NF4_NT, TE_BF16>(p, grid, s); break;
         case A_ROW * 100 + B_NF4_NN * 10 + TE_BF16: launch<A_ROW, B_NF4_NN, TE_BF16>(p, grid, s); break;
@@ -360,8 +378,10 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
         default: throw Error{QLX_EUNSUPPORTED, "gemm: operand combination not built"};
     }
     check_launch("gemm");
+    }
     if (p.splits > 1) {
         const int64_t MN = int64_t(p.M) * p.N;
+        ProfScope prof("splitk_reduce", double(MN) * p.splits, double(MN) * (4.0 * p.splits + cb + (p.R ? 4 : 0)), s);
         hipLaunchKernelGGL(k_splitk_reduce, dim3(unsigned((MN + 255) / 256)), dim3(256), 0, s, p);
         check_launch("gemm splitk reduce");
     }

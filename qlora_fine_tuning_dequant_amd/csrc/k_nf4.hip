@@ -86,6 +86,7 @@ void launch_nf4_quantize(const uint16_t* w, int64_t n, uint8_t* packed, float* a
     if (n <= 0) return;
     const int64_t nblk = (n + 63) / 64;
     const int64_t grid = (nblk + 3) / 4;
+    ProfScope prof("nf4_quantize", 8.0 * n, n * (2.0 + 0.5 + 4.0 / 64), s);
     hipLaunchKernelGGL(k_nf4_quantize, dim3(unsigned(grid)), dim3(256), 0, s, w, n, packed, absmax);
     check_launch("nf4_quantize");
 }
@@ -95,6 +96,7 @@ void launch_nf4_dequant(const uint8_t* packed, const float* absmax, int64_t n, i
     if (n <= 0) return;
     const int64_t groups = (n + 7) / 8;
     const int64_t grid = (groups + 255) / 256;
+    ProfScope prof("nf4_dequant", double(n), n * (0.5 + 4.0 / 64 + (out_dtype == QLX_BF16 ? 2 : 4)), s);
     if (out_dtype == QLX_BF16)
         hipLaunchKernelGGL(k_nf4_dequant<1>, dim3(unsigned(grid)), dim3(256), 0, s, packed, absmax, n, out);
     else

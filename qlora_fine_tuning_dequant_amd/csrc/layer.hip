@@ -227,6 +227,7 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
             p.lda2 = 3 * r;
             p.B2 = w.B_qkv;
             p.ldb2 = 3 * r;
+            p.slab_alg_k = r;  // block-diagonal: each output column sees one adapter
         }
         out_bf16(p, w.qkv, g.nqkv);
         gemm(p, A_ROW, B_NF4_NT, TE_BF16, w.partial, s);
@@ -301,6 +302,7 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
             p.lda2 = 2 * r;
             p.B2 = w.B_gu;
             p.ldb2 = 2 * r;
+            p.slab_alg_k = r;
         }
         out_bf16(p, w.gu, 2 * g.I);
         gemm(p, A_ROW, B_NF4_NT, TE_BF16, w.partial, s);

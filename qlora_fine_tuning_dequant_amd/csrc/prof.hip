@@ -1,0 +1,102 @@
+// Optional per-kernel timing with HIP events, recorded on the stream each
+// kernel is launched on. Off unless qlx_profile_begin() is called; then every
+// launcher brackets its kernel with an event pair and notes the kernel's
+// algorithmic flops and HBM bytes, and qlx_profile_end() sums them per kernel.
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <vector>
+
+#include "qlx_internal.h"
+
+namespace qlx {
+
+namespace {
+struct Rec {
+    const char* name;
+    double flops, bytes;
+    hipEvent_t b, e;
+};
+std::mutex g_mu;
+bool g_on = false;
+std::vector<Rec> g_recs;
+std::vector<hipEvent_t> g_pool;
+size_t g_used = 0;
+
+hipEvent_t take_event() {
+    if (g_used == g_pool.size()) {
+        hipEvent_t e;
+        QLX_CHECK_HIP(hipEventCreate(&e));
+        g_pool.push_back(e);
+    }
+    return g_pool[g_used++];
+}
+}  // namespace
+
+ProfScope::ProfScope(const char* name, double flops, double bytes, hipStream_t s) : s_(s) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!g_on) return;
+    idx_ = int64_t(g_recs.size());
+    Rec r{name, flops, bytes, take_event(), take_event()};
+    QLX_CHECK_HIP(hipEventRecord(r.b, s));
+    g_recs.push_back(r);
+}
+
+ProfScope::~ProfScope() {
+    if (idx_ < 0) return;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (idx_ < int64_t(g_recs.size())) (void)hipEventRecord(g_recs[idx_].e, s_);
+}
+
+}  // namespace qlx
+
+using namespace qlx;
+
+extern "C" int qlx_profile_begin(void) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_recs.clear();
+    g_used = 0;
+    g_on = true;
+    return QLX_OK;
+}
+
+extern "C" int qlx_profile_end(qlx_kernel_prof* out, int max_out, int* count) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_on = false;
+    try {
+        struct Agg {
+            int64_t n = 0;
+            double ms = 0, flops = 0, bytes = 0;
+        };
+        std::map<std::string, Agg> agg;
+        for (const Rec& r : g_recs) {
+            QLX_CHECK_HIP(hipEventSynchronize(r.e));
+            float ms = 0.f;
+            QLX_CHECK_HIP(hipEventElapsedTime(&ms, r.b, r.e));
+            Agg& a = agg[r.name];
+            a.n += 1;
+            a.ms += ms;
+            a.flops += r.flops;
+            a.bytes += r.bytes;
+        }
+        int i = 0;
+        for (const auto& kv : agg) {
+            if (out && i < max_out) {
+                std::memset(&out[i], 0, sizeof(qlx_kernel_prof));
+                std::strncpy(out[i].name, kv.first.c_str(), sizeof(out[i].name) - 1);
+                out[i].launches = kv.second.n;
+                out[i].ms = kv.second.ms;
+                out[i].flops = kv.second.flops;
+                out[i].bytes = kv.second.bytes;
+            }
+            ++i;
+        }
+        if (count) *count = i;
+        g_recs.clear();
+        g_used = 0;
+        return QLX_OK;
+    } catch (const Error& e) {
+        set_error(e.msg);
+        return e.code;
+    }
+}

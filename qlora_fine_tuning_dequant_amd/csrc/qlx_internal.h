@@ -28,6 +28,14 @@ struct Error {
     } while (0)
 void check_launch(const char* what);
 
+// Brackets one kernel launch with timing events when profiling is on.
+struct ProfScope {
+    ProfScope(const char* name, double flops, double bytes, hipStream_t s);
+    ~ProfScope();
+    hipStream_t s_;
+    int64_t idx_ = -1;
+};
+
 // ---------------------------------------------------------- workspace carving
 // Hands out 256-byte aligned sub-buffers of a caller workspace. With a null
 // base it only measures (every take() returns nullptr and bumps the size).
@@ -93,6 +101,7 @@ struct GemmParams {
     int seg_rows = 0;          // >0: row m goes to Cseg[m / seg_rows] row m % seg_rows
     void* Cseg[4] = {nullptr, nullptr, nullptr, nullptr};
     int causal = CAUSAL_NONE;
+    int slab_alg_k = -1;  // algorithmic K of the slab for flop accounting (-1: K2)
     // set by the launcher
     int a_vec = 0, b_vec = 0, a2_vec = 0, b2_vec = 0;
 };
