@@ -3,24 +3,27 @@
 //
 // What it computes: C = alpha * (A . op(B) + A2 . op(B2)) (+ R) (+ C_old),
 // fp32 accumulation. For the QLoRA linear (LoRA, Hu et al. 2021, section 4.1,
-// on the NF4 base that the pages describe: rug.gal article "En detalle") the
-// first phase runs over the frozen NF4 weight and the second phase ("slab",
+// on the frozen NF4 base the pages describe: rug.gal article "En detalle") the
+// first K phase runs over the NF4 weight and the second phase ("slab",
 // K2 = r or a few r) adds the LoRA term u . (sB)^T, so the adapter costs one
 // short extra K stretch instead of a separate pass over the output.
 //
-// Structure (one workgroup = 256 threads = 4 wavefronts, tile 128 x 128,
-// K chunks of 64):
-//   global -> registers -> (NF4: unpack nibble, code value from a 16-entry LDS
-//   table, * absmax, round to bf16) -> LDS tiles As[128][64+8], Bs[128][64+8]
-//   stored k-contiguous -> each wavefront computes a 64 x 64 sub-tile as 4 x 4
-//   MFMA 16x16x32 blocks, reading 16-byte fragments from LDS.
-// Loaders exist for every layout the training step needs (A row-major or
-// transposed; B NF4 [N][K] or [K][N], dense [N][K] or [K][N]), so no operand
-// is ever transposed in memory. Edges (M, N, K not multiples of the tile) are
-// zero-filled in the loaders and masked in the epilogue.
+// Structure: a workgroup of (BM/WM)*(BN/WN) wavefronts computes a BM x BN tile
+// in K chunks of 64. Each chunk: global loads of the NEXT chunk are issued into
+// registers, the wavefronts run their MFMAs on the CURRENT chunk from LDS, then
+// the prefetched registers are (for NF4: unpacked, looked up in a 16-entry LDS
+// table of code values, multiplied by the block absmax, rounded to bf16) and
+// written to the other LDS buffer; one barrier per chunk. LDS tiles are stored
+// k-contiguous ([rows][64+8]) so every MFMA fragment is one 16-byte LDS read.
+// Loaders exist for every operand layout the training step needs (A row-major
+// or transposed; B NF4 [N][K] or [K][N], dense [N][K] or [K][N]), so no operand
+// is ever transposed in memory. Edges are zero-filled by the loaders and
+// masked by the epilogue. Tiles are ordered so the M-tiles sharing one weight
+// tile run on the same XCD (one L2) together.
 // Split-K writes fp32 partials that a second kernel sums in a fixed order:
 // results depend only on shapes, never on timing or pointer values.
 #include <algorithm>
+#include <type_traits>
 
 #include "nf4_codes.h"
 #include "qlx_internal.h"
@@ -31,7 +34,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BN = 128, BK = 64, BKP = BK + 8, NTHR = 256;
+constexpr int BK = 64, BKP = BK + 8;
 
 template <int TE>
 __device__ inline f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c) {
@@ -43,163 +46,240 @@ __device__ inline f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c) {
                                                       0, 0, 0);
 }
 
-__device__ inline uint32_t pack2(uint16_t lo, uint16_t hi) { return uint32_t(lo) | (uint32_t(hi) << 16); }
+__device__ inline uint32_t pack2(uint32_t lo, uint32_t hi) { return (lo & 0xFFFFu) | (hi << 16); }
 
 // ---------------------------------------------------------------------------
-// Row-major loader: tile[r][k] = src[(r0 + r) * ld + k0 + k] for r < 128,
-// k < 64, zero outside [0, rows) x [0, K). Each thread moves 4 vectors of 8.
-__device__ inline void load_rowmajor(const uint16_t* __restrict__ src, int64_t ld, int r0, int k0, int rows, int K,
-                                     int vec_ok, uint16_t* __restrict__ tile) {
-    const int tid = threadIdx.x;
+// Row-major operand: tile[r][k] = src[(r0 + r) * ld + k0 + k], r < R, k < 64.
+template <int R, int NT>
+struct RowLoader {
+    static constexpr int U = R * (BK / 8) / NT;
+    static_assert(U >= 1 && R * (BK / 8) % NT == 0, "row loader shape");
+    uint4 v[U];
+    __device__ inline void load(const uint16_t* __restrict__ src, int64_t ld, int r0, int k0, int rows, int K,
+                                int vec_ok) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int v = tid + it * NTHR;
-        const int r = v >> 3, c = (v & 7) * 8;
-        const int gr = r0 + r, gc = k0 + c;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (gr < rows) {
-            const uint16_t* p = src + int64_t(gr) * ld + gc;
-            if (vec_ok && gc + 8 <= K) {
-                val = *reinterpret_cast<const uint4*>(p);
-            } else {
-                uint16_t e[8];
+        for (int u = 0; u < U; ++u) {
+            const int idx = threadIdx.x + u * NT;
+            const int r = idx >> 3, c = (idx & 7) * 8;
+            const int gr = r0 + r, gc = k0 + c;
+            uint4 val = make_uint4(0, 0, 0, 0);
+            if (gr < rows) {
+                const uint16_t* p = src + int64_t(gr) * ld + gc;
+                if (vec_ok && gc + 8 <= K) {
+                    val = *reinterpret_cast<const uint4*>(p);
+                } else {
+                    uint32_t e[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) e[j] = (gc + j < K) ? p[j] : uint16_t(0);
-                val = make_uint4(pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7]));
+                    for (int j = 0; j < 8; ++j) e[j] = (gc + j < K) ? p[j] : 0u;
+                    val = make_uint4(pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7]));
+                }
             }
-        }
-        *reinterpret_cast<uint4*>(tile + r * BKP + c) = val;
-    }
-}
-
-// Transposed loader: tile[r][k] = src[(k0 + k) * ld + r0 + r]. Each thread
-// reads 4 consecutive r from 8 consecutive k rows and writes 4 k-contiguous
-// 16-byte vectors.
-__device__ inline void load_transposed(const uint16_t* __restrict__ src, int64_t ld, int r0, int k0, int rows, int K,
-                                       int vec_ok, uint16_t* __restrict__ tile) {
-    const int tid = threadIdx.x;
-    const int rg = (tid & 31) * 4, kg = (tid >> 5) * 8;
-    uint16_t e[8][4];
-#pragma unroll
-    for (int kr = 0; kr < 8; ++kr) {
-        const int gk = k0 + kg + kr;
-        const int gr = r0 + rg;
-        if (gk < K) {
-            const uint16_t* p = src + int64_t(gk) * ld + gr;
-            if (vec_ok && gr + 4 <= rows) {
-                const uint2 w = *reinterpret_cast<const uint2*>(p);
-                e[kr][0] = uint16_t(w.x);
-                e[kr][1] = uint16_t(w.x >> 16);
-                e[kr][2] = uint16_t(w.y);
-                e[kr][3] = uint16_t(w.y >> 16);
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) e[kr][j] = (gr + j < rows) ? p[j] : uint16_t(0);
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) e[kr][j] = 0;
+            v[u] = val;
         }
     }
+    __device__ inline void store(uint16_t* __restrict__ tile) const {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint4 val = make_uint4(pack2(e[0][j], e[1][j]), pack2(e[2][j], e[3][j]), pack2(e[4][j], e[5][j]),
-                                     pack2(e[6][j], e[7][j]));
-        *reinterpret_cast<uint4*>(tile + (rg + j) * BKP + kg) = val;
+        for (int u = 0; u < U; ++u) {
+            const int idx = threadIdx.x + u * NT;
+            *reinterpret_cast<uint4*>(tile + (idx >> 3) * BKP + (idx & 7) * 8) = v[u];
+        }
     }
-}
+};
 
-__device__ inline uint16_t nf4_elem(const uint8_t* __restrict__ packed, const float* __restrict__ absmax,
+// Transposed operand: tile[r][k] = src[(k0 + k) * ld + r0 + r]. A unit is 4
+// consecutive r from 8 consecutive k rows, written as 4 k-contiguous vectors.
+template <int R, int NT>
+struct TransLoader {
+    static constexpr int U = (R / 4) * (BK / 8) / NT;
+    static_assert(U >= 1 && (R / 4) * (BK / 8) % NT == 0, "trans loader shape");
+    uint2 v[U][8];
+    __device__ inline void load(const uint16_t* __restrict__ src, int64_t ld, int r0, int k0, int rows, int K,
+                                int vec_ok) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int idx = threadIdx.x + u * NT;
+            const int rg = (idx % (R / 4)) * 4, kg = (idx / (R / 4)) * 8;
+            const int gr = r0 + rg;
+#pragma unroll
+            for (int kr = 0; kr < 8; ++kr) {
+                const int gk = k0 + kg + kr;
+                uint2 w = make_uint2(0, 0);
+                if (gk < K) {
+                    const uint16_t* p = src + int64_t(gk) * ld + gr;
+                    if (vec_ok && gr + 4 <= rows) {
+                        w = *reinterpret_cast<const uint2*>(p);
+                    } else {
+                        uint32_t e[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) e[j] = (gr + j < rows) ? p[j] : 0u;
+                        w = make_uint2(pack2(e[0], e[1]), pack2(e[2], e[3]));
+                    }
+                }
+                v[u][kr] = w;
+            }
+        }
+    }
+    __device__ inline void store(uint16_t* __restrict__ tile) const {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int idx = threadIdx.x + u * NT;
+            const int rg = (idx % (R / 4)) * 4, kg = (idx / (R / 4)) * 8;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int sh = (j & 1) * 16;
+                uint32_t e[8];
+#pragma unroll
+                for (int kr = 0; kr < 8; ++kr) e[kr] = ((j < 2 ? v[u][kr].x : v[u][kr].y) >> sh) & 0xFFFFu;
+                *reinterpret_cast<uint4*>(tile + (rg + j) * BKP + kg) =
+                    make_uint4(pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7]));
+            }
+        }
+    }
+};
+
+__device__ inline uint32_t nf4_elem(const uint8_t* __restrict__ packed, const float* __restrict__ absmax,
                                     int64_t flat, const float* lut) {
     const uint32_t byte = packed[flat >> 1];
     const int code = (flat & 1) ? int(byte & 15) : int(byte >> 4);
     return f32_to_bf16_bits(lut[code] * absmax[flat >> 6]);
 }
 
-// NF4 weight stored [N][K] (flat n*cols + k): tile[n][k] = bf16(c[code] * absmax).
-// Fast path: two threads per row, 32 codes (16 bytes) each, one absmax.
-__device__ inline void load_nf4_nt(const uint8_t* __restrict__ packed, const float* __restrict__ absmax, int64_t cols,
-                                   int n0, int k0, int N, int K, int aligned, const float* lut,
-                                   uint16_t* __restrict__ tile) {
-    const int tid = threadIdx.x;
-    const int r = tid >> 1, half = tid & 1;
-    const int gn = n0 + r, gk = k0 + half * 32;
-    uint16_t* dst = tile + r * BKP + half * 32;
-    if (gn < N && aligned && gk + 32 <= K) {
-        const int64_t flat = int64_t(gn) * cols + gk;
-        const uint4 w = *reinterpret_cast<const uint4*>(packed + (flat >> 1));
-        const float a = absmax[flat >> 6];
-        const uint32_t words[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            uint16_t o[8];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const uint32_t byte = (words[q] >> (8 * b)) & 0xFF;
-                o[2 * b] = f32_to_bf16_bits(lut[byte >> 4] * a);
-                o[2 * b + 1] = f32_to_bf16_bits(lut[byte & 15] * a);
-            }
-            *reinterpret_cast<uint4*>(dst + q * 8) = *reinterpret_cast<uint4*>(o);
-        }
-    } else {
-        for (int j = 0; j < 32; ++j) {
-            const int k = gk + j;
-            dst[j] = (gn < N && k < K) ? nf4_elem(packed, absmax, int64_t(gn) * cols + k, lut) : uint16_t(0);
-        }
-    }
+__device__ inline uint32_t deq2(uint32_t byte, float a, const float* lut) {
+    // byte -> bf16 pair (high nibble = even element in the low half)
+    return pack2(f32_to_bf16_bits(lut[byte >> 4] * a), f32_to_bf16_bits(lut[byte & 15] * a));
 }
 
-// NF4 weight stored [K][N] (flat k*cols + n): tile[n][k]. Each thread dequantizes
-// 4 consecutive n (2 bytes) from 8 consecutive k rows and writes 4 vectors.
-__device__ inline void load_nf4_nn(const uint8_t* __restrict__ packed, const float* __restrict__ absmax, int64_t cols,
-                                   int n0, int k0, int N, int K, int aligned, const float* lut,
-                                   uint16_t* __restrict__ tile) {
-    const int tid = threadIdx.x;
-    const int ng = (tid & 31) * 4, kg = (tid >> 5) * 8;
-    const int gn = n0 + ng;
-    uint16_t e[8][4];
+// NF4 weight stored [N][K] (flat n*cols + k): tile[n][k]. A unit is 32 codes
+// (16 bytes) of one row inside one 64-element absmax block.
+template <int R, int NT>
+struct Nf4NtLoader {
+    static constexpr int U = R * 2 / NT;
+    static_assert(U >= 1 && R * 2 % NT == 0, "nf4 nt loader shape");
+    uint4 w[U];
+    float a[U];
+    bool fast;
+    __device__ inline void load(const uint8_t* __restrict__ packed, const float* __restrict__ absmax, int64_t cols,
+                                int n0, int k0, int N, int K, int aligned) {
+        fast = aligned && n0 + R <= N && k0 + BK <= K;
+        if (!fast) return;
 #pragma unroll
-    for (int kr = 0; kr < 8; ++kr) {
-        const int gk = k0 + kg + kr;
-        if (gk < K && aligned && gn + 4 <= N) {
-            const int64_t flat = int64_t(gk) * cols + gn;
-            const uint32_t two = *reinterpret_cast<const uint16_t*>(packed + (flat >> 1));
-            const float a = absmax[flat >> 6];
-            e[kr][0] = f32_to_bf16_bits(lut[(two >> 4) & 15] * a);
-            e[kr][1] = f32_to_bf16_bits(lut[two & 15] * a);
-            e[kr][2] = f32_to_bf16_bits(lut[(two >> 12) & 15] * a);
-            e[kr][3] = f32_to_bf16_bits(lut[(two >> 8) & 15] * a);
-        } else {
+        for (int u = 0; u < U; ++u) {
+            const int idx = threadIdx.x + u * NT;
+            const int64_t flat = int64_t(n0 + (idx >> 1)) * cols + k0 + (idx & 1) * 32;
+            w[u] = *reinterpret_cast<const uint4*>(packed + (flat >> 1));
+            a[u] = absmax[flat >> 6];
+        }
+    }
+    __device__ inline void store(uint16_t* __restrict__ tile, const uint8_t* __restrict__ packed,
+                                 const float* __restrict__ absmax, int64_t cols, int n0, int k0, int N, int K,
+                                 const float* lut) const {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int idx = threadIdx.x + u * NT;
+            const int r = idx >> 1, half = idx & 1;
+            uint16_t* dst = tile + r * BKP + half * 32;
+            if (fast) {
+                const uint32_t words[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t x = words[q];
+                    *reinterpret_cast<uint4*>(dst + q * 8) =
+                        make_uint4(deq2(x & 0xFF, a[u], lut), deq2((x >> 8) & 0xFF, a[u], lut),
+                                   deq2((x >> 16) & 0xFF, a[u], lut), deq2(x >> 24, a[u], lut));
+                }
+            } else {
+                const int gn = n0 + r, gk = k0 + half * 32;
+                for (int j = 0; j < 32; ++j) {
+                    const int k = gk + j;
+                    dst[j] = (gn < N && k < K) ? uint16_t(nf4_elem(packed, absmax, int64_t(gn) * cols + k, lut))
+                                               : uint16_t(0);
+                }
+            }
+        }
+    }
+};
+
+// NF4 weight stored [K][N] (flat k*cols + n): tile[n][k]. A unit is 4
+// consecutive n (2 bytes) from each of 8 consecutive k rows.
+template <int R, int NT>
+struct Nf4NnLoader {
+    static constexpr int U = (R / 4) * (BK / 8) / NT;
+    static_assert(U >= 1 && (R / 4) * (BK / 8) % NT == 0, "nf4 nn loader shape");
+    uint32_t two[U][8];
+    float a[U][8];
+    bool fast;
+    __device__ inline void load(const uint8_t* __restrict__ packed, const float* __restrict__ absmax, int64_t cols,
+                                int n0, int k0, int N, int K, int aligned) {
+        fast = aligned && n0 + R <= N && k0 + BK <= K;
+        if (!fast) return;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int idx = threadIdx.x + u * NT;
+            const int ng = (idx % (R / 4)) * 4, kg = (idx / (R / 4)) * 8;
+#pragma unroll
+            for (int kr = 0; kr < 8; ++kr) {
+                const int64_t flat = int64_t(k0 + kg + kr) * cols + n0 + ng;
+                two[u][kr] = *reinterpret_cast<const uint16_t*>(packed + (flat >> 1));
+                a[u][kr] = absmax[flat >> 6];
+            }
+        }
+    }
+    __device__ inline void store(uint16_t* __restrict__ tile, const uint8_t* __restrict__ packed,
+                                 const float* __restrict__ absmax, int64_t cols, int n0, int k0, int N, int K,
+                                 const float* lut) const {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int idx = threadIdx.x + u * NT;
+            const int ng = (idx % (R / 4)) * 4, kg = (idx / (R / 4)) * 8;
+            uint32_t e[8][4];
+            if (fast) {
+#pragma unroll
+                for (int kr = 0; kr < 8; ++kr) {
+                    const uint32_t t = two[u][kr];
+                    const float s = a[u][kr];
+                    e[kr][0] = f32_to_bf16_bits(lut[(t >> 4) & 15] * s);
+                    e[kr][1] = f32_to_bf16_bits(lut[t & 15] * s);
+                    e[kr][2] = f32_to_bf16_bits(lut[(t >> 12) & 15] * s);
+                    e[kr][3] = f32_to_bf16_bits(lut[(t >> 8) & 15] * s);
+                }
+            } else {
+#pragma unroll
+                for (int kr = 0; kr < 8; ++kr) {
+                    const int gk = k0 + kg + kr;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int gn = n0 + ng + j;
+                        e[kr][j] = (gk < K && gn < N) ? nf4_elem(packed, absmax, int64_t(gk) * cols + gn, lut) : 0u;
+                    }
+                }
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                e[kr][j] = (gk < K && gn + j < N) ? nf4_elem(packed, absmax, int64_t(gk) * cols + gn + j, lut)
-                                                  : uint16_t(0);
+                *reinterpret_cast<uint4*>(tile + (ng + j) * BKP + kg) =
+                    make_uint4(pack2(e[0][j], e[1][j]), pack2(e[2][j], e[3][j]), pack2(e[4][j], e[5][j]),
+                               pack2(e[6][j], e[7][j]));
         }
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint4 val = make_uint4(pack2(e[0][j], e[1][j]), pack2(e[2][j], e[3][j]), pack2(e[4][j], e[5][j]),
-                                     pack2(e[6][j], e[7][j]));
-        *reinterpret_cast<uint4*>(tile + (ng + j) * BKP + kg) = val;
-    }
-}
+};
 
-// One K chunk of MFMAs: wavefront (wm, wn) owns rows wm*64.. and cols wn*64..
-template <int TE>
-__device__ inline void mma_chunk(const uint16_t* __restrict__ As, const uint16_t* __restrict__ Bs, f32x4 (&acc)[4][4],
-                                 int wm, int wn, int lane) {
+// One K chunk of MFMAs for wavefront (wm, wn) owning a WM x WN sub-tile.
+template <int TE, int WM, int WN>
+__device__ inline void mma_chunk(const uint16_t* __restrict__ As, const uint16_t* __restrict__ Bs,
+                                 f32x4 (&acc)[WM / 16][WN / 16], int wm, int wn, int lane) {
     const int lr = lane & 15, lk = (lane >> 4) * 8;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 32) {
-        uint4 a[4], b[4];
+        uint4 a[WM / 16], b[WN / 16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const uint4*>(As + (wm * 64 + i * 16 + lr) * BKP + kk + lk);
+        for (int i = 0; i < WM / 16; ++i)
+            a[i] = *reinterpret_cast<const uint4*>(As + (wm * WM + i * 16 + lr) * BKP + kk + lk);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const uint4*>(Bs + (wn * 64 + j * 16 + lr) * BKP + kk + lk);
+        for (int j = 0; j < WN / 16; ++j)
+            b[j] = *reinterpret_cast<const uint4*>(Bs + (wn * WN + j * 16 + lr) * BKP + kk + lk);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < WM / 16; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma16<TE>(a[i], b[j], acc[i][j]);
+            for (int j = 0; j < WN / 16; ++j) acc[i][j] = mfma16<TE>(a[i], b[j], acc[i][j]);
     }
 }
 
@@ -225,73 +305,180 @@ __device__ inline void store_out(const GemmParams& p, int bo, int bi, int row, i
     }
 }
 
-template <int AK, int BKIND, int TE>
-__global__ __launch_bounds__(NTHR) void k_gemm(const GemmParams p) {
-    __shared__ __align__(16) uint16_t As[BM * BKP];
-    __shared__ __align__(16) uint16_t Bs[BN * BKP];
-    __shared__ float lut[16];
+// Writes n consecutive outputs of one row starting at col (values already
+// accumulated, alpha not yet applied). Vector path for plain bf16 and fp32
+// (+ residual) rows; store_out element by element otherwise.
+__device__ inline void store_row(const GemmParams& p, int bo, int bi, int row, int col, const float* v, int n) {
+    if (p.seg_rows == 0 && !p.accumulate && col + n <= p.N && (n & 7) == 0) {
+        const int64_t off = int64_t(bo) * p.c_so + int64_t(bi) * p.c_si + int64_t(row) * p.ldc + col;
+        if (p.c_type == C_BF16 && (off & 7) == 0 && !p.R) {
+            uint16_t* dst = static_cast<uint16_t*>(p.C) + off;
+            for (int c = 0; c < n; c += 8) {
+                uint32_t w[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    w[k] = pack2(f32_to_bf16_bits(v[c + 2 * k] * p.alpha), f32_to_bf16_bits(v[c + 2 * k + 1] * p.alpha));
+                *reinterpret_cast<uint4*>(dst + c) = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+            return;
+        }
+        if (p.c_type == C_F32 && (off & 3) == 0 && (!p.R || ((int64_t(row) * p.ldr + col) & 3) == 0)) {
+            float* dst = static_cast<float*>(p.C) + off;
+            const float* r = p.R ? p.R + int64_t(row) * p.ldr + col : nullptr;
+            for (int c = 0; c < n; c += 4) {
+                float4 o = make_float4(v[c] * p.alpha, v[c + 1] * p.alpha, v[c + 2] * p.alpha, v[c + 3] * p.alpha);
+                if (r) {
+                    const float4 q = *reinterpret_cast<const float4*>(r + c);
+                    o.x += q.x;
+                    o.y += q.y;
+                    o.z += q.z;
+                    o.w += q.w;
+                }
+                *reinterpret_cast<float4*>(dst + c) = o;
+            }
+            return;
+        }
+    }
+    for (int c = 0; c < n; ++c)
+        if (col + c < p.N) store_out(p, bo, bi, row, col + c, v[c]);
+}
+
+template <int AK, int R, int NT>
+using ALoader = typename std::conditional<AK == A_ROW, RowLoader<R, NT>, TransLoader<R, NT>>::type;
+template <int BKIND, int R, int NT>
+using BLoader = typename std::conditional<
+    BKIND == B_NF4_NT, Nf4NtLoader<R, NT>,
+    typename std::conditional<BKIND == B_NF4_NN, Nf4NnLoader<R, NT>,
+                              typename std::conditional<BKIND == B_DENSE_NT, RowLoader<R, NT>,
+                                                        TransLoader<R, NT>>::type>::type>::type;
+
+template <int AK, int BKIND, int TE, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm(const GemmParams p) {
+    constexpr int NT = (BM / WM) * (BN / WN) * 64;
     constexpr bool kNf4 = (BKIND == B_NF4_NT || BKIND == B_NF4_NN);
+    __shared__ __align__(16) uint16_t As[2][BM * BKP];
+    __shared__ __align__(16) uint16_t Bs[2][BN * BKP];
+    __shared__ float lut[16];
     const int tid = threadIdx.x;
     if (kNf4 && tid < 16) lut[tid] = nf4_value(tid);
 
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-    const int split = blockIdx.z % p.splits;
-    const int bz = blockIdx.z / p.splits;
+    // tile order: the gy M-tiles of one N-tile are consecutive within an XCD
+    const int gx = (p.N + BN - 1) / BN, gy = (p.M + BM - 1) / BM;
+    const int ntile = gx * gy;
+    int t = blockIdx.x;
+    if (ntile % 8 == 0) t = (t % 8) * (ntile / 8) + t / 8;
+    const int m0 = (t % gy) * BM, n0 = (t / gy) * BN;
+    const int split = blockIdx.y % p.splits;
+    const int bz = blockIdx.y / p.splits;
     const int bo = bz / p.zdiv, bi = bz % p.zdiv;
     if (p.causal == CAUSAL_SKIP_UPPER && n0 > m0 + BM - 1) return;  // tile strictly above the diagonal
 
     const uint16_t* A = p.A + int64_t(bo) * p.a_so + int64_t(bi / p.a_grp) * p.a_si;
-    const uint16_t* Bd = static_cast<const uint16_t*>(p.B) + (kNf4 ? 0 : int64_t(bo) * p.b_so + int64_t(bi / p.b_grp) * p.b_si);
+    const uint16_t* Bd =
+        static_cast<const uint16_t*>(p.B) + (kNf4 ? 0 : int64_t(bo) * p.b_so + int64_t(bi / p.b_grp) * p.b_si);
     const uint8_t* Bq = static_cast<const uint8_t*>(p.B);
 
     int kbeg = split * p.kchunk, kend = min(p.K, kbeg + p.kchunk);
     if (p.causal == CAUSAL_K_LE_M) kend = min(kend, m0 + BM);
     if (p.causal == CAUSAL_K_GE_M) kbeg = max(kbeg, (m0 / BK) * BK);
 
-    const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-    f32x4 acc[4][4];
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / (BN / WN), wn = wave % (BN / WN);
+    f32x4 acc[WM / 16][WN / 16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WM / 16; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < WN / 16; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int k0 = kbeg; k0 < kend; k0 += BK) {
+    {
+        ALoader<AK, BM, NT> la;
+        BLoader<BKIND, BN, NT> lb;
+        __syncthreads();  // lut ready
+        if (kbeg < kend) {
+            la.load(A, p.lda, m0, kbeg, p.M, p.K, p.a_vec);
+            if constexpr (kNf4) {
+                lb.load(Bq, p.absmax, p.nf4_cols, n0, kbeg, p.N, p.K, p.b_vec);
+                lb.store(Bs[0], Bq, p.absmax, p.nf4_cols, n0, kbeg, p.N, p.K, lut);
+            } else {
+                lb.load(Bd, p.ldb, n0, kbeg, p.N, p.K, p.b_vec);
+                lb.store(Bs[0]);
+            }
+            la.store(As[0]);
+        }
         __syncthreads();
-        if (AK == A_ROW) load_rowmajor(A, p.lda, m0, k0, p.M, p.K, p.a_vec, As);
-        else load_transposed(A, p.lda, m0, k0, p.M, p.K, p.a_vec, As);
-        if (BKIND == B_NF4_NT) load_nf4_nt(Bq, p.absmax, p.nf4_cols, n0, k0, p.N, p.K, p.b_vec, lut, Bs);
-        else if (BKIND == B_NF4_NN) load_nf4_nn(Bq, p.absmax, p.nf4_cols, n0, k0, p.N, p.K, p.b_vec, lut, Bs);
-        else if (BKIND == B_DENSE_NT) load_rowmajor(Bd, p.ldb, n0, k0, p.N, p.K, p.b_vec, Bs);
-        else load_transposed(Bd, p.ldb, n0, k0, p.N, p.K, p.b_vec, Bs);
-        __syncthreads();
-        mma_chunk<TE>(As, Bs, acc, wm, wn, lane);
-    }
-    if (kNf4 && p.K2 > 0 && split == p.splits - 1) {
-        for (int k0 = 0; k0 < p.K2; k0 += BK) {
+        int buf = 0;
+        for (int k0 = kbeg; k0 < kend; k0 += BK) {
+            const int kn = k0 + BK;
+            const bool more = kn < kend;
+            if (more) {
+                la.load(A, p.lda, m0, kn, p.M, p.K, p.a_vec);
+                if constexpr (kNf4) lb.load(Bq, p.absmax, p.nf4_cols, n0, kn, p.N, p.K, p.b_vec);
+                else lb.load(Bd, p.ldb, n0, kn, p.N, p.K, p.b_vec);
+            }
+            mma_chunk<TE, WM, WN>(As[buf], Bs[buf], acc, wm, wn, lane);
+            if (more) {
+                la.store(As[buf ^ 1]);
+                if constexpr (kNf4) lb.store(Bs[buf ^ 1], Bq, p.absmax, p.nf4_cols, n0, kn, p.N, p.K, lut);
+                else lb.store(Bs[buf ^ 1]);
+            }
             __syncthreads();
-            load_rowmajor(p.A2, p.lda2, m0, k0, p.M, p.K2, p.a2_vec, As);
-            if (BKIND == B_NF4_NT) load_rowmajor(p.B2, p.ldb2, n0, k0, p.N, p.K2, p.b2_vec, Bs);
-            else load_transposed(p.B2, p.ldb2, n0, k0, p.N, p.K2, p.b2_vec, Bs);
-            __syncthreads();
-            mma_chunk<TE>(As, Bs, acc, wm, wn, lane);
+            buf ^= 1;
         }
     }
-
-    // epilogue: lane holds rows (lane/16)*4 + e of each 16x16 block, column lane%16
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = n0 + wn * 64 + j * 16 + (lane & 15);
-            if (col >= p.N) continue;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + e;
-                if (row >= p.M) continue;
-                if (p.splits > 1) p.partial[(int64_t(split) * p.M + row) * p.N + col] = acc[i][j][e];
-                else store_out(p, bo, bi, row, col, acc[i][j][e]);
+    if constexpr (kNf4) {
+        if (p.K2 > 0 && split == p.splits - 1) {
+            RowLoader<BM, NT> la;
+            typename std::conditional<BKIND == B_NF4_NT, RowLoader<BN, NT>, TransLoader<BN, NT>>::type lb;
+            for (int k0 = 0; k0 < p.K2; k0 += BK) {
+                la.load(p.A2, p.lda2, m0, k0, p.M, p.K2, p.a2_vec);
+                lb.load(p.B2, p.ldb2, n0, k0, p.N, p.K2, p.b2_vec);
+                la.store(As[0]);
+                lb.store(Bs[0]);
+                __syncthreads();
+                mma_chunk<TE, WM, WN>(As[0], Bs[0], acc, wm, wn, lane);
+                __syncthreads();
             }
         }
+    }
+
+    // epilogue: each wavefront stages one 16-row band of its sub-tile in LDS
+    // (static register indexing), then every lane writes 16 consecutive
+    // columns of one row (vector stores where the layout allows).
+    __syncthreads();
+    float* stage = reinterpret_cast<float*>(&As[0][0]) + wave * (16 * (WN + 4));
+    const int srow = lane / (64 / 16) % 16;                 // 0..15
+    const int scol = (lane % (64 / 16)) * (WN / 4);          // WN/4 columns per lane
+#pragma unroll
+    for (int i = 0; i < WM / 16; ++i) {
+#pragma unroll
+        for (int j = 0; j < WN / 16; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                stage[((lane >> 4) * 4 + e) * (WN + 4) + j * 16 + (lane & 15)] = acc[i][j][e];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int row = m0 + wm * WM + i * 16 + srow;
+        const int col0 = n0 + wn * WN + scol;
+        if (row < p.M) {
+            const float* src = stage + srow * (WN + 4) + scol;
+            if (p.splits > 1) {
+                float* dst = p.partial + (int64_t(split) * p.M + row) * p.N + col0;
+                if (col0 + WN / 4 <= p.N && (p.N & 3) == 0) {
+#pragma unroll
+                    for (int c = 0; c < WN / 4; c += 4)
+                        *reinterpret_cast<float4*>(dst + c) = make_float4(src[c], src[c + 1], src[c + 2], src[c + 3]);
+                } else {
+                    for (int c = 0; c < WN / 4; ++c)
+                        if (col0 + c < p.N) dst[c] = src[c];
+                }
+            } else {
+                store_row(p, bo, bi, row, col0, src, WN / 4);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
@@ -305,9 +492,29 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------
+struct TileCfg {
+    int bm, bn;
+};
+
+template <int AK, int BKIND, int TE, int BM, int BN, int WM, int WN>
+static void launch_cfg(const GemmParams& p, int batch_splits, hipStream_t s) {
+    const int gx = (p.N + BN - 1) / BN, gy = (p.M + BM - 1) / BM;
+    hipLaunchKernelGGL((k_gemm<AK, BKIND, TE, BM, BN, WM, WN>), dim3(gx * gy, batch_splits),
+                       dim3((BM / WM) * (BN / WN) * 64), 0, s, p);
+}
+
+// Tile shapes: NF4 GEMMs with enough rows use 256 x 128 (each weight tile is
+// dequantized half as often); everything else 128 x 128.
+static TileCfg pick_tile(const GemmParams& p, int bkind) {
+    const bool nf4 = (bkind == B_NF4_NT || bkind == B_NF4_NN);
+    if (nf4 && p.M >= 1024) return {256, 128};
+    return {128, 128};
+}
+
 template <int AK, int BKIND, int TE>
-static void launch(const GemmParams& p, dim3 grid, hipStream_t s) {
-    hipLaunchKernelGGL((k_gemm<AK, BKIND, TE>), grid, dim3(NTHR), 0, s, p);
+static void launch_kind(const GemmParams& p, TileCfg tc, int batch_splits, hipStream_t s) {
+    if (tc.bm == 256) launch_cfg<AK, BKIND, TE, 256, 128, 128, 64>(p, batch_splits, s);
+    else launch_cfg<AK, BKIND, TE, 128, 128, 64, 64>(p, batch_splits, s);
 }
 
 static bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; }
@@ -322,23 +529,24 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
     if (akind == A_ROW) p.a_vec = aligned16(p.A) && p.lda % 8 == 0 && p.a_so % 8 == 0 && p.a_si % 8 == 0;
     else p.a_vec = aligned8(p.A) && p.lda % 4 == 0 && p.a_so % 4 == 0 && p.a_si % 4 == 0;
     if (bkind == B_NF4_NT) p.b_vec = aligned16(p.B) && p.nf4_cols % 64 == 0;
-    else if (bkind == B_NF4_NN) p.b_vec = aligned16(p.B) && p.nf4_cols % 4 == 0;
+    else if (bkind == B_NF4_NN) p.b_vec = aligned16(p.B) && p.nf4_cols % 64 == 0;
     else if (bkind == B_DENSE_NT) p.b_vec = aligned16(p.B) && p.ldb % 8 == 0 && p.b_so % 8 == 0 && p.b_si % 8 == 0;
     else p.b_vec = aligned8(p.B) && p.ldb % 4 == 0 && p.b_so % 4 == 0 && p.b_si % 4 == 0;
     if (p.K2 > 0) {
         p.a2_vec = aligned16(p.A2) && p.lda2 % 8 == 0;
         p.b2_vec = (bkind == B_NF4_NT) ? (aligned16(p.B2) && p.ldb2 % 8 == 0) : (aligned8(p.B2) && p.ldb2 % 4 == 0);
     }
-    const int gx = (p.N + BN - 1) / BN, gy = (p.M + BM - 1) / BM;
-    // split-K for under-filled grids (256 CUs): shapes decide, nothing else
+    const TileCfg tc = pick_tile(p, bkind);
+    const int gx = (p.N + tc.bn - 1) / tc.bn, gy = (p.M + tc.bm - 1) / tc.bm;
+    // split-K when the grid would leave CUs idle: shapes decide, nothing else
     p.splits = 1;
     p.kchunk = ((p.K + BK - 1) / BK) * BK;
-    if (p.batch == 1 && p.causal == CAUSAL_NONE && partial_ws && p.K >= 1024) {
-        const int tiles = gx * gy;
-        int want = 512 / tiles;
-        want = std::min(want, p.K / 512);
+    const int tiles = gx * gy;
+    if (p.batch == 1 && p.causal == CAUSAL_NONE && partial_ws && tiles < 256 && p.K >= 256) {
+        int want = (512 + tiles - 1) / tiles;
+        want = std::min(want, p.K / 128);
         want = std::min(want, 16);
-        while (want > 1 && size_t(want) * tiles * BM * BN > kGemmPartialFloats) --want;
+        while (want > 1 && size_t(want) * tiles * tc.bm * tc.bn > kGemmPartialFloats) --want;
         if (want > 1) {
             const int kc = (((p.K + want - 1) / want) + BK - 1) / BK * BK;
             p.kchunk = kc;
@@ -346,8 +554,7 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
             p.partial = partial_ws;
         }
     }
-    QLX_REQUIRE(p.batch >= 1 && p.batch * p.splits <= 65535, QLX_EUNSUPPORTED, "gemm: grid.z too large");
-    dim3 grid(gx, gy, p.batch * p.splits);
+    QLX_REQUIRE(p.batch >= 1 && p.batch * p.splits <= 65535, QLX_EUNSUPPORTED, "gemm: grid too large");
     const int key = akind * 100 + bkind * 10 + te;
     // algorithmic work: multiply-adds actually needed (causal halves, no zero blocks)
     double pairs_k;
@@ -365,19 +572,30 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
                                    "gemm_bf16_tn", "gemm_f16_nt", "gemm_f16_nn", "gemm_other"};
     const int ni = key == 0 ? 0 : key == 10 ? 1 : key == 20 ? 2 : key == 30 ? 3 : key == 130 ? 4
                  : key == 21 ? 5 : key == 31 ? 6 : 7;
+    const int bsz = p.batch * p.splits;
     {
-    ProfScope prof(kNames[ni], flops, bytes, s);
-    switch (key) {
-        case A_ROW * 100 + B_NF4_NT * 10 + TE_BF16: launch<A_ROW, B_NF4_NT, TE_BF16>(p, grid, s); break;
-        case A_ROW * 100 + B_NF4_NN * 10 + TE_BF16: launch<A_ROW, B_NF4_NN, TE_BF16>(p, grid, s); break;
-        case A_ROW * 100 + B_DENSE_NT * 10 + TE_BF16: launch<A_ROW, B_DENSE_NT, TE_BF16>(p, grid, s); break;
-        case A_ROW * 100 + B_DENSE_NN * 10 + TE_BF16: launch<A_ROW, B_DENSE_NN, TE_BF16>(p, grid, s); break;
-        case A_TRANS * 100 + B_DENSE_NN * 10 + TE_BF16: launch<A_TRANS, B_DENSE_NN, TE_BF16>(p, grid, s); break;
-        case A_ROW * 100 + B_DENSE_NT * 10 + TE_F16: launch<A_ROW, B_DENSE_NT, TE_F16>(p, grid, s); break;
-        case A_ROW * 100 + B_DENSE_NN * 10 + TE_F16: launch<A_ROW, B_DENSE_NN, TE_F16>(p, grid, s); break;
-        default: throw Error{QLX_EUNSUPPORTED, "gemm: operand combination not built"};
-    }
-    check_launch("gemm");
+        ProfScope prof(kNames[ni], flops, bytes, s);
+        switch (key) {
+            case A_ROW * 100 + B_NF4_NT * 10 + TE_BF16: launch_kind<A_ROW, B_NF4_NT, TE_BF16>(p, tc, bsz, s); break;
+            case A_ROW * 100 + B_NF4_NN * 10 + TE_BF16: launch_kind<A_ROW, B_NF4_NN, TE_BF16>(p, tc, bsz, s); break;
+            case A_ROW * 100 + B_DENSE_NT * 10 + TE_BF16:
+                launch_cfg<A_ROW, B_DENSE_NT, TE_BF16, 128, 128, 64, 64>(p, bsz, s);
+                break;
+            case A_ROW * 100 + B_DENSE_NN * 10 + TE_BF16:
+                launch_cfg<A_ROW, B_DENSE_NN, TE_BF16, 128, 128, 64, 64>(p, bsz, s);
+                break;
+            case A_TRANS * 100 + B_DENSE_NN * 10 + TE_BF16:
+                launch_cfg<A_TRANS, B_DENSE_NN, TE_BF16, 128, 128, 64, 64>(p, bsz, s);
+                break;
+            case A_ROW * 100 + B_DENSE_NT * 10 + TE_F16:
+                launch_cfg<A_ROW, B_DENSE_NT, TE_F16, 128, 128, 64, 64>(p, bsz, s);
+                break;
+            case A_ROW * 100 + B_DENSE_NN * 10 + TE_F16:
+                launch_cfg<A_ROW, B_DENSE_NN, TE_F16, 128, 128, 64, 64>(p, bsz, s);
+                break;
+            default: throw Error{QLX_EUNSUPPORTED, "gemm: operand combination not built"};
+        }
+        check_launch("gemm");
     }
     if (p.splits > 1) {
         const int64_t MN = int64_t(p.M) * p.N;
