@@ -146,7 +146,7 @@ __device__ inline uint32_t nf4_elem(const uint8_t* __restrict__ packed, const fl
 
 __device__ inline uint32_t deq2(uint32_t byte, float a, const float* lut) {
     // byte -> bf16 pair (high nibble = even element in the low half)
-    return pack2(f32_to_bf16_bits(lut[byte >> 4] * a), f32_to_bf16_bits(lut[byte & 15] * a));
+    return f32x2_to_bf16x2(lut[byte >> 4] * a, lut[byte & 15] * a);
 }
 
 // NF4 weight stored [N][K] (flat n*cols + k): tile[n][k]. A unit is 32 codes
@@ -231,33 +231,40 @@ struct Nf4NnLoader {
         for (int u = 0; u < U; ++u) {
             const int idx = threadIdx.x + u * NT;
             const int ng = (idx % (R / 4)) * 4, kg = (idx / (R / 4)) * 8;
-            uint32_t e[8][4];
+            // e2[kr][h]: bf16 pair (n = ng + 2h, ng + 2h + 1) of k row kr
+            uint32_t e2[8][2];
             if (fast) {
 #pragma unroll
                 for (int kr = 0; kr < 8; ++kr) {
                     const uint32_t t = two[u][kr];
                     const float s = a[u][kr];
-                    e[kr][0] = f32_to_bf16_bits(lut[(t >> 4) & 15] * s);
-                    e[kr][1] = f32_to_bf16_bits(lut[t & 15] * s);
-                    e[kr][2] = f32_to_bf16_bits(lut[(t >> 12) & 15] * s);
-                    e[kr][3] = f32_to_bf16_bits(lut[(t >> 8) & 15] * s);
+                    e2[kr][0] = f32x2_to_bf16x2(lut[(t >> 4) & 15] * s, lut[t & 15] * s);
+                    e2[kr][1] = f32x2_to_bf16x2(lut[(t >> 12) & 15] * s, lut[(t >> 8) & 15] * s);
                 }
             } else {
 #pragma unroll
                 for (int kr = 0; kr < 8; ++kr) {
                     const int gk = k0 + kg + kr;
+                    uint32_t e[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int gn = n0 + ng + j;
-                        e[kr][j] = (gk < K && gn < N) ? nf4_elem(packed, absmax, int64_t(gk) * cols + gn, lut) : 0u;
+                        e[j] = (gk < K && gn < N) ? nf4_elem(packed, absmax, int64_t(gk) * cols + gn, lut) : 0u;
                     }
+                    e2[kr][0] = pack2(e[0], e[1]);
+                    e2[kr][1] = pack2(e[2], e[3]);
                 }
             }
+            // transpose: column j of the 8 x 4 block -> one k-contiguous vector
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j) {
+                const int h = j >> 1, sh = (j & 1) * 16;
+                uint32_t c[8];
+#pragma unroll
+                for (int kr = 0; kr < 8; ++kr) c[kr] = (e2[kr][h] >> sh) & 0xFFFFu;
                 *reinterpret_cast<uint4*>(tile + (ng + j) * BKP + kg) =
-                    make_uint4(pack2(e[0][j], e[1][j]), pack2(e[2][j], e[3][j]), pack2(e[4][j], e[5][j]),
-                               pack2(e[6][j], e[7][j]));
+                    make_uint4(pack2(c[0], c[1]), pack2(c[2], c[3]), pack2(c[4], c[5]), pack2(c[6], c[7]));
+            }
         }
     }
 };
@@ -317,7 +324,7 @@ __device__ inline void store_row(const GemmParams& p, int bo, int bi, int row, i
                 uint32_t w[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
-                    w[k] = pack2(f32_to_bf16_bits(v[c + 2 * k] * p.alpha), f32_to_bf16_bits(v[c + 2 * k + 1] * p.alpha));
+                    w[k] = f32x2_to_bf16x2(v[c + 2 * k] * p.alpha, v[c + 2 * k + 1] * p.alpha);
                 *reinterpret_cast<uint4*>(dst + c) = make_uint4(w[0], w[1], w[2], w[3]);
             }
             return;
@@ -503,11 +510,11 @@ static void launch_cfg(const GemmParams& p, int batch_splits, hipStream_t s) {
                        dim3((BM / WM) * (BN / WN) * 64), 0, s, p);
 }
 
-// Tile shapes: NF4 GEMMs with enough rows use 256 x 128 (each weight tile is
-// dequantized half as often); everything else 128 x 128.
+// Tile shapes: NF4 GEMMs with at least 512 rows use 256 x 128 (each weight
+// tile is dequantized half as often per MFMA); everything else 128 x 128.
 static TileCfg pick_tile(const GemmParams& p, int bkind) {
     const bool nf4 = (bkind == B_NF4_NT || bkind == B_NF4_NN);
-    if (nf4 && p.M >= 1024) return {256, 128};
+    if (nf4 && p.M >= 512) return {256, 128};
     return {128, 128};
 }
 
@@ -543,7 +550,8 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
     p.kchunk = ((p.K + BK - 1) / BK) * BK;
     const int tiles = gx * gy;
     if (p.batch == 1 && p.causal == CAUSAL_NONE && partial_ws && tiles < 256 && p.K >= 256) {
-        int want = (512 + tiles - 1) / tiles;
+        // about one workgroup per CU (the NF4 tiles hold one workgroup per CU)
+        int want = ((nf4 ? 256 : 512) + tiles - 1) / tiles;
         want = std::min(want, p.K / 128);
         want = std::min(want, 16);
         while (want > 1 && size_t(want) * tiles * tc.bm * tc.bn > kGemmPartialFloats) --want;

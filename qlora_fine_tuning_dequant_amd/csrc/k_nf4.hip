@@ -62,10 +62,9 @@ __global__ __launch_bounds__(256) void k_nf4_dequant(const uint8_t* __restrict__
             v[2 * b + 1] = nf4_value(byte & 15) * a;
         }
         if (OUT_BF16) {
-            uint16_t o[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = f32_to_bf16_bits(v[e]);
-            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + i0) = *reinterpret_cast<uint4*>(o);
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + i0) =
+                make_uint4(f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3]), f32x2_to_bf16x2(v[4], v[5]),
+                           f32x2_to_bf16x2(v[6], v[7]));
         } else {
             float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + i0);
             o[0] = make_float4(v[0], v[1], v[2], v[3]);

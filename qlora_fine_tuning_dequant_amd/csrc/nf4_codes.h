@@ -17,6 +17,12 @@ __device__ inline float nf4_value(int code) { return __builtin_bit_cast(float, k
 
 __device__ inline uint16_t f32_to_bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 __device__ inline uint16_t f32_to_f16_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+// Two floats -> packed bf16 pair (lo in bits 0..15), one v_cvt_pk_bf16_f32.
+__device__ inline uint32_t f32x2_to_bf16x2(float lo, float hi) {
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){lo, hi}, b2_t));
+}
 __device__ inline float bf16_bits_to_f32(uint16_t b) { return __builtin_bit_cast(float, uint32_t(b) << 16); }
 __device__ inline float f16_bits_to_f32(uint16_t b) { return float(__builtin_bit_cast(_Float16, b)); }
 }  // namespace qlx
