@@ -49,8 +49,16 @@ __device__ inline f32x4 mfma16(const uint4& a, const uint4& b, f32x4 c) {
 __device__ inline uint32_t pack2(uint32_t lo, uint32_t hi) { return (lo & 0xFFFFu) | (hi << 16); }
 
 // ---------------------------------------------------------------------------
+// Tile addressing: padded rows of BKP elements, or (SWZ) unpadded 64-element
+// rows whose 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7).
+template <bool SWZ>
+__device__ __forceinline__ int tile_off(int r, int c) {
+    if constexpr (SWZ) return r * 64 + ((c ^ ((r >> 1) & 7)) << 3);
+    else return r * BKP + c * 8;
+}
+
 // Row-major operand: tile[r][k] = src[(r0 + r) * ld + k0 + k], r < R, k < 64.
-template <int R, int NT>
+template <int R, int NT, bool SWZ = false>
 struct RowLoader {
     static constexpr int U = R * (BK / 8) / NT;
     static_assert(U >= 1 && R * (BK / 8) % NT == 0, "row loader shape");
@@ -81,14 +89,14 @@ struct RowLoader {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int idx = threadIdx.x + u * NT;
-            *reinterpret_cast<uint4*>(tile + (idx >> 3) * BKP + (idx & 7) * 8) = v[u];
+            *reinterpret_cast<uint4*>(tile + tile_off<SWZ>(idx >> 3, idx & 7)) = v[u];
         }
     }
 };
 
 // Transposed operand: tile[r][k] = src[(k0 + k) * ld + r0 + r]. A unit is 4
 // consecutive r from 8 consecutive k rows, written as 4 k-contiguous vectors.
-template <int R, int NT>
+template <int R, int NT, bool SWZ = false>
 struct TransLoader {
     static constexpr int U = (R / 4) * (BK / 8) / NT;
     static_assert(U >= 1 && (R / 4) * (BK / 8) % NT == 0, "trans loader shape");
@@ -130,7 +138,7 @@ struct TransLoader {
                 uint32_t e[8];
 #pragma unroll
                 for (int kr = 0; kr < 8; ++kr) e[kr] = ((j < 2 ? v[u][kr].x : v[u][kr].y) >> sh) & 0xFFFFu;
-                *reinterpret_cast<uint4*>(tile + (rg + j) * BKP + kg) =
+                *reinterpret_cast<uint4*>(tile + tile_off<SWZ>(rg + j, kg >> 3)) =
                     make_uint4(pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7]));
             }
         }
@@ -489,6 +497,249 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm(const GemmP
     }
 }
 
+// ---------------------------------------------------------------------------
+// Full-tile NF4 kernel (M % 256 == 0, N % 128 == 0, K % 128 == 0, 16-byte
+// aligned operands, NF4 rows a whole number of absmax blocks): a 256 x 128
+// tile on 4 wavefronts (2 x 2) of 128 x 64. LDS tiles are unpadded, with each
+// row's 16-byte chunk c stored at chunk c ^ ((row >> 1) & 7) so fragment reads
+// and stores are bank-conflict free. Operands of chunk t+2 are loaded into
+// registers while chunk t's MFMAs run and chunk t+1 is dequantized into the
+// other LDS buffer; the body is branch-free (loads past the end re-read the
+// last chunk) so the scheduler can interleave dequant VALU with the MFMAs.
+namespace fast {
+constexpr int BM = 256, BN = 128, NT = 256;
+__device__ __forceinline__ int swz(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 7)) << 3); }
+
+// A tile (256 rows x 64 k, bf16) straight from global memory into the
+// swizzled LDS layout with global_load_lds_dwordx4: each instruction writes
+// 1 KB of LDS, lane l at byte 16*l, so every lane fetches the 16 bytes that
+// belong at its slot. No registers, no VALU. The caller waits vmcnt(0) and
+// barriers before the tile is read.
+__device__ __forceinline__ void a_dma(const uint16_t* __restrict__ A, int64_t lda, int m0, int k0,
+                                      uint16_t* __restrict__ tile) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int blk = wave * 8 + u;                   // 1 KB block = 8 rows
+        const int r = blk * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);      // logical chunk stored at slot lane & 7
+        __builtin_amdgcn_global_load_lds(A + int64_t(m0 + r) * lda + k0 + c * 8, tile + blk * 512, 16, 0, 0);
+    }
+}
+// Scheduling hint for one chunk: spread the dequantization VALU and LDS
+// traffic between the 64 MFMAs instead of after them.
+__device__ __forceinline__ void interleave_hint() {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+}
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x3F70); }
+
+// NF4 [N][K]: thread = half a row's 64-element block (16 bytes, one absmax)
+struct Nf4Nt {
+    uint4 w;
+    float a;
+    __device__ __forceinline__ void load(const uint8_t* __restrict__ P, const float* __restrict__ S, int64_t cols, int n0,
+                                int k0) {
+        const int64_t flat = int64_t(n0 + (threadIdx.x >> 1)) * cols + k0 + (threadIdx.x & 1) * 32;
+        w = *reinterpret_cast<const uint4*>(P + (flat >> 1));
+        a = S[flat >> 6];
+    }
+    __device__ __forceinline__ void store(uint16_t* __restrict__ tile, const float* lut) const {
+        const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
+        const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+        uint32_t e2[4][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const uint32_t byte = (words[q] >> (8 * b)) & 0xFF;
+                e2[q][b] = f32x2_to_bf16x2(lut[byte >> 4] * a, lut[byte & 15] * a);
+            }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<uint4*>(tile + swz(r, half * 4 + q)) = make_uint4(e2[q][0], e2[q][1], e2[q][2], e2[q][3]);
+    }
+};
+
+// NF4 [K][N]: thread = 4 consecutive n from 8 consecutive k rows
+struct Nf4Nn {
+    uint32_t two[8];
+    float a[8];
+    __device__ __forceinline__ void load(const uint8_t* __restrict__ P, const float* __restrict__ S, int64_t cols, int n0,
+                                int k0) {
+        const int ng = (threadIdx.x & 31) * 4, kg = (threadIdx.x >> 5) * 8;
+#pragma unroll
+        for (int kr = 0; kr < 8; ++kr) {
+            const int64_t flat = int64_t(k0 + kg + kr) * cols + n0 + ng;
+            two[kr] = *reinterpret_cast<const uint16_t*>(P + (flat >> 1));
+            a[kr] = S[flat >> 6];
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t* __restrict__ tile, const float* lut) const {
+        const int ng = (threadIdx.x & 31) * 4, kg = (threadIdx.x >> 5) * 8;
+        uint32_t e2[8][2];
+#pragma unroll
+        for (int kr = 0; kr < 8; ++kr) {
+            const uint32_t t = two[kr];
+            e2[kr][0] = f32x2_to_bf16x2(lut[(t >> 4) & 15] * a[kr], lut[t & 15] * a[kr]);
+            e2[kr][1] = f32x2_to_bf16x2(lut[(t >> 12) & 15] * a[kr], lut[(t >> 8) & 15] * a[kr]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int h = j >> 1, sh = (j & 1) * 16;
+            uint32_t c[8];
+#pragma unroll
+            for (int kr = 0; kr < 8; ++kr) c[kr] = (e2[kr][h] >> sh) & 0xFFFFu;
+            *reinterpret_cast<uint4*>(tile + swz(ng + j, kg >> 3)) =
+                make_uint4(pack2(c[0], c[1]), pack2(c[2], c[3]), pack2(c[4], c[5]), pack2(c[6], c[7]));
+        }
+    }
+};
+
+// Fragment reads: row (base + i*16 + lr) swizzles with (lr >> 1) & 7 only, so
+// each K half (kk) has one per-lane base and every fragment is base + an
+// immediate offset.
+__device__ __forceinline__ void mma(const uint16_t* __restrict__ As, const uint16_t* __restrict__ Bs,
+                                    f32x4 (&acc)[8][4], int wm, int wn, int lane) {
+    const int lr = lane & 15, lc = lane >> 4, sw = (lr >> 1) & 7;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const int ch = ((kk * 4 + lc) ^ sw) << 3;
+        const uint16_t* ab = As + (wm * 128 + lr) * 64 + ch;
+        const uint16_t* bb = Bs + (wn * 64 + lr) * 64 + ch;
+        uint4 a[8], b[4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const uint4*>(ab + i * 16 * 64);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const uint4*>(bb + j * 16 * 64);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma16<TE_BF16>(a[i], b[j], acc[i][j]);
+    }
+}
+}  // namespace fast
+
+template <int BKIND>
+__global__ __launch_bounds__(256) void k_nf4_tile(const GemmParams p) {
+    using namespace fast;
+    using BRegs = typename std::conditional<BKIND == B_NF4_NT, Nf4Nt, Nf4Nn>::type;
+    __shared__ __align__(16) uint16_t A0[BM * 64];
+    __shared__ __align__(16) uint16_t A1[BM * 64];
+    __shared__ __align__(16) uint16_t B0[BN * 64];
+    __shared__ __align__(16) uint16_t B1[BN * 64];
+    __shared__ float lut[16];
+    const int tid = threadIdx.x;
+    if (tid < 16) lut[tid] = nf4_value(tid);
+
+    const int gx = p.N / BN, gy = p.M / BM;
+    const int ntile = gx * gy;
+    int t = blockIdx.x;
+    if (ntile % 8 == 0) t = (t % 8) * (ntile / 8) + t / 8;
+    const int m0 = (t % gy) * BM, n0 = (t / gy) * BN;
+    const int split = blockIdx.y;
+    const int kbeg = split * p.kchunk, kend = min(p.K, kbeg + p.kchunk);
+    const int nch = (kend - kbeg) / 64;  // even, >= 2
+    const uint16_t* A = p.A;
+    const uint8_t* P = static_cast<const uint8_t*>(p.B);
+    const float* S = p.absmax;
+    const int64_t cols = p.nf4_cols;
+
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // chunk t+1: A by DMA into the other LDS buffer, B into registers, both
+    // issued before chunk t's MFMAs; B is dequantized after them.
+    BRegs rb;
+    __syncthreads();  // lut
+    a_dma(A, p.lda, m0, kbeg, A0);
+    rb.load(P, S, cols, n0, kbeg);
+    rb.store(B0, lut);
+    wait_vmem_all();
+    __syncthreads();
+    for (int c = 0; c < nch; c += 2) {
+        {  // even chunk c in (A0, B0)
+            const int kn = kbeg + (c + 1) * 64;
+            a_dma(A, p.lda, m0, kn, A1);
+            rb.load(P, S, cols, n0, kn);
+            mma(A0, B0, acc, wm, wn, lane);
+            rb.store(B1, lut);
+            interleave_hint();
+            wait_vmem_all();
+            __syncthreads();
+        }
+        {  // odd chunk c+1 in (A1, B1)
+            const int kn = kbeg + min(c + 2, nch - 1) * 64;
+            a_dma(A, p.lda, m0, kn, A0);
+            rb.load(P, S, cols, n0, kn);
+            mma(A1, B1, acc, wm, wn, lane);
+            rb.store(B0, lut);
+            interleave_hint();
+            wait_vmem_all();
+            __syncthreads();
+        }
+    }
+    if (p.K2 > 0 && split == p.splits - 1) {  // LoRA slab, any K2 (zero-filled tail)
+        for (int k0 = 0; k0 < p.K2; k0 += 64) {
+            RowLoader<BM, NT, true> la;
+            la.load(p.A2, p.lda2, m0, k0, p.M, p.K2, p.a2_vec);
+            if constexpr (BKIND == B_NF4_NT) {
+                RowLoader<BN, NT, true> lb;
+                lb.load(p.B2, p.ldb2, n0, k0, p.N, p.K2, p.b2_vec);
+                lb.store(B0);
+            } else {
+                TransLoader<BN, NT, true> lb;
+                lb.load(p.B2, p.ldb2, n0, k0, p.N, p.K2, p.b2_vec);
+                lb.store(B0);
+            }
+            la.store(A0);
+            __syncthreads();
+            mma(A0, B0, acc, wm, wn, lane);
+            __syncthreads();
+        }
+    }
+
+    // epilogue (as the generic kernel): 16-row bands staged through LDS
+    constexpr int WN = 64;
+    float* stage = reinterpret_cast<float*>(A0) + wave * (16 * (WN + 4));
+    const int srow = (lane >> 2) & 15;
+    const int scol = (lane & 3) * (WN / 4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) stage[((lane >> 4) * 4 + e) * (WN + 4) + j * 16 + (lane & 15)] = acc[i][j][e];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int row = m0 + wm * 128 + i * 16 + srow;
+        const int col0 = n0 + wn * WN + scol;
+        const float* src = stage + srow * (WN + 4) + scol;
+        if (p.splits > 1) {
+            float* dst = p.partial + (int64_t(split) * p.M + row) * p.N + col0;
+#pragma unroll
+            for (int c = 0; c < WN / 4; c += 4)
+                *reinterpret_cast<float4*>(dst + c) = make_float4(src[c], src[c + 1], src[c + 2], src[c + 3]);
+        } else {
+            store_row(p, 0, 0, row, col0, src, WN / 4);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
 __global__ __launch_bounds__(256) void k_splitk_reduce(const GemmParams p) {
     const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t MN = int64_t(p.M) * p.N;
@@ -543,13 +794,28 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
         p.a2_vec = aligned16(p.A2) && p.lda2 % 8 == 0;
         p.b2_vec = (bkind == B_NF4_NT) ? (aligned16(p.B2) && p.ldb2 % 8 == 0) : (aligned8(p.B2) && p.ldb2 % 4 == 0);
     }
-    const TileCfg tc = pick_tile(p, bkind);
+    const bool fast_ok = nf4 && te == TE_BF16 && akind == A_ROW && p.batch == 1 && p.causal == CAUSAL_NONE &&
+                         p.M % 256 == 0 && p.N % 128 == 0 && p.K % 128 == 0 && p.K >= 128 && p.a_vec && p.b_vec &&
+                         (bkind == B_NF4_NT || p.nf4_cols % 4 == 0);  // never depends on the slab
+    const TileCfg tc = fast_ok ? TileCfg{256, 128} : pick_tile(p, bkind);
     const int gx = (p.N + tc.bn - 1) / tc.bn, gy = (p.M + tc.bm - 1) / tc.bm;
     // split-K when the grid would leave CUs idle: shapes decide, nothing else
     p.splits = 1;
     p.kchunk = ((p.K + BK - 1) / BK) * BK;
     const int tiles = gx * gy;
-    if (p.batch == 1 && p.causal == CAUSAL_NONE && partial_ws && tiles < 256 && p.K >= 256) {
+    if (fast_ok) {
+        // about one workgroup per CU; every split gets an even number (>= 8) of 64-wide chunks
+        if (partial_ws && tiles < 256) {
+            int want = std::min((256 + tiles - 1) / tiles, std::min(p.K / 512, 16));
+            while (want > 1 && size_t(want) * tiles * tc.bm * tc.bn > kGemmPartialFloats) --want;
+            if (want > 1) {
+                const int kc = (((p.K + want - 1) / want) + 127) / 128 * 128;
+                p.kchunk = kc;
+                p.splits = (p.K + kc - 1) / kc;
+                p.partial = partial_ws;
+            }
+        }
+    } else if (p.batch == 1 && p.causal == CAUSAL_NONE && partial_ws && tiles < 256 && p.K >= 256) {
         // about one workgroup per CU (the NF4 tiles hold one workgroup per CU)
         int want = ((nf4 ? 256 : 512) + tiles - 1) / tiles;
         want = std::min(want, p.K / 128);
@@ -584,8 +850,18 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
     {
         ProfScope prof(kNames[ni], flops, bytes, s);
         switch (key) {
-            case A_ROW * 100 + B_NF4_NT * 10 + TE_BF16: launch_kind<A_ROW, B_NF4_NT, TE_BF16>(p, tc, bsz, s); break;
-            case A_ROW * 100 + B_NF4_NN * 10 + TE_BF16: launch_kind<A_ROW, B_NF4_NN, TE_BF16>(p, tc, bsz, s); break;
+            case A_ROW * 100 + B_NF4_NT * 10 + TE_BF16:
+                if (fast_ok)
+                    hipLaunchKernelGGL(k_nf4_tile<B_NF4_NT>, dim3(tiles, p.splits), dim3(256), 0, s, p);
+                else
+                    launch_kind<A_ROW, B_NF4_NT, TE_BF16>(p, tc, bsz, s);
+                break;
+            case A_ROW * 100 + B_NF4_NN * 10 + TE_BF16:
+                if (fast_ok)
+                    hipLaunchKernelGGL(k_nf4_tile<B_NF4_NN>, dim3(tiles, p.splits), dim3(256), 0, s, p);
+                else
+                    launch_kind<A_ROW, B_NF4_NN, TE_BF16>(p, tc, bsz, s);
+                break;
             case A_ROW * 100 + B_DENSE_NT * 10 + TE_BF16:
                 launch_cfg<A_ROW, B_DENSE_NT, TE_BF16, 128, 128, 64, 64>(p, bsz, s);
                 break;

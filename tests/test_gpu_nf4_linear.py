@@ -107,7 +107,8 @@ def test_qlora_linear_fwd_bwd_vs_oracle(T, in_f, out_f, r):
     assert rel_l2(to_np(dA), 2 * dA_ref) < TOL and rel_l2(to_np(dB), 2 * dB_ref) < TOL
 
 
-@pytest.mark.parametrize("T,in_f,out_f,r", [(64, 256, 512, 8), (512, 4096, 4096, 64)])
+# (256, 512, 256, 8): full-tile kernel with a slab that is not a whole K chunk
+@pytest.mark.parametrize("T,in_f,out_f,r", [(64, 256, 512, 8), (256, 512, 256, 8), (512, 4096, 4096, 64)])
 def test_lora_zero_B_is_bit_exact_base_and_lora_off(T, in_f, out_f, r):
     wb = _w_bits(out_f, in_f, 5)
     W = q.NF4Matrix.quantize(bf16_dev(wb))
@@ -119,6 +120,14 @@ def test_lora_zero_B_is_bit_exact_base_and_lora_off(T, in_f, out_f, r):
     q.qlora_linear_fwd(x, W, A, B0, 2.0, y0)
     q.qlora_linear_fwd(x, W, None, None, 2.0, y_off)
     assert torch.equal(y0.view(torch.int16), y_off.view(torch.int16))
+    # and in the backward dX GEMM (slab du . A with B = 0 adds exact zeros)
+    dy = bf16_dev(synth.activations_bf16(6, T, out_f, 1))
+    dx0, dx_off = torch.empty(T, in_f, dtype=torch.bfloat16, device=DEV), torch.empty(T, in_f, dtype=torch.bfloat16, device=DEV)
+    dA = torch.empty(r, in_f, dtype=torch.float32, device=DEV)
+    dB = torch.empty(out_f, r, dtype=torch.float32, device=DEV)
+    q.qlora_linear_bwd(dy, x, W, A, B0, 2.0, dx0, dA, dB)
+    q.qlora_linear_bwd(dy, x, W, None, None, 2.0, dx_off, None, None)
+    assert torch.equal(dx0.view(torch.int16), dx_off.view(torch.int16))
     # and the base itself matches the oracle
     p_ref, a_ref = oracle.nf4_quantize(synth.bf16_bits_to_f32(wb))
     Wd = oracle.nf4_dequant(p_ref, a_ref, out_f * in_f).reshape(out_f, in_f)
