@@ -21,8 +21,10 @@ A [r, in], B [out, r], s = alpha / r (LoRA, Hu et al. 2021, section 4.1).
 
 Readings where the pages are silent: no dropout; no Llama-3.1 RoPE frequency
 rescaling; RMSNorm eps 1e-5; inverse frequencies theta^(-2j/hd) computed in
-fp64; the weights enter the GEMM as fp32 dequantized values (the GPU rounds
-them to bf16, which the stated tolerances cover).
+fp64; the frozen weight enters each matmul as its NF4 value rounded to bf16,
+the computation data type QLoRA dequantizes to (QLoRA paper, section 3);
+everything else (activations, LoRA adapters, reductions) stays in the
+working precision (fp32, or fp64 for the finite-difference checks).
 
 Parity pins: RMSNorm vs torch.nn.functional.rms_norm and RMS(out)=1; RoPE
 norm preservation, identity at position 0, relative-position property; causal
@@ -35,7 +37,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .nf4 import nf4_dequant
+from .nf4 import bf16_round, nf4_dequant
 
 PROJ = ("q", "k", "v", "o", "gate", "up", "down")
 
@@ -179,12 +181,16 @@ def qlora_linear_bwd(dy, x, u, W, A, B, s, need_dx=True):
 
 # Decoder layer ---------------------------------------------------------------
 def dequant_layer(layer_nf4: dict, d) -> dict:
-    """{proj: (packed, absmax)} -> {proj: fp32 W' [out, in]}."""
+    """{proj: (packed, absmax)} -> {proj: W' [out, in]}, the weight operand of
+    the layer's matmuls: the NF4 value fl32(c[code] * absmax) rounded to the
+    bf16 computation data type (QLoRA dequantizes its 4-bit storage type to
+    the 16-bit BrainFloat computation type before each matmul, section 3 and
+    equation 5 of the QLoRA paper). Values are returned as float32 arrays."""
     out = {}
     for p in PROJ:
         o, i = d.proj_shape(p)
         packed, absmax = layer_nf4[p]
-        out[p] = nf4_dequant(packed, absmax, o * i).reshape(o, i)
+        out[p] = bf16_round(nf4_dequant(packed, absmax, o * i)).reshape(o, i)
     return out
 
 

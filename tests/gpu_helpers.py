@@ -63,3 +63,45 @@ def gpu_model(q, d, seed, lora_init, std=0.02, random_gamma=False, lora_mult=1.0
 
 def oracle_lora(q_lora) -> dict:
     return {p: (to_np(q_lora.A[i]), to_np(q_lora.B[i])) for i, p in enumerate(PROJ_NAMES)}
+
+
+def run_sft(q, m, toks, mode, ctx=None):
+    """One stream_step_sft; returns (loss tensor, grads, stats)."""
+    B_ = q.binding
+    d = m.dims
+    ctx = ctx or q.Context(0)
+    grads = [q.LoraGrads(l) for l in m.lora]
+    loss = torch.empty(1, dtype=torch.float32, device=DEV)
+    ws = B_.workspace(B_.step_workspace_bytes(d, 0, toks.shape[0], toks.shape[1]))
+    q.stream_step_sft(ctx, m, torch.from_numpy(toks).to(DEV), mode, loss, grads, ws)
+    stats = ctx.sync()
+    return loss, grads, stats
+
+
+def run_dpo(q, m, ch, rj, prompt_len, beta, mode, sched, ctx=None):
+    """One stream_step_dpo; returns (loss, logps, grads, stats)."""
+    B_ = q.binding
+    d = m.dims
+    ctx = ctx or q.Context(0)
+    grads = [q.LoraGrads(l) for l in m.lora]
+    loss = torch.empty(1, dtype=torch.float32, device=DEV)
+    logps = torch.empty(4 * ch.shape[0], dtype=torch.float32, device=DEV)
+    ws = B_.workspace(B_.step_workspace_bytes(d, 1, ch.shape[0], ch.shape[1]))
+    q.stream_step_dpo(ctx, m, torch.from_numpy(ch).to(DEV), torch.from_numpy(rj).to(DEV), prompt_len, beta, mode,
+                      sched, loss, logps, grads, ws)
+    stats = ctx.sync()
+    return loss, logps, grads, stats
+
+
+def same_grads(ga, gb) -> bool:
+    return all(torch.equal(x, y) for a, b in zip(ga, gb) for x, y in zip(a.dA + a.dB, b.dA + b.dB))
+
+
+def grad_errors(grads, ref) -> dict:
+    from helpers import rel_l2
+    out = {}
+    for i, g in enumerate(grads):
+        for j, p in enumerate(PROJ_NAMES):
+            out[f"L{i}.dA_{p}"] = rel_l2(to_np(g.dA[j]), ref[i][p][0])
+            out[f"L{i}.dB_{p}"] = rel_l2(to_np(g.dB[j]), ref[i][p][1])
+    return out

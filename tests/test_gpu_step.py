@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import DEV, gpu_model, to_np
+from gpu_helpers import DEV, gpu_model, grad_errors, run_dpo, run_sft, same_grads, to_np
 from helpers import lora_list, oracle_model, rel_l2
 from synth import PROJ_NAMES
 
@@ -20,41 +20,15 @@ TOL = 2e-2
 
 
 def _sft(m, toks, mode, ctx=None):
-    d = m.dims
-    ctx = ctx or q.Context(0)
-    grads = [q.LoraGrads(l) for l in m.lora]
-    loss = torch.empty(1, dtype=torch.float32, device=DEV)
-    ws = B_.workspace(B_.step_workspace_bytes(d, 0, toks.shape[0], toks.shape[1]))
-    tok = torch.from_numpy(toks).to(DEV)
-    q.stream_step_sft(ctx, m, tok, mode, loss, grads, ws)
-    stats = ctx.sync()
-    return loss, grads, stats
+    return run_sft(q, m, toks, mode, ctx)
 
 
 def _dpo(m, ch, rj, prompt_len, beta, mode, sched, ctx=None):
-    d = m.dims
-    ctx = ctx or q.Context(0)
-    grads = [q.LoraGrads(l) for l in m.lora]
-    loss = torch.empty(1, dtype=torch.float32, device=DEV)
-    logps = torch.empty(4 * ch.shape[0], dtype=torch.float32, device=DEV)
-    ws = B_.workspace(B_.step_workspace_bytes(d, 1, ch.shape[0], ch.shape[1]))
-    q.stream_step_dpo(ctx, m, torch.from_numpy(ch).to(DEV), torch.from_numpy(rj).to(DEV), prompt_len, beta, mode,
-                      sched, loss, logps, grads, ws)
-    stats = ctx.sync()
-    return loss, logps, grads, stats
+    return run_dpo(q, m, ch, rj, prompt_len, beta, mode, sched, ctx)
 
 
-def _same(ga, gb):
-    return all(torch.equal(x, y) for a, b in zip(ga, gb) for x, y in zip(a.dA + a.dB, b.dA + b.dB))
-
-
-def _grad_errs(grads, ref):
-    out = {}
-    for i, g in enumerate(grads):
-        for j, p in enumerate(PROJ_NAMES):
-            out[f"L{i}.dA_{p}"] = rel_l2(to_np(g.dA[j]), ref[i][p][0])
-            out[f"L{i}.dB_{p}"] = rel_l2(to_np(g.dB[j]), ref[i][p][1])
-    return out
+_same = same_grads
+_grad_errs = grad_errors
 
 
 @pytest.fixture(scope="module")
