@@ -143,6 +143,46 @@ def cpu_baseline(d, batch: int, seq: int) -> dict:
                       f"step = {d.n_layers} x layer + head = {step_s:.1f} s"}
 
 
+def gemm_shapes(q) -> dict:
+    """TFLOP/s of the 8B-shaped NF4 GEMMs (LoRA off) through qlora_linear_fwd
+    (y = x W'^T) and qlora_linear_bwd (dx = dy W'), from the library's events."""
+    import torch
+    B_ = q.binding
+    dev = "cuda:0"
+    shapes = {"qkv": (4096, 6144), "o": (4096, 4096), "gate_up": (4096, 28672), "down": (14336, 4096)}
+    g = torch.Generator(device=dev).manual_seed(0)
+    out = {}
+    for T in (512, 2048):
+        for name, (K, N) in shapes.items():
+            W = q.NF4Matrix.quantize((torch.randn(N, K, device=dev, generator=g) * 0.02).to(torch.bfloat16))
+            x = torch.randn(T, K, device=dev, generator=g).to(torch.bfloat16)
+            dy = torch.randn(T, N, device=dev, generator=g).to(torch.bfloat16)
+            y = torch.empty(T, N, device=dev, dtype=torch.bfloat16)
+            dx = torch.empty(T, K, device=dev, dtype=torch.bfloat16)
+            ws = B_.workspace(B_.linear_workspace_bytes(T, K, N, 0))
+            for _ in range(3):
+                q.qlora_linear_fwd(x, W, None, None, 1.0, y, ws)
+                q.qlora_linear_bwd(dy, x, W, None, None, 1.0, dx, None, None, ws=ws)
+            torch.cuda.synchronize()
+            B_.profile_begin()
+            for _ in range(10):
+                q.qlora_linear_fwd(x, W, None, None, 1.0, y, ws)
+            for _ in range(10):
+                q.qlora_linear_bwd(dy, x, W, None, None, 1.0, dx, None, None, ws=ws)
+            torch.cuda.synchronize()
+            pr = B_.profile_end()
+            row = {}
+            for k, lab in (("gemm_nf4_nt", "fwd"), ("gemm_nf4_nn", "dx")):
+                v = pr[k]
+                row[lab + "_us"] = round(1000 * v["ms"] / v["launches"], 1)
+                row[lab + "_TFLOPs"] = round(v["flops"] / v["ms"] / 1e9, 1)
+            if "splitk_reduce" in pr:
+                row["splitk_reduce_us_per_launch"] = round(1000 * pr["splitk_reduce"]["ms"] / pr["splitk_reduce"]["launches"], 1)
+            out[f"T{T}_{name}"] = row
+            log(f"gemm T={T} {name}: {row}")
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,8 +190,14 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="sft8b_b1", choices=sorted(WORKLOADS))
     ap.add_argument("--mode", default="streamed", choices=["streamed", "resident"])
+    ap.add_argument("--dpo-ref", default="fused", choices=["fused", "separate"],
+                    help="DPO reference schedule: fused with the policy forward, or a separate pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timing")
+    ap.add_argument("--gemm-shapes", action="store_true",
+                    help="only time the 8B-shaped NF4 GEMMs (fwd and dX) at 512 and 2048 tokens")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of 1 GiB five times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).",
@@ -161,9 +207,23 @@ def main() -> int:
     import numpy as np
     import torch
 
+    if args.copy_calibration:
+        n = 1 << 29  # 2^29 bf16 = 1 GiB read + 1 GiB written per copy
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read_per_copy": 2 * n, "bytes_written_per_copy": 2 * n,
+                                               "copies": 5}}))
+        return 0
+
     import qlora_fine_tuning_dequant_amd as q
     import synth
     B_ = q.binding
+    if args.gemm_shapes:
+        print(json.dumps({"gemm_shapes": gemm_shapes(q)}))
+        return 0
     wl = WORKLOADS[args.workload]
     d = synth.LLAMA8B
     dev = "cuda:0"
@@ -191,12 +251,12 @@ def main() -> int:
         ch, rj = synth.dpo_pairs(SEED, pairs, seq, wl["prompt"], d.vocab)
         ch, rj = torch.from_numpy(ch).to(dev), torch.from_numpy(rj).to(dev)
         logps = torch.empty(4 * pairs, dtype=torch.float32, device=dev)
+        sched = B_.QLX_DPO_REF_FUSED if args.dpo_ref == "fused" else B_.QLX_DPO_REF_SEPARATE
         ws = B_.workspace(B_.step_workspace_bytes(d, 1, pairs, seq))
         tokens_per_step = 2 * pairs * seq
 
         def step():
-            q.stream_step_dpo(ctx, m, ch, rj, wl["prompt"], wl["beta"], mode, B_.QLX_DPO_REF_FUSED, loss, logps,
-                              grads, ws)
+            q.stream_step_dpo(ctx, m, ch, rj, wl["prompt"], wl["beta"], mode, sched, loss, logps, grads, ws)
 
     for i in range(args.warmup):
         step()
@@ -241,7 +301,8 @@ def main() -> int:
         "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl["name"], "global_batch": batch if wl["kind"] == "sft" else 2 * batch,
-                   "seq_len": seq, "mode": args.mode, "layers": d.n_layers, "lora_r": d.lora_r},
+                   "seq_len": seq, "mode": args.mode, "layers": d.n_layers, "lora_r": d.lora_r,
+                   **({"dpo_reference": args.dpo_ref} if wl["kind"] == "dpo" else {})},
         "roofline": roofline,
         "stream": {"layer_reads_per_step": reads, "h2d_GB_per_step": round(h2d_bytes / 1e9, 3),
                    "h2d_ms_per_step": round(h2d_ms, 2),
