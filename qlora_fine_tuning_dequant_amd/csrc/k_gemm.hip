@@ -498,144 +498,160 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm(const GemmP
 }
 
 // ---------------------------------------------------------------------------
-// Full-tile NF4 kernel (M % 256 == 0, N % 128 == 0, K % 128 == 0, 16-byte
+// Full-tile NF4 kernel (M % 256 == 0, N % 128 == 0, K % 64 == 0, 16-byte
 // aligned operands, NF4 rows a whole number of absmax blocks): a 256 x 128
-// tile on 4 wavefronts (2 x 2) of 128 x 64. LDS tiles are unpadded, with each
-// row's 16-byte chunk c stored at chunk c ^ ((row >> 1) & 7) so fragment reads
-// and stores are bank-conflict free. Operands of chunk t+2 are loaded into
-// registers while chunk t's MFMAs run and chunk t+1 is dequantized into the
-// other LDS buffer; the body is branch-free (loads past the end re-read the
-// last chunk) so the scheduler can interleave dequant VALU with the MFMAs.
+// tile on 8 wavefronts (4 x 2, two per SIMD) of 64 x 64, so one wavefront's
+// dequantization and LDS traffic overlaps the other's MFMAs.
+//
+// Every global read goes straight into LDS (global_load_lds): per 64-wide K
+// chunk the A tile (32 KB), the weight tile's packed codes (4 KB) and its
+// absmax values (512 B). A runs two chunks ahead and the codes three, in
+// three LDS stages each, so a stage has about two chunks of MFMA time to
+// arrive; the waits are explicit vmcnt counts that leave the newer stages in
+// flight (the compiler's own barrier would wait for everything). During chunk
+// t's MFMAs each thread dequantizes 16 elements of chunk t+1: one LDS read of
+// the packed codes, one 8-byte LDS lookup per code byte in a 256-entry table
+// of value pairs, two fp32 multiplies by the block absmax and one paired bf16
+// conversion, then 16-byte LDS writes into the swizzled bf16 tile.
+// LDS tiles are unpadded; the 16-byte chunk c of row r is stored at chunk
+// c ^ ((r >> 1) & 7), so fragment reads are conflict-free and each fragment
+// address is a per-lane base plus an immediate offset.
 namespace fast {
-constexpr int BM = 256, BN = 128, NT = 256;
+constexpr int BM = 256, BN = 128, NTH = 512, NW = 8, WGN = 2, WM = 64, WN = 64, FI = WM / 16, FJ = WN / 16;
+constexpr int SA = BM * 64 * 2, SB = BN * 64 * 2, SR = BN * 32, SS = 512;  // bytes per stage
+constexpr int OFF_A = 0, OFF_B = 3 * SA, OFF_R = OFF_B + 3 * SB, OFF_S = OFF_R + 3 * SR, OFF_L = OFF_S + 3 * SS;
+constexpr int LDS_BYTES = OFF_L + 256 * 8;
+static_assert(LDS_BYTES <= 160 * 1024, "fast NF4 tile exceeds LDS");
+constexpr int NA = BM / 8 / NW;  // 16-byte A DMAs per thread per chunk
+constexpr int NR = 2;            // code + absmax DMAs per thread per chunk
+
+typedef float f2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ int swz(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 7)) << 3); }
 
-// A tile (256 rows x 64 k, bf16) straight from global memory into the
-// swizzled LDS layout with global_load_lds_dwordx4: each instruction writes
-// 1 KB of LDS, lane l at byte 16*l, so every lane fetches the 16 bytes that
-// belong at its slot. No registers, no VALU. The caller waits vmcnt(0) and
-// barriers before the tile is read.
+// s_waitcnt vmcnt(VM) lgkmcnt(0), then a workgroup barrier that does not
+// drain the DMA queue (the "memory" clobber keeps LDS accesses on their side)
+template <int VM>
+__device__ __forceinline__ void stage_sync() {
+    static_assert(VM >= 0 && VM < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (0x7 << 4));
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// A tile (256 rows x 64 k, bf16): each wavefront moves 4 KB; one instruction
+// writes 1 KB of LDS (lane l at byte 16 l), so each lane fetches the 16 bytes
+// that belong in its slot of the swizzled layout.
 __device__ __forceinline__ void a_dma(const uint16_t* __restrict__ A, int64_t lda, int m0, int k0,
-                                      uint16_t* __restrict__ tile) {
+                                      char* __restrict__ dst) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint16_t* tile = reinterpret_cast<uint16_t*>(dst);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        const int blk = wave * 8 + u;                   // 1 KB block = 8 rows
+    for (int u = 0; u < NA; ++u) {
+        const int blk = wave * NA + u;
         const int r = blk * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ ((r >> 1) & 7);      // logical chunk stored at slot lane & 7
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
         __builtin_amdgcn_global_load_lds(A + int64_t(m0 + r) * lda + k0 + c * 8, tile + blk * 512, 16, 0, 0);
     }
 }
-// Scheduling hint for one chunk: spread the dequantization VALU and LDS
-// traffic between the 64 MFMAs instead of after them.
-__device__ __forceinline__ void interleave_hint() {
-#pragma unroll
-    for (int i = 0; i < 64; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+
+// Packed codes and absmax of one weight chunk, in natural order: NT [128 n][32 B]
+// with one absmax per row; NN [64 k][64 B] with two absmax per row. Every
+// wavefront issues exactly one 16-byte DMA (32 lanes) and one 4-byte DMA
+// (16 lanes), so the per-wavefront vmcnt bookkeeping is the same everywhere.
+template <int BKIND>
+__device__ __forceinline__ void code_dma(const uint8_t* __restrict__ P, const float* __restrict__ S, int64_t cols,
+                                         int n0, int k0, char* __restrict__ raw, char* __restrict__ sc) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane < 32) {
+        const int q = wave * 32 + lane;
+        int64_t byte;
+        if constexpr (BKIND == B_NF4_NN) byte = ((int64_t(k0 + (q >> 2)) * cols + n0) >> 1) + (q & 3) * 16;
+        else byte = ((int64_t(n0 + (q >> 1)) * cols + k0) >> 1) + (q & 1) * 16;
+        __builtin_amdgcn_global_load_lds(P + byte, raw + wave * 512, 16, 0, 0);
+    }
+    if (lane < 16) {
+        const int q = wave * 16 + lane;
+        int64_t blk;
+        if constexpr (BKIND == B_NF4_NN) blk = ((int64_t(k0 + (q >> 1)) * cols + n0) >> 6) + (q & 1);
+        else blk = (int64_t(n0 + q) * cols + k0) >> 6;
+        __builtin_amdgcn_global_load_lds(S + blk, sc + wave * 64, 4, 0, 0);
     }
 }
-// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
-__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x3F70); }
 
-// NF4 [N][K]: thread = half a row's 64-element block (16 bytes, one absmax)
-struct Nf4Nt {
-    uint4 w;
-    float a;
-    __device__ __forceinline__ void load(const uint8_t* __restrict__ P, const float* __restrict__ S, int64_t cols, int n0,
-                                int k0) {
-        const int64_t flat = int64_t(n0 + (threadIdx.x >> 1)) * cols + k0 + (threadIdx.x & 1) * 32;
-        w = *reinterpret_cast<const uint4*>(P + (flat >> 1));
-        a = S[flat >> 6];
-    }
-    __device__ __forceinline__ void store(uint16_t* __restrict__ tile, const float* lut) const {
-        const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
-        const uint32_t words[4] = {w.x, w.y, w.z, w.w};
-        uint32_t e2[4][4];
+// Codes of one chunk (LDS) -> bf16 tile [n][k] (LDS). lut2[b] holds the code
+// values of byte b's high nibble (the even element) and low nibble.
+template <int BKIND>
+__device__ __forceinline__ void dequant(const char* __restrict__ raw, const char* __restrict__ sc,
+                                        const f2* __restrict__ lut2, uint16_t* __restrict__ tile) {
+    const int t = threadIdx.x;
+    const float* s = reinterpret_cast<const float*>(sc);
+    if constexpr (BKIND == B_NF4_NT) {
+        // thread = 16 consecutive k of row t >> 2
+        const int r = t >> 2, q4 = t & 3;
+        const uint2 w = *reinterpret_cast<const uint2*>(raw + r * 32 + q4 * 8);
+        const float a = s[r];
+        uint32_t e[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const uint32_t byte = (words[q] >> (8 * b)) & 0xFF;
-                e2[q][b] = f32x2_to_bf16x2(lut[byte >> 4] * a, lut[byte & 15] * a);
-            }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<uint4*>(tile + swz(r, half * 4 + q)) = make_uint4(e2[q][0], e2[q][1], e2[q][2], e2[q][3]);
-    }
-};
-
-// NF4 [K][N]: thread = 4 consecutive n from 8 consecutive k rows
-struct Nf4Nn {
-    uint32_t two[8];
-    float a[8];
-    __device__ __forceinline__ void load(const uint8_t* __restrict__ P, const float* __restrict__ S, int64_t cols, int n0,
-                                int k0) {
-        const int ng = (threadIdx.x & 31) * 4, kg = (threadIdx.x >> 5) * 8;
-#pragma unroll
-        for (int kr = 0; kr < 8; ++kr) {
-            const int64_t flat = int64_t(k0 + kg + kr) * cols + n0 + ng;
-            two[kr] = *reinterpret_cast<const uint16_t*>(P + (flat >> 1));
-            a[kr] = S[flat >> 6];
+        for (int b = 0; b < 8; ++b) {
+            const f2 v = lut2[((b < 4 ? w.x : w.y) >> (8 * (b & 3))) & 0xFF];
+            e[b] = f32x2_to_bf16x2(v.x * a, v.y * a);
         }
-    }
-    __device__ __forceinline__ void store(uint16_t* __restrict__ tile, const float* lut) const {
-        const int ng = (threadIdx.x & 31) * 4, kg = (threadIdx.x >> 5) * 8;
-        uint32_t e2[8][2];
+        *reinterpret_cast<uint4*>(tile + swz(r, 2 * q4)) = make_uint4(e[0], e[1], e[2], e[3]);
+        *reinterpret_cast<uint4*>(tile + swz(r, 2 * q4 + 1)) = make_uint4(e[4], e[5], e[6], e[7]);
+    } else {
+        // thread = 4 consecutive n x 4 consecutive k; pairs along k convert together
+        const int ng = (t & 31) * 4, kg = (t >> 5) * 4;
+        f2 v[4][2];
+        float a[4];
 #pragma unroll
-        for (int kr = 0; kr < 8; ++kr) {
-            const uint32_t t = two[kr];
-            e2[kr][0] = f32x2_to_bf16x2(lut[(t >> 4) & 15] * a[kr], lut[t & 15] * a[kr]);
-            e2[kr][1] = f32x2_to_bf16x2(lut[(t >> 12) & 15] * a[kr], lut[(t >> 8) & 15] * a[kr]);
+        for (int kr = 0; kr < 4; ++kr) {
+            const uint32_t two = *reinterpret_cast<const uint16_t*>(raw + (kg + kr) * 64 + (ng >> 1));
+            a[kr] = s[(kg + kr) * 2 + (ng >> 6)];
+            v[kr][0] = lut2[two & 0xFF];
+            v[kr][1] = lut2[two >> 8];
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int h = j >> 1, sh = (j & 1) * 16;
-            uint32_t c[8];
+            float x[4];
 #pragma unroll
-            for (int kr = 0; kr < 8; ++kr) c[kr] = (e2[kr][h] >> sh) & 0xFFFFu;
-            *reinterpret_cast<uint4*>(tile + swz(ng + j, kg >> 3)) =
-                make_uint4(pack2(c[0], c[1]), pack2(c[2], c[3]), pack2(c[4], c[5]), pack2(c[6], c[7]));
+            for (int kr = 0; kr < 4; ++kr) x[kr] = ((j & 1) ? v[kr][j >> 1].y : v[kr][j >> 1].x) * a[kr];
+            *reinterpret_cast<uint2*>(tile + swz(ng + j, kg >> 3) + (kg & 4)) =
+                make_uint2(f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3]));
         }
     }
-};
+}
 
-// Fragment reads: row (base + i*16 + lr) swizzles with (lr >> 1) & 7 only, so
-// each K half (kk) has one per-lane base and every fragment is base + an
-// immediate offset.
+// One chunk of MFMAs for a 64 x 64 wavefront tile. Row (base + i*16 + lr)
+// swizzles with (lr >> 1) & 7 only, so each K half has one per-lane base.
 __device__ __forceinline__ void mma(const uint16_t* __restrict__ As, const uint16_t* __restrict__ Bs,
-                                    f32x4 (&acc)[8][4], int wm, int wn, int lane) {
+                                    f32x4 (&acc)[FI][FJ], int rm, int rn, int lane) {
     const int lr = lane & 15, lc = lane >> 4, sw = (lr >> 1) & 7;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
         const int ch = ((kk * 4 + lc) ^ sw) << 3;
-        const uint16_t* ab = As + (wm * 128 + lr) * 64 + ch;
-        const uint16_t* bb = Bs + (wn * 64 + lr) * 64 + ch;
-        uint4 a[8], b[4];
+        const uint16_t* ab = As + (rm + lr) * 64 + ch;
+        const uint16_t* bb = Bs + (rn + lr) * 64 + ch;
+        uint4 a[FI], b[FJ];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const uint4*>(ab + i * 16 * 64);
+        for (int i = 0; i < FI; ++i) a[i] = *reinterpret_cast<const uint4*>(ab + i * 16 * 64);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const uint4*>(bb + j * 16 * 64);
+        for (int j = 0; j < FJ; ++j) b[j] = *reinterpret_cast<const uint4*>(bb + j * 16 * 64);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < FI; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma16<TE_BF16>(a[i], b[j], acc[i][j]);
+            for (int j = 0; j < FJ; ++j) acc[i][j] = mfma16<TE_BF16>(a[i], b[j], acc[i][j]);
     }
 }
 }  // namespace fast
 
 template <int BKIND>
-__global__ __launch_bounds__(256) void k_nf4_tile(const GemmParams p) {
+__global__ __launch_bounds__(fast::NTH) void k_nf4_tile(const GemmParams p) {
     using namespace fast;
-    using BRegs = typename std::conditional<BKIND == B_NF4_NT, Nf4Nt, Nf4Nn>::type;
-    __shared__ __align__(16) uint16_t A0[BM * 64];
-    __shared__ __align__(16) uint16_t A1[BM * 64];
-    __shared__ __align__(16) uint16_t B0[BN * 64];
-    __shared__ __align__(16) uint16_t B1[BN * 64];
-    __shared__ float lut[16];
-    const int tid = threadIdx.x;
-    if (tid < 16) lut[tid] = nf4_value(tid);
+    extern __shared__ __align__(16) char lds[];
+    f2* lut2 = reinterpret_cast<f2*>(lds + OFF_L);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    if (tid < 256) lut2[tid] = f2{nf4_value(tid >> 4), nf4_value(tid & 15)};
 
     const int gx = p.N / BN, gy = p.M / BM;
     const int ntile = gx * gy;
@@ -644,86 +660,84 @@ __global__ __launch_bounds__(256) void k_nf4_tile(const GemmParams p) {
     const int m0 = (t % gy) * BM, n0 = (t / gy) * BN;
     const int split = blockIdx.y;
     const int kbeg = split * p.kchunk, kend = min(p.K, kbeg + p.kchunk);
-    const int nch = (kend - kbeg) / 64;  // even, >= 2
+    const int nch = (kend - kbeg) / 64;  // >= 1
     const uint16_t* A = p.A;
     const uint8_t* P = static_cast<const uint8_t*>(p.B);
     const float* S = p.absmax;
     const int64_t cols = p.nf4_cols;
 
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    f32x4 acc[8][4];
+    f32x4 acc[FI][FJ];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < FI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // chunk t+1: A by DMA into the other LDS buffer, B into registers, both
-    // issued before chunk t's MFMAs; B is dequantized after them.
-    BRegs rb;
-    __syncthreads();  // lut
-    a_dma(A, p.lda, m0, kbeg, A0);
-    rb.load(P, S, cols, n0, kbeg);
-    rb.store(B0, lut);
-    wait_vmem_all();
-    __syncthreads();
-    for (int c = 0; c < nch; c += 2) {
-        {  // even chunk c in (A0, B0)
-            const int kn = kbeg + (c + 1) * 64;
-            a_dma(A, p.lda, m0, kn, A1);
-            rb.load(P, S, cols, n0, kn);
-            mma(A0, B0, acc, wm, wn, lane);
-            rb.store(B1, lut);
-            interleave_hint();
-            wait_vmem_all();
-            __syncthreads();
-        }
-        {  // odd chunk c+1 in (A1, B1)
-            const int kn = kbeg + min(c + 2, nch - 1) * 64;
-            a_dma(A, p.lda, m0, kn, A0);
-            rb.load(P, S, cols, n0, kn);
-            mma(A1, B1, acc, wm, wn, lane);
-            rb.store(B0, lut);
-            interleave_hint();
-            wait_vmem_all();
-            __syncthreads();
-        }
+    // chunk c reads A stage c % 3 and bf16 stage c % 3; loads past the end
+    // re-read the last chunk into stages nobody reads again
+    auto kc = [&](int c) { return kbeg + min(c, nch - 1) * 64; };
+    auto sa = [&](int s) { return lds + OFF_A + s * SA; };
+    auto sb = [&](int s) { return reinterpret_cast<uint16_t*>(lds + OFF_B + s * SB); };
+    auto sr = [&](int s) { return lds + OFF_R + s * SR; };
+    auto ss = [&](int s) { return lds + OFF_S + s * SS; };
+    code_dma<BKIND>(P, S, cols, n0, kc(0), sr(0), ss(0));
+    a_dma(A, p.lda, m0, kc(0), sa(0));
+    code_dma<BKIND>(P, S, cols, n0, kc(1), sr(1), ss(1));
+    a_dma(A, p.lda, m0, kc(1), sa(1));
+    code_dma<BKIND>(P, S, cols, n0, kc(2), sr(2), ss(2));
+    stage_sync<2 * NA + 2 * NR>();  // codes 0 (and the table) in LDS
+    dequant<BKIND>(sr(0), ss(0), lut2, sb(0));
+    stage_sync<NA + NR>();          // A 0, codes 1, bf16 0
+    auto step = [&](int c, auto stage) {
+        constexpr int S0 = decltype(stage)::value, S1 = (S0 + 1) % 3, S2 = (S0 + 2) % 3;
+        a_dma(A, p.lda, m0, kc(c + 2), sa(S2));
+        code_dma<BKIND>(P, S, cols, n0, kc(c + 3), sr(S0), ss(S0));
+        mma(reinterpret_cast<const uint16_t*>(sa(S0)), sb(S0), acc, wm * WM, wn * WN, lane);
+        dequant<BKIND>(sr(S1), ss(S1), lut2, sb(S1));
+        stage_sync<NA + NR>();      // A c+1, codes c+2, bf16 c+1
+    };
+    for (int c = 0; c < nch; c += 3) {
+        step(c, std::integral_constant<int, 0>());
+        if (c + 1 < nch) step(c + 1, std::integral_constant<int, 1>());
+        if (c + 2 < nch) step(c + 2, std::integral_constant<int, 2>());
     }
+    stage_sync<0>();
+
     if (p.K2 > 0 && split == p.splits - 1) {  // LoRA slab, any K2 (zero-filled tail)
+        uint16_t* As0 = reinterpret_cast<uint16_t*>(sa(0));
+        uint16_t* Bs0 = sb(0);
         for (int k0 = 0; k0 < p.K2; k0 += 64) {
-            RowLoader<BM, NT, true> la;
+            RowLoader<BM, NTH, true> la;
             la.load(p.A2, p.lda2, m0, k0, p.M, p.K2, p.a2_vec);
             if constexpr (BKIND == B_NF4_NT) {
-                RowLoader<BN, NT, true> lb;
+                RowLoader<BN, NTH, true> lb;
                 lb.load(p.B2, p.ldb2, n0, k0, p.N, p.K2, p.b2_vec);
-                lb.store(B0);
-            } else {
-                TransLoader<BN, NT, true> lb;
+                lb.store(Bs0);
+            } else if (tid < 256) {
+                TransLoader<BN, 256, true> lb;
                 lb.load(p.B2, p.ldb2, n0, k0, p.N, p.K2, p.b2_vec);
-                lb.store(B0);
+                lb.store(Bs0);
             }
-            la.store(A0);
+            la.store(As0);
             __syncthreads();
-            mma(A0, B0, acc, wm, wn, lane);
+            mma(As0, Bs0, acc, wm * WM, wn * WN, lane);
             __syncthreads();
         }
     }
 
-    // epilogue (as the generic kernel): 16-row bands staged through LDS
-    constexpr int WN = 64;
-    float* stage = reinterpret_cast<float*>(A0) + wave * (16 * (WN + 4));
+    // epilogue: 16-row bands staged through LDS, 16 consecutive columns per lane
+    float* stage = reinterpret_cast<float*>(lds + OFF_A) + wave * (16 * (WN + 4));
     const int srow = (lane >> 2) & 15;
     const int scol = (lane & 3) * (WN / 4);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < FI; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < FJ; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) stage[((lane >> 4) * 4 + e) * (WN + 4) + j * 16 + (lane & 15)] = acc[i][j][e];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int row = m0 + wm * 128 + i * 16 + srow;
+        const int row = m0 + wm * WM + i * 16 + srow;
         const int col0 = n0 + wn * WN + scol;
         const float* src = stage + srow * (WN + 4) + scol;
         if (p.splits > 1) {
@@ -776,6 +790,22 @@ static void launch_kind(const GemmParams& p, TileCfg tc, int batch_splits, hipSt
 }
 
 static bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; }
+
+// The full-tile kernel takes 160 KB of dynamic LDS, which each device has to
+// allow once per kernel before the first launch.
+template <int BKIND>
+static void launch_fast(const GemmParams& p, int tiles, hipStream_t s) {
+    static bool allowed[64] = {};
+    int dev = 0;
+    QLX_CHECK_HIP(hipGetDevice(&dev));
+    QLX_REQUIRE(dev >= 0 && dev < 64, QLX_EUNSUPPORTED, "gemm: device index out of range");
+    if (!allowed[dev]) {
+        QLX_CHECK_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_nf4_tile<BKIND>),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, fast::LDS_BYTES));
+        allowed[dev] = true;
+    }
+    hipLaunchKernelGGL(k_nf4_tile<BKIND>, dim3(tiles, p.splits), dim3(fast::NTH), fast::LDS_BYTES, s, p);
+}
 static bool aligned8(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 7) == 0; }
 
 void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStream_t s) {
@@ -795,21 +825,21 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
         p.b2_vec = (bkind == B_NF4_NT) ? (aligned16(p.B2) && p.ldb2 % 8 == 0) : (aligned8(p.B2) && p.ldb2 % 4 == 0);
     }
     const bool fast_ok = nf4 && te == TE_BF16 && akind == A_ROW && p.batch == 1 && p.causal == CAUSAL_NONE &&
-                         p.M % 256 == 0 && p.N % 128 == 0 && p.K % 128 == 0 && p.K >= 128 && p.a_vec && p.b_vec &&
-                         (bkind == B_NF4_NT || p.nf4_cols % 4 == 0);  // never depends on the slab
-    const TileCfg tc = fast_ok ? TileCfg{256, 128} : pick_tile(p, bkind);
+                         p.M % fast::BM == 0 && p.N % fast::BN == 0 && p.K % 64 == 0 && p.K >= 64 && p.a_vec &&
+                         p.b_vec && aligned16(p.absmax) && p.nf4_cols % 64 == 0;  // never depends on the slab
+    const TileCfg tc = fast_ok ? TileCfg{fast::BM, fast::BN} : pick_tile(p, bkind);
     const int gx = (p.N + tc.bn - 1) / tc.bn, gy = (p.M + tc.bm - 1) / tc.bm;
     // split-K when the grid would leave CUs idle: shapes decide, nothing else
     p.splits = 1;
     p.kchunk = ((p.K + BK - 1) / BK) * BK;
     const int tiles = gx * gy;
     if (fast_ok) {
-        // about one workgroup per CU; every split gets an even number (>= 8) of 64-wide chunks
+        // about one workgroup per CU; every split gets at least 8 64-wide chunks
         if (partial_ws && tiles < 256) {
             int want = std::min((256 + tiles - 1) / tiles, std::min(p.K / 512, 16));
             while (want > 1 && size_t(want) * tiles * tc.bm * tc.bn > kGemmPartialFloats) --want;
             if (want > 1) {
-                const int kc = (((p.K + want - 1) / want) + 127) / 128 * 128;
+                const int kc = (((p.K + want - 1) / want) + 63) / 64 * 64;
                 p.kchunk = kc;
                 p.splits = (p.K + kc - 1) / kc;
                 p.partial = partial_ws;
@@ -852,13 +882,13 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
         switch (key) {
             case A_ROW * 100 + B_NF4_NT * 10 + TE_BF16:
                 if (fast_ok)
-                    hipLaunchKernelGGL(k_nf4_tile<B_NF4_NT>, dim3(tiles, p.splits), dim3(256), 0, s, p);
+                    launch_fast<B_NF4_NT>(p, tiles, s);
                 else
                     launch_kind<A_ROW, B_NF4_NT, TE_BF16>(p, tc, bsz, s);
                 break;
             case A_ROW * 100 + B_NF4_NN * 10 + TE_BF16:
                 if (fast_ok)
-                    hipLaunchKernelGGL(k_nf4_tile<B_NF4_NN>, dim3(tiles, p.splits), dim3(256), 0, s, p);
+                    launch_fast<B_NF4_NN>(p, tiles, s);
                 else
                     launch_kind<A_ROW, B_NF4_NN, TE_BF16>(p, tc, bsz, s);
                 break;
