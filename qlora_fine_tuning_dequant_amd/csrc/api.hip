@@ -532,6 +532,7 @@ static void head_logits(const qlx_model* m, const float* hL, int T, StepWs& w, f
     p.C = w.logits;
     p.ldc = d.vocab;
     p.c_type = C_F32;
+    p.tag = "gemm_head";
     gemm(p, A_ROW, B_DENSE_NT, TE_F16, partial, s);
 }
 // dh = RMSNorm^T( (dz . head) * alpha )
@@ -550,6 +551,7 @@ static void head_backward(const qlx_model* m, const float* hL, int T, float alph
     p.ldc = d.hidden;
     p.c_type = C_F32;
     p.alpha = alpha;
+    p.tag = "gemm_head_dx";
     gemm(p, A_ROW, B_DENSE_NN, TE_F16, partial, s);
     launch_rmsnorm_bwd(w.dnf, hL, m->final_norm, w.rstd_f, nullptr, T, d.hidden, dh_out, s);
 }

@@ -508,19 +508,23 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm(const GemmP
 // absmax values (512 B). A runs two chunks ahead and the codes three, in
 // three LDS stages each, so a stage has about two chunks of MFMA time to
 // arrive; the waits are explicit vmcnt counts that leave the newer stages in
-// flight (the compiler's own barrier would wait for everything). During chunk
-// t's MFMAs each thread dequantizes 16 elements of chunk t+1: one LDS read of
-// the packed codes, one 8-byte LDS lookup per code byte in a 256-entry table
-// of value pairs, two fp32 multiplies by the block absmax and one paired bf16
-// conversion, then 16-byte LDS writes into the swizzled bf16 tile.
-// LDS tiles are unpadded; the 16-byte chunk c of row r is stored at chunk
-// c ^ ((r >> 1) & 7), so fragment reads are conflict-free and each fragment
-// address is a per-lane base plus an immediate offset.
+// flight (the compiler's own barrier would wait for everything). Each DMA
+// address is a wavefront-uniform base (scalar registers, advanced once per
+// chunk) plus a per-lane 32-bit offset computed once, so the loop spends no
+// vector instructions on addressing. During chunk t's MFMAs each thread
+// dequantizes 16 elements of chunk t+1: one LDS read of the packed codes, one
+// 8-byte LDS lookup per code byte in a 256-entry table of value pairs (at LDS
+// address 0, so the address is the byte times 8), two fp32 multiplies by the
+// block absmax and one paired bf16 conversion, then 16-byte LDS writes into
+// the swizzled bf16 tile. LDS tiles are unpadded; the 16-byte chunk c of row
+// r is stored at chunk c ^ ((r >> 1) & 7), so fragment reads are
+// conflict-free and each fragment address is a per-lane base plus an
+// immediate offset.
 namespace fast {
 constexpr int BM = 256, BN = 128, NTH = 512, NW = 8, WGN = 2, WM = 64, WN = 64, FI = WM / 16, FJ = WN / 16;
 constexpr int SA = BM * 64 * 2, SB = BN * 64 * 2, SR = BN * 32, SS = 512;  // bytes per stage
-constexpr int OFF_A = 0, OFF_B = 3 * SA, OFF_R = OFF_B + 3 * SB, OFF_S = OFF_R + 3 * SR, OFF_L = OFF_S + 3 * SS;
-constexpr int LDS_BYTES = OFF_L + 256 * 8;
+constexpr int OFF_L = 0, OFF_A = 256 * 8, OFF_B = OFF_A + 3 * SA, OFF_R = OFF_B + 3 * SB, OFF_S = OFF_R + 3 * SR;
+constexpr int LDS_BYTES = OFF_S + 3 * SS;
 static_assert(LDS_BYTES <= 160 * 1024, "fast NF4 tile exceeds LDS");
 constexpr int NA = BM / 8 / NW;  // 16-byte A DMAs per thread per chunk
 constexpr int NR = 2;            // code + absmax DMAs per thread per chunk
@@ -538,53 +542,75 @@ __device__ __forceinline__ void stage_sync() {
     asm volatile("s_barrier" ::: "memory");
 }
 
-// A tile (256 rows x 64 k, bf16): each wavefront moves 4 KB; one instruction
-// writes 1 KB of LDS (lane l at byte 16 l), so each lane fetches the 16 bytes
-// that belong in its slot of the swizzled layout.
-__device__ __forceinline__ void a_dma(const uint16_t* __restrict__ A, int64_t lda, int m0, int k0,
-                                      char* __restrict__ dst) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint16_t* tile = reinterpret_cast<uint16_t*>(dst);
-#pragma unroll
-    for (int u = 0; u < NA; ++u) {
-        const int blk = wave * NA + u;
-        const int r = blk * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ ((r >> 1) & 7);
-        __builtin_amdgcn_global_load_lds(A + int64_t(m0 + r) * lda + k0 + c * 8, tile + blk * 512, 16, 0, 0);
-    }
+// Per-lane DMA offsets (bytes, fixed for the whole K loop) into three buffer
+// resources based at the tile's chunk-0 origin; a chunk adds a uniform
+// scalar offset, so the DMAs cost no vector instructions.
+//  A tile (256 rows x 64 k, bf16): each wavefront moves 4 KB in four 1 KB
+//  instructions; lane l of one instruction lands at byte 16 l of its 1 KB
+//  block, so it fetches the 16 bytes that belong in that slot of the
+//  swizzled layout.
+//  Codes, in natural order: NT [128 n][32 B] with one absmax per row; NN
+//  [64 k][64 B] with two absmax per row. Every wavefront issues exactly one
+//  16-byte DMA (32 lanes) and one 4-byte DMA (16 lanes), so the
+//  per-wavefront vmcnt bookkeeping is the same everywhere.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ __forceinline__ lds_ptr_t as_lds(char* p) {
+    return reinterpret_cast<lds_ptr_t>(reinterpret_cast<uintptr_t>(p));
 }
-
-// Packed codes and absmax of one weight chunk, in natural order: NT [128 n][32 B]
-// with one absmax per row; NN [64 k][64 B] with two absmax per row. Every
-// wavefront issues exactly one 16-byte DMA (32 lanes) and one 4-byte DMA
-// (16 lanes), so the per-wavefront vmcnt bookkeeping is the same everywhere.
+// raw buffer: stride 0, 2 GiB range (every offset used here is far below),
+// the gfx9 default data format word
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
+}
 template <int BKIND>
-__device__ __forceinline__ void code_dma(const uint8_t* __restrict__ P, const float* __restrict__ S, int64_t cols,
-                                         int n0, int k0, char* __restrict__ raw, char* __restrict__ sc) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane < 32) {
-        const int q = wave * 32 + lane;
-        int64_t byte;
-        if constexpr (BKIND == B_NF4_NN) byte = ((int64_t(k0 + (q >> 2)) * cols + n0) >> 1) + (q & 3) * 16;
-        else byte = ((int64_t(n0 + (q >> 1)) * cols + k0) >> 1) + (q & 1) * 16;
-        __builtin_amdgcn_global_load_lds(P + byte, raw + wave * 512, 16, 0, 0);
+struct DmaPlan {
+    uint32_t a[NA];
+    uint32_t code, scale;
+    int wave;  // wavefront-uniform
+    __amdgpu_buffer_rsrc_t ra, rc, rs;
+    __device__ __forceinline__ void init(const void* a0, const void* c0, const void* s0, int64_t lda, int64_t cols) {
+        const int lane = threadIdx.x & 63;
+        wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        ra = rsrc(a0);
+        rc = rsrc(c0);
+        rs = rsrc(s0);
+#pragma unroll
+        for (int u = 0; u < NA; ++u) {
+            const int r = (wave * NA + u) * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ ((r >> 1) & 7);
+            a[u] = uint32_t((int64_t(r) * lda + c * 8) * 2);
+        }
+        const int q = wave * 32 + (lane & 31), qs = wave * 16 + (lane & 15);
+        if constexpr (BKIND == B_NF4_NN) {
+            code = uint32_t(int64_t(q >> 2) * (cols >> 1) + (q & 3) * 16);
+            scale = uint32_t((int64_t(qs >> 1) * (cols >> 6) + (qs & 1)) * 4);
+        } else {
+            code = uint32_t(int64_t(q >> 1) * (cols >> 1) + (q & 1) * 16);
+            scale = uint32_t(int64_t(qs) * (cols >> 6) * 4);
+        }
     }
-    if (lane < 16) {
-        const int q = wave * 16 + lane;
-        int64_t blk;
-        if constexpr (BKIND == B_NF4_NN) blk = ((int64_t(k0 + (q >> 1)) * cols + n0) >> 6) + (q & 1);
-        else blk = (int64_t(n0 + q) * cols + k0) >> 6;
-        __builtin_amdgcn_global_load_lds(S + blk, sc + wave * 64, 4, 0, 0);
+    __device__ __forceinline__ void a_dma(uint32_t soff, char* __restrict__ dst) const {
+#pragma unroll
+        for (int u = 0; u < NA; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, as_lds(dst + (wave * NA + u) * 1024), 16, a[u], soff, 0, 0);
     }
-}
+    __device__ __forceinline__ void code_dma(uint32_t coff, uint32_t soff, char* __restrict__ raw,
+                                             char* __restrict__ sc) const {
+        const int lane = threadIdx.x & 63;
+        if (lane < 32) __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, as_lds(raw + wave * 512), 16, code, coff, 0, 0);
+        if (lane < 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, as_lds(sc + wave * 64), 4, scale, soff, 0, 0);
+    }
+};
 
-// Codes of one chunk (LDS) -> bf16 tile [n][k] (LDS). lut2[b] holds the code
-// values of byte b's high nibble (the even element) and low nibble.
+// Codes of one chunk (LDS) -> bf16 tile [n][k] (LDS). lut2[b] (LDS address
+// 8 b) holds the code values of byte b's high nibble (the even element) and
+// low nibble.
 template <int BKIND>
 __device__ __forceinline__ void dequant(const char* __restrict__ raw, const char* __restrict__ sc,
-                                        const f2* __restrict__ lut2, uint16_t* __restrict__ tile) {
+                                        const char* __restrict__ lds0, uint16_t* __restrict__ tile) {
     const int t = threadIdx.x;
     const float* s = reinterpret_cast<const float*>(sc);
+    auto lut = [&](uint32_t byte) { return *reinterpret_cast<const f2*>(lds0 + OFF_L + (byte << 3)); };
     if constexpr (BKIND == B_NF4_NT) {
         // thread = 16 consecutive k of row t >> 2
         const int r = t >> 2, q4 = t & 3;
@@ -593,7 +619,7 @@ __device__ __forceinline__ void dequant(const char* __restrict__ raw, const char
         uint32_t e[8];
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
-            const f2 v = lut2[((b < 4 ? w.x : w.y) >> (8 * (b & 3))) & 0xFF];
+            const f2 v = lut(((b < 4 ? w.x : w.y) >> (8 * (b & 3))) & 0xFF);
             e[b] = f32x2_to_bf16x2(v.x * a, v.y * a);
         }
         *reinterpret_cast<uint4*>(tile + swz(r, 2 * q4)) = make_uint4(e[0], e[1], e[2], e[3]);
@@ -607,8 +633,8 @@ __device__ __forceinline__ void dequant(const char* __restrict__ raw, const char
         for (int kr = 0; kr < 4; ++kr) {
             const uint32_t two = *reinterpret_cast<const uint16_t*>(raw + (kg + kr) * 64 + (ng >> 1));
             a[kr] = s[(kg + kr) * 2 + (ng >> 6)];
-            v[kr][0] = lut2[two & 0xFF];
-            v[kr][1] = lut2[two >> 8];
+            v[kr][0] = lut(two & 0xFF);
+            v[kr][1] = lut(two >> 8);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -648,10 +674,9 @@ template <int BKIND>
 __global__ __launch_bounds__(fast::NTH) void k_nf4_tile(const GemmParams p) {
     using namespace fast;
     extern __shared__ __align__(16) char lds[];
-    f2* lut2 = reinterpret_cast<f2*>(lds + OFF_L);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
-    if (tid < 256) lut2[tid] = f2{nf4_value(tid >> 4), nf4_value(tid & 15)};
+    if (tid < 256) reinterpret_cast<f2*>(lds + OFF_L)[tid] = f2{nf4_value(tid >> 4), nf4_value(tid & 15)};
 
     const int gx = p.N / BN, gy = p.M / BM;
     const int ntile = gx * gy;
@@ -661,10 +686,16 @@ __global__ __launch_bounds__(fast::NTH) void k_nf4_tile(const GemmParams p) {
     const int split = blockIdx.y;
     const int kbeg = split * p.kchunk, kend = min(p.K, kbeg + p.kchunk);
     const int nch = (kend - kbeg) / 64;  // >= 1
-    const uint16_t* A = p.A;
-    const uint8_t* P = static_cast<const uint8_t*>(p.B);
-    const float* S = p.absmax;
     const int64_t cols = p.nf4_cols;
+
+    // chunk-0 origins; per chunk A moves 128 bytes, the codes 32 bytes (NT)
+    // or 64 rows (NN), the absmax 1 entry (NT) or 64 rows (NN)
+    const int64_t flat0 = (BKIND == B_NF4_NN) ? int64_t(kbeg) * cols + n0 : int64_t(n0) * cols + kbeg;
+    DmaPlan<BKIND> plan;
+    plan.init(p.A + int64_t(m0) * p.lda + kbeg, static_cast<const char*>(p.B) + (flat0 >> 1), p.absmax + (flat0 >> 6),
+              p.lda, cols);
+    const uint32_t cstep = (BKIND == B_NF4_NN) ? uint32_t(32 * cols) : 32u;
+    const uint32_t sstep = (BKIND == B_NF4_NN) ? uint32_t(4 * cols) : 4u;  // bytes
 
     f32x4 acc[FI][FJ];
 #pragma unroll
@@ -674,25 +705,27 @@ __global__ __launch_bounds__(fast::NTH) void k_nf4_tile(const GemmParams p) {
 
     // chunk c reads A stage c % 3 and bf16 stage c % 3; loads past the end
     // re-read the last chunk into stages nobody reads again
-    auto kc = [&](int c) { return kbeg + min(c, nch - 1) * 64; };
+    auto cl = [&](int c) { return min(c, nch - 1); };
     auto sa = [&](int s) { return lds + OFF_A + s * SA; };
     auto sb = [&](int s) { return reinterpret_cast<uint16_t*>(lds + OFF_B + s * SB); };
     auto sr = [&](int s) { return lds + OFF_R + s * SR; };
     auto ss = [&](int s) { return lds + OFF_S + s * SS; };
-    code_dma<BKIND>(P, S, cols, n0, kc(0), sr(0), ss(0));
-    a_dma(A, p.lda, m0, kc(0), sa(0));
-    code_dma<BKIND>(P, S, cols, n0, kc(1), sr(1), ss(1));
-    a_dma(A, p.lda, m0, kc(1), sa(1));
-    code_dma<BKIND>(P, S, cols, n0, kc(2), sr(2), ss(2));
+    auto a_dma = [&](int c, int s) { plan.a_dma(uint32_t(cl(c)) * 128u, sa(s)); };
+    auto code_dma = [&](int c, int s) { plan.code_dma(uint32_t(cl(c)) * cstep, uint32_t(cl(c)) * sstep, sr(s), ss(s)); };
+    code_dma(0, 0);
+    a_dma(0, 0);
+    code_dma(1, 1);
+    a_dma(1, 1);
+    code_dma(2, 2);
     stage_sync<2 * NA + 2 * NR>();  // codes 0 (and the table) in LDS
-    dequant<BKIND>(sr(0), ss(0), lut2, sb(0));
+    dequant<BKIND>(sr(0), ss(0), lds, sb(0));
     stage_sync<NA + NR>();          // A 0, codes 1, bf16 0
     auto step = [&](int c, auto stage) {
         constexpr int S0 = decltype(stage)::value, S1 = (S0 + 1) % 3, S2 = (S0 + 2) % 3;
-        a_dma(A, p.lda, m0, kc(c + 2), sa(S2));
-        code_dma<BKIND>(P, S, cols, n0, kc(c + 3), sr(S0), ss(S0));
+        a_dma(c + 2, S2);
+        code_dma(c + 3, S0);
         mma(reinterpret_cast<const uint16_t*>(sa(S0)), sb(S0), acc, wm * WM, wn * WN, lane);
-        dequant<BKIND>(sr(S1), ss(S1), lut2, sb(S1));
+        dequant<BKIND>(sr(S1), ss(S1), lds, sb(S1));
         stage_sync<NA + NR>();      // A c+1, codes c+2, bf16 c+1
     };
     for (int c = 0; c < nch; c += 3) {
@@ -754,9 +787,29 @@ __global__ __launch_bounds__(fast::NTH) void k_nf4_tile(const GemmParams p) {
     }
 }
 
+// Sums the split-K partials in split order (fixed, so results do not depend
+// on timing). Four consecutive outputs per thread when N % 4 == 0.
 __global__ __launch_bounds__(256) void k_splitk_reduce(const GemmParams p) {
-    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t MN = int64_t(p.M) * p.N;
+    if ((p.N & 3) == 0) {
+        const int64_t idx = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
+        if (idx >= MN) return;
+        float4 v = *reinterpret_cast<const float4*>(p.partial + idx);
+        for (int s = 1; s < p.splits; ++s) {
+            const float4 w = *reinterpret_cast<const float4*>(p.partial + s * MN + idx);
+            v.x += w.x;
+            v.y += w.y;
+            v.z += w.z;
+            v.w += w.w;
+        }
+        const int row = int(idx / p.N), col = int(idx % p.N);
+        store_out(p, 0, 0, row, col, v.x);
+        store_out(p, 0, 0, row, col + 1, v.y);
+        store_out(p, 0, 0, row, col + 2, v.z);
+        store_out(p, 0, 0, row, col + 3, v.w);
+        return;
+    }
+    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (idx >= MN) return;
     float v = 0.f;
     for (int s = 0; s < p.splits; ++s) v += p.partial[s * MN + idx];
@@ -826,7 +879,9 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
     }
     const bool fast_ok = nf4 && te == TE_BF16 && akind == A_ROW && p.batch == 1 && p.causal == CAUSAL_NONE &&
                          p.M % fast::BM == 0 && p.N % fast::BN == 0 && p.K % 64 == 0 && p.K >= 64 && p.a_vec &&
-                         p.b_vec && aligned16(p.absmax) && p.nf4_cols % 64 == 0;  // never depends on the slab
+                         p.b_vec && aligned16(p.absmax) && p.nf4_cols % 64 == 0 &&
+                         int64_t(p.M) * p.lda * 2 < (int64_t(1) << 31) &&
+                         int64_t(p.N) * p.K / 2 < (int64_t(1) << 31);  // never depends on the slab
     const TileCfg tc = fast_ok ? TileCfg{fast::BM, fast::BN} : pick_tile(p, bkind);
     const int gx = (p.N + tc.bn - 1) / tc.bn, gy = (p.M + tc.bm - 1) / tc.bm;
     // split-K when the grid would leave CUs idle: shapes decide, nothing else
@@ -834,12 +889,26 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
     p.kchunk = ((p.K + BK - 1) / BK) * BK;
     const int tiles = gx * gy;
     if (fast_ok) {
-        // about one workgroup per CU; every split gets at least 8 64-wide chunks
-        if (partial_ws && tiles < 256) {
-            int want = std::min((256 + tiles - 1) / tiles, std::min(p.K / 512, 16));
-            while (want > 1 && size_t(want) * tiles * tc.bm * tc.bn > kGemmPartialFloats) --want;
-            if (want > 1) {
-                const int kc = (((p.K + want - 1) / want) + 63) / 64 * 64;
+        // One workgroup fits a CU, so the grid runs in rounds of 256. Pick the
+        // split count with the least estimated time, in units of one 64-wide
+        // chunk of one tile: rounds x (chunks per split + ~3 of pipeline fill
+        // and epilogue) + the reduce pass (fp32 partials at ~4 TB/s, a chunk
+        // being ~1.35 us, plus ~2 chunks of launch). Shapes decide, nothing else.
+        if (partial_ws) {
+            const int nch = p.K / 64;
+            const double mn = double(p.M) * p.N;
+            double best = 1e300;
+            int best_s = 1;
+            for (int sp = 1; sp <= 16 && nch / sp >= 4; ++sp) {
+                if (sp > 1 && size_t(sp) * tiles * tc.bm * tc.bn > kGemmPartialFloats) break;
+                const int per = (nch + sp - 1) / sp;
+                const double rounds = double((tiles * sp + 255) / 256);
+                double cost = rounds * (per + 3.0);
+                if (sp > 1) cost += mn * 4.0 * (sp + 1) / 4e12 / 1.35e-6 + 2.0;
+                if (cost < best - 1e-9) best = cost, best_s = sp;
+            }
+            if (best_s > 1) {
+                const int kc = (nch + best_s - 1) / best_s * 64;
                 p.kchunk = kc;
                 p.splits = (p.K + kc - 1) / kc;
                 p.partial = partial_ws;
@@ -878,7 +947,7 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
                  : key == 21 ? 5 : key == 31 ? 6 : 7;
     const int bsz = p.batch * p.splits;
     {
-        ProfScope prof(kNames[ni], flops, bytes, s);
+        ProfScope prof(p.tag ? p.tag : kNames[ni], flops, bytes, s);
         switch (key) {
             case A_ROW * 100 + B_NF4_NT * 10 + TE_BF16:
                 if (fast_ok)
@@ -914,7 +983,8 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
     if (p.splits > 1) {
         const int64_t MN = int64_t(p.M) * p.N;
         ProfScope prof("splitk_reduce", double(MN) * p.splits, double(MN) * (4.0 * p.splits + cb + (p.R ? 4 : 0)), s);
-        hipLaunchKernelGGL(k_splitk_reduce, dim3(unsigned((MN + 255) / 256)), dim3(256), 0, s, p);
+        const int64_t threads = (p.N & 3) == 0 ? MN / 4 : MN;
+        hipLaunchKernelGGL(k_splitk_reduce, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, p);
         check_launch("gemm splitk reduce");
     }
 }

@@ -217,6 +217,7 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
     if (L) {
         GemmParams pu = dense_gemm(T, 3 * r, H, w.n1, H, w.A_qkv, H);
         out_bf16(pu, w.u_qkv, 3 * r);
+        pu.tag = "gemm_lora_u";
         gemm(pu, A_ROW, B_DENSE_NT, TE_BF16, w.partial, s);
     }
     {
@@ -250,6 +251,7 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
         p.c_si = int64_t(S) * S;
         p.alpha = scale;
         p.causal = CAUSAL_SKIP_UPPER;
+        p.tag = "gemm_attn_qk";
         gemm(p, A_ROW, B_DENSE_NT, TE_BF16, nullptr, s);
     }
     launch_attn_softmax_fwd(w.scores, g.B * g.nH, S, w.P, s);
@@ -266,11 +268,13 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
         p.c_so = int64_t(S) * g.qdim;
         p.c_si = g.hd;
         p.causal = CAUSAL_K_LE_M;
+        p.tag = "gemm_attn_pv";
         gemm(p, A_ROW, B_DENSE_NN, TE_BF16, nullptr, s);
     }
     if (L) {
         GemmParams pu = dense_gemm(T, r, g.qdim, w.oattn, g.qdim, w.A_o, g.qdim);
         out_bf16(pu, w.u_o, r);
+        pu.tag = "gemm_lora_u";
         gemm(pu, A_ROW, B_DENSE_NT, TE_BF16, w.partial, s);
     }
     {  // h1 = h_in + o_proj(o)
@@ -292,6 +296,7 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
     if (L) {
         GemmParams pu = dense_gemm(T, 2 * r, H, w.n2, H, w.A_gu, H);
         out_bf16(pu, w.u_gu, 2 * r);
+        pu.tag = "gemm_lora_u";
         gemm(pu, A_ROW, B_DENSE_NT, TE_BF16, w.partial, s);
     }
     {
@@ -311,6 +316,7 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
     if (L) {
         GemmParams pu = dense_gemm(T, r, g.I, w.act, g.I, w.A_d, g.I);
         out_bf16(pu, w.u_d, r);
+        pu.tag = "gemm_lora_u";
         gemm(pu, A_ROW, B_DENSE_NT, TE_BF16, w.partial, s);
     }
     if (h_out) {
@@ -335,6 +341,7 @@ static void grad_B(const LayerGeom& g, const uint16_t* dy, int64_t ld_dy, int ou
     GemmParams p = dense_gemm(out, g.r, g.T, dy, ld_dy, u, ld_u);
     out_f32(p, dB, g.r);
     p.alpha = g.s;
+    p.tag = "gemm_lora_dB";
     gemm(p, A_TRANS, B_DENSE_NN, TE_BF16, w.partial, s);
 }
 // dA (stacked over nseg segments of r rows) = du^T x  (M = nseg*r, N = in, K = T).
@@ -346,6 +353,7 @@ static void grad_A(const LayerGeom& g, const uint16_t* du, int nseg, const uint1
     p.seg_rows = g.r;
     for (int i = 0; i < nseg; ++i) p.Cseg[i] = dA[i];
     p.C = dA[0];
+    p.tag = "gemm_lora_dA";
     gemm(p, A_TRANS, B_DENSE_NN, TE_BF16, w.partial, s);
 }
 
@@ -360,6 +368,7 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
     {
         GemmParams p = dense_gemm(T, r, H, w.dy16, H, w.B_d, r);
         out_bf16(p, w.du_d, r);
+        p.tag = "gemm_lora_du";
         gemm(p, A_ROW, B_DENSE_NN, TE_BF16, w.partial, s);
     }
     {
@@ -382,6 +391,7 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
     {
         GemmParams p = dense_gemm(T, 2 * r, 2 * g.I, w.dgu, 2 * g.I, w.B_gu, 2 * r);
         out_bf16(p, w.du_gu, 2 * r);
+        p.tag = "gemm_lora_du";
         gemm(p, A_ROW, B_DENSE_NN, TE_BF16, w.partial, s);
     }
     {
@@ -407,6 +417,7 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
     {
         GemmParams p = dense_gemm(T, r, H, w.dy16, H, w.B_o, r);
         out_bf16(p, w.du_o, r);
+        p.tag = "gemm_lora_du";
         gemm(p, A_ROW, B_DENSE_NN, TE_BF16, w.partial, s);
     }
     {
@@ -439,6 +450,7 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
         p.c_so = int64_t(g.nH) * S * g.hd;
         p.c_si = int64_t(S) * g.hd;
         p.causal = CAUSAL_K_GE_M;
+        p.tag = "gemm_attn_dv";
         gemm(p, A_TRANS, B_DENSE_NN, TE_BF16, nullptr, s);
     }
     {  // dP = dO v^T (into the scores buffer)
@@ -454,6 +466,7 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
         p.c_so = int64_t(g.nH) * S * S;
         p.c_si = int64_t(S) * S;
         p.causal = CAUSAL_SKIP_UPPER;
+        p.tag = "gemm_attn_dp";
         gemm(p, A_ROW, B_DENSE_NT, TE_BF16, nullptr, s);
     }
     launch_attn_softmax_bwd(w.P, w.scores, Z, S, w.dS, s);
@@ -471,6 +484,7 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
         p.c_si = g.hd;
         p.alpha = scale;
         p.causal = CAUSAL_K_LE_M;
+        p.tag = "gemm_attn_dq";
         gemm(p, A_ROW, B_DENSE_NN, TE_BF16, nullptr, s);
     }
     {  // dK_h = scale dS^T q
@@ -486,6 +500,7 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
         p.c_si = int64_t(S) * g.hd;
         p.alpha = scale;
         p.causal = CAUSAL_K_GE_M;
+        p.tag = "gemm_attn_dk";
         gemm(p, A_TRANS, B_DENSE_NN, TE_BF16, nullptr, s);
     }
     launch_gqa_reduce(w.dKh, g.B, g.nH, g.nKV, S, g.hd, w.dqkv, g.nqkv, g.qdim, s);
@@ -497,6 +512,7 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
     {
         GemmParams p = dense_gemm(T, 3 * r, g.nqkv, w.dqkv, g.nqkv, w.B_qkv, 3 * r);
         out_bf16(p, w.du_qkv, 3 * r);
+        p.tag = "gemm_lora_du";
         gemm(p, A_ROW, B_DENSE_NN, TE_BF16, w.partial, s);
     }
     if (dh_in) {

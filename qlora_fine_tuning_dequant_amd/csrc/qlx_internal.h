@@ -104,6 +104,7 @@ struct GemmParams {
     int slab_alg_k = -1;  // algorithmic K of the slab for flop accounting (-1: K2)
     // set by the launcher
     int a_vec = 0, b_vec = 0, a2_vec = 0, b2_vec = 0;
+    const char* tag = nullptr;  // profiling label (host side only; default: the operand kinds)
 };
 
 // Floats of split-K scratch the launcher may use for any one GEMM.
