@@ -96,16 +96,19 @@ struct RowLoader {
 
 // Transposed operand: tile[r][k] = src[(k0 + k) * ld + r0 + r]. A unit is 4
 // consecutive r from 8 consecutive k rows, written as 4 k-contiguous vectors.
+// With fewer units than threads, the surplus threads load and store nothing.
 template <int R, int NT, bool SWZ = false>
 struct TransLoader {
-    static constexpr int U = (R / 4) * (BK / 8) / NT;
-    static_assert(U >= 1 && (R / 4) * (BK / 8) % NT == 0, "trans loader shape");
+    static constexpr int UNITS = (R / 4) * (BK / 8);
+    static constexpr int U = UNITS >= NT ? UNITS / NT : 1;
+    static_assert(UNITS % NT == 0 || NT % UNITS == 0, "trans loader shape");
     uint2 v[U][8];
     __device__ inline void load(const uint16_t* __restrict__ src, int64_t ld, int r0, int k0, int rows, int K,
                                 int vec_ok) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int idx = threadIdx.x + u * NT;
+            if (UNITS < NT && idx >= UNITS) break;
             const int rg = (idx % (R / 4)) * 4, kg = (idx / (R / 4)) * 8;
             const int gr = r0 + rg;
 #pragma unroll
@@ -131,6 +134,7 @@ struct TransLoader {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int idx = threadIdx.x + u * NT;
+            if (UNITS < NT && idx >= UNITS) break;
             const int rg = (idx % (R / 4)) * 4, kg = (idx / (R / 4)) * 8;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -647,25 +651,87 @@ __device__ __forceinline__ void dequant(const char* __restrict__ raw, const char
     }
 }
 
-// One chunk of MFMAs for a 64 x 64 wavefront tile. Row (base + i*16 + lr)
-// swizzles with (lr >> 1) & 7 only, so each K half has one per-lane base.
+// One 64-wide chunk of MFMAs for a (16 FI_) x (16 FJ_) wavefront tile. Row
+// (base + i*16 + lr) swizzles with (lr >> 1) & 7 only, so each K half has one
+// per-lane base.
+template <int FI_, int FJ_>
 __device__ __forceinline__ void mma(const uint16_t* __restrict__ As, const uint16_t* __restrict__ Bs,
-                                    f32x4 (&acc)[FI][FJ], int rm, int rn, int lane) {
+                                    f32x4 (&acc)[FI_][FJ_], int rm, int rn, int lane) {
     const int lr = lane & 15, lc = lane >> 4, sw = (lr >> 1) & 7;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
         const int ch = ((kk * 4 + lc) ^ sw) << 3;
         const uint16_t* ab = As + (rm + lr) * 64 + ch;
         const uint16_t* bb = Bs + (rn + lr) * 64 + ch;
-        uint4 a[FI], b[FJ];
+        uint4 a[FI_], b[FJ_];
 #pragma unroll
-        for (int i = 0; i < FI; ++i) a[i] = *reinterpret_cast<const uint4*>(ab + i * 16 * 64);
+        for (int i = 0; i < FI_; ++i) a[i] = *reinterpret_cast<const uint4*>(ab + i * 16 * 64);
 #pragma unroll
-        for (int j = 0; j < FJ; ++j) b[j] = *reinterpret_cast<const uint4*>(bb + j * 16 * 64);
+        for (int j = 0; j < FJ_; ++j) b[j] = *reinterpret_cast<const uint4*>(bb + j * 16 * 64);
 #pragma unroll
-        for (int i = 0; i < FI; ++i)
+        for (int i = 0; i < FI_; ++i)
 #pragma unroll
-            for (int j = 0; j < FJ; ++j) acc[i][j] = mfma16<TE_BF16>(a[i], b[j], acc[i][j]);
+            for (int j = 0; j < FJ_; ++j) acc[i][j] = mfma16<TE_BF16>(a[i], b[j], acc[i][j]);
+    }
+}
+
+// LoRA slab of a full tile (last split only): K2 in 64-wide chunks through
+// the 64-wide swizzled layout at As (BM_ rows) and Bs (BN_ rows), zero-filled
+// past K2. The caller has drained every DMA and barriered.
+template <int BKIND, int BM_, int BN_, int FI_, int FJ_>
+__device__ __forceinline__ void slab(const GemmParams& p, uint16_t* As, uint16_t* Bs, f32x4 (&acc)[FI_][FJ_], int m0,
+                                     int n0, int rm, int rn, int lane) {
+    for (int k0 = 0; k0 < p.K2; k0 += 64) {
+        RowLoader<BM_, NTH, true> la;
+        la.load(p.A2, p.lda2, m0, k0, p.M, p.K2, p.a2_vec);
+        if constexpr (BKIND == B_NF4_NT) {
+            RowLoader<BN_, NTH, true> lb;
+            lb.load(p.B2, p.ldb2, n0, k0, p.N, p.K2, p.b2_vec);
+            lb.store(Bs);
+        } else {
+            TransLoader<BN_, NTH, true> lb;
+            lb.load(p.B2, p.ldb2, n0, k0, p.N, p.K2, p.b2_vec);
+            lb.store(Bs);
+        }
+        la.store(As);
+        __syncthreads();
+        mma(As, Bs, acc, rm, rn, lane);
+        __syncthreads();
+    }
+}
+
+// Epilogue of a full tile: each wavefront stages 16-row bands of its
+// (16 FI_) x WN_ tile through LDS (stage: 16 x (WN_ + 4) floats of its own),
+// then each lane writes WN_/4 consecutive columns of one row: fp32 partials
+// when split, the GEMM's output otherwise.
+template <int FI_, int WN_>
+__device__ __forceinline__ void epilogue(const GemmParams& p, const f32x4 (&acc)[FI_][WN_ / 16], float* stage, int row0,
+                                         int col0, int split, int lane) {
+    const int srow = (lane >> 2) & 15;
+    const int scol = (lane & 3) * (WN_ / 4);
+#pragma unroll
+    for (int i = 0; i < FI_; ++i) {
+#pragma unroll
+        for (int j = 0; j < WN_ / 16; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) stage[((lane >> 4) * 4 + e) * (WN_ + 4) + j * 16 + (lane & 15)] = acc[i][j][e];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int row = row0 + i * 16 + srow;
+        const int col = col0 + scol;
+        const float* src = stage + srow * (WN_ + 4) + scol;
+        if (p.splits > 1) {
+            float* dst = p.partial + (int64_t(split) * p.M + row) * p.N + col;
+#pragma unroll
+            for (int c = 0; c < WN_ / 4; c += 4)
+                *reinterpret_cast<float4*>(dst + c) = make_float4(src[c], src[c + 1], src[c + 2], src[c + 3]);
+        } else {
+            store_row(p, 0, 0, row, col, src, WN_ / 4);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 }  // namespace fast
@@ -735,56 +801,189 @@ __global__ __launch_bounds__(fast::NTH) void k_nf4_tile(const GemmParams p) {
     }
     stage_sync<0>();
 
-    if (p.K2 > 0 && split == p.splits - 1) {  // LoRA slab, any K2 (zero-filled tail)
-        uint16_t* As0 = reinterpret_cast<uint16_t*>(sa(0));
-        uint16_t* Bs0 = sb(0);
-        for (int k0 = 0; k0 < p.K2; k0 += 64) {
-            RowLoader<BM, NTH, true> la;
-            la.load(p.A2, p.lda2, m0, k0, p.M, p.K2, p.a2_vec);
-            if constexpr (BKIND == B_NF4_NT) {
-                RowLoader<BN, NTH, true> lb;
-                lb.load(p.B2, p.ldb2, n0, k0, p.N, p.K2, p.b2_vec);
-                lb.store(Bs0);
-            } else if (tid < 256) {
-                TransLoader<BN, 256, true> lb;
-                lb.load(p.B2, p.ldb2, n0, k0, p.N, p.K2, p.b2_vec);
-                lb.store(Bs0);
-            }
-            la.store(As0);
-            __syncthreads();
-            mma(As0, Bs0, acc, wm * WM, wn * WN, lane);
-            __syncthreads();
-        }
-    }
+    if (p.K2 > 0 && split == p.splits - 1)  // LoRA slab, any K2 (zero-filled tail)
+        slab<BKIND, BM, BN>(p, reinterpret_cast<uint16_t*>(sa(0)), sb(0), acc, m0, n0, wm * WM, wn * WN, lane);
+    epilogue<FI, WN>(p, acc, reinterpret_cast<float*>(lds + OFF_A) + wave * (16 * (WN + 4)), m0 + wm * WM,
+                     n0 + wn * WN, split, lane);
+}
 
-    // epilogue: 16-row bands staged through LDS, 16 consecutive columns per lane
-    float* stage = reinterpret_cast<float*>(lds + OFF_A) + wave * (16 * (WN + 4));
-    const int srow = (lane >> 2) & 15;
-    const int scol = (lane & 3) * (WN / 4);
+// ---------------------------------------------------------------------------
+// Wide NF4 tile (M % 512 == 0, otherwise as the full tile): 512 x 128 on 8
+// wavefronts (4 x 2) of 128 x 64, in K chunks of 32. Each dequantized weight
+// tile now serves 512 rows and each wavefront's fragment reads feed twice the
+// MFMAs, so LDS traffic per MFMA falls by about a third; the price is half as
+// many tiles, which pays where the 256 x 128 grid would leave part of a round
+// idle (the launcher decides from the shapes). The pipeline is the full
+// tile's: A two chunks ahead, codes three, explicit partial waits, scalar DMA
+// offsets, table lookups from LDS address 0. Rows are 64 bytes here, with
+// 16-byte chunk c of row r at c ^ ((r >> 2) & 3).
+namespace wide {
+constexpr int BM = 512, BN = 128, BKW = 32, NTH = 512, WGN = 2, WM = 128, WN = 64, FI = WM / 16, FJ = WN / 16;
+constexpr int SA = BM * BKW * 2, SB = BN * BKW * 2, SR = BN * BKW / 2, SS = 512;  // bytes per stage
+constexpr int OFF_L = 0, OFF_A = 256 * 8, OFF_B = OFF_A + 3 * SA, OFF_R = OFF_B + 3 * SB, OFF_S = OFF_R + 3 * SR;
+constexpr int LDS_BYTES = OFF_S + 3 * SS;
+static_assert(LDS_BYTES <= 160 * 1024, "wide NF4 tile exceeds LDS");
+static_assert(3 * SA >= BM * 64 * 2 && 3 * SB >= BN * 64 * 2, "slab tiles must fit the stage regions");
+constexpr int NA = SA / 1024 / 8;  // 1 KB A DMAs per wavefront per chunk
+constexpr int NR = 2;
+typedef float f2 __attribute__((ext_vector_type(2)));
+// 64-byte rows of four 16-byte chunks; chunk c of row r at c ^ ((r >> 2) & 3)
+__device__ __forceinline__ int swz(int r, int c) { return r * 32 + ((c ^ ((r >> 2) & 3)) << 3); }
+template <int BKIND>
+struct Plan {
+    uint32_t a[NA];
+    uint32_t code, scale;
+    int wave;
+    __amdgpu_buffer_rsrc_t ra, rc, rs;
+    __device__ __forceinline__ void init(const void* a0, const void* c0, const void* s0, int64_t lda, int64_t cols) {
+        const int lane = threadIdx.x & 63;
+        wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        ra = fast::rsrc(a0); rc = fast::rsrc(c0); rs = fast::rsrc(s0);
 #pragma unroll
-    for (int i = 0; i < FI; ++i) {
-#pragma unroll
-        for (int j = 0; j < FJ; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) stage[((lane >> 4) * 4 + e) * (WN + 4) + j * 16 + (lane & 15)] = acc[i][j][e];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int row = m0 + wm * WM + i * 16 + srow;
-        const int col0 = n0 + wn * WN + scol;
-        const float* src = stage + srow * (WN + 4) + scol;
-        if (p.splits > 1) {
-            float* dst = p.partial + (int64_t(split) * p.M + row) * p.N + col0;
-#pragma unroll
-            for (int c = 0; c < WN / 4; c += 4)
-                *reinterpret_cast<float4*>(dst + c) = make_float4(src[c], src[c + 1], src[c + 2], src[c + 3]);
-        } else {
-            store_row(p, 0, 0, row, col0, src, WN / 4);
+        for (int u = 0; u < NA; ++u) {
+            const int r = (wave * NA + u) * 16 + (lane >> 2);   // 1 KB = 16 rows x 64 B
+            const int c = (lane & 3) ^ ((r >> 2) & 3);
+            a[u] = uint32_t((int64_t(r) * lda + c * 8) * 2);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int q = wave * 16 + (lane & 15);                  // 128 x 16-byte code pieces
+        const int qs = (BKIND == B_NF4_NN) ? wave * 8 + (lane & 7) : wave * 16 + (lane & 15);
+        if constexpr (BKIND == B_NF4_NN) {
+            code = uint32_t(int64_t(q >> 2) * (cols >> 1) + (q & 3) * 16);       // 32 k-rows x 64 B
+            scale = uint32_t((int64_t(qs >> 1) * (cols >> 6) + (qs & 1)) * 4);  // 32 rows x 2 (lanes < 8)
+        } else {
+            code = uint32_t(int64_t(q) * (cols >> 1));                          // 128 rows x 16 B
+            scale = uint32_t(int64_t(qs) * (cols >> 6) * 4);                     // 128 rows x 1
+        }
     }
+    __device__ __forceinline__ void a_dma(uint32_t soff, char* __restrict__ dst) const {
+#pragma unroll
+        for (int u = 0; u < NA; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, fast::as_lds(dst + (wave * NA + u) * 1024), 16, a[u], soff, 0, 0);
+    }
+    __device__ __forceinline__ void code_dma(uint32_t coff, uint32_t soff, char* __restrict__ raw, char* __restrict__ sc) const {
+        const int lane = threadIdx.x & 63;
+        if (lane < 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, fast::as_lds(raw + wave * 256), 16, code, coff, 0, 0);
+        if (lane < (BKIND == B_NF4_NN ? 8 : 16))
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, fast::as_lds(sc + wave * (BKIND == B_NF4_NN ? 32 : 64)), 4, scale, soff, 0, 0);
+    }
+};
+template <int BKIND>
+__device__ __forceinline__ void dequant(const char* __restrict__ raw, const char* __restrict__ sc, const char* __restrict__ lds0,
+                                        uint16_t* __restrict__ tile) {
+    const int t = threadIdx.x;
+    const float* s = reinterpret_cast<const float*>(sc);
+    auto lut = [&](uint32_t byte) { return *reinterpret_cast<const f2*>(lds0 + OFF_L + (byte << 3)); };
+    if constexpr (BKIND == B_NF4_NT) {
+        const int r = t >> 2, q4 = t & 3;                        // 8 consecutive k of row r
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(raw + r * 16 + q4 * 4);
+        const float a = s[r];
+        uint32_t e[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const f2 v = lut((w >> (8 * b)) & 0xFF);
+            e[b] = f32x2_to_bf16x2(v.x * a, v.y * a);
+        }
+        *reinterpret_cast<uint4*>(tile + swz(r, q4)) = make_uint4(e[0], e[1], e[2], e[3]);
+    } else {
+        const int ng = (t & 63) * 2, kg = (t >> 6) * 4;            // 2 n x 4 k
+        f2 v[4];
+        float a[4];
+#pragma unroll
+        for (int kr = 0; kr < 4; ++kr) {
+            const uint32_t byte = *reinterpret_cast<const uint8_t*>(raw + (kg + kr) * 64 + (ng >> 1));
+            a[kr] = s[(kg + kr) * 2 + (ng >> 6)];
+            v[kr] = lut(byte);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            float x[4];
+#pragma unroll
+            for (int kr = 0; kr < 4; ++kr) x[kr] = (j ? v[kr].y : v[kr].x) * a[kr];
+            *reinterpret_cast<uint2*>(tile + swz(ng + j, kg >> 3) + (kg & 4)) =
+                make_uint2(f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3]));
+        }
+    }
+}
+__device__ __forceinline__ void mma(const uint16_t* __restrict__ As, const uint16_t* __restrict__ Bs, f32x4 (&acc)[FI][FJ],
+                                    int rm, int rn, int lane) {
+    const int lr = lane & 15, lc = lane >> 4;
+    // rows rm + i*16 + lr: (row >> 2) & 3 == (lr >> 2) & 3 since rm, i*16 are multiples of 16
+    const int ch = (lc ^ ((lr >> 2) & 3)) << 3;
+    const uint16_t* ab = As + (rm + lr) * 32 + ch;
+    const uint16_t* bb = Bs + (rn + lr) * 32 + ch;
+    uint4 a[FI], b[FJ];
+#pragma unroll
+    for (int i = 0; i < FI; ++i) a[i] = *reinterpret_cast<const uint4*>(ab + i * 16 * 32);
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) b[j] = *reinterpret_cast<const uint4*>(bb + j * 16 * 32);
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) acc[i][j] = mfma16<TE_BF16>(a[i], b[j], acc[i][j]);
+}
+}  // namespace wide
+
+template <int BKIND>
+__global__ __launch_bounds__(wide::NTH) void k_nf4_wide(const GemmParams p) {
+    using namespace wide;
+    extern __shared__ __align__(16) char lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    if (tid < 256) reinterpret_cast<f2*>(lds + OFF_L)[tid] = f2{nf4_value(tid >> 4), nf4_value(tid & 15)};
+    const int gx = p.N / BN, gy = p.M / BM;
+    const int ntile = gx * gy;
+    int t = blockIdx.x;
+    if (ntile % 8 == 0) t = (t % 8) * (ntile / 8) + t / 8;
+    const int m0 = (t % gy) * BM, n0 = (t / gy) * BN;
+    const int split = blockIdx.y;
+    const int kbeg = split * p.kchunk, kend = min(p.K, kbeg + p.kchunk);
+    const int nch = (kend - kbeg) / BKW;
+    const int64_t cols = p.nf4_cols;
+    const int64_t flat0 = (BKIND == B_NF4_NN) ? int64_t(kbeg) * cols + n0 : int64_t(n0) * cols + kbeg;
+    Plan<BKIND> plan;
+    plan.init(p.A + int64_t(m0) * p.lda + kbeg, static_cast<const char*>(p.B) + (flat0 >> 1), p.absmax + (flat0 >> 6), p.lda, cols);
+    // per 32-wide chunk: A 64 bytes; codes 16 bytes (NT) or 32 rows (NN); absmax: NT advances every
+    // other chunk (64-element blocks), NN 32 rows
+    const uint32_t cstep = (BKIND == B_NF4_NN) ? uint32_t(16 * cols) : 16u;
+    f32x4 acc[FI][FJ];
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto cl = [&](int c) { return min(c, nch - 1); };
+    auto soff = [&](int c) { return (BKIND == B_NF4_NN) ? uint32_t(cl(c)) * uint32_t(2 * cols) : uint32_t(cl(c) >> 1) * 4u; };
+    auto sa = [&](int s) { return lds + OFF_A + s * SA; };
+    auto sb = [&](int s) { return reinterpret_cast<uint16_t*>(lds + OFF_B + s * SB); };
+    auto sr = [&](int s) { return lds + OFF_R + s * SR; };
+    auto ss = [&](int s) { return lds + OFF_S + s * SS; };
+    auto a_dma = [&](int c, int s) { plan.a_dma(uint32_t(cl(c)) * 64u, sa(s)); };
+    auto code_dma = [&](int c, int s) { plan.code_dma(uint32_t(cl(c)) * cstep, soff(c), sr(s), ss(s)); };
+    code_dma(0, 0);
+    a_dma(0, 0);
+    code_dma(1, 1);
+    a_dma(1, 1);
+    code_dma(2, 2);
+    fast::stage_sync<2 * NA + 2 * NR>();
+    dequant<BKIND>(sr(0), ss(0), lds, sb(0));
+    fast::stage_sync<NA + NR>();
+    auto step = [&](int c, auto stage) {
+        constexpr int S0 = decltype(stage)::value, S1 = (S0 + 1) % 3, S2 = (S0 + 2) % 3;
+        a_dma(c + 2, S2);
+        code_dma(c + 3, S0);
+        mma(reinterpret_cast<const uint16_t*>(sa(S0)), sb(S0), acc, wm * WM, wn * WN, lane);
+        dequant<BKIND>(sr(S1), ss(S1), lds, sb(S1));
+        fast::stage_sync<NA + NR>();
+    };
+    for (int c = 0; c < nch; c += 3) {
+        step(c, std::integral_constant<int, 0>());
+        if (c + 1 < nch) step(c + 1, std::integral_constant<int, 1>());
+        if (c + 2 < nch) step(c + 2, std::integral_constant<int, 2>());
+    }
+    fast::stage_sync<0>();
+    if (p.K2 > 0 && split == p.splits - 1)  // slab tiles are 64 wide: A2 spans two A stages, B2 two B stages
+        fast::slab<BKIND, BM, BN>(p, reinterpret_cast<uint16_t*>(sa(0)), sb(0), acc, m0, n0, wm * WM, wn * WN, lane);
+    fast::epilogue<FI, WN>(p, acc, reinterpret_cast<float*>(lds + OFF_A) + wave * (16 * (WN + 4)), m0 + wm * WM,
+                           n0 + wn * WN, split, lane);
 }
 
 // Sums the split-K partials in split order (fixed, so results do not depend
@@ -794,14 +993,24 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const GemmParams p) {
     if ((p.N & 3) == 0) {
         const int64_t idx = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
         if (idx >= MN) return;
-        float4 v = *reinterpret_cast<const float4*>(p.partial + idx);
-        for (int s = 1; s < p.splits; ++s) {
-            const float4 w = *reinterpret_cast<const float4*>(p.partial + s * MN + idx);
-            v.x += w.x;
-            v.y += w.y;
-            v.z += w.z;
-            v.w += w.w;
+        const float4* src = reinterpret_cast<const float4*>(p.partial + idx);
+        const int64_t st = MN / 4;
+        auto add = [](float4& a, const float4& b) {
+            a.x += b.x;
+            a.y += b.y;
+            a.z += b.z;
+            a.w += b.w;
+        };
+        float4 v = src[0];
+        int s = 1;
+        for (; s + 4 <= p.splits; s += 4) {  // four loads in flight, added in split order
+            const float4 w0 = src[s * st], w1 = src[(s + 1) * st], w2 = src[(s + 2) * st], w3 = src[(s + 3) * st];
+            add(v, w0);
+            add(v, w1);
+            add(v, w2);
+            add(v, w3);
         }
+        for (; s < p.splits; ++s) add(v, src[s * st]);
         const int row = int(idx / p.N), col = int(idx % p.N);
         store_out(p, 0, 0, row, col, v.x);
         store_out(p, 0, 0, row, col + 1, v.y);
@@ -859,6 +1068,19 @@ static void launch_fast(const GemmParams& p, int tiles, hipStream_t s) {
     }
     hipLaunchKernelGGL(k_nf4_tile<BKIND>, dim3(tiles, p.splits), dim3(fast::NTH), fast::LDS_BYTES, s, p);
 }
+template <int BKIND>
+static void launch_wide(const GemmParams& p, int tiles, hipStream_t s) {
+    static bool allowed[64] = {};
+    int dev = 0;
+    QLX_CHECK_HIP(hipGetDevice(&dev));
+    QLX_REQUIRE(dev >= 0 && dev < 64, QLX_EUNSUPPORTED, "gemm: device index out of range");
+    if (!allowed[dev]) {
+        QLX_CHECK_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_nf4_wide<BKIND>),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, wide::LDS_BYTES));
+        allowed[dev] = true;
+    }
+    hipLaunchKernelGGL(k_nf4_wide<BKIND>, dim3(tiles, p.splits), dim3(wide::NTH), wide::LDS_BYTES, s, p);
+}
 static bool aligned8(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 7) == 0; }
 
 void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStream_t s) {
@@ -882,33 +1104,62 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
                          p.b_vec && aligned16(p.absmax) && p.nf4_cols % 64 == 0 &&
                          int64_t(p.M) * p.lda * 2 < (int64_t(1) << 31) &&
                          int64_t(p.N) * p.K / 2 < (int64_t(1) << 31);  // never depends on the slab
-    const TileCfg tc = fast_ok ? TileCfg{fast::BM, fast::BN} : pick_tile(p, bkind);
+    // Skinny dense products (the LoRA terms: one side is r, 2r or 3r) are
+    // bound by reading the long operand; 64 x 64 tiles with a K split keep
+    // many workgroups streaming it without a large partial buffer.
+    const bool skinny = !nf4 && te == TE_BF16 && p.batch == 1 && p.causal == CAUSAL_NONE && std::min(p.M, p.N) <= 256;
+    const TileCfg tc = fast_ok ? TileCfg{fast::BM, fast::BN} : skinny ? TileCfg{64, 64} : pick_tile(p, bkind);
     const int gx = (p.N + tc.bn - 1) / tc.bn, gy = (p.M + tc.bm - 1) / tc.bm;
     // split-K when the grid would leave CUs idle: shapes decide, nothing else
     p.splits = 1;
     p.kchunk = ((p.K + BK - 1) / BK) * BK;
-    const int tiles = gx * gy;
+    int tiles = gx * gy;
+    bool wide_tile = false;
     if (fast_ok) {
         // One workgroup fits a CU, so the grid runs in rounds of 256. Pick the
-        // split count with the least estimated time, in units of one 64-wide
-        // chunk of one tile: rounds x (chunks per split + ~3 of pipeline fill
-        // and epilogue) + the reduce pass (fp32 partials at ~4 TB/s, a chunk
-        // being ~1.35 us, plus ~2 chunks of launch). Shapes decide, nothing else.
-        if (partial_ws) {
-            const int nch = p.K / 64;
-            const double mn = double(p.M) * p.N;
-            double best = 1e300;
-            int best_s = 1;
+        // tile (256 x 128, or 512 x 128 when M allows) and split count with the
+        // least estimated time, in units of one 64-wide chunk of a 256 x 128
+        // tile: rounds x (chunks per split + ~3 of pipeline fill and epilogue)
+        // x tile cost (1.85 for the wide tile: twice the work at ~8% better
+        // throughput, fitted to the 8B-shaped projections; it must also win by
+        // 3%) + the reduce pass (fp32 partials at ~4 TB/s, a chunk being
+        // ~1.35 us, plus ~2 chunks of launch). Shapes decide, nothing else.
+        const int nch = p.K / 64;
+        const double mn = double(p.M) * p.N;
+        double best = 1e300;
+        int best_s = 1;
+        for (int wide = 0; wide < 2; ++wide) {
+            if (wide && p.M % wide::BM != 0) continue;
+            const int bm = wide ? wide::BM : fast::BM;
+            const int t = (p.M / bm) * (p.N / fast::BN);
+            const double unit = wide ? 1.85 * 1.03 : 1.0;
             for (int sp = 1; sp <= 16 && nch / sp >= 4; ++sp) {
-                if (sp > 1 && size_t(sp) * tiles * tc.bm * tc.bn > kGemmPartialFloats) break;
+                if (sp > 1 && (!partial_ws || size_t(sp) * p.M * p.N > kGemmPartialFloats)) break;
                 const int per = (nch + sp - 1) / sp;
-                const double rounds = double((tiles * sp + 255) / 256);
-                double cost = rounds * (per + 3.0);
+                const double rounds = double((t * sp + 255) / 256);
+                double cost = rounds * (per + 3.0) * unit;
                 if (sp > 1) cost += mn * 4.0 * (sp + 1) / 4e12 / 1.35e-6 + 2.0;
-                if (cost < best - 1e-9) best = cost, best_s = sp;
+                if (cost < best - 1e-9) best = cost, best_s = sp, wide_tile = wide;
             }
-            if (best_s > 1) {
-                const int kc = (nch + best_s - 1) / best_s * 64;
+        }
+        if (best_s > 1) {
+            const int kc = (nch + best_s - 1) / best_s * 64;
+            p.kchunk = kc;
+            p.splits = (p.K + kc - 1) / kc;
+            p.partial = partial_ws;
+        }
+        if (wide_tile) tiles = (p.M / wide::BM) * (p.N / fast::BN);
+        } else if (skinny) {
+        // measured on the 8B-shaped LoRA products: at least 512 workgroups
+        // (four fit a CU), at most 2048 of K per split, at least 256
+        if (partial_ws) {
+            int sp = 1;
+            while (sp < 16 && tiles * sp < 512) sp *= 2;
+            while (sp < 16 && p.K / sp > 2048) sp *= 2;
+            sp = std::min(sp, std::max(1, p.K / 256));
+            while (sp > 1 && size_t(sp) * tiles * tc.bm * tc.bn > kGemmPartialFloats) sp /= 2;
+            if (sp > 1) {
+                const int kc = (((p.K + sp - 1) / sp) + BK - 1) / BK * BK;
                 p.kchunk = kc;
                 p.splits = (p.K + kc - 1) / kc;
                 p.partial = partial_ws;
@@ -951,24 +1202,27 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
         switch (key) {
             case A_ROW * 100 + B_NF4_NT * 10 + TE_BF16:
                 if (fast_ok)
-                    launch_fast<B_NF4_NT>(p, tiles, s);
+                    wide_tile ? launch_wide<B_NF4_NT>(p, tiles, s) : launch_fast<B_NF4_NT>(p, tiles, s);
                 else
                     launch_kind<A_ROW, B_NF4_NT, TE_BF16>(p, tc, bsz, s);
                 break;
             case A_ROW * 100 + B_NF4_NN * 10 + TE_BF16:
                 if (fast_ok)
-                    launch_fast<B_NF4_NN>(p, tiles, s);
+                    wide_tile ? launch_wide<B_NF4_NN>(p, tiles, s) : launch_fast<B_NF4_NN>(p, tiles, s);
                 else
                     launch_kind<A_ROW, B_NF4_NN, TE_BF16>(p, tc, bsz, s);
                 break;
             case A_ROW * 100 + B_DENSE_NT * 10 + TE_BF16:
-                launch_cfg<A_ROW, B_DENSE_NT, TE_BF16, 128, 128, 64, 64>(p, bsz, s);
+                if (tc.bm == 64) launch_cfg<A_ROW, B_DENSE_NT, TE_BF16, 64, 64, 32, 32>(p, bsz, s);
+                else launch_cfg<A_ROW, B_DENSE_NT, TE_BF16, 128, 128, 64, 64>(p, bsz, s);
                 break;
             case A_ROW * 100 + B_DENSE_NN * 10 + TE_BF16:
-                launch_cfg<A_ROW, B_DENSE_NN, TE_BF16, 128, 128, 64, 64>(p, bsz, s);
+                if (tc.bm == 64) launch_cfg<A_ROW, B_DENSE_NN, TE_BF16, 64, 64, 32, 32>(p, bsz, s);
+                else launch_cfg<A_ROW, B_DENSE_NN, TE_BF16, 128, 128, 64, 64>(p, bsz, s);
                 break;
             case A_TRANS * 100 + B_DENSE_NN * 10 + TE_BF16:
-                launch_cfg<A_TRANS, B_DENSE_NN, TE_BF16, 128, 128, 64, 64>(p, bsz, s);
+                if (tc.bm == 64) launch_cfg<A_TRANS, B_DENSE_NN, TE_BF16, 64, 64, 32, 32>(p, bsz, s);
+                else launch_cfg<A_TRANS, B_DENSE_NN, TE_BF16, 128, 128, 64, 64>(p, bsz, s);
                 break;
             case A_ROW * 100 + B_DENSE_NT * 10 + TE_F16:
                 launch_cfg<A_ROW, B_DENSE_NT, TE_F16, 128, 128, 64, 64>(p, bsz, s);

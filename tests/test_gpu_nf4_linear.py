@@ -73,9 +73,12 @@ def _oracle_linear(xb, W_deq, A, B, s):
 # projection (blocks straddle rows), and 8B-shaped q / down projections.
 # (256, 384, 640, 8): full-tile kernel both ways, 6 and 10 K chunks (the
 # pipeline runs in steps of three); (256, 1216, 384, 8): split-K into 10 + 9
-# chunks; the 4096 / 14336 shapes split-K an 8B-width projection.
+# chunks; (512, 256, 16640, 8) forward and (512, 16640, 256, 8) dX: 260
+# tiles of 256 x 128 (two rounds), so the 512 x 128 tile runs them; the
+# 4096 / 14336 shapes split-K an 8B-width projection.
 SHAPES = [(64, 256, 512, 8), (37, 688, 256, 8), (200, 256, 1376, 16), (130, 96, 200, 4),
-          (256, 384, 640, 8), (256, 1216, 384, 8), (512, 4096, 4096, 64), (512, 14336, 4096, 64)]
+          (256, 384, 640, 8), (256, 1216, 384, 8), (512, 256, 16640, 8), (512, 16640, 256, 8),
+          (512, 4096, 4096, 64), (512, 14336, 4096, 64)]
 
 
 @pytest.mark.parametrize("T,in_f,out_f,r", SHAPES)
@@ -112,7 +115,7 @@ def test_qlora_linear_fwd_bwd_vs_oracle(T, in_f, out_f, r):
 
 # (256, 512, 256, 8): full-tile kernel with a slab that is not a whole K chunk
 @pytest.mark.parametrize("T,in_f,out_f,r", [(64, 256, 512, 8), (256, 512, 256, 8), (256, 384, 640, 8),
-                                           (512, 4096, 4096, 64)])
+                                           (512, 256, 16640, 8), (512, 16640, 256, 8), (512, 4096, 4096, 64)])
 def test_lora_zero_B_is_bit_exact_base_and_lora_off(T, in_f, out_f, r):
     wb = _w_bits(out_f, in_f, 5)
     W = q.NF4Matrix.quantize(bf16_dev(wb))
