@@ -11,9 +11,12 @@ prompts, beta 0.1).
 
 Prints ONE JSON line. `value` is tokens/s over the timed steps (inputs
 resident: weights in pinned host RAM as the method keeps them, tokens on the
-device). `roofline` reports the dominant kernel (the fused NF4-dequant MFMA
-GEMM) from HIP events recorded around every launch during the timed steps;
-`cpu_baseline` times the oracle on a bounded sample on this host.
+device). During the timed steps the library brackets only the fused
+NF4-dequant MFMA GEMMs with HIP events (every other kernel runs with none);
+`roofline` reports the dominant one of them from those events. One further,
+untimed step with events around every kernel gives the per-kernel table
+(`kernels`, `gpu_time`). `cpu_baseline` times the oracle on a bounded sample
+on this host.
 """
 from __future__ import annotations
 
@@ -173,9 +176,11 @@ def gemm_shapes(q) -> dict:
             pr = B_.profile_end()
             row = {}
             for k, lab in (("gemm_nf4_nt", "fwd"), ("gemm_nf4_nn", "dx")):
-                v = pr[k]
-                row[lab + "_us"] = round(1000 * v["ms"] / v["launches"], 1)
-                row[lab + "_TFLOPs"] = round(v["flops"] / v["ms"] / 1e9, 1)
+                rows = [v for name_, v in pr.items() if name_.startswith(k)]  # 256- or 512-row tile
+                ms, n, fl = (sum(v[f] for v in rows) for f in ("ms", "launches", "flops"))
+                row[lab + "_us"] = round(1000 * ms / n, 1)
+                row[lab + "_TFLOPs"] = round(fl / ms / 1e9, 1)
+                row[lab + "_tile"] = "512x128" if any(nm.endswith("_wide") for nm in pr if nm.startswith(k)) else "256x128"
             if "splitk_reduce" in pr:
                 row["splitk_reduce_us_per_launch"] = round(1000 * pr["splitk_reduce"]["ms"] / pr["splitk_reduce"]["launches"], 1)
             out[f"T{T}_{name}"] = row
@@ -264,7 +269,7 @@ def main() -> int:
         log(f"warmup {i + 1}/{args.warmup}: {st['step_ms']:.1f} ms, loss {loss.item():.4f}")
     torch.cuda.synchronize()
     if not args.no_profile:
-        B_.profile_begin()
+        B_.profile_begin("gemm_nf4")  # events around the NF4 GEMMs only
     stats = []
     t_start = time.perf_counter()
     for i in range(args.steps):
@@ -272,27 +277,34 @@ def main() -> int:
         stats.append(ctx.sync())
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    prof = B_.profile_end() if not args.no_profile else {}
+    live = B_.profile_end() if not args.no_profile else {}
     ms_step = 1000.0 * elapsed / args.steps
     value = tokens_per_step * args.steps / elapsed
     log(f"timed {args.steps} steps: {ms_step:.1f} ms/step, {value:.1f} tokens/s, loss {loss.item():.4f}")
+    prof = {}
+    if not args.no_profile:  # one more step, untimed, with events around every kernel
+        B_.profile_begin()
+        step()
+        ctx.sync()
+        torch.cuda.synchronize()
+        prof = B_.profile_end()
 
     reads = stats[-1]["layer_reads"]
     h2d_ms = float(np.mean([s["h2d_ms"] for s in stats]))
     h2d_bytes = stats[-1]["h2d_bytes"]
-    gemm_ms = sum(v["ms"] for k, v in prof.items() if k.startswith("gemm")) / max(args.steps, 1)
-    gemm_tf = sum(v["flops"] for k, v in prof.items() if k.startswith("gemm")) / max(args.steps, 1)
-    all_kernel_ms = sum(v["ms"] for v in prof.values()) / max(args.steps, 1)
+    gemm_ms = sum(v["ms"] for k, v in prof.items() if k.startswith("gemm"))
+    gemm_tf = sum(v["flops"] for k, v in prof.items() if k.startswith("gemm"))
+    all_kernel_ms = sum(v["ms"] for v in prof.values())
     roofline = None
-    if prof:
-        dom = max((k for k in prof if k.startswith("gemm_nf4")), key=lambda k: prof[k]["ms"])
-        p = prof[dom]
+    if live:
+        dom = max(live, key=lambda k: live[k]["ms"])
+        p = live[dom]
         ach = p["flops"] / (p["ms"] * 1e-3) / 1e12
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
                     "launches": p["launches"], "avg_launch_us": round(1000.0 * p["ms"] / p["launches"], 2),
                     "flops_per_launch": p["flops"] / p["launches"]}
-    kernels = {k: {"launches_per_step": v["launches"] // args.steps, "ms_per_step": round(v["ms"] / args.steps, 3),
+    kernels = {k: {"launches_per_step": v["launches"], "ms_per_step": round(v["ms"], 3),
                    "TFLOP/s": round(v["flops"] / max(v["ms"], 1e-9) / 1e9, 2),
                    "GB/s": round(v["bytes"] / max(v["ms"], 1e-9) / 1e6, 1)}
                for k, v in sorted(prof.items(), key=lambda kv: -kv[1]["ms"])}

@@ -252,6 +252,11 @@ typedef struct {
 } qlx_kernel_prof;
 
 int qlx_profile_begin(void);
+/* As qlx_profile_begin(), but only kernels whose row name starts with
+ * `name_prefix` are bracketed (the others run with no events at all), so a
+ * timed loop can measure one kernel family at almost no cost to the rest.
+ * NULL or "" selects every kernel. The prefix is copied. */
+int qlx_profile_begin_prefix(const char* name_prefix);
 int qlx_profile_end(qlx_kernel_prof* out, int max_out, int* count);
 
 #ifdef __cplusplus

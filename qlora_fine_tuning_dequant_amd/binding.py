@@ -27,7 +27,7 @@ EXPORTED = (
     "qlx_last_error", "qlx_version", "nf4_quantize", "nf4_dequant", "qlx_linear_workspace_bytes",
     "qlora_linear_fwd", "qlora_linear_bwd", "qlx_layer_blob_layout", "qlx_layer_workspace_bytes",
     "layer_fwd", "layer_bwd", "qlx_ctx_create", "qlx_ctx_destroy", "qlx_ctx_sync",
-    "qlx_step_workspace_bytes", "stream_step_sft", "stream_step_dpo", "qlx_profile_begin", "qlx_profile_end",
+    "qlx_step_workspace_bytes", "stream_step_sft", "stream_step_dpo", "qlx_profile_begin", "qlx_profile_begin_prefix", "qlx_profile_end",
 )
 
 
@@ -111,6 +111,7 @@ def lib() -> C.CDLL:
         "stream_step_dpo": (i32, [vp, C.POINTER(Model), vp, vp, i32, i32, i32, f32, i32, i32, vp, vp,
                                   C.POINTER(LoraGrad), vp, sz, vp]),
         "qlx_profile_begin": (i32, []),
+        "qlx_profile_begin_prefix": (i32, [C.c_char_p]),
         "qlx_profile_end": (i32, [C.POINTER(KernelProf), i32, C.POINTER(C.c_int)]),
     }
     for name, (res, args) in sig.items():
@@ -359,8 +360,13 @@ def stream_step_dpo(ctx: Context, model: StreamModel, chosen: torch.Tensor, reje
 
 
 # ------------------------------------------------------------------ profiling
-def profile_begin() -> None:
-    _check(lib().qlx_profile_begin())
+def profile_begin(prefix: str | None = None) -> None:
+    """Start per-kernel event timing; with `prefix`, only kernels whose row
+    name starts with it are timed (the rest run with no events)."""
+    if prefix:
+        _check(lib().qlx_profile_begin_prefix(prefix.encode()))
+    else:
+        _check(lib().qlx_profile_begin())
 
 
 def profile_end() -> dict:

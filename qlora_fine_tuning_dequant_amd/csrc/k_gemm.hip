@@ -25,6 +25,8 @@
 #include <algorithm>
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "nf4_codes.h"
 #include "qlx_internal.h"
 
@@ -1056,7 +1058,7 @@ static bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 
 // The full-tile kernel takes 160 KB of dynamic LDS, which each device has to
 // allow once per kernel before the first launch.
 template <int BKIND>
-static void launch_fast(const GemmParams& p, int tiles, hipStream_t s) {
+static void launch_fast(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {
     static bool allowed[64] = {};
     int dev = 0;
     QLX_CHECK_HIP(hipGetDevice(&dev));
@@ -1066,10 +1068,11 @@ static void launch_fast(const GemmParams& p, int tiles, hipStream_t s) {
                                           hipFuncAttributeMaxDynamicSharedMemorySize, fast::LDS_BYTES));
         allowed[dev] = true;
     }
-    hipLaunchKernelGGL(k_nf4_tile<BKIND>, dim3(tiles, p.splits), dim3(fast::NTH), fast::LDS_BYTES, s, p);
+    hipExtLaunchKernelGGL(k_nf4_tile<BKIND>, dim3(tiles, p.splits), dim3(fast::NTH), fast::LDS_BYTES, s, prof.start(),
+                          prof.stop(), 0, p);
 }
 template <int BKIND>
-static void launch_wide(const GemmParams& p, int tiles, hipStream_t s) {
+static void launch_wide(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {
     static bool allowed[64] = {};
     int dev = 0;
     QLX_CHECK_HIP(hipGetDevice(&dev));
@@ -1079,7 +1082,8 @@ static void launch_wide(const GemmParams& p, int tiles, hipStream_t s) {
                                           hipFuncAttributeMaxDynamicSharedMemorySize, wide::LDS_BYTES));
         allowed[dev] = true;
     }
-    hipLaunchKernelGGL(k_nf4_wide<BKIND>, dim3(tiles, p.splits), dim3(wide::NTH), wide::LDS_BYTES, s, p);
+    hipExtLaunchKernelGGL(k_nf4_wide<BKIND>, dim3(tiles, p.splits), dim3(wide::NTH), wide::LDS_BYTES, s, prof.start(),
+                          prof.stop(), 0, p);
 }
 static bool aligned8(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 7) == 0; }
 
@@ -1194,21 +1198,22 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
                                     (p.R ? M * N * 4 : 0) + (p.K2 ? (M + N) * p.K2 * 2.0 : 0));
     static const char* kNames[] = {"gemm_nf4_nt", "gemm_nf4_nn", "gemm_bf16_nt", "gemm_bf16_nn",
                                    "gemm_bf16_tn", "gemm_f16_nt", "gemm_f16_nn", "gemm_other"};
+    static const char* kWideNames[] = {"gemm_nf4_nt_wide", "gemm_nf4_nn_wide"};
     const int ni = key == 0 ? 0 : key == 10 ? 1 : key == 20 ? 2 : key == 30 ? 3 : key == 130 ? 4
                  : key == 21 ? 5 : key == 31 ? 6 : 7;
     const int bsz = p.batch * p.splits;
     {
-        ProfScope prof(p.tag ? p.tag : kNames[ni], flops, bytes, s);
+        ProfScope prof(p.tag ? p.tag : (wide_tile ? kWideNames[ni] : kNames[ni]), flops, bytes, s, fast_ok);
         switch (key) {
             case A_ROW * 100 + B_NF4_NT * 10 + TE_BF16:
                 if (fast_ok)
-                    wide_tile ? launch_wide<B_NF4_NT>(p, tiles, s) : launch_fast<B_NF4_NT>(p, tiles, s);
+                    wide_tile ? launch_wide<B_NF4_NT>(p, tiles, s, prof) : launch_fast<B_NF4_NT>(p, tiles, s, prof);
                 else
                     launch_kind<A_ROW, B_NF4_NT, TE_BF16>(p, tc, bsz, s);
                 break;
             case A_ROW * 100 + B_NF4_NN * 10 + TE_BF16:
                 if (fast_ok)
-                    wide_tile ? launch_wide<B_NF4_NN>(p, tiles, s) : launch_fast<B_NF4_NN>(p, tiles, s);
+                    wide_tile ? launch_wide<B_NF4_NN>(p, tiles, s, prof) : launch_fast<B_NF4_NN>(p, tiles, s, prof);
                 else
                     launch_kind<A_ROW, B_NF4_NN, TE_BF16>(p, tc, bsz, s);
                 break;

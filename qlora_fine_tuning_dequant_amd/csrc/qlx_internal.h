@@ -30,10 +30,16 @@ void check_launch(const char* what);
 
 // Brackets one kernel launch with timing events when profiling is on.
 struct ProfScope {
-    ProfScope(const char* name, double flops, double bytes, hipStream_t s);
+    // ext: the launcher records the pair itself through hipExtLaunchKernel
+    // (start() / stop(), null when this launch is not profiled), which times
+    // the kernel's own execution rather than the stream between two markers
+    ProfScope(const char* name, double flops, double bytes, hipStream_t s, bool ext = false);
     ~ProfScope();
+    hipEvent_t start() const;
+    hipEvent_t stop() const;
     hipStream_t s_;
     int64_t idx_ = -1;
+    bool ext_ = false;
 };
 
 // ---------------------------------------------------------- workspace carving
