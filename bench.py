@@ -5,7 +5,8 @@ Default workload: one streamed SFT step of a 32-layer Llama-3.1-8B-shaped
 model (hidden 4096, 32/8 heads, head_dim 128, SwiGLU 14336, vocab 128256),
 NF4 base layers in pinned host RAM fed to the GPU one decoder layer at a time,
 LoRA r 64 / alpha 16 on all 7 projections resident, batch 1, sequence 512,
-seeded synthetic weights and uniform random tokens (seed 1). Other workloads:
+seeded synthetic weights and uniform random tokens (seed 1); each step ends
+with the AdamW update of every LoRA factor (lr 2e-5). Other workloads:
 --workload sft8b_b4 (batch 4) and dpo8b (2 preference pairs, 128-token
 prompts, beta 0.1).
 
@@ -34,6 +35,7 @@ METRIC = "train tokens/s, streamed NF4+LoRA Llama-8B-shape step; % bf16 MFMA pea
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBPS = 8000.0
 SEED = 1
+LR = 2e-5  # the pages' learning rate (AdamW, betas 0.9 / 0.999, eps 1e-8, no weight decay)
 
 WORKLOADS = {
     "sft8b_b1": dict(kind="sft", batch=1, seq=512,
@@ -199,6 +201,8 @@ def main() -> int:
                     help="DPO reference schedule: fused with the policy forward, or a separate pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timing")
+    ap.add_argument("--no-optimizer", action="store_true",
+                    help="leave the AdamW update out of the step (loss + LoRA gradients only)")
     ap.add_argument("--gemm-shapes", action="store_true",
                     help="only time the 8B-shaped NF4 GEMMs (fwd and dX) at 512 and 2048 tokens")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -242,6 +246,8 @@ def main() -> int:
     mode = B_.QLX_STREAMED if args.mode == "streamed" else B_.QLX_RESIDENT
     ctx = q.Context(0)
     grads = [q.LoraGrads(l) for l in m.lora]
+    # the step's optimizer update: AdamW on every LoRA factor at the pages' lr
+    opt = None if args.no_optimizer else q.AdamW(d, m.lora, lr=LR)
     loss = torch.empty(1, dtype=torch.float32, device=dev)
     batch, seq = wl["batch"], wl["seq"]
     if wl["kind"] == "sft":
@@ -251,6 +257,8 @@ def main() -> int:
 
         def step():
             q.stream_step_sft(ctx, m, toks, mode, loss, grads, ws)
+            if opt:
+                opt.step(grads)
     else:
         pairs = batch
         ch, rj = synth.dpo_pairs(SEED, pairs, seq, wl["prompt"], d.vocab)
@@ -262,6 +270,8 @@ def main() -> int:
 
         def step():
             q.stream_step_dpo(ctx, m, ch, rj, wl["prompt"], wl["beta"], mode, sched, loss, logps, grads, ws)
+            if opt:
+                opt.step(grads)
 
     for i in range(args.warmup):
         step()
@@ -314,6 +324,7 @@ def main() -> int:
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl["name"], "global_batch": batch if wl["kind"] == "sft" else 2 * batch,
                    "seq_len": seq, "mode": args.mode, "layers": d.n_layers, "lora_r": d.lora_r,
+                   "optimizer": None if args.no_optimizer else f"adamw lr {LR}",
                    **({"dpo_reference": args.dpo_ref} if wl["kind"] == "dpo" else {})},
         "roofline": roofline,
         "stream": {"layer_reads_per_step": reads, "h2d_GB_per_step": round(h2d_bytes / 1e9, 3),

@@ -235,6 +235,34 @@ int stream_step_dpo(qlx_ctx* ctx, const qlx_model* model, const int32_t* chosen,
                     const qlx_lora_grad* grads, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Optimizer update of the training step: AdamW on every LoRA factor.
+ * The pages set the learning rate (2e-5, training section of the example
+ * configuration: guillermodelpino.com article, "Qué es Soup") and name no
+ * optimizer; the reading is AdamW with decoupled weight decay (Loshchilov &
+ * Hutter, "Decoupled Weight Decay Regularization", Algorithm 2), the decay
+ * scaled by lr as in PyTorch's AdamW, bias-corrected moments:
+ *   theta <- theta (1 - lr wd); m <- b1 m + (1-b1) g; v <- b2 v + (1-b2) g^2;
+ *   theta <- theta - lr/(1 - b1^t) * m / (sqrt(v)/sqrt(1 - b2^t) + eps).
+ * params, m, v: arrays of dims->n_layers qlx_lora_buf, each pointer a DEVICE
+ *   fp32 tensor laid out like the LoRA factor (A[p] [r, in_p], B[p] [out_p, r]),
+ *   updated in place (params are the same memory the model's qlx_lora
+ *   points to). m and v start at zero.
+ * grads: dims->n_layers qlx_lora_grad from the step.
+ * t: 1-based count of updates so far including this one (t >= 1).
+ * cfg: lr >= 0, 0 <= beta1, beta2 < 1, eps > 0, weight_decay >= 0.
+ * Tensors whose length is a multiple of 4 must be 16-byte aligned. One
+ * launch per layer on `stream`; QLX_EINVAL on bad arguments (nothing runs).
+ * ------------------------------------------------------------------------- */
+/* double so that 1 - beta is formed before any rounding (1 - fp32(0.999) is
+ * off by 1.3e-5); the kernel computes in fp32 */
+typedef struct { double lr, beta1, beta2, eps, weight_decay; } qlx_adamw_cfg;
+typedef struct { float* A[7]; float* B[7]; } qlx_lora_buf;
+
+int qlx_adamw_lora(const qlx_dims* dims, const qlx_lora_buf* params, const qlx_lora_grad* grads,
+                   const qlx_lora_buf* m, const qlx_lora_buf* v, int64_t t, const qlx_adamw_cfg* cfg,
+                   void* stream);
+
+/* ---------------------------------------------------------------------------
  * Per-kernel timing (observability). Between qlx_profile_begin() and
  * qlx_profile_end() every kernel the library launches is bracketed by a pair
  * of HIP events on its own stream; qlx_profile_end() waits for them and

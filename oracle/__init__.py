@@ -31,6 +31,8 @@ the published methods fill in the mathematics):
   * Llama decoder: RMSNorm (Zhang & Sennrich, 2019), RoPE rotate-half
     (Su et al., 2021), SwiGLU (Shazeer, 2020), grouped-query attention.
   * DPO (Rafailov et al., 2023), the sigmoid objective (equation 7).
+  * AdamW (Kingma & Ba, Algorithm 1; Loshchilov & Hutter, Algorithm 2) for
+    the optimizer update (the pages give only the learning rate).
 
 Parity status per function is stated in each module header; functions with
 no independent pin say "parity unpinned".
@@ -43,5 +45,6 @@ from .layer import (rmsnorm_fwd, rmsnorm_bwd, rope_cos_sin, rope_fwd, rope_bwd,
                     dequant_layer)
 from .model import (embed, head_ce, seq_logprobs, dpo_loss, model_forward,
                     sft_step, dpo_step)
+from .optim import adamw, adamw_lora
 
 __all__ = [n for n in dir() if not n.startswith("_")]

@@ -27,7 +27,7 @@ EXPORTED = (
     "qlx_last_error", "qlx_version", "nf4_quantize", "nf4_dequant", "qlx_linear_workspace_bytes",
     "qlora_linear_fwd", "qlora_linear_bwd", "qlx_layer_blob_layout", "qlx_layer_workspace_bytes",
     "layer_fwd", "layer_bwd", "qlx_ctx_create", "qlx_ctx_destroy", "qlx_ctx_sync",
-    "qlx_step_workspace_bytes", "stream_step_sft", "stream_step_dpo", "qlx_profile_begin", "qlx_profile_begin_prefix", "qlx_profile_end",
+    "qlx_step_workspace_bytes", "stream_step_sft", "stream_step_dpo", "qlx_profile_begin", "qlx_profile_begin_prefix", "qlx_profile_end", "qlx_adamw_lora",
 )
 
 
@@ -61,6 +61,15 @@ class Lora(C.Structure):
 
 class LoraGrad(C.Structure):
     _fields_ = [("dA", C.c_void_p * 7), ("dB", C.c_void_p * 7)]
+
+
+class LoraBuf(C.Structure):
+    _fields_ = [("A", C.c_void_p * 7), ("B", C.c_void_p * 7)]
+
+
+class AdamwCfg(C.Structure):
+    _fields_ = [("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double), ("eps", C.c_double),
+                ("weight_decay", C.c_double)]
 
 
 class Stats(C.Structure):
@@ -112,6 +121,8 @@ def lib() -> C.CDLL:
                                   C.POINTER(LoraGrad), vp, sz, vp]),
         "qlx_profile_begin": (i32, []),
         "qlx_profile_begin_prefix": (i32, [C.c_char_p]),
+        "qlx_adamw_lora": (i32, [C.POINTER(Dims), C.POINTER(LoraBuf), C.POINTER(LoraGrad), C.POINTER(LoraBuf),
+                                 C.POINTER(LoraBuf), C.c_int64, C.POINTER(AdamwCfg), C.c_void_p]),
         "qlx_profile_end": (i32, [C.POINTER(KernelProf), i32, C.POINTER(C.c_int)]),
     }
     for name, (res, args) in sig.items():
@@ -256,6 +267,43 @@ class LoraGrads:
 
     def c(self) -> LoraGrad:
         return LoraGrad((C.c_void_p * 7)(*[_ptr(a) for a in self.dA]), (C.c_void_p * 7)(*[_ptr(b) for b in self.dB]))
+
+
+def _lora_buf(A: Sequence[torch.Tensor], B: Sequence[torch.Tensor]) -> LoraBuf:
+    return LoraBuf((C.c_void_p * 7)(*[_ptr(a) for a in A]), (C.c_void_p * 7)(*[_ptr(b) for b in B]))
+
+
+def adamw_lora(dims, params: Sequence[LoraLayer], grads: Sequence[LoraGrads], m: Sequence[LoraLayer],
+               v: Sequence[LoraLayer], t: int, lr: float, beta1: float = 0.9, beta2: float = 0.999,
+               eps: float = 1e-8, weight_decay: float = 0.0, stream=None) -> None:
+    """qlx_adamw_lora: one AdamW update of every LoRA factor in place (params
+    are the model's LoraLayer tensors; m, v LoraLayer-shaped moment buffers)."""
+    d = Dims.of(dims)
+    L = d.n_layers
+    if not (len(params) == len(grads) == len(m) == len(v) == L):
+        raise ValueError("params, grads, m, v need one entry per layer")
+    P = (LoraBuf * L)(*[_lora_buf(x.A, x.B) for x in params])
+    G = (LoraGrad * L)(*[g.c() for g in grads])
+    Mb = (LoraBuf * L)(*[_lora_buf(x.A, x.B) for x in m])
+    Vb = (LoraBuf * L)(*[_lora_buf(x.A, x.B) for x in v])
+    cfg = AdamwCfg(lr, beta1, beta2, eps, weight_decay)
+    _check(lib().qlx_adamw_lora(C.byref(d), P, G, Mb, Vb, int(t), C.byref(cfg), _stream(stream)))
+
+
+class AdamW:
+    """AdamW state for a list of LoraLayer (zero moments, step count)."""
+
+    def __init__(self, dims, params: Sequence[LoraLayer], lr: float = 2e-5, beta1: float = 0.9,
+                 beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 0.0):
+        self.dims, self.params = dims, list(params)
+        self.m = [LoraLayer([torch.zeros_like(a) for a in p.A], [torch.zeros_like(b) for b in p.B]) for p in params]
+        self.v = [LoraLayer([torch.zeros_like(a) for a in p.A], [torch.zeros_like(b) for b in p.B]) for p in params]
+        self.t = 0
+        self.hp = dict(lr=lr, beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay)
+
+    def step(self, grads: Sequence[LoraGrads], stream=None) -> None:
+        self.t += 1
+        adamw_lora(self.dims, self.params, grads, self.m, self.v, self.t, stream=stream, **self.hp)
 
 
 def layer_workspace_bytes(dims, batch: int, seq: int) -> int:

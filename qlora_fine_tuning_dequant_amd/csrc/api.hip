@@ -773,3 +773,50 @@ int stream_step_dpo(qlx_ctx* ctx, const qlx_model* m, const int32_t* chosen, con
 }
 
 }  // extern "C"
+
+extern "C" int qlx_adamw_lora(const qlx_dims* d, const qlx_lora_buf* params, const qlx_lora_grad* grads,
+                              const qlx_lora_buf* m, const qlx_lora_buf* v, int64_t t, const qlx_adamw_cfg* cfg,
+                              void* stream) {
+    return guarded([&] {
+        validate_dims(d);
+        REQ_PTR(params, "params");
+        REQ_PTR(grads, "grads");
+        REQ_PTR(m, "m");
+        REQ_PTR(v, "v");
+        REQ_PTR(cfg, "cfg");
+        QLX_REQUIRE(t >= 1, QLX_EINVAL, "adamw: t (1-based update count) must be >= 1");
+        QLX_REQUIRE(std::isfinite(cfg->lr) && cfg->lr >= 0.0, QLX_EINVAL, "adamw: lr must be finite and >= 0");
+        QLX_REQUIRE(cfg->beta1 >= 0.0 && cfg->beta1 < 1.0 && cfg->beta2 >= 0.0 && cfg->beta2 < 1.0, QLX_EINVAL,
+                    "adamw: betas must lie in [0, 1)");
+        QLX_REQUIRE(std::isfinite(cfg->eps) && cfg->eps > 0.0, QLX_EINVAL, "adamw: eps must be finite and > 0");
+        QLX_REQUIRE(std::isfinite(cfg->weight_decay) && cfg->weight_decay >= 0.0, QLX_EINVAL,
+                    "adamw: weight_decay must be finite and >= 0");
+        const int L = d->n_layers, r = d->lora_r;
+        for (int l = 0; l < L; ++l) {
+            validate_grads(&grads[l]);
+            for (int p = 0; p < 7; ++p)
+                QLX_REQUIRE(params[l].A[p] && params[l].B[p] && m[l].A[p] && m[l].B[p] && v[l].A[p] && v[l].B[p],
+                            QLX_EINVAL, "adamw: every params/m/v A[p], B[p] must be set");
+        }
+        const LayerGeom g = make_geom(*d, 1, 1);
+        AdamScalars c;
+        c.decay = float(1.0 - cfg->lr * cfg->weight_decay);
+        c.b1 = float(cfg->beta1);
+        c.one_m_b1 = float(1.0 - cfg->beta1);
+        c.b2 = float(cfg->beta2);
+        c.one_m_b2 = float(1.0 - cfg->beta2);
+        c.step_size = float(cfg->lr / (1.0 - std::pow(cfg->beta1, double(t))));
+        c.inv_bc2_sqrt = float(1.0 / std::sqrt(1.0 - std::pow(cfg->beta2, double(t))));
+        c.eps = float(cfg->eps);
+        const hipStream_t s = static_cast<hipStream_t>(stream);
+        for (int l = 0; l < L; ++l) {
+            AdamTensor ts[14];
+            for (int p = 0; p < 7; ++p) {
+                ts[2 * p] = {params[l].A[p], grads[l].dA[p], m[l].A[p], v[l].A[p], int64_t(r) * g.in[p]};
+                ts[2 * p + 1] = {params[l].B[p], grads[l].dB[p], m[l].B[p], v[l].B[p], int64_t(g.out[p]) * r};
+            }
+            launch_adamw(ts, 14, c, s);
+        }
+    });
+}
+

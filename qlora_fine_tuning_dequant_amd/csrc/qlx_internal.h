@@ -117,6 +117,26 @@ struct GemmParams {
 constexpr size_t kGemmPartialFloats = size_t(1024) * 128 * 128;
 void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStream_t s);
 
+// ---------------------------------------------------------------- AdamW
+struct AdamTensor {
+    float* p;
+    const float* g;
+    float* m;
+    float* v;
+    int64_t n;
+};
+// per-step constants, computed on the host in double
+struct AdamScalars {
+    float decay;         // 1 - lr * weight_decay
+    float b1, one_m_b1;  // beta1, 1 - beta1
+    float b2, one_m_b2;  // beta2, 1 - beta2
+    float step_size;     // lr / (1 - beta1^t)
+    float inv_bc2_sqrt;  // 1 / sqrt(1 - beta2^t)
+    float eps;
+};
+constexpr int kAdamMaxTensors = 14;
+void launch_adamw(const AdamTensor* ts, int n, const AdamScalars& c, hipStream_t s);
+
 // ---------------------------------------------------------------- elementwise
 void launch_rmsnorm_fwd(const float* x, const float* g, int T, int H, float eps, void* out, int out_f16,
                         float* rstd, hipStream_t s);
