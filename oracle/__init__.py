@@ -31,6 +31,8 @@ the published methods fill in the mathematics):
   * Llama decoder: RMSNorm (Zhang & Sennrich, 2019), RoPE rotate-half
     (Su et al., 2021), SwiGLU (Shazeer, 2020), grouped-query attention.
   * DPO (Rafailov et al., 2023), the sigmoid objective (equation 7).
+  * ORPO (Hong et al., 2024), SimPO (Meng et al., 2024), KTO (Ethayarajh et
+    al., 2024) for the other preference objectives the pages list.
   * AdamW (Kingma & Ba, Algorithm 1; Loshchilov & Hutter, Algorithm 2) for
     the optimizer update (the pages give only the learning rate).
 
@@ -44,7 +46,8 @@ from .layer import (rmsnorm_fwd, rmsnorm_bwd, rope_cos_sin, rope_fwd, rope_bwd,
                     qlora_linear_fwd, qlora_linear_bwd, layer_fwd, layer_bwd,
                     dequant_layer)
 from .model import (embed, head_ce, seq_logprobs, dpo_loss, model_forward,
-                    sft_step, dpo_step)
+                    sft_step, dpo_step, pref_step)
+from .preference import orpo_loss, simpo_loss, kto_loss, kto_z0, kl_tokens
 from .optim import adamw, adamw_lora
 
 __all__ = [n for n in dir() if not n.startswith("_")]

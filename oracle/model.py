@@ -183,3 +183,45 @@ def dpo_step(model, lora, chosen, rejected, prompt_len, beta, d, dtype=np.float3
     grads = _backward_layers(model, lora, ckpt, dh, d, B, S, dtype)
     logps = np.concatenate([lp_pol[:P], lp_pol[P:], lp_ref[:P], lp_ref[P:]])
     return loss, logps, grads
+
+
+def pref_step(kind, model, lora, chosen, rejected, prompt_len, d, dtype=np.float32, z0_override=None, **hp):
+    """One preference step on the stream: kind "dpo" | "orpo" | "simpo" | "kto".
+    Returns (loss, logps [4P] = pol_c, pol_r, ref_c, ref_r (reference entries 0
+    for the reference-free kinds), grads). hp: the kind's hyperparameters.
+    z0_override (KTO only, for finite differences): use this z0."""
+    from .preference import kl_tokens, kto_loss, kto_z0, orpo_loss, simpo_loss
+    toks = np.concatenate([np.asarray(chosen), np.asarray(rejected)], axis=0)
+    B, S = toks.shape
+    P = B // 2
+    n = S - prompt_len
+    lp_ref = np.zeros(B)
+    if kind in ("dpo", "kto"):
+        href = model_forward(model, None, toks, d, dtype)
+        lp_ref = seq_logprobs(href, model["gf"], model["head"], toks, prompt_len, d.rms_eps)
+    hL, ckpt = model_forward(model, lora, toks, d, dtype, keep_ckpt=True)
+    lp_pol = seq_logprobs(hL, model["gf"], model["head"], toks, prompt_len, d.rms_eps)
+    if kind == "dpo":
+        loss, g = dpo_loss(lp_pol, lp_ref, hp.get("beta", 0.1))
+    elif kind == "orpo":
+        loss, g = orpo_loss(lp_pol, n, hp.get("lam", 0.1))
+    elif kind == "simpo":
+        loss, g = simpo_loss(lp_pol, n, hp.get("beta", 2.0), hp.get("gamma", 0.5))
+    elif kind == "kto":
+        if z0_override is None:
+            kt = kl_tokens(toks, prompt_len)
+            kp = seq_logprobs(model_forward(model, lora, kt, d, dtype), model["gf"], model["head"], kt, prompt_len,
+                              d.rms_eps)
+            kr = seq_logprobs(model_forward(model, None, kt, d, dtype), model["gf"], model["head"], kt, prompt_len,
+                              d.rms_eps)
+            z0 = kto_z0(kp, kr)
+        else:
+            z0 = z0_override
+        loss, g = kto_loss(lp_pol, lp_ref, z0, hp.get("beta", 0.1), hp.get("lam_d", 1.0), hp.get("lam_u", 1.0))
+    else:
+        raise ValueError(kind)
+    _, dh = seq_logprobs(hL, model["gf"], model["head"], toks, prompt_len, d.rms_eps, g=g.astype(dtype))
+    grads = _backward_layers(model, lora, ckpt, dh, d, B, S, dtype)
+    logps = np.concatenate([lp_pol[:P], lp_pol[P:], lp_ref[:P], lp_ref[P:]])
+    return loss, logps, grads
+
