@@ -7,8 +7,8 @@ NF4 base layers in pinned host RAM fed to the GPU one decoder layer at a time,
 LoRA r 64 / alpha 16 on all 7 projections resident, batch 1, sequence 512,
 seeded synthetic weights and uniform random tokens (seed 1); each step ends
 with the AdamW update of every LoRA factor (lr 2e-5). Other workloads:
---workload sft8b_b4 (batch 4) and dpo8b (2 preference pairs, 128-token
-prompts, beta 0.1).
+--workload sft8b_b4 (batch 4), dpo8b (2 preference pairs, 128-token
+prompts, beta 0.1), and orpo8b / simpo8b / kto8b on the same pairs.
 
 Prints ONE JSON line. `value` is tokens/s over the timed steps (inputs
 resident: weights in pinned host RAM as the method keeps them, tokens on the
@@ -44,6 +44,12 @@ WORKLOADS = {
                      name="streamed SFT step, 32-layer Llama-3.1-8B-shaped NF4 base + LoRA r64, batch 4, seq 512"),
     "dpo8b": dict(kind="dpo", batch=2, seq=512, prompt=128, beta=0.1,
                   name="streamed DPO step, 32-layer Llama-3.1-8B-shaped NF4 base + LoRA r64, 2 pairs x seq 512"),
+    "orpo8b": dict(kind="orpo", batch=2, seq=512, prompt=128,
+                   name="streamed ORPO step, 32-layer Llama-3.1-8B-shaped NF4 base + LoRA r64, 2 pairs x seq 512"),
+    "simpo8b": dict(kind="simpo", batch=2, seq=512, prompt=128,
+                    name="streamed SimPO step, 32-layer Llama-3.1-8B-shaped NF4 base + LoRA r64, 2 pairs x seq 512"),
+    "kto8b": dict(kind="kto", batch=2, seq=512, prompt=128,
+                  name="streamed KTO step, 32-layer Llama-3.1-8B-shaped NF4 base + LoRA r64, 2 pairs x seq 512"),
 }
 
 
@@ -265,11 +271,15 @@ def main() -> int:
         ch, rj = torch.from_numpy(ch).to(dev), torch.from_numpy(rj).to(dev)
         logps = torch.empty(4 * pairs, dtype=torch.float32, device=dev)
         sched = B_.QLX_DPO_REF_FUSED if args.dpo_ref == "fused" else B_.QLX_DPO_REF_SEPARATE
-        ws = B_.workspace(B_.step_workspace_bytes(d, 1, pairs, seq))
+        ws = B_.workspace(B_.step_workspace_bytes(d, 2 if wl["kind"] == "kto" else 1, pairs, seq))
         tokens_per_step = 2 * pairs * seq
 
         def step():
-            q.stream_step_dpo(ctx, m, ch, rj, wl["prompt"], wl["beta"], mode, sched, loss, logps, grads, ws)
+            if wl["kind"] == "dpo":
+                q.stream_step_dpo(ctx, m, ch, rj, wl["prompt"], wl["beta"], mode, sched, loss, logps, grads, ws)
+            else:  # ORPO, SimPO, KTO with the readings' hyperparameters
+                q.stream_step_pref(ctx, m, wl["kind"], ch, rj, wl["prompt"], mode, loss, logps, grads, ws,
+                                   ref_schedule=sched)
             if opt:
                 opt.step(grads)
 
@@ -325,7 +335,7 @@ def main() -> int:
         "config": {"workload": wl["name"], "global_batch": batch if wl["kind"] == "sft" else 2 * batch,
                    "seq_len": seq, "mode": args.mode, "layers": d.n_layers, "lora_r": d.lora_r,
                    "optimizer": None if args.no_optimizer else f"adamw lr {LR}",
-                   **({"dpo_reference": args.dpo_ref} if wl["kind"] == "dpo" else {})},
+                   **({"dpo_reference": args.dpo_ref} if wl["kind"] in ("dpo", "kto") else {})},
         "roofline": roofline,
         "stream": {"layer_reads_per_step": reads, "h2d_GB_per_step": round(h2d_bytes / 1e9, 3),
                    "h2d_ms_per_step": round(h2d_ms, 2),

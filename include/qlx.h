@@ -202,7 +202,10 @@ typedef struct {
 
 /* Workspace of a step: two device slots of one layer blob each (streamed
  * mode), n_layers+1 fp32 layer-boundary checkpoints, one layer's workspace
- * and the LM-head logits [T, vocab] fp32. kind: 0 = SFT, 1 = DPO (T = 2*pairs*seq). */
+ * and the LM-head logits [T, vocab] fp32. kind: 0 = SFT (batch = sequences),
+ * 1 = DPO, ORPO or SimPO, 2 = KTO (batch = pairs; T = 2*pairs*seq; KTO adds
+ * the mismatched pairs' tokens, two more fp32 hidden-state streams and
+ * their CE statistics). */
 size_t qlx_step_workspace_bytes(const qlx_dims* d, int kind, int batch, int seq);
 
 /* One SFT step: embedding, n_layers decoder layers streamed one at a time
@@ -233,6 +236,42 @@ int stream_step_dpo(qlx_ctx* ctx, const qlx_model* model, const int32_t* chosen,
                     const int32_t* rejected, int pairs, int seq, int prompt_len, float beta,
                     int mode, int ref_schedule, float* loss, float* logps,
                     const qlx_lora_grad* grads, void* ws, size_t ws_bytes, void* stream);
+
+/* The preference objectives the pages list on the same layer stream (rug.gal
+ * article, intro and "En detalle"; imasters article, "Do SFT para os métodos
+ * de preferência"): DPO, ORPO, SimPO and KTO, KTO with DPO's reference scheme
+ * (adapters off). Each loss is the published one, a function of per-sequence
+ * summed response log-probs s over n = seq - prompt_len tokens (l = s/n):
+ *   QLX_PREF_DPO   (Rafailov et al. 2023, eq. 7): as stream_step_dpo; beta.
+ *   QLX_PREF_ORPO  (Hong et al. 2024, eqs. 2-7): mean over pairs of
+ *     -l_c + beta * -log sigmoid(log odds_c - log odds_r),
+ *     log odds = l - log(1 - e^l); beta is ORPO's lambda (0.1). No reference.
+ *   QLX_PREF_SIMPO (Meng et al. 2024, eq. 6): mean over pairs of
+ *     -log sigmoid(beta (l_c - l_r) - gamma) (2.0, 0.5). No reference.
+ *   QLX_PREF_KTO   (Ethayarajh et al. 2024, eq. 8): chosen desirable,
+ *     rejected undesirable; r = s_pol - s_ref; z0 = max(0, mean over the
+ *     mismatched pairs (prompt j + completion (j+1) mod 2P) of s_pol - s_ref),
+ *     no gradient through z0; mean over examples of lambda_y - v with
+ *     v = lambda_d sigmoid(beta (r - z0)) or lambda_u sigmoid(beta (z0 - r))
+ *     (beta 0.1, lambdas 1).
+ * ref_schedule applies to DPO and KTO (QLX_DPO_REF_FUSED / _SEPARATE); the
+ * reference-free kinds read the stack as SFT does. logps as in
+ * stream_step_dpo (reference entries 0 for ORPO and SimPO). Workspace kind
+ * (qlx_step_workspace_bytes): 2 for KTO, 1 otherwise. Streamed and resident
+ * modes give identical bits. */
+enum { QLX_PREF_DPO = 0, QLX_PREF_ORPO = 1, QLX_PREF_SIMPO = 2, QLX_PREF_KTO = 3 };
+typedef struct {
+    int kind;
+    int ref_schedule;
+    float beta;
+    float gamma;
+    float lambda_d, lambda_u;
+} qlx_pref_cfg;
+
+int stream_step_pref(qlx_ctx* ctx, const qlx_model* model, const qlx_pref_cfg* cfg,
+                     const int32_t* chosen, const int32_t* rejected, int pairs, int seq,
+                     int prompt_len, int mode, float* loss, float* logps,
+                     const qlx_lora_grad* grads, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Optimizer update of the training step: AdamW on every LoRA factor.

@@ -20,6 +20,11 @@ QLX_OK, QLX_EINVAL, QLX_EUNSUPPORTED, QLX_EWORKSPACE, QLX_ENOTPINNED, QLX_EHIP =
 QLX_F32, QLX_BF16 = 0, 1
 QLX_STREAMED, QLX_RESIDENT = 0, 1
 QLX_DPO_REF_FUSED, QLX_DPO_REF_SEPARATE = 0, 1
+QLX_PREF_DPO, QLX_PREF_ORPO, QLX_PREF_SIMPO, QLX_PREF_KTO = 0, 1, 2, 3
+PREF_KINDS = {"dpo": QLX_PREF_DPO, "orpo": QLX_PREF_ORPO, "simpo": QLX_PREF_SIMPO, "kto": QLX_PREF_KTO}
+# the readings' default hyperparameters (beta, gamma, lambda_d, lambda_u)
+PREF_DEFAULTS = {"dpo": (0.1, 0.0, 1.0, 1.0), "orpo": (0.1, 0.0, 1.0, 1.0), "simpo": (2.0, 0.5, 1.0, 1.0),
+                 "kto": (0.1, 0.0, 1.0, 1.0)}
 BLOB_NSEG = 16
 PROJ = ("q", "k", "v", "o", "gate", "up", "down")
 
@@ -27,7 +32,7 @@ EXPORTED = (
     "qlx_last_error", "qlx_version", "nf4_quantize", "nf4_dequant", "qlx_linear_workspace_bytes",
     "qlora_linear_fwd", "qlora_linear_bwd", "qlx_layer_blob_layout", "qlx_layer_workspace_bytes",
     "layer_fwd", "layer_bwd", "qlx_ctx_create", "qlx_ctx_destroy", "qlx_ctx_sync",
-    "qlx_step_workspace_bytes", "stream_step_sft", "stream_step_dpo", "qlx_profile_begin", "qlx_profile_begin_prefix", "qlx_profile_end", "qlx_adamw_lora",
+    "qlx_step_workspace_bytes", "stream_step_sft", "stream_step_dpo", "stream_step_pref", "qlx_profile_begin", "qlx_profile_begin_prefix", "qlx_profile_end", "qlx_adamw_lora",
 )
 
 
@@ -70,6 +75,11 @@ class LoraBuf(C.Structure):
 class AdamwCfg(C.Structure):
     _fields_ = [("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double), ("eps", C.c_double),
                 ("weight_decay", C.c_double)]
+
+
+class PrefCfg(C.Structure):
+    _fields_ = [("kind", C.c_int), ("ref_schedule", C.c_int), ("beta", C.c_float), ("gamma", C.c_float),
+                ("lambda_d", C.c_float), ("lambda_u", C.c_float)]
 
 
 class Stats(C.Structure):
@@ -119,6 +129,8 @@ def lib() -> C.CDLL:
         "stream_step_sft": (i32, [vp, C.POINTER(Model), vp, i32, i32, i32, vp, C.POINTER(LoraGrad), vp, sz, vp]),
         "stream_step_dpo": (i32, [vp, C.POINTER(Model), vp, vp, i32, i32, i32, f32, i32, i32, vp, vp,
                                   C.POINTER(LoraGrad), vp, sz, vp]),
+        "stream_step_pref": (i32, [vp, C.POINTER(Model), C.POINTER(PrefCfg), vp, vp, i32, i32, i32, i32, vp, vp,
+                                   C.POINTER(LoraGrad), vp, sz, vp]),
         "qlx_profile_begin": (i32, []),
         "qlx_profile_begin_prefix": (i32, [C.c_char_p]),
         "qlx_adamw_lora": (i32, [C.POINTER(Dims), C.POINTER(LoraBuf), C.POINTER(LoraGrad), C.POINTER(LoraBuf),
@@ -405,6 +417,23 @@ def stream_step_dpo(ctx: Context, model: StreamModel, chosen: torch.Tensor, reje
     _check(lib().stream_step_dpo(ctx.h, C.byref(model.c), _ptr(chosen), _ptr(rejected), P, S, prompt_len,
                                  float(beta), mode, ref_schedule, _ptr(loss), _ptr(logps), ga, _ptr(ws),
                                  ws.numel(), _stream(stream)))
+
+
+def stream_step_pref(ctx: Context, model: StreamModel, kind: str, chosen: torch.Tensor, rejected: torch.Tensor,
+                     prompt_len: int, mode: int, loss: torch.Tensor, logps: torch.Tensor, grads: Sequence[LoraGrads],
+                     ws: torch.Tensor, ref_schedule: int = QLX_DPO_REF_FUSED, beta: float | None = None,
+                     gamma: float | None = None, lambda_d: float | None = None, lambda_u: float | None = None,
+                     stream=None) -> None:
+    """stream_step_pref: kind "dpo" | "orpo" | "simpo" | "kto"; unset
+    hyperparameters take the kind's defaults (PREF_DEFAULTS)."""
+    b0, g0, ld0, lu0 = PREF_DEFAULTS[kind]
+    cfg = PrefCfg(PREF_KINDS[kind], ref_schedule, b0 if beta is None else beta, g0 if gamma is None else gamma,
+                  ld0 if lambda_d is None else lambda_d, lu0 if lambda_u is None else lambda_u)
+    P, S = chosen.shape
+    ga = _grad_arr(grads)
+    _check(lib().stream_step_pref(ctx.h, C.byref(model.c), C.byref(cfg), _ptr(chosen), _ptr(rejected), P, S,
+                                  prompt_len, mode, _ptr(loss), _ptr(logps), ga, _ptr(ws), ws.numel(),
+                                  _stream(stream)))
 
 
 # ------------------------------------------------------------------ profiling

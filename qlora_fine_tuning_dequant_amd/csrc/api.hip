@@ -375,6 +375,10 @@ struct StepWs {
     float* dnf;  // [T, H]
     float* dh[2];
     float* gseq;
+    int32_t* kl_toks;                  // KTO only
+    float* hkl[2];                     // KTO: mismatched pairs, policy stream
+    float* hklr[2];                    // KTO: mismatched pairs, reference stream
+    float *kl_lse, *kl_pk, *kl_lse_r, *kl_pk_r;
 };
 
 static StepWs carve_step(Carver& c, const qlx_dims& d, int T, int kind, uint64_t blob_bytes) {
@@ -384,13 +388,24 @@ static StepWs carve_step(Carver& c, const qlx_dims& d, int T, int kind, uint64_t
     w.slot[0] = c.take<char>(blob_bytes);
     w.slot[1] = c.take<char>(blob_bytes);
     w.ckpt = c.take<float>((L + 1) * Tz * H);
-    if (kind == 1) {
+    if (kind >= 1) {
         w.href[0] = c.take<float>(Tz * H);
         w.href[1] = c.take<float>(Tz * H);
         w.toks = c.take<int32_t>(Tz);
         w.lse_ref = c.take<float>(Tz);
         w.pk_ref = c.take<float>(Tz);
         w.gseq = c.take<float>(64);
+    }
+    if (kind == 2) {  // KTO: the mismatched pairs' tokens, two forward streams and their CE stats
+        w.kl_toks = c.take<int32_t>(Tz);
+        for (int i = 0; i < 2; ++i) {
+            w.hkl[i] = c.take<float>(Tz * H);
+            w.hklr[i] = c.take<float>(Tz * H);
+        }
+        w.kl_lse = c.take<float>(Tz);
+        w.kl_pk = c.take<float>(Tz);
+        w.kl_lse_r = c.take<float>(Tz);
+        w.kl_pk_r = c.take<float>(Tz);
     }
     w.nf = c.take<uint16_t>(Tz * H);
     w.rstd_f = c.take<float>(Tz);
@@ -639,8 +654,8 @@ int qlx_ctx_sync(qlx_ctx* ctx, qlx_stats* stats) {
 }
 
 size_t qlx_step_workspace_bytes(const qlx_dims* d, int kind, int batch, int seq) {
-    if (!d || batch <= 0 || seq <= 0 || (kind != 0 && kind != 1)) return 0;
-    return step_ws_bytes(*d, kind, kind == 1 ? 2 * batch : batch, seq);
+    if (!d || batch <= 0 || seq <= 0 || kind < 0 || kind > 2) return 0;
+    return step_ws_bytes(*d, kind, kind >= 1 ? 2 * batch : batch, seq);
 }
 
 int stream_step_sft(qlx_ctx* ctx, const qlx_model* m, const int32_t* tokens, int batch, int seq, int mode,
@@ -690,85 +705,154 @@ int stream_step_sft(qlx_ctx* ctx, const qlx_model* m, const int32_t* tokens, int
     });
 }
 
-int stream_step_dpo(qlx_ctx* ctx, const qlx_model* m, const int32_t* chosen, const int32_t* rejected, int pairs,
-                    int seq, int prompt_len, float beta, int mode, int ref_schedule, float* loss, float* logps,
-                    const qlx_lora_grad* grads, void* ws, size_t ws_bytes, void* stream) {
-    return guarded([&] {
-        validate_model(ctx, m, mode);
-        QLX_REQUIRE(pairs > 0 && pairs <= 32, QLX_EINVAL, "pairs must be in 1..32");
-        validate_bs(2 * pairs, seq);
-        QLX_REQUIRE(prompt_len >= 1 && prompt_len < seq, QLX_EINVAL, "prompt_len must be in [1, seq)");
-        QLX_REQUIRE(ref_schedule == QLX_DPO_REF_FUSED || ref_schedule == QLX_DPO_REF_SEPARATE, QLX_EINVAL,
-                    "ref_schedule");
-        QLX_REQUIRE(beta == beta, QLX_EINVAL, "beta is NaN");
-        REQ_PTR(chosen, "chosen");
-        REQ_PTR(rejected, "rejected");
-        REQ_PTR(loss, "loss");
-        REQ_PTR(logps, "logps");
-        REQ_PTR(grads, "grads");
-        for (int i = 0; i < m->dims.n_layers; ++i) validate_grads(&grads[i]);
-        const qlx_dims& d = m->dims;
-        const int B = 2 * pairs;
-        check_ws(ws, ws_bytes, step_ws_bytes(d, 1, B, seq));
-        hipStream_t s = static_cast<hipStream_t>(stream);
-        uint64_t off[QLX_BLOB_NSEG], blob_bytes;
-        blob_layout(d, off, &blob_bytes);
-        const int T = B * seq;
-        Carver c(ws);
-        StepWs w = carve_step(c, d, T, 1, blob_bytes);
-        const LayerGeom g = make_geom(d, B, seq);
-        w.lw = carve_layer(c, g);
-        const size_t TH = size_t(T) * d.hidden;
-        const int L = d.n_layers;
+// One preference step: DPO, ORPO, SimPO or KTO on the same layer stream.
+// The reference-free kinds (ORPO, SimPO) skip the reference pass; KTO adds
+// forward-only passes over the mismatched pairs (policy and reference) for z0.
+static void pref_step(qlx_ctx* ctx, const qlx_model* m, const qlx_pref_cfg& cfg, const int32_t* chosen,
+                      const int32_t* rejected, int pairs, int seq, int prompt_len, int mode, float* loss, float* logps,
+                      const qlx_lora_grad* grads, void* ws, size_t ws_bytes, hipStream_t s) {
+    validate_model(ctx, m, mode);
+    QLX_REQUIRE(pairs > 0 && pairs <= 32, QLX_EINVAL, "pairs must be in 1..32");
+    validate_bs(2 * pairs, seq);
+    QLX_REQUIRE(prompt_len >= 1 && prompt_len < seq, QLX_EINVAL, "prompt_len must be in [1, seq)");
+    QLX_REQUIRE(cfg.kind >= QLX_PREF_DPO && cfg.kind <= QLX_PREF_KTO, QLX_EINVAL, "preference kind");
+    QLX_REQUIRE(cfg.ref_schedule == QLX_DPO_REF_FUSED || cfg.ref_schedule == QLX_DPO_REF_SEPARATE, QLX_EINVAL,
+                "ref_schedule");
+    QLX_REQUIRE(std::isfinite(cfg.beta) && std::isfinite(cfg.gamma) && std::isfinite(cfg.lambda_d) &&
+                    std::isfinite(cfg.lambda_u),
+                QLX_EINVAL, "preference hyperparameters must be finite");
+    REQ_PTR(chosen, "chosen");
+    REQ_PTR(rejected, "rejected");
+    REQ_PTR(loss, "loss");
+    REQ_PTR(logps, "logps");
+    REQ_PTR(grads, "grads");
+    for (int i = 0; i < m->dims.n_layers; ++i) validate_grads(&grads[i]);
+    const qlx_dims& d = m->dims;
+    const int B = 2 * pairs;
+    const bool kto = cfg.kind == QLX_PREF_KTO;
+    const bool need_ref = cfg.kind == QLX_PREF_DPO || kto;
+    const int wkind = kto ? 2 : 1;
+    check_ws(ws, ws_bytes, step_ws_bytes(d, wkind, B, seq));
+    uint64_t off[QLX_BLOB_NSEG], blob_bytes;
+    blob_layout(d, off, &blob_bytes);
+    const int T = B * seq;
+    Carver c(ws);
+    StepWs w = carve_step(c, d, T, wkind, blob_bytes);
+    const LayerGeom g = make_geom(d, B, seq);
+    w.lw = carve_layer(c, g);
+    const size_t TH = size_t(T) * d.hidden;
+    const int L = d.n_layers;
 
-        begin_step(ctx, s);
-        const size_t half = size_t(pairs) * seq * sizeof(int32_t);
-        QLX_CHECK_HIP(hipMemcpyAsync(w.toks, chosen, half, hipMemcpyDeviceToDevice, s));
-        QLX_CHECK_HIP(hipMemcpyAsync(w.toks + size_t(pairs) * seq, rejected, half, hipMemcpyDeviceToDevice, s));
-        Streamer st(ctx, m, mode, w, blob_bytes, s);
-        launch_embed(w.toks, m->embed_f16, T, d.hidden, d.vocab, w.ckpt, s);
-        const int start = prompt_len - 1;
-        float* ref_cur = w.ckpt;  // reference and policy share h_0
-        float* ref_nxt = w.href[0];
-        if (ref_schedule == QLX_DPO_REF_SEPARATE) {
-            st.prefetch(0);
-            for (int i = 0; i < L; ++i) {
-                const void* blob = st.acquire(i);
-                st.prefetch(i + 1);
-                layer_forward(g, blob_ptrs(d, blob), nullptr, false, ref_cur, ref_nxt, w.lw, s);
-                st.release(i);
-                ref_cur = ref_nxt;
-                ref_nxt = (ref_cur == w.href[0]) ? w.href[1] : w.href[0];
-            }
-            st.forget();  // the policy pass streams the stack again from layer 0
-        }
+    begin_step(ctx, s);
+    const size_t half = size_t(pairs) * seq * sizeof(int32_t);
+    QLX_CHECK_HIP(hipMemcpyAsync(w.toks, chosen, half, hipMemcpyDeviceToDevice, s));
+    QLX_CHECK_HIP(hipMemcpyAsync(w.toks + size_t(pairs) * seq, rejected, half, hipMemcpyDeviceToDevice, s));
+    Streamer st(ctx, m, mode, w, blob_bytes, s);
+    launch_embed(w.toks, m->embed_f16, T, d.hidden, d.vocab, w.ckpt, s);
+    // forward streams besides the policy's checkpoints: (input, ping, pong, lora)
+    struct Fwd {
+        float* cur;
+        float* buf[2];
+        const bool lora;
+    };
+    std::vector<Fwd> extra;
+    if (need_ref) extra.push_back(Fwd{w.ckpt, {w.href[0], w.href[1]}, false});  // reference shares h_0
+    if (kto) {
+        launch_kl_tokens(w.toks, B, seq, prompt_len, w.kl_toks, s);
+        launch_embed(w.kl_toks, m->embed_f16, T, d.hidden, d.vocab, w.hklr[0], s);
+        QLX_CHECK_HIP(hipMemcpyAsync(w.hkl[0], w.hklr[0], TH * sizeof(float), hipMemcpyDeviceToDevice, s));
+        extra.push_back(Fwd{w.hklr[0], {w.hklr[1], w.hklr[0]}, false});  // mismatched pairs, reference
+        extra.push_back(Fwd{w.hkl[0], {w.hkl[1], w.hkl[0]}, true});      // mismatched pairs, policy
+    }
+    auto advance = [&](Fwd& f, const BlobPtrs& wt, int i) {
+        float* nxt = (f.cur == f.buf[0]) ? f.buf[1] : f.buf[0];
+        layer_forward(g, wt, f.lora ? &m->lora[i] : nullptr, false, f.cur, nxt, w.lw, s);
+        f.cur = nxt;
+    };
+    const bool separate = need_ref && cfg.ref_schedule == QLX_DPO_REF_SEPARATE;
+    if (separate) {  // the forward-only streams first, then the policy pass streams the stack again
         st.prefetch(0);
         for (int i = 0; i < L; ++i) {
             const void* blob = st.acquire(i);
             st.prefetch(i + 1);
             const BlobPtrs wt = blob_ptrs(d, blob);
-            if (ref_schedule == QLX_DPO_REF_FUSED) {
-                layer_forward(g, wt, nullptr, false, ref_cur, ref_nxt, w.lw, s);
-                ref_cur = ref_nxt;
-                ref_nxt = (ref_cur == w.href[0]) ? w.href[1] : w.href[0];
-            }
-            layer_forward(g, wt, &m->lora[i], false, w.ckpt + size_t(i) * TH, w.ckpt + size_t(i + 1) * TH, w.lw, s);
+            for (Fwd& f : extra) advance(f, wt, i);
             st.release(i);
         }
-        // reference log-probs
-        head_logits(m, ref_cur, T, w, w.lw.partial, s);
+        st.forget();
+    }
+    st.prefetch(0);
+    for (int i = 0; i < L; ++i) {
+        const void* blob = st.acquire(i);
+        st.prefetch(i + 1);
+        const BlobPtrs wt = blob_ptrs(d, blob);
+        if (!separate)
+            for (Fwd& f : extra) advance(f, wt, i);
+        layer_forward(g, wt, &m->lora[i], false, w.ckpt + size_t(i) * TH, w.ckpt + size_t(i + 1) * TH, w.lw, s);
+        st.release(i);
+    }
+    const int start = prompt_len - 1;
+    if (need_ref) {  // reference log-probs
+        head_logits(m, extra[0].cur, T, w, w.lw.partial, s);
         launch_ce_stats(w.logits, T, d.vocab, w.toks, seq, start, w.lse_ref, w.pk_ref, s);
-        // policy log-probs, loss, and dL/dlp
-        const float* hL = w.ckpt + size_t(L) * TH;
-        head_logits(m, hL, T, w, w.lw.partial, s);
-        launch_ce_stats(w.logits, T, d.vocab, w.toks, seq, start, w.lse, w.picked, s);
-        launch_dpo_loss(w.lse, w.picked, w.lse_ref, w.pk_ref, pairs, seq, prompt_len, beta, loss, logps, w.gseq, s);
-        // dz = g_seq (onehot - softmax) = (softmax - onehot) * (-g_seq)
-        launch_ce_grad(w.logits, w.lse, T, d.vocab, w.toks, seq, start, 1, -kDzScale, w.gseq, w.dz, s);
-        head_backward(m, hL, T, 1.0f / kDzScale, w, w.dh[0], w.lw.partial, s);
-        ctx->stats.layer_passes = 3 * L;
-        backward_layers(st, m, g, w, w.dh[0], grads, s);
-        end_step(ctx, s);
+    }
+    if (kto) {  // mismatched pairs: reference, then policy
+        head_logits(m, extra[1].cur, T, w, w.lw.partial, s);
+        launch_ce_stats(w.logits, T, d.vocab, w.kl_toks, seq, start, w.kl_lse_r, w.kl_pk_r, s);
+        head_logits(m, extra[2].cur, T, w, w.lw.partial, s);
+        launch_ce_stats(w.logits, T, d.vocab, w.kl_toks, seq, start, w.kl_lse, w.kl_pk, s);
+    }
+    // policy log-probs, loss, and dL/dlp
+    const float* hL = w.ckpt + size_t(L) * TH;
+    head_logits(m, hL, T, w, w.lw.partial, s);
+    launch_ce_stats(w.logits, T, d.vocab, w.toks, seq, start, w.lse, w.picked, s);
+    PrefLossArgs la{};
+    la.lse_p = w.lse;
+    la.pk_p = w.picked;
+    la.lse_r = need_ref ? w.lse_ref : nullptr;
+    la.pk_r = need_ref ? w.pk_ref : nullptr;
+    la.kl_lse_p = kto ? w.kl_lse : nullptr;
+    la.kl_pk_p = kto ? w.kl_pk : nullptr;
+    la.kl_lse_r = kto ? w.kl_lse_r : nullptr;
+    la.kl_pk_r = kto ? w.kl_pk_r : nullptr;
+    la.pairs = pairs;
+    la.seq = seq;
+    la.nresp = seq - prompt_len;
+    la.kind = cfg.kind;
+    la.beta = cfg.beta;
+    la.gamma = cfg.gamma;
+    la.lambda_d = cfg.lambda_d;
+    la.lambda_u = cfg.lambda_u;
+    la.loss = loss;
+    la.logps = logps;
+    la.gseq = w.gseq;
+    launch_pref_loss(la, s);
+    // dz = g_seq (onehot - softmax) = (softmax - onehot) * (-g_seq)
+    launch_ce_grad(w.logits, w.lse, T, d.vocab, w.toks, seq, start, 1, -kDzScale, w.gseq, w.dz, s);
+    head_backward(m, hL, T, 1.0f / kDzScale, w, w.dh[0], w.lw.partial, s);
+    ctx->stats.layer_passes = int64_t(2 + extra.size()) * L;
+    backward_layers(st, m, g, w, w.dh[0], grads, s);
+    end_step(ctx, s);
+}
+
+int stream_step_dpo(qlx_ctx* ctx, const qlx_model* m, const int32_t* chosen, const int32_t* rejected, int pairs,
+                    int seq, int prompt_len, float beta, int mode, int ref_schedule, float* loss, float* logps,
+                    const qlx_lora_grad* grads, void* ws, size_t ws_bytes, void* stream) {
+    return guarded([&] {
+        QLX_REQUIRE(beta == beta, QLX_EINVAL, "beta is NaN");
+        qlx_pref_cfg cfg{QLX_PREF_DPO, ref_schedule, beta, 0.f, 1.f, 1.f};
+        pref_step(ctx, m, cfg, chosen, rejected, pairs, seq, prompt_len, mode, loss, logps, grads, ws, ws_bytes,
+                  static_cast<hipStream_t>(stream));
+    });
+}
+
+int stream_step_pref(qlx_ctx* ctx, const qlx_model* m, const qlx_pref_cfg* cfg, const int32_t* chosen,
+                     const int32_t* rejected, int pairs, int seq, int prompt_len, int mode, float* loss, float* logps,
+                     const qlx_lora_grad* grads, void* ws, size_t ws_bytes, void* stream) {
+    return guarded([&] {
+        REQ_PTR(cfg, "cfg");
+        pref_step(ctx, m, *cfg, chosen, rejected, pairs, seq, prompt_len, mode, loss, logps, grads, ws, ws_bytes,
+                  static_cast<hipStream_t>(stream));
     });
 }
 

@@ -426,55 +426,129 @@ void launch_sft_loss(const float* lse, const float* picked, int T, int seq, floa
     check_launch("sft_loss");
 }
 
-// DPO (Rafailov et al. 2023, eq. 7). lp[b] = sum over response rows of
-// (picked - lse); Delta_i = (pol_c - ref_c) - (pol_r - ref_r);
-// loss = mean_i softplus(-beta Delta_i); gseq = dloss/dlp_pol.
-__global__ __launch_bounds__(256) void k_dpo_loss(const float* __restrict__ lse_p, const float* __restrict__ pk_p,
-                                                  const float* __restrict__ lse_r, const float* __restrict__ pk_r,
-                                                  int pairs, int seq, float beta, float* __restrict__ loss,
-                                                  float* __restrict__ logps, float* __restrict__ gseq) {
+// Preference losses from per-sequence summed response log-probs. One
+// workgroup: per-sequence sums of picked - lse (rows outside the response are
+// zero), then one thread evaluates the loss and dL/ds in double:
+//  DPO (Rafailov et al. 2023, eq. 7): mean over pairs of -log sigmoid(beta Delta).
+//  ORPO (Hong et al. 2024, eqs. 2-7): mean over pairs of -l_c + lambda *
+//    -log sigmoid(log odds_c - log odds_r), l = s/n, log odds = l - log(1 - e^l).
+//  SimPO (Meng et al. 2024, eq. 6): mean over pairs of
+//    -log sigmoid(beta (l_c - l_r) - gamma).
+//  KTO (Ethayarajh et al. 2024, eq. 8): r = s_pol - s_ref; z0 = max(0, mean
+//    of the mismatched pairs' s_pol - s_ref), constant for the gradient;
+//    mean over examples of lambda_y - v, v = lambda_D sigmoid(beta (r - z0))
+//    for chosen, lambda_U sigmoid(beta (z0 - r)) for rejected.
+// logps: [4P] policy chosen, policy rejected, reference chosen, reference
+// rejected (zeros for the reference-free kinds). gseq: dL/ds per sequence.
+namespace {
+__device__ inline double log_sigmoid(double x) { return (x >= 0.0) ? -log1p(exp(-x)) : x - log1p(exp(x)); }
+__device__ inline double sigmoid(double x) { return (x >= 0.0) ? 1.0 / (1.0 + exp(-x)) : exp(x) / (1.0 + exp(x)); }
+__device__ inline double log1mexp(double l) { return (l > -0.6931471805599453) ? log(-expm1(l)) : log1p(-exp(l)); }
+
+__device__ float seq_sum(const float* __restrict__ lse, const float* __restrict__ pk, int b, int seq, float* red) {
+    float a = 0.f;
+    for (int s = threadIdx.x; s < seq; s += 256) {
+        const int64_t t = int64_t(b) * seq + s;
+        a += pk[t] - lse[t];
+    }
+    return block_sum256(a, red);
+}
+}  // namespace
+
+__global__ __launch_bounds__(256) void k_pref_loss(PrefLossArgs a) {
     __shared__ float red[4];
-    __shared__ float lp[2][64];
-    const int nseq = 2 * pairs;
+    __shared__ float lp[4][64];  // policy, reference, KL policy, KL reference
+    const int nseq = 2 * a.pairs;
     for (int b = 0; b < nseq; ++b) {
-        float a = 0.f, c = 0.f;
-        for (int s = threadIdx.x; s < seq; s += 256) {
-            const int64_t t = int64_t(b) * seq + s;
-            a += pk_p[t] - lse_p[t];
-            c += pk_r[t] - lse_r[t];
-        }
-        a = block_sum256(a, red);
-        c = block_sum256(c, red);
+        const float p = seq_sum(a.lse_p, a.pk_p, b, a.seq, red);
+        const float r = a.lse_r ? seq_sum(a.lse_r, a.pk_r, b, a.seq, red) : 0.f;
+        const float kp = a.kl_lse_p ? seq_sum(a.kl_lse_p, a.kl_pk_p, b, a.seq, red) : 0.f;
+        const float kr = a.kl_lse_r ? seq_sum(a.kl_lse_r, a.kl_pk_r, b, a.seq, red) : 0.f;
         if (threadIdx.x == 0) {
-            lp[0][b] = a;
-            lp[1][b] = c;
+            lp[0][b] = p;
+            lp[1][b] = r;
+            lp[2][b] = kp;
+            lp[3][b] = kr;
         }
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        double tot = 0.0;
-        for (int i = 0; i < pairs; ++i) {
-            const float delta = (lp[0][i] - lp[1][i]) - (lp[0][pairs + i] - lp[1][pairs + i]);
-            const double x = double(beta) * double(delta);
+    if (threadIdx.x != 0) return;
+    const int P = a.pairs;
+    const double n = double(a.nresp), beta = a.beta;
+    double tot = 0.0;
+    if (a.kind == PREF_DPO) {
+        for (int i = 0; i < P; ++i) {
+            const float delta = (lp[0][i] - lp[1][i]) - (lp[0][P + i] - lp[1][P + i]);
+            const double x = beta * double(delta);
             tot += (x >= 0.0) ? log1p(exp(-x)) : (-x + log1p(exp(x)));
-            const double g = -double(beta) / (1.0 + exp(x)) / double(pairs);
-            gseq[i] = float(g);
-            gseq[pairs + i] = float(-g);
+            const double g = -beta / (1.0 + exp(x)) / double(P);
+            a.gseq[i] = float(g);
+            a.gseq[P + i] = float(-g);
         }
-        loss[0] = float(tot / double(pairs));
+        a.loss[0] = float(tot / double(P));
+    } else if (a.kind == PREF_ORPO) {
+        for (int i = 0; i < P; ++i) {
+            const double lc = double(lp[0][i]) / n, lr = double(lp[0][P + i]) / n;
+            const double z = (lc - log1mexp(lc)) - (lr - log1mexp(lr));
+            tot += -lc - beta * log_sigmoid(z);
+            const double sg = sigmoid(-z);
+            a.gseq[i] = float((-1.0 - beta * sg / (-expm1(lc))) / (double(P) * n));
+            a.gseq[P + i] = float((beta * sg / (-expm1(lr))) / (double(P) * n));
+        }
+        a.loss[0] = float(tot / double(P));
+    } else if (a.kind == PREF_SIMPO) {
+        for (int i = 0; i < P; ++i) {
+            const double u = beta * (double(lp[0][i]) / n - double(lp[0][P + i]) / n) - double(a.gamma);
+            tot += -log_sigmoid(u);
+            const double g = -sigmoid(-u) * beta / (double(P) * n);
+            a.gseq[i] = float(g);
+            a.gseq[P + i] = float(-g);
+        }
+        a.loss[0] = float(tot / double(P));
+    } else {  // KTO
+        double kl = 0.0;
+        for (int b = 0; b < nseq; ++b) kl += double(lp[2][b]) - double(lp[3][b]);
+        const double z0 = fmax(0.0, kl / double(nseq));
         for (int b = 0; b < nseq; ++b) {
-            logps[b] = lp[0][b];
-            logps[nseq + b] = lp[1][b];
+            const double r = double(lp[0][b]) - double(lp[1][b]);
+            const bool des = b < P;
+            const double lam = des ? a.lambda_d : a.lambda_u;
+            const double x = des ? beta * (r - z0) : beta * (z0 - r);
+            const double sx = sigmoid(x);
+            tot += lam - lam * sx;
+            const double g = lam * beta * sx * sigmoid(-x) / double(nseq);
+            a.gseq[b] = float(des ? -g : g);
         }
+        a.loss[0] = float(tot / double(nseq));
+    }
+    for (int b = 0; b < nseq; ++b) {
+        a.logps[b] = lp[0][b];
+        a.logps[nseq + b] = lp[1][b];
     }
 }
-void launch_dpo_loss(const float* lse_pol, const float* pk_pol, const float* lse_ref, const float* pk_ref, int pairs,
-                     int seq, int prompt_len, float beta, float* loss, float* logps, float* gseq, hipStream_t s) {
-    (void)prompt_len;
-    ProfScope prof("loss_reduce", 4.0 * seq * pairs * 2, 16.0 * seq * pairs * 2, s);
-    hipLaunchKernelGGL(k_dpo_loss, dim3(1), dim3(256), 0, s, lse_pol, pk_pol, lse_ref, pk_ref, pairs, seq, beta, loss,
-                       logps, gseq);
-    check_launch("dpo_loss");
+
+void launch_pref_loss(const PrefLossArgs& a, hipStream_t s) {
+    QLX_REQUIRE(a.pairs >= 1 && 2 * a.pairs <= 64, QLX_EINVAL, "pref loss: pairs must be in 1..32");
+    const int nstat = 2 + (a.lse_r ? 2 : 0) + (a.kl_lse_p ? 4 : 0);
+    ProfScope prof("loss_reduce", 2.0 * a.seq * a.pairs * nstat, 8.0 * a.seq * a.pairs * nstat, s);
+    hipLaunchKernelGGL(k_pref_loss, dim3(1), dim3(256), 0, s, a);
+    check_launch("pref_loss");
+}
+
+// KTO's mismatched pairs: sequence j = its own prompt followed by the
+// completion of sequence (j + 1) mod B.
+__global__ __launch_bounds__(256) void k_kl_tokens(const int32_t* __restrict__ toks, int B, int seq, int prompt_len,
+                                                   int32_t* __restrict__ out) {
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= int64_t(B) * seq) return;
+    const int b = int(i / seq), t = int(i % seq);
+    out[i] = (t < prompt_len) ? toks[i] : toks[int64_t((b + 1) % B) * seq + t];
+}
+void launch_kl_tokens(const int32_t* toks, int B, int seq, int prompt_len, int32_t* out, hipStream_t s) {
+    const int64_t n = int64_t(B) * seq;
+    ProfScope prof("kl_tokens", 0.0, 8.0 * n, s);
+    hipLaunchKernelGGL(k_kl_tokens, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, toks, B, seq, prompt_len, out);
+    check_launch("kl_tokens");
 }
 
 }  // namespace qlx

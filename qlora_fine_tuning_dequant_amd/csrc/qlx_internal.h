@@ -169,8 +169,19 @@ void launch_ce_stats(const float* logits, int T, int V, const int32_t* tokens, i
 void launch_ce_grad(const float* logits, const float* lse, int T, int V, const int32_t* tokens, int seq,
                     int prompt_len, int mode, float sc, const float* gseq, uint16_t* dz, hipStream_t s);
 void launch_sft_loss(const float* lse, const float* picked, int T, int seq, float* loss, hipStream_t s);
-void launch_dpo_loss(const float* lse_pol, const float* pk_pol, const float* lse_ref, const float* pk_ref,
-                     int pairs, int seq, int prompt_len, float beta, float* loss, float* logps, float* gseq,
-                     hipStream_t s);
+enum PrefKind { PREF_DPO = 0, PREF_ORPO = 1, PREF_SIMPO = 2, PREF_KTO = 3 };
+struct PrefLossArgs {
+    const float *lse_p, *pk_p;            // policy CE stats [2P*seq]
+    const float *lse_r, *pk_r;            // reference (DPO, KTO), else null
+    const float *kl_lse_p, *kl_pk_p;      // KTO mismatched pairs, policy, else null
+    const float *kl_lse_r, *kl_pk_r;      // KTO mismatched pairs, reference, else null
+    int pairs, seq, nresp, kind;
+    float beta, gamma, lambda_d, lambda_u;
+    float* loss;
+    float* logps;  // [4P]
+    float* gseq;   // [2P]
+};
+void launch_pref_loss(const PrefLossArgs& a, hipStream_t s);
+void launch_kl_tokens(const int32_t* toks, int B, int seq, int prompt_len, int32_t* out, hipStream_t s);
 
 }  // namespace qlx

@@ -1,0 +1,97 @@
+"""GPU parity of ORPO, SimPO and KTO steps on the layer stream against the
+oracle, and their exact cases: streamed == resident to the bit, layer reads,
+KTO = 1/2 when policy equals reference, SimPO = log(1 + e^gamma) when chosen
+equals rejected, DPO through stream_step_pref == stream_step_dpo."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import DEV, gpu_model, grad_errors, run_dpo, same_grads, to_np
+from helpers import lora_list, oracle_model
+
+pytestmark = pytest.mark.gpu
+q = pytest.importorskip("qlora_fine_tuning_dequant_amd")
+B_ = q.binding
+TOL = 2e-2
+HP = {"orpo": dict(lam=0.1), "simpo": dict(beta=2.0, gamma=0.5), "kto": dict(beta=0.1)}
+
+
+def run_pref(m, kind, ch, rj, prompt_len, mode, ref_schedule=B_.QLX_DPO_REF_FUSED, ctx=None, **kw):
+    d = m.dims
+    ctx = ctx or q.Context(0)
+    grads = [q.LoraGrads(l) for l in m.lora]
+    loss = torch.empty(1, dtype=torch.float32, device=DEV)
+    logps = torch.empty(4 * ch.shape[0], dtype=torch.float32, device=DEV)
+    ws = B_.workspace(B_.step_workspace_bytes(d, 2 if kind == "kto" else 1, ch.shape[0], ch.shape[1]))
+    q.stream_step_pref(ctx, m, kind, torch.from_numpy(ch).to(DEV), torch.from_numpy(rj).to(DEV), prompt_len, mode,
+                       loss, logps, grads, ws, ref_schedule=ref_schedule, **kw)
+    st = ctx.sync()
+    return loss, logps, grads, st
+
+
+@pytest.mark.parametrize("kind", ["orpo", "simpo", "kto"])
+def test_pref_step_vs_oracle_and_streamed_equals_resident(kind):
+    d = synth.TINY
+    m, host = gpu_model(q, d, 0, "normal")
+    ch, rj = synth.dpo_pairs(0, 2, 64, 16, d.vocab)
+    l_s, lp_s, g_s, st_s = run_pref(m.with_blobs(host), kind, ch, rj, 16, B_.QLX_STREAMED)
+    l_r, lp_r, g_r, _ = run_pref(m, kind, ch, rj, 16, B_.QLX_RESIDENT)
+    assert torch.equal(l_s, l_r) and torch.equal(lp_s, lp_r) and same_grads(g_s, g_r)
+    assert st_s["layer_reads"] == 2 * d.n_layers - 2
+    ref_loss, ref_lp, ref_g = oracle.pref_step(kind, oracle_model(d, 0), lora_list(d, 0, "normal"), ch, rj, 16, d,
+                                               **HP[kind])
+    assert abs(l_s.item() - ref_loss) < 1e-2, (l_s.item(), ref_loss)
+    assert np.max(np.abs(to_np(lp_s) - ref_lp)) < 0.05 * np.max(np.abs(ref_lp))
+    bad = {k: v for k, v in grad_errors(g_s, ref_g).items() if not v < TOL}
+    assert not bad, bad
+
+
+def test_layer_reads_and_kto_schedules_on_four_layers():
+    d = dataclasses.replace(synth.TINY, n_layers=4)
+    m, host = gpu_model(q, d, 1, "normal")
+    sm = m.with_blobs(host)
+    ch, rj = synth.dpo_pairs(1, 2, 32, 8, d.vocab)
+    for kind in ("orpo", "simpo"):
+        _, _, _, st = run_pref(sm, kind, ch, rj, 8, B_.QLX_STREAMED)
+        assert st["layer_reads"] == 2 * 4 - 2 and st["layer_passes"] == 2 * 4, kind
+    l_f, lp_f, g_f, st_f = run_pref(sm, "kto", ch, rj, 8, B_.QLX_STREAMED, B_.QLX_DPO_REF_FUSED)
+    l_p, lp_p, g_p, st_p = run_pref(sm, "kto", ch, rj, 8, B_.QLX_STREAMED, B_.QLX_DPO_REF_SEPARATE)
+    assert st_f["layer_reads"] == 2 * 4 - 2 and st_p["layer_reads"] == 3 * 4 - 2
+    assert st_f["layer_passes"] == 5 * 4
+    assert torch.equal(l_f, l_p) and torch.equal(lp_f, lp_p) and same_grads(g_f, g_p)
+
+
+def test_kto_is_exactly_half_when_policy_equals_reference():
+    d = synth.TINY
+    m, host = gpu_model(q, d, 2, "zeroB")
+    ch, rj = synth.dpo_pairs(2, 2, 64, 16, d.vocab)
+    loss, logps, _, _ = run_pref(m.with_blobs(host), "kto", ch, rj, 16, B_.QLX_STREAMED)
+    lp = to_np(logps)
+    assert np.array_equal(lp[:4], lp[4:])
+    assert loss.item() == 0.5
+
+
+def test_simpo_and_orpo_when_chosen_equals_rejected():
+    d = synth.TINY
+    m, host = gpu_model(q, d, 3, "normal")
+    ch, _ = synth.dpo_pairs(3, 2, 64, 16, d.vocab)
+    loss, _, _, _ = run_pref(m.with_blobs(host), "simpo", ch, ch, 16, B_.QLX_STREAMED)
+    assert loss.item() == float(np.float32(np.log1p(np.exp(0.5))))
+    loss, logps, _, _ = run_pref(m.with_blobs(host), "orpo", ch, ch, 16, B_.QLX_STREAMED)
+    n = 64 - 16
+    nll = -float(np.mean(to_np(logps)[:2])) / n
+    assert loss.item() == pytest.approx(nll + 0.1 * np.log(2.0), rel=1e-6)   # odds term is lambda ln 2
+
+
+def test_dpo_through_pref_equals_stream_step_dpo():
+    d = synth.TINY
+    m, host = gpu_model(q, d, 0, "normal")
+    sm = m.with_blobs(host)
+    ch, rj = synth.dpo_pairs(0, 2, 64, 16, d.vocab)
+    l1, lp1, g1, _ = run_dpo(q, sm, ch, rj, 16, 0.1, B_.QLX_STREAMED, B_.QLX_DPO_REF_FUSED)
+    l2, lp2, g2, _ = run_pref(sm, "dpo", ch, rj, 16, B_.QLX_STREAMED, beta=0.1)
+    assert torch.equal(l1, l2) and torch.equal(lp1, lp2) and same_grads(g1, g2)
