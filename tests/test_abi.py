@@ -100,8 +100,10 @@ def test_workspace_sizes_scale_with_tokens():
     assert 0 < w1 < w2
     s1 = L.qlx_step_workspace_bytes(C.byref(d), 0, 1, 64)
     s_dpo = L.qlx_step_workspace_bytes(C.byref(d), 1, 1, 64)
-    assert s1 > w1 and s_dpo > s1
-    assert L.qlx_step_workspace_bytes(C.byref(d), 2, 1, 64) == 0
+    s_kto = L.qlx_step_workspace_bytes(C.byref(d), 2, 1, 64)   # KTO adds the mismatched pairs' buffers
+    assert s1 > w1 and s_dpo > s1 and s_kto > s_dpo
+    assert L.qlx_step_workspace_bytes(C.byref(d), 3, 1, 64) == 0
+    assert L.qlx_step_workspace_bytes(C.byref(d), -1, 1, 64) == 0
 
 
 def test_product_path_fails_loudly_without_the_library(tmp_path, monkeypatch):
