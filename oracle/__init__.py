@@ -49,5 +49,6 @@ from .model import (embed, head_ce, seq_logprobs, dpo_loss, model_forward,
                     sft_step, dpo_step, pref_step)
 from .preference import orpo_loss, simpo_loss, kto_loss, kto_z0, kl_tokens
 from .optim import adamw, adamw_lora
+from .merge import lora_merge
 
 __all__ = [n for n in dir() if not n.startswith("_")]
