@@ -274,6 +274,28 @@ int stream_step_pref(qlx_ctx* ctx, const qlx_model* model, const qlx_pref_cfg* c
                      const qlx_lora_grad* grads, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Adapter merge (the pages' `soup merge`: guillermodelpino.com article,
+ * command list; imasters article, closing section): fold one trained LoRA
+ * adapter into its NF4 base matrix,
+ *   W_merged = W' + scale * B A,  W' = fl32(c[code] * absmax),
+ * summed in fp32 (B A accumulated over r in ascending order) and rounded once
+ * to bf16 (RNE).
+ * W: the NF4 matrix [rows, cols] (canonical layout; a projection inside a
+ *   stacked q|k|v or gate|up matrix is addressed by offsetting packed by
+ *   row0*cols/2 bytes and absmax by row0*cols/64 entries). A: DEVICE fp32
+ *   [r, cols]; B: DEVICE fp32 [rows, r].
+ * out_kind QLX_MERGE_BF16: out = DEVICE bf16 [rows, cols], out_absmax unused.
+ * out_kind QLX_MERGE_NF4:  out = DEVICE packed NF4 [rows*cols/2], out_absmax
+ *   = DEVICE fp32 [rows*cols/64]: the bf16 merged matrix re-quantized by
+ *   nf4_quantize's rules (needs qlx_merge_workspace_bytes of workspace).
+ * r >= 1; QLX_EINVAL on bad arguments (nothing runs).
+ * ------------------------------------------------------------------------- */
+enum { QLX_MERGE_BF16 = 0, QLX_MERGE_NF4 = 1 };
+size_t qlx_merge_workspace_bytes(int64_t rows, int64_t cols, int out_kind);
+int qlx_lora_merge(qlx_nf4 W, const float* A, const float* B, int r, float scale, int out_kind,
+                   void* out, float* out_absmax, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Optimizer update of the training step: AdamW on every LoRA factor.
  * The pages set the learning rate (2e-5, training section of the example
  * configuration: guillermodelpino.com article, "Qué es Soup") and name no

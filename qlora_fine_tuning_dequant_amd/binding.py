@@ -21,6 +21,7 @@ QLX_F32, QLX_BF16 = 0, 1
 QLX_STREAMED, QLX_RESIDENT = 0, 1
 QLX_DPO_REF_FUSED, QLX_DPO_REF_SEPARATE = 0, 1
 QLX_PREF_DPO, QLX_PREF_ORPO, QLX_PREF_SIMPO, QLX_PREF_KTO = 0, 1, 2, 3
+QLX_MERGE_BF16, QLX_MERGE_NF4 = 0, 1
 PREF_KINDS = {"dpo": QLX_PREF_DPO, "orpo": QLX_PREF_ORPO, "simpo": QLX_PREF_SIMPO, "kto": QLX_PREF_KTO}
 # the readings' default hyperparameters (beta, gamma, lambda_d, lambda_u)
 PREF_DEFAULTS = {"dpo": (0.1, 0.0, 1.0, 1.0), "orpo": (0.1, 0.0, 1.0, 1.0), "simpo": (2.0, 0.5, 1.0, 1.0),
@@ -32,7 +33,7 @@ EXPORTED = (
     "qlx_last_error", "qlx_version", "nf4_quantize", "nf4_dequant", "qlx_linear_workspace_bytes",
     "qlora_linear_fwd", "qlora_linear_bwd", "qlx_layer_blob_layout", "qlx_layer_workspace_bytes",
     "layer_fwd", "layer_bwd", "qlx_ctx_create", "qlx_ctx_destroy", "qlx_ctx_sync",
-    "qlx_step_workspace_bytes", "stream_step_sft", "stream_step_dpo", "stream_step_pref", "qlx_profile_begin", "qlx_profile_begin_prefix", "qlx_profile_end", "qlx_adamw_lora",
+    "qlx_step_workspace_bytes", "stream_step_sft", "stream_step_dpo", "stream_step_pref", "qlx_merge_workspace_bytes", "qlx_lora_merge", "qlx_profile_begin", "qlx_profile_begin_prefix", "qlx_profile_end", "qlx_adamw_lora",
 )
 
 
@@ -131,6 +132,8 @@ def lib() -> C.CDLL:
                                   C.POINTER(LoraGrad), vp, sz, vp]),
         "stream_step_pref": (i32, [vp, C.POINTER(Model), C.POINTER(PrefCfg), vp, vp, i32, i32, i32, i32, vp, vp,
                                    C.POINTER(LoraGrad), vp, sz, vp]),
+        "qlx_merge_workspace_bytes": (sz, [C.c_int64, C.c_int64, i32]),
+        "qlx_lora_merge": (i32, [NF4, vp, vp, i32, f32, i32, vp, vp, vp, sz, vp]),
         "qlx_profile_begin": (i32, []),
         "qlx_profile_begin_prefix": (i32, [C.c_char_p]),
         "qlx_adamw_lora": (i32, [C.POINTER(Dims), C.POINTER(LoraBuf), C.POINTER(LoraGrad), C.POINTER(LoraBuf),
@@ -208,6 +211,28 @@ class NF4Matrix:
 
     def c(self) -> NF4:
         return NF4(_ptr(self.packed), _ptr(self.absmax), self.rows, self.cols)
+
+
+def lora_merge(W: NF4Matrix, A: torch.Tensor, B: torch.Tensor, scale: float, to_nf4: bool = False,
+               stream=None):
+    """qlx_lora_merge: W' + scale * B A rounded to bf16 [rows, cols], or (to_nf4)
+    that matrix re-quantized to a new NF4Matrix."""
+    r = A.shape[0]
+    if A.shape != (r, W.cols) or B.shape != (W.rows, r):
+        raise ValueError("A must be [r, cols] and B [rows, r]")
+    dev = W.packed.device
+    if not to_nf4:
+        out = torch.empty(W.rows, W.cols, dtype=torch.bfloat16, device=dev)
+        _check(lib().qlx_lora_merge(W.c(), _ptr(A), _ptr(B), r, float(scale), QLX_MERGE_BF16, _ptr(out), None, None,
+                                    0, _stream(stream)))
+        return out
+    n = W.rows * W.cols
+    packed = torch.empty((n + 1) // 2, dtype=torch.uint8, device=dev)
+    absmax = torch.empty((n + 63) // 64, dtype=torch.float32, device=dev)
+    ws = workspace(int(lib().qlx_merge_workspace_bytes(W.rows, W.cols, QLX_MERGE_NF4)), dev)
+    _check(lib().qlx_lora_merge(W.c(), _ptr(A), _ptr(B), r, float(scale), QLX_MERGE_NF4, _ptr(packed), _ptr(absmax),
+                                _ptr(ws), ws.numel(), _stream(stream)))
+    return NF4Matrix(packed, absmax, W.rows, W.cols)
 
 
 # -------------------------------------------------------------- QLoRA linear

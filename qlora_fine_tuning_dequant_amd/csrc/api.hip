@@ -904,3 +904,35 @@ extern "C" int qlx_adamw_lora(const qlx_dims* d, const qlx_lora_buf* params, con
     });
 }
 
+extern "C" size_t qlx_merge_workspace_bytes(int64_t rows, int64_t cols, int out_kind) {
+    if (rows < 0 || cols < 0 || (out_kind != QLX_MERGE_BF16 && out_kind != QLX_MERGE_NF4)) return 0;
+    return out_kind == QLX_MERGE_NF4 ? size_t(rows) * size_t(cols) * 2 : 0;
+}
+
+extern "C" int qlx_lora_merge(qlx_nf4 W, const float* A, const float* B, int r, float scale, int out_kind, void* out,
+                              float* out_absmax, void* ws, size_t ws_bytes, void* stream) {
+    return guarded([&] {
+        QLX_REQUIRE(W.rows >= 0 && W.cols >= 0, QLX_EINVAL, "merge: negative size");
+        QLX_REQUIRE(out_kind == QLX_MERGE_BF16 || out_kind == QLX_MERGE_NF4, QLX_EINVAL, "merge: out_kind");
+        QLX_REQUIRE(r >= 1, QLX_EINVAL, "merge: r must be >= 1");
+        QLX_REQUIRE(std::isfinite(scale), QLX_EINVAL, "merge: scale must be finite");
+        const int64_t n = W.rows * W.cols;
+        if (n == 0) return;
+        REQ_PTR(W.packed, "W.packed");
+        REQ_PTR(W.absmax, "W.absmax");
+        REQ_PTR(A, "A");
+        REQ_PTR(B, "B");
+        REQ_PTR(out, "out");
+        const hipStream_t s = static_cast<hipStream_t>(stream);
+        if (out_kind == QLX_MERGE_BF16) {
+            launch_lora_merge(W.packed, W.absmax, W.rows, W.cols, A, B, r, scale, static_cast<uint16_t*>(out), s);
+            return;
+        }
+        REQ_PTR(out_absmax, "out_absmax");
+        check_ws(ws, ws_bytes, qlx_merge_workspace_bytes(W.rows, W.cols, out_kind));
+        uint16_t* merged = static_cast<uint16_t*>(ws);
+        launch_lora_merge(W.packed, W.absmax, W.rows, W.cols, A, B, r, scale, merged, s);
+        launch_nf4_quantize(merged, n, static_cast<uint8_t*>(out), out_absmax, s);
+    });
+}
+

@@ -61,6 +61,8 @@ struct Carver {
 
 // ---------------------------------------------------------------- NF4
 void launch_nf4_quantize(const uint16_t* w, int64_t n, uint8_t* packed, float* absmax, hipStream_t s);
+void launch_lora_merge(const uint8_t* packed, const float* absmax, int64_t rows, int64_t cols, const float* A,
+                       const float* B, int r, float scale, uint16_t* out, hipStream_t s);
 void launch_nf4_dequant(const uint8_t* packed, const float* absmax, int64_t n, int out_dtype, void* out,
                         hipStream_t s);
 
