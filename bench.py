@@ -196,6 +196,52 @@ def gemm_shapes(q) -> dict:
     return out
 
 
+def merge_shapes(q) -> dict:
+    """Adapter merge (W' + s B A, r 64, alpha 16) of one 8B-shaped decoder
+    layer's seven projections, to bf16 and re-quantized to NF4, from the
+    library's events. The merge does 2 r fp32 flops per element against
+    2.5625 B of HBM traffic (codes, absmax, bf16 out), so it is bound by the
+    fp32 vector ALU (157.3 TFLOP/s) rather than HBM at r 64."""
+    import torch
+    B_ = q.binding
+    dev = "cuda:0"
+    r, scale = 64, 16.0 / 64
+    shapes = {"q": (4096, 4096), "k": (1024, 4096), "v": (1024, 4096), "o": (4096, 4096),
+              "gate": (14336, 4096), "up": (14336, 4096), "down": (4096, 14336)}
+    g = torch.Generator(device=dev).manual_seed(0)
+    out, tot = {}, {"lora_merge": [0.0, 0.0, 0.0], "nf4_quantize": [0.0, 0.0, 0.0]}
+    for name, (rows, cols) in shapes.items():
+        W = q.NF4Matrix.quantize((torch.randn(rows, cols, device=dev, generator=g) * 0.02).to(torch.bfloat16))
+        A = torch.randn(r, cols, device=dev, generator=g) * 0.01
+        Bm = torch.randn(rows, r, device=dev, generator=g) * 0.01
+        for _ in range(2):
+            q.lora_merge(W, A, Bm, scale)
+            q.lora_merge(W, A, Bm, scale, to_nf4=True)
+        torch.cuda.synchronize()
+        B_.profile_begin()
+        for _ in range(10):
+            q.lora_merge(W, A, Bm, scale)
+            q.lora_merge(W, A, Bm, scale, to_nf4=True)
+        torch.cuda.synchronize()
+        pr = B_.profile_end()
+        row = {}
+        for k in tot:
+            v = pr[k]
+            row[k + "_us"] = round(1000 * v["ms"] / v["launches"], 1)
+            for i, f in enumerate(("ms", "flops", "bytes")):
+                tot[k][i] += v[f] / v["launches"] if f != "ms" else v["ms"] / v["launches"]
+        row["merge_TFLOPs"] = round(pr["lora_merge"]["flops"] / pr["lora_merge"]["ms"] / 1e9, 1)
+        out[name] = row
+        log(f"merge {name} [{rows}x{cols}]: {row}")
+    ms, fl, by = tot["lora_merge"]
+    out["layer"] = {"lora_merge_us": round(1000 * ms, 1), "nf4_quantize_us": round(1000 * tot["nf4_quantize"][0], 1),
+                    "merge_TFLOPs": round(fl / ms / 1e9, 1), "merge_frac_fp32_alu": round(fl / ms / 1e9 / 157.3, 3),
+                    "merge_GBs": round(by / ms / 1e6, 1),
+                    "nf4_quantize_GBs": round(tot["nf4_quantize"][2] / tot["nf4_quantize"][0] / 1e6, 1)}
+    log(f"merge layer: {out['layer']}")
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,6 +257,8 @@ def main() -> int:
                     help="leave the AdamW update out of the step (loss + LoRA gradients only)")
     ap.add_argument("--gemm-shapes", action="store_true",
                     help="only time the 8B-shaped NF4 GEMMs (fwd and dX) at 512 and 2048 tokens")
+    ap.add_argument("--merge-shapes", action="store_true",
+                    help="only time the adapter merge of one 8B-shaped layer's seven projections (bf16 and NF4 out)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB five times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -238,6 +286,9 @@ def main() -> int:
     B_ = q.binding
     if args.gemm_shapes:
         print(json.dumps({"gemm_shapes": gemm_shapes(q)}))
+        return 0
+    if args.merge_shapes:
+        print(json.dumps({"merge_shapes": merge_shapes(q)}))
         return 0
     wl = WORKLOADS[args.workload]
     d = synth.LLAMA8B

@@ -7,10 +7,10 @@ Pages: the tool merges the adapter into the base model (guillermodelpino.com
 article, command list: `soup merge`; imasters article, closing section). The
 merged weight is the weight the QLoRA linear computes with, written out:
     W_merged = W' + s * B A,   W' = fl32(c[code] * absmax),  s = alpha / r
-(LoRA, Hu et al. 2021, section 4.1: "we can explicitly compute and store
-W = W0 + BA"), computed in float64 here and rounded to bf16 through fp32
-(round to nearest even both times; bf16 is the computation type the weights
-are used in). The NF4 output re-quantizes that
+(LoRA, Hu et al. 2021, section 4.1: for inference the low-rank product can
+be added into the frozen weight once), computed in float64 here and rounded
+to bf16 through fp32 (round to nearest even both times; bf16 is the
+computation type the weights are used in). The NF4 output re-quantizes that
 bf16 matrix with the ordinary quantizer (same blocks over the flattened
 matrix).
 

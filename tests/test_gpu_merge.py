@@ -28,7 +28,11 @@ def _case(rows, cols, r, seed):
     return W, A, B
 
 
-@pytest.mark.parametrize("rows,cols,r", [(96, 128, 8), (100, 200, 5), (37, 64, 64), (4096, 4096, 64)])
+# (33, 70, 3) and (5, 301, 40): columns not a multiple of 4 (element-wise path),
+# 301 also leaves a partial last column tile; 40 and 70 split r into a
+# partial step.
+@pytest.mark.parametrize("rows,cols,r", [(96, 128, 8), (100, 200, 5), (37, 64, 64), (33, 70, 3), (5, 301, 40),
+                                        (65, 260, 70), (4096, 4096, 64)])
 def test_bf16_merge_vs_oracle(rows, cols, r):
     W, A, B = _case(rows, cols, r, rows + cols)
     out = q.lora_merge(W, f32_dev(A), f32_dev(B), 0.25)

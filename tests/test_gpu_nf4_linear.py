@@ -40,6 +40,24 @@ def test_nf4_quantize_and_dequant_bit_exact(rows, cols):
     assert np.array_equal(out16.view(torch.int16).cpu().numpy().view(np.uint16), oracle.bf16_rne_bits(d_ref))
 
 
+@pytest.mark.parametrize("n", [64 * 40, 64 * 40 + 21])
+def test_nf4_quantize_unaligned_buffers_bit_exact(n):
+    """Inputs and codes at odd offsets take the element-wise path (no 16-B
+    loads or 4-B stores): same codes and scales as the oracle."""
+    wb = _w_bits(1, n, 7 + n).reshape(-1)
+    w_full = torch.zeros(n + 1, dtype=torch.bfloat16, device=DEV)
+    w_full[1:] = bf16_dev(wb)
+    w = w_full[1:]                                            # 2-B aligned only
+    p_full = torch.zeros((n + 1) // 2 + 1, dtype=torch.uint8, device=DEV)
+    packed = p_full[1:]                                       # odd address
+    absmax = torch.empty((n + 63) // 64, dtype=torch.float32, device=DEV)
+    q.nf4_quantize(w, packed, absmax)
+    p_ref, a_ref = oracle.nf4_quantize(synth.bf16_bits_to_f32(wb))
+    assert np.array_equal(to_np(packed), p_ref)
+    assert np.array_equal(to_np(absmax).view(np.uint32), a_ref.view(np.uint32))
+    assert int(p_full[0]) == 0
+
+
 def test_nf4_special_blocks_bit_exact():
     c = oracle.nf4_codebook()
     rows = []
