@@ -57,11 +57,14 @@ typedef enum {
     QLX_EUNSUPPORTED = 2,  /* valid request this build does not handle */
     QLX_EWORKSPACE = 3,    /* ws_bytes smaller than the reported requirement */
     QLX_ENOTPINNED = 4,    /* a streamed layer blob is not pinned host memory */
-    QLX_EHIP = 5           /* the HIP runtime reported an error */
+    QLX_EHIP = 5,          /* the HIP runtime reported an error */
+    QLX_EIO = 6            /* a layer file could not be created, opened or read */
 } qlx_status;
 
 enum { QLX_F32 = 0, QLX_BF16 = 1 };                /* nf4_dequant output type */
-enum { QLX_STREAMED = 0, QLX_RESIDENT = 1 };       /* where layer blobs live */
+/* where layer blobs live: pinned host RAM, device memory, or a layer file
+ * attached to the context (qlx_ctx_set_layer_source) */
+enum { QLX_STREAMED = 0, QLX_RESIDENT = 1, QLX_STREAMED_DISK = 2 };
 enum { QLX_DPO_REF_FUSED = 0, QLX_DPO_REF_SEPARATE = 1 };
 
 /* Thread-local text of the last non-OK status (never NULL). */
@@ -177,6 +180,8 @@ typedef struct {
     int64_t layer_passes;  /* layer computations (fwd, recompute+bwd, reference) */
     float step_ms;         /* first to last event of the last step */
     float h2d_ms;          /* sum of the copies' durations (side stream) */
+    int64_t disk_bytes;    /* bytes read from the layer file (QLX_STREAMED_DISK) */
+    float disk_ms;         /* host wall time of those reads */
 } qlx_stats;
 
 int qlx_ctx_create(qlx_ctx** out, int device);
@@ -184,11 +189,49 @@ int qlx_ctx_destroy(qlx_ctx* ctx);
 /* Waits for all work of the last step and fills *stats (HOST) if non-NULL. */
 int qlx_ctx_sync(qlx_ctx* ctx, qlx_stats* stats);
 
+/* Disk stream source (rug.gal article, "En detalle": the frozen base sits in
+ * CPU memory or on disk; imasters article, "Como cabe um 8B em 4 GB": the
+ * `stream_source: auto` setting, RAM when the stack fits and the NVMe disk
+ * when it does not).
+ * A layer file holds the n_layers blobs of a model, blob i at byte offset
+ * i * stride, stride = the blob size (qlx_layer_blob_layout) rounded up to
+ * 4096, zero padded. Reads use O_DIRECT (no page cache) unless the file
+ * system refuses it or QLX_FILE_BUFFERED is given; four reader threads per
+ * file keep several 8 MiB reads in flight. A file serves one context at a
+ * time. */
+typedef struct qlx_layer_file qlx_layer_file;
+enum { QLX_FILE_BUFFERED = 1 };  /* qlx_layer_file_open: read through the page cache */
+
+/* Writes the stack file: blobs = HOST array of n_layers HOST pointers (any
+ * host memory) to blobs laid out as qlx_layer_blob_layout says. Creates or
+ * truncates path; fsyncs before returning. */
+int qlx_layer_file_write(const char* path, const qlx_dims* d, const void* const* blobs);
+/* Opens a stack file for the model dims d; QLX_EIO if it is missing or
+ * shorter than n_layers * stride. flags: 0 or QLX_FILE_BUFFERED. */
+int qlx_layer_file_open(qlx_layer_file** out, const char* path, const qlx_dims* d, int flags);
+/* Waits for copies still reading its staging buffers, then frees it. NULL is
+ * a no-op. Detach it from its context first. */
+int qlx_layer_file_close(qlx_layer_file* f);
+/* *direct (HOST) = 1 if reads bypass the page cache; *stride = blob stride. */
+int qlx_layer_file_info(const qlx_layer_file* f, int* direct, uint64_t* stride);
+/* Reads layer i's blob into dst (HOST, blob-size bytes, any alignment). */
+int qlx_layer_file_read(qlx_layer_file* f, int layer, void* dst);
+/* Attaches f (NULL detaches) as the context's source for QLX_STREAMED_DISK.
+ * The first attach allocates two pinned staging buffers of one stride each
+ * on the context's device; a file stays bound to that device. */
+int qlx_ctx_set_layer_source(qlx_ctx* ctx, qlx_layer_file* f);
+/* `stream_source: auto`: *mode (HOST) = QLX_STREAMED if the stack
+ * (stack_bytes) plus reserve_bytes fits in the host's available memory
+ * (MemAvailable), else QLX_STREAMED_DISK. */
+int qlx_stream_source_auto(uint64_t stack_bytes, uint64_t reserve_bytes, int* mode);
+
 /* The model a step runs on.
  * layer_blobs: HOST array of n_layers pointers to layer blobs; in
  *   QLX_STREAMED mode they must be pinned host memory (hipHostMalloc or
  *   registered by the runtime's pinned allocator); in QLX_RESIDENT mode they
- *   are device memory and no copy happens.
+ *   are device memory and no copy happens; in QLX_STREAMED_DISK mode they are
+ *   not read (may be NULL) and the layers come from the context's layer file,
+ *   disk -> pinned staging -> device slot, with the same bits.
  * embed_f16, lm_head_f16: DEVICE fp16 [vocab, hidden] (untied, frozen).
  * final_norm: DEVICE fp32 [hidden]. lora: HOST array of n_layers qlx_lora. */
 typedef struct {

@@ -16,9 +16,10 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlx.so")
 
-QLX_OK, QLX_EINVAL, QLX_EUNSUPPORTED, QLX_EWORKSPACE, QLX_ENOTPINNED, QLX_EHIP = range(6)
+QLX_OK, QLX_EINVAL, QLX_EUNSUPPORTED, QLX_EWORKSPACE, QLX_ENOTPINNED, QLX_EHIP, QLX_EIO = range(7)
 QLX_F32, QLX_BF16 = 0, 1
-QLX_STREAMED, QLX_RESIDENT = 0, 1
+QLX_STREAMED, QLX_RESIDENT, QLX_STREAMED_DISK = 0, 1, 2
+QLX_FILE_BUFFERED = 1
 QLX_DPO_REF_FUSED, QLX_DPO_REF_SEPARATE = 0, 1
 QLX_PREF_DPO, QLX_PREF_ORPO, QLX_PREF_SIMPO, QLX_PREF_KTO = 0, 1, 2, 3
 QLX_MERGE_BF16, QLX_MERGE_NF4 = 0, 1
@@ -34,6 +35,8 @@ EXPORTED = (
     "qlora_linear_fwd", "qlora_linear_bwd", "qlx_layer_blob_layout", "qlx_layer_workspace_bytes",
     "layer_fwd", "layer_bwd", "qlx_ctx_create", "qlx_ctx_destroy", "qlx_ctx_sync",
     "qlx_step_workspace_bytes", "stream_step_sft", "stream_step_dpo", "stream_step_pref", "qlx_merge_workspace_bytes", "qlx_lora_merge", "qlx_profile_begin", "qlx_profile_begin_prefix", "qlx_profile_end", "qlx_adamw_lora",
+    "qlx_layer_file_write", "qlx_layer_file_open", "qlx_layer_file_close", "qlx_layer_file_info",
+    "qlx_layer_file_read", "qlx_ctx_set_layer_source", "qlx_stream_source_auto",
 )
 
 
@@ -85,7 +88,7 @@ class PrefCfg(C.Structure):
 
 class Stats(C.Structure):
     _fields_ = [("layer_reads", C.c_int64), ("h2d_bytes", C.c_int64), ("layer_passes", C.c_int64),
-                ("step_ms", C.c_float), ("h2d_ms", C.c_float)]
+                ("step_ms", C.c_float), ("h2d_ms", C.c_float), ("disk_bytes", C.c_int64), ("disk_ms", C.c_float)]
 
 
 class KernelProf(C.Structure):
@@ -139,6 +142,13 @@ def lib() -> C.CDLL:
         "qlx_adamw_lora": (i32, [C.POINTER(Dims), C.POINTER(LoraBuf), C.POINTER(LoraGrad), C.POINTER(LoraBuf),
                                  C.POINTER(LoraBuf), C.c_int64, C.POINTER(AdamwCfg), C.c_void_p]),
         "qlx_profile_end": (i32, [C.POINTER(KernelProf), i32, C.POINTER(C.c_int)]),
+        "qlx_layer_file_write": (i32, [C.c_char_p, C.POINTER(Dims), C.POINTER(C.c_void_p)]),
+        "qlx_layer_file_open": (i32, [C.POINTER(vp), C.c_char_p, C.POINTER(Dims), i32]),
+        "qlx_layer_file_close": (i32, [vp]),
+        "qlx_layer_file_info": (i32, [vp, C.POINTER(C.c_int), C.POINTER(C.c_uint64)]),
+        "qlx_layer_file_read": (i32, [vp, i32, vp]),
+        "qlx_ctx_set_layer_source": (i32, [vp, vp]),
+        "qlx_stream_source_auto": (i32, [C.c_uint64, C.c_uint64, C.POINTER(C.c_int)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -378,6 +388,11 @@ class Context:
         _check(lib().qlx_ctx_create(C.byref(h), device))
         self.h = h
 
+    def set_layer_source(self, f: "LayerFile | None") -> None:
+        """Attaches a stack file for QLX_STREAMED_DISK (None detaches)."""
+        _check(lib().qlx_ctx_set_layer_source(self.h, f.h if f is not None else None))
+        self.source = f  # keeps the file alive while attached
+
     def sync(self) -> dict:
         st = Stats()
         _check(lib().qlx_ctx_sync(self.h, C.byref(st)))
@@ -395,22 +410,82 @@ class Context:
             pass
 
 
+class LayerFile:
+    """A stack file on disk (qlx_layer_file): blob i at i * stride. Reads go
+    around the page cache (O_DIRECT) unless buffered=True or the file system
+    refuses it."""
+
+    @staticmethod
+    def write(path: str, dims, blobs: Sequence) -> None:
+        """blobs: host buffers (uint8 tensors or numpy arrays) of one layer blob each."""
+        d = Dims.of(dims)
+        ptrs = [b.data_ptr() if isinstance(b, torch.Tensor) else b.ctypes.data for b in blobs]
+        if len(ptrs) != d.n_layers:
+            raise ValueError(f"{len(ptrs)} blobs for {d.n_layers} layers")
+        for b in blobs:
+            if isinstance(b, torch.Tensor) and b.is_cuda:
+                raise ValueError("layer blobs for the file must be host memory")
+        arr = (C.c_void_p * len(ptrs))(*ptrs)
+        _check(lib().qlx_layer_file_write(os.fsencode(path), C.byref(d), C.cast(arr, C.POINTER(C.c_void_p))))
+
+    def __init__(self, path: str, dims, buffered: bool = False):
+        self.dims = Dims.of(dims)
+        h = C.c_void_p()
+        _check(lib().qlx_layer_file_open(C.byref(h), os.fsencode(path), C.byref(self.dims),
+                                         QLX_FILE_BUFFERED if buffered else 0))
+        self.h = h
+        self.path = path
+
+    def info(self) -> dict:
+        direct, stride = C.c_int(), C.c_uint64()
+        _check(lib().qlx_layer_file_info(self.h, C.byref(direct), C.byref(stride)))
+        return {"direct": bool(direct.value), "stride": int(stride.value)}
+
+    def read(self, layer: int, out) -> None:
+        """Reads layer `layer`'s blob into a host buffer (tensor or numpy array)."""
+        ptr = out.data_ptr() if isinstance(out, torch.Tensor) else out.ctypes.data
+        _check(lib().qlx_layer_file_read(self.h, layer, ptr))
+
+    def close(self) -> None:
+        if self.h:
+            lib().qlx_layer_file_close(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def stream_source_auto(stack_bytes: int, reserve_bytes: int = 0) -> int:
+    """QLX_STREAMED if the stack (plus reserve) fits in available host memory, else QLX_STREAMED_DISK."""
+    mode = C.c_int()
+    _check(lib().qlx_stream_source_auto(int(stack_bytes), int(reserve_bytes), C.byref(mode)))
+    return mode.value
+
+
 class StreamModel:
     """Holds the tensors of a model and the C struct pointing at them.
-    blobs: pinned host uint8 tensors (streamed) or device uint8 tensors (resident)."""
+    blobs: pinned host uint8 tensors (streamed) or device uint8 tensors
+    (resident); None for a model that only streams from a layer file."""
 
-    def __init__(self, dims, blobs: Sequence[torch.Tensor], embed_f16: torch.Tensor, head_f16: torch.Tensor,
+    def __init__(self, dims, blobs: Sequence[torch.Tensor] | None, embed_f16: torch.Tensor, head_f16: torch.Tensor,
                  final_norm: torch.Tensor, lora: Sequence[LoraLayer]):
         self.dims = Dims.of(dims)
         _, total = blob_layout(self.dims)
-        for bl in blobs:
+        for bl in blobs or ():
             if bl.numel() * bl.element_size() < total:
                 raise ValueError(f"layer blob holds {bl.numel() * bl.element_size()} bytes, layout needs {total}")
-        self.blobs, self.embed, self.head, self.final_norm, self.lora = list(blobs), embed_f16, head_f16, final_norm, list(lora)
-        n = len(self.blobs)
-        self._blob_arr = (C.c_void_p * n)(*[_ptr(b) for b in self.blobs])
-        self._lora_arr = (Lora * n)(*[l.c() for l in self.lora])
-        self.c = Model(self.dims, C.cast(self._blob_arr, C.POINTER(C.c_void_p)), _ptr(embed_f16), _ptr(head_f16),
+        self.blobs = list(blobs) if blobs is not None else None
+        self.embed, self.head, self.final_norm, self.lora = embed_f16, head_f16, final_norm, list(lora)
+        if self.blobs is not None:
+            self._blob_arr = (C.c_void_p * len(self.blobs))(*[_ptr(b) for b in self.blobs])
+            blob_ptr = C.cast(self._blob_arr, C.POINTER(C.c_void_p))
+        else:
+            self._blob_arr, blob_ptr = None, None
+        self._lora_arr = (Lora * len(self.lora))(*[l.c() for l in self.lora])
+        self.c = Model(self.dims, blob_ptr, _ptr(embed_f16), _ptr(head_f16),
                        _ptr(final_norm), C.cast(self._lora_arr, C.POINTER(Lora)))
 
     def with_blobs(self, blobs: Sequence[torch.Tensor]) -> "StreamModel":

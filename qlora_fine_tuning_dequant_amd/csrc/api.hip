@@ -20,7 +20,10 @@
 #include <cstring>
 #include <vector>
 
+#include <chrono>
+
 #include "layer.h"
+#include "source.h"
 
 namespace qlx {
 
@@ -31,25 +34,7 @@ void check_launch(const char* what) {
     if (e != hipSuccess) throw Error{QLX_EHIP, std::string(what) + ": " + hipGetErrorString(e)};
 }
 
-template <typename F>
-static int guarded(F&& f) {
-    try {
-        f();
-        return QLX_OK;
-    } catch (const Error& e) {
-        set_error(e.msg);
-        return e.code;
-    } catch (const std::exception& e) {
-        set_error(std::string("internal error: ") + e.what());
-        return QLX_EHIP;
-    } catch (...) {
-        set_error("internal error");
-        return QLX_EHIP;
-    }
-}
-
 static inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
-#define REQ_PTR(p, name) QLX_REQUIRE((p) != nullptr, QLX_EINVAL, std::string(name) + " is NULL")
 #define REQ_AL(p, name) QLX_REQUIRE(al16(p), QLX_EINVAL, std::string(name) + " must be 16-byte aligned")
 
 static void check_ws(void* ws, size_t ws_bytes, size_t need) {
@@ -357,6 +342,7 @@ struct qlx_ctx {
     std::vector<hipEvent_t> copy_ev;  // timing pairs for copies (begin, end)
     size_t copies_used = 0;
     qlx_stats stats{};
+    qlx_layer_file* source = nullptr;  // QLX_STREAMED_DISK
 };
 
 namespace qlx {
@@ -464,10 +450,29 @@ class Streamer {
     void issue_copy(int i, int sl) {
         // the slot's previous contents must be finished with on the main stream
         QLX_CHECK_HIP(hipStreamWaitEvent(ctx_->side, ctx_->compute_done[sl], 0));
+        const void* src = nullptr;
+        int k = -1;
+        qlx_layer_file* f = ctx_->source;
+        if (mode_ == QLX_STREAMED_DISK) {
+            // disk -> pinned staging buffer k (once the copy that last read it
+            // is done) on this thread, then staging -> slot on the side stream
+            k = f->next;
+            f->next = (k + 1) % kStaging;
+            QLX_CHECK_HIP(hipEventSynchronize(f->staging_free[k]));
+            const auto t0 = std::chrono::steady_clock::now();
+            layer_file_read(f, i, f->staging[k]);
+            ctx_->stats.disk_ms +=
+                std::chrono::duration<float, std::milli>(std::chrono::steady_clock::now() - t0).count();
+            ctx_->stats.disk_bytes += int64_t(f->stride);
+            src = f->staging[k];
+        } else {
+            src = m_->layer_blobs[i];
+        }
         hipEvent_t* ev = next_timing_pair();
         if (ev) QLX_CHECK_HIP(hipEventRecord(ev[0], ctx_->side));
-        QLX_CHECK_HIP(hipMemcpyAsync(w_.slot[sl], m_->layer_blobs[i], bytes_, hipMemcpyHostToDevice, ctx_->side));
+        QLX_CHECK_HIP(hipMemcpyAsync(w_.slot[sl], src, bytes_, hipMemcpyHostToDevice, ctx_->side));
         if (ev) QLX_CHECK_HIP(hipEventRecord(ev[1], ctx_->side));
+        if (k >= 0) QLX_CHECK_HIP(hipEventRecord(f->staging_free[k], ctx_->side));
         QLX_CHECK_HIP(hipEventRecord(ctx_->copy_done[sl], ctx_->side));
         held_[sl] = i;
         ctx_->stats.layer_reads += 1;
@@ -492,18 +497,29 @@ static void validate_model(qlx_ctx* ctx, const qlx_model* m, int mode) {
     REQ_PTR(ctx, "ctx");
     REQ_PTR(m, "model");
     validate_dims(&m->dims);
-    QLX_REQUIRE(mode == QLX_STREAMED || mode == QLX_RESIDENT, QLX_EINVAL, "mode must be QLX_STREAMED or QLX_RESIDENT");
-    REQ_PTR(m->layer_blobs, "model.layer_blobs");
+    QLX_REQUIRE(mode == QLX_STREAMED || mode == QLX_RESIDENT || mode == QLX_STREAMED_DISK, QLX_EINVAL,
+                "mode must be QLX_STREAMED, QLX_RESIDENT or QLX_STREAMED_DISK");
+    if (mode == QLX_STREAMED_DISK) {
+        const qlx_layer_file* f = ctx->source;
+        QLX_REQUIRE(f != nullptr, QLX_EINVAL, "QLX_STREAMED_DISK needs a layer file attached to the context");
+        uint64_t off[QLX_BLOB_NSEG], blob_bytes = 0;
+        blob_layout(m->dims, off, &blob_bytes);
+        QLX_REQUIRE(f->dims.n_layers == m->dims.n_layers && f->blob_bytes == blob_bytes, QLX_EINVAL,
+                    "the context's layer file was opened for other model dims");
+    } else {
+        REQ_PTR(m->layer_blobs, "model.layer_blobs");
+    }
     REQ_PTR(m->embed_f16, "model.embed_f16");
     REQ_PTR(m->lm_head_f16, "model.lm_head_f16");
     REQ_PTR(m->final_norm, "model.final_norm");
     REQ_PTR(m->lora, "model.lora");
     REQ_AL(m->lm_head_f16, "model.lm_head_f16");
     for (int i = 0; i < m->dims.n_layers; ++i) {
+        validate_lora(&m->lora[i]);
+        if (mode == QLX_STREAMED_DISK) continue;
         const void* b = m->layer_blobs[i];
         QLX_REQUIRE(b != nullptr, QLX_EINVAL, "model.layer_blobs[" + std::to_string(i) + "] is NULL");
         REQ_AL(b, "layer blob");
-        validate_lora(&m->lora[i]);
         if (mode == QLX_STREAMED) {
             hipPointerAttribute_t attr;
             const hipError_t e = hipPointerGetAttributes(&attr, b);
@@ -630,6 +646,28 @@ int qlx_ctx_destroy(qlx_ctx* ctx) {
         (void)hipEventDestroy(ctx->step_end);
         (void)hipStreamDestroy(ctx->side);
         delete ctx;
+    });
+}
+
+int qlx_ctx_set_layer_source(qlx_ctx* ctx, qlx_layer_file* f) {
+    return guarded([&] {
+        REQ_PTR(ctx, "ctx");
+        if (!f) {
+            ctx->source = nullptr;
+            return;
+        }
+        QLX_REQUIRE(f->device < 0 || f->device == ctx->device, QLX_EINVAL,
+                    "the layer file is bound to device " + std::to_string(f->device));
+        QLX_CHECK_HIP(hipSetDevice(ctx->device));
+        if (f->device < 0) {
+            for (int k = 0; k < kStaging; ++k) {
+                QLX_CHECK_HIP(hipHostMalloc(reinterpret_cast<void**>(&f->staging[k]), f->stride, hipHostMallocDefault));
+                QLX_CHECK_HIP(hipEventCreateWithFlags(&f->staging_free[k], hipEventDisableTiming));
+                QLX_CHECK_HIP(hipEventRecord(f->staging_free[k], ctx->side));  // free from the start
+            }
+            f->device = ctx->device;
+        }
+        ctx->source = f;
     });
 }
 

@@ -4,6 +4,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <exception>
 #include <string>
 
 #include "qlx.h"
@@ -27,6 +28,25 @@ struct Error {
         if (!(cond)) throw ::qlx::Error{(code), (msg)};                              \
     } while (0)
 void check_launch(const char* what);
+#define REQ_PTR(p, name) QLX_REQUIRE((p) != nullptr, QLX_EINVAL, std::string(name) + " is NULL")
+
+// Runs f and turns what it throws into a status (the ABI's error contract).
+template <typename F>
+inline int guarded(F&& f) {
+    try {
+        f();
+        return QLX_OK;
+    } catch (const Error& e) {
+        set_error(e.msg);
+        return e.code;
+    } catch (const std::exception& e) {
+        set_error(std::string("internal error: ") + e.what());
+        return QLX_EHIP;
+    } catch (...) {
+        set_error("internal error");
+        return QLX_EHIP;
+    }
+}
 
 // Brackets one kernel launch with timing events when profiling is on.
 struct ProfScope {

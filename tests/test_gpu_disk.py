@@ -1,0 +1,88 @@
+"""GPU checks of the disk stream source: steps whose layers come from a stack
+file (disk -> pinned staging -> device slot) give the same bits as the
+RAM-streamed and resident runs, read the stack as often, and reject a missing
+or mismatched file before any launch."""
+import dataclasses
+
+import pytest
+import torch
+
+import synth
+from gpu_helpers import gpu_model, run_dpo, run_sft, same_grads
+
+pytestmark = pytest.mark.gpu
+q = pytest.importorskip("qlora_fine_tuning_dequant_amd")
+B_ = q.binding
+
+
+@pytest.fixture(scope="module")
+def four(tmp_path_factory):
+    d = dataclasses.replace(synth.TINY, n_layers=4)
+    m, host = gpu_model(q, d, 1, "normal")
+    path = str(tmp_path_factory.mktemp("stack") / "stack.bin")
+    q.LayerFile.write(path, d, host)
+    return d, m, host, path
+
+
+def _disk_model(m):
+    return q.StreamModel(m.dims, None, m.embed, m.head, m.final_norm, m.lora)
+
+
+@pytest.mark.parametrize("buffered", [False, True])
+def test_sft_from_disk_equals_ram_and_resident(four, buffered):
+    d, m, host, path = four
+    toks = synth.tokens(1, 2, 32, d.vocab)
+    f = q.LayerFile(path, d, buffered=buffered)
+    print("layer file", f.info(), flush=True)
+    ctx = q.Context(0)
+    ctx.set_layer_source(f)
+    l_d, g_d, st_d = run_sft(q, _disk_model(m), toks, B_.QLX_STREAMED_DISK, ctx)
+    l_s, g_s, st_s = run_sft(q, m.with_blobs(host), toks, B_.QLX_STREAMED)
+    l_r, g_r, _ = run_sft(q, m, toks, B_.QLX_RESIDENT)
+    assert torch.equal(l_d, l_s) and same_grads(g_d, g_s)
+    assert torch.equal(l_d, l_r) and same_grads(g_d, g_r)
+    assert st_d["layer_reads"] == 2 * 4 - 2 and st_d["h2d_bytes"] == st_s["h2d_bytes"]
+    assert st_d["disk_bytes"] == st_d["layer_reads"] * f.info()["stride"] and st_s["disk_bytes"] == 0
+    # the same context again: the staging ring is reused across steps
+    for _ in range(2):
+        l2, g2, _ = run_sft(q, _disk_model(m), toks, B_.QLX_STREAMED_DISK, ctx)
+        assert torch.equal(l2, l_d) and same_grads(g2, g_d)
+    ctx.set_layer_source(None)
+    ctx.close()
+    f.close()
+
+
+def test_dpo_from_disk_both_schedules(four):
+    d, m, host, path = four
+    ch, rj = synth.dpo_pairs(1, 2, 32, 8, d.vocab)
+    f = q.LayerFile(path, d)
+    ctx = q.Context(0)
+    ctx.set_layer_source(f)
+    for sched, reads in ((B_.QLX_DPO_REF_FUSED, 2 * 4 - 2), (B_.QLX_DPO_REF_SEPARATE, 3 * 4 - 2)):
+        l_d, lp_d, g_d, st_d = run_dpo(q, _disk_model(m), ch, rj, 8, 0.1, B_.QLX_STREAMED_DISK, sched, ctx)
+        l_s, lp_s, g_s, _ = run_dpo(q, m.with_blobs(host), ch, rj, 8, 0.1, B_.QLX_STREAMED, sched)
+        assert torch.equal(l_d, l_s) and torch.equal(lp_d, lp_s) and same_grads(g_d, g_s)
+        assert st_d["layer_reads"] == reads and st_d["disk_bytes"] == reads * f.info()["stride"]
+    ctx.set_layer_source(None)
+    ctx.close()
+    f.close()
+
+
+def test_disk_mode_needs_a_matching_file(four, tmp_path):
+    d, m, host, path = four
+    toks = synth.tokens(1, 1, 32, d.vocab)
+    ctx = q.Context(0)
+    with pytest.raises(B_.QlxError) as e:        # no file attached
+        run_sft(q, _disk_model(m), toks, B_.QLX_STREAMED_DISK, ctx)
+    assert e.value.code == B_.QLX_EINVAL and "layer file" in str(e.value)
+    d2 = dataclasses.replace(d, n_layers=2)      # a file for a 2-layer stack
+    p2 = str(tmp_path / "two.bin")
+    q.LayerFile.write(p2, d2, host[:2])
+    f2 = q.LayerFile(p2, d2)
+    ctx.set_layer_source(f2)
+    with pytest.raises(B_.QlxError) as e:
+        run_sft(q, _disk_model(m), toks, B_.QLX_STREAMED_DISK, ctx)
+    assert e.value.code == B_.QLX_EINVAL and "other model dims" in str(e.value)
+    ctx.set_layer_source(None)
+    ctx.close()
+    f2.close()
