@@ -9,6 +9,9 @@ seeded synthetic weights and uniform random tokens (seed 1); each step ends
 with the AdamW update of every LoRA factor (lr 2e-5). Other workloads:
 --workload sft8b_b4 (batch 4), dpo8b (2 preference pairs, 128-token
 prompts, beta 0.1), and orpo8b / simpo8b / kto8b on the same pairs.
+--source disk streams the stack from a file read with O_DIRECT (disk ->
+pinned staging -> device); --source auto takes RAM when the stack fits in
+available host memory and the file otherwise.
 
 Prints ONE JSON line. `value` is tokens/s over the timed steps (inputs
 resident: weights in pinned host RAM as the method keeps them, tokens on the
@@ -25,6 +28,7 @@ import argparse
 import json
 import os
 import sys
+import tempfile
 import threading
 import time
 
@@ -249,6 +253,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="sft8b_b1", choices=sorted(WORKLOADS))
     ap.add_argument("--mode", default="streamed", choices=["streamed", "resident"])
+    ap.add_argument("--source", default="ram", choices=["ram", "disk", "auto"],
+                    help="where the streamed stack lives: pinned host RAM, a stack file read with O_DIRECT, or "
+                         "RAM when it fits in available memory and the file otherwise")
+    ap.add_argument("--stack-file", default=None,
+                    help="stack file for --source disk/auto (default: a file in the temp directory, removed at exit)")
     ap.add_argument("--dpo-ref", default="fused", choices=["fused", "separate"],
                     help="DPO reference schedule: fused with the policy forward, or a separate pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -302,6 +311,23 @@ def main() -> int:
     log(f"model ready in {time.perf_counter() - t0:.1f} s")
     mode = B_.QLX_STREAMED if args.mode == "streamed" else B_.QLX_RESIDENT
     ctx = q.Context(0)
+    source, layer_file, stack_path = "ram" if args.mode == "streamed" else "device", None, None
+    if args.mode == "streamed" and args.source != "ram":
+        _, blob_bytes = B_.blob_layout(d)
+        if args.source == "auto":
+            mode = B_.stream_source_auto(d.n_layers * blob_bytes, reserve_bytes=8 << 30)
+        else:
+            mode = B_.QLX_STREAMED_DISK
+        if mode == B_.QLX_STREAMED_DISK:
+            stack_path = args.stack_file or os.path.join(tempfile.gettempdir(), f"qlx_stack_{os.getpid()}.bin")
+            t0 = time.perf_counter()
+            q.LayerFile.write(stack_path, d, m.blobs)
+            log(f"stack file {stack_path}: {d.n_layers} x {blob_bytes / 1e6:.1f} MB written in "
+                f"{time.perf_counter() - t0:.1f} s")
+            layer_file = q.LayerFile(stack_path, d)
+            ctx.set_layer_source(layer_file)
+            source = "disk (O_DIRECT)" if layer_file.info()["direct"] else "disk (page cache)"
+        log(f"stream source: {source}")
     grads = [q.LoraGrads(l) for l in m.lora]
     # the step's optimizer update: AdamW on every LoRA factor at the pages' lr
     opt = None if args.no_optimizer else q.AdamW(d, m.lora, lr=LR)
@@ -360,6 +386,11 @@ def main() -> int:
         torch.cuda.synchronize()
         prof = B_.profile_end()
 
+    if layer_file is not None:
+        ctx.set_layer_source(None)
+        layer_file.close()
+        if args.stack_file is None:
+            os.remove(stack_path)
     reads = stats[-1]["layer_reads"]
     h2d_ms = float(np.mean([s["h2d_ms"] for s in stats]))
     h2d_bytes = stats[-1]["h2d_bytes"]
@@ -384,13 +415,19 @@ def main() -> int:
         "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl["name"], "global_batch": batch if wl["kind"] == "sft" else 2 * batch,
-                   "seq_len": seq, "mode": args.mode, "layers": d.n_layers, "lora_r": d.lora_r,
+                   "seq_len": seq, "mode": args.mode, "source": source, "layers": d.n_layers,
+                   "lora_r": d.lora_r,
                    "optimizer": None if args.no_optimizer else f"adamw lr {LR}",
                    **({"dpo_reference": args.dpo_ref} if wl["kind"] in ("dpo", "kto") else {})},
         "roofline": roofline,
         "stream": {"layer_reads_per_step": reads, "h2d_GB_per_step": round(h2d_bytes / 1e9, 3),
                    "h2d_ms_per_step": round(h2d_ms, 2),
-                   "h2d_GBps": round(h2d_bytes / max(h2d_ms, 1e-9) / 1e6, 1) if h2d_ms else None},
+                   "h2d_GBps": round(h2d_bytes / max(h2d_ms, 1e-9) / 1e6, 1) if h2d_ms else None,
+                   **({"disk_GB_per_step": round(stats[-1]["disk_bytes"] / 1e9, 3),
+                       "disk_read_ms_per_step": round(float(np.mean([s["disk_ms"] for s in stats])), 1),
+                       "disk_GBps": round(stats[-1]["disk_bytes"] / max(float(np.mean([s["disk_ms"] for s in stats])),
+                                                                        1e-9) / 1e6, 1)}
+                      if layer_file is not None else {})},
         "gpu_time": {"kernels_ms_per_step": round(all_kernel_ms, 2), "gemm_ms_per_step": round(gemm_ms, 2),
                      "gemm_TFLOP_per_step": round(gemm_tf / 1e12, 3),
                      "gemm_TFLOPs_avg": round(gemm_tf / max(gemm_ms, 1e-9) / 1e9, 1)},

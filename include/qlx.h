@@ -196,9 +196,9 @@ int qlx_ctx_sync(qlx_ctx* ctx, qlx_stats* stats);
  * A layer file holds the n_layers blobs of a model, blob i at byte offset
  * i * stride, stride = the blob size (qlx_layer_blob_layout) rounded up to
  * 4096, zero padded. Reads use O_DIRECT (no page cache) unless the file
- * system refuses it or QLX_FILE_BUFFERED is given; four reader threads per
- * file keep several 8 MiB reads in flight. A file serves one context at a
- * time. */
+ * system refuses it or QLX_FILE_BUFFERED is given; reader threads (16, or
+ * the environment variable QLX_FILE_READERS at open, 1..64) keep several
+ * 8 MiB reads in flight. A file serves one context at a time. */
 typedef struct qlx_layer_file qlx_layer_file;
 enum { QLX_FILE_BUFFERED = 1 };  /* qlx_layer_file_open: read through the page cache */
 

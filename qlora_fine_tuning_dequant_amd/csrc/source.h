@@ -14,7 +14,7 @@ namespace qlx {
 constexpr int kStaging = 2;                 // pinned staging buffers per file
 constexpr uint64_t kFileAlign = 4096;       // blob stride and direct-I/O alignment
 constexpr uint64_t kReadChunk = 8ull << 20; // one pread job
-constexpr int kReaders = 4;                 // reader threads per file
+constexpr int kReaders = 16;                // reader threads per file
 }  // namespace qlx
 
 struct qlx_layer_file {

@@ -5,8 +5,8 @@
 // at offset i * stride (stride = the blob size rounded up to 4 KiB, zero
 // padded), read with O_DIRECT where the file system allows it, so a read is a
 // disk read and not a page-cache copy. A read is split into 8 MiB jobs served
-// by four reader threads (several requests in flight on the device) through
-// per-thread bounce buffers; the
+// by 16 reader threads (a whole layer's requests in flight on the device)
+// through per-thread bounce buffers; the
 // streamer reads into one of two pinned staging buffers and copies that to a
 // device slot, so disk, host link and compute form a three-stage pipeline.
 #include <fcntl.h>
@@ -29,7 +29,7 @@ static std::string errstr(int e) { return std::string(std::strerror(e)); }
 // A direct read cannot land in the runtime's pinned allocation (the kernel
 // cannot pin those pages for the transfer: EFAULT), so with O_DIRECT each
 // reader reads into its own aligned bounce buffer and copies from there; the
-// copies of one layer's chunks run on the four threads in parallel with the
+// copies of one layer's chunks run on the reader threads in parallel with the
 // other chunks' reads.
 static void reader(qlx_layer_file* f) {
     void* bounce = nullptr;
@@ -202,7 +202,10 @@ int qlx_layer_file_open(qlx_layer_file** out, const char* path, const qlx_dims* 
         f->dims = *d;
         f->blob_bytes = blob_bytes;
         f->stride = stride;
-        for (int k = 0; k < kReaders; ++k) f->workers.emplace_back(reader, f);
+        // QLX_FILE_READERS (1..64) overrides the reader count (requests in flight)
+        int readers = kReaders;
+        if (const char* e = std::getenv("QLX_FILE_READERS")) readers = std::max(1, std::min(64, std::atoi(e)));
+        for (int k = 0; k < readers; ++k) f->workers.emplace_back(reader, f);
         *out = f;
     });
 }
