@@ -189,6 +189,31 @@ int qlx_ctx_destroy(qlx_ctx* ctx);
 /* Waits for all work of the last step and fills *stats (HOST) if non-NULL. */
 int qlx_ctx_sync(qlx_ctx* ctx, qlx_stats* stats);
 
+/* Stream debugging (fault injection for the one race the streamer can have:
+ * a copy overwriting a slot that a kernel still reads). None changes what a
+ * step computes; every mode but QLX_DEBUG_POISON_LIVE must give the same bits
+ * as a normal run.
+ *   QLX_DEBUG_SERIALIZE: synchronize after every copy and every layer (no
+ *     overlap at all).
+ *   QLX_DEBUG_POISON: before a slot is refilled, fill it with 0xFF bytes (NaN
+ *     absmax and norm gains), so a read after its release turns into NaN.
+ *   QLX_DEBUG_DELAY_COPY / _DELAY_COMPUTE: a spin of about delay_us on the
+ *     copy stream before each copy / on the compute stream before each layer,
+ *     shifting the overlap either way.
+ *   QLX_DEBUG_POISON_LIVE: control for the poison: fills each slot right after
+ *     its copy, so the step must come out NaN.
+ * The copies of one layer run in two halves on two side streams (two copy
+ * engines); the environment variable QLX_COPY_SPLIT=1 at context creation
+ * keeps them on one. */
+enum {
+    QLX_DEBUG_SERIALIZE = 1,
+    QLX_DEBUG_POISON = 2,
+    QLX_DEBUG_DELAY_COPY = 4,
+    QLX_DEBUG_DELAY_COMPUTE = 8,
+    QLX_DEBUG_POISON_LIVE = 16
+};
+int qlx_ctx_set_debug(qlx_ctx* ctx, int flags, int delay_us);
+
 /* Disk stream source (rug.gal article, "En detalle": the frozen base sits in
  * CPU memory or on disk; imasters article, "Como cabe um 8B em 4 GB": the
  * `stream_source: auto` setting, RAM when the stack fits and the NVMe disk

@@ -20,6 +20,8 @@ QLX_OK, QLX_EINVAL, QLX_EUNSUPPORTED, QLX_EWORKSPACE, QLX_ENOTPINNED, QLX_EHIP, 
 QLX_F32, QLX_BF16 = 0, 1
 QLX_STREAMED, QLX_RESIDENT, QLX_STREAMED_DISK = 0, 1, 2
 QLX_FILE_BUFFERED = 1
+QLX_DEBUG_SERIALIZE, QLX_DEBUG_POISON, QLX_DEBUG_DELAY_COPY, QLX_DEBUG_DELAY_COMPUTE, QLX_DEBUG_POISON_LIVE = (
+    1, 2, 4, 8, 16)
 QLX_DPO_REF_FUSED, QLX_DPO_REF_SEPARATE = 0, 1
 QLX_PREF_DPO, QLX_PREF_ORPO, QLX_PREF_SIMPO, QLX_PREF_KTO = 0, 1, 2, 3
 QLX_MERGE_BF16, QLX_MERGE_NF4 = 0, 1
@@ -36,7 +38,7 @@ EXPORTED = (
     "layer_fwd", "layer_bwd", "qlx_ctx_create", "qlx_ctx_destroy", "qlx_ctx_sync",
     "qlx_step_workspace_bytes", "stream_step_sft", "stream_step_dpo", "stream_step_pref", "qlx_merge_workspace_bytes", "qlx_lora_merge", "qlx_profile_begin", "qlx_profile_begin_prefix", "qlx_profile_end", "qlx_adamw_lora",
     "qlx_layer_file_write", "qlx_layer_file_open", "qlx_layer_file_close", "qlx_layer_file_info",
-    "qlx_layer_file_read", "qlx_ctx_set_layer_source", "qlx_stream_source_auto",
+    "qlx_layer_file_read", "qlx_ctx_set_layer_source", "qlx_stream_source_auto", "qlx_ctx_set_debug",
 )
 
 
@@ -149,6 +151,7 @@ def lib() -> C.CDLL:
         "qlx_layer_file_read": (i32, [vp, i32, vp]),
         "qlx_ctx_set_layer_source": (i32, [vp, vp]),
         "qlx_stream_source_auto": (i32, [C.c_uint64, C.c_uint64, C.POINTER(C.c_int)]),
+        "qlx_ctx_set_debug": (i32, [vp, i32, i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -387,6 +390,10 @@ class Context:
         h = C.c_void_p()
         _check(lib().qlx_ctx_create(C.byref(h), device))
         self.h = h
+
+    def set_debug(self, flags: int, delay_us: int = 0) -> None:
+        """Stream fault injection (QLX_DEBUG_*): serialize, poison freed slots, delay copies or compute."""
+        _check(lib().qlx_ctx_set_debug(self.h, flags, delay_us))
 
     def set_layer_source(self, f: "LayerFile | None") -> None:
         """Attaches a stack file for QLX_STREAMED_DISK (None detaches)."""

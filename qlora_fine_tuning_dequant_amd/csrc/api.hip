@@ -17,6 +17,7 @@
 // QLX_DPO_REF_SEPARATE streams a separate reference pass first.
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -336,6 +337,12 @@ int layer_bwd(const qlx_dims* d, const void* blob, const qlx_lora* lora, const f
 struct qlx_ctx {
     int device = 0;
     hipStream_t side = nullptr;
+    hipStream_t side2 = nullptr;      // second copy stream (copy_split == 2)
+    hipEvent_t half_done = nullptr;   // side2's half of the current copy
+    hipEvent_t copy_start = nullptr;  // side is ready to overwrite the slot
+    int copy_split = 2;
+    int debug = 0;                    // QLX_DEBUG_* flags
+    int delay_us = 0;
     hipEvent_t copy_done[2] = {nullptr, nullptr};
     hipEvent_t compute_done[2] = {nullptr, nullptr};
     hipEvent_t step_begin = nullptr, step_end = nullptr;
@@ -431,6 +438,7 @@ class Streamer {
         const int sl = slot_of(i);
         if (held_[sl] != i) issue_copy(i, sl);
         QLX_CHECK_HIP(hipStreamWaitEvent(main_, ctx_->copy_done[sl], 0));
+        if (ctx_->debug & QLX_DEBUG_DELAY_COMPUTE) launch_spin(ctx_->delay_us, main_);
         return w_.slot[sl];
     }
     void prefetch(int i) {
@@ -442,6 +450,7 @@ class Streamer {
     void release(int i) {
         if (mode_ == QLX_RESIDENT) return;
         QLX_CHECK_HIP(hipEventRecord(ctx_->compute_done[slot_of(i)], main_));
+        if (ctx_->debug & QLX_DEBUG_SERIALIZE) QLX_CHECK_HIP(hipStreamSynchronize(main_));
     }
     void forget() { held_[0] = held_[1] = -1; }
 
@@ -468,12 +477,33 @@ class Streamer {
         } else {
             src = m_->layer_blobs[i];
         }
+        // debugging: a freed slot is filled with NaN bytes before it is
+        // refilled (a read of it after its release would show as NaN), and a
+        // spin shifts the copy against the compute
+        if (ctx_->debug & QLX_DEBUG_POISON)
+            launch_fill_u32(reinterpret_cast<uint32_t*>(w_.slot[sl]), int64_t(bytes_ / 4), 0xFFFFFFFFu, ctx_->side);
+        if (ctx_->debug & QLX_DEBUG_DELAY_COPY) launch_spin(ctx_->delay_us, ctx_->side);
         hipEvent_t* ev = next_timing_pair();
         if (ev) QLX_CHECK_HIP(hipEventRecord(ev[0], ctx_->side));
-        QLX_CHECK_HIP(hipMemcpyAsync(w_.slot[sl], src, bytes_, hipMemcpyHostToDevice, ctx_->side));
+        if (ctx_->copy_split == 2 && bytes_ > 8192) {
+            // the two halves on two streams, so two copy engines share the link
+            const uint64_t h = (bytes_ / 2 + 4095) & ~uint64_t(4095);
+            QLX_CHECK_HIP(hipEventRecord(ctx_->copy_start, ctx_->side));
+            QLX_CHECK_HIP(hipStreamWaitEvent(ctx_->side2, ctx_->copy_start, 0));
+            QLX_CHECK_HIP(hipMemcpyAsync(w_.slot[sl] + h, static_cast<const char*>(src) + h, bytes_ - h,
+                                         hipMemcpyHostToDevice, ctx_->side2));
+            QLX_CHECK_HIP(hipEventRecord(ctx_->half_done, ctx_->side2));
+            QLX_CHECK_HIP(hipMemcpyAsync(w_.slot[sl], src, h, hipMemcpyHostToDevice, ctx_->side));
+            QLX_CHECK_HIP(hipStreamWaitEvent(ctx_->side, ctx_->half_done, 0));
+        } else {
+            QLX_CHECK_HIP(hipMemcpyAsync(w_.slot[sl], src, bytes_, hipMemcpyHostToDevice, ctx_->side));
+        }
         if (ev) QLX_CHECK_HIP(hipEventRecord(ev[1], ctx_->side));
         if (k >= 0) QLX_CHECK_HIP(hipEventRecord(f->staging_free[k], ctx_->side));
+        if (ctx_->debug & QLX_DEBUG_POISON_LIVE)  // control: poisons the slot it just filled
+            launch_fill_u32(reinterpret_cast<uint32_t*>(w_.slot[sl]), int64_t(bytes_ / 4), 0xFFFFFFFFu, ctx_->side);
         QLX_CHECK_HIP(hipEventRecord(ctx_->copy_done[sl], ctx_->side));
+        if (ctx_->debug & QLX_DEBUG_SERIALIZE) QLX_CHECK_HIP(hipStreamSynchronize(ctx_->side));
         held_[sl] = i;
         ctx_->stats.layer_reads += 1;
         ctx_->stats.h2d_bytes += int64_t(bytes_);
@@ -620,6 +650,11 @@ int qlx_ctx_create(qlx_ctx** out, int device) {
         qlx_ctx* c = new qlx_ctx();
         c->device = device;
         QLX_CHECK_HIP(hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking));
+        QLX_CHECK_HIP(hipStreamCreateWithFlags(&c->side2, hipStreamNonBlocking));
+        QLX_CHECK_HIP(hipEventCreateWithFlags(&c->half_done, hipEventDisableTiming));
+        QLX_CHECK_HIP(hipEventCreateWithFlags(&c->copy_start, hipEventDisableTiming));
+        // QLX_COPY_SPLIT=1: one copy stream (default 2: each layer copy in two halves on two streams)
+        if (const char* e = std::getenv("QLX_COPY_SPLIT")) c->copy_split = std::atoi(e) == 1 ? 1 : 2;
         for (int i = 0; i < 2; ++i) {
             QLX_CHECK_HIP(hipEventCreateWithFlags(&c->copy_done[i], hipEventDisableTiming));
             QLX_CHECK_HIP(hipEventCreateWithFlags(&c->compute_done[i], hipEventDisableTiming));
@@ -644,8 +679,24 @@ int qlx_ctx_destroy(qlx_ctx* ctx) {
         }
         (void)hipEventDestroy(ctx->step_begin);
         (void)hipEventDestroy(ctx->step_end);
+        (void)hipStreamSynchronize(ctx->side2);
+        (void)hipEventDestroy(ctx->half_done);
+        (void)hipEventDestroy(ctx->copy_start);
+        (void)hipStreamDestroy(ctx->side2);
         (void)hipStreamDestroy(ctx->side);
         delete ctx;
+    });
+}
+
+int qlx_ctx_set_debug(qlx_ctx* ctx, int flags, int delay_us) {
+    return guarded([&] {
+        REQ_PTR(ctx, "ctx");
+        QLX_REQUIRE((flags & ~(QLX_DEBUG_SERIALIZE | QLX_DEBUG_POISON | QLX_DEBUG_DELAY_COPY | QLX_DEBUG_DELAY_COMPUTE |
+                               QLX_DEBUG_POISON_LIVE)) == 0,
+                    QLX_EINVAL, "unknown debug flags");
+        QLX_REQUIRE(delay_us >= 0 && delay_us <= 1000000, QLX_EINVAL, "delay_us must be in 0..1000000");
+        ctx->debug = flags;
+        ctx->delay_us = delay_us;
     });
 }
 

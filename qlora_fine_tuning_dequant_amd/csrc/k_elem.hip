@@ -8,6 +8,7 @@
 // Every reduction runs in a fixed order (per-thread strided partial sums,
 // xor-shuffle wavefront trees, then the waves in index order), so results
 // never depend on scheduling.
+#include <algorithm>
 #include <cmath>
 
 #include "nf4_codes.h"
@@ -219,6 +220,30 @@ void launch_f32_to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s) {
     ProfScope prof("f32_to_bf16", 0.0, 6.0 * n, s);
     hipLaunchKernelGGL(k_f32_to_bf16, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, x, n, y);
     check_launch("f32_to_bf16");
+}
+
+// ------------------------------------------------------------------ stream debugging
+// Fills n 32-bit words with one pattern (the poison of a freed slot).
+__global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
+        p[i] = v;
+}
+void launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
+    if (n <= 0) return;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_fill_u32, dim3(unsigned(blocks)), dim3(256), 0, s, p, n, v);
+    check_launch("fill_u32");
+}
+// Occupies its stream for about `sleeps` x 8k cycles (a fixed count of
+// s_sleep 127, so it always ends): shifts when the next operation starts.
+__global__ void k_spin(int sleeps) {
+    for (int i = 0; i < sleeps; ++i) __builtin_amdgcn_s_sleep(127);
+}
+void launch_spin(int delay_us, hipStream_t s) {
+    if (delay_us <= 0) return;
+    const int sleeps = std::min(1 << 20, delay_us / 3 + 1);  // s_sleep 127 ~ 8128 cycles ~ 3.4 us
+    hipLaunchKernelGGL(k_spin, dim3(1), dim3(64), 0, s, sleeps);
+    check_launch("spin");
 }
 
 // ------------------------------------------------------------------ LoRA staging

@@ -171,6 +171,8 @@ void launch_swiglu_fwd(const uint16_t* gu, int T, int I, uint16_t* act, hipStrea
 void launch_swiglu_bwd(const uint16_t* dact, const uint16_t* gu, int T, int I, uint16_t* dgu, hipStream_t s);
 void launch_embed(const int32_t* tok, const uint16_t* E, int T, int H, int V, float* h, hipStream_t s);
 void launch_f32_to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s);
+void launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
+void launch_spin(int delay_us, hipStream_t s);
 struct LoraSeg {
     const float* A;  // [r, in]
     const float* B;  // [out_p, r]

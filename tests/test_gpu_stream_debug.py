@@ -1,0 +1,98 @@
+"""Fault injection on the layer stream: the one race the streamer can have is
+a copy overwriting a slot that a kernel still reads. Serializing everything,
+poisoning every freed slot with NaN bytes before it is refilled, and delaying
+the copies or the compute must all leave the loss and every gradient
+identical to the normal run; poisoning the live slot instead (the control)
+must show up as NaN."""
+import dataclasses
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_helpers import gpu_model, run_dpo, run_sft, same_grads
+
+pytestmark = pytest.mark.gpu
+q = pytest.importorskip("qlora_fine_tuning_dequant_amd")
+B_ = q.binding
+
+
+@pytest.fixture(scope="module")
+def four():
+    d = dataclasses.replace(synth.TINY, n_layers=4)
+    m, host = gpu_model(q, d, 3, "normal")
+    return d, m.with_blobs(host)
+
+
+MODES = [
+    ("serialize", B_.QLX_DEBUG_SERIALIZE, 0),
+    ("poison", B_.QLX_DEBUG_POISON, 0),
+    ("poison+delay_copy", B_.QLX_DEBUG_POISON | B_.QLX_DEBUG_DELAY_COPY, 300),
+    ("poison+delay_compute", B_.QLX_DEBUG_POISON | B_.QLX_DEBUG_DELAY_COMPUTE, 300),
+    ("poison+serialize", B_.QLX_DEBUG_POISON | B_.QLX_DEBUG_SERIALIZE, 0),
+]
+
+
+@pytest.mark.parametrize("name,flags,delay", MODES, ids=[m[0] for m in MODES])
+def test_sft_under_fault_injection_is_bit_identical(four, name, flags, delay):
+    d, sm = four
+    toks = synth.tokens(3, 2, 32, d.vocab)
+    l0, g0, _ = run_sft(q, sm, toks, B_.QLX_STREAMED)
+    ctx = q.Context(0)
+    ctx.set_debug(flags, delay)
+    print("debug mode", name, flush=True)
+    l1, g1, st = run_sft(q, sm, toks, B_.QLX_STREAMED, ctx)
+    assert np.isfinite(l1.item())
+    assert torch.equal(l0, l1) and same_grads(g0, g1)
+    assert st["layer_reads"] == 2 * 4 - 2
+    ctx.close()
+
+
+def test_dpo_separate_reference_under_poison_and_delays(four):
+    d, sm = four
+    ch, rj = synth.dpo_pairs(3, 2, 32, 8, d.vocab)
+    l0, lp0, g0, _ = run_dpo(q, sm, ch, rj, 8, 0.1, B_.QLX_STREAMED, B_.QLX_DPO_REF_SEPARATE)
+    for flags in (B_.QLX_DEBUG_POISON | B_.QLX_DEBUG_DELAY_COPY, B_.QLX_DEBUG_POISON | B_.QLX_DEBUG_DELAY_COMPUTE):
+        ctx = q.Context(0)
+        ctx.set_debug(flags, 300)
+        l1, lp1, g1, _ = run_dpo(q, sm, ch, rj, 8, 0.1, B_.QLX_STREAMED, B_.QLX_DPO_REF_SEPARATE, ctx)
+        assert torch.equal(l0, l1) and torch.equal(lp0, lp1) and same_grads(g0, g1)
+        ctx.close()
+
+
+def test_one_copy_stream_equals_two(four, monkeypatch):
+    """Each layer copy runs in two halves on two streams by default;
+    QLX_COPY_SPLIT=1 at context creation keeps one stream: same bits."""
+    d, sm = four
+    toks = synth.tokens(3, 1, 32, d.vocab)
+    l2, g2, _ = run_sft(q, sm, toks, B_.QLX_STREAMED)
+    monkeypatch.setenv("QLX_COPY_SPLIT", "1")
+    ctx = q.Context(0)
+    monkeypatch.delenv("QLX_COPY_SPLIT")
+    ctx.set_debug(B_.QLX_DEBUG_POISON)
+    l1, g1, _ = run_sft(q, sm, toks, B_.QLX_STREAMED, ctx)
+    assert torch.equal(l1, l2) and same_grads(g1, g2)
+    ctx.close()
+
+
+def test_poisoning_the_live_slot_shows_up(four):
+    """Control: the poison reaches what the kernels read."""
+    d, sm = four
+    toks = synth.tokens(3, 1, 32, d.vocab)
+    ctx = q.Context(0)
+    ctx.set_debug(B_.QLX_DEBUG_POISON_LIVE)
+    l1, _, _ = run_sft(q, sm, toks, B_.QLX_STREAMED, ctx)
+    assert np.isnan(l1.item())
+    ctx.close()
+
+
+def test_bad_debug_arguments():
+    ctx = q.Context(0)
+    L = B_.lib()
+    assert L.qlx_ctx_set_debug(ctx.h, 64, 0) == B_.QLX_EINVAL
+    assert L.qlx_ctx_set_debug(ctx.h, B_.QLX_DEBUG_DELAY_COPY, -1) == B_.QLX_EINVAL
+    assert L.qlx_ctx_set_debug(None, 0, 0) == B_.QLX_EINVAL
+    assert L.qlx_ctx_set_debug(ctx.h, 0, 0) == B_.QLX_OK
+    ctx.close()
