@@ -14,8 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libqlx.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["k_nf4.hip", "k_gemm.hip", "k_elem.hip", "optim.hip", "merge.hip", "layer.hip", "api.hip", "source.hip",
-           "prof.hip"]
+SOURCES = ["k_nf4.hip", "k_gemm.hip", "k_elem.hip", "attention.hip", "optim.hip", "merge.hip", "layer.hip", "api.hip",
+           "source.hip", "prof.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -1,0 +1,406 @@
+// Causal grouped-query attention, flash-style (the score matrix is never
+// stored): forward with an online softmax that keeps each query's log-sum-exp
+// for the backward, and a backward that recomputes the probabilities block by
+// block. The method is the Llama decoder's attention (softmax(q k^T / sqrt(d)
+// + causal mask) v, grouped-query: nH / nKV query heads share one key/value
+// head); the tiling is the FlashAttention scheme (Dao et al., 2022; Dao,
+// 2023) written for CDNA4 wave64 MFMA v_mfma_f32_16x16x32_bf16.
+//
+// Forward, one workgroup per (64 queries, head, sequence), 4 wavefronts of
+// 16 queries. It computes S^T = K Q^T rather than S, so each lane holds the
+// scores of ONE query (4 keys per 16-key tile): the running max and sum are
+// per-lane scalars shared by the 4 lanes of a query, the rescale of the
+// output is a per-lane multiply, and the probabilities already sit in the
+// layout of the B operand of O^T += V^T P^T (V is staged transposed in LDS).
+// P is rounded to bf16 for that product (as the reference path rounds its
+// probabilities); the running sum uses the fp32 values.
+//
+// Backward (deterministic, no atomics): D_q = sum_d dO o; dK/dV per (key block
+// of 64, query head), each wavefront owning 16 keys and walking the query
+// blocks at or after its own (S = Q K^T here, so each lane holds one KEY and
+// P^T, dS^T are A operands in registers); the per-head fp32 dK, dV are then
+// summed over the heads of a group in a fixed order by the GQA reduce. dQ in a
+// separate pass per (64 queries, head), S^T formulation as in the forward.
+#include <cmath>
+
+#include "nf4_codes.h"
+#include "qlx_internal.h"
+
+namespace qlx {
+
+namespace {
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline f32x4 mfma(const uint4& a, const uint4& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                   0, 0);
+}
+__device__ inline uint32_t pack_bf16(float lo, float hi) { return f32x2_to_bf16x2(lo, hi); }
+
+constexpr int QB = 64;       // queries (or keys) per workgroup block
+constexpr int TP = QB + 8;   // row stride (elements) of a transposed [HD][64] tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Stages rows [r0, r0 + 64) x HD of a [T, ld] bf16 matrix (column offset col)
+// into LDS, row-major (stride HD + 8) and/or transposed (stride TP); rows at or
+// past `rows` are zeros. 256 threads: 4 per row, HD/4 columns each.
+template <int HD, bool ROW, bool TRANS>
+__device__ inline void stage(const uint16_t* __restrict__ src, int64_t ld, int64_t base_row, int r0, int rows,
+                             int64_t col, uint16_t* __restrict__ dst_row, uint16_t* __restrict__ dst_t) {
+    const int tid = threadIdx.x, r = tid >> 2, part = tid & 3;
+    const bool ok = r0 + r < rows;
+    const uint16_t* s = src + (base_row + r0 + r) * ld + col + part * (HD / 4);
+#pragma unroll
+    for (int c8 = 0; c8 < HD / 32; ++c8) {
+        const uint4 v = ok ? *reinterpret_cast<const uint4*>(s + c8 * 8) : make_uint4(0, 0, 0, 0);
+        const int c0 = part * (HD / 4) + c8 * 8;
+        if (ROW) *reinterpret_cast<uint4*>(dst_row + r * (HD + 8) + c0) = v;
+        if (TRANS) {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dst_t[(c0 + 2 * e) * TP + r] = uint16_t(w[e] & 0xFFFF);
+                dst_t[(c0 + 2 * e + 1) * TP + r] = uint16_t(w[e] >> 16);
+            }
+        }
+    }
+}
+
+// A-operand fragment of a transposed tile for a 32-wide slice js of the
+// 64-row block, in the order the accumulator layout hands out rows: lane
+// (row d = lane & 15 of the 16-row tile dt, group g = lane >> 4) takes block
+// rows 32 js + 4 g + {0..3} and 32 js + 16 + 4 g + {0..3}.
+template <int HD>
+__device__ inline uint4 tfrag(const uint16_t* __restrict__ t, int dt, int js, int lane) {
+    const uint16_t* p = t + (dt * 16 + (lane & 15)) * TP + js * 32 + (lane >> 4) * 4;
+    const uint2 lo = *reinterpret_cast<const uint2*>(p);
+    const uint2 hi = *reinterpret_cast<const uint2*>(p + 16);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+}  // namespace
+
+// ------------------------------------------------------------------ forward
+template <int HD>
+__global__ __launch_bounds__(256) void k_flash_fwd(const AttnArgs a) {
+    __shared__ __align__(16) uint16_t Ks[QB * (HD + 8)];
+    __shared__ __align__(16) uint16_t Vt[HD * TP];
+    const int nqb = (a.S + QB - 1) / QB;
+    const int qb = nqb - 1 - int(blockIdx.x);  // longest (latest) query blocks first
+    const int h = blockIdx.y, b = blockIdx.z, kh = h / (a.nH / a.nKV);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+    const int q = qb * QB + wave * 16 + lr;
+    const int64_t row0 = int64_t(b) * a.S;
+    uint4 qf[HD / 32];
+#pragma unroll
+    for (int ds = 0; ds < HD / 32; ++ds)
+        qf[ds] = q < a.S ? *reinterpret_cast<const uint4*>(a.qkv + (row0 + q) * a.ld + int64_t(h) * HD + ds * 32 + g * 8)
+                         : make_uint4(0, 0, 0, 0);
+    f32x4 o[HD / 16];
+#pragma unroll
+    for (int dt = 0; dt < HD / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.f;
+    const float c = a.scale * kLog2e;
+    const int64_t kcol = a.qdim + int64_t(kh) * HD, vcol = kcol + a.kvdim;
+    for (int kb = 0; kb <= qb; ++kb) {
+        stage<HD, true, false>(a.qkv, a.ld, row0, kb * QB, a.S, kcol, Ks, nullptr);
+        stage<HD, false, true>(a.qkv, a.ld, row0, kb * QB, a.S, vcol, nullptr, Vt);
+        __syncthreads();
+        f32x4 st[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ds = 0; ds < HD / 32; ++ds)
+                st[kt] = mfma(*reinterpret_cast<const uint4*>(Ks + (kt * 16 + lr) * (HD + 8) + ds * 32 + g * 8), qf[ds],
+                              st[kt]);
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int key = kb * QB + kt * 16 + g * 4 + e;
+                if (key > q || key >= a.S) st[kt][e] = -INFINITY;
+                mx = fmaxf(mx, st[kt][e]);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mnew = fmaxf(m, mx);  // finite: key block 0 holds key 0 <= q
+        const float alpha = exp2f((m - mnew) * c);
+        m = mnew;
+        const float mc = m * c;
+        float ps = 0.f;
+        uint32_t pk[4][2];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            float p[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                p[e] = exp2f(fmaf(st[kt][e], c, -mc));
+                ps += p[e];
+            }
+            pk[kt][0] = pack_bf16(p[0], p[1]);
+            pk[kt][1] = pack_bf16(p[2], p[3]);
+        }
+        l = l * alpha + ps;
+#pragma unroll
+        for (int dt = 0; dt < HD / 16; ++dt) o[dt] *= alpha;
+#pragma unroll
+        for (int js = 0; js < 2; ++js) {
+            const uint4 pf = make_uint4(pk[2 * js][0], pk[2 * js][1], pk[2 * js + 1][0], pk[2 * js + 1][1]);
+#pragma unroll
+            for (int dt = 0; dt < HD / 16; ++dt) o[dt] = mfma(tfrag<HD>(Vt, dt, js, lane), pf, o[dt]);
+        }
+        __syncthreads();
+    }
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (q >= a.S) return;
+    const float inv = 1.f / l;
+    uint16_t* dst = a.o + (row0 + q) * a.ldo + int64_t(h) * HD + g * 4;
+#pragma unroll
+    for (int dt = 0; dt < HD / 16; ++dt)
+        *reinterpret_cast<uint2*>(dst + dt * 16) =
+            make_uint2(pack_bf16(o[dt][0] * inv, o[dt][1] * inv), pack_bf16(o[dt][2] * inv, o[dt][3] * inv));
+    if (g == 0) a.lse[(int64_t(b) * a.nH + h) * a.S + q] = m * a.scale + logf(l);
+}
+
+// ------------------------------------------------------------------ backward
+// D[b, h, q] = sum_d dO[q, h d] o[q, h d], one thread per (query, head).
+__global__ __launch_bounds__(256) void k_flash_bwd_dot(const AttnArgs a, int hd) {
+    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t T = int64_t(a.B) * a.S;
+    if (idx >= T * a.nH) return;
+    const int64_t t = idx / a.nH;
+    const int h = int(idx % a.nH);
+    const uint16_t* x = a.dO + t * a.ldo + int64_t(h) * hd;
+    const uint16_t* y = a.O + t * a.ldo + int64_t(h) * hd;
+    float s = 0.f;
+    for (int d = 0; d < hd; d += 8) {
+        const uint4 u = *reinterpret_cast<const uint4*>(x + d), v = *reinterpret_cast<const uint4*>(y + d);
+        const uint32_t uw[4] = {u.x, u.y, u.z, u.w}, vw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            s = fmaf(__builtin_bit_cast(float, uw[e] << 16), __builtin_bit_cast(float, vw[e] << 16), s);
+            s = fmaf(__builtin_bit_cast(float, uw[e] & 0xFFFF0000u), __builtin_bit_cast(float, vw[e] & 0xFFFF0000u), s);
+        }
+    }
+    const int64_t b = t / a.S, qi = t % a.S;
+    a.Dq[(b * a.nH + h) * a.S + qi] = s;
+}
+
+// dK_h, dV_h (fp32, per query head) for one block of 64 keys.
+template <int HD>
+__global__ __launch_bounds__(256) void k_flash_bwd_kv(const AttnArgs a) {
+    __shared__ __align__(16) uint16_t Qs[QB * (HD + 8)];
+    __shared__ __align__(16) uint16_t Qt[HD * TP];
+    __shared__ __align__(16) uint16_t Ds[QB * (HD + 8)];  // dO row-major
+    __shared__ __align__(16) uint16_t Dt[HD * TP];        // dO transposed
+    __shared__ float lse_s[QB], dq_s[QB];
+    const int nkb = (a.S + QB - 1) / QB;
+    const int kb = int(blockIdx.x);  // early key blocks see the most queries
+    const int h = blockIdx.y, b = blockIdx.z, kh = h / (a.nH / a.nKV);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+    const int key = kb * QB + wave * 16 + lr;  // this lane's key (B-operand column of S and dP)
+    const int64_t row0 = int64_t(b) * a.S;
+    const int64_t kcol = a.qdim + int64_t(kh) * HD, vcol = kcol + a.kvdim;
+    uint4 kf[HD / 32], vf[HD / 32];
+#pragma unroll
+    for (int ds = 0; ds < HD / 32; ++ds) {
+        const bool ok = key < a.S;
+        kf[ds] = ok ? *reinterpret_cast<const uint4*>(a.qkv + (row0 + key) * a.ld + kcol + ds * 32 + g * 8)
+                    : make_uint4(0, 0, 0, 0);
+        vf[ds] = ok ? *reinterpret_cast<const uint4*>(a.qkv + (row0 + key) * a.ld + vcol + ds * 32 + g * 8)
+                    : make_uint4(0, 0, 0, 0);
+    }
+    f32x4 dk[HD / 16], dv[HD / 16];
+#pragma unroll
+    for (int dt = 0; dt < HD / 16; ++dt) dk[dt] = dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float c = a.scale * kLog2e;
+    const int64_t zrow = (int64_t(b) * a.nH + h) * a.S;
+    for (int qb = kb; qb < nkb; ++qb) {
+        stage<HD, true, true>(a.qkv, a.ld, row0, qb * QB, a.S, int64_t(h) * HD, Qs, Qt);
+        stage<HD, true, true>(a.dO, a.ldo, row0, qb * QB, a.S, int64_t(h) * HD, Ds, Dt);
+        if (tid < QB) {
+            const int qq = qb * QB + tid;
+            lse_s[tid] = qq < a.S ? a.lse[zrow + qq] * kLog2e : 0.f;
+            dq_s[tid] = qq < a.S ? a.Dq[zrow + qq] : 0.f;
+        }
+        __syncthreads();
+        // S = Q K^T and dP = dO V^T for 64 queries x this wavefront's 16 keys
+        f32x4 s[4], dp[4];
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) {
+            s[qt] = dp[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ds = 0; ds < HD / 32; ++ds) {
+                s[qt] = mfma(*reinterpret_cast<const uint4*>(Qs + (qt * 16 + lr) * (HD + 8) + ds * 32 + g * 8), kf[ds],
+                             s[qt]);
+                dp[qt] = mfma(*reinterpret_cast<const uint4*>(Ds + (qt * 16 + lr) * (HD + 8) + ds * 32 + g * 8), vf[ds],
+                              dp[qt]);
+            }
+        }
+        // P and dS = P (dP - D), lane = key, 16 queries per lane
+        uint32_t pk[4][2], sk[4][2];
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) {
+            float p[4], d[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ql = qt * 16 + g * 4 + e, qq = qb * QB + ql;
+                const bool live = qq < a.S && key < a.S && key <= qq;
+                p[e] = live ? exp2f(fmaf(s[qt][e], c, -lse_s[ql])) : 0.f;
+                d[e] = p[e] * (dp[qt][e] - dq_s[ql]);
+            }
+            pk[qt][0] = pack_bf16(p[0], p[1]);
+            pk[qt][1] = pack_bf16(p[2], p[3]);
+            sk[qt][0] = pack_bf16(d[0], d[1]);
+            sk[qt][1] = pack_bf16(d[2], d[3]);
+        }
+        // dV += P^T dO and dK += dS^T Q over the 64 queries (two slices of 32)
+#pragma unroll
+        for (int js = 0; js < 2; ++js) {
+            const uint4 pa = make_uint4(pk[2 * js][0], pk[2 * js][1], pk[2 * js + 1][0], pk[2 * js + 1][1]);
+            const uint4 sa = make_uint4(sk[2 * js][0], sk[2 * js][1], sk[2 * js + 1][0], sk[2 * js + 1][1]);
+#pragma unroll
+            for (int dt = 0; dt < HD / 16; ++dt) {
+                dv[dt] = mfma(pa, tfrag<HD>(Dt, dt, js, lane), dv[dt]);
+                dk[dt] = mfma(sa, tfrag<HD>(Qt, dt, js, lane), dk[dt]);
+            }
+        }
+        __syncthreads();
+    }
+    // dk[dt][e], dv[dt][e]: key kb*64 + 16 wave + 4 g + e, dim 16 dt + lr
+    const int64_t zk = (int64_t(b) * a.nH + h) * a.S;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int kk = kb * QB + wave * 16 + g * 4 + e;
+        if (kk >= a.S) continue;
+#pragma unroll
+        for (int dt = 0; dt < HD / 16; ++dt) {
+            a.dKh[(zk + kk) * HD + dt * 16 + lr] = dk[dt][e] * a.scale;
+            a.dVh[(zk + kk) * HD + dt * 16 + lr] = dv[dt][e];
+        }
+    }
+}
+
+// dQ for 64 queries of one head.
+template <int HD>
+__global__ __launch_bounds__(256) void k_flash_bwd_q(const AttnArgs a) {
+    __shared__ __align__(16) uint16_t Ks[QB * (HD + 8)];
+    __shared__ __align__(16) uint16_t Vs[QB * (HD + 8)];
+    __shared__ __align__(16) uint16_t Kt[HD * TP];
+    const int nqb = (a.S + QB - 1) / QB;
+    const int qb = nqb - 1 - int(blockIdx.x);
+    const int h = blockIdx.y, b = blockIdx.z, kh = h / (a.nH / a.nKV);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, g = lane >> 4;
+    const int q = qb * QB + wave * 16 + lr;
+    const int64_t row0 = int64_t(b) * a.S;
+    const bool qok = q < a.S;
+    uint4 qf[HD / 32], df[HD / 32];
+#pragma unroll
+    for (int ds = 0; ds < HD / 32; ++ds) {
+        qf[ds] = qok ? *reinterpret_cast<const uint4*>(a.qkv + (row0 + q) * a.ld + int64_t(h) * HD + ds * 32 + g * 8)
+                     : make_uint4(0, 0, 0, 0);
+        df[ds] = qok ? *reinterpret_cast<const uint4*>(a.dO + (row0 + q) * a.ldo + int64_t(h) * HD + ds * 32 + g * 8)
+                     : make_uint4(0, 0, 0, 0);
+    }
+    const int64_t zq = (int64_t(b) * a.nH + h) * a.S + q;
+    const float lse2 = qok ? a.lse[zq] * kLog2e : 0.f, dd = qok ? a.Dq[zq] : 0.f;
+    f32x4 dq[HD / 16];
+#pragma unroll
+    for (int dt = 0; dt < HD / 16; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float c = a.scale * kLog2e;
+    const int64_t kcol = a.qdim + int64_t(kh) * HD, vcol = kcol + a.kvdim;
+    for (int kb = 0; kb <= qb; ++kb) {
+        stage<HD, true, true>(a.qkv, a.ld, row0, kb * QB, a.S, kcol, Ks, Kt);
+        stage<HD, true, false>(a.qkv, a.ld, row0, kb * QB, a.S, vcol, Vs, nullptr);
+        __syncthreads();
+        uint32_t sk[4][2];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f}, dpt = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ds = 0; ds < HD / 32; ++ds) {
+                st = mfma(*reinterpret_cast<const uint4*>(Ks + (kt * 16 + lr) * (HD + 8) + ds * 32 + g * 8), qf[ds], st);
+                dpt = mfma(*reinterpret_cast<const uint4*>(Vs + (kt * 16 + lr) * (HD + 8) + ds * 32 + g * 8), df[ds],
+                           dpt);
+            }
+            float d[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int key = kb * QB + kt * 16 + g * 4 + e;
+                const bool live = qok && key < a.S && key <= q;
+                const float p = live ? exp2f(fmaf(st[e], c, -lse2)) : 0.f;
+                d[e] = p * (dpt[e] - dd);
+            }
+            sk[kt][0] = pack_bf16(d[0], d[1]);
+            sk[kt][1] = pack_bf16(d[2], d[3]);
+        }
+        // dQ^T += K^T dS^T over the 64 keys
+#pragma unroll
+        for (int js = 0; js < 2; ++js) {
+            const uint4 sb = make_uint4(sk[2 * js][0], sk[2 * js][1], sk[2 * js + 1][0], sk[2 * js + 1][1]);
+#pragma unroll
+            for (int dt = 0; dt < HD / 16; ++dt) dq[dt] = mfma(tfrag<HD>(Kt, dt, js, lane), sb, dq[dt]);
+        }
+        __syncthreads();
+    }
+    if (!qok) return;
+    uint16_t* dst = a.dqkv + (row0 + q) * a.lddq + int64_t(h) * HD + g * 4;
+#pragma unroll
+    for (int dt = 0; dt < HD / 16; ++dt)
+        *reinterpret_cast<uint2*>(dst + dt * 16) = make_uint2(pack_bf16(dq[dt][0] * a.scale, dq[dt][1] * a.scale),
+                                                              pack_bf16(dq[dt][2] * a.scale, dq[dt][3] * a.scale));
+}
+
+// ------------------------------------------------------------------ launchers
+static void check_attn(const AttnArgs& a) {
+    QLX_REQUIRE(a.hd == 64 || a.hd == 128, QLX_EUNSUPPORTED, "attention: head_dim must be 64 or 128");
+    QLX_REQUIRE(a.nKV > 0 && a.nH % a.nKV == 0, QLX_EINVAL, "attention: n_heads must be a multiple of n_kv_heads");
+    QLX_REQUIRE(a.ld % 8 == 0 && a.ldo % 8 == 0 && a.qdim % 8 == 0 && a.kvdim % 8 == 0, QLX_EUNSUPPORTED,
+                "attention: row strides must be multiples of 8 elements");
+    QLX_REQUIRE(a.nH <= 65535 && a.B <= 65535, QLX_EUNSUPPORTED, "attention: grid too large");
+}
+
+void launch_flash_fwd(const AttnArgs& a, hipStream_t s) {
+    if (a.B == 0 || a.S == 0) return;
+    check_attn(a);
+    const dim3 grid(unsigned((a.S + QB - 1) / QB), unsigned(a.nH), unsigned(a.B));
+    const double Sd = a.S;
+    const double flops = 4.0 * a.B * a.nH * a.hd * (Sd * (Sd + 1) / 2);
+    ProfScope prof("attn_fwd", flops, double(a.B) * a.S * (a.qdim * 4.0 + a.kvdim * 4.0 + a.nH * 4.0), s);
+    if (a.hd == 128) hipLaunchKernelGGL(k_flash_fwd<128>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_flash_fwd<64>, grid, dim3(256), 0, s, a);
+    check_launch("attn_fwd");
+}
+
+void launch_flash_bwd(const AttnArgs& a, hipStream_t s) {
+    if (a.B == 0 || a.S == 0) return;
+    check_attn(a);
+    const int64_t n = int64_t(a.B) * a.S * a.nH;
+    {
+        ProfScope prof("attn_bwd_dot", 2.0 * n * a.hd, double(n) * (a.hd * 4.0 + 4.0), s);
+        hipLaunchKernelGGL(k_flash_bwd_dot, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, a, a.hd);
+        check_launch("attn_bwd_dot");
+    }
+    const dim3 grid(unsigned((a.S + QB - 1) / QB), unsigned(a.nH), unsigned(a.B));
+    const double Sd = a.S, causal = Sd * (Sd + 1) / 2;
+    {  // recompute S and dP, then dV and dK: 4 products
+        ProfScope prof("attn_bwd_kv", 8.0 * a.B * a.nH * a.hd * causal,
+                       double(a.B) * a.S * (a.qdim * 4.0 + a.kvdim * 4.0 + a.nH * 2.0 * a.hd * 4.0), s);
+        if (a.hd == 128) hipLaunchKernelGGL(k_flash_bwd_kv<128>, grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(k_flash_bwd_kv<64>, grid, dim3(256), 0, s, a);
+        check_launch("attn_bwd_kv");
+    }
+    {  // recompute S and dP, then dQ: 3 products
+        ProfScope prof("attn_bwd_q", 6.0 * a.B * a.nH * a.hd * causal,
+                       double(a.B) * a.S * (a.qdim * 6.0 + a.kvdim * 4.0), s);
+        if (a.hd == 128) hipLaunchKernelGGL(k_flash_bwd_q<128>, grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(k_flash_bwd_q<64>, grid, dim3(256), 0, s, a);
+        check_launch("attn_bwd_q");
+    }
+}
+
+}  // namespace qlx

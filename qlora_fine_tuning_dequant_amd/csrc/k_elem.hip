@@ -293,54 +293,6 @@ void launch_lora_pack(const LoraSeg* segs, int nseg, int r, int in_f, float scal
     check_launch("lora_pack");
 }
 
-// ------------------------------------------------------------------ attention softmax
-// scores [Z, S, S] (already scaled by 1/sqrt(hd)); P[i][j] = softmax over j <= i,
-// 0 for j > i. One wavefront per row; only j <= i is read.
-__global__ __launch_bounds__(256) void k_attn_softmax_fwd(const float* __restrict__ sc, int Z, int S,
-                                                          uint16_t* __restrict__ P) {
-    const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    if (row >= int64_t(Z) * S) return;
-    const int lane = threadIdx.x & 63;
-    const int i = int(row % S);
-    const float* s = sc + row * S;
-    float m = -INFINITY;
-    for (int j = lane; j <= i; j += 64) m = fmaxf(m, s[j]);
-    m = wave_max(m);
-    float sum = 0.f;
-    for (int j = lane; j <= i; j += 64) sum += expf(s[j] - m);
-    sum = wave_sum(sum);
-    uint16_t* p = P + row * S;
-    for (int j = lane; j < S; j += 64) p[j] = (j <= i) ? f32_to_bf16_bits(expf(s[j] - m) / sum) : uint16_t(0);
-}
-// dS = P * (dP - sum_j P dP), zeros above the diagonal.
-__global__ __launch_bounds__(256) void k_attn_softmax_bwd(const uint16_t* __restrict__ P, const float* __restrict__ dP,
-                                                          int Z, int S, uint16_t* __restrict__ dS) {
-    const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    if (row >= int64_t(Z) * S) return;
-    const int lane = threadIdx.x & 63;
-    const int i = int(row % S);
-    const uint16_t* p = P + row * S;
-    const float* d = dP + row * S;
-    float D = 0.f;
-    for (int j = lane; j <= i; j += 64) D += bf16_bits_to_f32(p[j]) * d[j];
-    D = wave_sum(D);
-    uint16_t* o = dS + row * S;
-    for (int j = lane; j < S; j += 64)
-        o[j] = (j <= i) ? f32_to_bf16_bits(bf16_bits_to_f32(p[j]) * (d[j] - D)) : uint16_t(0);
-}
-void launch_attn_softmax_fwd(const float* scores, int Z, int S, uint16_t* P, hipStream_t s) {
-    const int64_t rows = int64_t(Z) * S;
-    ProfScope prof("attn_softmax_fwd", 5.0 * Z * (S * (S + 1.0) / 2), Z * (4.0 * (S * (S + 1.0) / 2) + 2.0 * S * S), s);
-    hipLaunchKernelGGL(k_attn_softmax_fwd, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, scores, Z, S, P);
-    check_launch("attn_softmax_fwd");
-}
-void launch_attn_softmax_bwd(const uint16_t* P, const float* dP, int Z, int S, uint16_t* dS, hipStream_t s) {
-    const int64_t rows = int64_t(Z) * S;
-    ProfScope prof("attn_softmax_bwd", 4.0 * Z * (S * (S + 1.0) / 2), Z * (6.0 * (S * (S + 1.0) / 2) + 2.0 * S * S), s);
-    hipLaunchKernelGGL(k_attn_softmax_bwd, dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, P, dP, Z, S, dS);
-    check_launch("attn_softmax_bwd");
-}
-
 // Per-query-head gradients dh [B*nH, S, hd] -> per-KV-head sums written as bf16
 // into out[(b*S + t)*ldo + col0 + kvh*hd + d]; group members summed in order.
 __global__ void k_gqa_reduce(const float* __restrict__ dh, int B, int nH, int nKV, int S, int hd,

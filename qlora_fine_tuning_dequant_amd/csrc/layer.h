@@ -22,17 +22,17 @@ struct BlobPtrs {
 };
 
 // Every intermediate of one layer's forward and backward (bf16 activations,
-// fp32 residual-stream values, fp32 attention scores, LoRA staging, split-K
+// fp32 residual-stream values, attention log-sum-exp, LoRA staging, split-K
 // scratch). Carved from the caller's workspace.
 struct LayerWs {
     uint16_t *n1, *qkv, *oattn, *n2, *gu, *act;
-    float *h1, *rstd1, *rstd2, *scores;
-    uint16_t* P;
+    float *h1, *rstd1, *rstd2;
+    float *lse, *Dq;  // [B, nH, S] attention log-sum-exp and sum_d dO o
     uint16_t *u_qkv, *u_o, *u_gu, *u_d;
     uint16_t *A_qkv, *B_qkv, *A_o, *B_o, *A_gu, *B_gu, *A_d, *B_d;
     float* rope_cs;
     float* partial;
-    uint16_t *dy16, *dact, *dgu, *doattn, *dqkv, *dS;
+    uint16_t *dy16, *dact, *dgu, *doattn, *dqkv;
     uint16_t *du_d, *du_gu, *du_o, *du_qkv;
     float *dn2, *dh1, *dKh, *dVh, *dn1;
 };

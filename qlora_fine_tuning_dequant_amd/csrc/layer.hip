@@ -103,7 +103,7 @@ BlobPtrs blob_ptrs(const qlx_dims& d, const void* blob) {
 LayerWs carve_layer(Carver& c, const LayerGeom& g) {
     LayerWs w;
     const size_t T = size_t(g.T), H = size_t(g.H), r = size_t(g.r);
-    const size_t Z = size_t(g.B) * g.nH, SS = size_t(g.S) * g.S;
+    const size_t Z = size_t(g.B) * g.nH;
     w.n1 = c.take<uint16_t>(T * H);
     w.qkv = c.take<uint16_t>(T * g.nqkv);
     w.oattn = c.take<uint16_t>(T * g.qdim);
@@ -113,8 +113,8 @@ LayerWs carve_layer(Carver& c, const LayerGeom& g) {
     w.h1 = c.take<float>(T * H);
     w.rstd1 = c.take<float>(T);
     w.rstd2 = c.take<float>(T);
-    w.scores = c.take<float>(Z * SS);
-    w.P = c.take<uint16_t>(Z * SS);
+    w.lse = c.take<float>(Z * g.S);
+    w.Dq = c.take<float>(Z * g.S);
     w.u_qkv = c.take<uint16_t>(T * 3 * r);
     w.u_o = c.take<uint16_t>(T * r);
     w.u_gu = c.take<uint16_t>(T * 2 * r);
@@ -135,7 +135,6 @@ LayerWs carve_layer(Carver& c, const LayerGeom& g) {
     w.dgu = c.take<uint16_t>(T * 2 * g.I);
     w.doattn = c.take<uint16_t>(T * g.qdim);
     w.dqkv = c.take<uint16_t>(T * g.nqkv);
-    w.dS = c.take<uint16_t>(Z * SS);
     w.du_d = c.take<uint16_t>(T * r);
     w.du_gu = c.take<uint16_t>(T * 2 * r);
     w.du_o = c.take<uint16_t>(T * r);
@@ -190,6 +189,31 @@ static void out_f32(GemmParams& p, float* C, int64_t ldc) {
     p.c_type = C_F32;
 }
 
+static AttnArgs attn_args(const LayerGeom& g, LayerWs& w) {
+    AttnArgs a;
+    a.qkv = w.qkv;
+    a.ld = g.nqkv;
+    a.B = g.B;
+    a.S = g.S;
+    a.nH = g.nH;
+    a.nKV = g.nKV;
+    a.hd = g.hd;
+    a.qdim = g.qdim;
+    a.kvdim = g.kvdim;
+    a.scale = 1.0f / sqrtf(float(g.hd));
+    a.o = w.oattn;
+    a.ldo = g.qdim;
+    a.lse = w.lse;
+    a.dO = w.doattn;
+    a.O = w.oattn;
+    a.Dq = w.Dq;
+    a.dKh = w.dKh;
+    a.dVh = w.dVh;
+    a.dqkv = w.dqkv;
+    a.lddq = g.nqkv;
+    return a;
+}
+
 void stage_lora(const LayerGeom& g, const qlx_lora* lora, LayerWs& w, hipStream_t s) {
     const int r = g.r;
     LoraSeg qkv[3] = {{lora->A[0], lora->B[0], g.qdim}, {lora->A[1], lora->B[1], g.kvdim},
@@ -235,42 +259,7 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
     }
     launch_rope(w.qkv, g.nqkv, T, g.S, 0, g.nH, g.hd, w.rope_cs, 0, s);
     launch_rope(w.qkv, g.nqkv, T, g.S, g.qdim, g.nKV, g.hd, w.rope_cs, 0, s);
-    const int S = g.S, grp = g.nH / g.nKV;
-    const float scale = 1.0f / sqrtf(float(g.hd));
-    {  // scores = scale * q k^T, causal tiles only
-        GemmParams p = dense_gemm(S, S, g.hd, w.qkv, g.nqkv, w.qkv + g.qdim, g.nqkv);
-        p.batch = g.B * g.nH;
-        p.zdiv = g.nH;
-        p.a_so = int64_t(S) * g.nqkv;
-        p.a_si = g.hd;
-        p.b_so = int64_t(S) * g.nqkv;
-        p.b_si = g.hd;
-        p.b_grp = grp;
-        out_f32(p, w.scores, S);
-        p.c_so = int64_t(g.nH) * S * S;
-        p.c_si = int64_t(S) * S;
-        p.alpha = scale;
-        p.causal = CAUSAL_SKIP_UPPER;
-        p.tag = "gemm_attn_qk";
-        gemm(p, A_ROW, B_DENSE_NT, TE_BF16, nullptr, s);
-    }
-    launch_attn_softmax_fwd(w.scores, g.B * g.nH, S, w.P, s);
-    {  // o = P v
-        GemmParams p = dense_gemm(S, g.hd, S, w.P, S, w.qkv + g.qdim + g.kvdim, g.nqkv);
-        p.batch = g.B * g.nH;
-        p.zdiv = g.nH;
-        p.a_so = int64_t(g.nH) * S * S;
-        p.a_si = int64_t(S) * S;
-        p.b_so = int64_t(S) * g.nqkv;
-        p.b_si = g.hd;
-        p.b_grp = grp;
-        out_bf16(p, w.oattn, g.qdim);
-        p.c_so = int64_t(S) * g.qdim;
-        p.c_si = g.hd;
-        p.causal = CAUSAL_K_LE_M;
-        p.tag = "gemm_attn_pv";
-        gemm(p, A_ROW, B_DENSE_NN, TE_BF16, nullptr, s);
-    }
+    launch_flash_fwd(attn_args(g, w), s);
     if (L) {
         GemmParams pu = dense_gemm(T, r, g.qdim, w.oattn, g.qdim, w.A_o, g.qdim);
         out_bf16(pu, w.u_o, r);
@@ -359,8 +348,7 @@ static void grad_A(const LayerGeom& g, const uint16_t* du, int nseg, const uint1
 
 void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora, const float* h_in,
                     const float* dh_out, float* dh_in, const qlx_lora_grad* grads, LayerWs& w, hipStream_t s) {
-    const int T = g.T, H = g.H, r = g.r, S = g.S, grp = g.nH / g.nKV;
-    const float scale = 1.0f / sqrtf(float(g.hd));
+    const int T = g.T, H = g.H, r = g.r, S = g.S;
     layer_forward(g, wt, lora, false, h_in, nullptr, w, s);
 
     // ---- down projection: out = h1 + down(act)
@@ -436,73 +424,8 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
         grad_A(g, w.du_o, 1, w.oattn, g.qdim, dA, w, s);
     }
 
-    // ---- attention
-    const int Z = g.B * g.nH;
-    {  // dV_h = P^T dO (keys >= ... causal: query >= key)
-        GemmParams p = dense_gemm(S, g.hd, S, w.P, S, w.doattn, g.qdim);
-        p.batch = Z;
-        p.zdiv = g.nH;
-        p.a_so = int64_t(g.nH) * S * S;
-        p.a_si = int64_t(S) * S;
-        p.b_so = int64_t(S) * g.qdim;
-        p.b_si = g.hd;
-        out_f32(p, w.dVh, g.hd);
-        p.c_so = int64_t(g.nH) * S * g.hd;
-        p.c_si = int64_t(S) * g.hd;
-        p.causal = CAUSAL_K_GE_M;
-        p.tag = "gemm_attn_dv";
-        gemm(p, A_TRANS, B_DENSE_NN, TE_BF16, nullptr, s);
-    }
-    {  // dP = dO v^T (into the scores buffer)
-        GemmParams p = dense_gemm(S, S, g.hd, w.doattn, g.qdim, w.qkv + g.qdim + g.kvdim, g.nqkv);
-        p.batch = Z;
-        p.zdiv = g.nH;
-        p.a_so = int64_t(S) * g.qdim;
-        p.a_si = g.hd;
-        p.b_so = int64_t(S) * g.nqkv;
-        p.b_si = g.hd;
-        p.b_grp = grp;
-        out_f32(p, w.scores, S);
-        p.c_so = int64_t(g.nH) * S * S;
-        p.c_si = int64_t(S) * S;
-        p.causal = CAUSAL_SKIP_UPPER;
-        p.tag = "gemm_attn_dp";
-        gemm(p, A_ROW, B_DENSE_NT, TE_BF16, nullptr, s);
-    }
-    launch_attn_softmax_bwd(w.P, w.scores, Z, S, w.dS, s);
-    {  // dq = scale dS k  -> dqkv q columns
-        GemmParams p = dense_gemm(S, g.hd, S, w.dS, S, w.qkv + g.qdim, g.nqkv);
-        p.batch = Z;
-        p.zdiv = g.nH;
-        p.a_so = int64_t(g.nH) * S * S;
-        p.a_si = int64_t(S) * S;
-        p.b_so = int64_t(S) * g.nqkv;
-        p.b_si = g.hd;
-        p.b_grp = grp;
-        out_bf16(p, w.dqkv, g.nqkv);
-        p.c_so = int64_t(S) * g.nqkv;
-        p.c_si = g.hd;
-        p.alpha = scale;
-        p.causal = CAUSAL_K_LE_M;
-        p.tag = "gemm_attn_dq";
-        gemm(p, A_ROW, B_DENSE_NN, TE_BF16, nullptr, s);
-    }
-    {  // dK_h = scale dS^T q
-        GemmParams p = dense_gemm(S, g.hd, S, w.dS, S, w.qkv, g.nqkv);
-        p.batch = Z;
-        p.zdiv = g.nH;
-        p.a_so = int64_t(g.nH) * S * S;
-        p.a_si = int64_t(S) * S;
-        p.b_so = int64_t(S) * g.nqkv;
-        p.b_si = g.hd;
-        out_f32(p, w.dKh, g.hd);
-        p.c_so = int64_t(g.nH) * S * g.hd;
-        p.c_si = int64_t(S) * g.hd;
-        p.alpha = scale;
-        p.causal = CAUSAL_K_GE_M;
-        p.tag = "gemm_attn_dk";
-        gemm(p, A_TRANS, B_DENSE_NN, TE_BF16, nullptr, s);
-    }
+    // ---- attention: dq into dqkv, per-head fp32 dK, dV summed over each group below
+    launch_flash_bwd(attn_args(g, w), s);
     launch_gqa_reduce(w.dKh, g.B, g.nH, g.nKV, S, g.hd, w.dqkv, g.nqkv, g.qdim, s);
     launch_gqa_reduce(w.dVh, g.B, g.nH, g.nKV, S, g.hd, w.dqkv, g.nqkv, g.qdim + g.kvdim, s);
     launch_rope(w.dqkv, g.nqkv, T, S, 0, g.nH, g.hd, w.rope_cs, 1, s);

@@ -172,6 +172,26 @@ void launch_swiglu_bwd(const uint16_t* dact, const uint16_t* gu, int T, int I, u
 void launch_embed(const int32_t* tok, const uint16_t* E, int T, int H, int V, float* h, hipStream_t s);
 void launch_f32_to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s);
 void launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
+
+// Flash-style causal GQA attention over q|k|v packed per token row.
+struct AttnArgs {
+    const uint16_t* qkv = nullptr;  // [B*S, ld]: q at column 0, k at qdim, v at qdim + kvdim (bf16)
+    int64_t ld = 0;
+    int B = 0, S = 0, nH = 0, nKV = 0, hd = 0;
+    int64_t qdim = 0, kvdim = 0;
+    float scale = 1.f;
+    uint16_t* o = nullptr;  // [B*S, ldo] attention output (forward)
+    int64_t ldo = 0;        // also the row stride of dO and O (backward)
+    float* lse = nullptr;   // [B, nH, S] natural log-sum-exp of the scaled scores
+    const uint16_t* dO = nullptr;
+    const uint16_t* O = nullptr;
+    float* Dq = nullptr;                      // [B, nH, S] sum_d dO o
+    float *dKh = nullptr, *dVh = nullptr;     // [B, nH, S, hd] fp32 per query head
+    uint16_t* dqkv = nullptr;                 // dq written at column 0 (bf16)
+    int64_t lddq = 0;
+};
+void launch_flash_fwd(const AttnArgs& a, hipStream_t s);
+void launch_flash_bwd(const AttnArgs& a, hipStream_t s);
 void launch_spin(int delay_us, hipStream_t s);
 struct LoraSeg {
     const float* A;  // [r, in]
@@ -180,8 +200,6 @@ struct LoraSeg {
 };
 void launch_lora_pack(const LoraSeg* segs, int nseg, int r, int in_f, float scale, uint16_t* Acat,
                       uint16_t* Bbd, hipStream_t s);
-void launch_attn_softmax_fwd(const float* scores, int Z, int S, uint16_t* P, hipStream_t s);
-void launch_attn_softmax_bwd(const uint16_t* P, const float* dP, int Z, int S, uint16_t* dS, hipStream_t s);
 void launch_gqa_reduce(const float* dh, int B, int nH, int nKV, int S, int hd, uint16_t* out, int64_t ldo,
                        int col0, hipStream_t s);
 // Cross-entropy pieces over logits [T, V] (fp32).
