@@ -256,9 +256,8 @@ struct LoraSegs {
     int out[3];
     int nseg;
 };
-__global__ void k_lora_pack(const LoraSegs sg, int r, int in_f, float scale, uint16_t* __restrict__ Acat,
-                            uint16_t* __restrict__ Bbd, int64_t nA, int64_t nB, int ntot) {
-    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+__device__ inline void lora_pack_one(const LoraSegs& sg, int r, int in_f, float scale, uint16_t* __restrict__ Acat,
+                                     uint16_t* __restrict__ Bbd, int64_t nA, int64_t nB, int64_t idx) {
     if (idx < nA) {
         const int64_t row = idx / in_f, k = idx % in_f;
         const int p = int(row / r), i = int(row % r);
@@ -273,6 +272,23 @@ __global__ void k_lora_pack(const LoraSegs sg, int r, int in_f, float scale, uin
     int off = 0, p = 0;
     while (p < sg.nseg - 1 && n >= off + sg.out[p]) off += sg.out[p++];
     Bbd[jdx] = (p == q) ? f32_to_bf16_bits(scale * sg.B[p][int64_t(n - off) * r + j]) : uint16_t(0);
+}
+__global__ void k_lora_pack(const LoraSegs sg, int r, int in_f, float scale, uint16_t* __restrict__ Acat,
+                            uint16_t* __restrict__ Bbd, int64_t nA, int64_t nB, int ntot) {
+    lora_pack_one(sg, r, in_f, scale, Acat, Bbd, nA, nB, int64_t(blockIdx.x) * blockDim.x + threadIdx.x);
+}
+struct LoraPackArgs {
+    LoraSegs sg[4];
+    int in_f[4];
+    uint16_t* Acat[4];
+    uint16_t* Bbd[4];
+    int64_t nA[4], nB[4];
+};
+// grid row y packs job y; rows past a job's size return at once
+__global__ void k_lora_pack_jobs(const LoraPackArgs a, int r, float scale) {
+    const int y = blockIdx.y;
+    lora_pack_one(a.sg[y], r, a.in_f[y], scale, a.Acat[y], a.Bbd[y], a.nA[y], a.nB[y],
+                  int64_t(blockIdx.x) * blockDim.x + threadIdx.x);
 }
 void launch_lora_pack(const LoraSeg* segs, int nseg, int r, int in_f, float scale, uint16_t* Acat, uint16_t* Bbd,
                       hipStream_t s) {
@@ -290,6 +306,37 @@ void launch_lora_pack(const LoraSeg* segs, int nseg, int r, int in_f, float scal
     ProfScope prof("lora_pack", double(nB), 4.0 * nA + 2.0 * nA + 2.0 * nB + 4.0 * (nB / nseg), s);
     hipLaunchKernelGGL(k_lora_pack, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, sg, r, in_f, scale, Acat, Bbd,
                        nA, nB, ntot);
+    check_launch("lora_pack");
+}
+
+void launch_lora_pack_jobs(const LoraPackJob* jobs, int njobs, int r, float scale, hipStream_t s) {
+    QLX_REQUIRE(njobs >= 1 && njobs <= 4, QLX_EINVAL, "lora pack: 1..4 jobs");
+    LoraPackArgs a{};
+    int64_t nmax = 0;
+    double bytes = 0, elems = 0;
+    for (int y = 0; y < njobs; ++y) {
+        const LoraPackJob& jb = jobs[y];
+        int ntot = 0;
+        for (int p = 0; p < jb.nseg; ++p) {
+            a.sg[y].A[p] = jb.segs[p].A;
+            a.sg[y].B[p] = jb.segs[p].B;
+            a.sg[y].out[p] = jb.segs[p].out_p;
+            ntot += jb.segs[p].out_p;
+        }
+        a.sg[y].nseg = jb.nseg;
+        a.in_f[y] = jb.in_f;
+        a.Acat[y] = jb.Acat;
+        a.Bbd[y] = jb.Bbd;
+        a.nA[y] = int64_t(jb.nseg) * r * jb.in_f;
+        a.nB[y] = int64_t(ntot) * jb.nseg * r;
+        nmax = std::max(nmax, a.nA[y] + a.nB[y]);
+        bytes += 6.0 * a.nA[y] + 2.0 * a.nB[y] + 4.0 * (a.nB[y] / jb.nseg);
+        elems += double(a.nB[y]);
+    }
+    if (nmax == 0) return;
+    ProfScope prof("lora_pack", elems, bytes, s);
+    hipLaunchKernelGGL(k_lora_pack_jobs, dim3(unsigned((nmax + 255) / 256), unsigned(njobs)), dim3(256), 0, s, a, r,
+                       scale);
     check_launch("lora_pack");
 }
 

@@ -31,6 +31,7 @@ struct LayerWs {
     uint16_t *u_qkv, *u_o, *u_gu, *u_d;
     uint16_t *A_qkv, *B_qkv, *A_o, *B_o, *A_gu, *B_gu, *A_d, *B_d;
     float* rope_cs;
+    bool rope_ready = false;  // host flag: rope_cs holds this geometry's table
     float* partial;
     uint16_t *dy16, *dact, *dgu, *doattn, *dqkv;
     uint16_t *du_d, *du_gu, *du_o, *du_qkv;

@@ -216,15 +216,15 @@ static AttnArgs attn_args(const LayerGeom& g, LayerWs& w) {
 
 void stage_lora(const LayerGeom& g, const qlx_lora* lora, LayerWs& w, hipStream_t s) {
     const int r = g.r;
+    // the layer's four packs (q|k|v, o, gate|up, down) in one launch
     LoraSeg qkv[3] = {{lora->A[0], lora->B[0], g.qdim}, {lora->A[1], lora->B[1], g.kvdim},
                       {lora->A[2], lora->B[2], g.kvdim}};
-    launch_lora_pack(qkv, 3, r, g.H, g.s, w.A_qkv, w.B_qkv, s);
     LoraSeg o[1] = {{lora->A[3], lora->B[3], g.H}};
-    launch_lora_pack(o, 1, r, g.qdim, g.s, w.A_o, w.B_o, s);
     LoraSeg gu[2] = {{lora->A[4], lora->B[4], g.I}, {lora->A[5], lora->B[5], g.I}};
-    launch_lora_pack(gu, 2, r, g.H, g.s, w.A_gu, w.B_gu, s);
     LoraSeg dn[1] = {{lora->A[6], lora->B[6], g.H}};
-    launch_lora_pack(dn, 1, r, g.I, g.s, w.A_d, w.B_d, s);
+    const LoraPackJob jobs[4] = {{qkv, 3, g.H, w.A_qkv, w.B_qkv}, {o, 1, g.qdim, w.A_o, w.B_o},
+                                 {gu, 2, g.H, w.A_gu, w.B_gu}, {dn, 1, g.I, w.A_d, w.B_d}};
+    launch_lora_pack_jobs(jobs, 4, r, g.s, s);
 }
 
 // Forward. h_out == nullptr skips the down projection (the backward does not
@@ -234,7 +234,10 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
     const int T = g.T, H = g.H, r = g.r;
     const bool L = lora != nullptr;
     if (L && !lora_staged) stage_lora(g, lora, w, s);
-    launch_rope_table(g.S, g.hd, g.theta, w.rope_cs, s);
+    if (!w.rope_ready) {  // once per workspace: every layer pass of a step shares the table
+        launch_rope_table(g.S, g.hd, g.theta, w.rope_cs, s);
+        w.rope_ready = true;
+    }
 
     // attention block
     launch_rmsnorm_fwd(h_in, wt.g1, T, H, g.eps, w.n1, 0, w.rstd1, s);

@@ -200,6 +200,13 @@ struct LoraSeg {
 };
 void launch_lora_pack(const LoraSeg* segs, int nseg, int r, int in_f, float scale, uint16_t* Acat,
                       uint16_t* Bbd, hipStream_t s);
+// Several packs in one launch (one per grid row).
+struct LoraPackJob {
+    const LoraSeg* segs;
+    int nseg, in_f;
+    uint16_t *Acat, *Bbd;
+};
+void launch_lora_pack_jobs(const LoraPackJob* jobs, int njobs, int r, float scale, hipStream_t s);
 void launch_gqa_reduce(const float* dh, int B, int nH, int nKV, int S, int hd, uint16_t* out, int64_t ldo,
                        int col0, hipStream_t s);
 // Cross-entropy pieces over logits [T, V] (fp32).
