@@ -354,6 +354,8 @@ struct qlx_ctx {
 
 namespace qlx {
 
+constexpr int kVocabChunk = 16384;  // LM-head backward: dz columns per chunk
+
 struct StepWs {
     char* slot[2];
     float* ckpt;     // (L+1) x [T, H]
@@ -362,8 +364,8 @@ struct StepWs {
     LayerWs lw;
     uint16_t* nf;  // fp16 [T, H]
     float* rstd_f;
-    float* logits;  // [T, V]
-    uint16_t* dz;   // fp16 [T, V]
+    float *ce_pm, *ce_ps;  // [T, V/64] LM-head row partials (max, sum exp)
+    uint16_t* dzc;         // fp16 [T, kVocabChunk] one vocabulary chunk of dz
     float *lse, *picked, *lse_ref, *pk_ref;
     float* dnf;  // [T, H]
     float* dh[2];
@@ -402,8 +404,9 @@ static StepWs carve_step(Carver& c, const qlx_dims& d, int T, int kind, uint64_t
     }
     w.nf = c.take<uint16_t>(Tz * H);
     w.rstd_f = c.take<float>(Tz);
-    w.logits = c.take<float>(Tz * V);
-    w.dz = c.take<uint16_t>(Tz * V);
+    w.ce_pm = c.take<float>(Tz * ((V + 63) / 64));
+    w.ce_ps = c.take<float>(Tz * ((V + 63) / 64));
+    w.dzc = c.take<uint16_t>(Tz * kVocabChunk);
     w.lse = c.take<float>(Tz);
     w.picked = c.take<float>(Tz);
     w.dnf = c.take<float>(Tz * H);
@@ -578,9 +581,17 @@ static void end_step(qlx_ctx* ctx, hipStream_t main) {
     QLX_CHECK_HIP(hipEventRecord(ctx->step_end, main));
 }
 
-// Final RMSNorm (fp16 out) + LM head logits [T, V] (fp32).
-static void head_logits(const qlx_model* m, const float* hL, int T, StepWs& w, float* partial, hipStream_t s) {
+// Fused LM head + cross-entropy. Forward: final RMSNorm (fp16 out), then the
+// head GEMM whose epilogue reduces each row's logits to per-64-column (max,
+// sum exp) partials and picks the target's logit; a row reduce gives lse. The
+// [T, V] logits never exist. Backward: per vocabulary chunk of kVocabChunk
+// columns, the head GEMM again with an epilogue writing fp16 dz = (softmax -
+// onehot) * scale, then dnf += dz_chunk . head_chunk (fp32, chunk order), then
+// RMSNorm backward.
+static void head_stats(const qlx_model* m, const float* hL, int T, const int32_t* tokens, int seq, int start,
+                       float* lse, float* picked, StepWs& w, float* partial, hipStream_t s) {
     const qlx_dims& d = m->dims;
+    const int nb = (d.vocab + 63) / 64;
     launch_rmsnorm_fwd(hL, m->final_norm, T, d.hidden, d.rms_eps, w.nf, 1, w.rstd_f, s);
     GemmParams p;
     p.M = T;
@@ -590,30 +601,64 @@ static void head_logits(const qlx_model* m, const float* hL, int T, StepWs& w, f
     p.lda = d.hidden;
     p.B = m->lm_head_f16;
     p.ldb = d.hidden;
-    p.C = w.logits;
-    p.ldc = d.vocab;
-    p.c_type = C_F32;
+    p.c_type = C_F16;
+    p.ce_mode = 1;
+    p.ce_tokens = tokens;
+    p.ce_seq = seq;
+    p.ce_start = start;
+    p.ce_pm = w.ce_pm;
+    p.ce_ps = w.ce_ps;
+    p.ce_pld = nb;
+    p.ce_picked = picked;
     p.tag = "gemm_head";
     gemm(p, A_ROW, B_DENSE_NT, TE_F16, partial, s);
+    launch_ce_reduce(w.ce_pm, w.ce_ps, nb, T, d.vocab, tokens, seq, start, lse, picked, s);
 }
-// dh = RMSNorm^T( (dz . head) * alpha )
-static void head_backward(const qlx_model* m, const float* hL, int T, float alpha, StepWs& w, float* dh_out,
-                          float* partial, hipStream_t s) {
+// dh = RMSNorm^T( (dz . head) * alpha ), dz = (softmax - onehot) * sc (* gseq per sequence)
+static void head_grad(const qlx_model* m, const float* hL, int T, const int32_t* tokens, int seq, int start,
+                      const float* lse, float sc, const float* gseq, float alpha, StepWs& w, float* dh_out,
+                      float* partial, hipStream_t s) {
     const qlx_dims& d = m->dims;
-    GemmParams p;
-    p.M = T;
-    p.N = d.hidden;
-    p.K = d.vocab;
-    p.A = w.dz;
-    p.lda = d.vocab;
-    p.B = m->lm_head_f16;
-    p.ldb = d.hidden;
-    p.C = w.dnf;
-    p.ldc = d.hidden;
-    p.c_type = C_F32;
-    p.alpha = alpha;
-    p.tag = "gemm_head_dx";
-    gemm(p, A_ROW, B_DENSE_NN, TE_F16, partial, s);
+    for (int c0 = 0; c0 < d.vocab; c0 += kVocabChunk) {
+        const int cw = std::min(kVocabChunk, d.vocab - c0);
+        const uint16_t* head = m->lm_head_f16 + size_t(c0) * d.hidden;
+        GemmParams p;
+        p.M = T;
+        p.N = cw;
+        p.K = d.hidden;
+        p.A = w.nf;
+        p.lda = d.hidden;
+        p.B = head;
+        p.ldb = d.hidden;
+        p.C = w.dzc;
+        p.ldc = kVocabChunk;
+        p.c_type = C_F16;
+        p.ce_mode = 2;
+        p.ce_tokens = tokens;
+        p.ce_seq = seq;
+        p.ce_start = start;
+        p.ce_col0 = c0;
+        p.ce_lse = lse;
+        p.ce_sc = sc;
+        p.ce_gseq = gseq;
+        p.tag = "gemm_head_dz";
+        gemm(p, A_ROW, B_DENSE_NT, TE_F16, partial, s);
+        GemmParams q;
+        q.M = T;
+        q.N = d.hidden;
+        q.K = cw;
+        q.A = w.dzc;
+        q.lda = kVocabChunk;
+        q.B = head;
+        q.ldb = d.hidden;
+        q.C = w.dnf;
+        q.ldc = d.hidden;
+        q.c_type = C_F32;
+        q.alpha = alpha;
+        q.accumulate = c0 > 0;
+        q.tag = "gemm_head_dx";
+        gemm(q, A_ROW, B_DENSE_NN, TE_F16, partial, s);
+    }
     launch_rmsnorm_bwd(w.dnf, hL, m->final_norm, w.rstd_f, nullptr, T, d.hidden, dh_out, s);
 }
 
@@ -782,12 +827,10 @@ int stream_step_sft(qlx_ctx* ctx, const qlx_model* m, const int32_t* tokens, int
             st.release(i);
         }
         const float* hL = w.ckpt + size_t(L) * TH;
-        head_logits(m, hL, T, w, w.lw.partial, s);
-        launch_ce_stats(w.logits, T, d.vocab, tokens, seq, 0, w.lse, w.picked, s);
+        head_stats(m, hL, T, tokens, seq, 0, w.lse, w.picked, w, w.lw.partial, s);
         launch_sft_loss(w.lse, w.picked, T, seq, loss, s);
-        launch_ce_grad(w.logits, w.lse, T, d.vocab, tokens, seq, 0, 0, kDzScale, nullptr, w.dz, s);
         const float alpha = 1.0f / (kDzScale * float(batch) * float(seq - 1));
-        head_backward(m, hL, T, alpha, w, w.dh[0], w.lw.partial, s);
+        head_grad(m, hL, T, tokens, seq, 0, w.lse, kDzScale, nullptr, alpha, w, w.dh[0], w.lw.partial, s);
         ctx->stats.layer_passes = 2 * L;
         backward_layers(st, m, g, w, w.dh[0], grads, s);
         end_step(ctx, s);
@@ -882,19 +925,15 @@ static void pref_step(qlx_ctx* ctx, const qlx_model* m, const qlx_pref_cfg& cfg,
     }
     const int start = prompt_len - 1;
     if (need_ref) {  // reference log-probs
-        head_logits(m, extra[0].cur, T, w, w.lw.partial, s);
-        launch_ce_stats(w.logits, T, d.vocab, w.toks, seq, start, w.lse_ref, w.pk_ref, s);
+        head_stats(m, extra[0].cur, T, w.toks, seq, start, w.lse_ref, w.pk_ref, w, w.lw.partial, s);
     }
     if (kto) {  // mismatched pairs: reference, then policy
-        head_logits(m, extra[1].cur, T, w, w.lw.partial, s);
-        launch_ce_stats(w.logits, T, d.vocab, w.kl_toks, seq, start, w.kl_lse_r, w.kl_pk_r, s);
-        head_logits(m, extra[2].cur, T, w, w.lw.partial, s);
-        launch_ce_stats(w.logits, T, d.vocab, w.kl_toks, seq, start, w.kl_lse, w.kl_pk, s);
+        head_stats(m, extra[1].cur, T, w.kl_toks, seq, start, w.kl_lse_r, w.kl_pk_r, w, w.lw.partial, s);
+        head_stats(m, extra[2].cur, T, w.kl_toks, seq, start, w.kl_lse, w.kl_pk, w, w.lw.partial, s);
     }
     // policy log-probs, loss, and dL/dlp
     const float* hL = w.ckpt + size_t(L) * TH;
-    head_logits(m, hL, T, w, w.lw.partial, s);
-    launch_ce_stats(w.logits, T, d.vocab, w.toks, seq, start, w.lse, w.picked, s);
+    head_stats(m, hL, T, w.toks, seq, start, w.lse, w.picked, w, w.lw.partial, s);
     PrefLossArgs la{};
     la.lse_p = w.lse;
     la.pk_p = w.picked;
@@ -917,8 +956,7 @@ static void pref_step(qlx_ctx* ctx, const qlx_model* m, const qlx_pref_cfg& cfg,
     la.gseq = w.gseq;
     launch_pref_loss(la, s);
     // dz = g_seq (onehot - softmax) = (softmax - onehot) * (-g_seq)
-    launch_ce_grad(w.logits, w.lse, T, d.vocab, w.toks, seq, start, 1, -kDzScale, w.gseq, w.dz, s);
-    head_backward(m, hL, T, 1.0f / kDzScale, w, w.dh[0], w.lw.partial, s);
+    head_grad(m, hL, T, w.toks, seq, start, w.lse, -kDzScale, w.gseq, 1.0f / kDzScale, w, w.dh[0], w.lw.partial, s);
     ctx->stats.layer_passes = int64_t(2 + extra.size()) * L;
     backward_layers(st, m, g, w, w.dh[0], grads, s);
     end_step(ctx, s);

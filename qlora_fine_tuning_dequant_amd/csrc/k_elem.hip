@@ -373,63 +373,43 @@ __device__ inline int row_target(const int32_t* tokens, int t, int seq, int star
     return tokens[t + 1];
 }
 
-__global__ __launch_bounds__(256) void k_ce_stats(const float* __restrict__ z, int T, int V,
-                                                  const int32_t* __restrict__ tokens, int seq, int start,
-                                                  float* __restrict__ lse, float* __restrict__ picked) {
-    __shared__ float red[4];
-    const int t = blockIdx.x;
+// lse of each row from the LM-head epilogue's per-64-column partials
+// (max m_b, sum s_b of exp(z - m_b)): m = max_b m_b, lse = m + log(sum_b s_b
+// exp(m_b - m)), one wavefront per row, blocks split over lanes in a fixed
+// pattern and joined in a fixed tree. Rows without a target get lse =
+// picked = 0; a target outside the vocabulary gives NaN.
+__global__ __launch_bounds__(256) void k_ce_reduce(const float* __restrict__ pm, const float* __restrict__ ps, int nb,
+                                                   int T, int V, const int32_t* __restrict__ tokens, int seq, int start,
+                                                   float* __restrict__ lse, float* __restrict__ picked) {
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (t >= T) return;
     const int tgt = row_target(tokens, t, seq, start);
-    if (tgt < 0) {  // uniform across the workgroup
-        if (threadIdx.x == 0) {
-            lse[t] = 0.f;
-            picked[t] = 0.f;
-        }
+    if (tgt < 0) {
+        if (lane == 0) lse[t] = picked[t] = 0.f;
         return;
     }
-    const float* zr = z + int64_t(t) * V;
+    const float* m_ = pm + int64_t(t) * nb;
+    const float* s_ = ps + int64_t(t) * nb;
     float m = -INFINITY;
-    for (int j = threadIdx.x; j < V; j += 256) m = fmaxf(m, zr[j]);
-    m = block_max256(m, red);
+    for (int b = lane; b < nb; b += 64) m = fmaxf(m, m_[b]);
+    m = wave_max(m);
     float sum = 0.f;
-    for (int j = threadIdx.x; j < V; j += 256) sum += expf(zr[j] - m);
-    sum = block_sum256(sum, red);
-    if (threadIdx.x == 0) {
+    for (int b = lane; b < nb; b += 64)
+        if (m_[b] > -INFINITY) sum += s_[b] * expf(m_[b] - m);
+    sum = wave_sum(sum);
+    if (lane == 0) {
         const bool ok = tgt < V;
         lse[t] = ok ? m + logf(sum) : __int_as_float(0x7fc00000);
-        picked[t] = ok ? zr[tgt] : __int_as_float(0x7fc00000);
+        if (!ok) picked[t] = __int_as_float(0x7fc00000);
     }
 }
-
-__global__ __launch_bounds__(256) void k_ce_grad(const float* __restrict__ z, const float* __restrict__ lse, int T,
-                                                 int V, const int32_t* __restrict__ tokens, int seq, int start,
-                                                 int mode, float sc, const float* __restrict__ gseq,
-                                                 uint16_t* __restrict__ dz) {
-    const int t = blockIdx.y;
-    const int j = blockIdx.x * 256 + threadIdx.x;
-    if (j >= V) return;
-    const int tgt = row_target(tokens, t, seq, start);
-    uint16_t* o = dz + int64_t(t) * V;
-    if (tgt < 0) {
-        o[j] = 0;
-        return;
-    }
-    const float scale = (mode == 1) ? sc * gseq[t / seq] : sc;
-    const float p = expf(z[int64_t(t) * V + j] - lse[t]);
-    o[j] = f32_to_f16_bits((p - (j == tgt ? 1.f : 0.f)) * scale);
-}
-
-void launch_ce_stats(const float* logits, int T, int V, const int32_t* tokens, int seq, int start, float* lse,
-                     float* picked, hipStream_t s) {
-    ProfScope prof("ce_stats", 3.0 * T * V, 4.0 * T * V, s);
-    hipLaunchKernelGGL(k_ce_stats, dim3(T), dim3(256), 0, s, logits, T, V, tokens, seq, start, lse, picked);
-    check_launch("ce_stats");
-}
-void launch_ce_grad(const float* logits, const float* lse, int T, int V, const int32_t* tokens, int seq, int start,
-                    int mode, float sc, const float* gseq, uint16_t* dz, hipStream_t s) {
-    ProfScope prof("ce_grad", 4.0 * T * V, 6.0 * T * V, s);
-    hipLaunchKernelGGL(k_ce_grad, dim3((V + 255) / 256, T), dim3(256), 0, s, logits, lse, T, V, tokens, seq, start,
-                       mode, sc, gseq, dz);
-    check_launch("ce_grad");
+void launch_ce_reduce(const float* pm, const float* ps, int nb, int T, int V, const int32_t* tokens, int seq, int start,
+                      float* lse, float* picked, hipStream_t s) {
+    if (T <= 0) return;
+    ProfScope prof("ce_reduce", 3.0 * T * nb, 8.0 * T * nb, s);
+    hipLaunchKernelGGL(k_ce_reduce, dim3(unsigned((T + 3) / 4)), dim3(256), 0, s, pm, ps, nb, T, V, tokens, seq, start,
+                       lse, picked);
+    check_launch("ce_reduce");
 }
 
 // SFT loss = sum over target rows of (lse - picked) / (#rows with a target).

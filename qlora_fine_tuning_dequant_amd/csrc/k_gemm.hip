@@ -373,6 +373,67 @@ using BLoader = typename std::conditional<
                               typename std::conditional<BKIND == B_DENSE_NT, RowLoader<R, NT>,
                                                         TransLoader<R, NT>>::type>::type>::type;
 
+// LM-head cross-entropy epilogues. The lane holds 16 consecutive columns
+// col0.. of one row; the 4 lanes of a row are lanes 4k..4k+3 of the
+// wavefront (one 64-column block). Mode 1: the block's max and sum of
+// exp(z - max) (joined over the 4 lanes), and the target's logit. Mode 2: fp16
+// dz = (exp(z - lse) - onehot) * scale.
+__device__ inline int ce_target(const GemmParams& p, int t) {
+    const int s = t % p.ce_seq;
+    if (s < p.ce_start || s >= p.ce_seq - 1) return -1;
+    return p.ce_tokens[t + 1];
+}
+__device__ void ce_epilogue(const GemmParams& p, int row, int col0, const float* src) {
+    const bool rok = row < p.M;
+    const int tgt = rok ? ce_target(p, row) : -1;
+    const int v0 = p.ce_col0 + col0;  // vocab index of src[0]
+    if (p.ce_mode == 1) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+            if (col0 + c < p.N) mx = fmaxf(mx, src[c]);
+        float sm = 0.f;
+        if (mx > -INFINITY) {
+#pragma unroll
+            for (int c = 0; c < 16; ++c)
+                if (col0 + c < p.N) sm += expf(src[c] - mx);
+        }
+#pragma unroll
+        for (int off = 1; off <= 2; off <<= 1) {
+            const float om = __shfl_xor(mx, off, 64), os = __shfl_xor(sm, off, 64);
+            const float nm = fmaxf(mx, om);
+            sm = (nm == -INFINITY) ? 0.f : sm * expf(mx - nm) + os * expf(om - nm);
+            mx = nm;
+        }
+        if (rok && (threadIdx.x & 3) == 0 && col0 < p.N) {
+            const int64_t o = int64_t(row) * p.ce_pld + v0 / 64;
+            p.ce_pm[o] = mx;
+            p.ce_ps[o] = sm;
+        }
+        if (rok && tgt >= v0 && tgt < v0 + 16 && tgt - p.ce_col0 < p.N) p.ce_picked[row] = src[tgt - v0];
+        return;
+    }
+    if (!rok) return;
+    const float scale = p.ce_sc * (p.ce_gseq ? p.ce_gseq[row / p.ce_seq] : 1.f);
+    const float lse = tgt >= 0 ? p.ce_lse[row] : 0.f;
+    float v[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+        v[c] = tgt < 0 ? 0.f : (expf(src[c] - lse) - (v0 + c == tgt ? 1.f : 0.f)) * scale;
+    uint16_t* dst = static_cast<uint16_t*>(p.C) + int64_t(row) * p.ldc + col0;
+    if (col0 + 16 <= p.N && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+        uint32_t w[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            w[k] = uint32_t(f32_to_f16_bits(v[2 * k])) | (uint32_t(f32_to_f16_bits(v[2 * k + 1])) << 16);
+        reinterpret_cast<uint4*>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        reinterpret_cast<uint4*>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    } else {
+        for (int c = 0; c < 16; ++c)
+            if (col0 + c < p.N) dst[c] = f32_to_f16_bits(v[c]);
+    }
+}
+
 template <int AK, int BKIND, int TE, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm(const GemmParams p) {
     constexpr int NT = (BM / WM) * (BN / WN) * 64;
@@ -481,7 +542,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm(const GemmP
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         const int row = m0 + wm * WM + i * 16 + srow;
         const int col0 = n0 + wn * WN + scol;
-        if (row < p.M) {
+        if (WN == 64 && p.ce_mode) {  // every lane: the row's 4 lanes combine
+            ce_epilogue(p, row, col0, stage + srow * (WN + 4) + scol);
+        } else if (row < p.M) {
             const float* src = stage + srow * (WN + 4) + scol;
             if (p.splits > 1) {
                 float* dst = p.partial + (int64_t(split) * p.M + row) * p.N + col0;
@@ -1092,6 +1155,10 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
     const bool nf4 = (bkind == B_NF4_NT || bkind == B_NF4_NN);
     QLX_REQUIRE(!(p.K2 > 0 && !nf4), QLX_EINVAL, "gemm: the LoRA slab rides only on NF4 GEMMs");
     QLX_REQUIRE(!(te == TE_F16 && nf4), QLX_EINVAL, "gemm: NF4 operands are bf16");
+    QLX_REQUIRE(!p.ce_mode || (te == TE_F16 && akind == A_ROW && bkind == B_DENSE_NT && p.batch == 1 &&
+                               p.causal == CAUSAL_NONE && p.ce_seq > 0),
+                QLX_EINVAL, "gemm: the cross-entropy epilogues take a plain fp16 NT product");
+    if (p.ce_mode) partial_ws = nullptr;  // no split: the epilogue needs whole sums
     // vector-load eligibility (uniform per launch; depends on layout, not data)
     if (akind == A_ROW) p.a_vec = aligned16(p.A) && p.lda % 8 == 0 && p.a_so % 8 == 0 && p.a_si % 8 == 0;
     else p.a_vec = aligned8(p.A) && p.lda % 4 == 0 && p.a_so % 4 == 0 && p.a_si % 4 == 0;
