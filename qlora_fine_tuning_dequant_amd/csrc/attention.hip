@@ -15,6 +15,13 @@
 // P is rounded to bf16 for that product (as the reference path rounds its
 // probabilities); the running sum uses the fp32 values.
 //
+// RoPE (rotate-half, pairs (j, j + hd/2)) is applied to q|k in place by one
+// launch before the forward (rotating while loading would redo each key
+// block's rotation for every query block that stages it). The backward rotates
+// dq back in registers before its store (a lane's dims d and d + hd/2 sit in
+// accumulator tiles dt and dt + hd/32) and dk in the GQA reduce, so dq|dk
+// come out as gradients of the unrotated q|k.
+//
 // Backward (deterministic, no atomics): D_q = sum_d dO o; dK/dV per (key block
 // of 64, query head), each wavefront owning 16 keys and walking the query
 // blocks at or after its own (S = Q K^T here, so each lane holds one KEY and
@@ -78,6 +85,7 @@ __device__ inline uint4 tfrag(const uint16_t* __restrict__ t, int dt, int js, in
     const uint2 hi = *reinterpret_cast<const uint2*>(p + 16);
     return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
+
 }  // namespace
 
 // ------------------------------------------------------------------ forward
@@ -348,11 +356,23 @@ __global__ __launch_bounds__(256) void k_flash_bwd_q(const AttnArgs a) {
         __syncthreads();
     }
     if (!qok) return;
+    // dq of the rotated q, rotated back (the transpose of the rotation):
+    // dq[dt][e] is dim dt*16 + 4g + e, its pair dim in tile dt + HD/32
+    const float2* cs = a.rope + int64_t(q) * (HD / 2);
+#pragma unroll
+    for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float2 c = cs[dt * 16 + g * 4 + e];
+            const float x1 = dq[dt][e] * a.scale, x2 = dq[dt + HD / 32][e] * a.scale;
+            dq[dt][e] = x1 * c.x + x2 * c.y;
+            dq[dt + HD / 32][e] = x2 * c.x - x1 * c.y;
+        }
     uint16_t* dst = a.dqkv + (row0 + q) * a.lddq + int64_t(h) * HD + g * 4;
 #pragma unroll
     for (int dt = 0; dt < HD / 16; ++dt)
-        *reinterpret_cast<uint2*>(dst + dt * 16) = make_uint2(pack_bf16(dq[dt][0] * a.scale, dq[dt][1] * a.scale),
-                                                              pack_bf16(dq[dt][2] * a.scale, dq[dt][3] * a.scale));
+        *reinterpret_cast<uint2*>(dst + dt * 16) =
+            make_uint2(pack_bf16(dq[dt][0], dq[dt][1]), pack_bf16(dq[dt][2], dq[dt][3]));
 }
 
 // ------------------------------------------------------------------ launchers
@@ -362,6 +382,7 @@ static void check_attn(const AttnArgs& a) {
     QLX_REQUIRE(a.ld % 8 == 0 && a.ldo % 8 == 0 && a.qdim % 8 == 0 && a.kvdim % 8 == 0, QLX_EUNSUPPORTED,
                 "attention: row strides must be multiples of 8 elements");
     QLX_REQUIRE(a.nH <= 65535 && a.B <= 65535, QLX_EUNSUPPORTED, "attention: grid too large");
+    QLX_REQUIRE(a.rope != nullptr, QLX_EINVAL, "attention: RoPE table is NULL (dq is rotated back)");
 }
 
 void launch_flash_fwd(const AttnArgs& a, hipStream_t s) {

@@ -111,10 +111,9 @@ __global__ void k_rope_table(int seq, int hd, double theta, float2* cs) {
     cs[idx] = make_float2(float(cos(ang)), float(sin(ang)));
 }
 
-// Rotate pairs (j, j + hd/2) of every head in columns [col0, col0 + nheads*hd)
-// of a bf16 [T, ld] buffer; row t has position t % seq. inverse = transpose.
+// RoPE, forward rotation of each (j, j + hd/2) pair; one thread per pair.
 __global__ void k_rope(uint16_t* __restrict__ buf, int64_t ld, int T, int seq, int col0, int nheads, int hd,
-                       const float2* __restrict__ cs, int inverse) {
+                       const float2* __restrict__ cs) {
     const int half = hd / 2;
     const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t total = int64_t(T) * nheads * half;
@@ -125,16 +124,8 @@ __global__ void k_rope(uint16_t* __restrict__ buf, int64_t ld, int T, int seq, i
     const float2 c = cs[(t % seq) * half + j];
     uint16_t* p = buf + int64_t(t) * ld + col0 + h * hd + j;
     const float x1 = bf16_bits_to_f32(p[0]), x2 = bf16_bits_to_f32(p[half]);
-    float y1, y2;
-    if (!inverse) {
-        y1 = x1 * c.x - x2 * c.y;
-        y2 = x2 * c.x + x1 * c.y;
-    } else {
-        y1 = x1 * c.x + x2 * c.y;
-        y2 = x2 * c.x - x1 * c.y;
-    }
-    p[0] = f32_to_bf16_bits(y1);
-    p[half] = f32_to_bf16_bits(y2);
+    p[0] = f32_to_bf16_bits(x1 * c.x - x2 * c.y);
+    p[half] = f32_to_bf16_bits(x2 * c.x + x1 * c.y);
 }
 
 void launch_rope_table(int seq, int hd, float theta, float* cs, hipStream_t s) {
@@ -144,13 +135,13 @@ void launch_rope_table(int seq, int hd, float theta, float* cs, hipStream_t s) {
                        reinterpret_cast<float2*>(cs));
     check_launch("rope_table");
 }
-void launch_rope(uint16_t* buf, int64_t ld, int T, int seq, int col0, int nheads, int hd, const float* cs, int inverse,
+void launch_rope(uint16_t* buf, int64_t ld, int T, int seq, int col0, int nheads, int hd, const float* cs,
                  hipStream_t s) {
     const int64_t total = int64_t(T) * nheads * (hd / 2);
     if (total <= 0) return;
     ProfScope prof("rope", 6.0 * total, 8.0 * total, s);
     hipLaunchKernelGGL(k_rope, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, buf, ld, T, seq, col0, nheads,
-                       hd, reinterpret_cast<const float2*>(cs), inverse);
+                       hd, reinterpret_cast<const float2*>(cs));
     check_launch("rope");
 }
 
@@ -343,30 +334,45 @@ void launch_lora_pack_jobs(const LoraPackJob* jobs, int njobs, int r, float scal
 // Per-query-head gradients dh [B*nH, S, hd] -> per-KV-head sums written as bf16
 // into out[(b*S + t)*ldo + col0 + kvh*hd + d]; group members summed in order.
 __global__ void k_gqa_reduce(const float* __restrict__ dh, int B, int nH, int nKV, int S, int hd,
-                             uint16_t* __restrict__ out, int64_t ldo, int col0) {
+                             uint16_t* __restrict__ out, int64_t ldo, int col0, const float2* __restrict__ rope) {
     const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t total = int64_t(B) * nKV * S * hd;
+    const int half = hd / 2, np = rope ? half : hd;  // a thread: one dim, or one rotated pair
+    const int64_t total = int64_t(B) * nKV * S * np;
     if (idx >= total) return;
-    const int d = int(idx % hd);
-    const int t = int((idx / hd) % S);
-    const int kvh = int((idx / (int64_t(hd) * S)) % nKV);
-    const int b = int(idx / (int64_t(hd) * S * nKV));
+    const int d = int(idx % np);
+    const int t = int((idx / np) % S);
+    const int kvh = int((idx / (int64_t(np) * S)) % nKV);
+    const int b = int(idx / (int64_t(np) * S * nKV));
     const int grp = nH / nKV;
-    float v = 0.f;
-    for (int g = 0; g < grp; ++g) v += dh[((int64_t(b) * nH + kvh * grp + g) * S + t) * hd + d];
-    out[(int64_t(b) * S + t) * ldo + col0 + kvh * hd + d] = f32_to_bf16_bits(v);
+    float v = 0.f, w = 0.f;
+    for (int g = 0; g < grp; ++g) {
+        const float* src = dh + ((int64_t(b) * nH + kvh * grp + g) * S + t) * hd;
+        v += src[d];
+        if (rope) w += src[d + half];
+    }
+    uint16_t* o = out + (int64_t(b) * S + t) * ldo + col0 + kvh * hd;
+    if (!rope) {
+        o[d] = f32_to_bf16_bits(v);
+        return;
+    }
+    const float2 c = rope[int64_t(t) * half + d];  // the rotation's transpose
+    o[d] = f32_to_bf16_bits(v * c.x + w * c.y);
+    o[d + half] = f32_to_bf16_bits(w * c.x - v * c.y);
 }
 void launch_gqa_reduce(const float* dh, int B, int nH, int nKV, int S, int hd, uint16_t* out, int64_t ldo, int col0,
-                       hipStream_t s) {
-    const int64_t total = int64_t(B) * nKV * S * hd;
-    ProfScope prof("gqa_reduce", double(total) * (nH / nKV), double(total) * (4.0 * (nH / nKV) + 2.0), s);
+                       const float* rope, hipStream_t s) {
+    const int64_t total = int64_t(B) * nKV * S * (rope ? hd / 2 : hd);
+    if (total <= 0) return;
+    ProfScope prof("gqa_reduce", double(B) * nKV * S * hd * (nH / nKV), double(B) * nKV * S * hd * (4.0 * (nH / nKV) + 2.0),
+                   s);
     hipLaunchKernelGGL(k_gqa_reduce, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, dh, B, nH, nKV, S, hd, out,
-                       ldo, col0);
+                       ldo, col0, reinterpret_cast<const float2*>(rope));
     check_launch("gqa_reduce");
 }
 
 // ------------------------------------------------------------------ cross-entropy
-// Row t (position s = t % seq) has a target iff start <= s < seq-1; target = tokens[t+1].
+// Row t predicts tokens[t + 1] when its position in the sequence lies in
+// [start, seq - 1); otherwise it has no target (-1).
 __device__ inline int row_target(const int32_t* tokens, int t, int seq, int start) {
     const int s = t % seq;
     if (s < start || s >= seq - 1) return -1;

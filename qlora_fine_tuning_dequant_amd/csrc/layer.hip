@@ -211,6 +211,7 @@ static AttnArgs attn_args(const LayerGeom& g, LayerWs& w) {
     a.dVh = w.dVh;
     a.dqkv = w.dqkv;
     a.lddq = g.nqkv;
+    a.rope = reinterpret_cast<const float2*>(w.rope_cs);
     return a;
 }
 
@@ -260,8 +261,7 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
         out_bf16(p, w.qkv, g.nqkv);
         gemm(p, A_ROW, B_NF4_NT, TE_BF16, w.partial, s);
     }
-    launch_rope(w.qkv, g.nqkv, T, g.S, 0, g.nH, g.hd, w.rope_cs, 0, s);
-    launch_rope(w.qkv, g.nqkv, T, g.S, g.qdim, g.nKV, g.hd, w.rope_cs, 0, s);
+    launch_rope(w.qkv, g.nqkv, T, g.S, 0, g.nH + g.nKV, g.hd, w.rope_cs, s);  // q and k heads are contiguous
     launch_flash_fwd(attn_args(g, w), s);
     if (L) {
         GemmParams pu = dense_gemm(T, r, g.qdim, w.oattn, g.qdim, w.A_o, g.qdim);
@@ -429,10 +429,8 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
 
     // ---- attention: dq into dqkv, per-head fp32 dK, dV summed over each group below
     launch_flash_bwd(attn_args(g, w), s);
-    launch_gqa_reduce(w.dKh, g.B, g.nH, g.nKV, S, g.hd, w.dqkv, g.nqkv, g.qdim, s);
-    launch_gqa_reduce(w.dVh, g.B, g.nH, g.nKV, S, g.hd, w.dqkv, g.nqkv, g.qdim + g.kvdim, s);
-    launch_rope(w.dqkv, g.nqkv, T, S, 0, g.nH, g.hd, w.rope_cs, 1, s);
-    launch_rope(w.dqkv, g.nqkv, T, S, g.qdim, g.nKV, g.hd, w.rope_cs, 1, s);
+    launch_gqa_reduce(w.dKh, g.B, g.nH, g.nKV, S, g.hd, w.dqkv, g.nqkv, g.qdim, w.rope_cs, s);  // dk, rotated back
+    launch_gqa_reduce(w.dVh, g.B, g.nH, g.nKV, S, g.hd, w.dqkv, g.nqkv, g.qdim + g.kvdim, nullptr, s);
 
     // ---- q/k/v projections
     {

@@ -179,8 +179,9 @@ void launch_rmsnorm_fwd(const float* x, const float* g, int T, int H, float eps,
 void launch_rmsnorm_bwd(const float* dy, const float* x, const float* g, const float* rstd, const float* dres,
                         int T, int H, float* dx, hipStream_t s);
 void launch_rope_table(int seq, int hd, float theta, float* cs, hipStream_t s);
-void launch_rope(uint16_t* buf, int64_t ld, int T, int seq, int col0, int nheads, int hd, const float* cs,
-                 int inverse, hipStream_t s);
+// Rotates pairs (j, j + hd/2) of nheads heads in columns [col0, col0 + nheads*hd)
+// of a bf16 [T, ld] buffer in place; row t has position t % seq.
+void launch_rope(uint16_t* buf, int64_t ld, int T, int seq, int col0, int nheads, int hd, const float* cs, hipStream_t s);
 void launch_swiglu_fwd(const uint16_t* gu, int T, int I, uint16_t* act, hipStream_t s);
 void launch_swiglu_bwd(const uint16_t* dact, const uint16_t* gu, int T, int I, uint16_t* dgu, hipStream_t s);
 void launch_embed(const int32_t* tok, const uint16_t* E, int T, int H, int V, float* h, hipStream_t s);
@@ -203,6 +204,7 @@ struct AttnArgs {
     float *dKh = nullptr, *dVh = nullptr;     // [B, nH, S, hd] fp32 per query head
     uint16_t* dqkv = nullptr;                 // dq written at column 0 (bf16)
     int64_t lddq = 0;
+    const float2* rope = nullptr;             // [S, hd/2] (cos, sin): dq rotated back before its store
 };
 void launch_flash_fwd(const AttnArgs& a, hipStream_t s);
 void launch_flash_bwd(const AttnArgs& a, hipStream_t s);
@@ -221,8 +223,10 @@ struct LoraPackJob {
     uint16_t *Acat, *Bbd;
 };
 void launch_lora_pack_jobs(const LoraPackJob* jobs, int njobs, int r, float scale, hipStream_t s);
+// rope non-null: each (j, j + hd/2) pair of the sums is rotated back (RoPE
+// transpose, table [S, hd/2]) before the bf16 store.
 void launch_gqa_reduce(const float* dh, int B, int nH, int nKV, int S, int hd, uint16_t* out, int64_t ldo,
-                       int col0, hipStream_t s);
+                       int col0, const float* rope, hipStream_t s);
 // Cross-entropy pieces over logits [T, V] (fp32).
 // target[t] < 0 marks a row with no loss. lse[t], picked[t] = z[t, target].
 void launch_ce_reduce(const float* pm, const float* ps, int nb, int T, int V, const int32_t* tokens, int seq, int start,
