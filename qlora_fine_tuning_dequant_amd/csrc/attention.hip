@@ -74,6 +74,37 @@ __device__ inline void stage(const uint16_t* __restrict__ src, int64_t ld, int64
     }
 }
 
+// The two halves of stage(), so a block's global loads can be in flight
+// while the previous block computes: load_rows into registers, then
+// store_rows into LDS (same thread-to-element map as stage()).
+template <int HD>
+__device__ inline void load_rows(const uint16_t* __restrict__ src, int64_t ld, int64_t base_row, int r0, int rows,
+                                 int64_t col, uint4 (&v)[HD / 32]) {
+    const int tid = threadIdx.x, r = tid >> 2, part = tid & 3;
+    const bool ok = r0 + r < rows;
+    const uint16_t* s = src + (base_row + r0 + r) * ld + col + part * (HD / 4);
+#pragma unroll
+    for (int c8 = 0; c8 < HD / 32; ++c8) v[c8] = ok ? *reinterpret_cast<const uint4*>(s + c8 * 8) : make_uint4(0, 0, 0, 0);
+}
+template <int HD, bool ROW, bool TRANS>
+__device__ inline void store_rows(const uint4 (&v)[HD / 32], uint16_t* __restrict__ dst_row,
+                                  uint16_t* __restrict__ dst_t) {
+    const int tid = threadIdx.x, r = tid >> 2, part = tid & 3;
+#pragma unroll
+    for (int c8 = 0; c8 < HD / 32; ++c8) {
+        const int c0 = part * (HD / 4) + c8 * 8;
+        if (ROW) *reinterpret_cast<uint4*>(dst_row + r * (HD + 8) + c0) = v[c8];
+        if (TRANS) {
+            const uint32_t w[4] = {v[c8].x, v[c8].y, v[c8].z, v[c8].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dst_t[(c0 + 2 * e) * TP + r] = uint16_t(w[e] & 0xFFFF);
+                dst_t[(c0 + 2 * e + 1) * TP + r] = uint16_t(w[e] >> 16);
+            }
+        }
+    }
+}
+
 // A-operand fragment of a transposed tile for a 32-wide slice js of the
 // 64-row block, in the order the accumulator layout hands out rows: lane
 // (row d = lane & 15 of the 16-row tile dt, group g = lane >> 4) takes block
@@ -110,10 +141,17 @@ __global__ __launch_bounds__(256) void k_flash_fwd(const AttnArgs a) {
     float m = -INFINITY, l = 0.f;
     const float c = a.scale * kLog2e;
     const int64_t kcol = a.qdim + int64_t(kh) * HD, vcol = kcol + a.kvdim;
+    uint4 kr[HD / 32], vr[HD / 32];  // the next key block, in flight during this one's compute
+    load_rows<HD>(a.qkv, a.ld, row0, 0, a.S, kcol, kr);
+    load_rows<HD>(a.qkv, a.ld, row0, 0, a.S, vcol, vr);
     for (int kb = 0; kb <= qb; ++kb) {
-        stage<HD, true, false>(a.qkv, a.ld, row0, kb * QB, a.S, kcol, Ks, nullptr);
-        stage<HD, false, true>(a.qkv, a.ld, row0, kb * QB, a.S, vcol, nullptr, Vt);
+        store_rows<HD, true, false>(kr, Ks, nullptr);
+        store_rows<HD, false, true>(vr, nullptr, Vt);
         __syncthreads();
+        if (kb < qb) {
+            load_rows<HD>(a.qkv, a.ld, row0, (kb + 1) * QB, a.S, kcol, kr);
+            load_rows<HD>(a.qkv, a.ld, row0, (kb + 1) * QB, a.S, vcol, vr);
+        }
         f32x4 st[4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
@@ -227,6 +265,8 @@ __global__ __launch_bounds__(256) void k_flash_bwd_kv(const AttnArgs a) {
     for (int dt = 0; dt < HD / 16; ++dt) dk[dt] = dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     const float c = a.scale * kLog2e;
     const int64_t zrow = (int64_t(b) * a.nH + h) * a.S;
+    // (no register prefetch here: at 272 registers it halves the occupancy,
+    // which costs more than the hidden load latency saves)
     for (int qb = kb; qb < nkb; ++qb) {
         stage<HD, true, true>(a.qkv, a.ld, row0, qb * QB, a.S, int64_t(h) * HD, Qs, Qt);
         stage<HD, true, true>(a.dO, a.ldo, row0, qb * QB, a.S, int64_t(h) * HD, Ds, Dt);
@@ -321,10 +361,17 @@ __global__ __launch_bounds__(256) void k_flash_bwd_q(const AttnArgs a) {
     for (int dt = 0; dt < HD / 16; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     const float c = a.scale * kLog2e;
     const int64_t kcol = a.qdim + int64_t(kh) * HD, vcol = kcol + a.kvdim;
+    uint4 kr[HD / 32], vr[HD / 32];
+    load_rows<HD>(a.qkv, a.ld, row0, 0, a.S, kcol, kr);
+    load_rows<HD>(a.qkv, a.ld, row0, 0, a.S, vcol, vr);
     for (int kb = 0; kb <= qb; ++kb) {
-        stage<HD, true, true>(a.qkv, a.ld, row0, kb * QB, a.S, kcol, Ks, Kt);
-        stage<HD, true, false>(a.qkv, a.ld, row0, kb * QB, a.S, vcol, Vs, nullptr);
+        store_rows<HD, true, true>(kr, Ks, Kt);
+        store_rows<HD, true, false>(vr, Vs, nullptr);
         __syncthreads();
+        if (kb < qb) {
+            load_rows<HD>(a.qkv, a.ld, row0, (kb + 1) * QB, a.S, kcol, kr);
+            load_rows<HD>(a.qkv, a.ld, row0, (kb + 1) * QB, a.S, vcol, vr);
+        }
         uint32_t sk[4][2];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
