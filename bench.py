@@ -57,6 +57,26 @@ WORKLOADS = {
 }
 
 
+# HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc passes
+# (FETCH_SIZE, WRITE_SIZE) over the default workload, each scaled by the same
+# counter on a plain 1 GiB device copy (factors 2.000 and 1.000); valid only
+# for the kernel source they were taken on (SHA-256 prefix of csrc/k_gemm.hip).
+MEASURED_TRAFFIC = {("sft8b_b1", "streamed", "gemm_nf4_nn"): {"bytes": int((130.1 + 28.8) * 1e6),
+                                                              "k_gemm_sha256": "dda1e0507517fb1a"}}
+
+
+def measured_traffic(workload: str, mode: str, kernel: str):
+    import hashlib
+    rec = MEASURED_TRAFFIC.get((workload, mode, kernel))
+    if rec is None:
+        return None
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "qlora_fine_tuning_dequant_amd", "csrc",
+                       "k_gemm.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    return rec["bytes"] if sha == rec["k_gemm_sha256"] else None
+
+
 def log(msg: str) -> None:
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
@@ -403,7 +423,8 @@ def main() -> int:
         p = live[dom]
         ach = p["flops"] / (p["ms"] * 1e-3) / 1e12
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                    "traffic": measured_traffic(args.workload, args.mode if args.source == "ram" else "disk", dom),
                     "launches": p["launches"], "avg_launch_us": round(1000.0 * p["ms"] / p["launches"], 2),
                     "flops_per_launch": p["flops"] / p["launches"]}
     kernels = {k: {"launches_per_step": v["launches"], "ms_per_step": round(v["ms"], 3),
