@@ -46,6 +46,11 @@ WORKLOADS = {
                      name="streamed SFT step, 32-layer Llama-3.1-8B-shaped NF4 base + LoRA r64, batch 1, seq 512"),
     "sft8b_b4": dict(kind="sft", batch=4, seq=512,
                      name="streamed SFT step, 32-layer Llama-3.1-8B-shaped NF4 base + LoRA r64, batch 4, seq 512"),
+    # out-of-config batch sweep (where copies start to hide behind compute)
+    "sft8b_b8": dict(kind="sft", batch=8, seq=512,
+                     name="streamed SFT step, 32-layer Llama-3.1-8B-shaped NF4 base + LoRA r64, batch 8, seq 512"),
+    "sft8b_b16": dict(kind="sft", batch=16, seq=512,
+                      name="streamed SFT step, 32-layer Llama-3.1-8B-shaped NF4 base + LoRA r64, batch 16, seq 512"),
     "dpo8b": dict(kind="dpo", batch=2, seq=512, prompt=128, beta=0.1,
                   name="streamed DPO step, 32-layer Llama-3.1-8B-shaped NF4 base + LoRA r64, 2 pairs x seq 512"),
     "orpo8b": dict(kind="orpo", batch=2, seq=512, prompt=128,
@@ -178,6 +183,64 @@ def cpu_baseline(d, batch: int, seq: int) -> dict:
                       f"step = {d.n_layers} x layer + head = {step_s:.1f} s"}
 
 
+def cpu_baseline_detail() -> dict:
+    """The CPU-baseline leg in full (the oracle as it stands, on this host):
+    the tiny model's whole SFT step (L 2, H 256, batch 1 x 64) and one
+    8B-shaped layer's forward + recompute + backward at batch 1 x 512, each
+    with every BLAS thread and with one; the 32-layer step estimate is 32 x
+    that layer + the LM head."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import oracle
+    import synth
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+
+    def model(d, seed):
+        layers = []
+        for l in range(d.n_layers):
+            nf4 = {p: oracle.nf4_quantize(synth.bf16_bits_to_f32(synth.proj_weight_bf16(d, seed, l, p)))
+                   for p in synth.PROJ_NAMES}
+            g1, g2 = synth.norm_weights(d, seed, l)
+            layers.append(dict(nf4=nf4, g1=g1, g2=g2))
+        return dict(layers=layers, embed=synth.embedding_f16(d, seed), head=synth.lm_head_f16(d, seed),
+                    gf=synth.final_norm_weight(d, seed))
+
+    def c1():
+        d = synth.TINY
+        m = model(d, 0)
+        lora = [synth.lora_params(d, 0, l, "normal") for l in range(d.n_layers)]
+        toks = synth.tokens(0, 1, 64, d.vocab)
+        t0 = time.perf_counter()
+        oracle.sft_step(m, lora, toks, d)
+        return time.perf_counter() - t0
+
+    def c2():
+        d, batch, seq = synth.LLAMA8B, 1, 512
+        T = batch * seq
+        nf4 = {p: oracle.nf4_quantize(synth.bf16_bits_to_f32(synth.proj_weight_bf16(d, SEED, 0, p)))
+               for p in synth.PROJ_NAMES}
+        lp = synth.lora_params(d, SEED, 0, "kaiming")
+        g1, g2 = synth.norm_weights(d, SEED, 0)
+        h = synth.activations_f32(SEED, T, d.hidden, 0)
+        dh = synth.activations_f32(SEED, T, d.hidden, 1) * np.float32(1e-4)
+        t0 = time.perf_counter()
+        W = oracle.dequant_layer(nf4, d)
+        oracle.layer_fwd(h, W, g1, g2, lp, d, batch, seq)
+        W = oracle.dequant_layer(nf4, d)
+        _, cache = oracle.layer_fwd(h, W, g1, g2, lp, d, batch, seq, keep=True)
+        oracle.layer_bwd(dh, W, g1, g2, lp, d, batch, seq, cache)
+        return time.perf_counter() - t0
+
+    out = {"host_cpus": os.cpu_count(), "blas_threads": int(threads)}
+    out["C1_sft_step_s"] = round(c1(), 3)
+    out["C2_layer_fwd_recompute_bwd_s"] = round(c2(), 3)
+    with threadpool_limits(limits=1):
+        out["C1_sft_step_s_1thread"] = round(c1(), 3)
+        out["C2_layer_fwd_recompute_bwd_s_1thread"] = round(c2(), 3)
+    return out
+
+
 def gemm_shapes(q) -> dict:
     """TFLOP/s of the 8B-shaped NF4 GEMMs (LoRA off) through qlora_linear_fwd
     (y = x W'^T) and qlora_linear_bwd (dx = dy W'), from the library's events."""
@@ -266,6 +329,50 @@ def merge_shapes(q) -> dict:
     return out
 
 
+def measure_peaks(q) -> dict:
+    """The device's own peaks next to the vendor's: a bf16 MFMA loop and a
+    16-byte HBM copy kernel from the library, and one layer-blob-sized
+    (122.7 MB) pinned host-to-device hipMemcpyAsync."""
+    import torch
+    import synth
+    B_ = q.binding
+    L = B_.lib()
+    dev = "cuda:0"
+    s = torch.cuda.current_stream()
+    out = {}
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps  # ms
+
+    wgs, iters = 256 * 8, 20000
+    buf = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    for shape, key in ((0, "mfma_bf16_16x16x32_TFLOPs"), (1, "mfma_bf16_32x32x16_TFLOPs")):
+        ms = timed(lambda: B_._check(L.qlx_peak_mfma(iters, wgs, shape, buf.data_ptr(), s.cuda_stream)), 3)
+        out[key] = round(131072.0 * iters * wgs * 4 / ms / 1e9, 1)
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    ms = timed(lambda: B_._check(L.qlx_peak_copy(src.data_ptr(), dst.data_ptr(), n, s.cuda_stream)), 10)
+    out["hbm_copy_GBps"] = round(2.0 * n / ms / 1e6, 1)
+    del src, dst
+    _, blob = B_.blob_layout(synth.LLAMA8B)
+    h = torch.empty(blob, dtype=torch.uint8, pin_memory=True)
+    d = torch.empty(blob, dtype=torch.uint8, device=dev)
+    ms = timed(lambda: d.copy_(h, non_blocking=True), 10)
+    out["h2d_pinned_GBps"] = round(blob / ms / 1e6, 1)
+    out["h2d_bytes"] = blob
+    out["vendor"] = {"mfma_bf16_TFLOPs": PEAK_BF16_TFLOPS, "hbm_GBps": 8000.0, "pcie_gen5_x16_GBps": 64.0}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -288,6 +395,10 @@ def main() -> int:
                     help="only time the 8B-shaped NF4 GEMMs (fwd and dX) at 512 and 2048 tokens")
     ap.add_argument("--merge-shapes", action="store_true",
                     help="only time the adapter merge of one 8B-shaped layer's seven projections (bf16 and NF4 out)")
+    ap.add_argument("--cpu-baseline-detail", action="store_true",
+                    help="only time the oracle on this host: tiny SFT step and one 8B layer, all threads and one")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only measure the device's peaks: bf16 MFMA loop, HBM copy, 122.7 MB pinned H2D copy")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB five times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -297,6 +408,10 @@ def main() -> int:
         return 2
 
     import numpy as np
+
+    if args.cpu_baseline_detail:
+        print(json.dumps({"cpu_baseline_detail": cpu_baseline_detail()}))
+        return 0
     import torch
 
     if args.copy_calibration:
@@ -318,6 +433,9 @@ def main() -> int:
         return 0
     if args.merge_shapes:
         print(json.dumps({"merge_shapes": merge_shapes(q)}))
+        return 0
+    if args.peaks:
+        print(json.dumps({"peaks": measure_peaks(q)}))
         return 0
     wl = WORKLOADS[args.workload]
     d = synth.LLAMA8B
@@ -427,9 +545,14 @@ def main() -> int:
                     "traffic": measured_traffic(args.workload, args.mode if args.source == "ram" else "disk", dom),
                     "launches": p["launches"], "avg_launch_us": round(1000.0 * p["ms"] / p["launches"], 2),
                     "flops_per_launch": p["flops"] / p["launches"]}
+    # per kernel: rate and fraction of the vendor peak that bounds it (MFMA for
+    # the products, HBM for the rest)
     kernels = {k: {"launches_per_step": v["launches"], "ms_per_step": round(v["ms"], 3),
                    "TFLOP/s": round(v["flops"] / max(v["ms"], 1e-9) / 1e9, 2),
-                   "GB/s": round(v["bytes"] / max(v["ms"], 1e-9) / 1e6, 1)}
+                   "GB/s": round(v["bytes"] / max(v["ms"], 1e-9) / 1e6, 1),
+                   **({"mfma_frac": round(v["flops"] / max(v["ms"], 1e-9) / 1e9 / PEAK_BF16_TFLOPS, 4)}
+                      if k.startswith(("gemm", "attn_fwd", "attn_bwd_kv", "attn_bwd_q"))
+                      else {"hbm_frac": round(v["bytes"] / max(v["ms"], 1e-9) / 1e6 / 8000.0, 4)})}
                for k, v in sorted(prof.items(), key=lambda kv: -kv[1]["ms"])}
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

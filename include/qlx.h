@@ -416,6 +416,17 @@ int qlx_profile_begin(void);
 int qlx_profile_begin_prefix(const char* name_prefix);
 int qlx_profile_end(qlx_kernel_prof* out, int max_out, int* count);
 
+/* Measured peaks of the device, for roofline figures (not part of a step).
+ * qlx_peak_mfma: `workgroups` workgroups of 4 wavefronts, each wavefront
+ *   running `iters` x (shape 0) 8 independent v_mfma_f32_16x16x32_bf16 or
+ *   (shape 1) 4 independent v_mfma_f32_32x32x16_bf16 on register operands:
+ *   131072 x iters flops per wavefront either way. out: DEVICE fp32
+ *   [workgroups * 256], written to keep the loop alive.
+ * qlx_peak_copy: a 16-byte grid-stride copy of `bytes` (multiple of 16,
+ *   both buffers DEVICE and 16-byte aligned): bytes read + bytes written. */
+int qlx_peak_mfma(int64_t iters, int workgroups, int shape, float* out, void* stream);
+int qlx_peak_copy(const void* src, void* dst, uint64_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,6 +39,7 @@ EXPORTED = (
     "qlx_step_workspace_bytes", "stream_step_sft", "stream_step_dpo", "stream_step_pref", "qlx_merge_workspace_bytes", "qlx_lora_merge", "qlx_profile_begin", "qlx_profile_begin_prefix", "qlx_profile_end", "qlx_adamw_lora",
     "qlx_layer_file_write", "qlx_layer_file_open", "qlx_layer_file_close", "qlx_layer_file_info",
     "qlx_layer_file_read", "qlx_ctx_set_layer_source", "qlx_stream_source_auto", "qlx_ctx_set_debug",
+    "qlx_peak_mfma", "qlx_peak_copy",
 )
 
 
@@ -152,6 +153,8 @@ def lib() -> C.CDLL:
         "qlx_ctx_set_layer_source": (i32, [vp, vp]),
         "qlx_stream_source_auto": (i32, [C.c_uint64, C.c_uint64, C.POINTER(C.c_int)]),
         "qlx_ctx_set_debug": (i32, [vp, i32, i32]),
+        "qlx_peak_mfma": (i32, [C.c_int64, i32, i32, vp, vp]),
+        "qlx_peak_copy": (i32, [vp, vp, C.c_uint64, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libqlx.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["k_nf4.hip", "k_gemm.hip", "k_elem.hip", "attention.hip", "optim.hip", "merge.hip", "layer.hip", "api.hip",
-           "source.hip", "prof.hip"]
+           "source.hip", "prof.hip", "peaks.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -23,10 +23,13 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 instructions stay off (see the build notes)
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-Wall", "-Wno-unused-function",
-         "-Wno-unused-command-line-argument"]
-# MFMA accumulators in ordinary VGPRs: with AGPR accumulators the register
-# allocator splits the tile between the two files and shuffles it every chunk
-EXTRA = {"k_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+         "-Wno-unused-command-line-argument",
+         # MFMA accumulators in ordinary VGPRs: with AGPR accumulators the
+         # register allocator splits them between the two files and shuffles
+         # them through v_accvgpr moves in every loop iteration (measured: a
+         # 16x16x32 bf16 MFMA loop at 56% of peak with the moves, 95% without)
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+EXTRA: dict = {}
 
 
 def _compile(src: str) -> str:

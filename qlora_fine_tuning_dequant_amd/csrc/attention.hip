@@ -265,17 +265,22 @@ __global__ __launch_bounds__(256) void k_flash_bwd_kv(const AttnArgs a) {
     for (int dt = 0; dt < HD / 16; ++dt) dk[dt] = dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     const float c = a.scale * kLog2e;
     const int64_t zrow = (int64_t(b) * a.nH + h) * a.S;
-    // (no register prefetch here: at 272 registers it halves the occupancy,
-    // which costs more than the hidden load latency saves)
+    uint4 qr[HD / 32], dr[HD / 32];  // the next query block, in flight during this one's compute
+    load_rows<HD>(a.qkv, a.ld, row0, kb * QB, a.S, int64_t(h) * HD, qr);
+    load_rows<HD>(a.dO, a.ldo, row0, kb * QB, a.S, int64_t(h) * HD, dr);
     for (int qb = kb; qb < nkb; ++qb) {
-        stage<HD, true, true>(a.qkv, a.ld, row0, qb * QB, a.S, int64_t(h) * HD, Qs, Qt);
-        stage<HD, true, true>(a.dO, a.ldo, row0, qb * QB, a.S, int64_t(h) * HD, Ds, Dt);
+        store_rows<HD, true, true>(qr, Qs, Qt);
+        store_rows<HD, true, true>(dr, Ds, Dt);
         if (tid < QB) {
             const int qq = qb * QB + tid;
             lse_s[tid] = qq < a.S ? a.lse[zrow + qq] * kLog2e : 0.f;
             dq_s[tid] = qq < a.S ? a.Dq[zrow + qq] : 0.f;
         }
         __syncthreads();
+        if (qb + 1 < nkb) {
+            load_rows<HD>(a.qkv, a.ld, row0, (qb + 1) * QB, a.S, int64_t(h) * HD, qr);
+            load_rows<HD>(a.dO, a.ldo, row0, (qb + 1) * QB, a.S, int64_t(h) * HD, dr);
+        }
         // S = Q K^T and dP = dO V^T for 64 queries x this wavefront's 16 keys
         f32x4 s[4], dp[4];
 #pragma unroll
