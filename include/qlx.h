@@ -235,7 +235,9 @@ int qlx_layer_file_write(const char* path, const qlx_dims* d, const void* const*
  * shorter than n_layers * stride. flags: 0 or QLX_FILE_BUFFERED. */
 int qlx_layer_file_open(qlx_layer_file** out, const char* path, const qlx_dims* d, int flags);
 /* Waits for copies still reading its staging buffers, then frees it. NULL is
- * a no-op. Detach it from its context first. */
+ * a no-op. QLX_EINVAL (and nothing freed) while a context still holds it:
+ * detach it first (qlx_ctx_set_layer_source(ctx, NULL)) or destroy that
+ * context. */
 int qlx_layer_file_close(qlx_layer_file* f);
 /* *direct (HOST) = 1 if reads bypass the page cache; *stride = blob stride. */
 int qlx_layer_file_info(const qlx_layer_file* f, int* direct, uint64_t* stride);

@@ -457,8 +457,9 @@ class LayerFile:
         _check(lib().qlx_layer_file_read(self.h, layer, ptr))
 
     def close(self) -> None:
+        """Frees the file; raises QlxError while a context still holds it."""
         if self.h:
-            lib().qlx_layer_file_close(self.h)
+            _check(lib().qlx_layer_file_close(self.h))
             self.h = None
 
     def __del__(self):

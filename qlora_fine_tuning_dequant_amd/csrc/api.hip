@@ -717,6 +717,7 @@ int qlx_ctx_destroy(qlx_ctx* ctx) {
         if (!ctx) return;
         (void)hipSetDevice(ctx->device);
         (void)hipStreamSynchronize(ctx->side);
+        if (ctx->source) ctx->source->attached -= 1;  // the file outlives the context
         for (auto& e : ctx->copy_ev) (void)hipEventDestroy(e);
         for (int i = 0; i < 2; ++i) {
             (void)hipEventDestroy(ctx->copy_done[i]);
@@ -748,7 +749,9 @@ int qlx_ctx_set_debug(qlx_ctx* ctx, int flags, int delay_us) {
 int qlx_ctx_set_layer_source(qlx_ctx* ctx, qlx_layer_file* f) {
     return guarded([&] {
         REQ_PTR(ctx, "ctx");
+        if (f == ctx->source) return;
         if (!f) {
+            ctx->source->attached -= 1;
             ctx->source = nullptr;
             return;
         }
@@ -763,7 +766,9 @@ int qlx_ctx_set_layer_source(qlx_ctx* ctx, qlx_layer_file* f) {
             }
             f->device = ctx->device;
         }
+        if (ctx->source) ctx->source->attached -= 1;
         ctx->source = f;
+        f->attached += 1;
     });
 }
 

@@ -40,6 +40,7 @@ struct qlx_layer_file {
 
     // pinned staging ring, bound to one device by qlx_ctx_set_layer_source
     int device = -1;
+    int attached = 0;  // contexts that hold this file (qlx_ctx_set_layer_source)
     char* staging[qlx::kStaging] = {};
     hipEvent_t staging_free[qlx::kStaging] = {};
     int next = 0;

@@ -212,7 +212,11 @@ int qlx_layer_file_open(qlx_layer_file** out, const char* path, const qlx_dims* 
 
 int qlx_layer_file_close(qlx_layer_file* f) {
     return guarded([&] {
-        if (f) close_file(f);
+        if (!f) return;
+        QLX_REQUIRE(f->attached == 0, QLX_EINVAL,
+                    "layer file is still attached to " + std::to_string(f->attached) +
+                        " context(s): detach it (qlx_ctx_set_layer_source(ctx, NULL)) first");
+        close_file(f);
     });
 }
 

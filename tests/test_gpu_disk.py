@@ -86,3 +86,26 @@ def test_disk_mode_needs_a_matching_file(four, tmp_path):
     ctx.set_layer_source(None)
     ctx.close()
     f2.close()
+
+
+def test_attached_file_cannot_be_closed(four):
+    d, m, host, path = four
+    f = q.LayerFile(path, d)
+    ctx = q.Context(0)
+    ctx.set_layer_source(f)
+    with pytest.raises(B_.QlxError) as e:  # still held by the context: nothing freed
+        f.close()
+    assert e.value.code == B_.QLX_EINVAL and "attached" in str(e.value)
+    toks = synth.tokens(1, 1, 32, d.vocab)
+    l_d, _, _ = run_sft(q, _disk_model(m), toks, B_.QLX_STREAMED_DISK, ctx)  # the file still works
+    l_s, _, _ = run_sft(q, m.with_blobs(host), toks, B_.QLX_STREAMED)
+    assert torch.equal(l_d, l_s)
+    ctx.set_layer_source(f)  # attaching the same file twice counts once
+    ctx.close()              # a destroyed context releases its file
+    f.close()
+    g = q.LayerFile(path, d)
+    ctx2 = q.Context(0)
+    ctx2.set_layer_source(g)
+    ctx2.set_layer_source(None)
+    g.close()
+    ctx2.close()
