@@ -44,6 +44,8 @@ __device__ inline float block_max256(float v, float* red) {
     return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
+static bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 // ------------------------------------------------------------------ RMSNorm
 // y = x * rstd * g, rstd = 1 / sqrt(mean(x^2) + eps). One workgroup per row.
 __global__ __launch_bounds__(256) void k_rmsnorm_fwd(const float* __restrict__ x, const float* __restrict__ g, int H,
@@ -84,19 +86,122 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const float* __restrict__ d
     }
 }
 
+// Row kept in registers (NV float4 per thread, H = 1024 NV): one HBM read
+// of x, 16-byte loads and 8-byte stores. Same formulas as above.
+template <int NV>
+__global__ __launch_bounds__(256) void k_rmsnorm_fwd_v(const float* __restrict__ x, const float* __restrict__ g, int H,
+                                                       float eps, void* __restrict__ out, int out_f16,
+                                                       float* __restrict__ rstd) {
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const float4* xr = reinterpret_cast<const float4*>(x + row * H);
+    const float4* gr = reinterpret_cast<const float4*>(g);
+    float4 v[NV];
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        v[k] = xr[threadIdx.x + 256 * k];
+        ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
+    }
+    ss = block_sum256(ss, red);
+    const float r = 1.0f / sqrtf(ss / float(H) + eps);
+    if (threadIdx.x == 0 && rstd) rstd[row] = r;
+    uint2* o = reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + row * H);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const float4 gg = gr[threadIdx.x + 256 * k];
+        const float y0 = v[k].x * r * gg.x, y1 = v[k].y * r * gg.y, y2 = v[k].z * r * gg.z, y3 = v[k].w * r * gg.w;
+        o[threadIdx.x + 256 * k] =
+            out_f16 ? make_uint2(uint32_t(f32_to_f16_bits(y0)) | (uint32_t(f32_to_f16_bits(y1)) << 16),
+                                 uint32_t(f32_to_f16_bits(y2)) | (uint32_t(f32_to_f16_bits(y3)) << 16))
+                    : make_uint2(f32x2_to_bf16x2(y0, y1), f32x2_to_bf16x2(y2, y3));
+    }
+}
+template <int NV>
+__global__ __launch_bounds__(256) void k_rmsnorm_bwd_v(const float* __restrict__ dy, const float* __restrict__ x,
+                                                       const float* __restrict__ g, const float* __restrict__ rstd,
+                                                       const float* __restrict__ dres, int H, float* __restrict__ dx) {
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const float4* dyr = reinterpret_cast<const float4*>(dy + row * H);
+    const float4* xr = reinterpret_cast<const float4*>(x + row * H);
+    const float4* gr = reinterpret_cast<const float4*>(g);
+    const float r = rstd[row];
+    float4 a[NV], b[NV];  // dy * g, x * r
+    float dot = 0.f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const float4 d = dyr[threadIdx.x + 256 * k], xx = xr[threadIdx.x + 256 * k], gg = gr[threadIdx.x + 256 * k];
+        a[k] = make_float4(d.x * gg.x, d.y * gg.y, d.z * gg.z, d.w * gg.w);
+        b[k] = make_float4(xx.x * r, xx.y * r, xx.z * r, xx.w * r);
+        dot += a[k].x * b[k].x + a[k].y * b[k].y + a[k].z * b[k].z + a[k].w * b[k].w;
+    }
+    dot = block_sum256(dot, red) / float(H);
+    float4* o = reinterpret_cast<float4*>(dx + row * H);
+    const float4* dr = dres ? reinterpret_cast<const float4*>(dres + row * H) : nullptr;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        float4 v = make_float4(r * (a[k].x - b[k].x * dot), r * (a[k].y - b[k].y * dot), r * (a[k].z - b[k].z * dot),
+                               r * (a[k].w - b[k].w * dot));
+        if (dr) {
+            const float4 q = dr[threadIdx.x + 256 * k];
+            v.x += q.x;
+            v.y += q.y;
+            v.z += q.z;
+            v.w += q.w;
+        }
+        o[threadIdx.x + 256 * k] = v;
+    }
+}
+static bool rms_vec(int H, const void* a, const void* b, const void* c, const void* d) {
+    return H % 1024 == 0 && H <= 4096 && al16(a) && al16(b) && al16(c) && (!d || al16(d));
+}
+
 void launch_rmsnorm_fwd(const float* x, const float* g, int T, int H, float eps, void* out, int out_f16, float* rstd,
                         hipStream_t s) {
     if (T <= 0) return;
     ProfScope prof("rmsnorm_fwd", 4.0 * T * H, double(T) * H * (4.0 + (out_f16 ? 2 : 2)) + 4.0 * H, s);
-    hipLaunchKernelGGL(k_rmsnorm_fwd, dim3(T), dim3(256), 0, s, x, g, H, eps, out, out_f16, rstd);
+    if (rms_vec(H, x, g, out, nullptr) && (reinterpret_cast<uintptr_t>(out) & 7) == 0) {
+        switch (H / 1024) {
+            case 1: hipLaunchKernelGGL(k_rmsnorm_fwd_v<1>, dim3(T), dim3(256), 0, s, x, g, H, eps, out, out_f16, rstd); break;
+            case 2: hipLaunchKernelGGL(k_rmsnorm_fwd_v<2>, dim3(T), dim3(256), 0, s, x, g, H, eps, out, out_f16, rstd); break;
+            case 3: hipLaunchKernelGGL(k_rmsnorm_fwd_v<3>, dim3(T), dim3(256), 0, s, x, g, H, eps, out, out_f16, rstd); break;
+            default: hipLaunchKernelGGL(k_rmsnorm_fwd_v<4>, dim3(T), dim3(256), 0, s, x, g, H, eps, out, out_f16, rstd);
+        }
+    } else {
+        hipLaunchKernelGGL(k_rmsnorm_fwd, dim3(T), dim3(256), 0, s, x, g, H, eps, out, out_f16, rstd);
+    }
     check_launch("rmsnorm_fwd");
 }
 void launch_rmsnorm_bwd(const float* dy, const float* x, const float* g, const float* rstd, const float* dres, int T,
                         int H, float* dx, hipStream_t s) {
     if (T <= 0) return;
     ProfScope prof("rmsnorm_bwd", 8.0 * T * H, double(T) * H * (12.0 + (dres ? 4 : 0)), s);
-    hipLaunchKernelGGL(k_rmsnorm_bwd, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx);
+    if (rms_vec(H, dy, x, g, dres) && al16(dx)) {
+        switch (H / 1024) {
+            case 1: hipLaunchKernelGGL(k_rmsnorm_bwd_v<1>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx); break;
+            case 2: hipLaunchKernelGGL(k_rmsnorm_bwd_v<2>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx); break;
+            case 3: hipLaunchKernelGGL(k_rmsnorm_bwd_v<3>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx); break;
+            default: hipLaunchKernelGGL(k_rmsnorm_bwd_v<4>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx);
+        }
+    } else {
+        hipLaunchKernelGGL(k_rmsnorm_bwd, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx);
+    }
     check_launch("rmsnorm_bwd");
+}
+
+// bf16 x8 <-> fp32 x8 for 16-byte accesses.
+__device__ inline void unpack8(const uint4& v, float (&f)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        f[2 * k] = __builtin_bit_cast(float, w[k] << 16);
+        f[2 * k + 1] = __builtin_bit_cast(float, w[k] & 0xFFFF0000u);
+    }
+}
+__device__ inline uint4 pack8_bf16(const float (&f)[8]) {
+    return make_uint4(f32x2_to_bf16x2(f[0], f[1]), f32x2_to_bf16x2(f[2], f[3]), f32x2_to_bf16x2(f[4], f[5]),
+                      f32x2_to_bf16x2(f[6], f[7]));
 }
 
 // ------------------------------------------------------------------ RoPE
@@ -128,6 +233,34 @@ __global__ void k_rope(uint16_t* __restrict__ buf, int64_t ld, int T, int seq, i
     p[half] = f32_to_bf16_bits(x2 * c.x + x1 * c.y);
 }
 
+// Same rotation, eight consecutive pairs per thread (16-byte loads and
+// stores of each half; hd/2 a multiple of 8, rows 16-byte aligned).
+__global__ void k_rope8(uint16_t* __restrict__ buf, int64_t ld, int T, int seq, int col0, int nheads, int hd,
+                        const float2* __restrict__ cs) {
+    const int half = hd / 2, h8 = half / 8;
+    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t total = int64_t(T) * nheads * h8;
+    if (idx >= total) return;
+    const int j = int(idx % h8) * 8;
+    const int h = int((idx / h8) % nheads);
+    const int t = int(idx / (int64_t(h8) * nheads));
+    const float4* c4 = reinterpret_cast<const float4*>(cs + (t % seq) * half + j);
+    uint16_t* p = buf + int64_t(t) * ld + col0 + h * hd + j;
+    float a[8], b[8], ra[8], rb[8];
+    unpack8(*reinterpret_cast<const uint4*>(p), a);
+    unpack8(*reinterpret_cast<const uint4*>(p + half), b);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float4 c = c4[k];  // (cos, sin) of pairs 2k and 2k+1
+        ra[2 * k] = a[2 * k] * c.x - b[2 * k] * c.y;
+        rb[2 * k] = b[2 * k] * c.x + a[2 * k] * c.y;
+        ra[2 * k + 1] = a[2 * k + 1] * c.z - b[2 * k + 1] * c.w;
+        rb[2 * k + 1] = b[2 * k + 1] * c.z + a[2 * k + 1] * c.w;
+    }
+    *reinterpret_cast<uint4*>(p) = pack8_bf16(ra);
+    *reinterpret_cast<uint4*>(p + half) = pack8_bf16(rb);
+}
+
 void launch_rope_table(int seq, int hd, float theta, float* cs, hipStream_t s) {
     const int n = seq * (hd / 2);
     ProfScope prof("rope_table", 0.0, 8.0 * n, s);
@@ -140,6 +273,13 @@ void launch_rope(uint16_t* buf, int64_t ld, int T, int seq, int col0, int nheads
     const int64_t total = int64_t(T) * nheads * (hd / 2);
     if (total <= 0) return;
     ProfScope prof("rope", 6.0 * total, 8.0 * total, s);
+    if ((hd / 2) % 8 == 0 && ld % 8 == 0 && col0 % 8 == 0 && al16(buf) && al16(cs)) {
+        const int64_t t8 = total / 8;
+        hipLaunchKernelGGL(k_rope8, dim3(unsigned((t8 + 255) / 256)), dim3(256), 0, s, buf, ld, T, seq, col0, nheads,
+                           hd, reinterpret_cast<const float2*>(cs));
+        check_launch("rope");
+        return;
+    }
     hipLaunchKernelGGL(k_rope, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, buf, ld, T, seq, col0, nheads,
                        hd, reinterpret_cast<const float2*>(cs));
     check_launch("rope");
@@ -147,25 +287,59 @@ void launch_rope(uint16_t* buf, int64_t ld, int T, int seq, int col0, int nheads
 
 // ------------------------------------------------------------------ SwiGLU
 // gu = [gate | up] bf16 [T, 2I]; act = silu(gate) * up.
+__device__ inline float silu_sig(float g) { return 1.0f / (1.0f + expf(-g)); }
+// VEC: 8 consecutive i per thread with 16-byte accesses (I % 8 == 0, 16-byte
+// aligned buffers); the arithmetic per element is the same either way.
+template <bool VEC>
 __global__ void k_swiglu_fwd(const uint16_t* __restrict__ gu, int T, int I, uint16_t* __restrict__ act) {
     const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (VEC) {
+        const int I8 = I / 8;
+        if (idx >= int64_t(T) * I8) return;
+        const int64_t t = idx / I8, i = (idx % I8) * 8;
+        float g[8], u[8], y[8];
+        unpack8(*reinterpret_cast<const uint4*>(gu + t * 2 * I + i), g);
+        unpack8(*reinterpret_cast<const uint4*>(gu + t * 2 * I + I + i), u);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = g[e] * silu_sig(g[e]) * u[e];
+        *reinterpret_cast<uint4*>(act + t * I + i) = pack8_bf16(y);
+        return;
+    }
     if (idx >= int64_t(T) * I) return;
     const int64_t t = idx / I, i = idx % I;
     const float g = bf16_bits_to_f32(gu[t * 2 * I + i]);
     const float u = bf16_bits_to_f32(gu[t * 2 * I + I + i]);
-    const float sg = 1.0f / (1.0f + expf(-g));
-    act[idx] = f32_to_bf16_bits(g * sg * u);
+    act[idx] = f32_to_bf16_bits(g * silu_sig(g) * u);
 }
 // dgate = da * up * silu'(gate), dup = da * silu(gate); silu' = s (1 + g (1 - s)).
+template <bool VEC>
 __global__ void k_swiglu_bwd(const uint16_t* __restrict__ dact, const uint16_t* __restrict__ gu, int T, int I,
                              uint16_t* __restrict__ dgu) {
     const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (VEC) {
+        const int I8 = I / 8;
+        if (idx >= int64_t(T) * I8) return;
+        const int64_t t = idx / I8, i = (idx % I8) * 8;
+        float g[8], u[8], da[8], dg[8], du[8];
+        unpack8(*reinterpret_cast<const uint4*>(gu + t * 2 * I + i), g);
+        unpack8(*reinterpret_cast<const uint4*>(gu + t * 2 * I + I + i), u);
+        unpack8(*reinterpret_cast<const uint4*>(dact + t * I + i), da);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float sg = silu_sig(g[e]);
+            dg[e] = da[e] * u[e] * (sg * (1.0f + g[e] * (1.0f - sg)));
+            du[e] = da[e] * g[e] * sg;
+        }
+        *reinterpret_cast<uint4*>(dgu + t * 2 * I + i) = pack8_bf16(dg);
+        *reinterpret_cast<uint4*>(dgu + t * 2 * I + I + i) = pack8_bf16(du);
+        return;
+    }
     if (idx >= int64_t(T) * I) return;
     const int64_t t = idx / I, i = idx % I;
     const float g = bf16_bits_to_f32(gu[t * 2 * I + i]);
     const float u = bf16_bits_to_f32(gu[t * 2 * I + I + i]);
     const float da = bf16_bits_to_f32(dact[idx]);
-    const float sg = 1.0f / (1.0f + expf(-g));
+    const float sg = silu_sig(g);
     dgu[t * 2 * I + i] = f32_to_bf16_bits(da * u * (sg * (1.0f + g * (1.0f - sg))));
     dgu[t * 2 * I + I + i] = f32_to_bf16_bits(da * g * sg);
 }
@@ -173,14 +347,22 @@ void launch_swiglu_fwd(const uint16_t* gu, int T, int I, uint16_t* act, hipStrea
     const int64_t n = int64_t(T) * I;
     if (n <= 0) return;
     ProfScope prof("swiglu_fwd", 5.0 * n, 6.0 * n, s);
-    hipLaunchKernelGGL(k_swiglu_fwd, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, gu, T, I, act);
+    if (I % 8 == 0 && al16(gu) && al16(act))
+        hipLaunchKernelGGL(k_swiglu_fwd<true>, dim3(unsigned((n / 8 + 255) / 256)), dim3(256), 0, s, gu, T, I, act);
+    else
+        hipLaunchKernelGGL(k_swiglu_fwd<false>, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, gu, T, I, act);
     check_launch("swiglu_fwd");
 }
 void launch_swiglu_bwd(const uint16_t* dact, const uint16_t* gu, int T, int I, uint16_t* dgu, hipStream_t s) {
     const int64_t n = int64_t(T) * I;
     if (n <= 0) return;
     ProfScope prof("swiglu_bwd", 10.0 * n, 10.0 * n, s);
-    hipLaunchKernelGGL(k_swiglu_bwd, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, dact, gu, T, I, dgu);
+    if (I % 8 == 0 && al16(gu) && al16(dact) && al16(dgu))
+        hipLaunchKernelGGL(k_swiglu_bwd<true>, dim3(unsigned((n / 8 + 255) / 256)), dim3(256), 0, s, dact, gu, T, I,
+                           dgu);
+    else
+        hipLaunchKernelGGL(k_swiglu_bwd<false>, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, dact, gu, T, I,
+                           dgu);
     check_launch("swiglu_bwd");
 }
 
@@ -202,14 +384,27 @@ void launch_embed(const int32_t* tok, const uint16_t* E, int T, int H, int V, fl
     check_launch("embed");
 }
 
+// 8 elements per thread (two 16-byte loads, one 16-byte store) where the
+// buffers allow, else one.
+template <bool VEC>
 __global__ void k_f32_to_bf16(const float* __restrict__ x, int64_t n, uint16_t* __restrict__ y) {
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (VEC) {
+        if (i >= n / 8) return;
+        const float4 a = reinterpret_cast<const float4*>(x)[2 * i], b = reinterpret_cast<const float4*>(x)[2 * i + 1];
+        reinterpret_cast<uint4*>(y)[i] = make_uint4(f32x2_to_bf16x2(a.x, a.y), f32x2_to_bf16x2(a.z, a.w),
+                                                    f32x2_to_bf16x2(b.x, b.y), f32x2_to_bf16x2(b.z, b.w));
+        return;
+    }
     if (i < n) y[i] = f32_to_bf16_bits(x[i]);
 }
 void launch_f32_to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s) {
     if (n <= 0) return;
     ProfScope prof("f32_to_bf16", 0.0, 6.0 * n, s);
-    hipLaunchKernelGGL(k_f32_to_bf16, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, x, n, y);
+    if (n % 8 == 0 && al16(x) && al16(y))
+        hipLaunchKernelGGL(k_f32_to_bf16<true>, dim3(unsigned((n / 8 + 255) / 256)), dim3(256), 0, s, x, n, y);
+    else
+        hipLaunchKernelGGL(k_f32_to_bf16<false>, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, x, n, y);
     check_launch("f32_to_bf16");
 }
 
@@ -264,6 +459,39 @@ __device__ inline void lora_pack_one(const LoraSegs& sg, int r, int in_f, float 
     while (p < sg.nseg - 1 && n >= off + sg.out[p]) off += sg.out[p++];
     Bbd[jdx] = (p == q) ? f32_to_bf16_bits(scale * sg.B[p][int64_t(n - off) * r + j]) : uint16_t(0);
 }
+// Eight consecutive elements per thread (in_f and r multiples of 8, every
+// pointer 16-byte aligned): two float4 loads and one 16-byte store. idx8
+// counts groups of eight; a group never straddles an A row or a B block.
+__device__ inline void lora_pack_one8(const LoraSegs& sg, int r, int in_f, float scale, uint16_t* __restrict__ Acat,
+                                      uint16_t* __restrict__ Bbd, int64_t nA, int64_t nB, int64_t idx8) {
+    const int64_t idx = idx8 * 8;
+    float f[8];
+    if (idx < nA) {
+        const int64_t row = idx / in_f, k = idx % in_f;
+        const int p = int(row / r), i = int(row % r);
+        const float4* src = reinterpret_cast<const float4*>(sg.A[p] + int64_t(i) * in_f + k);
+        const float4 u = src[0], v = src[1];
+        f[0] = u.x, f[1] = u.y, f[2] = u.z, f[3] = u.w, f[4] = v.x, f[5] = v.y, f[6] = v.z, f[7] = v.w;
+        *reinterpret_cast<uint4*>(Acat + idx) = pack8_bf16(f);
+        return;
+    }
+    const int64_t jdx = idx - nA;
+    if (jdx >= nB) return;
+    const int rr = sg.nseg * r;
+    const int n = int(jdx / rr), c = int(jdx % rr);
+    const int q = c / r, j = c % r;
+    int off = 0, p = 0;
+    while (p < sg.nseg - 1 && n >= off + sg.out[p]) off += sg.out[p++];
+    uint4 o = make_uint4(0, 0, 0, 0);
+    if (p == q) {
+        const float4* src = reinterpret_cast<const float4*>(sg.B[p] + int64_t(n - off) * r + j);
+        const float4 u = src[0], v = src[1];
+        f[0] = scale * u.x, f[1] = scale * u.y, f[2] = scale * u.z, f[3] = scale * u.w;
+        f[4] = scale * v.x, f[5] = scale * v.y, f[6] = scale * v.z, f[7] = scale * v.w;
+        o = pack8_bf16(f);
+    }
+    *reinterpret_cast<uint4*>(Bbd + jdx) = o;
+}
 __global__ void k_lora_pack(const LoraSegs sg, int r, int in_f, float scale, uint16_t* __restrict__ Acat,
                             uint16_t* __restrict__ Bbd, int64_t nA, int64_t nB, int ntot) {
     lora_pack_one(sg, r, in_f, scale, Acat, Bbd, nA, nB, int64_t(blockIdx.x) * blockDim.x + threadIdx.x);
@@ -276,10 +504,14 @@ struct LoraPackArgs {
     int64_t nA[4], nB[4];
 };
 // grid row y packs job y; rows past a job's size return at once
+template <bool VEC>
 __global__ void k_lora_pack_jobs(const LoraPackArgs a, int r, float scale) {
     const int y = blockIdx.y;
-    lora_pack_one(a.sg[y], r, a.in_f[y], scale, a.Acat[y], a.Bbd[y], a.nA[y], a.nB[y],
-                  int64_t(blockIdx.x) * blockDim.x + threadIdx.x);
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (VEC)
+        lora_pack_one8(a.sg[y], r, a.in_f[y], scale, a.Acat[y], a.Bbd[y], a.nA[y], a.nB[y], i);
+    else
+        lora_pack_one(a.sg[y], r, a.in_f[y], scale, a.Acat[y], a.Bbd[y], a.nA[y], a.nB[y], i);
 }
 void launch_lora_pack(const LoraSeg* segs, int nseg, int r, int in_f, float scale, uint16_t* Acat, uint16_t* Bbd,
                       hipStream_t s) {
@@ -305,6 +537,7 @@ void launch_lora_pack_jobs(const LoraPackJob* jobs, int njobs, int r, float scal
     LoraPackArgs a{};
     int64_t nmax = 0;
     double bytes = 0, elems = 0;
+    bool vec = r % 8 == 0;
     for (int y = 0; y < njobs; ++y) {
         const LoraPackJob& jb = jobs[y];
         int ntot = 0;
@@ -313,7 +546,9 @@ void launch_lora_pack_jobs(const LoraPackJob* jobs, int njobs, int r, float scal
             a.sg[y].B[p] = jb.segs[p].B;
             a.sg[y].out[p] = jb.segs[p].out_p;
             ntot += jb.segs[p].out_p;
+            vec = vec && al16(jb.segs[p].A) && al16(jb.segs[p].B);
         }
+        vec = vec && jb.in_f % 8 == 0 && al16(jb.Acat) && al16(jb.Bbd);
         a.sg[y].nseg = jb.nseg;
         a.in_f[y] = jb.in_f;
         a.Acat[y] = jb.Acat;
@@ -326,8 +561,12 @@ void launch_lora_pack_jobs(const LoraPackJob* jobs, int njobs, int r, float scal
     }
     if (nmax == 0) return;
     ProfScope prof("lora_pack", elems, bytes, s);
-    hipLaunchKernelGGL(k_lora_pack_jobs, dim3(unsigned((nmax + 255) / 256), unsigned(njobs)), dim3(256), 0, s, a, r,
-                       scale);
+    if (vec)
+        hipLaunchKernelGGL(k_lora_pack_jobs<true>, dim3(unsigned((nmax / 8 + 255) / 256), unsigned(njobs)), dim3(256), 0,
+                           s, a, r, scale);
+    else
+        hipLaunchKernelGGL(k_lora_pack_jobs<false>, dim3(unsigned((nmax + 255) / 256), unsigned(njobs)), dim3(256), 0,
+                           s, a, r, scale);
     check_launch("lora_pack");
 }
 

@@ -58,6 +58,20 @@ def test_tiny_layer_vs_oracle(batch, seq, random_gamma):
     assert not bad, (bad, res)
 
 
+@pytest.mark.parametrize("hidden,inter,r", [(1024, 2816, 8), (2048, 5464, 16), (3072, 8196, 12)])
+def test_mid_width_layer_vs_oracle(hidden, inter, r):
+    """Hidden sizes 1024, 2048 and 3072 (each register-resident RMSNorm width);
+    intermediate sizes that are (2816, 5464) and are not (8196) a multiple of
+    8, and LoRA ranks that are (8, 16) and are not (12): both paths of the
+    SwiGLU and adapter-packing kernels."""
+    import dataclasses
+    d = dataclasses.replace(synth.TINY, hidden=hidden, n_heads=hidden // 128, n_kv_heads=2, head_dim=128,
+                            inter=inter, n_layers=1, lora_r=r)
+    res = _run(d, 4, 1, 40, "normal")
+    bad = {k: v for k, v in res.items() if not v < TOL}
+    assert not bad, (bad, res)
+
+
 def test_llama8b_layer_vs_oracle():
     """One Llama-3.1-8B-shaped layer, batch 1, seq 512 (full size)."""
     res = _run(synth.LLAMA8B_LAYER, 2, 1, 512, "kaiming")
