@@ -86,10 +86,11 @@ def log(msg: str) -> None:
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def build_model(q, d, seed: int, want_device_blobs: bool = False):
+def build_model(q, d, seed: int, want_device_blobs: bool = False, wire: bool = False):
     """Quantize every layer's seeded bf16 weights on the GPU (nf4_quantize)
-    into a device blob and keep a pinned host copy. Host-side generation of
-    layer i+1 overlaps the GPU work of layer i."""
+    into a device blob and keep a pinned host copy (in the wire form, block
+    maxima as bf16, when wire=True). Host-side generation of layer i+1
+    overlaps the GPU work of layer i."""
     import numpy as np
     import torch
 
@@ -98,6 +99,7 @@ def build_model(q, d, seed: int, want_device_blobs: bool = False):
     _, total = q.binding.blob_layout(d)
     host, dev_blobs = [], []
     staging = torch.empty(total, dtype=torch.uint8, device=dev)
+    host_staging = torch.empty(total, dtype=torch.uint8, pin_memory=True) if wire else None
 
     def gen(layer):
         return {p: synth.proj_weight_bf16(d, seed, layer, p) for p in synth.PROJ_NAMES}
@@ -122,9 +124,9 @@ def build_model(q, d, seed: int, want_device_blobs: bool = False):
         g1, g2 = synth.norm_weights(d, seed, layer)
         blob = torch.empty(total, dtype=torch.uint8, device=dev) if want_device_blobs else staging
         q.binding.fill_blob(d, blob, w, torch.from_numpy(g1).to(dev), torch.from_numpy(g2).to(dev))
-        h = torch.empty(total, dtype=torch.uint8, pin_memory=True)
+        h = host_staging if wire else torch.empty(total, dtype=torch.uint8, pin_memory=True)
         h.copy_(blob)
-        host.append(h)
+        host.append(q.binding.blob_to_wire(d, h) if wire else h)
         if want_device_blobs:
             dev_blobs.append(blob)
         del w
@@ -138,7 +140,8 @@ def build_model(q, d, seed: int, want_device_blobs: bool = False):
     emb = torch.from_numpy(synth.embedding_f16(d, seed).view(np.int16)).view(torch.float16).to(dev)
     head = torch.from_numpy(synth.lm_head_f16(d, seed).view(np.int16)).view(torch.float16).to(dev)
     gf = torch.from_numpy(synth.final_norm_weight(d, seed)).to(dev)
-    m = q.StreamModel(d, host, emb, head, gf, loras)
+    m = q.StreamModel(d, host, emb, head, gf, loras,
+                      q.binding.QLX_BLOB_WIRE if wire else q.binding.QLX_BLOB_FULL)
     return m, dev_blobs
 
 
@@ -380,6 +383,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="sft8b_b1", choices=sorted(WORKLOADS))
     ap.add_argument("--mode", default="streamed", choices=["streamed", "resident"])
+    ap.add_argument("--blob-form", default="wire", choices=["wire", "full"],
+                    help="streamed layer blobs: wire = block maxima as bf16 (lossless for bf16 weights, "
+                         "widened on the GPU), full = fp32 maxima as the kernels read them")
     ap.add_argument("--source", default="ram", choices=["ram", "disk", "auto"],
                     help="where the streamed stack lives: pinned host RAM, a stack file read with O_DIRECT, or "
                          "RAM when it fits in available memory and the file otherwise")
@@ -443,7 +449,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     log(f"workload {args.workload}: {wl['name']} ({args.mode})")
     t0 = time.perf_counter()
-    m, dev_blobs = build_model(q, d, SEED, want_device_blobs=(args.mode == "resident"))
+    wire = args.mode == "streamed" and args.blob_form == "wire"
+    m, dev_blobs = build_model(q, d, SEED, want_device_blobs=(args.mode == "resident"), wire=wire)
     if args.mode == "resident":
         m = m.with_blobs(dev_blobs)
     log(f"model ready in {time.perf_counter() - t0:.1f} s")
@@ -451,7 +458,7 @@ def main() -> int:
     ctx = q.Context(0)
     source, layer_file, stack_path = "ram" if args.mode == "streamed" else "device", None, None
     if args.mode == "streamed" and args.source != "ram":
-        _, blob_bytes = B_.blob_layout(d)
+        _, blob_bytes = B_.wire_layout(d) if wire else B_.blob_layout(d)
         if args.source == "auto":
             mode = B_.stream_source_auto(d.n_layers * blob_bytes, reserve_bytes=8 << 30)
         else:
@@ -459,10 +466,10 @@ def main() -> int:
         if mode == B_.QLX_STREAMED_DISK:
             stack_path = args.stack_file or os.path.join(tempfile.gettempdir(), f"qlx_stack_{os.getpid()}.bin")
             t0 = time.perf_counter()
-            q.LayerFile.write(stack_path, d, m.blobs)
+            q.LayerFile.write(stack_path, d, m.blobs, wire=wire)
             log(f"stack file {stack_path}: {d.n_layers} x {blob_bytes / 1e6:.1f} MB written in "
                 f"{time.perf_counter() - t0:.1f} s")
-            layer_file = q.LayerFile(stack_path, d)
+            layer_file = q.LayerFile(stack_path, d, wire=wire)
             ctx.set_layer_source(layer_file)
             source = "disk (O_DIRECT)" if layer_file.info()["direct"] else "disk (page cache)"
         log(f"stream source: {source}")
@@ -559,7 +566,8 @@ def main() -> int:
         "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl["name"], "global_batch": batch if wl["kind"] == "sft" else 2 * batch,
-                   "seq_len": seq, "mode": args.mode, "source": source, "layers": d.n_layers,
+                   "seq_len": seq, "mode": args.mode, "source": source,
+                   "blob_form": "wire" if wire else "full", "layers": d.n_layers,
                    "lora_r": d.lora_r,
                    "optimizer": None if args.no_optimizer else f"adamw lr {LR}",
                    **({"dpo_reference": args.dpo_ref} if wl["kind"] in ("dpo", "kto") else {})},

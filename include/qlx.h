@@ -147,6 +147,24 @@ int qlora_linear_bwd(const uint16_t* dy, const uint16_t* x, int64_t T, qlx_nf4 W
 #define QLX_BLOB_NSEG 16
 int qlx_layer_blob_layout(const qlx_dims* d, uint64_t offsets[QLX_BLOB_NSEG], uint64_t* total_bytes);
 
+/* Wire form of a layer blob: what a streamed layer sends over the host link.
+ * The NF4 scheme keeps one fp32 maximum per 64-element block (rug.gal
+ * article, "En detalle"); for weights quantized from bf16 that maximum is
+ * itself a bf16 value, so its low 16 bits are zero and the wire form keeps
+ * only the upper 16. Layout: the packed regions at the full form's offsets
+ * (offsets[0..6]), then all block maxima as bf16, q..down back to back
+ * (offsets[7..13]), then g_attn and g_mlp fp32 (offsets[14], [15]), each
+ * region 256-byte aligned; 4.25 instead of 4.5 bits per weight. After the
+ * copy the library widens the maxima back to fp32 on the device, so the
+ * kernels see the full form bit for bit. */
+enum { QLX_BLOB_FULL = 0, QLX_BLOB_WIRE = 1 };
+int qlx_layer_wire_layout(const qlx_dims* d, uint64_t offsets[QLX_BLOB_NSEG], uint64_t* total_bytes);
+/* Converts a full-form blob to the wire form (both HOST, any alignment;
+ * wire holds the wire layout's total_bytes). QLX_EINVAL, with wire left
+ * untouched, if a block maximum has any of its low 16 bits set (weights that
+ * were not bf16). */
+int qlx_layer_blob_to_wire(const qlx_dims* d, const void* blob, void* wire);
+
 /* LoRA adapters of one layer (fp32, device): A[p] [r, in_p], B[p] [out_p, r]
  * for p = q,k,v,o,gate,up,down. */
 typedef struct { const float* A[7]; const float* B[7]; } qlx_lora;
@@ -219,20 +237,26 @@ int qlx_ctx_set_debug(qlx_ctx* ctx, int flags, int delay_us);
  * `stream_source: auto` setting, RAM when the stack fits and the NVMe disk
  * when it does not).
  * A layer file holds the n_layers blobs of a model, blob i at byte offset
- * i * stride, stride = the blob size (qlx_layer_blob_layout) rounded up to
- * 4096, zero padded. Reads use O_DIRECT (no page cache) unless the file
+ * i * stride, stride = the blob size (qlx_layer_blob_layout, or
+ * qlx_layer_wire_layout for a file of wire-form blobs) rounded up to 4096,
+ * zero padded. Reads use O_DIRECT (no page cache) unless the file
  * system refuses it or QLX_FILE_BUFFERED is given; reader threads (16, or
  * the environment variable QLX_FILE_READERS at open, 1..64) keep several
  * 8 MiB reads in flight. A file serves one context at a time. */
 typedef struct qlx_layer_file qlx_layer_file;
-enum { QLX_FILE_BUFFERED = 1 };  /* qlx_layer_file_open: read through the page cache */
+enum {
+    QLX_FILE_BUFFERED = 1, /* qlx_layer_file_open: read through the page cache */
+    QLX_FILE_WIRE = 2      /* the file holds wire-form blobs (write and open) */
+};
 
 /* Writes the stack file: blobs = HOST array of n_layers HOST pointers (any
- * host memory) to blobs laid out as qlx_layer_blob_layout says. Creates or
+ * host memory) to blobs laid out as qlx_layer_blob_layout says, or as
+ * qlx_layer_wire_layout says with flags = QLX_FILE_WIRE. Creates or
  * truncates path; fsyncs before returning. */
-int qlx_layer_file_write(const char* path, const qlx_dims* d, const void* const* blobs);
+int qlx_layer_file_write(const char* path, const qlx_dims* d, const void* const* blobs, int flags);
 /* Opens a stack file for the model dims d; QLX_EIO if it is missing or
- * shorter than n_layers * stride. flags: 0 or QLX_FILE_BUFFERED. */
+ * shorter than n_layers * stride. flags: QLX_FILE_BUFFERED and/or
+ * QLX_FILE_WIRE (as the file was written). */
 int qlx_layer_file_open(qlx_layer_file** out, const char* path, const qlx_dims* d, int flags);
 /* Waits for copies still reading its staging buffers, then frees it. NULL is
  * a no-op. QLX_EINVAL (and nothing freed) while a context still holds it:
@@ -241,7 +265,8 @@ int qlx_layer_file_open(qlx_layer_file** out, const char* path, const qlx_dims* 
 int qlx_layer_file_close(qlx_layer_file* f);
 /* *direct (HOST) = 1 if reads bypass the page cache; *stride = blob stride. */
 int qlx_layer_file_info(const qlx_layer_file* f, int* direct, uint64_t* stride);
-/* Reads layer i's blob into dst (HOST, blob-size bytes, any alignment). */
+/* Reads layer i's blob into dst (HOST, the size of one blob of the file's form, any
+ * alignment). */
 int qlx_layer_file_read(qlx_layer_file* f, int layer, void* dst);
 /* Attaches f (NULL detaches) as the context's source for QLX_STREAMED_DISK.
  * The first attach allocates two pinned staging buffers of one stride each
@@ -260,7 +285,9 @@ int qlx_stream_source_auto(uint64_t stack_bytes, uint64_t reserve_bytes, int* mo
  *   not read (may be NULL) and the layers come from the context's layer file,
  *   disk -> pinned staging -> device slot, with the same bits.
  * embed_f16, lm_head_f16: DEVICE fp16 [vocab, hidden] (untied, frozen).
- * final_norm: DEVICE fp32 [hidden]. lora: HOST array of n_layers qlx_lora. */
+ * final_norm: DEVICE fp32 [hidden]. lora: HOST array of n_layers qlx_lora.
+ * blob_form: QLX_BLOB_FULL, or QLX_BLOB_WIRE for QLX_STREAMED host blobs in
+ *   the wire form (QLX_STREAMED_DISK takes the form from the layer file). */
 typedef struct {
     qlx_dims dims;
     const void* const* layer_blobs;
@@ -268,11 +295,14 @@ typedef struct {
     const uint16_t* lm_head_f16;
     const float* final_norm;
     const qlx_lora* lora;
+    int blob_form;
 } qlx_model;
 
-/* Workspace of a step: two device slots of one layer blob each (streamed
- * mode), n_layers+1 fp32 layer-boundary checkpoints, one layer's workspace
- * and the LM-head logits [T, vocab] fp32. kind: 0 = SFT (batch = sequences),
+/* Workspace of a step: two device slots of one full-form layer blob each
+ * plus room for a wire-form tail (streamed modes), n_layers+1 fp32
+ * layer-boundary checkpoints, one layer's workspace, the LM head's per-row
+ * partials [T, vocab/64] (max and sum of exponentials, fp32) and one
+ * vocabulary chunk of fp16 logit gradients [T, 16384]. kind: 0 = SFT (batch = sequences),
  * 1 = DPO, ORPO or SimPO, 2 = KTO (batch = pairs; T = 2*pairs*seq; KTO adds
  * the mismatched pairs' tokens, two more fp32 hidden-state streams and
  * their CE statistics). */

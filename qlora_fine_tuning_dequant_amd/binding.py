@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlx.so")
 QLX_OK, QLX_EINVAL, QLX_EUNSUPPORTED, QLX_EWORKSPACE, QLX_ENOTPINNED, QLX_EHIP, QLX_EIO = range(7)
 QLX_F32, QLX_BF16 = 0, 1
 QLX_STREAMED, QLX_RESIDENT, QLX_STREAMED_DISK = 0, 1, 2
-QLX_FILE_BUFFERED = 1
+QLX_FILE_BUFFERED, QLX_FILE_WIRE = 1, 2
+QLX_BLOB_FULL, QLX_BLOB_WIRE = 0, 1
 QLX_DEBUG_SERIALIZE, QLX_DEBUG_POISON, QLX_DEBUG_DELAY_COPY, QLX_DEBUG_DELAY_COMPUTE, QLX_DEBUG_POISON_LIVE = (
     1, 2, 4, 8, 16)
 QLX_DPO_REF_FUSED, QLX_DPO_REF_SEPARATE = 0, 1
@@ -39,7 +40,7 @@ EXPORTED = (
     "qlx_step_workspace_bytes", "stream_step_sft", "stream_step_dpo", "stream_step_pref", "qlx_merge_workspace_bytes", "qlx_lora_merge", "qlx_profile_begin", "qlx_profile_begin_prefix", "qlx_profile_end", "qlx_adamw_lora",
     "qlx_layer_file_write", "qlx_layer_file_open", "qlx_layer_file_close", "qlx_layer_file_info",
     "qlx_layer_file_read", "qlx_ctx_set_layer_source", "qlx_stream_source_auto", "qlx_ctx_set_debug",
-    "qlx_peak_mfma", "qlx_peak_copy",
+    "qlx_peak_mfma", "qlx_peak_copy", "qlx_layer_wire_layout", "qlx_layer_blob_to_wire",
 )
 
 
@@ -101,7 +102,8 @@ class KernelProf(C.Structure):
 
 class Model(C.Structure):
     _fields_ = [("dims", Dims), ("layer_blobs", C.POINTER(C.c_void_p)), ("embed_f16", C.c_void_p),
-                ("lm_head_f16", C.c_void_p), ("final_norm", C.c_void_p), ("lora", C.POINTER(Lora))]
+                ("lm_head_f16", C.c_void_p), ("final_norm", C.c_void_p), ("lora", C.POINTER(Lora)),
+                ("blob_form", C.c_int)]
 
 
 _lib = None
@@ -125,6 +127,8 @@ def lib() -> C.CDLL:
         "qlora_linear_fwd": (i32, [vp, i64, NF4, vp, vp, i32, f32, vp, vp, sz, vp]),
         "qlora_linear_bwd": (i32, [vp, vp, i64, NF4, vp, vp, i32, f32, vp, vp, vp, i32, vp, sz, vp]),
         "qlx_layer_blob_layout": (i32, [C.POINTER(Dims), C.POINTER(C.c_uint64), C.POINTER(C.c_uint64)]),
+        "qlx_layer_wire_layout": (i32, [C.POINTER(Dims), C.POINTER(C.c_uint64), C.POINTER(C.c_uint64)]),
+        "qlx_layer_blob_to_wire": (i32, [C.POINTER(Dims), vp, vp]),
         "qlx_layer_workspace_bytes": (sz, [C.POINTER(Dims), i32, i32]),
         "layer_fwd": (i32, [C.POINTER(Dims), vp, C.POINTER(Lora), vp, i32, i32, vp, vp, sz, vp]),
         "layer_bwd": (i32, [C.POINTER(Dims), vp, C.POINTER(Lora), vp, vp, i32, i32, vp, C.POINTER(LoraGrad),
@@ -145,7 +149,7 @@ def lib() -> C.CDLL:
         "qlx_adamw_lora": (i32, [C.POINTER(Dims), C.POINTER(LoraBuf), C.POINTER(LoraGrad), C.POINTER(LoraBuf),
                                  C.POINTER(LoraBuf), C.c_int64, C.POINTER(AdamwCfg), C.c_void_p]),
         "qlx_profile_end": (i32, [C.POINTER(KernelProf), i32, C.POINTER(C.c_int)]),
-        "qlx_layer_file_write": (i32, [C.c_char_p, C.POINTER(Dims), C.POINTER(C.c_void_p)]),
+        "qlx_layer_file_write": (i32, [C.c_char_p, C.POINTER(Dims), C.POINTER(C.c_void_p), i32]),
         "qlx_layer_file_open": (i32, [C.POINTER(vp), C.c_char_p, C.POINTER(Dims), i32]),
         "qlx_layer_file_close": (i32, [vp]),
         "qlx_layer_file_info": (i32, [vp, C.POINTER(C.c_int), C.POINTER(C.c_uint64)]),
@@ -283,6 +287,27 @@ def blob_layout(dims) -> tuple[list[int], int]:
     total = C.c_uint64()
     _check(lib().qlx_layer_blob_layout(C.byref(d), offs, C.byref(total)))
     return list(offs), int(total.value)
+
+
+def wire_layout(dims) -> tuple[list[int], int]:
+    """Offsets and size of the wire form of a layer blob (block maxima as bf16)."""
+    d = Dims.of(dims)
+    offs = (C.c_uint64 * BLOB_NSEG)()
+    total = C.c_uint64()
+    _check(lib().qlx_layer_wire_layout(C.byref(d), offs, C.byref(total)))
+    return list(offs), int(total.value)
+
+
+def blob_to_wire(dims, blob: torch.Tensor, pin_memory: bool = True) -> torch.Tensor:
+    """Host full-form blob -> new host uint8 tensor in the wire form (pinned
+    by default); raises QlxError if a block maximum is not a bf16 value."""
+    if blob.is_cuda:
+        raise ValueError("blob_to_wire converts host blobs")
+    d = Dims.of(dims)
+    _, total = wire_layout(d)
+    out = torch.empty(total, dtype=torch.uint8, pin_memory=pin_memory)
+    _check(lib().qlx_layer_blob_to_wire(C.byref(d), _ptr(blob), _ptr(out)))
+    return out
 
 
 def fill_blob(dims, blob: torch.Tensor, weights_bf16: dict, g1: torch.Tensor, g2: torch.Tensor,
@@ -426,8 +451,9 @@ class LayerFile:
     refuses it."""
 
     @staticmethod
-    def write(path: str, dims, blobs: Sequence) -> None:
-        """blobs: host buffers (uint8 tensors or numpy arrays) of one layer blob each."""
+    def write(path: str, dims, blobs: Sequence, wire: bool = False) -> None:
+        """blobs: host buffers (uint8 tensors or numpy arrays) of one layer blob
+        each, in the wire form when wire=True."""
         d = Dims.of(dims)
         ptrs = [b.data_ptr() if isinstance(b, torch.Tensor) else b.ctypes.data for b in blobs]
         if len(ptrs) != d.n_layers:
@@ -436,13 +462,15 @@ class LayerFile:
             if isinstance(b, torch.Tensor) and b.is_cuda:
                 raise ValueError("layer blobs for the file must be host memory")
         arr = (C.c_void_p * len(ptrs))(*ptrs)
-        _check(lib().qlx_layer_file_write(os.fsencode(path), C.byref(d), C.cast(arr, C.POINTER(C.c_void_p))))
+        _check(lib().qlx_layer_file_write(os.fsencode(path), C.byref(d), C.cast(arr, C.POINTER(C.c_void_p)),
+                                          QLX_FILE_WIRE if wire else 0))
 
-    def __init__(self, path: str, dims, buffered: bool = False):
+    def __init__(self, path: str, dims, buffered: bool = False, wire: bool = False):
         self.dims = Dims.of(dims)
+        self.wire = wire
         h = C.c_void_p()
         _check(lib().qlx_layer_file_open(C.byref(h), os.fsencode(path), C.byref(self.dims),
-                                         QLX_FILE_BUFFERED if buffered else 0))
+                                         (QLX_FILE_BUFFERED if buffered else 0) | (QLX_FILE_WIRE if wire else 0)))
         self.h = h
         self.path = path
 
@@ -479,12 +507,15 @@ def stream_source_auto(stack_bytes: int, reserve_bytes: int = 0) -> int:
 class StreamModel:
     """Holds the tensors of a model and the C struct pointing at them.
     blobs: pinned host uint8 tensors (streamed) or device uint8 tensors
-    (resident); None for a model that only streams from a layer file."""
+    (resident); None for a model that only streams from a layer file.
+    blob_form: QLX_BLOB_FULL, or QLX_BLOB_WIRE for streamed host blobs made
+    by blob_to_wire."""
 
     def __init__(self, dims, blobs: Sequence[torch.Tensor] | None, embed_f16: torch.Tensor, head_f16: torch.Tensor,
-                 final_norm: torch.Tensor, lora: Sequence[LoraLayer]):
+                 final_norm: torch.Tensor, lora: Sequence[LoraLayer], blob_form: int = QLX_BLOB_FULL):
         self.dims = Dims.of(dims)
-        _, total = blob_layout(self.dims)
+        self.blob_form = blob_form
+        _, total = wire_layout(self.dims) if blob_form == QLX_BLOB_WIRE else blob_layout(self.dims)
         for bl in blobs or ():
             if bl.numel() * bl.element_size() < total:
                 raise ValueError(f"layer blob holds {bl.numel() * bl.element_size()} bytes, layout needs {total}")
@@ -497,10 +528,10 @@ class StreamModel:
             self._blob_arr, blob_ptr = None, None
         self._lora_arr = (Lora * len(self.lora))(*[l.c() for l in self.lora])
         self.c = Model(self.dims, blob_ptr, _ptr(embed_f16), _ptr(head_f16),
-                       _ptr(final_norm), C.cast(self._lora_arr, C.POINTER(Lora)))
+                       _ptr(final_norm), C.cast(self._lora_arr, C.POINTER(Lora)), blob_form)
 
-    def with_blobs(self, blobs: Sequence[torch.Tensor]) -> "StreamModel":
-        return StreamModel(self.dims, blobs, self.embed, self.head, self.final_norm, self.lora)
+    def with_blobs(self, blobs: Sequence[torch.Tensor], blob_form: int = QLX_BLOB_FULL) -> "StreamModel":
+        return StreamModel(self.dims, blobs, self.embed, self.head, self.final_norm, self.lora, blob_form)
 
 
 def step_workspace_bytes(dims, kind: int, batch: int, seq: int) -> int:

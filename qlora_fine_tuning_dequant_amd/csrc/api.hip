@@ -274,6 +274,48 @@ int qlx_layer_blob_layout(const qlx_dims* d, uint64_t offsets[QLX_BLOB_NSEG], ui
     });
 }
 
+int qlx_layer_wire_layout(const qlx_dims* d, uint64_t offsets[QLX_BLOB_NSEG], uint64_t* total_bytes) {
+    return guarded([&] {
+        validate_dims(d);
+        REQ_PTR(offsets, "offsets");
+        REQ_PTR(total_bytes, "total_bytes");
+        wire_layout(*d, offsets, total_bytes);
+    });
+}
+
+int qlx_layer_blob_to_wire(const qlx_dims* d, const void* blob, void* wire) {
+    return guarded([&] {
+        validate_dims(d);
+        REQ_PTR(blob, "blob");
+        REQ_PTR(wire, "wire");
+        uint64_t fo[QLX_BLOB_NSEG], wo[QLX_BLOB_NSEG], ft, wt;
+        blob_layout(*d, fo, &ft);
+        wire_layout(*d, wo, &wt);
+        const char* b = static_cast<const char*>(blob);
+        char* w = static_cast<char*>(wire);
+        const uint64_t nb = absmax_blocks(*d);
+        // check every maximum first, so a refused blob leaves `wire` untouched
+        for (uint64_t i = 0; i < nb; ++i) {
+            uint32_t v;
+            std::memcpy(&v, b + fo[7] + 4 * i, 4);
+            QLX_REQUIRE((v & 0xFFFFu) == 0, QLX_EINVAL,
+                        "block maximum " + std::to_string(i) +
+                            " is not a bf16 value (its low 16 bits are set): the wire form holds blobs quantized "
+                            "from bf16 weights");
+        }
+        std::memset(w, 0, size_t(wt));
+        std::memcpy(w, b, size_t(fo[7]));  // packed regions, same offsets
+        for (uint64_t i = 0; i < nb; ++i) {
+            uint32_t v;
+            std::memcpy(&v, b + fo[7] + 4 * i, 4);
+            const uint16_t hi = uint16_t(v >> 16);
+            std::memcpy(w + wo[7] + 2 * i, &hi, 2);
+        }
+        std::memcpy(w + wo[14], b + fo[14], size_t(d->hidden) * 4);
+        std::memcpy(w + wo[15], b + fo[15], size_t(d->hidden) * 4);
+    });
+}
+
 size_t qlx_layer_workspace_bytes(const qlx_dims* d, int batch, int seq) {
     if (!d || batch <= 0 || seq <= 0) return 0;
     return layer_ws_bytes(make_geom(*d, batch, seq));
@@ -376,12 +418,21 @@ struct StepWs {
     float *kl_lse, *kl_pk, *kl_lse_r, *kl_pk_r;
 };
 
+static uint64_t wire_tail_bytes(const qlx_dims& d) {
+    uint64_t off[QLX_BLOB_NSEG], total;
+    wire_layout(d, off, &total);
+    return total - off[7];
+}
+
 static StepWs carve_step(Carver& c, const qlx_dims& d, int T, int kind, uint64_t blob_bytes) {
     StepWs w{};
     const LayerGeom g = make_geom(d, 1, T);  // only H, V needed here
     const size_t H = size_t(d.hidden), V = size_t(d.vocab), L = size_t(d.n_layers), Tz = size_t(T);
-    w.slot[0] = c.take<char>(blob_bytes);
-    w.slot[1] = c.take<char>(blob_bytes);
+    // a slot: the full-form blob, then room for a wire-form tail (block
+    // maxima as bf16 and the gains) that the widen kernel expands in place
+    const uint64_t slot_bytes = blob_bytes + wire_tail_bytes(d);
+    w.slot[0] = c.take<char>(slot_bytes);
+    w.slot[1] = c.take<char>(slot_bytes);
     w.ckpt = c.take<float>((L + 1) * Tz * H);
     if (kind >= 1) {
         w.href[0] = c.take<float>(Tz * H);
@@ -432,6 +483,10 @@ class Streamer {
     Streamer(qlx_ctx* ctx, const qlx_model* m, int mode, const StepWs& w, uint64_t blob_bytes, hipStream_t main)
         : ctx_(ctx), m_(m), mode_(mode), w_(w), bytes_(blob_bytes), main_(main) {
         held_[0] = held_[1] = -1;
+        form_ = mode == QLX_STREAMED_DISK ? ctx->source->form : mode == QLX_STREAMED ? m->blob_form : QLX_BLOB_FULL;
+        blob_layout(m->dims, full_, &bytes_);
+        wire_layout(m->dims, wire_, &wire_bytes_);
+        nblocks_ = int64_t(absmax_blocks(m->dims));
     }
     // Make layer i resident (if not already), wait for it on the main stream,
     // and return its device pointer. prefetch_next >= 0 also starts the copy
@@ -483,23 +538,35 @@ class Streamer {
         // debugging: a freed slot is filled with NaN bytes before it is
         // refilled (a read of it after its release would show as NaN), and a
         // spin shifts the copy against the compute
+        const bool wire = form_ == QLX_BLOB_WIRE;
+        const uint64_t nbytes = wire ? wire_bytes_ : bytes_;  // bytes that cross the link
         if (ctx_->debug & QLX_DEBUG_POISON)
-            launch_fill_u32(reinterpret_cast<uint32_t*>(w_.slot[sl]), int64_t(bytes_ / 4), 0xFFFFFFFFu, ctx_->side);
+            launch_fill_u32(reinterpret_cast<uint32_t*>(w_.slot[sl]), int64_t((bytes_ + wire_bytes_ - wire_[7]) / 4),
+                            0xFFFFFFFFu, ctx_->side);
         if (ctx_->debug & QLX_DEBUG_DELAY_COPY) launch_spin(ctx_->delay_us, ctx_->side);
         hipEvent_t* ev = next_timing_pair();
         if (ev) QLX_CHECK_HIP(hipEventRecord(ev[0], ctx_->side));
-        if (ctx_->copy_split == 2 && bytes_ > 8192) {
+        const char* s8 = static_cast<const char*>(src);
+        if (ctx_->copy_split == 2 && nbytes > 8192) {
             // the two halves on two streams, so two copy engines share the link
-            const uint64_t h = (bytes_ / 2 + 4095) & ~uint64_t(4095);
+            const uint64_t h = (nbytes / 2 + 4095) & ~uint64_t(4095);
             QLX_CHECK_HIP(hipEventRecord(ctx_->copy_start, ctx_->side));
             QLX_CHECK_HIP(hipStreamWaitEvent(ctx_->side2, ctx_->copy_start, 0));
-            QLX_CHECK_HIP(hipMemcpyAsync(w_.slot[sl] + h, static_cast<const char*>(src) + h, bytes_ - h,
-                                         hipMemcpyHostToDevice, ctx_->side2));
+            put(s8, h, nbytes, w_.slot[sl], ctx_->side2);
             QLX_CHECK_HIP(hipEventRecord(ctx_->half_done, ctx_->side2));
-            QLX_CHECK_HIP(hipMemcpyAsync(w_.slot[sl], src, h, hipMemcpyHostToDevice, ctx_->side));
+            put(s8, 0, h, w_.slot[sl], ctx_->side);
             QLX_CHECK_HIP(hipStreamWaitEvent(ctx_->side, ctx_->half_done, 0));
         } else {
-            QLX_CHECK_HIP(hipMemcpyAsync(w_.slot[sl], src, bytes_, hipMemcpyHostToDevice, ctx_->side));
+            put(s8, 0, nbytes, w_.slot[sl], ctx_->side);
+        }
+        if (wire) {  // maxima bf16 -> fp32 and the gains into their full-form places
+            char* b = w_.slot[sl];
+            char* tail = b + bytes_;  // wire offset wire_[7] landed here
+            launch_blob_widen(reinterpret_cast<const uint16_t*>(tail), nblocks_,
+                              reinterpret_cast<const float*>(tail + (wire_[14] - wire_[7])),
+                              reinterpret_cast<const float*>(tail + (wire_[15] - wire_[7])), m_->dims.hidden,
+                              reinterpret_cast<uint32_t*>(b + full_[7]), reinterpret_cast<float*>(b + full_[14]),
+                              reinterpret_cast<float*>(b + full_[15]), ctx_->side);
         }
         if (ev) QLX_CHECK_HIP(hipEventRecord(ev[1], ctx_->side));
         if (k >= 0) QLX_CHECK_HIP(hipEventRecord(f->staging_free[k], ctx_->side));
@@ -509,7 +576,18 @@ class Streamer {
         if (ctx_->debug & QLX_DEBUG_SERIALIZE) QLX_CHECK_HIP(hipStreamSynchronize(ctx_->side));
         held_[sl] = i;
         ctx_->stats.layer_reads += 1;
-        ctx_->stats.h2d_bytes += int64_t(bytes_);
+        ctx_->stats.h2d_bytes += int64_t(nbytes);
+    }
+    // Copies bytes [lo, hi) of a layer's source blob to their place in slot
+    // `dst`: the full form is copied as is; in the wire form the packed
+    // regions (before wire_[7]) keep their offsets and the tail lands after
+    // the full-form blob, where the widen kernel reads it.
+    void put(const char* src, uint64_t lo, uint64_t hi, char* dst, hipStream_t st) {
+        const uint64_t P = form_ == QLX_BLOB_WIRE ? wire_[7] : hi;
+        if (lo < std::min(hi, P))
+            QLX_CHECK_HIP(hipMemcpyAsync(dst + lo, src + lo, std::min(hi, P) - lo, hipMemcpyHostToDevice, st));
+        const uint64_t a = std::max(lo, P);
+        if (a < hi) QLX_CHECK_HIP(hipMemcpyAsync(dst + bytes_ + (a - P), src + a, hi - a, hipMemcpyHostToDevice, st));
     }
     hipEvent_t* next_timing_pair() {
         if (ctx_->copies_used + 2 > ctx_->copy_ev.size()) return nullptr;
@@ -521,9 +599,12 @@ class Streamer {
     const qlx_model* m_;
     int mode_;
     const StepWs& w_;
-    uint64_t bytes_;
+    uint64_t bytes_;  // full-form blob
     hipStream_t main_;
     int held_[2];
+    int form_ = QLX_BLOB_FULL;
+    uint64_t full_[QLX_BLOB_NSEG] = {}, wire_[QLX_BLOB_NSEG] = {}, wire_bytes_ = 0;
+    int64_t nblocks_ = 0;
 };
 
 static void validate_model(qlx_ctx* ctx, const qlx_model* m, int mode) {
@@ -536,11 +617,14 @@ static void validate_model(qlx_ctx* ctx, const qlx_model* m, int mode) {
         const qlx_layer_file* f = ctx->source;
         QLX_REQUIRE(f != nullptr, QLX_EINVAL, "QLX_STREAMED_DISK needs a layer file attached to the context");
         uint64_t off[QLX_BLOB_NSEG], blob_bytes = 0;
-        blob_layout(m->dims, off, &blob_bytes);
+        if (f->form == QLX_BLOB_WIRE) wire_layout(m->dims, off, &blob_bytes);
+        else blob_layout(m->dims, off, &blob_bytes);
         QLX_REQUIRE(f->dims.n_layers == m->dims.n_layers && f->blob_bytes == blob_bytes, QLX_EINVAL,
                     "the context's layer file was opened for other model dims");
     } else {
         REQ_PTR(m->layer_blobs, "model.layer_blobs");
+        QLX_REQUIRE(m->blob_form == QLX_BLOB_FULL || (m->blob_form == QLX_BLOB_WIRE && mode == QLX_STREAMED),
+                    QLX_EINVAL, "model.blob_form: QLX_BLOB_FULL, or QLX_BLOB_WIRE with QLX_STREAMED");
     }
     REQ_PTR(m->embed_f16, "model.embed_f16");
     REQ_PTR(m->lm_head_f16, "model.lm_head_f16");

@@ -420,6 +420,44 @@ void launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s) {
     hipLaunchKernelGGL(k_fill_u32, dim3(unsigned(blocks)), dim3(256), 0, s, p, n, v);
     check_launch("fill_u32");
 }
+// Wire form -> full form of a layer blob's tail in device memory: each block
+// maximum's bf16 bits become the upper half of its fp32 word (exact: the
+// maxima of bf16 weights are bf16 values) and the two RMSNorm gains are
+// copied. Threads [0, ceil(nb/4)) take four maxima each, the next H threads
+// one element of each gain.
+__global__ void k_blob_widen(const uint16_t* __restrict__ m16, int64_t nb, const float* __restrict__ g1s,
+                             const float* __restrict__ g2s, int H, uint32_t* __restrict__ m32,
+                             float* __restrict__ g1d, float* __restrict__ g2d) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t n4 = (nb + 3) / 4;
+    if (i < n4) {
+        const int64_t j = i * 4;
+        if (j + 4 <= nb) {
+            const uint2 v = *reinterpret_cast<const uint2*>(m16 + j);
+            *reinterpret_cast<uint4*>(m32 + j) = make_uint4(v.x << 16, v.x & 0xFFFF0000u, v.y << 16, v.y & 0xFFFF0000u);
+        } else {
+            for (int64_t k = j; k < nb; ++k) m32[k] = uint32_t(m16[k]) << 16;
+        }
+        return;
+    }
+    const int64_t k = i - n4;
+    if (k < H) {
+        g1d[k] = g1s[k];
+        g2d[k] = g2s[k];
+    }
+}
+void launch_blob_widen(const uint16_t* m16, int64_t nb, const float* g1s, const float* g2s, int H, uint32_t* m32,
+                       float* g1d, float* g2d, hipStream_t s) {
+    QLX_REQUIRE((reinterpret_cast<uintptr_t>(m16) & 7) == 0 && al16(m32), QLX_EINVAL,
+                "blob widen: maxima must be 8-byte (source) and 16-byte (destination) aligned");
+    const int64_t threads = (nb + 3) / 4 + H;
+    if (threads <= 0) return;
+    ProfScope prof("blob_widen", 0.0, 6.0 * double(nb) + 16.0 * H, s);
+    hipLaunchKernelGGL(k_blob_widen, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, m16, nb, g1s, g2s, H, m32,
+                       g1d, g2d);
+    check_launch("blob_widen");
+}
+
 // Occupies its stream for about `sleeps` x 8k cycles (a fixed count of
 // s_sleep 127, so it always ends): shifts when the next operation starts.
 __global__ void k_spin(int sleeps) {

@@ -41,6 +41,11 @@ struct LayerWs {
 LayerGeom make_geom(const qlx_dims& d, int batch, int seq);
 void validate_dims(const qlx_dims* d);
 void blob_layout(const qlx_dims& d, uint64_t off[QLX_BLOB_NSEG], uint64_t* total);
+// Wire form of a layer blob (block maxima as bf16; offsets as in blob_layout,
+// [7..13] pointing at bf16 arrays). The packed regions sit at the same offsets
+// in both forms and end where the wire form's maxima begin (off[7]).
+void wire_layout(const qlx_dims& d, uint64_t off[QLX_BLOB_NSEG], uint64_t* total);
+uint64_t absmax_blocks(const qlx_dims& d);  // NF4 blocks in one layer
 BlobPtrs blob_ptrs(const qlx_dims& d, const void* blob);
 LayerWs carve_layer(Carver& c, const LayerGeom& g);
 size_t layer_ws_bytes(const LayerGeom& g);

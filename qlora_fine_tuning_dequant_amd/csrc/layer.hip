@@ -86,6 +86,35 @@ void blob_layout(const qlx_dims& d, uint64_t off[QLX_BLOB_NSEG], uint64_t* total
     *total = o;
 }
 
+// Wire form: the packed regions exactly as above, then every block maximum
+// as its upper 16 bits (bf16) back to back, then the two gains. Block maxima
+// of bf16 weights are bf16 values, so the low 16 bits dropped are zero.
+void wire_layout(const qlx_dims& d, uint64_t off[QLX_BLOB_NSEG], uint64_t* total) {
+    const LayerGeom g = make_geom(d, 1, 1);
+    auto al = [](uint64_t x) { return (x + 255) & ~uint64_t(255); };
+    uint64_t full[QLX_BLOB_NSEG], ftotal;
+    blob_layout(d, full, &ftotal);
+    uint64_t o = full[7];
+    for (int p = 0; p < 7; ++p) {
+        off[p] = full[p];
+        off[7 + p] = o;
+        o += uint64_t(g.nel[p] / 64) * 2;
+    }
+    o = al(o);
+    off[14] = o;
+    o = al(o + uint64_t(g.H) * 4);
+    off[15] = o;
+    o = al(o + uint64_t(g.H) * 4);
+    *total = o;
+}
+
+uint64_t absmax_blocks(const qlx_dims& d) {
+    const LayerGeom g = make_geom(d, 1, 1);
+    uint64_t nb = 0;
+    for (int p = 0; p < 7; ++p) nb += uint64_t(g.nel[p] / 64);
+    return nb;
+}
+
 BlobPtrs blob_ptrs(const qlx_dims& d, const void* blob) {
     uint64_t off[QLX_BLOB_NSEG], total;
     blob_layout(d, off, &total);

@@ -187,6 +187,10 @@ void launch_swiglu_bwd(const uint16_t* dact, const uint16_t* gu, int T, int I, u
 void launch_embed(const int32_t* tok, const uint16_t* E, int T, int H, int V, float* h, hipStream_t s);
 void launch_f32_to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s);
 void launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
+// Layer blob wire form -> full form on the device: m32[i] = m16[i] << 16 for
+// the nb block maxima; g1d/g2d = g1s/g2s (H floats each).
+void launch_blob_widen(const uint16_t* m16, int64_t nb, const float* g1s, const float* g2s, int H, uint32_t* m32,
+                       float* g1d, float* g2d, hipStream_t s);
 
 // Flash-style causal GQA attention over q|k|v packed per token row.
 struct AttnArgs {

@@ -22,6 +22,7 @@ struct qlx_layer_file {
     int fd = -1;
     bool direct = false;  // O_DIRECT: reads bypass the page cache
     qlx_dims dims{};
+    int form = 0;  // QLX_BLOB_FULL or QLX_BLOB_WIRE
     uint64_t blob_bytes = 0, stride = 0;
 
     // reader pool: a layer read is split into kReadChunk jobs

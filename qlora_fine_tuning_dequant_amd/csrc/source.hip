@@ -88,9 +88,10 @@ void layer_file_read(qlx_layer_file* f, int layer, void* dst) {
     QLX_REQUIRE(!f->short_read, QLX_EIO, "reading layer " + std::to_string(layer) + " of " + f->path + ": file ends early");
 }
 
-static uint64_t stride_of(const qlx_dims& d, uint64_t* blob_bytes) {
+static uint64_t stride_of(const qlx_dims& d, int form, uint64_t* blob_bytes) {
     uint64_t off[QLX_BLOB_NSEG];
-    blob_layout(d, off, blob_bytes);
+    if (form == QLX_BLOB_WIRE) wire_layout(d, off, blob_bytes);
+    else blob_layout(d, off, blob_bytes);
     return (*blob_bytes + kFileAlign - 1) / kFileAlign * kFileAlign;
 }
 
@@ -121,13 +122,14 @@ using namespace qlx;
 
 extern "C" {
 
-int qlx_layer_file_write(const char* path, const qlx_dims* d, const void* const* blobs) {
+int qlx_layer_file_write(const char* path, const qlx_dims* d, const void* const* blobs, int flags) {
     return guarded([&] {
         REQ_PTR(path, "path");
         REQ_PTR(blobs, "blobs");
         validate_dims(d);
+        QLX_REQUIRE((flags & ~QLX_FILE_WIRE) == 0, QLX_EINVAL, "layer-file write flags: 0 or QLX_FILE_WIRE");
         uint64_t blob_bytes = 0;
-        const uint64_t stride = stride_of(*d, &blob_bytes);
+        const uint64_t stride = stride_of(*d, (flags & QLX_FILE_WIRE) ? QLX_BLOB_WIRE : QLX_BLOB_FULL, &blob_bytes);
         for (int i = 0; i < d->n_layers; ++i)
             QLX_REQUIRE(blobs[i] != nullptr, QLX_EINVAL, "blobs[" + std::to_string(i) + "] is NULL");
         const int fd = open(path, O_WRONLY | O_CREAT | O_TRUNC | O_CLOEXEC, 0644);
@@ -162,10 +164,11 @@ int qlx_layer_file_open(qlx_layer_file** out, const char* path, const qlx_dims* 
         REQ_PTR(out, "out");
         REQ_PTR(path, "path");
         validate_dims(d);
-        QLX_REQUIRE((flags & ~QLX_FILE_BUFFERED) == 0, QLX_EINVAL, "unknown layer-file flags");
+        QLX_REQUIRE((flags & ~(QLX_FILE_BUFFERED | QLX_FILE_WIRE)) == 0, QLX_EINVAL, "unknown layer-file flags");
         *out = nullptr;
+        const int form = (flags & QLX_FILE_WIRE) ? QLX_BLOB_WIRE : QLX_BLOB_FULL;
         uint64_t blob_bytes = 0;
-        const uint64_t stride = stride_of(*d, &blob_bytes);
+        const uint64_t stride = stride_of(*d, form, &blob_bytes);
         int fd = -1;
         bool direct = false;
         if (!(flags & QLX_FILE_BUFFERED)) {
@@ -200,6 +203,7 @@ int qlx_layer_file_open(qlx_layer_file** out, const char* path, const qlx_dims* 
         f->fd = fd;
         f->direct = direct;
         f->dims = *d;
+        f->form = form;
         f->blob_bytes = blob_bytes;
         f->stride = stride;
         // QLX_FILE_READERS (1..64) overrides the reader count (requests in flight)

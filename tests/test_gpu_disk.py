@@ -109,3 +109,32 @@ def test_attached_file_cannot_be_closed(four):
     ctx2.set_layer_source(None)
     g.close()
     ctx2.close()
+
+
+def test_wire_form_stack_file(four, tmp_path):
+    """A stack file of wire-form blobs: SFT and DPO give the resident run's
+    bits while reading (and copying) the smaller blobs."""
+    d, m, host, path = four
+    wire = [B_.blob_to_wire(d, h, pin_memory=False) for h in host]
+    wpath = str(tmp_path / "wire.bin")
+    q.LayerFile.write(wpath, d, wire, wire=True)
+    f = q.LayerFile(wpath, d, wire=True)
+    full = q.LayerFile(path, d)
+    assert f.info()["stride"] < full.info()["stride"]
+    full.close()
+    ctx = q.Context(0)
+    ctx.set_layer_source(f)
+    toks = synth.tokens(1, 2, 32, d.vocab)
+    l_d, g_d, st_d = run_sft(q, _disk_model(m), toks, B_.QLX_STREAMED_DISK, ctx)
+    l_r, g_r, _ = run_sft(q, m, toks, B_.QLX_RESIDENT)
+    assert torch.equal(l_d, l_r) and same_grads(g_d, g_r)
+    _, wt = B_.wire_layout(d)
+    assert st_d["h2d_bytes"] == st_d["layer_reads"] * wt
+    assert st_d["disk_bytes"] == st_d["layer_reads"] * f.info()["stride"]
+    ch, rj = synth.dpo_pairs(1, 2, 32, 8, d.vocab)
+    l_d, lp_d, g_d, _ = run_dpo(q, _disk_model(m), ch, rj, 8, 0.1, B_.QLX_STREAMED_DISK, B_.QLX_DPO_REF_SEPARATE, ctx)
+    l_r, lp_r, g_r, _ = run_dpo(q, m, ch, rj, 8, 0.1, B_.QLX_RESIDENT, B_.QLX_DPO_REF_FUSED)
+    assert torch.equal(l_d, l_r) and torch.equal(lp_d, lp_r) and same_grads(g_d, g_r)
+    ctx.set_layer_source(None)
+    ctx.close()
+    f.close()

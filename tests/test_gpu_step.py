@@ -111,3 +111,33 @@ def test_streamed_mode_rejects_unpinned_blobs(tiny):
     with pytest.raises(q.QlxError) as e:
         _sft(m, toks, B_.QLX_STREAMED)  # device pointers are not pinned host memory
     assert e.value.code == B_.QLX_ENOTPINNED
+
+
+def test_wire_form_streams_bit_identical_with_fewer_bytes():
+    """Streaming the wire form (block maxima as bf16, widened on the GPU
+    after the copy) gives the resident run's loss, log-probs and gradients
+    bit for bit, for SFT and both DPO schedules, and moves exactly the wire
+    form's bytes per layer read."""
+    d = dataclasses.replace(synth.TINY, n_layers=4)
+    m, host = gpu_model(q, d, 5, "normal")
+    wire = [B_.blob_to_wire(d, h) for h in host]
+    sw = m.with_blobs(wire, B_.QLX_BLOB_WIRE)
+    _, wt = B_.wire_layout(d)
+    toks = synth.tokens(5, 2, 32, d.vocab)
+    l_w, g_w, st_w = _sft(sw, toks, B_.QLX_STREAMED)
+    l_r, g_r, _ = _sft(m, toks, B_.QLX_RESIDENT)
+    assert torch.equal(l_w, l_r) and _same(g_w, g_r)
+    assert st_w["layer_reads"] == 2 * 4 - 2 and st_w["h2d_bytes"] == st_w["layer_reads"] * wt
+    ch, rj = synth.dpo_pairs(5, 2, 32, 8, d.vocab)
+    l_r, lp_r, g_r, _ = _dpo(m, ch, rj, 8, 0.1, B_.QLX_RESIDENT, B_.QLX_DPO_REF_FUSED)
+    for sched in (B_.QLX_DPO_REF_FUSED, B_.QLX_DPO_REF_SEPARATE):
+        l_w, lp_w, g_w, _ = _dpo(sw, ch, rj, 8, 0.1, B_.QLX_STREAMED, sched)
+        assert torch.equal(l_w, l_r) and torch.equal(lp_w, lp_r) and _same(g_w, g_r)
+
+
+def test_wire_form_only_for_streamed_host_blobs(tiny):
+    d, m, host = tiny
+    toks = synth.tokens(0, 1, 64, d.vocab)
+    with pytest.raises(q.QlxError) as e:
+        _sft(m.with_blobs(m.blobs, B_.QLX_BLOB_WIRE), toks, B_.QLX_RESIDENT)
+    assert e.value.code == B_.QLX_EINVAL

@@ -96,3 +96,38 @@ def test_bad_debug_arguments():
     assert L.qlx_ctx_set_debug(None, 0, 0) == B_.QLX_EINVAL
     assert L.qlx_ctx_set_debug(ctx.h, 0, 0) == B_.QLX_OK
     ctx.close()
+
+
+@pytest.mark.parametrize("flags", [B_.QLX_DEBUG_POISON | B_.QLX_DEBUG_DELAY_COPY,
+                                   B_.QLX_DEBUG_POISON | B_.QLX_DEBUG_DELAY_COMPUTE,
+                                   B_.QLX_DEBUG_POISON | B_.QLX_DEBUG_SERIALIZE],
+                         ids=["poison+delay_copy", "poison+delay_compute", "poison+serialize"])
+def test_wire_form_under_fault_injection(four, flags, monkeypatch):
+    """Wire-form blobs: the widen kernel runs on the copy stream between the
+    copy and the slot's ready event; a poisoned slot (whole slot, tail
+    staging included) still gives the normal bits, with one or two copy
+    streams."""
+    d, sm = four
+    wire = [B_.blob_to_wire(d, h) for h in sm.blobs]
+    sw = sm.with_blobs(wire, B_.QLX_BLOB_WIRE)
+    toks = synth.tokens(3, 2, 32, d.vocab)
+    l0, g0, _ = run_sft(q, sm, toks, B_.QLX_STREAMED)
+    for split in ("2", "1"):
+        monkeypatch.setenv("QLX_COPY_SPLIT", split)
+        ctx = q.Context(0)
+        monkeypatch.delenv("QLX_COPY_SPLIT")
+        ctx.set_debug(flags, 300)
+        print("wire debug", flags, "split", split, flush=True)
+        l1, g1, _ = run_sft(q, sw, toks, B_.QLX_STREAMED, ctx)
+        assert torch.equal(l0, l1) and same_grads(g0, g1)
+        ctx.close()
+
+
+def test_wire_form_poisoning_the_live_slot_shows_up(four):
+    d, sm = four
+    sw = sm.with_blobs([B_.blob_to_wire(d, h) for h in sm.blobs], B_.QLX_BLOB_WIRE)
+    ctx = q.Context(0)
+    ctx.set_debug(B_.QLX_DEBUG_POISON_LIVE)
+    l1, _, _ = run_sft(q, sw, synth.tokens(3, 1, 32, d.vocab), B_.QLX_STREAMED, ctx)
+    assert np.isnan(l1.item())
+    ctx.close()

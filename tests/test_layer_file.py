@@ -76,11 +76,14 @@ def test_errors(tmp_path):
     # NULL blob pointer in the write call
     arr = (C.c_void_p * 2)(None, None)
     assert L.qlx_layer_file_write(os.fsencode(path), C.byref(_dims(2)),
-                                  C.cast(arr, C.POINTER(C.c_void_p))) == b.QLX_EINVAL
+                                  C.cast(arr, C.POINTER(C.c_void_p)), 0) == b.QLX_EINVAL
+    # unknown write flags
+    assert L.qlx_layer_file_write(os.fsencode(path), C.byref(_dims(2)),
+                                  C.cast(arr, C.POINTER(C.c_void_p)), 4) == b.QLX_EINVAL
     # a directory that does not exist
     assert L.qlx_layer_file_write(os.fsencode(str(tmp_path / "no" / "x.bin")), C.byref(_dims(2)),
                                   C.cast((C.c_void_p * 2)(*[bl.ctypes.data for bl in _blobs(_dims(2))]),
-                                         C.POINTER(C.c_void_p))) == b.QLX_EIO
+                                         C.POINTER(C.c_void_p)), 0) == b.QLX_EIO
     assert L.qlx_layer_file_close(None) == b.QLX_OK
 
 

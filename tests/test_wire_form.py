@@ -1,0 +1,116 @@
+"""CPU checks of the layer blob's wire form (host side of the library): the
+layout keeps the packed regions where the full form has them and stores
+each block maximum as its upper 16 bits; the conversion is lossless for
+blobs whose maxima are bf16 values (every maximum of bf16 weights is one)
+and refuses any other blob without touching the output; stack files of
+wire blobs read back byte for byte."""
+import numpy as np
+import pytest
+
+from qlora_fine_tuning_dequant_amd import binding as b
+
+
+def _dims(n_layers=2, hidden=256, inter=688):
+    return b.Dims(hidden=hidden, n_heads=4, n_kv_heads=2, head_dim=64, inter=inter, vocab=1024, n_layers=n_layers,
+                  lora_r=8, lora_alpha=16.0, rms_eps=1e-5, rope_theta=5e5)
+
+
+def _nblocks(d):
+    q, kv, o, mlp = d.n_heads * d.head_dim, d.n_kv_heads * d.head_dim, d.hidden, d.inter
+    nel = [q * d.hidden, kv * d.hidden, kv * d.hidden, o * q, mlp * d.hidden, mlp * d.hidden, d.hidden * mlp]
+    return [n // 64 for n in nel]
+
+
+def _full_blob(d, seed):
+    """A full-form blob with random packed bytes, bf16-valued maxima (as
+    fp32 words with zero low halves) and random gains."""
+    off, total = b.blob_layout(d)
+    g = np.random.default_rng(seed)
+    blob = np.zeros(total, np.uint8)
+    blob[:off[7]] = g.integers(0, 256, off[7], dtype=np.uint8)
+    nb = sum(_nblocks(d))
+    hi = (g.integers(0x3C00, 0x3E00, nb, dtype=np.uint32))  # positive bf16 bit patterns near 0.01..0.1
+    blob[off[7]:off[7] + 4 * nb] = (hi << 16).astype('<u4').view(np.uint8)
+    for k in (14, 15):
+        blob[off[k]:off[k] + 4 * d.hidden] = g.standard_normal(d.hidden).astype('<f4').view(np.uint8)
+    return blob
+
+
+def _t(a):
+    import torch
+    return torch.from_numpy(a)
+
+
+@pytest.mark.parametrize("hidden,inter", [(256, 688), (4096, 14336)])
+def test_wire_layout(hidden, inter):
+    d = _dims(hidden=hidden, inter=inter)
+    fo, ft = b.blob_layout(d)
+    wo, wt = b.wire_layout(d)
+    nb = _nblocks(d)
+    assert wo[:8] == fo[:8]                      # packed regions unchanged; maxima start where they did
+    for p in range(6):                           # bf16 maxima back to back
+        assert wo[8 + p] == wo[7 + p] + 2 * nb[p]
+    assert wo[14] % 256 == 0 and wo[14] >= wo[13] + 2 * nb[6]
+    assert wo[15] == wo[14] + ((4 * hidden + 255) // 256) * 256
+    assert wt % 256 == 0 and wt == wo[15] + ((4 * hidden + 255) // 256) * 256
+    assert ft - wt == ((fo[14] - fo[7]) - (wo[14] - wo[7]))  # only the maxima shrink
+    if hidden == 4096:   # Llama-3.1-8B layer: 4.25 instead of 4.5 bits per weight on the wire
+        n_w = sum(nb) * 64
+        assert abs(wt * 8 / n_w - 4.25) < 0.01 and abs(ft * 8 / n_w - 4.5) < 0.01
+
+
+def test_blob_to_wire_is_lossless():
+    d = _dims()
+    fo, ft = b.blob_layout(d)
+    wo, wt = b.wire_layout(d)
+    blob = _full_blob(d, 1)
+    wire = b.blob_to_wire(d, _t(blob), pin_memory=False).numpy()
+    assert wire.size == wt
+    assert np.array_equal(wire[:fo[7]], blob[:fo[7]])
+    nb = sum(_nblocks(d))
+    m32 = blob[fo[7]:fo[7] + 4 * nb].view('<u4')
+    m16 = wire[wo[7]:wo[7] + 2 * nb].view('<u2')
+    assert np.array_equal(m16.astype(np.uint32) << 16, m32)   # widening gives the fp32 maxima back exactly
+    for k in (14, 15):
+        assert np.array_equal(wire[wo[k]:wo[k] + 4 * d.hidden], blob[fo[k]:fo[k] + 4 * d.hidden])
+    pad = np.ones(wt, bool)                                    # everything else is zero padding
+    pad[:wo[7] + 2 * nb] = False
+    for k in (14, 15):
+        pad[wo[k]:wo[k] + 4 * d.hidden] = False
+    assert not wire[pad].any()
+
+
+def test_blob_to_wire_refuses_non_bf16_maxima():
+    d = _dims()
+    fo, _ = b.blob_layout(d)
+    _, wt = b.wire_layout(d)
+    blob = _full_blob(d, 2)
+    nb = sum(_nblocks(d))
+    k = nb - 3
+    blob[fo[7] + 4 * k] = 1                                    # a low bit of one maximum
+    out = np.full(wt, 0xAB, np.uint8)
+    with pytest.raises(b.QlxError) as e:
+        b._check(b.lib().qlx_layer_blob_to_wire(b.C.byref(d), blob.ctypes.data, out.ctypes.data))
+    assert e.value.code == b.QLX_EINVAL and str(k) in str(e.value)
+    assert (out == 0xAB).all()                                 # untouched
+
+
+def test_wire_stack_file_reads_back(tmp_path):
+    d = _dims(n_layers=3)
+    _, wt = b.wire_layout(d)
+    _, ft = b.blob_layout(d)
+    wires = [b.blob_to_wire(d, _t(_full_blob(d, 10 + i)), pin_memory=False).numpy() for i in range(3)]
+    path = str(tmp_path / "wire.bin")
+    b.LayerFile.write(path, d, wires, wire=True)
+    f = b.LayerFile(path, d, wire=True)
+    stride = f.info()["stride"]
+    assert stride % 4096 == 0 and wt <= stride < wt + 4096
+    for i in (2, 0, 1):
+        out = np.zeros(wt, np.uint8)
+        f.read(i, out)
+        assert np.array_equal(out, wires[i])
+    f.close()
+    # the same file opened as full-form blobs is too short (or mismatched): refused
+    if 3 * ((ft + 4095) // 4096 * 4096) > 3 * stride:
+        with pytest.raises(b.QlxError):
+            b.LayerFile(path, d)
