@@ -386,6 +386,9 @@ def main() -> int:
     ap.add_argument("--blob-form", default="wire", choices=["wire", "full"],
                     help="streamed layer blobs: wire = block maxima as bf16 (lossless for bf16 weights, "
                          "widened on the GPU), full = fp32 maxima as the kernels read them")
+    ap.add_argument("--keep-layers", default="on", choices=["on", "off"],
+                    help="streamed: the two layers a step leaves in the slots serve the next step's forward "
+                         "(qlx_ctx_set_keep_layers); off copies every layer every step")
     ap.add_argument("--source", default="ram", choices=["ram", "disk", "auto"],
                     help="where the streamed stack lives: pinned host RAM, a stack file read with O_DIRECT, or "
                          "RAM when it fits in available memory and the file otherwise")
@@ -456,6 +459,8 @@ def main() -> int:
     log(f"model ready in {time.perf_counter() - t0:.1f} s")
     mode = B_.QLX_STREAMED if args.mode == "streamed" else B_.QLX_RESIDENT
     ctx = q.Context(0)
+    keep = args.mode == "streamed" and args.keep_layers == "on"
+    ctx.set_keep_layers(keep)
     source, layer_file, stack_path = "ram" if args.mode == "streamed" else "device", None, None
     if args.mode == "streamed" and args.source != "ram":
         _, blob_bytes = B_.wire_layout(d) if wire else B_.blob_layout(d)
@@ -567,7 +572,7 @@ def main() -> int:
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl["name"], "global_batch": batch if wl["kind"] == "sft" else 2 * batch,
                    "seq_len": seq, "mode": args.mode, "source": source,
-                   "blob_form": "wire" if wire else "full", "layers": d.n_layers,
+                   "blob_form": "wire" if wire else "full", "keep_layers": keep, "layers": d.n_layers,
                    "lora_r": d.lora_r,
                    "optimizer": None if args.no_optimizer else f"adamw lr {LR}",
                    **({"dpo_reference": args.dpo_ref} if wl["kind"] in ("dpo", "kto") else {})},

@@ -232,6 +232,19 @@ enum {
 };
 int qlx_ctx_set_debug(qlx_ctx* ctx, int flags, int delay_us);
 
+/* Keep-layers (on = 1, off = 0; off by default): at the end of a streamed
+ * step the two slots hold layers 1 and 0, the first two layers the next
+ * step's forward needs. With keep-layers on, the next step on this context
+ * uses them without copying them again when its workspace slots are the same
+ * memory, the layers' sources are the same (the same host blob pointers, or
+ * the same attached layer file) and the blob form is the same: steady-state
+ * layer reads per step fall by 2 and the first layer's compute starts at
+ * once. The caller promises that neither the workspace nor those host blobs
+ * (or the file) are written between the steps; resident-mode steps and
+ * qlx_ctx_set_keep_layers itself forget what the slots held. Results are
+ * bit-identical to a step that copies every layer. */
+int qlx_ctx_set_keep_layers(qlx_ctx* ctx, int on);
+
 /* Disk stream source (rug.gal article, "En detalle": the frozen base sits in
  * CPU memory or on disk; imasters article, "Como cabe um 8B em 4 GB": the
  * `stream_source: auto` setting, RAM when the stack fits and the NVMe disk

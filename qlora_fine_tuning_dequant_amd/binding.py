@@ -40,7 +40,7 @@ EXPORTED = (
     "qlx_step_workspace_bytes", "stream_step_sft", "stream_step_dpo", "stream_step_pref", "qlx_merge_workspace_bytes", "qlx_lora_merge", "qlx_profile_begin", "qlx_profile_begin_prefix", "qlx_profile_end", "qlx_adamw_lora",
     "qlx_layer_file_write", "qlx_layer_file_open", "qlx_layer_file_close", "qlx_layer_file_info",
     "qlx_layer_file_read", "qlx_ctx_set_layer_source", "qlx_stream_source_auto", "qlx_ctx_set_debug",
-    "qlx_peak_mfma", "qlx_peak_copy", "qlx_layer_wire_layout", "qlx_layer_blob_to_wire",
+    "qlx_peak_mfma", "qlx_peak_copy", "qlx_layer_wire_layout", "qlx_layer_blob_to_wire", "qlx_ctx_set_keep_layers",
 )
 
 
@@ -157,6 +157,7 @@ def lib() -> C.CDLL:
         "qlx_ctx_set_layer_source": (i32, [vp, vp]),
         "qlx_stream_source_auto": (i32, [C.c_uint64, C.c_uint64, C.POINTER(C.c_int)]),
         "qlx_ctx_set_debug": (i32, [vp, i32, i32]),
+        "qlx_ctx_set_keep_layers": (i32, [vp, i32]),
         "qlx_peak_mfma": (i32, [C.c_int64, i32, i32, vp, vp]),
         "qlx_peak_copy": (i32, [vp, vp, C.c_uint64, vp]),
     }
@@ -418,6 +419,11 @@ class Context:
         h = C.c_void_p()
         _check(lib().qlx_ctx_create(C.byref(h), device))
         self.h = h
+
+    def set_keep_layers(self, on: bool = True) -> None:
+        """Keep the two layers a step leaves in the slots for the next step
+        (same workspace and blobs; see qlx_ctx_set_keep_layers)."""
+        _check(lib().qlx_ctx_set_keep_layers(self.h, 1 if on else 0))
 
     def set_debug(self, flags: int, delay_us: int = 0) -> None:
         """Stream fault injection (QLX_DEBUG_*): serialize, poison freed slots, delay copies or compute."""

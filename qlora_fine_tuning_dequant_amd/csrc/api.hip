@@ -392,6 +392,14 @@ struct qlx_ctx {
     size_t copies_used = 0;
     qlx_stats stats{};
     qlx_layer_file* source = nullptr;  // QLX_STREAMED_DISK
+    // qlx_ctx_set_keep_layers: what each slot held when the last step ended
+    int keep_layers = 0;
+    struct Kept {
+        int layer = -1;
+        const void* src = nullptr;  // the layer's host blob, or the layer file
+        const char* slot = nullptr;
+        int form = 0;
+    } kept[2];
 };
 
 namespace qlx {
@@ -487,6 +495,21 @@ class Streamer {
         blob_layout(m->dims, full_, &bytes_);
         wire_layout(m->dims, wire_, &wire_bytes_);
         nblocks_ = int64_t(absmax_blocks(m->dims));
+        // keep-layers: a slot still holds what the last step left in it when
+        // it is the same workspace slot and the layer's source and form match
+        for (int sl = 0; sl < 2; ++sl) {
+            const qlx_ctx::Kept k = ctx->kept[sl];
+            ctx->kept[sl] = qlx_ctx::Kept{};  // valid again only once this step completes its enqueue
+            if (ctx->keep_layers && mode != QLX_RESIDENT && k.layer >= 0 && k.layer < m->dims.n_layers &&
+                k.slot == w_.slot[sl] && k.form == form_ && k.src == source_of(k.layer) && slot_of(k.layer) == sl)
+                held_[sl] = k.layer;
+        }
+    }
+    // End of a step: with keep-layers on, remember what the slots hold.
+    void keep() {
+        if (!ctx_->keep_layers || mode_ == QLX_RESIDENT) return;
+        for (int sl = 0; sl < 2; ++sl)
+            if (held_[sl] >= 0) ctx_->kept[sl] = qlx_ctx::Kept{held_[sl], source_of(held_[sl]), w_.slot[sl], form_};
     }
     // Make layer i resident (if not already), wait for it on the main stream,
     // and return its device pointer. prefetch_next >= 0 also starts the copy
@@ -514,6 +537,9 @@ class Streamer {
 
    private:
     int slot_of(int i) const { return i & 1; }
+    const void* source_of(int i) const {
+        return mode_ == QLX_STREAMED_DISK ? static_cast<const void*>(ctx_->source) : m_->layer_blobs[i];
+    }
     void issue_copy(int i, int sl) {
         // the slot's previous contents must be finished with on the main stream
         QLX_CHECK_HIP(hipStreamWaitEvent(ctx_->side, ctx_->compute_done[sl], 0));
@@ -830,6 +856,15 @@ int qlx_ctx_set_debug(qlx_ctx* ctx, int flags, int delay_us) {
     });
 }
 
+int qlx_ctx_set_keep_layers(qlx_ctx* ctx, int on) {
+    return guarded([&] {
+        REQ_PTR(ctx, "ctx");
+        QLX_REQUIRE(on == 0 || on == 1, QLX_EINVAL, "keep_layers: 0 or 1");
+        ctx->keep_layers = on;
+        ctx->kept[0] = ctx->kept[1] = qlx_ctx::Kept{};
+    });
+}
+
 int qlx_ctx_set_layer_source(qlx_ctx* ctx, qlx_layer_file* f) {
     return guarded([&] {
         REQ_PTR(ctx, "ctx");
@@ -922,6 +957,7 @@ int stream_step_sft(qlx_ctx* ctx, const qlx_model* m, const int32_t* tokens, int
         head_grad(m, hL, T, tokens, seq, 0, w.lse, kDzScale, nullptr, alpha, w, w.dh[0], w.lw.partial, s);
         ctx->stats.layer_passes = 2 * L;
         backward_layers(st, m, g, w, w.dh[0], grads, s);
+        st.keep();
         end_step(ctx, s);
     });
 }
@@ -1048,6 +1084,7 @@ static void pref_step(qlx_ctx* ctx, const qlx_model* m, const qlx_pref_cfg& cfg,
     head_grad(m, hL, T, w.toks, seq, start, w.lse, -kDzScale, w.gseq, 1.0f / kDzScale, w, w.dh[0], w.lw.partial, s);
     ctx->stats.layer_passes = int64_t(2 + extra.size()) * L;
     backward_layers(st, m, g, w, w.dh[0], grads, s);
+    st.keep();
     end_step(ctx, s);
 }
 

@@ -131,3 +131,67 @@ def test_wire_form_poisoning_the_live_slot_shows_up(four):
     l1, _, _ = run_sft(q, sw, synth.tokens(3, 1, 32, d.vocab), B_.QLX_STREAMED, ctx)
     assert np.isnan(l1.item())
     ctx.close()
+
+
+def _sft_ws(sm, toks, ctx, ws):
+    grads = [q.LoraGrads(l) for l in sm.lora]
+    loss = torch.empty(1, dtype=torch.float32, device="cuda:0")
+    q.stream_step_sft(ctx, sm, torch.from_numpy(toks).to("cuda:0"), B_.QLX_STREAMED, loss, grads, ws)
+    return loss, grads, ctx.sync()
+
+
+def test_keep_layers_across_steps(four):
+    """Keep-layers: the second step on the same context, workspace and blobs
+    reuses the two layers the first left in the slots (2L - 4 reads instead of
+    2L - 2) and gives the same bits; other blobs, another workspace, or the
+    setting switched off copy every layer again."""
+    d, sm = four
+    toks = synth.tokens(3, 2, 32, d.vocab)
+    l0, g0, _ = run_sft(q, sm, toks, B_.QLX_STREAMED)
+    ws = B_.workspace(B_.step_workspace_bytes(d, 0, 2, 32))
+    ctx = q.Context(0)
+    ctx.set_keep_layers(True)
+    reads = []
+    for _ in range(3):
+        l1, g1, st = _sft_ws(sm, toks, ctx, ws)
+        assert torch.equal(l0, l1) and same_grads(g0, g1)
+        reads.append(st["layer_reads"])
+    assert reads == [2 * 4 - 2, 2 * 4 - 4, 2 * 4 - 4]
+    # the same bytes at other host addresses: copied again
+    other = sm.with_blobs([h.clone().pin_memory() for h in sm.blobs])
+    l2, g2, st = _sft_ws(other, toks, ctx, ws)
+    assert st["layer_reads"] == 2 * 4 - 2 and torch.equal(l0, l2) and same_grads(g0, g2)
+    # another workspace: copied again
+    ws2 = B_.workspace(B_.step_workspace_bytes(d, 0, 2, 32))
+    _, _, st = _sft_ws(other, toks, ctx, ws2)
+    assert st["layer_reads"] == 2 * 4 - 2
+    # poisoning freed slots does not touch the kept ones
+    ctx.set_debug(B_.QLX_DEBUG_POISON)
+    l3, g3, st = _sft_ws(other, toks, ctx, ws2)
+    assert st["layer_reads"] == 2 * 4 - 4 and torch.equal(l0, l3) and same_grads(g0, g3)
+    ctx.set_keep_layers(False)
+    _, _, st = _sft_ws(other, toks, ctx, ws2)
+    assert st["layer_reads"] == 2 * 4 - 2
+    ctx.close()
+
+
+def test_keep_layers_dpo_and_wire_form(four):
+    d, sm = four
+    ch, rj = synth.dpo_pairs(3, 2, 32, 8, d.vocab)
+    l0, lp0, g0, _ = run_dpo(q, sm, ch, rj, 8, 0.1, B_.QLX_STREAMED, B_.QLX_DPO_REF_SEPARATE)
+    sw = sm.with_blobs([B_.blob_to_wire(d, h) for h in sm.blobs], B_.QLX_BLOB_WIRE)
+    for model in (sm, sw):
+        ws = B_.workspace(B_.step_workspace_bytes(d, 1, 2, 32))
+        ctx = q.Context(0)
+        ctx.set_keep_layers(True)
+        reads = []
+        for _ in range(2):
+            grads = [q.LoraGrads(l) for l in model.lora]
+            loss = torch.empty(1, dtype=torch.float32, device="cuda:0")
+            logps = torch.empty(8, dtype=torch.float32, device="cuda:0")
+            q.stream_step_dpo(ctx, model, torch.from_numpy(ch).to("cuda:0"), torch.from_numpy(rj).to("cuda:0"), 8,
+                              0.1, B_.QLX_STREAMED, B_.QLX_DPO_REF_SEPARATE, loss, logps, grads, ws)
+            reads.append(ctx.sync()["layer_reads"])
+            assert torch.equal(loss, l0) and torch.equal(logps, lp0) and same_grads(grads, g0)
+        assert reads == [3 * 4 - 2, 3 * 4 - 4]
+        ctx.close()
