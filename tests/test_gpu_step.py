@@ -141,3 +141,20 @@ def test_wire_form_only_for_streamed_host_blobs(tiny):
     with pytest.raises(q.QlxError) as e:
         _sft(m.with_blobs(m.blobs, B_.QLX_BLOB_WIRE), toks, B_.QLX_RESIDENT)
     assert e.value.code == B_.QLX_EINVAL
+
+
+def test_wire_form_with_a_ragged_block_count():
+    """Odd dims whose NF4 block count is not a multiple of 4 (hidden 96,
+    intermediate 68: 690 blocks), so the widen kernel's scalar tail runs:
+    streamed wire == resident, bit for bit."""
+    d = dataclasses.replace(synth.TINY, hidden=96, n_heads=1, n_kv_heads=1, head_dim=64, inter=68, n_layers=3)
+    m, host = gpu_model(q, d, 6, "normal")
+    fo, _ = B_.blob_layout(d)
+    wo, wt = B_.wire_layout(d)
+    assert (wo[14] - wo[7]) >= 2 * 690 and (fo[14] - fo[7]) >= 4 * 690
+    sw = m.with_blobs([B_.blob_to_wire(d, h) for h in host], B_.QLX_BLOB_WIRE)
+    toks = synth.tokens(6, 2, 24, d.vocab)
+    l_w, g_w, st = _sft(sw, toks, B_.QLX_STREAMED)
+    l_r, g_r, _ = _sft(m, toks, B_.QLX_RESIDENT)
+    assert torch.equal(l_w, l_r) and _same(g_w, g_r)
+    assert st["h2d_bytes"] == st["layer_reads"] * wt

@@ -10,9 +10,9 @@ import pytest
 from qlora_fine_tuning_dequant_amd import binding as b
 
 
-def _dims(n_layers=2, hidden=256, inter=688):
-    return b.Dims(hidden=hidden, n_heads=4, n_kv_heads=2, head_dim=64, inter=inter, vocab=1024, n_layers=n_layers,
-                  lora_r=8, lora_alpha=16.0, rms_eps=1e-5, rope_theta=5e5)
+def _dims(n_layers=2, hidden=256, inter=688, heads=(4, 2)):
+    return b.Dims(hidden=hidden, n_heads=heads[0], n_kv_heads=heads[1], head_dim=64, inter=inter, vocab=1024,
+                  n_layers=n_layers, lora_r=8, lora_alpha=16.0, rms_eps=1e-5, rope_theta=5e5)
 
 
 def _nblocks(d):
@@ -59,8 +59,10 @@ def test_wire_layout(hidden, inter):
         assert abs(wt * 8 / n_w - 4.25) < 0.01 and abs(ft * 8 / n_w - 4.5) < 0.01
 
 
-def test_blob_to_wire_is_lossless():
-    d = _dims()
+@pytest.mark.parametrize("hidden,inter,heads", [(256, 688, (4, 2)), (96, 68, (1, 1))])
+def test_blob_to_wire_is_lossless(hidden, inter, heads):
+    """Also at a block count that is not a multiple of 4 (hidden 96: 690)."""
+    d = _dims(hidden=hidden, inter=inter, heads=heads)
     fo, ft = b.blob_layout(d)
     wo, wt = b.wire_layout(d)
     blob = _full_blob(d, 1)
