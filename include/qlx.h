@@ -240,9 +240,10 @@ int qlx_ctx_set_debug(qlx_ctx* ctx, int flags, int delay_us);
  * the same attached layer file) and the blob form is the same: steady-state
  * layer reads per step fall by 2 and the first layer's compute starts at
  * once. The caller promises that neither the workspace nor those host blobs
- * (or the file) are written between the steps; resident-mode steps and
- * qlx_ctx_set_keep_layers itself forget what the slots held. Results are
- * bit-identical to a step that copies every layer. */
+ * (or the file) are written between the steps; resident-mode steps,
+ * qlx_ctx_set_layer_source and qlx_ctx_set_keep_layers itself forget what
+ * the slots held. Results are bit-identical to a step that copies every
+ * layer. */
 int qlx_ctx_set_keep_layers(qlx_ctx* ctx, int on);
 
 /* Disk stream source (rug.gal article, "En detalle": the frozen base sits in

@@ -869,6 +869,9 @@ int qlx_ctx_set_layer_source(qlx_ctx* ctx, qlx_layer_file* f) {
     return guarded([&] {
         REQ_PTR(ctx, "ctx");
         if (f == ctx->source) return;
+        // slots filled from another source are never taken for this one's layers
+        // (a later file could even reuse the detached one's address)
+        ctx->kept[0] = ctx->kept[1] = qlx_ctx::Kept{};
         if (!f) {
             ctx->source->attached -= 1;
             ctx->source = nullptr;

@@ -138,3 +138,36 @@ def test_wire_form_stack_file(four, tmp_path):
     ctx.set_layer_source(None)
     ctx.close()
     f.close()
+
+
+def test_keep_layers_with_a_layer_file(four):
+    """Keep-layers on the disk source: the second step reuses the two slot
+    layers; re-attaching a source forgets them (a new file could sit at the
+    old one's address)."""
+    d, m, host, path = four
+    toks = synth.tokens(1, 2, 32, d.vocab)
+    l_r, g_r, _ = run_sft(q, m, toks, B_.QLX_RESIDENT)
+    f = q.LayerFile(path, d)
+    ctx = q.Context(0)
+    ctx.set_layer_source(f)
+    ctx.set_keep_layers(True)
+    ws = B_.workspace(B_.step_workspace_bytes(d, 0, 2, 32))
+    dm = _disk_model(m)
+
+    def step():
+        grads = [q.LoraGrads(l) for l in dm.lora]
+        loss = torch.empty(1, dtype=torch.float32, device="cuda:0")
+        q.stream_step_sft(ctx, dm, torch.from_numpy(toks).to("cuda:0"), B_.QLX_STREAMED_DISK, loss, grads, ws)
+        st = ctx.sync()
+        assert torch.equal(loss, l_r) and same_grads(grads, g_r)
+        return st["layer_reads"], st["disk_bytes"]
+
+    r1, b1 = step()
+    r2, b2 = step()
+    assert (r1, r2) == (2 * 4 - 2, 2 * 4 - 4) and b2 == r2 * f.info()["stride"]
+    ctx.set_layer_source(None)
+    ctx.set_layer_source(f)
+    assert step()[0] == 2 * 4 - 2
+    ctx.set_layer_source(None)
+    ctx.close()
+    f.close()
