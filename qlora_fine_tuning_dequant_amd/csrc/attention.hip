@@ -213,27 +213,33 @@ __global__ __launch_bounds__(256) void k_flash_fwd(const AttnArgs a) {
 }
 
 // ------------------------------------------------------------------ backward
-// D[b, h, q] = sum_d dO[q, h d] o[q, h d], one thread per (query, head).
+// D[b, h, q] = sum_d dO[q, h d] o[q, h d]: hd/8 lanes per (query, head),
+// each with one 16-byte load of dO and of o (consecutive lanes read
+// consecutive bytes of a token row), joined by xor shuffles in a fixed order.
 __global__ __launch_bounds__(256) void k_flash_bwd_dot(const AttnArgs a, int hd) {
+    const int L = hd / 8;  // 8 or 16 lanes per (query, head)
     const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t T = int64_t(a.B) * a.S;
-    if (idx >= T * a.nH) return;
-    const int64_t t = idx / a.nH;
-    const int h = int(idx % a.nH);
-    const uint16_t* x = a.dO + t * a.ldo + int64_t(h) * hd;
-    const uint16_t* y = a.O + t * a.ldo + int64_t(h) * hd;
+    const int64_t pair = idx / L;
+    const int part = int(idx % L);
+    const bool live = pair < T * a.nH;
+    const int64_t pc = live ? pair : 0;
+    const int64_t t = pc / a.nH;
+    const int h = int(pc % a.nH);
+    const uint4 u = *reinterpret_cast<const uint4*>(a.dO + t * a.ldo + int64_t(h) * hd + part * 8);
+    const uint4 v = *reinterpret_cast<const uint4*>(a.O + t * a.ldo + int64_t(h) * hd + part * 8);
+    const uint32_t uw[4] = {u.x, u.y, u.z, u.w}, vw[4] = {v.x, v.y, v.z, v.w};
     float s = 0.f;
-    for (int d = 0; d < hd; d += 8) {
-        const uint4 u = *reinterpret_cast<const uint4*>(x + d), v = *reinterpret_cast<const uint4*>(y + d);
-        const uint32_t uw[4] = {u.x, u.y, u.z, u.w}, vw[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            s = fmaf(__builtin_bit_cast(float, uw[e] << 16), __builtin_bit_cast(float, vw[e] << 16), s);
-            s = fmaf(__builtin_bit_cast(float, uw[e] & 0xFFFF0000u), __builtin_bit_cast(float, vw[e] & 0xFFFF0000u), s);
-        }
+    for (int e = 0; e < 4; ++e) {
+        s = fmaf(__builtin_bit_cast(float, uw[e] << 16), __builtin_bit_cast(float, vw[e] << 16), s);
+        s = fmaf(__builtin_bit_cast(float, uw[e] & 0xFFFF0000u), __builtin_bit_cast(float, vw[e] & 0xFFFF0000u), s);
     }
-    const int64_t b = t / a.S, qi = t % a.S;
-    a.Dq[(b * a.nH + h) * a.S + qi] = s;
+    for (int off = L / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    if (live && part == 0) {
+        const int64_t b = t / a.S, qi = t % a.S;
+        a.Dq[(b * a.nH + h) * a.S + qi] = s;
+    }
 }
 
 // dK_h, dV_h (fp32, per query head) for one block of 64 keys.
@@ -455,7 +461,8 @@ void launch_flash_bwd(const AttnArgs& a, hipStream_t s) {
     const int64_t n = int64_t(a.B) * a.S * a.nH;
     {
         ProfScope prof("attn_bwd_dot", 2.0 * n * a.hd, double(n) * (a.hd * 4.0 + 4.0), s);
-        hipLaunchKernelGGL(k_flash_bwd_dot, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, a, a.hd);
+        const int64_t threads = n * (a.hd / 8);
+        hipLaunchKernelGGL(k_flash_bwd_dot, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, a, a.hd);
         check_launch("attn_bwd_dot");
     }
     const dim3 grid(unsigned((a.S + QB - 1) / QB), unsigned(a.nH), unsigned(a.B));
