@@ -398,6 +398,9 @@ def main() -> int:
                     help="DPO reference schedule: fused with the policy forward, or a separate pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timing")
+    ap.add_argument("--optimizer", default="fused", choices=["fused", "separate"],
+                    help="AdamW on the adapters: fused = each layer updated inside the step right after its "
+                         "backward (qlx_ctx_set_adamw), separate = one qlx_adamw_lora call after the step")
     ap.add_argument("--no-optimizer", action="store_true",
                     help="leave the AdamW update out of the step (loss + LoRA gradients only)")
     ap.add_argument("--gemm-shapes", action="store_true",
@@ -481,6 +484,9 @@ def main() -> int:
     grads = [q.LoraGrads(l) for l in m.lora]
     # the step's optimizer update: AdamW on every LoRA factor at the pages' lr
     opt = None if args.no_optimizer else q.AdamW(d, m.lora, lr=LR)
+    fused_opt = opt is not None and args.optimizer == "fused"
+    if fused_opt:  # each layer's adapters updated inside the step, right after its backward
+        ctx.set_adamw(opt)
     loss = torch.empty(1, dtype=torch.float32, device=dev)
     batch, seq = wl["batch"], wl["seq"]
     if wl["kind"] == "sft":
@@ -490,7 +496,7 @@ def main() -> int:
 
         def step():
             q.stream_step_sft(ctx, m, toks, mode, loss, grads, ws)
-            if opt:
+            if opt and not fused_opt:
                 opt.step(grads)
     else:
         pairs = batch
@@ -507,7 +513,7 @@ def main() -> int:
             else:  # ORPO, SimPO, KTO with the readings' hyperparameters
                 q.stream_step_pref(ctx, m, wl["kind"], ch, rj, wl["prompt"], mode, loss, logps, grads, ws,
                                    ref_schedule=sched)
-            if opt:
+            if opt and not fused_opt:
                 opt.step(grads)
 
     for i in range(args.warmup):
@@ -574,7 +580,8 @@ def main() -> int:
                    "seq_len": seq, "mode": args.mode, "source": source,
                    "blob_form": "wire" if wire else "full", "keep_layers": keep, "layers": d.n_layers,
                    "lora_r": d.lora_r,
-                   "optimizer": None if args.no_optimizer else f"adamw lr {LR}",
+                   "optimizer": None if args.no_optimizer else
+                   f"adamw lr {LR}" + (", per layer inside the backward" if fused_opt else ", after the step"),
                    **({"dpo_reference": args.dpo_ref} if wl["kind"] in ("dpo", "kto") else {})},
         "roofline": roofline,
         "stream": {"layer_reads_per_step": reads, "h2d_GB_per_step": round(h2d_bytes / 1e9, 3),

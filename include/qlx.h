@@ -437,6 +437,22 @@ int qlx_adamw_lora(const qlx_dims* dims, const qlx_lora_buf* params, const qlx_l
                    const qlx_lora_buf* m, const qlx_lora_buf* v, int64_t t, const qlx_adamw_cfg* cfg,
                    void* stream);
 
+/* Fused AdamW (off by default). Registers AdamW on a context: every later
+ * step on it (SFT or preference) updates layer i's adapters right after
+ * layer i's backward, on the step's stream, where it overlaps the copies and
+ * compute of the layers still to come (nothing later in the step reads
+ * them). The result is bit-identical to qlx_adamw_lora with the same t after
+ * the step. params, m, v: HOST arrays of n_layers qlx_lora_buf (device fp32
+ * buffers, copied as pointers; the buffers must stay valid while
+ * registered); params must be the adapters of the model each step runs on,
+ * or the step fails with QLX_EINVAL before any launch. t_next: the update
+ * count of the next step (>= 1); each step call that returns QLX_OK adds 1.
+ * params = NULL switches it off. */
+int qlx_ctx_set_adamw(qlx_ctx* ctx, int n_layers, const qlx_lora_buf* params, const qlx_lora_buf* m,
+                      const qlx_lora_buf* v, const qlx_adamw_cfg* cfg, int64_t t_next);
+/* *t_next (HOST) = the update count the next step will use; 0 when off. */
+int qlx_ctx_adamw_t(const qlx_ctx* ctx, int64_t* t_next);
+
 /* ---------------------------------------------------------------------------
  * Per-kernel timing (observability). Between qlx_profile_begin() and
  * qlx_profile_end() every kernel the library launches is bracketed by a pair

@@ -41,6 +41,7 @@ EXPORTED = (
     "qlx_layer_file_write", "qlx_layer_file_open", "qlx_layer_file_close", "qlx_layer_file_info",
     "qlx_layer_file_read", "qlx_ctx_set_layer_source", "qlx_stream_source_auto", "qlx_ctx_set_debug",
     "qlx_peak_mfma", "qlx_peak_copy", "qlx_layer_wire_layout", "qlx_layer_blob_to_wire", "qlx_ctx_set_keep_layers",
+    "qlx_ctx_set_adamw", "qlx_ctx_adamw_t",
 )
 
 
@@ -158,6 +159,9 @@ def lib() -> C.CDLL:
         "qlx_stream_source_auto": (i32, [C.c_uint64, C.c_uint64, C.POINTER(C.c_int)]),
         "qlx_ctx_set_debug": (i32, [vp, i32, i32]),
         "qlx_ctx_set_keep_layers": (i32, [vp, i32]),
+        "qlx_ctx_set_adamw": (i32, [vp, i32, C.POINTER(LoraBuf), C.POINTER(LoraBuf), C.POINTER(LoraBuf),
+                                    C.POINTER(AdamwCfg), C.c_int64]),
+        "qlx_ctx_adamw_t": (i32, [vp, C.POINTER(C.c_int64)]),
         "qlx_peak_mfma": (i32, [C.c_int64, i32, i32, vp, vp]),
         "qlx_peak_copy": (i32, [vp, vp, C.c_uint64, vp]),
     }
@@ -420,6 +424,30 @@ class Context:
         _check(lib().qlx_ctx_create(C.byref(h), device))
         self.h = h
 
+    def set_adamw(self, opt: "AdamW | None") -> None:
+        """Fused AdamW: each step on this context updates layer i's adapters
+        right after layer i's backward (bit-identical to opt.step(grads)
+        after the step); opt.t follows the steps. None switches it off."""
+        if opt is None:
+            _check(lib().qlx_ctx_set_adamw(self.h, 0, None, None, None, None, 0))
+            self.adam = None
+            return
+        L = len(opt.params)
+        P = (LoraBuf * L)(*[_lora_buf(x.A, x.B) for x in opt.params])
+        Mb = (LoraBuf * L)(*[_lora_buf(x.A, x.B) for x in opt.m])
+        Vb = (LoraBuf * L)(*[_lora_buf(x.A, x.B) for x in opt.v])
+        h = opt.hp
+        cfg = AdamwCfg(h["lr"], h["beta1"], h["beta2"], h["eps"], h["weight_decay"])
+        _check(lib().qlx_ctx_set_adamw(self.h, L, P, Mb, Vb, C.byref(cfg), opt.t + 1))
+        self.adam = opt
+
+    def _stepped(self) -> None:
+        """After a step call: the fused AdamW's update count moved on."""
+        if getattr(self, "adam", None) is not None:
+            t = C.c_int64()
+            _check(lib().qlx_ctx_adamw_t(self.h, C.byref(t)))
+            self.adam.t = int(t.value) - 1
+
     def set_keep_layers(self, on: bool = True) -> None:
         """Keep the two layers a step leaves in the slots for the next step
         (same workspace and blobs; see qlx_ctx_set_keep_layers)."""
@@ -555,6 +583,7 @@ def stream_step_sft(ctx: Context, model: StreamModel, tokens: torch.Tensor, mode
     ga = _grad_arr(grads)
     _check(lib().stream_step_sft(ctx.h, C.byref(model.c), _ptr(tokens), B, S, mode, _ptr(loss), ga, _ptr(ws),
                                  ws.numel(), _stream(stream)))
+    ctx._stepped()
 
 
 def stream_step_dpo(ctx: Context, model: StreamModel, chosen: torch.Tensor, rejected: torch.Tensor,
@@ -565,6 +594,7 @@ def stream_step_dpo(ctx: Context, model: StreamModel, chosen: torch.Tensor, reje
     _check(lib().stream_step_dpo(ctx.h, C.byref(model.c), _ptr(chosen), _ptr(rejected), P, S, prompt_len,
                                  float(beta), mode, ref_schedule, _ptr(loss), _ptr(logps), ga, _ptr(ws),
                                  ws.numel(), _stream(stream)))
+    ctx._stepped()
 
 
 def stream_step_pref(ctx: Context, model: StreamModel, kind: str, chosen: torch.Tensor, rejected: torch.Tensor,
@@ -582,6 +612,7 @@ def stream_step_pref(ctx: Context, model: StreamModel, kind: str, chosen: torch.
     _check(lib().stream_step_pref(ctx.h, C.byref(model.c), C.byref(cfg), _ptr(chosen), _ptr(rejected), P, S,
                                   prompt_len, mode, _ptr(loss), _ptr(logps), ga, _ptr(ws), ws.numel(),
                                   _stream(stream)))
+    ctx._stepped()
 
 
 # ------------------------------------------------------------------ profiling

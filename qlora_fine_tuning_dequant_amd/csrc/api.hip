@@ -394,6 +394,14 @@ struct qlx_ctx {
     qlx_layer_file* source = nullptr;  // QLX_STREAMED_DISK
     // qlx_ctx_set_keep_layers: what each slot held when the last step ended
     int keep_layers = 0;
+    // qlx_ctx_set_adamw: AdamW applied to each layer's adapters inside the
+    // backward, as soon as that layer's gradients are final
+    struct FusedAdam {
+        bool on = false;
+        std::vector<qlx_lora_buf> params, m, v;
+        qlx_adamw_cfg cfg{};
+        int64_t t = 0;  // update count of the next step
+    } adam;
     struct Kept {
         int layer = -1;
         const void* src = nullptr;  // the layer's host blob, or the layer file
@@ -633,6 +641,17 @@ class Streamer {
     int64_t nblocks_ = 0;
 };
 
+// A fused AdamW must update exactly the step's adapters.
+static void check_fused_adam(const qlx_ctx* ctx, const qlx_model* m) {
+    if (!ctx->adam.on) return;
+    QLX_REQUIRE(int(ctx->adam.params.size()) == m->dims.n_layers, QLX_EINVAL,
+                "fused AdamW: registered for another number of layers");
+    for (int l = 0; l < m->dims.n_layers; ++l)
+        for (int p = 0; p < 7; ++p)
+            QLX_REQUIRE(ctx->adam.params[l].A[p] == m->lora[l].A[p] && ctx->adam.params[l].B[p] == m->lora[l].B[p],
+                        QLX_EINVAL, "fused AdamW: its parameters are not the model's adapters");
+}
+
 static void validate_model(qlx_ctx* ctx, const qlx_model* m, int mode) {
     REQ_PTR(ctx, "ctx");
     REQ_PTR(m, "model");
@@ -656,6 +675,7 @@ static void validate_model(qlx_ctx* ctx, const qlx_model* m, int mode) {
     REQ_PTR(m->lm_head_f16, "model.lm_head_f16");
     REQ_PTR(m->final_norm, "model.final_norm");
     REQ_PTR(m->lora, "model.lora");
+    check_fused_adam(ctx, m);
     REQ_AL(m->lm_head_f16, "model.lm_head_f16");
     for (int i = 0; i < m->dims.n_layers; ++i) {
         validate_lora(&m->lora[i]);
@@ -775,21 +795,64 @@ static void head_grad(const qlx_model* m, const float* hL, int T, const int32_t*
 // dz is stored in fp16 scaled by 2^12 so that softmax values ~1/V stay normal.
 constexpr float kDzScale = 4096.f;
 
-static void backward_layers(Streamer& st, const qlx_model* m, const LayerGeom& g, StepWs& w, float* dh,
+static void check_adamw_cfg(const qlx_adamw_cfg* cfg, int64_t t) {
+    REQ_PTR(cfg, "cfg");
+    QLX_REQUIRE(t >= 1, QLX_EINVAL, "adamw: t (1-based update count) must be >= 1");
+    QLX_REQUIRE(std::isfinite(cfg->lr) && cfg->lr >= 0.0, QLX_EINVAL, "adamw: lr must be finite and >= 0");
+    QLX_REQUIRE(cfg->beta1 >= 0.0 && cfg->beta1 < 1.0 && cfg->beta2 >= 0.0 && cfg->beta2 < 1.0, QLX_EINVAL,
+                "adamw: betas must lie in [0, 1)");
+    QLX_REQUIRE(std::isfinite(cfg->eps) && cfg->eps > 0.0, QLX_EINVAL, "adamw: eps must be finite and > 0");
+    QLX_REQUIRE(std::isfinite(cfg->weight_decay) && cfg->weight_decay >= 0.0, QLX_EINVAL,
+                "adamw: weight_decay must be finite and >= 0");
+}
+// Update-t constants, formed in double (1 - beta before any rounding).
+static AdamScalars adam_scalars(const qlx_adamw_cfg& cfg, int64_t t) {
+    AdamScalars c;
+    c.decay = float(1.0 - cfg.lr * cfg.weight_decay);
+    c.b1 = float(cfg.beta1);
+    c.one_m_b1 = float(1.0 - cfg.beta1);
+    c.b2 = float(cfg.beta2);
+    c.one_m_b2 = float(1.0 - cfg.beta2);
+    c.step_size = float(cfg.lr / (1.0 - std::pow(cfg.beta1, double(t))));
+    c.inv_bc2_sqrt = float(1.0 / std::sqrt(1.0 - std::pow(cfg.beta2, double(t))));
+    c.eps = float(cfg.eps);
+    return c;
+}
+// AdamW on one layer's 14 adapter tensors: one launch.
+static void adamw_layer(const LayerGeom& g, int r, const qlx_lora_buf& p, const qlx_lora_grad& gr,
+                        const qlx_lora_buf& m, const qlx_lora_buf& v, const AdamScalars& c, hipStream_t s) {
+    AdamTensor ts[14];
+    for (int q = 0; q < 7; ++q) {
+        ts[2 * q] = {p.A[q], gr.dA[q], m.A[q], v.A[q], int64_t(r) * g.in[q]};
+        ts[2 * q + 1] = {p.B[q], gr.dB[q], m.B[q], v.B[q], int64_t(g.out[q]) * r};
+    }
+    launch_adamw(ts, 14, c, s);
+}
+
+// The backward over all layers, last to first. With a fused AdamW on the
+// context, layer i's adapters are updated right after its backward: nothing
+// later in the step reads them, and the update overlaps the copies and
+// compute of the layers still to come.
+static void backward_layers(qlx_ctx* ctx, Streamer& st, const qlx_model* m, const LayerGeom& g, StepWs& w, float* dh,
                             const qlx_lora_grad* grads, hipStream_t s) {
     const int L = m->dims.n_layers;
     const size_t TH = size_t(g.T) * g.H;
     float* cur = dh;
     float* nxt = (dh == w.dh[0]) ? w.dh[1] : w.dh[0];
+    const qlx_ctx::FusedAdam& fa = ctx->adam;
+    const LayerGeom g1 = make_geom(m->dims, 1, 1);
+    const AdamScalars ac = fa.on ? adam_scalars(fa.cfg, fa.t) : AdamScalars{};
     for (int i = L - 1; i >= 0; --i) {
         const void* blob = st.acquire(i);
         st.prefetch(i - 1);
         layer_backward(g, blob_ptrs(m->dims, blob), &m->lora[i], w.ckpt + size_t(i) * TH, cur, i > 0 ? nxt : nullptr,
                        &grads[i], w.lw, s);
+        if (fa.on) adamw_layer(g1, m->dims.lora_r, fa.params[i], grads[i], fa.m[i], fa.v[i], ac, s);
         st.release(i);
         std::swap(cur, nxt);
     }
 }
+
 
 }  // namespace qlx
 
@@ -862,6 +925,41 @@ int qlx_ctx_set_keep_layers(qlx_ctx* ctx, int on) {
         QLX_REQUIRE(on == 0 || on == 1, QLX_EINVAL, "keep_layers: 0 or 1");
         ctx->keep_layers = on;
         ctx->kept[0] = ctx->kept[1] = qlx_ctx::Kept{};
+    });
+}
+
+int qlx_ctx_set_adamw(qlx_ctx* ctx, int n_layers, const qlx_lora_buf* params, const qlx_lora_buf* m,
+                      const qlx_lora_buf* v, const qlx_adamw_cfg* cfg, int64_t t_next) {
+    return guarded([&] {
+        REQ_PTR(ctx, "ctx");
+        if (!params) {
+            ctx->adam = qlx_ctx::FusedAdam{};
+            return;
+        }
+        REQ_PTR(m, "m");
+        REQ_PTR(v, "v");
+        QLX_REQUIRE(n_layers >= 1, QLX_EINVAL, "adamw: n_layers must be >= 1");
+        check_adamw_cfg(cfg, t_next);
+        for (int l = 0; l < n_layers; ++l)
+            for (int p = 0; p < 7; ++p)
+                QLX_REQUIRE(params[l].A[p] && params[l].B[p] && m[l].A[p] && m[l].B[p] && v[l].A[p] && v[l].B[p],
+                            QLX_EINVAL, "adamw: every params/m/v A[p], B[p] must be set");
+        qlx_ctx::FusedAdam fa;
+        fa.on = true;
+        fa.params.assign(params, params + n_layers);
+        fa.m.assign(m, m + n_layers);
+        fa.v.assign(v, v + n_layers);
+        fa.cfg = *cfg;
+        fa.t = t_next;
+        ctx->adam = std::move(fa);
+    });
+}
+
+int qlx_ctx_adamw_t(const qlx_ctx* ctx, int64_t* t_next) {
+    return guarded([&] {
+        REQ_PTR(ctx, "ctx");
+        REQ_PTR(t_next, "t_next");
+        *t_next = ctx->adam.on ? ctx->adam.t : 0;
     });
 }
 
@@ -959,8 +1057,9 @@ int stream_step_sft(qlx_ctx* ctx, const qlx_model* m, const int32_t* tokens, int
         const float alpha = 1.0f / (kDzScale * float(batch) * float(seq - 1));
         head_grad(m, hL, T, tokens, seq, 0, w.lse, kDzScale, nullptr, alpha, w, w.dh[0], w.lw.partial, s);
         ctx->stats.layer_passes = 2 * L;
-        backward_layers(st, m, g, w, w.dh[0], grads, s);
+        backward_layers(ctx, st, m, g, w, w.dh[0], grads, s);
         st.keep();
+        if (ctx->adam.on) ctx->adam.t += 1;
         end_step(ctx, s);
     });
 }
@@ -1086,8 +1185,9 @@ static void pref_step(qlx_ctx* ctx, const qlx_model* m, const qlx_pref_cfg& cfg,
     // dz = g_seq (onehot - softmax) = (softmax - onehot) * (-g_seq)
     head_grad(m, hL, T, w.toks, seq, start, w.lse, -kDzScale, w.gseq, 1.0f / kDzScale, w, w.dh[0], w.lw.partial, s);
     ctx->stats.layer_passes = int64_t(2 + extra.size()) * L;
-    backward_layers(st, m, g, w, w.dh[0], grads, s);
+    backward_layers(ctx, st, m, g, w, w.dh[0], grads, s);
     st.keep();
+    if (ctx->adam.on) ctx->adam.t += 1;
     end_step(ctx, s);
 }
 
@@ -1123,14 +1223,7 @@ extern "C" int qlx_adamw_lora(const qlx_dims* d, const qlx_lora_buf* params, con
         REQ_PTR(grads, "grads");
         REQ_PTR(m, "m");
         REQ_PTR(v, "v");
-        REQ_PTR(cfg, "cfg");
-        QLX_REQUIRE(t >= 1, QLX_EINVAL, "adamw: t (1-based update count) must be >= 1");
-        QLX_REQUIRE(std::isfinite(cfg->lr) && cfg->lr >= 0.0, QLX_EINVAL, "adamw: lr must be finite and >= 0");
-        QLX_REQUIRE(cfg->beta1 >= 0.0 && cfg->beta1 < 1.0 && cfg->beta2 >= 0.0 && cfg->beta2 < 1.0, QLX_EINVAL,
-                    "adamw: betas must lie in [0, 1)");
-        QLX_REQUIRE(std::isfinite(cfg->eps) && cfg->eps > 0.0, QLX_EINVAL, "adamw: eps must be finite and > 0");
-        QLX_REQUIRE(std::isfinite(cfg->weight_decay) && cfg->weight_decay >= 0.0, QLX_EINVAL,
-                    "adamw: weight_decay must be finite and >= 0");
+        check_adamw_cfg(cfg, t);
         const int L = d->n_layers, r = d->lora_r;
         for (int l = 0; l < L; ++l) {
             validate_grads(&grads[l]);
@@ -1139,24 +1232,9 @@ extern "C" int qlx_adamw_lora(const qlx_dims* d, const qlx_lora_buf* params, con
                             QLX_EINVAL, "adamw: every params/m/v A[p], B[p] must be set");
         }
         const LayerGeom g = make_geom(*d, 1, 1);
-        AdamScalars c;
-        c.decay = float(1.0 - cfg->lr * cfg->weight_decay);
-        c.b1 = float(cfg->beta1);
-        c.one_m_b1 = float(1.0 - cfg->beta1);
-        c.b2 = float(cfg->beta2);
-        c.one_m_b2 = float(1.0 - cfg->beta2);
-        c.step_size = float(cfg->lr / (1.0 - std::pow(cfg->beta1, double(t))));
-        c.inv_bc2_sqrt = float(1.0 / std::sqrt(1.0 - std::pow(cfg->beta2, double(t))));
-        c.eps = float(cfg->eps);
+        const AdamScalars c = adam_scalars(*cfg, t);
         const hipStream_t s = static_cast<hipStream_t>(stream);
-        for (int l = 0; l < L; ++l) {
-            AdamTensor ts[14];
-            for (int p = 0; p < 7; ++p) {
-                ts[2 * p] = {params[l].A[p], grads[l].dA[p], m[l].A[p], v[l].A[p], int64_t(r) * g.in[p]};
-                ts[2 * p + 1] = {params[l].B[p], grads[l].dB[p], m[l].B[p], v[l].B[p], int64_t(g.out[p]) * r};
-            }
-            launch_adamw(ts, 14, c, s);
-        }
+        for (int l = 0; l < L; ++l) adamw_layer(g, r, params[l], grads[l], m[l], v[l], c, s);
     });
 }
 

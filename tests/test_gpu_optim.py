@@ -129,3 +129,62 @@ def test_training_lowers_the_loss_on_a_fixed_batch():
     losses, _, _ = _gpu_loop(d, 7, toks, B_.QLX_STREAMED, 8, 1e-2)
     assert losses[-1] < losses[0] - 0.05, losses
     assert all(np.isfinite(losses))
+
+
+def test_fused_adamw_equals_the_separate_update():
+    """AdamW registered on the context (each layer updated right after its
+    backward) gives the same bits as qlx_adamw_lora after each step: losses,
+    parameters and both moments over 3 steps, SFT and DPO, streamed (with
+    keep-layers) and resident; the update count follows the steps."""
+    import dataclasses
+    d = dataclasses.replace(synth.TINY, n_layers=3)
+    toks = torch.from_numpy(synth.tokens(5, 2, 32, d.vocab)).to(DEV)
+    ch, rj = (torch.from_numpy(x).to(DEV) for x in synth.dpo_pairs(5, 2, 32, 8, d.vocab))
+
+    def run(fused, mode, kind):
+        m, host = gpu_model(q, d, 5, "normal")
+        model = m.with_blobs(host) if mode == B_.QLX_STREAMED else m
+        opt = q.AdamW(d, m.lora, lr=1e-3, weight_decay=0.01)
+        ctx = q.Context(0)
+        ctx.set_keep_layers(True)
+        if fused:
+            ctx.set_adamw(opt)
+        ws = B_.workspace(B_.step_workspace_bytes(d, 0 if kind == "sft" else 1, 2, 32))
+        out = []
+        for _ in range(3):
+            grads = [q.LoraGrads(l) for l in m.lora]
+            loss = torch.empty(1, dtype=torch.float32, device=DEV)
+            if kind == "sft":
+                q.stream_step_sft(ctx, model, toks, mode, loss, grads, ws)
+            else:
+                lp = torch.empty(8, dtype=torch.float32, device=DEV)
+                q.stream_step_dpo(ctx, model, ch, rj, 8, 0.1, mode, B_.QLX_DPO_REF_FUSED, loss, lp, grads, ws)
+            if not fused:
+                opt.step(grads)
+            out.append(loss.clone())
+        torch.cuda.synchronize()
+        assert opt.t == 3
+        ctx.close()
+        state = [x for L in (opt.params + opt.m + opt.v) for x in L.A + L.B]
+        return out, state
+
+    for kind in ("sft", "dpo"):
+        for mode in (B_.QLX_STREAMED, B_.QLX_RESIDENT):
+            l0, s0 = run(False, mode, kind)
+            l1, s1 = run(True, mode, kind)
+            assert all(torch.equal(a, b) for a, b in zip(l0, l1)), (kind, mode)
+            assert all(torch.equal(a, b) for a, b in zip(s0, s1)), (kind, mode)
+
+
+def test_fused_adamw_needs_the_models_adapters():
+    d = synth.TINY
+    m, host = gpu_model(q, d, 6, "normal")
+    other = [q.LoraLayer([a.clone() for a in L.A], [b.clone() for b in L.B]) for L in m.lora]
+    ctx = q.Context(0)
+    ctx.set_adamw(q.AdamW(d, other))
+    with pytest.raises(q.QlxError) as e:
+        run_sft(q, m, synth.tokens(6, 1, 32, d.vocab), B_.QLX_RESIDENT, ctx)
+    assert e.value.code == B_.QLX_EINVAL and "adapters" in str(e.value)
+    ctx.set_adamw(None)
+    run_sft(q, m, synth.tokens(6, 1, 32, d.vocab), B_.QLX_RESIDENT, ctx)
+    ctx.close()
