@@ -719,7 +719,7 @@ __device__ __forceinline__ void dequant(const char* __restrict__ raw, const char
 // One 64-wide chunk of MFMAs for a (16 FI_) x (16 FJ_) wavefront tile. Row
 // (base + i*16 + lr) swizzles with (lr >> 1) & 7 only, so each K half has one
 // per-lane base.
-template <int FI_, int FJ_>
+template <int FI_, int FJ_, int TE_ = TE_BF16>
 __device__ __forceinline__ void mma(const uint16_t* __restrict__ As, const uint16_t* __restrict__ Bs,
                                     f32x4 (&acc)[FI_][FJ_], int rm, int rn, int lane) {
     const int lr = lane & 15, lc = lane >> 4, sw = (lr >> 1) & 7;
@@ -736,7 +736,7 @@ __device__ __forceinline__ void mma(const uint16_t* __restrict__ As, const uint1
 #pragma unroll
         for (int i = 0; i < FI_; ++i)
 #pragma unroll
-            for (int j = 0; j < FJ_; ++j) acc[i][j] = mfma16<TE_BF16>(a[i], b[j], acc[i][j]);
+            for (int j = 0; j < FJ_; ++j) acc[i][j] = mfma16<TE_>(a[i], b[j], acc[i][j]);
     }
 }
 
@@ -769,7 +769,7 @@ __device__ __forceinline__ void slab(const GemmParams& p, uint16_t* As, uint16_t
 // (16 FI_) x WN_ tile through LDS (stage: 16 x (WN_ + 4) floats of its own),
 // then each lane writes WN_/4 consecutive columns of one row: fp32 partials
 // when split, the GEMM's output otherwise.
-template <int FI_, int WN_>
+template <int FI_, int WN_, bool CE = false>
 __device__ __forceinline__ void epilogue(const GemmParams& p, const f32x4 (&acc)[FI_][WN_ / 16], float* stage, int row0,
                                          int col0, int split, int lane) {
     const int srow = (lane >> 2) & 15;
@@ -786,7 +786,9 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const f32x4 (&acc)
         const int row = row0 + i * 16 + srow;
         const int col = col0 + scol;
         const float* src = stage + srow * (WN_ + 4) + scol;
-        if (p.splits > 1) {
+        if constexpr (CE) {
+            ce_epilogue(p, row, col, src);
+        } else if (p.splits > 1) {
             float* dst = p.partial + (int64_t(split) * p.M + row) * p.N + col;
 #pragma unroll
             for (int c = 0; c < WN_ / 4; c += 4)
@@ -870,6 +872,113 @@ __global__ __launch_bounds__(fast::NTH) void k_nf4_tile(const GemmParams p) {
         slab<BKIND, BM, BN>(p, reinterpret_cast<uint16_t*>(sa(0)), sb(0), acc, m0, n0, wm * WM, wn * WN, lane);
     epilogue<FI, WN>(p, acc, reinterpret_cast<float*>(lds + OFF_A) + wave * (16 * (WN + 4)), m0 + wm * WM,
                      n0 + wn * WN, split, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Full-tile dense NT kernel for the LM head's fp16 products with the
+// cross-entropy epilogues (M % 256 == 0, N % 128 == 0, K % 64 == 0, 16-byte
+// aligned rows): the NF4 tile's pipeline with the weight tile fetched like the
+// activations. Per 64-wide K chunk each wavefront moves 4 KB of the 256-row A
+// tile and 2 KB of the 128-row B tile straight into LDS (global_load_lds, a
+// per-lane offset computed once plus a scalar offset per chunk), both two
+// chunks ahead in three stages; the same explicit partial waits, the same
+// XOR-swizzled unpadded tiles and 8 wavefronts of 64 x 64.
+namespace dense {
+using fast::BM;
+using fast::BN;
+using fast::NTH;
+using fast::NW;
+using fast::WGN;
+using fast::WM;
+using fast::WN;
+using fast::FI;
+using fast::FJ;
+using fast::SA;
+using fast::SB;
+constexpr int OFF_A = 0, OFF_B = 3 * SA, LDS_BYTES = OFF_B + 3 * SB;
+static_assert(LDS_BYTES <= 160 * 1024, "dense tile exceeds LDS");
+constexpr int NA = BM / 8 / NW, NB = BN / 8 / NW;  // 1 KB DMAs per wavefront per chunk
+struct Plan {
+    uint32_t a[NA], b[NB];
+    int wave;
+    __amdgpu_buffer_rsrc_t ra, rb;
+    // lane l of a 1 KB block lands at byte 16 l: row (block row 0) + (l >> 3),
+    // slot l & 7, which holds the row's global chunk (l & 7) ^ ((row >> 1) & 7)
+    __device__ __forceinline__ void init(const void* a0, const void* b0, int64_t lda, int64_t ldb) {
+        const int lane = threadIdx.x & 63;
+        wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        ra = fast::rsrc(a0);
+        rb = fast::rsrc(b0);
+#pragma unroll
+        for (int u = 0; u < NA; ++u) {
+            const int r = (wave * NA + u) * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ ((r >> 1) & 7);
+            a[u] = uint32_t((int64_t(r) * lda + c * 8) * 2);
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int r = (wave * NB + u) * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ ((r >> 1) & 7);
+            b[u] = uint32_t((int64_t(r) * ldb + c * 8) * 2);
+        }
+    }
+    __device__ __forceinline__ void dma(uint32_t soff, char* __restrict__ da, char* __restrict__ db) const {
+#pragma unroll
+        for (int u = 0; u < NA; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, fast::as_lds(da + (wave * NA + u) * 1024), 16, a[u], soff, 0,
+                                                     0);
+#pragma unroll
+        for (int u = 0; u < NB; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, fast::as_lds(db + (wave * NB + u) * 1024), 16, b[u], soff, 0,
+                                                     0);
+    }
+};
+}  // namespace dense
+
+template <int TE>
+__global__ __launch_bounds__(dense::NTH) void k_dense_tile(const GemmParams p) {
+    using namespace dense;
+    extern __shared__ __align__(16) char lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int gx = p.N / BN, gy = p.M / BM;
+    const int ntile = gx * gy;
+    int t = blockIdx.x;
+    if (ntile % 8 == 0) t = (t % 8) * (ntile / 8) + t / 8;
+    const int m0 = (t % gy) * BM, n0 = (t / gy) * BN;
+    const int nch = p.K / 64;  // >= 1
+    Plan plan;
+    plan.init(p.A + int64_t(m0) * p.lda, static_cast<const uint16_t*>(p.B) + int64_t(n0) * p.ldb, p.lda, p.ldb);
+
+    f32x4 acc[FI][FJ];
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // chunk c goes to stage c % 3; DMAs past the end re-read the last chunk
+    // into a stage nobody reads again, so every step issues the same count
+    auto sa = [&](int st) { return lds + OFF_A + st * SA; };
+    auto sb = [&](int st) { return lds + OFF_B + st * SB; };
+    auto dma = [&](int c, int st) { plan.dma(uint32_t(min(c, nch - 1)) * 128u, sa(st), sb(st)); };
+    dma(0, 0);
+    dma(1, 1);
+    fast::stage_sync<NA + NB>();  // chunk 0 in LDS
+    auto step = [&](int c, auto stage) {
+        constexpr int S0 = decltype(stage)::value, S2 = (S0 + 2) % 3;
+        dma(c + 2, S2);  // S2 was last read by chunk c - 1, finished before the last barrier
+        fast::mma<FI, FJ, TE>(reinterpret_cast<const uint16_t*>(sa(S0)), reinterpret_cast<const uint16_t*>(sb(S0)),
+                              acc, wm * WM, wn * WN, lane);
+        fast::stage_sync<NA + NB>();  // chunk c + 1 in LDS, c + 2 in flight
+    };
+    for (int c = 0; c < nch; c += 3) {
+        step(c, std::integral_constant<int, 0>());
+        if (c + 1 < nch) step(c + 1, std::integral_constant<int, 1>());
+        if (c + 2 < nch) step(c + 2, std::integral_constant<int, 2>());
+    }
+    fast::stage_sync<0>();
+    fast::epilogue<FI, WN, true>(p, acc, reinterpret_cast<float*>(lds + OFF_A) + wave * (16 * (WN + 4)),
+                                 m0 + wm * WM, n0 + wn * WN, 0, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1148,6 +1257,19 @@ static void launch_wide(const GemmParams& p, int tiles, hipStream_t s, const Pro
     hipExtLaunchKernelGGL(k_nf4_wide<BKIND>, dim3(tiles, p.splits), dim3(wide::NTH), wide::LDS_BYTES, s, prof.start(),
                           prof.stop(), 0, p);
 }
+static void launch_dense(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {
+    static bool allowed[64] = {};
+    int dev = 0;
+    QLX_CHECK_HIP(hipGetDevice(&dev));
+    QLX_REQUIRE(dev >= 0 && dev < 64, QLX_EUNSUPPORTED, "gemm: device index out of range");
+    if (!allowed[dev]) {
+        QLX_CHECK_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dense_tile<TE_F16>),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, dense::LDS_BYTES));
+        allowed[dev] = true;
+    }
+    hipExtLaunchKernelGGL(k_dense_tile<TE_F16>, dim3(tiles), dim3(dense::NTH), dense::LDS_BYTES, s, prof.start(),
+                          prof.stop(), 0, p);
+}
 static bool aligned8(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 7) == 0; }
 
 void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStream_t s) {
@@ -1179,7 +1301,15 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
     // bound by reading the long operand; 64 x 64 tiles with a K split keep
     // many workgroups streaming it without a large partial buffer.
     const bool skinny = !nf4 && te == TE_BF16 && p.batch == 1 && p.causal == CAUSAL_NONE && std::min(p.M, p.N) <= 256;
-    const TileCfg tc = fast_ok ? TileCfg{fast::BM, fast::BN} : skinny ? TileCfg{64, 64} : pick_tile(p, bkind);
+    // the LM head's fp16 NT products with a cross-entropy epilogue (never split)
+    const bool dense_fast = p.ce_mode && te == TE_F16 && akind == A_ROW && bkind == B_DENSE_NT && p.batch == 1 &&
+                            p.M % dense::BM == 0 && p.N % dense::BN == 0 && p.K % 64 == 0 && p.K >= 64 && p.a_vec &&
+                            p.b_vec && int64_t(dense::BM) * p.lda * 2 + int64_t(p.K) * 2 < (int64_t(1) << 31) &&
+                            int64_t(dense::BN) * p.ldb * 2 + int64_t(p.K) * 2 < (int64_t(1) << 31);
+    const TileCfg tc = fast_ok ? TileCfg{fast::BM, fast::BN}
+                       : dense_fast ? TileCfg{dense::BM, dense::BN}
+                       : skinny     ? TileCfg{64, 64}
+                                    : pick_tile(p, bkind);
     const int gx = (p.N + tc.bn - 1) / tc.bn, gy = (p.M + tc.bm - 1) / tc.bm;
     // split-K when the grid would leave CUs idle: shapes decide, nothing else
     p.splits = 1;
@@ -1270,7 +1400,8 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
                  : key == 21 ? 5 : key == 31 ? 6 : 7;
     const int bsz = p.batch * p.splits;
     {
-        ProfScope prof(p.tag ? p.tag : (wide_tile ? kWideNames[ni] : kNames[ni]), flops, bytes, s, fast_ok);
+        ProfScope prof(p.tag ? p.tag : (wide_tile ? kWideNames[ni] : kNames[ni]), flops, bytes, s,
+                       fast_ok || dense_fast);
         switch (key) {
             case A_ROW * 100 + B_NF4_NT * 10 + TE_BF16:
                 if (fast_ok)
@@ -1297,7 +1428,8 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
                 else launch_cfg<A_TRANS, B_DENSE_NN, TE_BF16, 128, 128, 64, 64>(p, bsz, s);
                 break;
             case A_ROW * 100 + B_DENSE_NT * 10 + TE_F16:
-                launch_cfg<A_ROW, B_DENSE_NT, TE_F16, 128, 128, 64, 64>(p, bsz, s);
+                if (dense_fast) launch_dense(p, tiles, s, prof);
+                else launch_cfg<A_ROW, B_DENSE_NT, TE_F16, 128, 128, 64, 64>(p, bsz, s);
                 break;
             case A_ROW * 100 + B_DENSE_NN * 10 + TE_F16:
                 launch_cfg<A_ROW, B_DENSE_NN, TE_F16, 128, 128, 64, 64>(p, bsz, s);

@@ -158,3 +158,18 @@ def test_wire_form_with_a_ragged_block_count():
     l_r, g_r, _ = _sft(m, toks, B_.QLX_RESIDENT)
     assert torch.equal(l_w, l_r) and _same(g_w, g_r)
     assert st["h2d_bytes"] == st["layer_reads"] * wt
+
+
+def test_tiny_sft_with_full_head_tiles_vs_oracle():
+    """4 x 64 = 256 tokens: the LM head's fp16 products (vocab 1024, hidden
+    256) take the full-tile DMA kernel with the cross-entropy epilogues."""
+    d = synth.TINY
+    m, host = gpu_model(q, d, 8, "normal")
+    toks = synth.tokens(8, 4, 64, d.vocab)
+    loss, g, _ = _sft(m.with_blobs(host), toks, B_.QLX_STREAMED)
+    loss_r, g_r, _ = _sft(m, toks, B_.QLX_RESIDENT)
+    assert torch.equal(loss, loss_r) and _same(g, g_r)
+    ref_loss, ref_g = oracle.sft_step(oracle_model(d, 8), lora_list(d, 8, "normal"), toks, d)
+    assert abs(loss.item() - ref_loss) < 1e-2
+    bad = {k: v for k, v in _grad_errs(g, ref_g).items() if not v < TOL}
+    assert not bad, bad
