@@ -829,10 +829,13 @@ static void adamw_layer(const LayerGeom& g, int r, const qlx_lora_buf& p, const 
     launch_adamw(ts, 14, c, s);
 }
 
-// The backward over all layers, last to first. With a fused AdamW on the
-// context, layer i's adapters are updated right after its backward: nothing
-// later in the step reads them, and the update overlaps the copies and
-// compute of the layers still to come.
+// The backward over all layers, last to first. The layer workspace still
+// holds the last layer's forward activations (its policy forward is the last
+// layer pass of every step's forward; the head only uses its own buffers and
+// the split-K scratch), so that layer is not recomputed. With a fused AdamW
+// on the context, layer i's adapters are updated right after its backward:
+// nothing later in the step reads them, and the update overlaps the copies
+// and compute of the layers still to come.
 static void backward_layers(qlx_ctx* ctx, Streamer& st, const qlx_model* m, const LayerGeom& g, StepWs& w, float* dh,
                             const qlx_lora_grad* grads, hipStream_t s) {
     const int L = m->dims.n_layers;
@@ -846,7 +849,7 @@ static void backward_layers(qlx_ctx* ctx, Streamer& st, const qlx_model* m, cons
         const void* blob = st.acquire(i);
         st.prefetch(i - 1);
         layer_backward(g, blob_ptrs(m->dims, blob), &m->lora[i], w.ckpt + size_t(i) * TH, cur, i > 0 ? nxt : nullptr,
-                       &grads[i], w.lw, s);
+                       &grads[i], w.lw, s, /*recompute=*/i != L - 1);
         if (fa.on) adamw_layer(g1, m->dims.lora_r, fa.params[i], grads[i], fa.m[i], fa.v[i], ac, s);
         st.release(i);
         std::swap(cur, nxt);

@@ -52,7 +52,11 @@ size_t layer_ws_bytes(const LayerGeom& g);
 void stage_lora(const LayerGeom& g, const qlx_lora* lora, LayerWs& w, hipStream_t s);
 void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora, bool lora_staged, const float* h_in,
                    float* h_out, LayerWs& w, hipStream_t s);
+// recompute = false: w still holds this layer's forward activations and
+// staged adapters (the last layer_forward on w was this layer's, with
+// `lora`, from h_in), so the forward is not run again.
 void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora, const float* h_in,
-                    const float* dh_out, float* dh_in, const qlx_lora_grad* grads, LayerWs& w, hipStream_t s);
+                    const float* dh_out, float* dh_in, const qlx_lora_grad* grads, LayerWs& w, hipStream_t s,
+                    bool recompute = true);
 
 }  // namespace qlx

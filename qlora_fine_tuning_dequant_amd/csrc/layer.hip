@@ -379,9 +379,10 @@ static void grad_A(const LayerGeom& g, const uint16_t* du, int nseg, const uint1
 }
 
 void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora, const float* h_in,
-                    const float* dh_out, float* dh_in, const qlx_lora_grad* grads, LayerWs& w, hipStream_t s) {
+                    const float* dh_out, float* dh_in, const qlx_lora_grad* grads, LayerWs& w, hipStream_t s,
+                    bool recompute) {
     const int T = g.T, H = g.H, r = g.r, S = g.S;
-    layer_forward(g, wt, lora, false, h_in, nullptr, w, s);
+    if (recompute) layer_forward(g, wt, lora, false, h_in, nullptr, w, s);
 
     // ---- down projection: out = h1 + down(act)
     launch_f32_to_bf16(dh_out, int64_t(T) * H, w.dy16, s);
