@@ -417,6 +417,7 @@ constexpr int kVocabChunk = 16384;  // LM-head backward: dz columns per chunk
 struct StepWs {
     char* slot[2];
     float* ckpt;     // (L+1) x [T, H]
+    uint16_t* usave;  // L x [T, 7r] bf16: each layer's u = x A^T from its forward, for its backward
     float* href[2];  // reference stream (DPO)
     int32_t* toks;   // [T]
     LayerWs lw;
@@ -450,6 +451,7 @@ static StepWs carve_step(Carver& c, const qlx_dims& d, int T, int kind, uint64_t
     w.slot[0] = c.take<char>(slot_bytes);
     w.slot[1] = c.take<char>(slot_bytes);
     w.ckpt = c.take<float>((L + 1) * Tz * H);
+    w.usave = c.take<uint16_t>(L * Tz * 7 * size_t(d.lora_r));
     if (kind >= 1) {
         w.href[0] = c.take<float>(Tz * H);
         w.href[1] = c.take<float>(Tz * H);
@@ -829,6 +831,11 @@ static void adamw_layer(const LayerGeom& g, int r, const qlx_lora_buf& p, const 
     launch_adamw(ts, 14, c, s);
 }
 
+// Layer i's kept u (u_qkv | u_o | u_gu | u_d, T x 7r bf16).
+static uint16_t* u_area(const StepWs& w, const LayerGeom& g, int i) {
+    return w.usave + size_t(i) * size_t(g.T) * 7 * size_t(g.r);
+}
+
 // The backward over all layers, last to first. The layer workspace still
 // holds the last layer's forward activations (its policy forward is the last
 // layer pass of every step's forward; the head only uses its own buffers and
@@ -848,8 +855,9 @@ static void backward_layers(qlx_ctx* ctx, Streamer& st, const qlx_model* m, cons
     for (int i = L - 1; i >= 0; --i) {
         const void* blob = st.acquire(i);
         st.prefetch(i - 1);
+        point_u(w.lw, u_area(w, g, i), g);  // its forward's u: the recompute skips those products
         layer_backward(g, blob_ptrs(m->dims, blob), &m->lora[i], w.ckpt + size_t(i) * TH, cur, i > 0 ? nxt : nullptr,
-                       &grads[i], w.lw, s, /*recompute=*/i != L - 1);
+                       &grads[i], w.lw, s, /*recompute=*/i != L - 1, /*u_given=*/true);
         if (fa.on) adamw_layer(g1, m->dims.lora_r, fa.params[i], grads[i], fa.m[i], fa.v[i], ac, s);
         st.release(i);
         std::swap(cur, nxt);
@@ -1050,6 +1058,7 @@ int stream_step_sft(qlx_ctx* ctx, const qlx_model* m, const int32_t* tokens, int
         for (int i = 0; i < L; ++i) {
             const void* blob = st.acquire(i);
             st.prefetch(i + 1);
+            point_u(w.lw, u_area(w, g, i), g);  // kept for this layer's backward
             layer_forward(g, blob_ptrs(d, blob), &m->lora[i], false, w.ckpt + size_t(i) * TH,
                           w.ckpt + size_t(i + 1) * TH, w.lw, s);
             st.release(i);
@@ -1126,8 +1135,13 @@ static void pref_step(qlx_ctx* ctx, const qlx_model* m, const qlx_pref_cfg& cfg,
         extra.push_back(Fwd{w.hklr[0], {w.hklr[1], w.hklr[0]}, false});  // mismatched pairs, reference
         extra.push_back(Fwd{w.hkl[0], {w.hkl[1], w.hkl[0]}, true});      // mismatched pairs, policy
     }
+    uint16_t* const own_u[4] = {w.lw.u_qkv, w.lw.u_o, w.lw.u_gu, w.lw.u_d};
     auto advance = [&](Fwd& f, const BlobPtrs& wt, int i) {
         float* nxt = (f.cur == f.buf[0]) ? f.buf[1] : f.buf[0];
+        w.lw.u_qkv = own_u[0];  // forward-only passes: u in the layer workspace's own buffers
+        w.lw.u_o = own_u[1];
+        w.lw.u_gu = own_u[2];
+        w.lw.u_d = own_u[3];
         layer_forward(g, wt, f.lora ? &m->lora[i] : nullptr, false, f.cur, nxt, w.lw, s);
         f.cur = nxt;
     };
@@ -1150,6 +1164,7 @@ static void pref_step(qlx_ctx* ctx, const qlx_model* m, const qlx_pref_cfg& cfg,
         const BlobPtrs wt = blob_ptrs(d, blob);
         if (!separate)
             for (Fwd& f : extra) advance(f, wt, i);
+        point_u(w.lw, u_area(w, g, i), g);  // kept for this layer's backward
         layer_forward(g, wt, &m->lora[i], false, w.ckpt + size_t(i) * TH, w.ckpt + size_t(i + 1) * TH, w.lw, s);
         st.release(i);
     }

@@ -50,13 +50,17 @@ BlobPtrs blob_ptrs(const qlx_dims& d, const void* blob);
 LayerWs carve_layer(Carver& c, const LayerGeom& g);
 size_t layer_ws_bytes(const LayerGeom& g);
 void stage_lora(const LayerGeom& g, const qlx_lora* lora, LayerWs& w, hipStream_t s);
+// u_given: w.u_qkv, u_o, u_gu, u_d already hold this layer's u = x A^T (kept
+// from its forward), so those four products are not run again.
 void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora, bool lora_staged, const float* h_in,
-                   float* h_out, LayerWs& w, hipStream_t s);
+                   float* h_out, LayerWs& w, hipStream_t s, bool u_given = false);
+// Points w's u buffers at a caller area of T * 7r bf16 (u_qkv | u_o | u_gu | u_d).
+void point_u(LayerWs& w, uint16_t* base, const LayerGeom& g);
 // recompute = false: w still holds this layer's forward activations and
 // staged adapters (the last layer_forward on w was this layer's, with
 // `lora`, from h_in), so the forward is not run again.
 void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora, const float* h_in,
                     const float* dh_out, float* dh_in, const qlx_lora_grad* grads, LayerWs& w, hipStream_t s,
-                    bool recompute = true);
+                    bool recompute = true, bool u_given = false);
 
 }  // namespace qlx

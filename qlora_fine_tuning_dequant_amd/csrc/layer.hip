@@ -129,6 +129,14 @@ BlobPtrs blob_ptrs(const qlx_dims& d, const void* blob) {
     return w;
 }
 
+void point_u(LayerWs& w, uint16_t* base, const LayerGeom& g) {
+    const size_t T = size_t(g.T), r = size_t(g.r);
+    w.u_qkv = base;
+    w.u_o = base + T * 3 * r;
+    w.u_gu = base + T * 4 * r;
+    w.u_d = base + T * 6 * r;
+}
+
 LayerWs carve_layer(Carver& c, const LayerGeom& g) {
     LayerWs w;
     const size_t T = size_t(g.T), H = size_t(g.H), r = size_t(g.r);
@@ -260,9 +268,10 @@ void stage_lora(const LayerGeom& g, const qlx_lora* lora, LayerWs& w, hipStream_
 // Forward. h_out == nullptr skips the down projection (the backward does not
 // need the layer output). lora_staged: adapters already staged in w.
 void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora, bool lora_staged, const float* h_in,
-                   float* h_out, LayerWs& w, hipStream_t s) {
+                   float* h_out, LayerWs& w, hipStream_t s, bool u_given) {
     const int T = g.T, H = g.H, r = g.r;
     const bool L = lora != nullptr;
+    const bool U = L && !u_given;  // compute the adapters' u = x A^T here
     if (L && !lora_staged) stage_lora(g, lora, w, s);
     if (!w.rope_ready) {  // once per workspace: every layer pass of a step shares the table
         launch_rope_table(g.S, g.hd, g.theta, w.rope_cs, s);
@@ -271,7 +280,7 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
 
     // attention block
     launch_rmsnorm_fwd(h_in, wt.g1, T, H, g.eps, w.n1, 0, w.rstd1, s);
-    if (L) {
+    if (U) {
         GemmParams pu = dense_gemm(T, 3 * r, H, w.n1, H, w.A_qkv, H);
         out_bf16(pu, w.u_qkv, 3 * r);
         pu.tag = "gemm_lora_u";
@@ -292,7 +301,7 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
     }
     launch_rope(w.qkv, g.nqkv, T, g.S, 0, g.nH + g.nKV, g.hd, w.rope_cs, s);  // q and k heads are contiguous
     launch_flash_fwd(attn_args(g, w), s);
-    if (L) {
+    if (U) {
         GemmParams pu = dense_gemm(T, r, g.qdim, w.oattn, g.qdim, w.A_o, g.qdim);
         out_bf16(pu, w.u_o, r);
         pu.tag = "gemm_lora_u";
@@ -314,7 +323,7 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
     }
     // MLP block
     launch_rmsnorm_fwd(w.h1, wt.g2, T, H, g.eps, w.n2, 0, w.rstd2, s);
-    if (L) {
+    if (U) {
         GemmParams pu = dense_gemm(T, 2 * r, H, w.n2, H, w.A_gu, H);
         out_bf16(pu, w.u_gu, 2 * r);
         pu.tag = "gemm_lora_u";
@@ -334,7 +343,7 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
         gemm(p, A_ROW, B_NF4_NT, TE_BF16, w.partial, s);
     }
     launch_swiglu_fwd(w.gu, T, g.I, w.act, s);
-    if (L) {
+    if (U) {
         GemmParams pu = dense_gemm(T, r, g.I, w.act, g.I, w.A_d, g.I);
         out_bf16(pu, w.u_d, r);
         pu.tag = "gemm_lora_u";
@@ -380,9 +389,9 @@ static void grad_A(const LayerGeom& g, const uint16_t* du, int nseg, const uint1
 
 void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora, const float* h_in,
                     const float* dh_out, float* dh_in, const qlx_lora_grad* grads, LayerWs& w, hipStream_t s,
-                    bool recompute) {
+                    bool recompute, bool u_given) {
     const int T = g.T, H = g.H, r = g.r, S = g.S;
-    if (recompute) layer_forward(g, wt, lora, false, h_in, nullptr, w, s);
+    if (recompute) layer_forward(g, wt, lora, false, h_in, nullptr, w, s, u_given);
 
     // ---- down projection: out = h1 + down(act)
     launch_f32_to_bf16(dh_out, int64_t(T) * H, w.dy16, s);
