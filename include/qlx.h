@@ -126,7 +126,8 @@ int qlora_linear_fwd(const uint16_t* x, int64_t T, qlx_nf4 W, const float* A, co
  *   du = s dy B;  dx = dy W' + du A (bf16 [T, in], NULL = skip);
  *   dB = s dy^T (x A^T) (fp32 [out, r]);  dA = du^T x (fp32 [r, in]).
  * accumulate = 1 adds into dA/dB instead of overwriting them. With LoRA off
- * (A = B = NULL) only dx is produced. */
+ * (A = B = NULL) only dx is produced. T = 0 writes no dx and leaves dA/dB
+ * zero (or unchanged with accumulate = 1); the forward with T = 0 is a no-op. */
 int qlora_linear_bwd(const uint16_t* dy, const uint16_t* x, int64_t T, qlx_nf4 W,
                      const float* A, const float* B, int r, float scale,
                      uint16_t* dx, float* dA, float* dB, int accumulate,
@@ -174,7 +175,8 @@ typedef struct { float* dA[7]; float* dB[7]; } qlx_lora_grad;
  * o QLoRA + residual, RMSNorm, SwiGLU QLoRA MLP + residual).
  * h_in / h_out: the fp32 residual stream [batch*seq, hidden] (row b*seq + t).
  * blob: DEVICE layer blob (layout above). lora = NULL runs the base only.
- * Positions restart at 0 for every sequence; attention is causal. */
+ * Positions restart at 0 for every sequence; attention is causal.
+ * batch >= 1 and seq >= 1, else QLX_EINVAL. */
 size_t qlx_layer_workspace_bytes(const qlx_dims* d, int batch, int seq);
 int layer_fwd(const qlx_dims* d, const void* blob, const qlx_lora* lora, const float* h_in,
               int batch, int seq, float* h_out, void* ws, size_t ws_bytes, void* stream);
@@ -328,7 +330,8 @@ size_t qlx_step_workspace_bytes(const qlx_dims* d, int kind, int batch, int seq)
  * layer-boundary checkpoints; the two layers still in the slots at the turn
  * are not copied again), final RMSNorm, fp16 LM head, next-token
  * cross-entropy averaged over batch*(seq-1) positions.
- * tokens: DEVICE int32 [batch, seq]. loss: DEVICE fp32 scalar.
+ * tokens: DEVICE int32 [batch, seq], batch >= 1, seq >= 2 (else QLX_EINVAL:
+ * a next-token loss needs a second position). loss: DEVICE fp32 scalar.
  * grads: HOST array of n_layers qlx_lora_grad (device fp32 buffers, overwritten).
  * Streamed and resident modes give bit-identical loss and gradients. */
 int stream_step_sft(qlx_ctx* ctx, const qlx_model* model, const int32_t* tokens, int batch,
@@ -337,7 +340,8 @@ int stream_step_sft(qlx_ctx* ctx, const qlx_model* model, const int32_t* tokens,
 
 /* One DPO step (Rafailov et al. 2023, eq. 7; reference = the same layer
  * stream with LoRA off). chosen/rejected: DEVICE int32 [pairs, seq]; the
- * response of each sequence is positions prompt_len..seq-1. The batch is
+ * response of each sequence is positions prompt_len..seq-1 (1 <= prompt_len
+ * < seq, 1 <= pairs <= 32, else QLX_EINVAL). The batch is
  * [chosen_1..chosen_P, rejected_1..rejected_P].
  * ref_schedule = QLX_DPO_REF_FUSED computes the reference forward on each
  *   layer while it is resident for the policy forward (layer reads as SFT);

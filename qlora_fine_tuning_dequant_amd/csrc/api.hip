@@ -174,7 +174,14 @@ int qlora_linear_bwd(const uint16_t* dy, const uint16_t* x, int64_t T, qlx_nf4 W
             REQ_PTR(dA, "dA");
             REQ_PTR(dB, "dB");
         }
-        if (T == 0) return;
+        if (T == 0) {  // empty sums over the tokens: dA = dB = 0 (or unchanged when accumulating)
+            if (A && !accumulate) {
+                hipStream_t s = static_cast<hipStream_t>(stream);
+                launch_fill_u32(reinterpret_cast<uint32_t*>(dA), int64_t(r) * W.cols, 0u, s);
+                launch_fill_u32(reinterpret_cast<uint32_t*>(dB), W.rows * int64_t(r), 0u, s);
+            }
+            return;
+        }
         REQ_PTR(dy, "dy");
         REQ_PTR(x, "x");
         const int rr = A ? r : 0;

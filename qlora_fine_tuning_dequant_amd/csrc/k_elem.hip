@@ -409,7 +409,8 @@ void launch_f32_to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------ stream debugging
-// Fills n 32-bit words with one pattern (the poison of a freed slot).
+// Fills n 32-bit words with one pattern (the poison of a freed slot, the
+// zero gradients of an empty batch).
 __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
         p[i] = v;

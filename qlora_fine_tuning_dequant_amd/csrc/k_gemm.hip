@@ -462,6 +462,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm(const GemmP
     const uint16_t* A = p.A + int64_t(bo) * p.a_so + int64_t(bi / p.a_grp) * p.a_si;
     const uint16_t* Bd =
         static_cast<const uint16_t*>(p.B) + (kNf4 ? 0 : int64_t(bo) * p.b_so + int64_t(bi / p.b_grp) * p.b_si);
+    if constexpr (BKIND == B_DENSE_NN)
+        if (p.seg_rows > 0) Bd += p.bseg[m0 / p.seg_rows];  // the segment's B columns
     const uint8_t* Bq = static_cast<const uint8_t*>(p.B);
 
     int kbeg = split * p.kchunk, kend = min(p.K, kbeg + p.kchunk);
@@ -1292,6 +1294,15 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
     else if (bkind == B_NF4_NN) p.b_vec = aligned16(p.B) && p.nf4_cols % 64 == 0;
     else if (bkind == B_DENSE_NT) p.b_vec = aligned16(p.B) && p.ldb % 8 == 0 && p.b_so % 8 == 0 && p.b_si % 8 == 0;
     else p.b_vec = aligned8(p.B) && p.ldb % 4 == 0 && p.b_so % 4 == 0 && p.b_si % 4 == 0;
+    if (p.seg_rows > 0)
+        QLX_REQUIRE(p.batch == 1 && int64_t(p.M) <= 8 * int64_t(p.seg_rows), QLX_EINVAL,
+                    "gemm: at most 8 output segments, no batching");
+    for (int i = 0; i < 8; ++i) {
+        if (p.bseg[i] == 0) continue;
+        QLX_REQUIRE(bkind == B_DENSE_NN && p.seg_rows > 0 && p.seg_rows % 128 == 0 && p.bseg[i] % 4 == 0 &&
+                        p.causal == CAUSAL_NONE,
+                    QLX_EINVAL, "gemm: per-segment B offsets need a dense NN B and 128-row segments");
+    }
     if (p.K2 > 0) {
         p.a2_vec = aligned16(p.A2) && p.lda2 % 8 == 0;
         p.b2_vec = (bkind == B_NF4_NT) ? (aligned16(p.B2) && p.ldb2 % 8 == 0) : (aligned8(p.B2) && p.ldb2 % 4 == 0);

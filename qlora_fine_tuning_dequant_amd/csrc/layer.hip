@@ -374,6 +374,35 @@ static void grad_B(const LayerGeom& g, const uint16_t* dy, int64_t ld_dy, int ou
     p.tag = "gemm_lora_dB";
     gemm(p, A_TRANS, B_DENSE_NN, TE_BF16, w.partial, s);
 }
+// dB of projections whose outputs are consecutive column blocks of dy, cut
+// into nseg segments of seg rows, in one product: segment i reads the r
+// columns of u from ucol[i] and writes its rows to dB[i]. Where a segment is
+// not a whole number of 128-row tiles (or there are more than 8), each
+// projection's product runs on its own: proj[j] = {first segment, segments}.
+static void grad_B_group(const LayerGeom& g, const uint16_t* dy, int64_t ld_dy, int seg, int nseg, const uint16_t* u,
+                         int64_t ld_u, const int* ucol, float* const* dB, LayerWs& w, hipStream_t s) {
+    bool one = seg % 128 == 0 && nseg <= 8;
+    for (int i = 0; i < nseg; ++i) one = one && ucol[i] % 4 == 0;
+    if (one) {
+        GemmParams p = dense_gemm(nseg * seg, g.r, g.T, dy, ld_dy, u, ld_u);
+        out_f32(p, dB[0], g.r);
+        p.seg_rows = seg;
+        for (int i = 0; i < nseg; ++i) {
+            p.Cseg[i] = dB[i];
+            p.bseg[i] = ucol[i];
+        }
+        p.alpha = g.s;
+        p.tag = "gemm_lora_dB";
+        gemm(p, A_TRANS, B_DENSE_NN, TE_BF16, w.partial, s);
+        return;
+    }
+    for (int i = 0; i < nseg;) {  // runs of segments with the same u columns are one projection
+        int j = i + 1;
+        while (j < nseg && ucol[j] == ucol[i] && dB[j] == dB[j - 1] + int64_t(seg) * g.r) ++j;
+        grad_B(g, dy + int64_t(i) * seg, ld_dy, (j - i) * seg, u + ucol[i], ld_u, dB[i], w, s);
+        i = j;
+    }
+}
 // dA (stacked over nseg segments of r rows) = du^T x  (M = nseg*r, N = in, K = T).
 static void grad_A(const LayerGeom& g, const uint16_t* du, int nseg, const uint16_t* x, int in_f, float* const* dA,
                    LayerWs& w, hipStream_t s) {
@@ -434,8 +463,11 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
         out_f32(p, w.dn2, H);
         gemm(p, A_ROW, B_NF4_NN, TE_BF16, w.partial, s);
     }
-    grad_B(g, w.dgu, 2 * g.I, g.I, w.u_gu, 2 * r, grads->dB[4], w, s);
-    grad_B(g, w.dgu + g.I, 2 * g.I, g.I, w.u_gu + r, 2 * r, grads->dB[5], w, s);
+    {
+        const int ucol[2] = {0, r};
+        float* dB[2] = {grads->dB[4], grads->dB[5]};
+        grad_B_group(g, w.dgu, 2 * g.I, g.I, 2, w.u_gu, 2 * r, ucol, dB, w, s);
+    }
     {
         float* dA[2] = {grads->dA[4], grads->dA[5]};
         grad_A(g, w.du_gu, 2, w.n2, H, dA, w, s);
@@ -489,9 +521,21 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
         gemm(p, A_ROW, B_NF4_NN, TE_BF16, w.partial, s);
         launch_rmsnorm_bwd(w.dn1, h_in, wt.g1, w.rstd1, w.dh1, T, H, dh_in, s);
     }
-    grad_B(g, w.dqkv, g.nqkv, g.qdim, w.u_qkv, 3 * r, grads->dB[0], w, s);
-    grad_B(g, w.dqkv + g.qdim, g.nqkv, g.kvdim, w.u_qkv + r, 3 * r, grads->dB[1], w, s);
-    grad_B(g, w.dqkv + g.qdim + g.kvdim, g.nqkv, g.kvdim, w.u_qkv + 2 * r, 3 * r, grads->dB[2], w, s);
+    {  // q as qdim / kvdim segments of kvdim rows, then k and v
+        const int nq = g.qdim / g.kvdim;
+        int ucol[8];
+        float* dB[8];
+        if (g.qdim % g.kvdim == 0 && nq + 2 <= 8) {
+            for (int i = 0; i < nq; ++i) ucol[i] = 0, dB[i] = grads->dB[0] + int64_t(i) * g.kvdim * r;
+            ucol[nq] = r, dB[nq] = grads->dB[1];
+            ucol[nq + 1] = 2 * r, dB[nq + 1] = grads->dB[2];
+            grad_B_group(g, w.dqkv, g.nqkv, g.kvdim, nq + 2, w.u_qkv, 3 * r, ucol, dB, w, s);
+        } else {
+            grad_B(g, w.dqkv, g.nqkv, g.qdim, w.u_qkv, 3 * r, grads->dB[0], w, s);
+            grad_B(g, w.dqkv + g.qdim, g.nqkv, g.kvdim, w.u_qkv + r, 3 * r, grads->dB[1], w, s);
+            grad_B(g, w.dqkv + g.qdim + g.kvdim, g.nqkv, g.kvdim, w.u_qkv + 2 * r, 3 * r, grads->dB[2], w, s);
+        }
+    }
     {
         float* dA[3] = {grads->dA[0], grads->dA[1], grads->dA[2]};
         grad_A(g, w.du_qkv, 3, w.n1, H, dA, w, s);

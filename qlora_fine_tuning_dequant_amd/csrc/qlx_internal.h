@@ -126,8 +126,12 @@ struct GemmParams {
     const float* R = nullptr;  // residual added after alpha (fp32, ldr), no batching
     int64_t ldr = 0;
     int accumulate = 0;        // C (fp32) += result
-    int seg_rows = 0;          // >0: row m goes to Cseg[m / seg_rows] row m % seg_rows
-    void* Cseg[4] = {nullptr, nullptr, nullptr, nullptr};
+    int seg_rows = 0;          // >0: row m goes to Cseg[m / seg_rows] row m % seg_rows (M <= 8 seg_rows)
+    void* Cseg[8] = {};
+    // dense NN B with seg_rows > 0: the M-tiles of segment i read B from
+    // element offset bseg[i] (a multiple of 4; seg_rows a multiple of 128 when
+    // any offset is non-zero, so no tile straddles two segments)
+    int64_t bseg[8] = {};
     int causal = CAUSAL_NONE;
     int slab_alg_k = -1;  // algorithmic K of the slab for flop accounting (-1: K2)
     // LM-head cross-entropy epilogues (fp16 NT products on 64-wide wavefront

@@ -92,6 +92,25 @@ def test_linear_and_layer_argument_checks_run_before_any_launch():
     assert L.layer_bwd(C.byref(d), 256, None, 512, 512, 1, 64, None, None, 4096, need, None) == b.QLX_EINVAL
 
 
+def test_empty_inputs_are_no_ops_and_negative_sizes_are_refused():
+    """Zero elements or zero tokens return OK before any pointer is read or
+    anything is launched (so NULL buffers are fine); negative sizes are errors."""
+    L = b.lib()
+    assert L.nf4_quantize(None, 0, 64, None, None, None) == b.QLX_OK
+    assert L.nf4_quantize(None, 64, 0, None, None, None) == b.QLX_OK
+    assert L.nf4_dequant(None, None, 0, 64, b.QLX_F32, None, None) == b.QLX_OK
+    assert L.nf4_quantize(None, -1, 64, None, None, None) == b.QLX_EINVAL
+    assert L.nf4_dequant(None, None, 1, -64, b.QLX_BF16, None, None) == b.QLX_EINVAL
+    assert L.nf4_dequant(None, None, 0, 64, 7, None, None) == b.QLX_EINVAL    # dtype checked first
+    W = b.NF4(256, 512, 16, 16)  # fake but aligned addresses; nothing is launched
+    assert L.qlora_linear_fwd(None, 0, W, None, None, 0, 1.0, None, None, 0, None) == b.QLX_OK
+    assert L.qlora_linear_fwd(None, -1, W, None, None, 0, 1.0, None, None, 0, None) == b.QLX_EINVAL
+    assert L.qlora_linear_bwd(None, None, 0, W, None, None, 0, 1.0, None, None, None, 0, None, 0, None) == b.QLX_OK
+    # LoRA on, T = 0, accumulating: dA and dB stay as they are (no launch)
+    assert L.qlora_linear_bwd(None, None, 0, W, 1024, 2048, 4, 1.0, None, 4096, 8192, 1, None, 0, None) == b.QLX_OK
+    assert L.qlora_linear_bwd(None, None, 0, W, 1024, 2048, 4, 1.0, None, None, 8192, 1, None, 0, None) == b.QLX_EINVAL
+
+
 def test_workspace_sizes_scale_with_tokens():
     L = b.lib()
     d = _dims()

@@ -160,6 +160,40 @@ def test_lora_zero_B_is_bit_exact_base_and_lora_off(T, in_f, out_f, r):
     assert rel_l2(to_np(y_off), y_ref) < TOL
 
 
+def test_empty_inputs():
+    """Zero elements / zero tokens: quantize and dequant leave their outputs
+    alone, the forward writes nothing, and the backward's empty sums over the
+    tokens give dA = dB = +0.0 exactly (accumulating leaves them unchanged)."""
+    packed = torch.full((4,), 0xAB, dtype=torch.uint8, device=DEV)
+    absmax = torch.full((2,), 3.0, dtype=torch.float32, device=DEV)
+    q.nf4_quantize(torch.empty(0, 64, dtype=torch.bfloat16, device=DEV), packed, absmax)
+    out = torch.full((8,), 5.0, dtype=torch.float32, device=DEV)
+    q.nf4_dequant(packed, absmax, 0, 64, out)
+    torch.cuda.synchronize()
+    assert (packed == 0xAB).all() and (absmax == 3.0).all() and (out == 5.0).all()
+
+    out_f, in_f, r = 256, 512, 8
+    W = q.NF4Matrix.quantize(bf16_dev(_w_bits(out_f, in_f, 3)))
+    g = np.random.default_rng(3)
+    A = f32_dev(g.standard_normal((r, in_f)).astype(np.float32))
+    B = f32_dev(g.standard_normal((out_f, r)).astype(np.float32))
+    x = torch.empty(0, in_f, dtype=torch.bfloat16, device=DEV)
+    dy = torch.empty(0, out_f, dtype=torch.bfloat16, device=DEV)
+    y = torch.empty(0, out_f, dtype=torch.bfloat16, device=DEV)
+    dx = torch.empty(0, in_f, dtype=torch.bfloat16, device=DEV)
+    q.qlora_linear_fwd(x, W, A, B, 2.0, y)
+    dA = torch.full((r, in_f), float("nan"), dtype=torch.float32, device=DEV)
+    dB = torch.full((out_f, r), float("nan"), dtype=torch.float32, device=DEV)
+    q.qlora_linear_bwd(dy, x, W, A, B, 2.0, dx, dA, dB)
+    torch.cuda.synchronize()
+    assert (dA.view(torch.int32) == 0).all() and (dB.view(torch.int32) == 0).all()
+    dA.fill_(1.5)
+    dB.fill_(-2.5)
+    q.qlora_linear_bwd(dy, x, W, A, B, 2.0, None, dA, dB, accumulate=True)
+    torch.cuda.synchronize()
+    assert (dA == 1.5).all() and (dB == -2.5).all()
+
+
 def test_linear_dequant_operand_is_exactly_bf16_of_dequant():
     """A one-hot input row selects a weight column, so y = bf16(W'[:, j]) exactly."""
     out_f, in_f = 256, 512
