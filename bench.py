@@ -62,17 +62,17 @@ WORKLOADS = {
 }
 
 
-# HBM bytes per launch of the NF4 GEMM rows that come out dominant on the
-# default workload (gemm_nf4_nn in a plain run; gemm_nf4_nt_wide under the
-# rocprofv3 kernel trace, which stretches one of its dispatches per run to
-# ~7 ms), from two rocprofv3 --pmc passes
+# HBM bytes per launch of the NF4 GEMM rows that can come out dominant on the
+# default workload (gemm_nf4_nn; under a short rocprofv3 kernel trace, whose
+# occasional multi-millisecond dispatch stalls land on one kernel, another
+# row can win), from two rocprofv3 --pmc passes
 # (FETCH_SIZE, WRITE_SIZE) over the default workload, each scaled by the same
 # counter on a plain 1 GiB device copy (factors 2.000 and 1.000); valid only
 # for the kernel source they were taken on (SHA-256 prefix of csrc/k_gemm.hip).
-MEASURED_TRAFFIC = {("sft8b_b1", "streamed", "gemm_nf4_nn"): {"bytes": int((116.5 + 28.8) * 1e6),
-                                                              "k_gemm_sha256": "41a216cf9004bf9d"},
-                    ("sft8b_b1", "streamed", "gemm_nf4_nt_wide"): {"bytes": int((108.7 + 29.4) * 1e6),
-                                                                   "k_gemm_sha256": "41a216cf9004bf9d"}}
+MEASURED_TRAFFIC = {("sft8b_b1", "streamed", "gemm_nf4_nn"): {"bytes": int((114.8 + 28.8) * 1e6),
+                                                              "k_gemm_sha256": "94913fdd93f4a6cd"},
+                    ("sft8b_b1", "streamed", "gemm_nf4_nt_wide"): {"bytes": int((108.5 + 29.4) * 1e6),
+                                                                   "k_gemm_sha256": "94913fdd93f4a6cd"}}
 
 
 def measured_traffic(workload: str, mode: str, kernel: str):
