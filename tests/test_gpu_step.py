@@ -113,6 +113,30 @@ def test_streamed_mode_rejects_unpinned_blobs(tiny):
     assert e.value.code == B_.QLX_ENOTPINNED
 
 
+def test_degenerate_step_shapes_are_rejected_before_any_launch(tiny):
+    """batch 0, seq 1 (no next token), pairs 0 and a prompt that leaves no
+    response are QLX_EINVAL; the context steps normally afterwards."""
+    d, m, host = tiny
+    ctx = q.Context(0)
+    grads = [q.LoraGrads(l) for l in m.lora]
+    loss = torch.empty(1, dtype=torch.float32, device=DEV)
+    logps = torch.empty(8, dtype=torch.float32, device=DEV)
+    ws = B_.workspace(B_.step_workspace_bytes(d, 1, 2, 64))
+    tok = lambda b, s: torch.zeros(b, s, dtype=torch.int32, device=DEV)  # noqa: E731
+    R, F = B_.QLX_RESIDENT, B_.QLX_DPO_REF_FUSED
+    cases = [lambda: q.stream_step_sft(ctx, m, tok(1, 1), R, loss, grads, ws),
+             lambda: q.stream_step_sft(ctx, m, tok(0, 64), R, loss, grads, ws),
+             lambda: q.stream_step_dpo(ctx, m, tok(0, 64), tok(0, 64), 16, 0.1, R, F, loss, logps, grads, ws),
+             lambda: q.stream_step_dpo(ctx, m, tok(2, 64), tok(2, 64), 64, 0.1, R, F, loss, logps, grads, ws),
+             lambda: q.stream_step_dpo(ctx, m, tok(2, 64), tok(2, 64), 0, 0.1, R, F, loss, logps, grads, ws)]
+    for f in cases:
+        with pytest.raises(q.QlxError) as e:
+            f()
+        assert e.value.code == B_.QLX_EINVAL
+    loss2, _, _ = _sft(m, synth.tokens(0, 1, 64, d.vocab), R, ctx)
+    assert np.isfinite(loss2.item())
+
+
 def test_wire_form_streams_bit_identical_with_fewer_bytes():
     """Streaming the wire form (block maxima as bf16, widened on the GPU
     after the copy) gives the resident run's loss, log-probs and gradients
