@@ -525,8 +525,9 @@ class Streamer {
     // End of a step: with keep-layers on, remember what the slots hold.
     void keep() {
         if (!ctx_->keep_layers || mode_ == QLX_RESIDENT) return;
-        for (int sl = 0; sl < 2; ++sl)
-            if (held_[sl] >= 0) ctx_->kept[sl] = qlx_ctx::Kept{held_[sl], source_of(held_[sl]), w_.slot[sl], form_};
+        for (int sl = 0; sl < 2; ++sl)  // (a slot whose widen never ran is not kept)
+            if (held_[sl] >= 0 && !widen_pending_[sl])
+                ctx_->kept[sl] = qlx_ctx::Kept{held_[sl], source_of(held_[sl]), w_.slot[sl], form_};
     }
     // Make layer i resident (if not already), wait for it on the main stream,
     // and return its device pointer. prefetch_next >= 0 also starts the copy
@@ -536,6 +537,21 @@ class Streamer {
         const int sl = slot_of(i);
         if (held_[sl] != i) issue_copy(i, sl);
         QLX_CHECK_HIP(hipStreamWaitEvent(main_, ctx_->copy_done[sl], 0));
+        if (widen_pending_[sl]) {
+            // wire form: block maxima bf16 -> fp32 and the gains into their
+            // full-form places, on the compute stream, so the copy stream
+            // goes straight on to the next layer's bytes
+            char* b = w_.slot[sl];
+            const char* tail = b + bytes_;  // wire offset wire_[7] landed here
+            launch_blob_widen(reinterpret_cast<const uint16_t*>(tail), nblocks_,
+                              reinterpret_cast<const float*>(tail + (wire_[14] - wire_[7])),
+                              reinterpret_cast<const float*>(tail + (wire_[15] - wire_[7])), m_->dims.hidden,
+                              reinterpret_cast<uint32_t*>(b + full_[7]), reinterpret_cast<float*>(b + full_[14]),
+                              reinterpret_cast<float*>(b + full_[15]), main_);
+            widen_pending_[sl] = false;
+            if (ctx_->debug & QLX_DEBUG_POISON_LIVE)  // control: poisons the slot it just filled
+                launch_fill_u32(reinterpret_cast<uint32_t*>(b), int64_t(bytes_ / 4), 0xFFFFFFFFu, main_);
+        }
         if (ctx_->debug & QLX_DEBUG_DELAY_COMPUTE) launch_spin(ctx_->delay_us, main_);
         return w_.slot[sl];
     }
@@ -593,8 +609,16 @@ class Streamer {
         if (ctx_->copy_split == 2 && nbytes > 8192) {
             // the two halves on two streams, so two copy engines share the link
             const uint64_t h = (nbytes / 2 + 4095) & ~uint64_t(4095);
-            QLX_CHECK_HIP(hipEventRecord(ctx_->copy_start, ctx_->side));
-            QLX_CHECK_HIP(hipStreamWaitEvent(ctx_->side2, ctx_->copy_start, 0));
+            if (ctx_->debug & (QLX_DEBUG_POISON | QLX_DEBUG_DELAY_COPY)) {
+                // after the poison fill / spin on the first copy stream
+                QLX_CHECK_HIP(hipEventRecord(ctx_->copy_start, ctx_->side));
+                QLX_CHECK_HIP(hipStreamWaitEvent(ctx_->side2, ctx_->copy_start, 0));
+            } else {
+                // only after the slot's previous user, as the first half: at a
+                // layer boundary neither copy stream waits for the other
+                // (a hop between the two streams cost ~30 us of idle link)
+                QLX_CHECK_HIP(hipStreamWaitEvent(ctx_->side2, ctx_->compute_done[sl], 0));
+            }
             put(s8, h, nbytes, w_.slot[sl], ctx_->side2);
             QLX_CHECK_HIP(hipEventRecord(ctx_->half_done, ctx_->side2));
             put(s8, 0, h, w_.slot[sl], ctx_->side);
@@ -602,18 +626,10 @@ class Streamer {
         } else {
             put(s8, 0, nbytes, w_.slot[sl], ctx_->side);
         }
-        if (wire) {  // maxima bf16 -> fp32 and the gains into their full-form places
-            char* b = w_.slot[sl];
-            char* tail = b + bytes_;  // wire offset wire_[7] landed here
-            launch_blob_widen(reinterpret_cast<const uint16_t*>(tail), nblocks_,
-                              reinterpret_cast<const float*>(tail + (wire_[14] - wire_[7])),
-                              reinterpret_cast<const float*>(tail + (wire_[15] - wire_[7])), m_->dims.hidden,
-                              reinterpret_cast<uint32_t*>(b + full_[7]), reinterpret_cast<float*>(b + full_[14]),
-                              reinterpret_cast<float*>(b + full_[15]), ctx_->side);
-        }
+        widen_pending_[sl] = wire;  // the widen runs on the compute stream in acquire()
         if (ev) QLX_CHECK_HIP(hipEventRecord(ev[1], ctx_->side));
         if (k >= 0) QLX_CHECK_HIP(hipEventRecord(f->staging_free[k], ctx_->side));
-        if (ctx_->debug & QLX_DEBUG_POISON_LIVE)  // control: poisons the slot it just filled
+        if ((ctx_->debug & QLX_DEBUG_POISON_LIVE) && !wire)  // control: poisons the slot it just filled
             launch_fill_u32(reinterpret_cast<uint32_t*>(w_.slot[sl]), int64_t(bytes_ / 4), 0xFFFFFFFFu, ctx_->side);
         QLX_CHECK_HIP(hipEventRecord(ctx_->copy_done[sl], ctx_->side));
         if (ctx_->debug & QLX_DEBUG_SERIALIZE) QLX_CHECK_HIP(hipStreamSynchronize(ctx_->side));
@@ -645,6 +661,7 @@ class Streamer {
     uint64_t bytes_;  // full-form blob
     hipStream_t main_;
     int held_[2];
+    bool widen_pending_[2] = {false, false};  // wire-form slot copied, not yet widened
     int form_ = QLX_BLOB_FULL;
     uint64_t full_[QLX_BLOB_NSEG] = {}, wire_[QLX_BLOB_NSEG] = {}, wire_bytes_ = 0;
     int64_t nblocks_ = 0;
