@@ -15,11 +15,12 @@ available host memory and the file otherwise.
 
 Prints ONE JSON line. `value` is tokens/s over the timed steps (inputs
 resident: weights in pinned host RAM as the method keeps them, tokens on the
-device). During the timed steps the library brackets only the fused
-NF4-dequant MFMA GEMMs with HIP events (every other kernel runs with none);
-`roofline` reports the dominant one of them from those events. One further,
-untimed step with events around every kernel gives the per-kernel table
-(`kernels`, `gpu_time`). `cpu_baseline` times the oracle on a bounded sample
+device), which run with no profiling events. The same number of steps then
+runs again, untimed, with the library bracketing only the fused NF4-dequant
+MFMA GEMMs with HIP events (every other kernel runs with none); `roofline`
+reports the dominant one of them from those events. One further, untimed
+step with events around every kernel gives the per-kernel table (`kernels`,
+`gpu_time`). `cpu_baseline` times the oracle on a bounded sample
 on this host.
 """
 from __future__ import annotations
@@ -534,22 +535,28 @@ def main() -> int:
         st = ctx.sync()
         log(f"warmup {i + 1}/{args.warmup}: {st['step_ms']:.1f} ms, loss {loss.item():.4f}")
     torch.cuda.synchronize()
-    if not args.no_profile:
-        B_.profile_begin("gemm_nf4")  # events around the NF4 GEMMs only
-    # the steps are enqueued back to back (the host never waits between them);
-    # the context's statistics are those of the last step
+    # the steps are enqueued back to back (the host never waits between them)
+    # with no profiling events; the context's statistics are those of the last step
     t_start = time.perf_counter()
     for i in range(args.steps):
         step()
     stats = [ctx.sync()]
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    live = B_.profile_end() if not args.no_profile else {}
     ms_step = 1000.0 * elapsed / args.steps
     value = tokens_per_step * args.steps / elapsed
     log(f"timed {args.steps} steps: {ms_step:.1f} ms/step, {value:.1f} tokens/s, loss {loss.item():.4f}")
-    prof = {}
-    if not args.no_profile:  # one more step, untimed, with events around every kernel
+    live, prof = {}, {}
+    if not args.no_profile:
+        # after the timed steps, the same number of steps again (untimed) with
+        # events around the NF4 GEMMs only, for the roofline of the dominant one
+        B_.profile_begin("gemm_nf4")
+        for i in range(args.steps):
+            step()
+        ctx.sync()
+        torch.cuda.synchronize()
+        live = B_.profile_end()
+        # and one more step with events around every kernel
         B_.profile_begin()
         step()
         ctx.sync()

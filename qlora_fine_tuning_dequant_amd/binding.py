@@ -14,7 +14,9 @@ from typing import Sequence
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlx.so")
+# QLX_LIB names another build of the same library (the host-sanitizer builds
+# the CPU tests run under); by default the in-tree libqlx.so
+LIB_PATH = os.environ.get("QLX_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlx.so")
 
 QLX_OK, QLX_EINVAL, QLX_EUNSUPPORTED, QLX_EWORKSPACE, QLX_ENOTPINNED, QLX_EHIP, QLX_EIO = range(7)
 QLX_F32, QLX_BF16 = 0, 1

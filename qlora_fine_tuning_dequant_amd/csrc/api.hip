@@ -389,6 +389,7 @@ struct qlx_ctx {
     hipStream_t side2 = nullptr;      // second copy stream (copy_split == 2)
     hipEvent_t half_done = nullptr;   // side2's half of the current copy
     hipEvent_t copy_start = nullptr;  // side is ready to overwrite the slot
+    hipEvent_t join = nullptr;        // end of a step: the copy streams' work joined into the main stream
     int copy_split = 2;
     int debug = 0;                    // QLX_DEBUG_* flags
     int delay_us = 0;
@@ -729,11 +730,9 @@ static void begin_step(qlx_ctx* ctx, hipStream_t main) {
     QLX_CHECK_HIP(hipEventRecord(ctx->compute_done[1], main));
 }
 static void end_step(qlx_ctx* ctx, hipStream_t main) {
-    hipEvent_t join;
-    QLX_CHECK_HIP(hipEventCreateWithFlags(&join, hipEventDisableTiming));
-    QLX_CHECK_HIP(hipEventRecord(join, ctx->side));
-    QLX_CHECK_HIP(hipStreamWaitEvent(main, join, 0));
-    QLX_CHECK_HIP(hipEventDestroy(join));
+    // (side2's half of every copy is already waited for on side)
+    QLX_CHECK_HIP(hipEventRecord(ctx->join, ctx->side));
+    QLX_CHECK_HIP(hipStreamWaitEvent(main, ctx->join, 0));
     QLX_CHECK_HIP(hipEventRecord(ctx->step_end, main));
 }
 
@@ -906,6 +905,7 @@ int qlx_ctx_create(qlx_ctx** out, int device) {
         QLX_CHECK_HIP(hipStreamCreateWithFlags(&c->side2, hipStreamNonBlocking));
         QLX_CHECK_HIP(hipEventCreateWithFlags(&c->half_done, hipEventDisableTiming));
         QLX_CHECK_HIP(hipEventCreateWithFlags(&c->copy_start, hipEventDisableTiming));
+        QLX_CHECK_HIP(hipEventCreateWithFlags(&c->join, hipEventDisableTiming));
         // QLX_COPY_SPLIT=1: one copy stream (default 2: each layer copy in two halves on two streams)
         if (const char* e = std::getenv("QLX_COPY_SPLIT")) c->copy_split = std::atoi(e) == 1 ? 1 : 2;
         for (int i = 0; i < 2; ++i) {
@@ -936,6 +936,7 @@ int qlx_ctx_destroy(qlx_ctx* ctx) {
         (void)hipStreamSynchronize(ctx->side2);
         (void)hipEventDestroy(ctx->half_done);
         (void)hipEventDestroy(ctx->copy_start);
+        (void)hipEventDestroy(ctx->join);
         (void)hipStreamDestroy(ctx->side2);
         (void)hipStreamDestroy(ctx->side);
         delete ctx;

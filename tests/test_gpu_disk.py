@@ -1,18 +1,24 @@
 """GPU checks of the disk stream source: steps whose layers come from a stack
-file (disk -> pinned staging -> device slot) give the same bits as the
-RAM-streamed and resident runs, read the stack as often, and reject a missing
-or mismatched file before any launch."""
+file (disk -> pinned staging -> device slot) match the oracle's SFT and DPO
+steps on the same seeded model, give the same bits as the RAM-streamed and
+resident runs, read the stack as often, and reject a missing or mismatched
+file before any launch."""
 import dataclasses
 
+import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
-from gpu_helpers import gpu_model, run_dpo, run_sft, same_grads
+from gpu_helpers import grad_errors, gpu_model, run_dpo, run_sft, same_grads, to_np
+from helpers import lora_list, oracle_model
 
 pytestmark = pytest.mark.gpu
 q = pytest.importorskip("qlora_fine_tuning_dequant_amd")
 B_ = q.binding
+# each sequence's summed response log-prob against the oracle's, relative
+LP_REL = 1e-3
 
 
 @pytest.fixture(scope="module")
@@ -41,6 +47,11 @@ def test_sft_from_disk_equals_ram_and_resident(four, buffered):
     l_r, g_r, _ = run_sft(q, m, toks, B_.QLX_RESIDENT)
     assert torch.equal(l_d, l_s) and same_grads(g_d, g_s)
     assert torch.equal(l_d, l_r) and same_grads(g_d, g_r)
+    # and against the oracle's step on the same seeded model
+    ref_loss, ref_g = oracle.sft_step(oracle_model(d, 1), lora_list(d, 1, "normal"), toks, d)
+    assert abs(l_d.item() - ref_loss) <= 1e-2, (l_d.item(), ref_loss)
+    bad = {k: v for k, v in grad_errors(g_d, ref_g).items() if not v <= 2e-2}
+    assert not bad, bad
     assert st_d["layer_reads"] == 2 * 4 - 2 and st_d["h2d_bytes"] == st_s["h2d_bytes"]
     assert st_d["disk_bytes"] == st_d["layer_reads"] * f.info()["stride"] and st_s["disk_bytes"] == 0
     # the same context again: the staging ring is reused across steps
@@ -58,11 +69,18 @@ def test_dpo_from_disk_both_schedules(four):
     f = q.LayerFile(path, d)
     ctx = q.Context(0)
     ctx.set_layer_source(f)
+    ref_loss, ref_lp, ref_g = oracle.dpo_step(oracle_model(d, 1), lora_list(d, 1, "normal"), ch, rj, 8, 0.1, d)
     for sched, reads in ((B_.QLX_DPO_REF_FUSED, 2 * 4 - 2), (B_.QLX_DPO_REF_SEPARATE, 3 * 4 - 2)):
         l_d, lp_d, g_d, st_d = run_dpo(q, _disk_model(m), ch, rj, 8, 0.1, B_.QLX_STREAMED_DISK, sched, ctx)
         l_s, lp_s, g_s, _ = run_dpo(q, m.with_blobs(host), ch, rj, 8, 0.1, B_.QLX_STREAMED, sched)
         assert torch.equal(l_d, l_s) and torch.equal(lp_d, lp_s) and same_grads(g_d, g_s)
         assert st_d["layer_reads"] == reads and st_d["disk_bytes"] == reads * f.info()["stride"]
+        # against the oracle: loss, each sequence's summed log-prob, every gradient
+        assert abs(l_d.item() - ref_loss) <= 1e-2, (l_d.item(), ref_loss)
+        lp = to_np(lp_d)
+        assert np.all(np.abs(lp - ref_lp) <= LP_REL * np.abs(ref_lp)), (lp, ref_lp)
+        bad = {k: v for k, v in grad_errors(g_d, ref_g).items() if not v <= 2e-2}
+        assert not bad, bad
     ctx.set_layer_source(None)
     ctx.close()
     f.close()

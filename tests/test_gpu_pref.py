@@ -45,7 +45,8 @@ def test_pref_step_vs_oracle_and_streamed_equals_resident(kind):
     ref_loss, ref_lp, ref_g = oracle.pref_step(kind, oracle_model(d, 0), lora_list(d, 0, "normal"), ch, rj, 16, d,
                                                **HP[kind])
     assert abs(l_s.item() - ref_loss) < 1e-2, (l_s.item(), ref_loss)
-    assert np.max(np.abs(to_np(lp_s) - ref_lp)) < 0.05 * np.max(np.abs(ref_lp))
+    # each sequence's summed log-prob (0 for the reference-free kinds), relative to itself
+    assert np.all(np.abs(to_np(lp_s) - ref_lp) <= 1e-3 * np.abs(ref_lp)), (to_np(lp_s), ref_lp)
     bad = {k: v for k, v in grad_errors(g_s, ref_g).items() if not v < TOL}
     assert not bad, bad
 

@@ -195,3 +195,28 @@ def test_keep_layers_dpo_and_wire_form(four):
             assert torch.equal(loss, l0) and torch.equal(logps, lp0) and same_grads(grads, g0)
         assert reads == [3 * 4 - 2, 3 * 4 - 4]
         ctx.close()
+
+
+@pytest.mark.parametrize("form", ["full", "wire"])
+def test_split_copies_with_delayed_compute_alone(four, form):
+    """The production branch of the split copy (no poison fill): the second
+    copy stream waits only for the slot's previous user. With the compute
+    delayed by a spin before every layer, a half copy that started before
+    that user finished would overwrite weights still being read and change
+    the bits; SFT and separate-reference DPO must equal the resident run."""
+    d, sm = four
+    rm = sm.with_blobs([b.to("cuda:0") for b in sm.blobs])
+    model = sm if form == "full" else sm.with_blobs([B_.blob_to_wire(d, h) for h in sm.blobs], B_.QLX_BLOB_WIRE)
+    toks = synth.tokens(3, 2, 32, d.vocab)
+    l0, g0, _ = run_sft(q, rm, toks, B_.QLX_RESIDENT)
+    ch, rj = synth.dpo_pairs(3, 2, 32, 8, d.vocab)
+    dl0, dlp0, dg0, _ = run_dpo(q, rm, ch, rj, 8, 0.1, B_.QLX_RESIDENT, B_.QLX_DPO_REF_SEPARATE)
+    ctx = q.Context(0)  # default: two copy streams
+    ctx.set_debug(B_.QLX_DEBUG_DELAY_COMPUTE, 300)
+    print("split copies, delayed compute, form", form, flush=True)
+    l1, g1, st = run_sft(q, model, toks, B_.QLX_STREAMED, ctx)
+    assert torch.equal(l0, l1) and same_grads(g0, g1) and st["layer_reads"] == 2 * 4 - 2
+    dl1, dlp1, dg1, st = run_dpo(q, model, ch, rj, 8, 0.1, B_.QLX_STREAMED, B_.QLX_DPO_REF_SEPARATE, ctx)
+    assert torch.equal(dl0, dl1) and torch.equal(dlp0, dlp1) and same_grads(dg0, dg1)
+    assert st["layer_reads"] == 3 * 4 - 2
+    ctx.close()
