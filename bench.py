@@ -92,7 +92,7 @@ def log(msg: str) -> None:
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def build_model(q, d, seed: int, want_device_blobs: bool = False, wire: bool = False):
+def build_model(q, d, seed: int, want_device_blobs: bool = False, wire: bool = False, act: int | None = None):
     """Quantize every layer's seeded bf16 weights on the GPU (nf4_quantize)
     into a device blob and keep a pinned host copy (in the wire form, block
     maxima as bf16, when wire=True). Host-side generation of layer i+1
@@ -147,7 +147,7 @@ def build_model(q, d, seed: int, want_device_blobs: bool = False, wire: bool = F
     head = torch.from_numpy(synth.lm_head_f16(d, seed).view(np.int16)).view(torch.float16).to(dev)
     gf = torch.from_numpy(synth.final_norm_weight(d, seed)).to(dev)
     m = q.StreamModel(d, host, emb, head, gf, loras,
-                      q.binding.QLX_BLOB_WIRE if wire else q.binding.QLX_BLOB_FULL)
+                      q.binding.QLX_BLOB_WIRE if wire else q.binding.QLX_BLOB_FULL, act_dtype=act)
     return m, dev_blobs
 
 
@@ -390,6 +390,99 @@ def measure_peaks(q) -> dict:
     return out
 
 
+def _union(iv):
+    """Total length of the union of [start, end) intervals (ns)."""
+    tot, cur_s, cur_e = 0, None, None
+    for a, b in sorted(iv):
+        if cur_e is None or a > cur_e:
+            if cur_e is not None:
+                tot += cur_e - cur_s
+            cur_s, cur_e = a, b
+        else:
+            cur_e = max(cur_e, b)
+    return tot + (cur_e - cur_s if cur_e is not None else 0)
+
+
+def _overlap(a_iv, b_iv):
+    """Length of (union of a) intersected with (union of b), in ns."""
+    def merged(iv):
+        out = []
+        for x, y in sorted(iv):
+            if out and x <= out[-1][1]:
+                out[-1][1] = max(out[-1][1], y)
+            else:
+                out.append([x, y])
+        return out
+    A, B = merged(a_iv), merged(b_iv)
+    i = j = tot = 0
+    while i < len(A) and j < len(B):
+        lo, hi = max(A[i][0], B[j][0]), min(A[i][1], B[j][1])
+        if hi > lo:
+            tot += hi - lo
+        if A[i][1] < B[j][1]:
+            i += 1
+        else:
+            j += 1
+    return tot
+
+
+def rocpd_summary(path: str, top: int = 25) -> str:
+    """Text summary of a rocprofv3 trace database (--kernel-trace and
+    --memory-copy-trace): per-kernel dispatch statistics, and the layer
+    stream's host-to-device copies (those above 4 MB: the streamer's halves
+    of each layer blob) with their rate and their overlap with kernels, over
+    the window from the first to the last such copy."""
+    import sqlite3
+    db = sqlite3.connect(path)
+    cur = db.cursor()
+    lines = []
+    ks = cur.execute("select name, start, end from kernels").fetchall()
+    agg = {}
+    for name, a, b in ks:
+        e = agg.setdefault(name, [0, 0])
+        e[0] += 1
+        e[1] += b - a
+    total = sum(v[1] for v in agg.values())
+    lines.append(f"kernel dispatches: {len(ks)}, total kernel time {total / 1e6:.2f} ms")
+    lines.append("")
+    lines.append("| kernel | calls | total ms | avg us | % |")
+    lines.append("|---|---|---|---|---|")
+    for name, (n, t) in sorted(agg.items(), key=lambda kv: -kv[1][1])[:top]:
+        lines.append(f"| `{name[:90]}` | {n} | {t / 1e6:.3f} | {t / n / 1e3:.2f} | {100.0 * t / max(total, 1):.1f} |")
+    try:
+        cps = cur.execute("select start, end, size, stream_id, name from memory_copies").fetchall()
+    except sqlite3.OperationalError:
+        cps = []
+    h2d = [c for c in cps if c[4] == "MEMORY_COPY_HOST_TO_DEVICE" and c[2] > 4_000_000]
+    if h2d:
+        w0, w1 = min(c[0] for c in h2d), max(c[1] for c in h2d)
+        kin = [(max(a, w0), min(b, w1)) for _, a, b in ks if b > w0 and a < w1]
+        civ = [(c[0], c[1]) for c in h2d]
+        nbytes = sum(c[2] for c in h2d)
+        busy = _union(civ)
+        kbusy = _union(kin)
+        ov = _overlap(civ, kin)
+        streams = {}
+        for c in h2d:
+            e = streams.setdefault(c[3], [0, 0, 0])
+            e[0] += 1
+            e[1] += c[2]
+            e[2] += c[1] - c[0]
+        lines.append("")
+        lines.append(f"layer-stream host-to-device copies (> 4 MB): {len(h2d)} copies, {nbytes / 1e9:.3f} GB, "
+                     f"window {(w1 - w0) / 1e6:.1f} ms")
+        lines.append(f"- link busy (union of copy intervals): {busy / 1e6:.1f} ms -> {nbytes / max(busy, 1):.1f} GB/s "
+                     f"while copying; {nbytes / max(w1 - w0, 1):.1f} GB/s over the window")
+        for sid, (n, b, t) in sorted(streams.items()):
+            lines.append(f"- stream {sid}: {n} copies, {b / 1e9:.3f} GB, {t / 1e6:.1f} ms of copy time, "
+                         f"{b / max(t, 1):.1f} GB/s per copy")
+        lines.append(f"- kernels busy inside the window: {kbusy / 1e6:.1f} ms ({100.0 * kbusy / max(w1 - w0, 1):.1f}%)")
+        lines.append(f"- copy time overlapped by kernels: {ov / 1e6:.1f} ms = {100.0 * ov / max(busy, 1):.1f}% of link-busy "
+                     f"time; kernel time overlapped by copies: {100.0 * ov / max(kbusy, 1):.1f}%")
+        lines.append(f"- neither copying nor computing: {(w1 - w0 - busy - kbusy + ov) / 1e6:.1f} ms")
+    return "\n".join(lines)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -410,6 +503,10 @@ def main() -> int:
                     help="stack file for --source disk/auto (default: a file in the temp directory, removed at exit)")
     ap.add_argument("--dpo-ref", default="fused", choices=["fused", "separate"],
                     help="DPO reference schedule: fused with the policy forward, or a separate pass")
+    ap.add_argument("--act", default="f16", choices=["f16", "bf16"],
+                    help="16-bit type of activations and gradients between kernels and in the MFMA products (the "
+                         "weight operand is bf16 of its NF4 value either way): f16 (10 significand bits, meets the "
+                         "2e-2 gradient tolerance at 32 layers) or bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timing")
     ap.add_argument("--optimizer", default="fused", choices=["fused", "separate"],
@@ -425,6 +522,9 @@ def main() -> int:
                     help="only time the oracle on this host: tiny SFT step and one 8B layer, all threads and one")
     ap.add_argument("--peaks", action="store_true",
                     help="only measure the device's peaks: bf16 MFMA loop, HBM copy, 122.7 MB pinned H2D copy")
+    ap.add_argument("--rocpd-summary", default=None, metavar="DB",
+                    help="only print a summary of a rocprofv3 trace database (kernels; layer-stream copies and "
+                         "their overlap with kernels)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB five times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -432,6 +532,10 @@ def main() -> int:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).",
               file=sys.stderr)
         return 2
+
+    if args.rocpd_summary:
+        print(rocpd_summary(args.rocpd_summary))
+        return 0
 
     import numpy as np
 
@@ -470,7 +574,8 @@ def main() -> int:
     log(f"workload {args.workload}: {wl['name']} ({args.mode})")
     t0 = time.perf_counter()
     wire = args.mode == "streamed" and args.blob_form == "wire"
-    m, dev_blobs = build_model(q, d, SEED, want_device_blobs=(args.mode == "resident"), wire=wire)
+    act = B_.QLX_ACT_F16 if args.act == "f16" else B_.QLX_ACT_BF16
+    m, dev_blobs = build_model(q, d, SEED, want_device_blobs=(args.mode == "resident"), wire=wire, act=act)
     if args.mode == "resident":
         m = m.with_blobs(dev_blobs)
     log(f"model ready in {time.perf_counter() - t0:.1f} s")
@@ -596,9 +701,10 @@ def main() -> int:
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": args.act, "data": "synthetic",
         "config": {"workload": wl["name"], "global_batch": batch if wl["kind"] == "sft" else 2 * batch,
                    "seq_len": seq, "mode": args.mode, "source": source,
+                   "activations": args.act, "weight_operand": "bf16 of the NF4 value",
                    "blob_form": "wire" if wire else "full", "keep_layers": keep, "layers": d.n_layers,
                    "lora_r": d.lora_r,
                    "optimizer": None if args.no_optimizer else

@@ -73,10 +73,23 @@ const char* qlx_last_error(void);
 const char* qlx_version(void);
 
 /* Decoder dimensions. rms_eps 1e-5 and rope_theta 5e5 for the Llama-3.1
- * shape; lora_alpha / lora_r is the LoRA scale s. */
+ * shape; lora_alpha / lora_r is the LoRA scale s.
+ * act_dtype: the 16-bit type of the activations and gradients the layer and
+ * step calls keep between kernels and feed to the MFMA products.
+ *   QLX_ACT_BF16 (0): bf16 activations, bf16 weight operand (QLoRA's
+ *     computation type; the frozen weight enters as bf16 of its NF4 value).
+ *   QLX_ACT_F16 (1): fp16 activations and gradients; the weight operand is
+ *     still bf16 of the NF4 value, carried in fp16 (exact for magnitudes in
+ *     [2^-17, 65504]), so only the activation side changes: 10 significand
+ *     bits instead of 7 at the same MFMA rate. Gradients travel scaled by a
+ *     power of two (chosen per step from the loss's largest per-position
+ *     logit gradient) and come out unscaled.
+ * fp32 everywhere else (residual stream, reductions, LoRA gradients). */
+enum { QLX_ACT_BF16 = 0, QLX_ACT_F16 = 1 };
 typedef struct {
     int32_t hidden, n_heads, n_kv_heads, head_dim, inter, vocab, n_layers, lora_r;
     float lora_alpha, rms_eps, rope_theta;
+    int32_t act_dtype;
 } qlx_dims;
 
 /* ---------------------------------------------------------------------------

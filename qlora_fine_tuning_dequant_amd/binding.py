@@ -28,6 +28,12 @@ QLX_DEBUG_SERIALIZE, QLX_DEBUG_POISON, QLX_DEBUG_DELAY_COPY, QLX_DEBUG_DELAY_COM
 QLX_DPO_REF_FUSED, QLX_DPO_REF_SEPARATE = 0, 1
 QLX_PREF_DPO, QLX_PREF_ORPO, QLX_PREF_SIMPO, QLX_PREF_KTO = 0, 1, 2, 3
 QLX_MERGE_BF16, QLX_MERGE_NF4 = 0, 1
+QLX_ACT_BF16, QLX_ACT_F16 = 0, 1
+# 16-bit activation type of layer and step calls when the caller names none:
+# fp16 (10 significand bits, the same MFMA rate as bf16; the weight operand
+# is bf16 of its NF4 value either way). QLX_ACT=bf16 in the environment
+# switches the default.
+ACT_DEFAULT = QLX_ACT_BF16 if os.environ.get("QLX_ACT", "").lower() == "bf16" else QLX_ACT_F16
 PREF_KINDS = {"dpo": QLX_PREF_DPO, "orpo": QLX_PREF_ORPO, "simpo": QLX_PREF_SIMPO, "kto": QLX_PREF_KTO}
 # the readings' default hyperparameters (beta, gamma, lambda_d, lambda_u)
 PREF_DEFAULTS = {"dpo": (0.1, 0.0, 1.0, 1.0), "orpo": (0.1, 0.0, 1.0, 1.0), "simpo": (2.0, 0.5, 1.0, 1.0),
@@ -57,14 +63,21 @@ class Dims(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("n_heads", C.c_int32), ("n_kv_heads", C.c_int32),
                 ("head_dim", C.c_int32), ("inter", C.c_int32), ("vocab", C.c_int32),
                 ("n_layers", C.c_int32), ("lora_r", C.c_int32), ("lora_alpha", C.c_float),
-                ("rms_eps", C.c_float), ("rope_theta", C.c_float)]
+                ("rms_eps", C.c_float), ("rope_theta", C.c_float), ("act_dtype", C.c_int32)]
 
     @classmethod
-    def of(cls, d) -> "Dims":
+    def of(cls, d, act_dtype: int | None = None) -> "Dims":
+        """C dims from any object with the decoder fields. act_dtype (QLX_ACT_BF16
+        or QLX_ACT_F16): the 16-bit activation type of layer and step calls; by
+        default d's own act_dtype if it has one, else ACT_DEFAULT."""
         if isinstance(d, Dims):
-            return d
+            if act_dtype is None or act_dtype == d.act_dtype:
+                return d
+            return cls(d.hidden, d.n_heads, d.n_kv_heads, d.head_dim, d.inter, d.vocab, d.n_layers, d.lora_r,
+                       d.lora_alpha, d.rms_eps, d.rope_theta, int(act_dtype))
+        act = act_dtype if act_dtype is not None else getattr(d, "act_dtype", ACT_DEFAULT)
         return cls(d.hidden, d.n_heads, d.n_kv_heads, d.head_dim, d.inter, d.vocab, d.n_layers,
-                   d.lora_r, float(d.lora_alpha), float(d.rms_eps), float(d.rope_theta))
+                   d.lora_r, float(d.lora_alpha), float(d.rms_eps), float(d.rope_theta), int(act))
 
 
 class NF4(C.Structure):
@@ -548,8 +561,9 @@ class StreamModel:
     by blob_to_wire."""
 
     def __init__(self, dims, blobs: Sequence[torch.Tensor] | None, embed_f16: torch.Tensor, head_f16: torch.Tensor,
-                 final_norm: torch.Tensor, lora: Sequence[LoraLayer], blob_form: int = QLX_BLOB_FULL):
-        self.dims = Dims.of(dims)
+                 final_norm: torch.Tensor, lora: Sequence[LoraLayer], blob_form: int = QLX_BLOB_FULL,
+                 act_dtype: int | None = None):
+        self.dims = Dims.of(dims, act_dtype)
         self.blob_form = blob_form
         _, total = wire_layout(self.dims) if blob_form == QLX_BLOB_WIRE else blob_layout(self.dims)
         for bl in blobs or ():
@@ -568,6 +582,11 @@ class StreamModel:
 
     def with_blobs(self, blobs: Sequence[torch.Tensor], blob_form: int = QLX_BLOB_FULL) -> "StreamModel":
         return StreamModel(self.dims, blobs, self.embed, self.head, self.final_norm, self.lora, blob_form)
+
+    def with_act(self, act_dtype: int) -> "StreamModel":
+        """The same model computing with another 16-bit activation type."""
+        return StreamModel(Dims.of(self.dims, act_dtype), self.blobs, self.embed, self.head, self.final_norm, self.lora,
+                           self.blob_form)
 
 
 def step_workspace_bytes(dims, kind: int, batch: int, seq: int) -> int:

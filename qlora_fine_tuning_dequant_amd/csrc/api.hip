@@ -19,6 +19,8 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
+#include <string>
 #include <vector>
 
 #include <chrono>
@@ -115,6 +117,56 @@ size_t qlx_linear_workspace_bytes(int64_t T, int64_t in_f, int64_t out_f, int r)
     return c.size();
 }
 
+}  // extern "C"
+
+namespace qlx {
+// The QLoRA linear forward on a workspace laid out by carve_linear, whose
+// split-K partial region holds partial_cap floats.
+static void linear_fwd(const uint16_t* x, int64_t T, const qlx_nf4& W, const float* A, const float* B, int r,
+                       float scale, uint16_t* y, LinearWs w, size_t partial_cap, hipStream_t s) {
+    const int M = int(T), N = int(W.rows), K = int(W.cols);
+    GemmParams p;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.A = x;
+    p.lda = K;
+    p.B = W.packed;
+    p.absmax = W.absmax;
+    p.nf4_cols = K;
+    p.partial_cap = partial_cap;
+    if (A) {
+        LoraSeg seg{A, B, N};
+        launch_lora_pack(&seg, 1, r, K, scale, w.Ab, w.Bb, 0, s);  // the linear calls take bf16
+        GemmParams pu;
+        pu.M = M;
+        pu.N = r;
+        pu.K = K;
+        pu.A = x;
+        pu.lda = K;
+        pu.B = w.Ab;
+        pu.ldb = K;
+        pu.C = w.u;
+        pu.ldc = r;
+        pu.c_type = C_BF16;
+        pu.partial_cap = partial_cap;
+        gemm(pu, A_ROW, B_DENSE_NT, TE_BF16, w.partial, s);
+        p.K2 = r;
+        p.A2 = w.u;
+        p.lda2 = r;
+        p.B2 = w.Bb;
+        p.ldb2 = r;
+    }
+    p.C = y;
+    p.ldc = N;
+    p.c_type = C_BF16;
+    gemm(p, A_ROW, B_NF4_NT, TE_BF16, w.partial, s);
+}
+
+}  // namespace qlx
+
+extern "C" {
+
 int qlora_linear_fwd(const uint16_t* x, int64_t T, qlx_nf4 W, const float* A, const float* B, int r, float scale,
                      uint16_t* y, void* ws, size_t ws_bytes, void* stream) {
     return guarded([&] {
@@ -124,44 +176,9 @@ int qlora_linear_fwd(const uint16_t* x, int64_t T, qlx_nf4 W, const float* A, co
         REQ_PTR(y, "y");
         const int rr = A ? r : 0;
         check_ws(ws, ws_bytes, qlx_linear_workspace_bytes(T, W.cols, W.rows, rr));
-        hipStream_t s = static_cast<hipStream_t>(stream);
         Carver c(ws);
-        LinearWs w = carve_linear(c, T, W.cols, W.rows, rr);
-        const int M = int(T), N = int(W.rows), K = int(W.cols);
-        GemmParams p;
-        p.M = M;
-        p.N = N;
-        p.K = K;
-        p.A = x;
-        p.lda = K;
-        p.B = W.packed;
-        p.absmax = W.absmax;
-        p.nf4_cols = K;
-        if (A) {
-            LoraSeg seg{A, B, N};
-            launch_lora_pack(&seg, 1, r, K, scale, w.Ab, w.Bb, s);
-            GemmParams pu;
-            pu.M = M;
-            pu.N = r;
-            pu.K = K;
-            pu.A = x;
-            pu.lda = K;
-            pu.B = w.Ab;
-            pu.ldb = K;
-            pu.C = w.u;
-            pu.ldc = r;
-            pu.c_type = C_BF16;
-            gemm(pu, A_ROW, B_DENSE_NT, TE_BF16, w.partial, s);
-            p.K2 = r;
-            p.A2 = w.u;
-            p.lda2 = r;
-            p.B2 = w.Bb;
-            p.ldb2 = r;
-        }
-        p.C = y;
-        p.ldc = N;
-        p.c_type = C_BF16;
-        gemm(p, A_ROW, B_NF4_NT, TE_BF16, w.partial, s);
+        const LinearWs w = carve_linear(c, T, W.cols, W.rows, rr);
+        linear_fwd(x, T, W, A, B, r, scale, y, w, kGemmPartialFloats, static_cast<hipStream_t>(stream));
     });
 }
 
@@ -192,7 +209,7 @@ int qlora_linear_bwd(const uint16_t* dy, const uint16_t* x, int64_t T, qlx_nf4 W
         const int M = int(T), N = int(W.rows), K = int(W.cols);  // forward: y [T, N] = x [T, K] W^T
         if (A) {
             LoraSeg seg{A, B, N};
-            launch_lora_pack(&seg, 1, r, K, scale, w.Ab, w.Bb, s);
+            launch_lora_pack(&seg, 1, r, K, scale, w.Ab, w.Bb, 0, s);  // the linear calls take bf16
             GemmParams pu;  // u = x A^T
             pu.M = M;
             pu.N = r;
@@ -820,6 +837,27 @@ static void head_grad(const qlx_model* m, const float* hL, int T, const int32_t*
 // dz is stored in fp16 scaled by 2^12 so that softmax values ~1/V stay normal.
 constexpr float kDzScale = 4096.f;
 
+// Gradient scale of a step's backward with fp16 activations: the power of two
+// that puts the loss's largest possible per-position logit gradient (bound)
+// at 2^10. The layers' 16-bit gradients then stay far above fp16's smallest
+// normal value (2^-14) and below its largest (65504) as long as they grow at
+// most ~60x over the head's bound through the stack. With bf16 (fp32's
+// exponent range) no scale is needed: 1.
+static float grad_scale(const LayerGeom& g, double bound) {
+    if (!g.f16 || !(bound > 0.0)) return 1.f;
+    return float(std::exp2(std::floor(std::log2(1024.0 / bound))));
+}
+// the preference losses' bound on |dL/dz| per position (= |dL/dlp| of a sequence)
+static double pref_grad_bound(const qlx_pref_cfg& cfg, int pairs, int nresp) {
+    const double P = pairs, n = std::max(1, nresp), b = cfg.beta;
+    switch (cfg.kind) {
+        case QLX_PREF_ORPO: return (1.0 + b) / (P * n);  // while the mean response probability stays below 1/2
+        case QLX_PREF_SIMPO: return b / (P * n);
+        case QLX_PREF_KTO: return std::max(cfg.lambda_d, cfg.lambda_u) * b / 4.0 / (2.0 * P);
+        default: return b / P;  // DPO
+    }
+}
+
 static void check_adamw_cfg(const qlx_adamw_cfg* cfg, int64_t t) {
     REQ_PTR(cfg, "cfg");
     QLX_REQUIRE(t >= 1, QLX_EINVAL, "adamw: t (1-based update count) must be >= 1");
@@ -1071,7 +1109,8 @@ int stream_step_sft(qlx_ctx* ctx, const qlx_model* m, const int32_t* tokens, int
         const int T = batch * seq;
         Carver c(ws);
         StepWs w = carve_step(c, d, T, 0, blob_bytes);
-        const LayerGeom g = make_geom(d, batch, seq);
+        LayerGeom g = make_geom(d, batch, seq);
+        g.gsc = grad_scale(g, 1.0 / (double(batch) * double(seq - 1)));  // SFT: |dL/dz| <= 1/N
         w.lw = carve_layer(c, g);
         const size_t TH = size_t(T) * d.hidden;
         const int L = d.n_layers;
@@ -1134,7 +1173,8 @@ static void pref_step(qlx_ctx* ctx, const qlx_model* m, const qlx_pref_cfg& cfg,
     const int T = B * seq;
     Carver c(ws);
     StepWs w = carve_step(c, d, T, wkind, blob_bytes);
-    const LayerGeom g = make_geom(d, B, seq);
+    LayerGeom g = make_geom(d, B, seq);
+    g.gsc = grad_scale(g, pref_grad_bound(cfg, pairs, seq - prompt_len));
     w.lw = carve_layer(c, g);
     const size_t TH = size_t(T) * d.hidden;
     const int L = d.n_layers;

@@ -12,8 +12,8 @@
 // per-lane scalars shared by the 4 lanes of a query, the rescale of the
 // output is a per-lane multiply, and the probabilities already sit in the
 // layout of the B operand of O^T += V^T P^T (V is staged transposed in LDS).
-// P is rounded to bf16 for that product (as the reference path rounds its
-// probabilities); the running sum uses the fp32 values.
+// P is rounded to the 16-bit operand type for that product; the running sum
+// uses the fp32 values.
 //
 // RoPE (rotate-half, pairs (j, j + hd/2)) is applied to q|k in place by one
 // launch before the forward (rotating while loading would redo each key
@@ -37,13 +37,25 @@ namespace qlx {
 
 namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// 16-bit operands are bf16 (TE_BF16) or fp16 (TE_F16): q, k, v, o, dO, and
+// the probabilities and score gradients rounded for the products.
+template <int TE>
 __device__ inline f32x4 mfma(const uint4& a, const uint4& b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
-                                                   0, 0);
+    if constexpr (TE == TE_BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                       0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                      0, 0);
 }
-__device__ inline uint32_t pack_bf16(float lo, float hi) { return f32x2_to_bf16x2(lo, hi); }
+template <int TE>
+__device__ inline uint32_t pack2(float lo, float hi) {
+    if constexpr (TE == TE_BF16) return f32x2_to_bf16x2(lo, hi);
+    else return f32x2_to_f16x2(lo, hi);
+}
 
 constexpr int QB = 64;       // queries (or keys) per workgroup block
 constexpr int TP = QB + 8;   // row stride (elements) of a transposed [HD][64] tile
@@ -120,7 +132,7 @@ __device__ inline uint4 tfrag(const uint16_t* __restrict__ t, int dt, int js, in
 }  // namespace
 
 // ------------------------------------------------------------------ forward
-template <int HD>
+template <int HD, int TE>
 __global__ __launch_bounds__(256) void k_flash_fwd(const AttnArgs a) {
     __shared__ __align__(16) uint16_t Ks[QB * (HD + 8)];
     __shared__ __align__(16) uint16_t Vt[HD * TP];
@@ -158,7 +170,7 @@ __global__ __launch_bounds__(256) void k_flash_fwd(const AttnArgs a) {
             st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ds = 0; ds < HD / 32; ++ds)
-                st[kt] = mfma(*reinterpret_cast<const uint4*>(Ks + (kt * 16 + lr) * (HD + 8) + ds * 32 + g * 8), qf[ds],
+                st[kt] = mfma<TE>(*reinterpret_cast<const uint4*>(Ks + (kt * 16 + lr) * (HD + 8) + ds * 32 + g * 8), qf[ds],
                               st[kt]);
         }
         float mx = -INFINITY;
@@ -186,8 +198,8 @@ __global__ __launch_bounds__(256) void k_flash_fwd(const AttnArgs a) {
                 p[e] = exp2f(fmaf(st[kt][e], c, -mc));
                 ps += p[e];
             }
-            pk[kt][0] = pack_bf16(p[0], p[1]);
-            pk[kt][1] = pack_bf16(p[2], p[3]);
+            pk[kt][0] = pack2<TE>(p[0], p[1]);
+            pk[kt][1] = pack2<TE>(p[2], p[3]);
         }
         l = l * alpha + ps;
 #pragma unroll
@@ -196,7 +208,7 @@ __global__ __launch_bounds__(256) void k_flash_fwd(const AttnArgs a) {
         for (int js = 0; js < 2; ++js) {
             const uint4 pf = make_uint4(pk[2 * js][0], pk[2 * js][1], pk[2 * js + 1][0], pk[2 * js + 1][1]);
 #pragma unroll
-            for (int dt = 0; dt < HD / 16; ++dt) o[dt] = mfma(tfrag<HD>(Vt, dt, js, lane), pf, o[dt]);
+            for (int dt = 0; dt < HD / 16; ++dt) o[dt] = mfma<TE>(tfrag<HD>(Vt, dt, js, lane), pf, o[dt]);
         }
         __syncthreads();
     }
@@ -208,7 +220,7 @@ __global__ __launch_bounds__(256) void k_flash_fwd(const AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < HD / 16; ++dt)
         *reinterpret_cast<uint2*>(dst + dt * 16) =
-            make_uint2(pack_bf16(o[dt][0] * inv, o[dt][1] * inv), pack_bf16(o[dt][2] * inv, o[dt][3] * inv));
+            make_uint2(pack2<TE>(o[dt][0] * inv, o[dt][1] * inv), pack2<TE>(o[dt][2] * inv, o[dt][3] * inv));
     if (g == 0) a.lse[(int64_t(b) * a.nH + h) * a.S + q] = m * a.scale + logf(l);
 }
 
@@ -216,6 +228,7 @@ __global__ __launch_bounds__(256) void k_flash_fwd(const AttnArgs a) {
 // D[b, h, q] = sum_d dO[q, h d] o[q, h d]: hd/8 lanes per (query, head),
 // each with one 16-byte load of dO and of o (consecutive lanes read
 // consecutive bytes of a token row), joined by xor shuffles in a fixed order.
+template <int TE>
 __global__ __launch_bounds__(256) void k_flash_bwd_dot(const AttnArgs a, int hd) {
     const int L = hd / 8;  // 8 or 16 lanes per (query, head)
     const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -232,8 +245,13 @@ __global__ __launch_bounds__(256) void k_flash_bwd_dot(const AttnArgs a, int hd)
     float s = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        s = fmaf(__builtin_bit_cast(float, uw[e] << 16), __builtin_bit_cast(float, vw[e] << 16), s);
-        s = fmaf(__builtin_bit_cast(float, uw[e] & 0xFFFF0000u), __builtin_bit_cast(float, vw[e] & 0xFFFF0000u), s);
+        if constexpr (TE == TE_BF16) {
+            s = fmaf(__builtin_bit_cast(float, uw[e] << 16), __builtin_bit_cast(float, vw[e] << 16), s);
+            s = fmaf(__builtin_bit_cast(float, uw[e] & 0xFFFF0000u), __builtin_bit_cast(float, vw[e] & 0xFFFF0000u), s);
+        } else {
+            s = fmaf(f16_bits_to_f32(uint16_t(uw[e])), f16_bits_to_f32(uint16_t(vw[e])), s);
+            s = fmaf(f16_bits_to_f32(uint16_t(uw[e] >> 16)), f16_bits_to_f32(uint16_t(vw[e] >> 16)), s);
+        }
     }
     for (int off = L / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
     if (live && part == 0) {
@@ -243,7 +261,7 @@ __global__ __launch_bounds__(256) void k_flash_bwd_dot(const AttnArgs a, int hd)
 }
 
 // dK_h, dV_h (fp32, per query head) for one block of 64 keys.
-template <int HD>
+template <int HD, int TE>
 __global__ __launch_bounds__(256) void k_flash_bwd_kv(const AttnArgs a) {
     __shared__ __align__(16) uint16_t Qs[QB * (HD + 8)];
     __shared__ __align__(16) uint16_t Qt[HD * TP];
@@ -294,9 +312,9 @@ __global__ __launch_bounds__(256) void k_flash_bwd_kv(const AttnArgs a) {
             s[qt] = dp[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ds = 0; ds < HD / 32; ++ds) {
-                s[qt] = mfma(*reinterpret_cast<const uint4*>(Qs + (qt * 16 + lr) * (HD + 8) + ds * 32 + g * 8), kf[ds],
+                s[qt] = mfma<TE>(*reinterpret_cast<const uint4*>(Qs + (qt * 16 + lr) * (HD + 8) + ds * 32 + g * 8), kf[ds],
                              s[qt]);
-                dp[qt] = mfma(*reinterpret_cast<const uint4*>(Ds + (qt * 16 + lr) * (HD + 8) + ds * 32 + g * 8), vf[ds],
+                dp[qt] = mfma<TE>(*reinterpret_cast<const uint4*>(Ds + (qt * 16 + lr) * (HD + 8) + ds * 32 + g * 8), vf[ds],
                               dp[qt]);
             }
         }
@@ -312,10 +330,10 @@ __global__ __launch_bounds__(256) void k_flash_bwd_kv(const AttnArgs a) {
                 p[e] = live ? exp2f(fmaf(s[qt][e], c, -lse_s[ql])) : 0.f;
                 d[e] = p[e] * (dp[qt][e] - dq_s[ql]);
             }
-            pk[qt][0] = pack_bf16(p[0], p[1]);
-            pk[qt][1] = pack_bf16(p[2], p[3]);
-            sk[qt][0] = pack_bf16(d[0], d[1]);
-            sk[qt][1] = pack_bf16(d[2], d[3]);
+            pk[qt][0] = pack2<TE>(p[0], p[1]);
+            pk[qt][1] = pack2<TE>(p[2], p[3]);
+            sk[qt][0] = pack2<TE>(d[0], d[1]);
+            sk[qt][1] = pack2<TE>(d[2], d[3]);
         }
         // dV += P^T dO and dK += dS^T Q over the 64 queries (two slices of 32)
 #pragma unroll
@@ -324,8 +342,8 @@ __global__ __launch_bounds__(256) void k_flash_bwd_kv(const AttnArgs a) {
             const uint4 sa = make_uint4(sk[2 * js][0], sk[2 * js][1], sk[2 * js + 1][0], sk[2 * js + 1][1]);
 #pragma unroll
             for (int dt = 0; dt < HD / 16; ++dt) {
-                dv[dt] = mfma(pa, tfrag<HD>(Dt, dt, js, lane), dv[dt]);
-                dk[dt] = mfma(sa, tfrag<HD>(Qt, dt, js, lane), dk[dt]);
+                dv[dt] = mfma<TE>(pa, tfrag<HD>(Dt, dt, js, lane), dv[dt]);
+                dk[dt] = mfma<TE>(sa, tfrag<HD>(Qt, dt, js, lane), dk[dt]);
             }
         }
         __syncthreads();
@@ -345,7 +363,7 @@ __global__ __launch_bounds__(256) void k_flash_bwd_kv(const AttnArgs a) {
 }
 
 // dQ for 64 queries of one head.
-template <int HD>
+template <int HD, int TE>
 __global__ __launch_bounds__(256) void k_flash_bwd_q(const AttnArgs a) {
     __shared__ __align__(16) uint16_t Ks[QB * (HD + 8)];
     __shared__ __align__(16) uint16_t Vs[QB * (HD + 8)];
@@ -389,8 +407,8 @@ __global__ __launch_bounds__(256) void k_flash_bwd_q(const AttnArgs a) {
             f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f}, dpt = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ds = 0; ds < HD / 32; ++ds) {
-                st = mfma(*reinterpret_cast<const uint4*>(Ks + (kt * 16 + lr) * (HD + 8) + ds * 32 + g * 8), qf[ds], st);
-                dpt = mfma(*reinterpret_cast<const uint4*>(Vs + (kt * 16 + lr) * (HD + 8) + ds * 32 + g * 8), df[ds],
+                st = mfma<TE>(*reinterpret_cast<const uint4*>(Ks + (kt * 16 + lr) * (HD + 8) + ds * 32 + g * 8), qf[ds], st);
+                dpt = mfma<TE>(*reinterpret_cast<const uint4*>(Vs + (kt * 16 + lr) * (HD + 8) + ds * 32 + g * 8), df[ds],
                            dpt);
             }
             float d[4];
@@ -401,15 +419,15 @@ __global__ __launch_bounds__(256) void k_flash_bwd_q(const AttnArgs a) {
                 const float p = live ? exp2f(fmaf(st[e], c, -lse2)) : 0.f;
                 d[e] = p * (dpt[e] - dd);
             }
-            sk[kt][0] = pack_bf16(d[0], d[1]);
-            sk[kt][1] = pack_bf16(d[2], d[3]);
+            sk[kt][0] = pack2<TE>(d[0], d[1]);
+            sk[kt][1] = pack2<TE>(d[2], d[3]);
         }
         // dQ^T += K^T dS^T over the 64 keys
 #pragma unroll
         for (int js = 0; js < 2; ++js) {
             const uint4 sb = make_uint4(sk[2 * js][0], sk[2 * js][1], sk[2 * js + 1][0], sk[2 * js + 1][1]);
 #pragma unroll
-            for (int dt = 0; dt < HD / 16; ++dt) dq[dt] = mfma(tfrag<HD>(Kt, dt, js, lane), sb, dq[dt]);
+            for (int dt = 0; dt < HD / 16; ++dt) dq[dt] = mfma<TE>(tfrag<HD>(Kt, dt, js, lane), sb, dq[dt]);
         }
         __syncthreads();
     }
@@ -430,7 +448,7 @@ __global__ __launch_bounds__(256) void k_flash_bwd_q(const AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < HD / 16; ++dt)
         *reinterpret_cast<uint2*>(dst + dt * 16) =
-            make_uint2(pack_bf16(dq[dt][0], dq[dt][1]), pack_bf16(dq[dt][2], dq[dt][3]));
+            make_uint2(pack2<TE>(dq[dt][0], dq[dt][1]), pack2<TE>(dq[dt][2], dq[dt][3]));
 }
 
 // ------------------------------------------------------------------ launchers
@@ -450,8 +468,13 @@ void launch_flash_fwd(const AttnArgs& a, hipStream_t s) {
     const double Sd = a.S;
     const double flops = 4.0 * a.B * a.nH * a.hd * (Sd * (Sd + 1) / 2);
     ProfScope prof("attn_fwd", flops, double(a.B) * a.S * (a.qdim * 4.0 + a.kvdim * 4.0 + a.nH * 4.0), s);
-    if (a.hd == 128) hipLaunchKernelGGL(k_flash_fwd<128>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(k_flash_fwd<64>, grid, dim3(256), 0, s, a);
+    if (a.hd == 128) {
+        if (a.f16) hipLaunchKernelGGL((k_flash_fwd<128, TE_F16>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((k_flash_fwd<128, TE_BF16>), grid, dim3(256), 0, s, a);
+    } else {
+        if (a.f16) hipLaunchKernelGGL((k_flash_fwd<64, TE_F16>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((k_flash_fwd<64, TE_BF16>), grid, dim3(256), 0, s, a);
+    }
     check_launch("attn_fwd");
 }
 
@@ -462,7 +485,8 @@ void launch_flash_bwd(const AttnArgs& a, hipStream_t s) {
     {
         ProfScope prof("attn_bwd_dot", 2.0 * n * a.hd, double(n) * (a.hd * 4.0 + 4.0), s);
         const int64_t threads = n * (a.hd / 8);
-        hipLaunchKernelGGL(k_flash_bwd_dot, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, a, a.hd);
+        if (a.f16) hipLaunchKernelGGL(k_flash_bwd_dot<TE_F16>, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, a, a.hd);
+        else hipLaunchKernelGGL(k_flash_bwd_dot<TE_BF16>, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, a, a.hd);
         check_launch("attn_bwd_dot");
     }
     const dim3 grid(unsigned((a.S + QB - 1) / QB), unsigned(a.nH), unsigned(a.B));
@@ -470,15 +494,25 @@ void launch_flash_bwd(const AttnArgs& a, hipStream_t s) {
     {  // recompute S and dP, then dV and dK: 4 products
         ProfScope prof("attn_bwd_kv", 8.0 * a.B * a.nH * a.hd * causal,
                        double(a.B) * a.S * (a.qdim * 4.0 + a.kvdim * 4.0 + a.nH * 2.0 * a.hd * 4.0), s);
-        if (a.hd == 128) hipLaunchKernelGGL(k_flash_bwd_kv<128>, grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL(k_flash_bwd_kv<64>, grid, dim3(256), 0, s, a);
+        if (a.hd == 128) {
+            if (a.f16) hipLaunchKernelGGL((k_flash_bwd_kv<128, TE_F16>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((k_flash_bwd_kv<128, TE_BF16>), grid, dim3(256), 0, s, a);
+        } else {
+            if (a.f16) hipLaunchKernelGGL((k_flash_bwd_kv<64, TE_F16>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((k_flash_bwd_kv<64, TE_BF16>), grid, dim3(256), 0, s, a);
+        }
         check_launch("attn_bwd_kv");
     }
     {  // recompute S and dP, then dQ: 3 products
         ProfScope prof("attn_bwd_q", 6.0 * a.B * a.nH * a.hd * causal,
                        double(a.B) * a.S * (a.qdim * 6.0 + a.kvdim * 4.0), s);
-        if (a.hd == 128) hipLaunchKernelGGL(k_flash_bwd_q<128>, grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL(k_flash_bwd_q<64>, grid, dim3(256), 0, s, a);
+        if (a.hd == 128) {
+            if (a.f16) hipLaunchKernelGGL((k_flash_bwd_q<128, TE_F16>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((k_flash_bwd_q<128, TE_BF16>), grid, dim3(256), 0, s, a);
+        } else {
+            if (a.f16) hipLaunchKernelGGL((k_flash_bwd_q<64, TE_F16>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((k_flash_bwd_q<64, TE_BF16>), grid, dim3(256), 0, s, a);
+        }
         check_launch("attn_bwd_q");
     }
 }

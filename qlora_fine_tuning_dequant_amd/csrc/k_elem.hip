@@ -190,18 +190,18 @@ void launch_rmsnorm_bwd(const float* dy, const float* x, const float* g, const f
     check_launch("rmsnorm_bwd");
 }
 
-// bf16 x8 <-> fp32 x8 for 16-byte accesses.
-__device__ inline void unpack8(const uint4& v, float (&f)[8]) {
+// 16-bit activations (bf16, or fp16 when f16) x8 <-> fp32 x8 for 16-byte accesses.
+__device__ inline void unpack8(const uint4& v, float (&f)[8], bool f16) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        f[2 * k] = __builtin_bit_cast(float, w[k] << 16);
-        f[2 * k + 1] = __builtin_bit_cast(float, w[k] & 0xFFFF0000u);
+        f[2 * k] = act_to_f32(uint16_t(w[k]), f16);
+        f[2 * k + 1] = act_to_f32(uint16_t(w[k] >> 16), f16);
     }
 }
-__device__ inline uint4 pack8_bf16(const float (&f)[8]) {
-    return make_uint4(f32x2_to_bf16x2(f[0], f[1]), f32x2_to_bf16x2(f[2], f[3]), f32x2_to_bf16x2(f[4], f[5]),
-                      f32x2_to_bf16x2(f[6], f[7]));
+__device__ inline uint4 pack8(const float (&f)[8], bool f16) {
+    return make_uint4(f32x2_to_act2(f[0], f[1], f16), f32x2_to_act2(f[2], f[3], f16), f32x2_to_act2(f[4], f[5], f16),
+                      f32x2_to_act2(f[6], f[7], f16));
 }
 
 // ------------------------------------------------------------------ RoPE
@@ -218,7 +218,7 @@ __global__ void k_rope_table(int seq, int hd, double theta, float2* cs) {
 
 // RoPE, forward rotation of each (j, j + hd/2) pair; one thread per pair.
 __global__ void k_rope(uint16_t* __restrict__ buf, int64_t ld, int T, int seq, int col0, int nheads, int hd,
-                       const float2* __restrict__ cs) {
+                       const float2* __restrict__ cs, int f16) {
     const int half = hd / 2;
     const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t total = int64_t(T) * nheads * half;
@@ -228,15 +228,15 @@ __global__ void k_rope(uint16_t* __restrict__ buf, int64_t ld, int T, int seq, i
     const int t = int(idx / (int64_t(half) * nheads));
     const float2 c = cs[(t % seq) * half + j];
     uint16_t* p = buf + int64_t(t) * ld + col0 + h * hd + j;
-    const float x1 = bf16_bits_to_f32(p[0]), x2 = bf16_bits_to_f32(p[half]);
-    p[0] = f32_to_bf16_bits(x1 * c.x - x2 * c.y);
-    p[half] = f32_to_bf16_bits(x2 * c.x + x1 * c.y);
+    const float x1 = act_to_f32(p[0], f16), x2 = act_to_f32(p[half], f16);
+    p[0] = f32_to_act(x1 * c.x - x2 * c.y, f16);
+    p[half] = f32_to_act(x2 * c.x + x1 * c.y, f16);
 }
 
 // Same rotation, eight consecutive pairs per thread (16-byte loads and
 // stores of each half; hd/2 a multiple of 8, rows 16-byte aligned).
 __global__ void k_rope8(uint16_t* __restrict__ buf, int64_t ld, int T, int seq, int col0, int nheads, int hd,
-                        const float2* __restrict__ cs) {
+                        const float2* __restrict__ cs, int f16) {
     const int half = hd / 2, h8 = half / 8;
     const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t total = int64_t(T) * nheads * h8;
@@ -247,8 +247,8 @@ __global__ void k_rope8(uint16_t* __restrict__ buf, int64_t ld, int T, int seq, 
     const float4* c4 = reinterpret_cast<const float4*>(cs + (t % seq) * half + j);
     uint16_t* p = buf + int64_t(t) * ld + col0 + h * hd + j;
     float a[8], b[8], ra[8], rb[8];
-    unpack8(*reinterpret_cast<const uint4*>(p), a);
-    unpack8(*reinterpret_cast<const uint4*>(p + half), b);
+    unpack8(*reinterpret_cast<const uint4*>(p), a, f16);
+    unpack8(*reinterpret_cast<const uint4*>(p + half), b, f16);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const float4 c = c4[k];  // (cos, sin) of pairs 2k and 2k+1
@@ -257,8 +257,8 @@ __global__ void k_rope8(uint16_t* __restrict__ buf, int64_t ld, int T, int seq, 
         ra[2 * k + 1] = a[2 * k + 1] * c.z - b[2 * k + 1] * c.w;
         rb[2 * k + 1] = b[2 * k + 1] * c.z + a[2 * k + 1] * c.w;
     }
-    *reinterpret_cast<uint4*>(p) = pack8_bf16(ra);
-    *reinterpret_cast<uint4*>(p + half) = pack8_bf16(rb);
+    *reinterpret_cast<uint4*>(p) = pack8(ra, f16);
+    *reinterpret_cast<uint4*>(p + half) = pack8(rb, f16);
 }
 
 void launch_rope_table(int seq, int hd, float theta, float* cs, hipStream_t s) {
@@ -268,7 +268,7 @@ void launch_rope_table(int seq, int hd, float theta, float* cs, hipStream_t s) {
                        reinterpret_cast<float2*>(cs));
     check_launch("rope_table");
 }
-void launch_rope(uint16_t* buf, int64_t ld, int T, int seq, int col0, int nheads, int hd, const float* cs,
+void launch_rope(uint16_t* buf, int64_t ld, int T, int seq, int col0, int nheads, int hd, const float* cs, int f16,
                  hipStream_t s) {
     const int64_t total = int64_t(T) * nheads * (hd / 2);
     if (total <= 0) return;
@@ -276,93 +276,93 @@ void launch_rope(uint16_t* buf, int64_t ld, int T, int seq, int col0, int nheads
     if ((hd / 2) % 8 == 0 && ld % 8 == 0 && col0 % 8 == 0 && al16(buf) && al16(cs)) {
         const int64_t t8 = total / 8;
         hipLaunchKernelGGL(k_rope8, dim3(unsigned((t8 + 255) / 256)), dim3(256), 0, s, buf, ld, T, seq, col0, nheads,
-                           hd, reinterpret_cast<const float2*>(cs));
+                           hd, reinterpret_cast<const float2*>(cs), f16);
         check_launch("rope");
         return;
     }
     hipLaunchKernelGGL(k_rope, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, buf, ld, T, seq, col0, nheads,
-                       hd, reinterpret_cast<const float2*>(cs));
+                       hd, reinterpret_cast<const float2*>(cs), f16);
     check_launch("rope");
 }
 
 // ------------------------------------------------------------------ SwiGLU
-// gu = [gate | up] bf16 [T, 2I]; act = silu(gate) * up.
+// gu = [gate | up] 16-bit [T, 2I]; act = silu(gate) * up.
 __device__ inline float silu_sig(float g) { return 1.0f / (1.0f + expf(-g)); }
 // VEC: 8 consecutive i per thread with 16-byte accesses (I % 8 == 0, 16-byte
 // aligned buffers); the arithmetic per element is the same either way.
 template <bool VEC>
-__global__ void k_swiglu_fwd(const uint16_t* __restrict__ gu, int T, int I, uint16_t* __restrict__ act) {
+__global__ void k_swiglu_fwd(const uint16_t* __restrict__ gu, int T, int I, uint16_t* __restrict__ act, int f16) {
     const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (VEC) {
         const int I8 = I / 8;
         if (idx >= int64_t(T) * I8) return;
         const int64_t t = idx / I8, i = (idx % I8) * 8;
         float g[8], u[8], y[8];
-        unpack8(*reinterpret_cast<const uint4*>(gu + t * 2 * I + i), g);
-        unpack8(*reinterpret_cast<const uint4*>(gu + t * 2 * I + I + i), u);
+        unpack8(*reinterpret_cast<const uint4*>(gu + t * 2 * I + i), g, f16);
+        unpack8(*reinterpret_cast<const uint4*>(gu + t * 2 * I + I + i), u, f16);
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = g[e] * silu_sig(g[e]) * u[e];
-        *reinterpret_cast<uint4*>(act + t * I + i) = pack8_bf16(y);
+        *reinterpret_cast<uint4*>(act + t * I + i) = pack8(y, f16);
         return;
     }
     if (idx >= int64_t(T) * I) return;
     const int64_t t = idx / I, i = idx % I;
-    const float g = bf16_bits_to_f32(gu[t * 2 * I + i]);
-    const float u = bf16_bits_to_f32(gu[t * 2 * I + I + i]);
-    act[idx] = f32_to_bf16_bits(g * silu_sig(g) * u);
+    const float g = act_to_f32(gu[t * 2 * I + i], f16);
+    const float u = act_to_f32(gu[t * 2 * I + I + i], f16);
+    act[idx] = f32_to_act(g * silu_sig(g) * u, f16);
 }
 // dgate = da * up * silu'(gate), dup = da * silu(gate); silu' = s (1 + g (1 - s)).
 template <bool VEC>
 __global__ void k_swiglu_bwd(const uint16_t* __restrict__ dact, const uint16_t* __restrict__ gu, int T, int I,
-                             uint16_t* __restrict__ dgu) {
+                             uint16_t* __restrict__ dgu, int f16) {
     const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (VEC) {
         const int I8 = I / 8;
         if (idx >= int64_t(T) * I8) return;
         const int64_t t = idx / I8, i = (idx % I8) * 8;
         float g[8], u[8], da[8], dg[8], du[8];
-        unpack8(*reinterpret_cast<const uint4*>(gu + t * 2 * I + i), g);
-        unpack8(*reinterpret_cast<const uint4*>(gu + t * 2 * I + I + i), u);
-        unpack8(*reinterpret_cast<const uint4*>(dact + t * I + i), da);
+        unpack8(*reinterpret_cast<const uint4*>(gu + t * 2 * I + i), g, f16);
+        unpack8(*reinterpret_cast<const uint4*>(gu + t * 2 * I + I + i), u, f16);
+        unpack8(*reinterpret_cast<const uint4*>(dact + t * I + i), da, f16);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float sg = silu_sig(g[e]);
             dg[e] = da[e] * u[e] * (sg * (1.0f + g[e] * (1.0f - sg)));
             du[e] = da[e] * g[e] * sg;
         }
-        *reinterpret_cast<uint4*>(dgu + t * 2 * I + i) = pack8_bf16(dg);
-        *reinterpret_cast<uint4*>(dgu + t * 2 * I + I + i) = pack8_bf16(du);
+        *reinterpret_cast<uint4*>(dgu + t * 2 * I + i) = pack8(dg, f16);
+        *reinterpret_cast<uint4*>(dgu + t * 2 * I + I + i) = pack8(du, f16);
         return;
     }
     if (idx >= int64_t(T) * I) return;
     const int64_t t = idx / I, i = idx % I;
-    const float g = bf16_bits_to_f32(gu[t * 2 * I + i]);
-    const float u = bf16_bits_to_f32(gu[t * 2 * I + I + i]);
-    const float da = bf16_bits_to_f32(dact[idx]);
+    const float g = act_to_f32(gu[t * 2 * I + i], f16);
+    const float u = act_to_f32(gu[t * 2 * I + I + i], f16);
+    const float da = act_to_f32(dact[idx], f16);
     const float sg = silu_sig(g);
-    dgu[t * 2 * I + i] = f32_to_bf16_bits(da * u * (sg * (1.0f + g * (1.0f - sg))));
-    dgu[t * 2 * I + I + i] = f32_to_bf16_bits(da * g * sg);
+    dgu[t * 2 * I + i] = f32_to_act(da * u * (sg * (1.0f + g * (1.0f - sg))), f16);
+    dgu[t * 2 * I + I + i] = f32_to_act(da * g * sg, f16);
 }
-void launch_swiglu_fwd(const uint16_t* gu, int T, int I, uint16_t* act, hipStream_t s) {
+void launch_swiglu_fwd(const uint16_t* gu, int T, int I, uint16_t* act, int f16, hipStream_t s) {
     const int64_t n = int64_t(T) * I;
     if (n <= 0) return;
     ProfScope prof("swiglu_fwd", 5.0 * n, 6.0 * n, s);
     if (I % 8 == 0 && al16(gu) && al16(act))
-        hipLaunchKernelGGL(k_swiglu_fwd<true>, dim3(unsigned((n / 8 + 255) / 256)), dim3(256), 0, s, gu, T, I, act);
+        hipLaunchKernelGGL(k_swiglu_fwd<true>, dim3(unsigned((n / 8 + 255) / 256)), dim3(256), 0, s, gu, T, I, act, f16);
     else
-        hipLaunchKernelGGL(k_swiglu_fwd<false>, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, gu, T, I, act);
+        hipLaunchKernelGGL(k_swiglu_fwd<false>, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, gu, T, I, act, f16);
     check_launch("swiglu_fwd");
 }
-void launch_swiglu_bwd(const uint16_t* dact, const uint16_t* gu, int T, int I, uint16_t* dgu, hipStream_t s) {
+void launch_swiglu_bwd(const uint16_t* dact, const uint16_t* gu, int T, int I, uint16_t* dgu, int f16, hipStream_t s) {
     const int64_t n = int64_t(T) * I;
     if (n <= 0) return;
     ProfScope prof("swiglu_bwd", 10.0 * n, 10.0 * n, s);
     if (I % 8 == 0 && al16(gu) && al16(dact) && al16(dgu))
         hipLaunchKernelGGL(k_swiglu_bwd<true>, dim3(unsigned((n / 8 + 255) / 256)), dim3(256), 0, s, dact, gu, T, I,
-                           dgu);
+                           dgu, f16);
     else
         hipLaunchKernelGGL(k_swiglu_bwd<false>, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, dact, gu, T, I,
-                           dgu);
+                           dgu, f16);
     check_launch("swiglu_bwd");
 }
 
@@ -384,28 +384,31 @@ void launch_embed(const int32_t* tok, const uint16_t* E, int T, int H, int V, fl
     check_launch("embed");
 }
 
-// 8 elements per thread (two 16-byte loads, one 16-byte store) where the
-// buffers allow, else one.
+// y = 16-bit(x * scale) (bf16, or fp16 when f16; scale a power of two that
+// moves gradients into fp16's normal range). 8 elements per thread (two
+// 16-byte loads, one 16-byte store) where the buffers allow, else one.
 template <bool VEC>
-__global__ void k_f32_to_bf16(const float* __restrict__ x, int64_t n, uint16_t* __restrict__ y) {
+__global__ void k_f32_to_act(const float* __restrict__ x, int64_t n, uint16_t* __restrict__ y, int f16, float sc) {
     const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (VEC) {
         if (i >= n / 8) return;
         const float4 a = reinterpret_cast<const float4*>(x)[2 * i], b = reinterpret_cast<const float4*>(x)[2 * i + 1];
-        reinterpret_cast<uint4*>(y)[i] = make_uint4(f32x2_to_bf16x2(a.x, a.y), f32x2_to_bf16x2(a.z, a.w),
-                                                    f32x2_to_bf16x2(b.x, b.y), f32x2_to_bf16x2(b.z, b.w));
+        reinterpret_cast<uint4*>(y)[i] =
+            make_uint4(f32x2_to_act2(a.x * sc, a.y * sc, f16), f32x2_to_act2(a.z * sc, a.w * sc, f16),
+                       f32x2_to_act2(b.x * sc, b.y * sc, f16), f32x2_to_act2(b.z * sc, b.w * sc, f16));
         return;
     }
-    if (i < n) y[i] = f32_to_bf16_bits(x[i]);
+    if (i < n) y[i] = f32_to_act(x[i] * sc, f16);
 }
-void launch_f32_to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s) {
+void launch_f32_to_act(const float* x, int64_t n, uint16_t* y, int f16, float scale, hipStream_t s) {
     if (n <= 0) return;
-    ProfScope prof("f32_to_bf16", 0.0, 6.0 * n, s);
+    ProfScope prof("f32_to_16", 0.0, 6.0 * n, s);
     if (n % 8 == 0 && al16(x) && al16(y))
-        hipLaunchKernelGGL(k_f32_to_bf16<true>, dim3(unsigned((n / 8 + 255) / 256)), dim3(256), 0, s, x, n, y);
+        hipLaunchKernelGGL(k_f32_to_act<true>, dim3(unsigned((n / 8 + 255) / 256)), dim3(256), 0, s, x, n, y, f16,
+                           scale);
     else
-        hipLaunchKernelGGL(k_f32_to_bf16<false>, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, x, n, y);
-    check_launch("f32_to_bf16");
+        hipLaunchKernelGGL(k_f32_to_act<false>, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, x, n, y, f16, scale);
+    check_launch("f32_to_16");
 }
 
 // ------------------------------------------------------------------ stream debugging
@@ -472,21 +475,23 @@ void launch_spin(int delay_us, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------ LoRA staging
-// Acat [nseg*r, in] = bf16(A_p) stacked; Bbd [sum out_p, nseg*r] block-diagonal
-// with block p = bf16(scale * B_p), zeros elsewhere. The zeros contribute
-// exact +0 products, so a projection only sees its own adapter.
+// Acat [nseg*r, in] = 16-bit(A_p) stacked; Bbd [sum out_p, nseg*r]
+// block-diagonal with block p = 16-bit(scale * B_p), zeros elsewhere (bf16,
+// or fp16 when f16). The zeros contribute exact +0 products, so a projection
+// only sees its own adapter.
 struct LoraSegs {
     const float* A[3];
     const float* B[3];
     int out[3];
     int nseg;
+    int f16;
 };
 __device__ inline void lora_pack_one(const LoraSegs& sg, int r, int in_f, float scale, uint16_t* __restrict__ Acat,
                                      uint16_t* __restrict__ Bbd, int64_t nA, int64_t nB, int64_t idx) {
     if (idx < nA) {
         const int64_t row = idx / in_f, k = idx % in_f;
         const int p = int(row / r), i = int(row % r);
-        Acat[idx] = f32_to_bf16_bits(sg.A[p][int64_t(i) * in_f + k]);
+        Acat[idx] = f32_to_act(sg.A[p][int64_t(i) * in_f + k], sg.f16);
         return;
     }
     const int64_t jdx = idx - nA;
@@ -496,7 +501,7 @@ __device__ inline void lora_pack_one(const LoraSegs& sg, int r, int in_f, float 
     const int q = c / r, j = c % r;
     int off = 0, p = 0;
     while (p < sg.nseg - 1 && n >= off + sg.out[p]) off += sg.out[p++];
-    Bbd[jdx] = (p == q) ? f32_to_bf16_bits(scale * sg.B[p][int64_t(n - off) * r + j]) : uint16_t(0);
+    Bbd[jdx] = (p == q) ? f32_to_act(scale * sg.B[p][int64_t(n - off) * r + j], sg.f16) : uint16_t(0);
 }
 // Eight consecutive elements per thread (in_f and r multiples of 8, every
 // pointer 16-byte aligned): two float4 loads and one 16-byte store. idx8
@@ -511,7 +516,7 @@ __device__ inline void lora_pack_one8(const LoraSegs& sg, int r, int in_f, float
         const float4* src = reinterpret_cast<const float4*>(sg.A[p] + int64_t(i) * in_f + k);
         const float4 u = src[0], v = src[1];
         f[0] = u.x, f[1] = u.y, f[2] = u.z, f[3] = u.w, f[4] = v.x, f[5] = v.y, f[6] = v.z, f[7] = v.w;
-        *reinterpret_cast<uint4*>(Acat + idx) = pack8_bf16(f);
+        *reinterpret_cast<uint4*>(Acat + idx) = pack8(f, sg.f16);
         return;
     }
     const int64_t jdx = idx - nA;
@@ -527,7 +532,7 @@ __device__ inline void lora_pack_one8(const LoraSegs& sg, int r, int in_f, float
         const float4 u = src[0], v = src[1];
         f[0] = scale * u.x, f[1] = scale * u.y, f[2] = scale * u.z, f[3] = scale * u.w;
         f[4] = scale * v.x, f[5] = scale * v.y, f[6] = scale * v.z, f[7] = scale * v.w;
-        o = pack8_bf16(f);
+        o = pack8(f, sg.f16);
     }
     *reinterpret_cast<uint4*>(Bbd + jdx) = o;
 }
@@ -553,8 +558,9 @@ __global__ void k_lora_pack_jobs(const LoraPackArgs a, int r, float scale) {
         lora_pack_one(a.sg[y], r, a.in_f[y], scale, a.Acat[y], a.Bbd[y], a.nA[y], a.nB[y], i);
 }
 void launch_lora_pack(const LoraSeg* segs, int nseg, int r, int in_f, float scale, uint16_t* Acat, uint16_t* Bbd,
-                      hipStream_t s) {
+                      int f16, hipStream_t s) {
     LoraSegs sg{};
+    sg.f16 = f16;
     int ntot = 0;
     for (int p = 0; p < nseg; ++p) {
         sg.A[p] = segs[p].A;
@@ -571,7 +577,7 @@ void launch_lora_pack(const LoraSeg* segs, int nseg, int r, int in_f, float scal
     check_launch("lora_pack");
 }
 
-void launch_lora_pack_jobs(const LoraPackJob* jobs, int njobs, int r, float scale, hipStream_t s) {
+void launch_lora_pack_jobs(const LoraPackJob* jobs, int njobs, int r, float scale, int f16, hipStream_t s) {
     QLX_REQUIRE(njobs >= 1 && njobs <= 4, QLX_EINVAL, "lora pack: 1..4 jobs");
     LoraPackArgs a{};
     int64_t nmax = 0;
@@ -589,6 +595,7 @@ void launch_lora_pack_jobs(const LoraPackJob* jobs, int njobs, int r, float scal
         }
         vec = vec && jb.in_f % 8 == 0 && al16(jb.Acat) && al16(jb.Bbd);
         a.sg[y].nseg = jb.nseg;
+        a.sg[y].f16 = f16;
         a.in_f[y] = jb.in_f;
         a.Acat[y] = jb.Acat;
         a.Bbd[y] = jb.Bbd;
@@ -609,10 +616,12 @@ void launch_lora_pack_jobs(const LoraPackJob* jobs, int njobs, int r, float scal
     check_launch("lora_pack");
 }
 
-// Per-query-head gradients dh [B*nH, S, hd] -> per-KV-head sums written as bf16
-// into out[(b*S + t)*ldo + col0 + kvh*hd + d]; group members summed in order.
+// Per-query-head gradients dh [B*nH, S, hd] -> per-KV-head sums written as
+// 16-bit values (bf16, or fp16 when f16) into out[(b*S + t)*ldo + col0 +
+// kvh*hd + d]; group members summed in order.
 __global__ void k_gqa_reduce(const float* __restrict__ dh, int B, int nH, int nKV, int S, int hd,
-                             uint16_t* __restrict__ out, int64_t ldo, int col0, const float2* __restrict__ rope) {
+                             uint16_t* __restrict__ out, int64_t ldo, int col0, const float2* __restrict__ rope,
+                             int f16) {
     const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int half = hd / 2, np = rope ? half : hd;  // a thread: one dim, or one rotated pair
     const int64_t total = int64_t(B) * nKV * S * np;
@@ -630,21 +639,21 @@ __global__ void k_gqa_reduce(const float* __restrict__ dh, int B, int nH, int nK
     }
     uint16_t* o = out + (int64_t(b) * S + t) * ldo + col0 + kvh * hd;
     if (!rope) {
-        o[d] = f32_to_bf16_bits(v);
+        o[d] = f32_to_act(v, f16);
         return;
     }
     const float2 c = rope[int64_t(t) * half + d];  // the rotation's transpose
-    o[d] = f32_to_bf16_bits(v * c.x + w * c.y);
-    o[d + half] = f32_to_bf16_bits(w * c.x - v * c.y);
+    o[d] = f32_to_act(v * c.x + w * c.y, f16);
+    o[d + half] = f32_to_act(w * c.x - v * c.y, f16);
 }
 void launch_gqa_reduce(const float* dh, int B, int nH, int nKV, int S, int hd, uint16_t* out, int64_t ldo, int col0,
-                       const float* rope, hipStream_t s) {
+                       const float* rope, int f16, hipStream_t s) {
     const int64_t total = int64_t(B) * nKV * S * (rope ? hd / 2 : hd);
     if (total <= 0) return;
     ProfScope prof("gqa_reduce", double(B) * nKV * S * hd * (nH / nKV), double(B) * nKV * S * hd * (4.0 * (nH / nKV) + 2.0),
                    s);
     hipLaunchKernelGGL(k_gqa_reduce, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, dh, B, nH, nKV, S, hd, out,
-                       ldo, col0, reinterpret_cast<const float2*>(rope));
+                       ldo, col0, reinterpret_cast<const float2*>(rope), f16);
     check_launch("gqa_reduce");
 }
 

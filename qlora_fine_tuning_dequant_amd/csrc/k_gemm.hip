@@ -28,6 +28,8 @@
 // results depend only on shapes, never on timing or pointer values.
 #include <algorithm>
 #include <atomic>
+#include <cstdlib>
+#include <string>
 #include <type_traits>
 
 #include <hip/hip_ext.h>
@@ -156,21 +158,38 @@ struct TransLoader {
     }
 };
 
+// The weight operand is the dequantized value rounded to bf16 (QLoRA's
+// computation type). With fp16 activations (TE_F16) that bf16 value is then
+// converted to fp16, exactly for every |value| in [2^-17, 65504] (fp16 holds
+// bf16's 8-bit significands there), so the product sees the same weights.
+template <int TE>
+__device__ __forceinline__ uint32_t wpair(float lo, float hi) {
+    const uint32_t b = f32x2_to_bf16x2(lo, hi);
+    if constexpr (TE == TE_BF16) return b;
+    else return bf16x2_to_f16x2(b);
+}
+template <int TE>
+__device__ __forceinline__ uint32_t wone(float v) {
+    return wpair<TE>(v, 0.f) & 0xFFFFu;
+}
+
+template <int TE>
 __device__ inline uint32_t nf4_elem(const uint8_t* __restrict__ packed, const float* __restrict__ absmax,
                                     int64_t flat, const float* lut) {
     const uint32_t byte = packed[flat >> 1];
     const int code = (flat & 1) ? int(byte & 15) : int(byte >> 4);
-    return f32_to_bf16_bits(lut[code] * absmax[flat >> 6]);
+    return wone<TE>(lut[code] * absmax[flat >> 6]);
 }
 
+template <int TE>
 __device__ inline uint32_t deq2(uint32_t byte, float a, const float* lut) {
-    // byte -> bf16 pair (high nibble = even element in the low half)
-    return f32x2_to_bf16x2(lut[byte >> 4] * a, lut[byte & 15] * a);
+    // byte -> 16-bit pair (high nibble = even element in the low half)
+    return wpair<TE>(lut[byte >> 4] * a, lut[byte & 15] * a);
 }
 
 // NF4 weight stored [N][K] (flat n*cols + k): tile[n][k]. A unit is 32 codes
 // (16 bytes) of one row inside one 64-element absmax block.
-template <int R, int NT>
+template <int R, int NT, int TE>
 struct Nf4NtLoader {
     static constexpr int U = R * 2 / NT;
     static_assert(U >= 1 && R * 2 % NT == 0, "nf4 nt loader shape");
@@ -203,14 +222,14 @@ struct Nf4NtLoader {
                 for (int q = 0; q < 4; ++q) {
                     const uint32_t x = words[q];
                     *reinterpret_cast<uint4*>(dst + q * 8) =
-                        make_uint4(deq2(x & 0xFF, a[u], lut), deq2((x >> 8) & 0xFF, a[u], lut),
-                                   deq2((x >> 16) & 0xFF, a[u], lut), deq2(x >> 24, a[u], lut));
+                        make_uint4(deq2<TE>(x & 0xFF, a[u], lut), deq2<TE>((x >> 8) & 0xFF, a[u], lut),
+                                   deq2<TE>((x >> 16) & 0xFF, a[u], lut), deq2<TE>(x >> 24, a[u], lut));
                 }
             } else {
                 const int gn = n0 + r, gk = k0 + half * 32;
                 for (int j = 0; j < 32; ++j) {
                     const int k = gk + j;
-                    dst[j] = (gn < N && k < K) ? uint16_t(nf4_elem(packed, absmax, int64_t(gn) * cols + k, lut))
+                    dst[j] = (gn < N && k < K) ? uint16_t(nf4_elem<TE>(packed, absmax, int64_t(gn) * cols + k, lut))
                                                : uint16_t(0);
                 }
             }
@@ -220,7 +239,7 @@ struct Nf4NtLoader {
 
 // NF4 weight stored [K][N] (flat k*cols + n): tile[n][k]. A unit is 4
 // consecutive n (2 bytes) from each of 8 consecutive k rows.
-template <int R, int NT>
+template <int R, int NT, int TE>
 struct Nf4NnLoader {
     static constexpr int U = (R / 4) * (BK / 8) / NT;
     static_assert(U >= 1 && (R / 4) * (BK / 8) % NT == 0, "nf4 nn loader shape");
@@ -257,8 +276,8 @@ struct Nf4NnLoader {
                 for (int kr = 0; kr < 8; ++kr) {
                     const uint32_t t = two[u][kr];
                     const float s = a[u][kr];
-                    e2[kr][0] = f32x2_to_bf16x2(lut[(t >> 4) & 15] * s, lut[t & 15] * s);
-                    e2[kr][1] = f32x2_to_bf16x2(lut[(t >> 12) & 15] * s, lut[(t >> 8) & 15] * s);
+                    e2[kr][0] = wpair<TE>(lut[(t >> 4) & 15] * s, lut[t & 15] * s);
+                    e2[kr][1] = wpair<TE>(lut[(t >> 12) & 15] * s, lut[(t >> 8) & 15] * s);
                 }
             } else {
 #pragma unroll
@@ -268,7 +287,7 @@ struct Nf4NnLoader {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int gn = n0 + ng + j;
-                        e[j] = (gk < K && gn < N) ? nf4_elem(packed, absmax, int64_t(gk) * cols + gn, lut) : 0u;
+                        e[j] = (gk < K && gn < N) ? nf4_elem<TE>(packed, absmax, int64_t(gk) * cols + gn, lut) : 0u;
                     }
                     e2[kr][0] = pack2(e[0], e[1]);
                     e2[kr][1] = pack2(e[2], e[3]);
@@ -337,13 +356,16 @@ __device__ inline void store_out(const GemmParams& p, int bo, int bi, int row, i
 __device__ inline void store_row(const GemmParams& p, int bo, int bi, int row, int col, const float* v, int n) {
     if (p.seg_rows == 0 && !p.accumulate && col + n <= p.N && (n & 7) == 0) {
         const int64_t off = int64_t(bo) * p.c_so + int64_t(bi) * p.c_si + int64_t(row) * p.ldc + col;
-        if (p.c_type == C_BF16 && (off & 7) == 0 && !p.R) {
+        if ((p.c_type == C_BF16 || p.c_type == C_F16) && (off & 7) == 0 && !p.R) {
             uint16_t* dst = static_cast<uint16_t*>(p.C) + off;
+            const bool h = p.c_type == C_F16;
             for (int c = 0; c < n; c += 8) {
                 uint32_t w[4];
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    w[k] = f32x2_to_bf16x2(v[c + 2 * k] * p.alpha, v[c + 2 * k + 1] * p.alpha);
+                for (int k = 0; k < 4; ++k) {
+                    const float lo = v[c + 2 * k] * p.alpha, hi = v[c + 2 * k + 1] * p.alpha;
+                    w[k] = h ? f32x2_to_f16x2(lo, hi) : f32x2_to_bf16x2(lo, hi);
+                }
                 *reinterpret_cast<uint4*>(dst + c) = make_uint4(w[0], w[1], w[2], w[3]);
             }
             return;
@@ -371,10 +393,10 @@ __device__ inline void store_row(const GemmParams& p, int bo, int bi, int row, i
 
 template <int AK, int R, int NT>
 using ALoader = typename std::conditional<AK == A_ROW, RowLoader<R, NT>, TransLoader<R, NT>>::type;
-template <int BKIND, int R, int NT>
+template <int BKIND, int R, int NT, int TE>
 using BLoader = typename std::conditional<
-    BKIND == B_NF4_NT, Nf4NtLoader<R, NT>,
-    typename std::conditional<BKIND == B_NF4_NN, Nf4NnLoader<R, NT>,
+    BKIND == B_NF4_NT, Nf4NtLoader<R, NT, TE>,
+    typename std::conditional<BKIND == B_NF4_NN, Nf4NnLoader<R, NT, TE>,
                               typename std::conditional<BKIND == B_DENSE_NT, RowLoader<R, NT>,
                                                         TransLoader<R, NT>>::type>::type>::type;
 
@@ -481,7 +503,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm(const GemmP
 
     {
         ALoader<AK, BM, NT> la;
-        BLoader<BKIND, BN, NT> lb;
+        BLoader<BKIND, BN, NT, TE> lb;
         __syncthreads();  // lut ready
         if (kbeg < kend) {
             la.load(A, p.lda, m0, kbeg, p.M, p.K, p.a_vec);
@@ -681,7 +703,7 @@ struct DmaPlan {
 // Codes of one chunk (LDS) -> bf16 tile [n][k] (LDS). lut2[b] (LDS address
 // 8 b) holds the code values of byte b's high nibble (the even element) and
 // low nibble.
-template <int BKIND>
+template <int BKIND, int TE>
 __device__ __forceinline__ void dequant(const char* __restrict__ raw, const char* __restrict__ sc,
                                         const char* __restrict__ lds0, uint16_t* __restrict__ tile) {
     const int t = threadIdx.x;
@@ -696,7 +718,7 @@ __device__ __forceinline__ void dequant(const char* __restrict__ raw, const char
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
             const f2 v = lut(((b < 4 ? w.x : w.y) >> (8 * (b & 3))) & 0xFF);
-            e[b] = f32x2_to_bf16x2(v.x * a, v.y * a);
+            e[b] = wpair<TE>(v.x * a, v.y * a);
         }
         *reinterpret_cast<uint4*>(tile + swz(r, 2 * q4)) = make_uint4(e[0], e[1], e[2], e[3]);
         *reinterpret_cast<uint4*>(tile + swz(r, 2 * q4 + 1)) = make_uint4(e[4], e[5], e[6], e[7]);
@@ -718,7 +740,7 @@ __device__ __forceinline__ void dequant(const char* __restrict__ raw, const char
 #pragma unroll
             for (int kr = 0; kr < 4; ++kr) x[kr] = ((j & 1) ? v[kr][j >> 1].y : v[kr][j >> 1].x) * a[kr];
             *reinterpret_cast<uint2*>(tile + swz(ng + j, kg >> 3) + (kg & 4)) =
-                make_uint2(f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3]));
+                make_uint2(wpair<TE>(x[0], x[1]), wpair<TE>(x[2], x[3]));
         }
     }
 }
@@ -750,7 +772,7 @@ __device__ __forceinline__ void mma(const uint16_t* __restrict__ As, const uint1
 // LoRA slab of a full tile (last split only): K2 in 64-wide chunks through
 // the 64-wide swizzled layout at As (BM_ rows) and Bs (BN_ rows), zero-filled
 // past K2. The caller has drained every DMA and barriered.
-template <int BKIND, int BM_, int BN_, int FI_, int FJ_>
+template <int BKIND, int BM_, int BN_, int TE, int FI_, int FJ_>
 __device__ __forceinline__ void slab(const GemmParams& p, uint16_t* As, uint16_t* Bs, f32x4 (&acc)[FI_][FJ_], int m0,
                                      int n0, int rm, int rn, int lane) {
     for (int k0 = 0; k0 < p.K2; k0 += 64) {
@@ -767,7 +789,7 @@ __device__ __forceinline__ void slab(const GemmParams& p, uint16_t* As, uint16_t
         }
         la.store(As);
         __syncthreads();
-        mma(As, Bs, acc, rm, rn, lane);
+        mma<FI_, FJ_, TE>(As, Bs, acc, rm, rn, lane);
         __syncthreads();
     }
 }
@@ -810,7 +832,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, const f32x4 (&acc)
 }
 }  // namespace fast
 
-template <int BKIND>
+template <int BKIND, int TE>
 __global__ __launch_bounds__(fast::NTH) void k_nf4_tile(const GemmParams p) {
     using namespace fast;
     extern __shared__ __align__(16) char lds[];
@@ -858,14 +880,14 @@ __global__ __launch_bounds__(fast::NTH) void k_nf4_tile(const GemmParams p) {
     a_dma(1, 1);
     code_dma(2, 2);
     stage_sync<2 * NA + 2 * NR>();  // codes 0 (and the table) in LDS
-    dequant<BKIND>(sr(0), ss(0), lds, sb(0));
+    dequant<BKIND, TE>(sr(0), ss(0), lds, sb(0));
     stage_sync<NA + NR>();          // A 0, codes 1, bf16 0
     auto step = [&](int c, auto stage) {
         constexpr int S0 = decltype(stage)::value, S1 = (S0 + 1) % 3, S2 = (S0 + 2) % 3;
         a_dma(c + 2, S2);
         code_dma(c + 3, S0);
-        mma(reinterpret_cast<const uint16_t*>(sa(S0)), sb(S0), acc, wm * WM, wn * WN, lane);
-        dequant<BKIND>(sr(S1), ss(S1), lds, sb(S1));
+        mma<FI, FJ, TE>(reinterpret_cast<const uint16_t*>(sa(S0)), sb(S0), acc, wm * WM, wn * WN, lane);
+        dequant<BKIND, TE>(sr(S1), ss(S1), lds, sb(S1));
         stage_sync<NA + NR>();      // A c+1, codes c+2, bf16 c+1
     };
     for (int c = 0; c < nch; c += 3) {
@@ -876,7 +898,7 @@ __global__ __launch_bounds__(fast::NTH) void k_nf4_tile(const GemmParams p) {
     stage_sync<0>();
 
     if (p.K2 > 0 && split == p.splits - 1)  // LoRA slab, any K2 (zero-filled tail)
-        slab<BKIND, BM, BN>(p, reinterpret_cast<uint16_t*>(sa(0)), sb(0), acc, m0, n0, wm * WM, wn * WN, lane);
+        slab<BKIND, BM, BN, TE>(p, reinterpret_cast<uint16_t*>(sa(0)), sb(0), acc, m0, n0, wm * WM, wn * WN, lane);
     epilogue<FI, WN>(p, acc, reinterpret_cast<float*>(lds + OFF_A) + wave * (16 * (WN + 4)), m0 + wm * WM,
                      n0 + wn * WN, split, lane);
 }
@@ -1048,7 +1070,7 @@ struct Plan {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, fast::as_lds(sc + wave * (BKIND == B_NF4_NN ? 32 : 64)), 4, scale, soff, 0, 0);
     }
 };
-template <int BKIND>
+template <int BKIND, int TE>
 __device__ __forceinline__ void dequant(const char* __restrict__ raw, const char* __restrict__ sc, const char* __restrict__ lds0,
                                         uint16_t* __restrict__ tile) {
     const int t = threadIdx.x;
@@ -1062,7 +1084,7 @@ __device__ __forceinline__ void dequant(const char* __restrict__ raw, const char
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const f2 v = lut((w >> (8 * b)) & 0xFF);
-            e[b] = f32x2_to_bf16x2(v.x * a, v.y * a);
+            e[b] = wpair<TE>(v.x * a, v.y * a);
         }
         *reinterpret_cast<uint4*>(tile + swz(r, q4)) = make_uint4(e[0], e[1], e[2], e[3]);
     } else {
@@ -1081,10 +1103,11 @@ __device__ __forceinline__ void dequant(const char* __restrict__ raw, const char
 #pragma unroll
             for (int kr = 0; kr < 4; ++kr) x[kr] = (j ? v[kr].y : v[kr].x) * a[kr];
             *reinterpret_cast<uint2*>(tile + swz(ng + j, kg >> 3) + (kg & 4)) =
-                make_uint2(f32x2_to_bf16x2(x[0], x[1]), f32x2_to_bf16x2(x[2], x[3]));
+                make_uint2(wpair<TE>(x[0], x[1]), wpair<TE>(x[2], x[3]));
         }
     }
 }
+template <int TE>
 __device__ __forceinline__ void mma(const uint16_t* __restrict__ As, const uint16_t* __restrict__ Bs, f32x4 (&acc)[FI][FJ],
                                     int rm, int rn, int lane) {
     const int lr = lane & 15, lc = lane >> 4;
@@ -1100,11 +1123,11 @@ __device__ __forceinline__ void mma(const uint16_t* __restrict__ As, const uint1
 #pragma unroll
     for (int i = 0; i < FI; ++i)
 #pragma unroll
-        for (int j = 0; j < FJ; ++j) acc[i][j] = mfma16<TE_BF16>(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < FJ; ++j) acc[i][j] = mfma16<TE>(a[i], b[j], acc[i][j]);
 }
 }  // namespace wide
 
-template <int BKIND>
+template <int BKIND, int TE>
 __global__ __launch_bounds__(wide::NTH) void k_nf4_wide(const GemmParams p) {
     using namespace wide;
     extern __shared__ __align__(16) char lds[];
@@ -1145,14 +1168,14 @@ __global__ __launch_bounds__(wide::NTH) void k_nf4_wide(const GemmParams p) {
     a_dma(1, 1);
     code_dma(2, 2);
     fast::stage_sync<2 * NA + 2 * NR>();
-    dequant<BKIND>(sr(0), ss(0), lds, sb(0));
+    dequant<BKIND, TE>(sr(0), ss(0), lds, sb(0));
     fast::stage_sync<NA + NR>();
     auto step = [&](int c, auto stage) {
         constexpr int S0 = decltype(stage)::value, S1 = (S0 + 1) % 3, S2 = (S0 + 2) % 3;
         a_dma(c + 2, S2);
         code_dma(c + 3, S0);
-        mma(reinterpret_cast<const uint16_t*>(sa(S0)), sb(S0), acc, wm * WM, wn * WN, lane);
-        dequant<BKIND>(sr(S1), ss(S1), lds, sb(S1));
+        mma<TE>(reinterpret_cast<const uint16_t*>(sa(S0)), sb(S0), acc, wm * WM, wn * WN, lane);
+        dequant<BKIND, TE>(sr(S1), ss(S1), lds, sb(S1));
         fast::stage_sync<NA + NR>();
     };
     for (int c = 0; c < nch; c += 3) {
@@ -1162,9 +1185,224 @@ __global__ __launch_bounds__(wide::NTH) void k_nf4_wide(const GemmParams p) {
     }
     fast::stage_sync<0>();
     if (p.K2 > 0 && split == p.splits - 1)  // slab tiles are 64 wide: A2 spans two A stages, B2 two B stages
-        fast::slab<BKIND, BM, BN>(p, reinterpret_cast<uint16_t*>(sa(0)), sb(0), acc, m0, n0, wm * WM, wn * WN, lane);
+        fast::slab<BKIND, BM, BN, TE>(p, reinterpret_cast<uint16_t*>(sa(0)), sb(0), acc, m0, n0, wm * WM, wn * WN, lane);
     fast::epilogue<FI, WN>(p, acc, reinterpret_cast<float*>(lds + OFF_A) + wave * (16 * (WN + 4)), m0 + wm * WM,
                            n0 + wn * WN, split, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Tall NF4 tile (M % 512 == 0, N % 64 == 0, K % 64 == 0): 512 x 64 on 8
+// wavefronts stacked along M, each owning 64 rows x all 64 columns. The
+// activation operand never passes through LDS: each wavefront loads its own
+// 64 rows straight into registers (raw buffer loads, per-lane offsets fixed
+// for the whole K loop plus a scalar offset per chunk), two chunks ahead of
+// the MFMAs that read them. LDS holds only the weight side: the packed codes
+// and block maxima of each 64-wide K chunk (DMA, three chunks ahead), the 16
+// code values (a 64-byte table, so every lookup is conflict-free: lanes that
+// read the same code share one bank word), and the dequantized bf16 tile in
+// three stages. Each dequantized weight tile serves 512 rows and every
+// wavefront reads it once per chunk, so the LDS traffic per MFMA is about
+// 40% of the 256 x 128 tile's.
+//
+// The K index of a chunk is permuted inside the MFMA (a contraction does not
+// care which k pairs with which, as long as both operands agree): lane group g
+// (lane >> 4) of K step t holds k = 16 g + 8 t + (0..7), so the two 16-byte
+// loads a lane makes per row and chunk are adjacent in memory; the weight
+// tile is read with the same map.
+namespace tall {
+constexpr int BM = 512, BN = 64, NTH = 512, NW = 8, WM = 64, WN = 64, FI = WM / 16, FJ = WN / 16;
+constexpr int SB = BN * 64 * 2;  // one bf16 weight stage: 8 KB
+constexpr int SR = BN * 32;      // packed codes of one chunk: 2 KB
+constexpr int SS = 2048;         // block maxima of one chunk: 8 x 64 floats (see CodePlan)
+constexpr int OFF_L = 0, OFF_B = 256, OFF_R = OFF_B + 3 * SB, OFF_S = OFF_R + 3 * SR;
+constexpr int LDS_MAIN = OFF_S + 3 * SS;
+// the LoRA slab reuses LDS from 0 once the main loop has drained: A2 tile
+// 512 x 64 bf16, then B2 64 x 64; the epilogue stages 8 x 16 x 68 floats
+constexpr int SLAB_B = BM * 64 * 2;
+constexpr int LDS_BYTES = (LDS_MAIN > SLAB_B + SB) ? LDS_MAIN : SLAB_B + SB;
+static_assert(LDS_BYTES <= 160 * 1024 && NW * 16 * (WN + 4) * 4 <= LDS_BYTES, "tall NF4 tile LDS");
+constexpr int NA = FI * 2;  // 16-byte activation loads per lane per chunk
+constexpr int NR = 2;       // code + block-maximum DMAs per wavefront per chunk
+
+// Activation loads: lane (r = lane & 15, g = lane >> 4) of wavefront w reads
+// row 64 w + 16 i + r, bytes [32 g, 32 g + 32) of the chunk's 128.
+struct APlan {
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t off[FI];
+    __device__ __forceinline__ void init(const uint16_t* a0, int64_t lda, int wave, int lane) {
+        rs = fast::rsrc(a0);
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+            off[i] = uint32_t((int64_t(wave * WM + i * 16 + (lane & 15)) * lda + (lane >> 4) * 16) * 2);
+    }
+    __device__ __forceinline__ void load(uint32_t soff, uint4 (&a)[FI][2]) const {
+#pragma unroll
+        for (int i = 0; i < FI; ++i) {
+            a[i][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], soff, 0));
+            a[i][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off[i] + 16, soff, 0));
+        }
+    }
+};
+
+// Codes and block maxima of one chunk, DMA'd into LDS, where a row is an
+// output column n (NT) or a K row (NN): in both layouts a chunk is 64 rows of
+// 32 code bytes and one block maximum per row. Wavefront w moves rows
+// [8 w, 8 w + 8) with two 4-byte DMAs over all 64 lanes (no lane masked off,
+// so the compiler's count of loads in flight stays exact): the codes as
+// [row][32 bytes]; the maxima as 64 floats per wavefront, lane l holding row
+// 8 w + (l & 7) (eight copies of each).
+struct CodePlan {
+    __amdgpu_buffer_rsrc_t rc, rs;
+    uint32_t code, scale;
+    int wave;
+    __device__ __forceinline__ void init(const void* c0, const void* s0, int64_t cols, int lane) {
+        wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        rc = fast::rsrc(c0);
+        rs = fast::rsrc(s0);
+        code = uint32_t(int64_t(wave * 8 + (lane >> 3)) * (cols >> 1) + (lane & 7) * 4);
+        scale = uint32_t(int64_t(wave * 8 + (lane & 7)) * (cols >> 6) * 4);
+    }
+    __device__ __forceinline__ void dma(uint32_t coff, uint32_t soff, char* __restrict__ raw,
+                                        char* __restrict__ sc) const {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, fast::as_lds(raw + wave * 256), 4, code, coff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, fast::as_lds(sc + wave * 256), 4, scale, soff, 0, 0);
+    }
+};
+// block maximum of row r (0..63) in a chunk's maxima stage
+__device__ __forceinline__ float row_max(const float* s, int r) { return s[(r >> 3) * 64 + (r & 7)]; }
+
+// Codes of one chunk (LDS) -> bf16 tile [64 n][64 k] (LDS, fast::swz layout):
+// each thread produces one 16-byte chunk of one row, 8 consecutive k.
+template <int BKIND, int TE>
+__device__ __forceinline__ void dequant(const char* __restrict__ raw, const char* __restrict__ sc,
+                                        const float* __restrict__ lut, uint16_t* __restrict__ tile) {
+    const int t = threadIdx.x;
+    const float* s = reinterpret_cast<const float*>(sc);
+    uint32_t e[4];
+    if constexpr (BKIND == B_NF4_NT) {
+        // row n = t >> 3, k = 8 (t & 7) + (0..7): four code bytes, one block maximum
+        const int n = t >> 3, q = t & 7;
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(raw + n * 32 + q * 4);
+        const float a = row_max(s, n);
+#pragma unroll
+        for (int b = 0; b < 4; ++b)  // byte b: high nibble = even element
+            e[b] = wpair<TE>(lut[(w >> (8 * b + 4)) & 15] * a, lut[(w >> (8 * b)) & 15] * a);
+        *reinterpret_cast<uint4*>(tile + fast::swz(n, q)) = make_uint4(e[0], e[1], e[2], e[3]);
+    } else {
+        // column n = t & 63 of K rows 8 kc .. 8 kc + 7 (kc = t >> 6): one nibble
+        // of each row's byte n / 2, each row with its own block maximum
+        const int n = t & 63, kc = t >> 6, sh = (n & 1) ? 0 : 4;
+        float v[8];
+#pragma unroll
+        for (int kr = 0; kr < 8; ++kr) {
+            const uint32_t byte = *reinterpret_cast<const uint8_t*>(raw + (kc * 8 + kr) * 32 + (n >> 1));
+            v[kr] = lut[(byte >> sh) & 15] * row_max(s, kc * 8 + kr);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) e[b] = wpair<TE>(v[2 * b], v[2 * b + 1]);
+        *reinterpret_cast<uint4*>(tile + fast::swz(n, kc)) = make_uint4(e[0], e[1], e[2], e[3]);
+    }
+}
+
+// One chunk of MFMAs: activation fragments from registers, weight fragments
+// from the bf16 tile (row 16 j + (lane & 15), 16-byte chunk 2 g + t).
+template <int TE>
+__device__ __forceinline__ void mma(const uint4 (&a)[FI][2], const uint16_t* __restrict__ Bs, f32x4 (&acc)[FI][FJ],
+                                    int lane) {
+    const int lr = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        uint4 b[FJ];
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) b[j] = *reinterpret_cast<const uint4*>(Bs + fast::swz(j * 16 + lr, 2 * g + t));
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+#pragma unroll
+            for (int j = 0; j < FJ; ++j) acc[i][j] = mfma16<TE>(a[i][t], b[j], acc[i][j]);
+    }
+}
+}  // namespace tall
+
+template <int BKIND, int TE>
+__global__ __launch_bounds__(tall::NTH) void k_nf4_tall(const GemmParams p) {
+    using namespace tall;
+    extern __shared__ __align__(16) char lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float* lut = reinterpret_cast<float*>(lds + OFF_L);
+    if (tid < 16) lut[tid] = nf4_value(tid);
+
+    const int gx = p.N / BN, gy = p.M / BM;
+    const int ntile = gx * gy;
+    int t = blockIdx.x;
+    if (ntile % 8 == 0) t = (t % 8) * (ntile / 8) + t / 8;
+    const int m0 = (t / gx) * BM, n0 = (t % gx) * BN;  // the gx N-tiles of one M-tile together
+    const int split = blockIdx.y;
+    const int kbeg = split * p.kchunk, kend = min(p.K, kbeg + p.kchunk);
+    const int nch = (kend - kbeg) / 64;  // >= 1
+    const int64_t cols = p.nf4_cols;
+    const int64_t flat0 = (BKIND == B_NF4_NN) ? int64_t(kbeg) * cols + n0 : int64_t(n0) * cols + kbeg;
+
+    APlan ap;
+    ap.init(p.A + int64_t(m0) * p.lda + kbeg, p.lda, wave, lane);
+    CodePlan cp;
+    cp.init(static_cast<const char*>(p.B) + (flat0 >> 1), p.absmax + (flat0 >> 6), cols, lane);
+    // per chunk: codes 32 bytes on (NT) or 64 rows down (NN); maxima one
+    // entry on (NT) or 64 rows down (NN); activations 128 bytes on
+    const uint32_t cstep = (BKIND == B_NF4_NN) ? uint32_t(32 * cols) : 32u;
+    const uint32_t sstep = (BKIND == B_NF4_NN) ? uint32_t(4 * cols) : 4u;
+
+    f32x4 acc[FI][FJ];
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // chunk c: activations in register set c % 3, codes and bf16 weights in
+    // LDS stage c % 3; loads past the end re-read the last chunk into a set
+    // or stage nobody reads again, so every step issues the same NA + NR
+    // vector-memory instructions. The loop body is three whole steps (the
+    // register sets rotate with period 3) and the last nch % 3 steps follow
+    // it, so the register allocation of the loop is the same on every path.
+    auto cl = [&](int c) { return uint32_t(min(c, nch - 1)); };
+    auto sb = [&](int s) { return reinterpret_cast<uint16_t*>(lds + OFF_B + s * SB); };
+    auto sr = [&](int s) { return lds + OFF_R + s * SR; };
+    auto ss = [&](int s) { return lds + OFF_S + s * SS; };
+    auto code_dma = [&](int c, int s) { cp.dma(cl(c) * cstep, cl(c) * sstep, sr(s), ss(s)); };
+    uint4 ar[3][FI][2];
+    code_dma(0, 0);
+    code_dma(1, 1);
+    ap.load(cl(0) * 128u, ar[0]);
+    code_dma(2, 2);
+    ap.load(cl(1) * 128u, ar[1]);
+    fast::stage_sync<NA + NR + NA>();  // codes 0 and 1 (and the table) in LDS
+    dequant<BKIND, TE>(sr(0), ss(0), lut, sb(0));
+    fast::stage_sync<NA + NR + NA>();  // bf16 stage 0 complete
+    auto step = [&](int c, auto r3) {
+        constexpr int S0 = decltype(r3)::value, S1 = (S0 + 1) % 3, S2 = (S0 + 2) % 3;
+        ap.load(cl(c + 2) * 128u, ar[S2]);
+        code_dma(c + 3, S0);  // code stage c % 3 was dequantized last step
+        tall::mma<TE>(ar[S0], sb(S0), acc, lane);
+        dequant<BKIND, TE>(sr(S1), ss(S1), lut, sb(S1));
+        fast::stage_sync<NA + NR>();  // codes c + 2 and activations c + 1 landed; bf16 c + 1 complete
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    const int nfull = nch - nch % 3;
+    for (int c = 0; c < nfull; c += 3) {
+        step(c, I0());
+        step(c + 1, I1());
+        step(c + 2, I2());
+    }
+    if (nfull < nch) step(nfull, I0());
+    if (nfull + 1 < nch) step(nfull + 1, I1());
+    fast::stage_sync<0>();
+
+    if (p.K2 > 0 && split == p.splits - 1)  // LoRA slab, any K2 (zero-filled tail)
+        fast::slab<BKIND, BM, BN, TE>(p, reinterpret_cast<uint16_t*>(lds), reinterpret_cast<uint16_t*>(lds + SLAB_B), acc,
+                                  m0, n0, wave * WM, 0, lane);
+    fast::epilogue<FI, WN>(p, acc, reinterpret_cast<float*>(lds) + wave * (16 * (WN + 4)), m0 + wave * WM, n0, split,
+                           lane);
 }
 
 // Sums the split-K partials in split order (fixed, so results do not depend
@@ -1246,18 +1484,25 @@ static void allow_lds(std::atomic<bool> (&allowed)[64], const void* fn, int byte
         allowed[dev].store(true, std::memory_order_release);
     }
 }
-template <int BKIND>
+template <int BKIND, int TE>
 static void launch_fast(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {
     static std::atomic<bool> allowed[64];
-    allow_lds(allowed, reinterpret_cast<const void*>(&k_nf4_tile<BKIND>), fast::LDS_BYTES);
-    hipExtLaunchKernelGGL(k_nf4_tile<BKIND>, dim3(tiles, p.splits), dim3(fast::NTH), fast::LDS_BYTES, s, prof.start(),
+    allow_lds(allowed, reinterpret_cast<const void*>(&k_nf4_tile<BKIND, TE>), fast::LDS_BYTES);
+    hipExtLaunchKernelGGL(k_nf4_tile<BKIND, TE>, dim3(tiles, p.splits), dim3(fast::NTH), fast::LDS_BYTES, s, prof.start(),
                           prof.stop(), 0, p);
 }
-template <int BKIND>
+template <int BKIND, int TE>
 static void launch_wide(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {
     static std::atomic<bool> allowed[64];
-    allow_lds(allowed, reinterpret_cast<const void*>(&k_nf4_wide<BKIND>), wide::LDS_BYTES);
-    hipExtLaunchKernelGGL(k_nf4_wide<BKIND>, dim3(tiles, p.splits), dim3(wide::NTH), wide::LDS_BYTES, s, prof.start(),
+    allow_lds(allowed, reinterpret_cast<const void*>(&k_nf4_wide<BKIND, TE>), wide::LDS_BYTES);
+    hipExtLaunchKernelGGL(k_nf4_wide<BKIND, TE>, dim3(tiles, p.splits), dim3(wide::NTH), wide::LDS_BYTES, s, prof.start(),
+                          prof.stop(), 0, p);
+}
+template <int BKIND, int TE>
+static void launch_tall(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {
+    static std::atomic<bool> allowed[64];
+    allow_lds(allowed, reinterpret_cast<const void*>(&k_nf4_tall<BKIND, TE>), tall::LDS_BYTES);
+    hipExtLaunchKernelGGL(k_nf4_tall<BKIND, TE>, dim3(tiles, p.splits), dim3(tall::NTH), tall::LDS_BYTES, s, prof.start(),
                           prof.stop(), 0, p);
 }
 static void launch_dense(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {
@@ -1268,11 +1513,63 @@ static void launch_dense(const GemmParams& p, int tiles, hipStream_t s, const Pr
 }
 static bool aligned8(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 7) == 0; }
 
+// Relative cost of one 64-wide chunk of the 512 x 64 NF4 tile against one of
+// the 256 x 128 tile (same work per chunk): measured 1.4-1.8x on the 8B-shaped
+// projections (its activation loads, one 16-byte fragment per lane straight
+// from memory, move twice the bytes per MFMA through the vector memory path
+// of the LDS-staged tiles), so the cost model never picks it.
+constexpr double kTallUnit = 1.6;
+// QLX_NF4_TILE = 256x128 | 512x128 | 512x64 pins the full-tile NF4 shape
+// wherever it applies (for measurements); unset: chosen by the cost model.
+static int nf4_shape_override() {
+    const char* e = std::getenv("QLX_NF4_TILE");
+    if (!e) return -1;
+    const std::string v(e);
+    return v == "256x128" ? 0 : v == "512x128" ? 1 : v == "512x64" ? 2 : -1;
+}
+
+// Kernel choice for one element type (every operand combination the step uses).
+template <int TE>
+static void dispatch(const GemmParams& p, int akind, int bkind, bool fast_ok, bool dense_fast, int shape, TileCfg tc,
+                     int tiles, int bsz, hipStream_t s, const ProfScope& prof) {
+    switch (akind * 10 + bkind) {
+        case A_ROW * 10 + B_NF4_NT:
+            if (fast_ok)
+                shape == 2 ? launch_tall<B_NF4_NT, TE>(p, tiles, s, prof)
+                : shape == 1 ? launch_wide<B_NF4_NT, TE>(p, tiles, s, prof)
+                             : launch_fast<B_NF4_NT, TE>(p, tiles, s, prof);
+            else
+                launch_kind<A_ROW, B_NF4_NT, TE>(p, tc, bsz, s);
+            break;
+        case A_ROW * 10 + B_NF4_NN:
+            if (fast_ok)
+                shape == 2 ? launch_tall<B_NF4_NN, TE>(p, tiles, s, prof)
+                : shape == 1 ? launch_wide<B_NF4_NN, TE>(p, tiles, s, prof)
+                             : launch_fast<B_NF4_NN, TE>(p, tiles, s, prof);
+            else
+                launch_kind<A_ROW, B_NF4_NN, TE>(p, tc, bsz, s);
+            break;
+        case A_ROW * 10 + B_DENSE_NT:
+            if (dense_fast && TE == TE_F16) launch_dense(p, tiles, s, prof);
+            else if (tc.bm == 64) launch_cfg<A_ROW, B_DENSE_NT, TE, 64, 64, 32, 32>(p, bsz, s);
+            else launch_cfg<A_ROW, B_DENSE_NT, TE, 128, 128, 64, 64>(p, bsz, s);
+            break;
+        case A_ROW * 10 + B_DENSE_NN:
+            if (tc.bm == 64) launch_cfg<A_ROW, B_DENSE_NN, TE, 64, 64, 32, 32>(p, bsz, s);
+            else launch_cfg<A_ROW, B_DENSE_NN, TE, 128, 128, 64, 64>(p, bsz, s);
+            break;
+        case A_TRANS * 10 + B_DENSE_NN:
+            if (tc.bm == 64) launch_cfg<A_TRANS, B_DENSE_NN, TE, 64, 64, 32, 32>(p, bsz, s);
+            else launch_cfg<A_TRANS, B_DENSE_NN, TE, 128, 128, 64, 64>(p, bsz, s);
+            break;
+        default: throw Error{QLX_EUNSUPPORTED, "gemm: operand combination not built"};
+    }
+}
+
 void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStream_t s) {
     if (p.M <= 0 || p.N <= 0) return;
     const bool nf4 = (bkind == B_NF4_NT || bkind == B_NF4_NN);
     QLX_REQUIRE(!(p.K2 > 0 && !nf4), QLX_EINVAL, "gemm: the LoRA slab rides only on NF4 GEMMs");
-    QLX_REQUIRE(!(te == TE_F16 && nf4), QLX_EINVAL, "gemm: NF4 operands are bf16");
     QLX_REQUIRE(!p.ce_mode || (te == TE_F16 && akind == A_ROW && bkind == B_DENSE_NT && p.batch == 1 &&
                                p.causal == CAUSAL_NONE && p.ce_seq > 0),
                 QLX_EINVAL, "gemm: the cross-entropy epilogues take a plain fp16 NT product");
@@ -1297,7 +1594,7 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
         p.a2_vec = aligned16(p.A2) && p.lda2 % 8 == 0;
         p.b2_vec = (bkind == B_NF4_NT) ? (aligned16(p.B2) && p.ldb2 % 8 == 0) : (aligned8(p.B2) && p.ldb2 % 4 == 0);
     }
-    const bool fast_ok = nf4 && te == TE_BF16 && akind == A_ROW && p.batch == 1 && p.causal == CAUSAL_NONE &&
+    const bool fast_ok = nf4 && akind == A_ROW && p.batch == 1 && p.causal == CAUSAL_NONE &&
                          p.M % fast::BM == 0 && p.N % fast::BN == 0 && p.K % 64 == 0 && p.K >= 64 && p.a_vec &&
                          p.b_vec && aligned16(p.absmax) && p.nf4_cols % 64 == 0 &&
                          int64_t(p.M) * p.lda * 2 < (int64_t(1) << 31) &&
@@ -1305,7 +1602,7 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
     // Skinny dense products (the LoRA terms: one side is r, 2r or 3r) are
     // bound by reading the long operand; 64 x 64 tiles with a K split keep
     // many workgroups streaming it without a large partial buffer.
-    const bool skinny = !nf4 && te == TE_BF16 && p.batch == 1 && p.causal == CAUSAL_NONE && std::min(p.M, p.N) <= 256;
+    const bool skinny = !nf4 && !p.ce_mode && p.batch == 1 && p.causal == CAUSAL_NONE && std::min(p.M, p.N) <= 256;
     // the LM head's fp16 NT products with a cross-entropy epilogue (never split)
     const bool dense_fast = p.ce_mode && te == TE_F16 && akind == A_ROW && bkind == B_DENSE_NT && p.batch == 1 &&
                             p.M % dense::BM == 0 && p.N % dense::BN == 0 && p.K % 64 == 0 && p.K >= 64 && p.a_vec &&
@@ -1320,6 +1617,7 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
     p.splits = 1;
     p.kchunk = ((p.K + BK - 1) / BK) * BK;
     int tiles = gx * gy;
+    int shape = 0;  // full-tile NF4 kernels: 0 = 256 x 128, 1 = 512 x 128 (wide), 2 = 512 x 64 (tall)
     bool wide_tile = false;
     if (fast_ok) {
         // One workgroup fits a CU, so the grid runs in rounds of 256. Pick the
@@ -1334,18 +1632,21 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
         const double mn = double(p.M) * p.N;
         double best = 1e300;
         int best_s = 1;
-        for (int wide = 0; wide < 2; ++wide) {
-            if (wide && p.M % wide::BM != 0) continue;
-            const int bm = wide ? wide::BM : fast::BM;
-            const int t = (p.M / bm) * (p.N / fast::BN);
-            const double unit = wide ? 1.85 * 1.03 : 1.0;
+        // tile shape: 0 = 256 x 128, 1 = 512 x 128, 2 = 512 x 64 (each chunk
+        // of the 512 x 128 shape is two 256 x 128 chunks of work)
+        const int forced = nf4_shape_override();
+        for (int sh = 0; sh < 3; ++sh) {
+            if (sh > 0 && p.M % 512 != 0) continue;
+            if (forced >= 0 && sh != forced && !(forced > 0 && p.M % 512 != 0 && sh == 0)) continue;
+            const int t = (p.M / (sh ? 512 : 256)) * (p.N / (sh == 2 ? 64 : 128));
+            const double unit = sh == 1 ? 1.85 * 1.03 : sh == 2 ? kTallUnit : 1.0;
             for (int sp = 1; sp <= 16 && nch / sp >= 4; ++sp) {
-                if (sp > 1 && (!partial_ws || size_t(sp) * p.M * p.N > kGemmPartialFloats)) break;
+                if (sp > 1 && (!partial_ws || size_t(sp) * p.M * p.N > p.partial_cap)) break;
                 const int per = (nch + sp - 1) / sp;
                 const double rounds = double((t * sp + 255) / 256);
                 double cost = rounds * (per + 3.0) * unit;
                 if (sp > 1) cost += mn * 4.0 * (sp + 1) / 4e12 / 1.35e-6 + 2.0;
-                if (cost < best - 1e-9) best = cost, best_s = sp, wide_tile = wide;
+                if (cost < best - 1e-9) best = cost, best_s = sp, shape = sh;
             }
         }
         if (best_s > 1) {
@@ -1354,7 +1655,9 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
             p.splits = (p.K + kc - 1) / kc;
             p.partial = partial_ws;
         }
-        if (wide_tile) tiles = (p.M / wide::BM) * (p.N / fast::BN);
+        wide_tile = shape == 1;
+        if (shape == 1) tiles = (p.M / wide::BM) * (p.N / fast::BN);
+        if (shape == 2) tiles = (p.M / tall::BM) * (p.N / tall::BN);
         } else if (skinny) {
         // measured on the 8B-shaped LoRA products: at least 512 workgroups
         // (four fit a CU), at most 2048 of K per split, at least 256
@@ -1363,7 +1666,7 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
             while (sp < 16 && tiles * sp < 512) sp *= 2;
             while (sp < 16 && p.K / sp > 2048) sp *= 2;
             sp = std::min(sp, std::max(1, p.K / 256));
-            while (sp > 1 && size_t(sp) * tiles * tc.bm * tc.bn > kGemmPartialFloats) sp /= 2;
+            while (sp > 1 && size_t(sp) * tiles * tc.bm * tc.bn > p.partial_cap) sp /= 2;
             if (sp > 1) {
                 const int kc = (((p.K + sp - 1) / sp) + BK - 1) / BK * BK;
                 p.kchunk = kc;
@@ -1376,7 +1679,7 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
         int want = ((nf4 ? 256 : 512) + tiles - 1) / tiles;
         want = std::min(want, p.K / 128);
         want = std::min(want, 16);
-        while (want > 1 && size_t(want) * tiles * tc.bm * tc.bn > kGemmPartialFloats) --want;
+        while (want > 1 && size_t(want) * tiles * tc.bm * tc.bn > p.partial_cap) --want;
         if (want > 1) {
             const int kc = (((p.K + want - 1) / want) + BK - 1) / BK * BK;
             p.kchunk = kc;
@@ -1394,53 +1697,24 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
     else pairs_k = M * N * K;
     const double k2 = p.K2 > 0 ? (p.slab_alg_k >= 0 ? p.slab_alg_k : p.K2) : 0;
     const double flops = 2.0 * p.batch * (pairs_k + M * N * k2);
-    const double belt = (te == TE_F16 || !nf4) ? 2.0 : 0.5 + 4.0 / 64.0;
+    const double belt = !nf4 ? 2.0 : 0.5 + 4.0 / 64.0;
     const double cb = p.c_type == C_F32 ? 4.0 : 2.0;
     const double bytes = p.batch * (M * K * 2 + N * K * belt + M * N * cb * (p.accumulate ? 2 : 1) +
                                     (p.R ? M * N * 4 : 0) + (p.K2 ? (M + N) * p.K2 * 2.0 : 0));
     static const char* kNames[] = {"gemm_nf4_nt", "gemm_nf4_nn", "gemm_bf16_nt", "gemm_bf16_nn",
                                    "gemm_bf16_tn", "gemm_f16_nt", "gemm_f16_nn", "gemm_other"};
     static const char* kWideNames[] = {"gemm_nf4_nt_wide", "gemm_nf4_nn_wide"};
-    const int ni = key == 0 ? 0 : key == 10 ? 1 : key == 20 ? 2 : key == 30 ? 3 : key == 130 ? 4
+    static const char* kTallNames[] = {"gemm_nf4_nt_tall", "gemm_nf4_nn_tall"};
+    const int ab = akind * 10 + bkind;  // the NF4 rows keep their names under either activation type
+    const int ni = ab == 0 ? 0 : ab == 1 ? 1 : key == 20 ? 2 : key == 30 ? 3 : key == 130 ? 4
                  : key == 21 ? 5 : key == 31 ? 6 : 7;
     const int bsz = p.batch * p.splits;
     {
-        ProfScope prof(p.tag ? p.tag : (wide_tile ? kWideNames[ni] : kNames[ni]), flops, bytes, s,
+        ProfScope prof(p.tag ? p.tag : (shape == 2 && fast_ok && ni < 2) ? kTallNames[ni]
+                                     : (wide_tile ? kWideNames[ni] : kNames[ni]), flops, bytes, s,
                        fast_ok || dense_fast);
-        switch (key) {
-            case A_ROW * 100 + B_NF4_NT * 10 + TE_BF16:
-                if (fast_ok)
-                    wide_tile ? launch_wide<B_NF4_NT>(p, tiles, s, prof) : launch_fast<B_NF4_NT>(p, tiles, s, prof);
-                else
-                    launch_kind<A_ROW, B_NF4_NT, TE_BF16>(p, tc, bsz, s);
-                break;
-            case A_ROW * 100 + B_NF4_NN * 10 + TE_BF16:
-                if (fast_ok)
-                    wide_tile ? launch_wide<B_NF4_NN>(p, tiles, s, prof) : launch_fast<B_NF4_NN>(p, tiles, s, prof);
-                else
-                    launch_kind<A_ROW, B_NF4_NN, TE_BF16>(p, tc, bsz, s);
-                break;
-            case A_ROW * 100 + B_DENSE_NT * 10 + TE_BF16:
-                if (tc.bm == 64) launch_cfg<A_ROW, B_DENSE_NT, TE_BF16, 64, 64, 32, 32>(p, bsz, s);
-                else launch_cfg<A_ROW, B_DENSE_NT, TE_BF16, 128, 128, 64, 64>(p, bsz, s);
-                break;
-            case A_ROW * 100 + B_DENSE_NN * 10 + TE_BF16:
-                if (tc.bm == 64) launch_cfg<A_ROW, B_DENSE_NN, TE_BF16, 64, 64, 32, 32>(p, bsz, s);
-                else launch_cfg<A_ROW, B_DENSE_NN, TE_BF16, 128, 128, 64, 64>(p, bsz, s);
-                break;
-            case A_TRANS * 100 + B_DENSE_NN * 10 + TE_BF16:
-                if (tc.bm == 64) launch_cfg<A_TRANS, B_DENSE_NN, TE_BF16, 64, 64, 32, 32>(p, bsz, s);
-                else launch_cfg<A_TRANS, B_DENSE_NN, TE_BF16, 128, 128, 64, 64>(p, bsz, s);
-                break;
-            case A_ROW * 100 + B_DENSE_NT * 10 + TE_F16:
-                if (dense_fast) launch_dense(p, tiles, s, prof);
-                else launch_cfg<A_ROW, B_DENSE_NT, TE_F16, 128, 128, 64, 64>(p, bsz, s);
-                break;
-            case A_ROW * 100 + B_DENSE_NN * 10 + TE_F16:
-                launch_cfg<A_ROW, B_DENSE_NN, TE_F16, 128, 128, 64, 64>(p, bsz, s);
-                break;
-            default: throw Error{QLX_EUNSUPPORTED, "gemm: operand combination not built"};
-        }
+        if (te == TE_BF16) dispatch<TE_BF16>(p, akind, bkind, fast_ok, dense_fast, shape, tc, tiles, bsz, s, prof);
+        else dispatch<TE_F16>(p, akind, bkind, fast_ok, dense_fast, shape, tc, tiles, bsz, s, prof);
         check_launch("gemm");
     }
     if (p.splits > 1) {

@@ -11,6 +11,12 @@ struct LayerGeom {
     int qdim, kvdim, nqkv;
     int out[7], in[7];
     int64_t nel[7];
+    // 16-bit activation type: f16 = 1 for fp16 (MFMA TE_F16, stores C_F16),
+    // else bf16; te / ct are the GEMM element and output codes
+    int f16 = 0, te = TE_BF16, ct = C_BF16;
+    // gradient scale: the backward's 16-bit gradients hold gsc x the true
+    // values (a power of two; 1 with bf16), fp32 outputs come out unscaled
+    float gsc = 1.f;
     bool hidden_ok() const { return H % 4 == 0 && qdim % 4 == 0 && I % 4 == 0 && kvdim % 4 == 0; }
 };
 

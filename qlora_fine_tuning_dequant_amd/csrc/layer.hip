@@ -46,6 +46,9 @@ LayerGeom make_geom(const qlx_dims& d, int batch, int seq) {
         g.in[p] = ins[p];
         g.nel[p] = int64_t(outs[p]) * ins[p];
     }
+    g.f16 = d.act_dtype == QLX_ACT_F16 ? 1 : 0;
+    g.te = g.f16 ? TE_F16 : TE_BF16;
+    g.ct = g.f16 ? C_F16 : C_BF16;
     return g;
 }
 
@@ -56,6 +59,8 @@ void validate_dims(const qlx_dims* d) {
                 QLX_EINVAL, "dims: every size must be positive");
     QLX_REQUIRE(d->n_heads % d->n_kv_heads == 0, QLX_EINVAL, "dims: n_heads must be a multiple of n_kv_heads");
     QLX_REQUIRE(d->head_dim % 2 == 0, QLX_EINVAL, "dims: head_dim must be even (rotate-half RoPE)");
+    QLX_REQUIRE(d->act_dtype == QLX_ACT_BF16 || d->act_dtype == QLX_ACT_F16, QLX_EINVAL,
+                "dims: act_dtype must be QLX_ACT_BF16 or QLX_ACT_F16");
     QLX_REQUIRE(d->lora_alpha == d->lora_alpha && d->rms_eps > 0 && d->rope_theta > 0, QLX_EINVAL,
                 "dims: lora_alpha, rms_eps, rope_theta must be finite and positive");
     const LayerGeom g = make_geom(*d, 1, 1);
@@ -215,10 +220,10 @@ static GemmParams dense_gemm(int M, int N, int K, const uint16_t* A, int64_t lda
     p.ldb = ldb;
     return p;
 }
-static void out_bf16(GemmParams& p, uint16_t* C, int64_t ldc) {
+static void out16(GemmParams& p, uint16_t* C, int64_t ldc, const LayerGeom& g) {
     p.C = C;
     p.ldc = ldc;
-    p.c_type = C_BF16;
+    p.c_type = g.ct;
 }
 static void out_f32(GemmParams& p, float* C, int64_t ldc) {
     p.C = C;
@@ -249,6 +254,7 @@ static AttnArgs attn_args(const LayerGeom& g, LayerWs& w) {
     a.dqkv = w.dqkv;
     a.lddq = g.nqkv;
     a.rope = reinterpret_cast<const float2*>(w.rope_cs);
+    a.f16 = g.f16;
     return a;
 }
 
@@ -262,7 +268,7 @@ void stage_lora(const LayerGeom& g, const qlx_lora* lora, LayerWs& w, hipStream_
     LoraSeg dn[1] = {{lora->A[6], lora->B[6], g.H}};
     const LoraPackJob jobs[4] = {{qkv, 3, g.H, w.A_qkv, w.B_qkv}, {o, 1, g.qdim, w.A_o, w.B_o},
                                  {gu, 2, g.H, w.A_gu, w.B_gu}, {dn, 1, g.I, w.A_d, w.B_d}};
-    launch_lora_pack_jobs(jobs, 4, r, g.s, s);
+    launch_lora_pack_jobs(jobs, 4, r, g.s, g.f16, s);
 }
 
 // Forward. h_out == nullptr skips the down projection (the backward does not
@@ -279,12 +285,12 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
     }
 
     // attention block
-    launch_rmsnorm_fwd(h_in, wt.g1, T, H, g.eps, w.n1, 0, w.rstd1, s);
+    launch_rmsnorm_fwd(h_in, wt.g1, T, H, g.eps, w.n1, g.f16, w.rstd1, s);
     if (U) {
         GemmParams pu = dense_gemm(T, 3 * r, H, w.n1, H, w.A_qkv, H);
-        out_bf16(pu, w.u_qkv, 3 * r);
+        out16(pu, w.u_qkv, 3 * r, g);
         pu.tag = "gemm_lora_u";
-        gemm(pu, A_ROW, B_DENSE_NT, TE_BF16, w.partial, s);
+        gemm(pu, A_ROW, B_DENSE_NT, g.te, w.partial, s);
     }
     {
         GemmParams p = nf4_gemm(T, g.nqkv, H, w.n1, H, wt.packed[0], wt.absmax[0], H);
@@ -296,16 +302,16 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
             p.ldb2 = 3 * r;
             p.slab_alg_k = r;  // block-diagonal: each output column sees one adapter
         }
-        out_bf16(p, w.qkv, g.nqkv);
-        gemm(p, A_ROW, B_NF4_NT, TE_BF16, w.partial, s);
+        out16(p, w.qkv, g.nqkv, g);
+        gemm(p, A_ROW, B_NF4_NT, g.te, w.partial, s);
     }
-    launch_rope(w.qkv, g.nqkv, T, g.S, 0, g.nH + g.nKV, g.hd, w.rope_cs, s);  // q and k heads are contiguous
+    launch_rope(w.qkv, g.nqkv, T, g.S, 0, g.nH + g.nKV, g.hd, w.rope_cs, g.f16, s);  // q and k heads are contiguous
     launch_flash_fwd(attn_args(g, w), s);
     if (U) {
         GemmParams pu = dense_gemm(T, r, g.qdim, w.oattn, g.qdim, w.A_o, g.qdim);
-        out_bf16(pu, w.u_o, r);
+        out16(pu, w.u_o, r, g);
         pu.tag = "gemm_lora_u";
-        gemm(pu, A_ROW, B_DENSE_NT, TE_BF16, w.partial, s);
+        gemm(pu, A_ROW, B_DENSE_NT, g.te, w.partial, s);
     }
     {  // h1 = h_in + o_proj(o)
         GemmParams p = nf4_gemm(T, H, g.qdim, w.oattn, g.qdim, wt.packed[3], wt.absmax[3], g.qdim);
@@ -319,15 +325,15 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
         out_f32(p, w.h1, H);
         p.R = h_in;
         p.ldr = H;
-        gemm(p, A_ROW, B_NF4_NT, TE_BF16, w.partial, s);
+        gemm(p, A_ROW, B_NF4_NT, g.te, w.partial, s);
     }
     // MLP block
-    launch_rmsnorm_fwd(w.h1, wt.g2, T, H, g.eps, w.n2, 0, w.rstd2, s);
+    launch_rmsnorm_fwd(w.h1, wt.g2, T, H, g.eps, w.n2, g.f16, w.rstd2, s);
     if (U) {
         GemmParams pu = dense_gemm(T, 2 * r, H, w.n2, H, w.A_gu, H);
-        out_bf16(pu, w.u_gu, 2 * r);
+        out16(pu, w.u_gu, 2 * r, g);
         pu.tag = "gemm_lora_u";
-        gemm(pu, A_ROW, B_DENSE_NT, TE_BF16, w.partial, s);
+        gemm(pu, A_ROW, B_DENSE_NT, g.te, w.partial, s);
     }
     {
         GemmParams p = nf4_gemm(T, 2 * g.I, H, w.n2, H, wt.packed[4], wt.absmax[4], H);
@@ -339,15 +345,15 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
             p.ldb2 = 2 * r;
             p.slab_alg_k = r;
         }
-        out_bf16(p, w.gu, 2 * g.I);
-        gemm(p, A_ROW, B_NF4_NT, TE_BF16, w.partial, s);
+        out16(p, w.gu, 2 * g.I, g);
+        gemm(p, A_ROW, B_NF4_NT, g.te, w.partial, s);
     }
-    launch_swiglu_fwd(w.gu, T, g.I, w.act, s);
+    launch_swiglu_fwd(w.gu, T, g.I, w.act, g.f16, s);
     if (U) {
         GemmParams pu = dense_gemm(T, r, g.I, w.act, g.I, w.A_d, g.I);
-        out_bf16(pu, w.u_d, r);
+        out16(pu, w.u_d, r, g);
         pu.tag = "gemm_lora_u";
-        gemm(pu, A_ROW, B_DENSE_NT, TE_BF16, w.partial, s);
+        gemm(pu, A_ROW, B_DENSE_NT, g.te, w.partial, s);
     }
     if (h_out) {
         GemmParams p = nf4_gemm(T, H, g.I, w.act, g.I, wt.packed[6], wt.absmax[6], g.I);
@@ -361,7 +367,7 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
         out_f32(p, h_out, H);
         p.R = w.h1;
         p.ldr = H;
-        gemm(p, A_ROW, B_NF4_NT, TE_BF16, w.partial, s);
+        gemm(p, A_ROW, B_NF4_NT, g.te, w.partial, s);
     }
 }
 
@@ -370,9 +376,9 @@ static void grad_B(const LayerGeom& g, const uint16_t* dy, int64_t ld_dy, int ou
                    float* dB, LayerWs& w, hipStream_t s) {
     GemmParams p = dense_gemm(out, g.r, g.T, dy, ld_dy, u, ld_u);
     out_f32(p, dB, g.r);
-    p.alpha = g.s;
+    p.alpha = g.s / g.gsc;  // dy holds gsc x the gradient
     p.tag = "gemm_lora_dB";
-    gemm(p, A_TRANS, B_DENSE_NN, TE_BF16, w.partial, s);
+    gemm(p, A_TRANS, B_DENSE_NN, g.te, w.partial, s);
 }
 // dB of projections whose outputs are consecutive column blocks of dy, cut
 // into nseg segments of seg rows, in one product: segment i reads the r
@@ -391,9 +397,9 @@ static void grad_B_group(const LayerGeom& g, const uint16_t* dy, int64_t ld_dy, 
             p.Cseg[i] = dB[i];
             p.bseg[i] = ucol[i];
         }
-        p.alpha = g.s;
+        p.alpha = g.s / g.gsc;
         p.tag = "gemm_lora_dB";
-        gemm(p, A_TRANS, B_DENSE_NN, TE_BF16, w.partial, s);
+        gemm(p, A_TRANS, B_DENSE_NN, g.te, w.partial, s);
         return;
     }
     for (int i = 0; i < nseg;) {  // runs of segments with the same u columns are one projection
@@ -412,8 +418,9 @@ static void grad_A(const LayerGeom& g, const uint16_t* du, int nseg, const uint1
     p.seg_rows = g.r;
     for (int i = 0; i < nseg; ++i) p.Cseg[i] = dA[i];
     p.C = dA[0];
+    p.alpha = 1.0f / g.gsc;  // du holds gsc x the gradient
     p.tag = "gemm_lora_dA";
-    gemm(p, A_TRANS, B_DENSE_NN, TE_BF16, w.partial, s);
+    gemm(p, A_TRANS, B_DENSE_NN, g.te, w.partial, s);
 }
 
 void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora, const float* h_in,
@@ -423,12 +430,12 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
     if (recompute) layer_forward(g, wt, lora, false, h_in, nullptr, w, s, u_given);
 
     // ---- down projection: out = h1 + down(act)
-    launch_f32_to_bf16(dh_out, int64_t(T) * H, w.dy16, s);
+    launch_f32_to_act(dh_out, int64_t(T) * H, w.dy16, g.f16, g.gsc, s);  // gradients scaled by gsc from here
     {
         GemmParams p = dense_gemm(T, r, H, w.dy16, H, w.B_d, r);
-        out_bf16(p, w.du_d, r);
+        out16(p, w.du_d, r, g);
         p.tag = "gemm_lora_du";
-        gemm(p, A_ROW, B_DENSE_NN, TE_BF16, w.partial, s);
+        gemm(p, A_ROW, B_DENSE_NN, g.te, w.partial, s);
     }
     {
         GemmParams p = nf4_gemm(T, g.I, H, w.dy16, H, wt.packed[6], wt.absmax[6], g.I);
@@ -437,8 +444,8 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
         p.lda2 = r;
         p.B2 = w.A_d;
         p.ldb2 = g.I;
-        out_bf16(p, w.dact, g.I);
-        gemm(p, A_ROW, B_NF4_NN, TE_BF16, w.partial, s);
+        out16(p, w.dact, g.I, g);
+        gemm(p, A_ROW, B_NF4_NN, g.te, w.partial, s);
     }
     grad_B(g, w.dy16, H, H, w.u_d, r, grads->dB[6], w, s);
     {
@@ -446,12 +453,12 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
         grad_A(g, w.du_d, 1, w.act, g.I, dA, w, s);
     }
     // ---- SwiGLU and gate/up
-    launch_swiglu_bwd(w.dact, w.gu, T, g.I, w.dgu, s);
+    launch_swiglu_bwd(w.dact, w.gu, T, g.I, w.dgu, g.f16, s);
     {
         GemmParams p = dense_gemm(T, 2 * r, 2 * g.I, w.dgu, 2 * g.I, w.B_gu, 2 * r);
-        out_bf16(p, w.du_gu, 2 * r);
+        out16(p, w.du_gu, 2 * r, g);
         p.tag = "gemm_lora_du";
-        gemm(p, A_ROW, B_DENSE_NN, TE_BF16, w.partial, s);
+        gemm(p, A_ROW, B_DENSE_NN, g.te, w.partial, s);
     }
     {
         GemmParams p = nf4_gemm(T, H, 2 * g.I, w.dgu, 2 * g.I, wt.packed[4], wt.absmax[4], H);
@@ -461,7 +468,8 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
         p.B2 = w.A_gu;
         p.ldb2 = H;
         out_f32(p, w.dn2, H);
-        gemm(p, A_ROW, B_NF4_NN, TE_BF16, w.partial, s);
+        p.alpha = 1.0f / g.gsc;  // back to true gradients on the fp32 residual path
+        gemm(p, A_ROW, B_NF4_NN, g.te, w.partial, s);
     }
     {
         const int ucol[2] = {0, r};
@@ -475,12 +483,12 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
     launch_rmsnorm_bwd(w.dn2, w.h1, wt.g2, w.rstd2, dh_out, T, H, w.dh1, s);
 
     // ---- o projection: h1 = h + o(oattn)
-    launch_f32_to_bf16(w.dh1, int64_t(T) * H, w.dy16, s);
+    launch_f32_to_act(w.dh1, int64_t(T) * H, w.dy16, g.f16, g.gsc, s);
     {
         GemmParams p = dense_gemm(T, r, H, w.dy16, H, w.B_o, r);
-        out_bf16(p, w.du_o, r);
+        out16(p, w.du_o, r, g);
         p.tag = "gemm_lora_du";
-        gemm(p, A_ROW, B_DENSE_NN, TE_BF16, w.partial, s);
+        gemm(p, A_ROW, B_DENSE_NN, g.te, w.partial, s);
     }
     {
         GemmParams p = nf4_gemm(T, g.qdim, H, w.dy16, H, wt.packed[3], wt.absmax[3], g.qdim);
@@ -489,8 +497,8 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
         p.lda2 = r;
         p.B2 = w.A_o;
         p.ldb2 = g.qdim;
-        out_bf16(p, w.doattn, g.qdim);
-        gemm(p, A_ROW, B_NF4_NN, TE_BF16, w.partial, s);
+        out16(p, w.doattn, g.qdim, g);
+        gemm(p, A_ROW, B_NF4_NN, g.te, w.partial, s);
     }
     grad_B(g, w.dy16, H, H, w.u_o, r, grads->dB[3], w, s);
     {
@@ -500,15 +508,15 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
 
     // ---- attention: dq into dqkv, per-head fp32 dK, dV summed over each group below
     launch_flash_bwd(attn_args(g, w), s);
-    launch_gqa_reduce(w.dKh, g.B, g.nH, g.nKV, S, g.hd, w.dqkv, g.nqkv, g.qdim, w.rope_cs, s);  // dk, rotated back
-    launch_gqa_reduce(w.dVh, g.B, g.nH, g.nKV, S, g.hd, w.dqkv, g.nqkv, g.qdim + g.kvdim, nullptr, s);
+    launch_gqa_reduce(w.dKh, g.B, g.nH, g.nKV, S, g.hd, w.dqkv, g.nqkv, g.qdim, w.rope_cs, g.f16, s);  // dk, rotated back
+    launch_gqa_reduce(w.dVh, g.B, g.nH, g.nKV, S, g.hd, w.dqkv, g.nqkv, g.qdim + g.kvdim, nullptr, g.f16, s);
 
     // ---- q/k/v projections
     {
         GemmParams p = dense_gemm(T, 3 * r, g.nqkv, w.dqkv, g.nqkv, w.B_qkv, 3 * r);
-        out_bf16(p, w.du_qkv, 3 * r);
+        out16(p, w.du_qkv, 3 * r, g);
         p.tag = "gemm_lora_du";
-        gemm(p, A_ROW, B_DENSE_NN, TE_BF16, w.partial, s);
+        gemm(p, A_ROW, B_DENSE_NN, g.te, w.partial, s);
     }
     if (dh_in) {
         GemmParams p = nf4_gemm(T, H, g.nqkv, w.dqkv, g.nqkv, wt.packed[0], wt.absmax[0], H);
@@ -518,7 +526,8 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
         p.B2 = w.A_qkv;
         p.ldb2 = H;
         out_f32(p, w.dn1, H);
-        gemm(p, A_ROW, B_NF4_NN, TE_BF16, w.partial, s);
+        p.alpha = 1.0f / g.gsc;
+        gemm(p, A_ROW, B_NF4_NN, g.te, w.partial, s);
         launch_rmsnorm_bwd(w.dn1, h_in, wt.g1, w.rstd1, w.dh1, T, H, dh_in, s);
     }
     {  // q as qdim / kvdim segments of kvdim rows, then k and v

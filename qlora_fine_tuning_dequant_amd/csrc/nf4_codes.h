@@ -23,6 +23,23 @@ __device__ inline uint32_t f32x2_to_bf16x2(float lo, float hi) {
     typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){lo, hi}, b2_t));
 }
+// Two floats -> packed fp16 pair (lo in bits 0..15), round to nearest even.
+__device__ inline uint32_t f32x2_to_f16x2(float lo, float hi) {
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){lo, hi}, h2_t));
+}
+// Packed bf16 pair -> packed fp16 pair holding the same two values (exact
+// wherever fp16 can represent them: magnitudes in [2^-17, 65504] or zero).
+__device__ inline uint32_t bf16x2_to_f16x2(uint32_t b) {
+    return f32x2_to_f16x2(__builtin_bit_cast(float, b << 16), __builtin_bit_cast(float, b & 0xFFFF0000u));
+}
 __device__ inline float bf16_bits_to_f32(uint16_t b) { return __builtin_bit_cast(float, uint32_t(b) << 16); }
 __device__ inline float f16_bits_to_f32(uint16_t b) { return float(__builtin_bit_cast(_Float16, b)); }
+// A 16-bit activation (bf16 or fp16 bits, by the format flag) <-> fp32.
+__device__ inline float act_to_f32(uint16_t b, bool f16) { return f16 ? f16_bits_to_f32(b) : bf16_bits_to_f32(b); }
+__device__ inline uint16_t f32_to_act(float f, bool f16) { return f16 ? f32_to_f16_bits(f) : f32_to_bf16_bits(f); }
+__device__ inline uint32_t f32x2_to_act2(float lo, float hi, bool f16) {
+    return f16 ? f32x2_to_f16x2(lo, hi) : f32x2_to_bf16x2(lo, hi);
+}
 }  // namespace qlx

@@ -115,9 +115,11 @@ struct GemmParams {
     // batching over grid.z: z -> (bo = z / zdiv, bi = z % zdiv)
     int batch = 1, zdiv = 1, a_grp = 1, b_grp = 1;
     int64_t a_so = 0, a_si = 0, b_so = 0, b_si = 0, c_so = 0, c_si = 0;
-    // split-K (chosen by the launcher; shapes only)
+    // split-K (chosen by the launcher from the shapes and the room for
+    // partials: at most partial_cap floats at partial_ws)
     int splits = 1, kchunk = 0;
     float* partial = nullptr;
+    size_t partial_cap = size_t(1024) * 128 * 128;
     // epilogue
     void* C = nullptr;
     int64_t ldc = 0;
@@ -185,11 +187,14 @@ void launch_rmsnorm_bwd(const float* dy, const float* x, const float* g, const f
 void launch_rope_table(int seq, int hd, float theta, float* cs, hipStream_t s);
 // Rotates pairs (j, j + hd/2) of nheads heads in columns [col0, col0 + nheads*hd)
 // of a bf16 [T, ld] buffer in place; row t has position t % seq.
-void launch_rope(uint16_t* buf, int64_t ld, int T, int seq, int col0, int nheads, int hd, const float* cs, hipStream_t s);
-void launch_swiglu_fwd(const uint16_t* gu, int T, int I, uint16_t* act, hipStream_t s);
-void launch_swiglu_bwd(const uint16_t* dact, const uint16_t* gu, int T, int I, uint16_t* dgu, hipStream_t s);
+// 16-bit activations below are bf16, or fp16 when f16 != 0.
+void launch_rope(uint16_t* buf, int64_t ld, int T, int seq, int col0, int nheads, int hd, const float* cs, int f16,
+                 hipStream_t s);
+void launch_swiglu_fwd(const uint16_t* gu, int T, int I, uint16_t* act, int f16, hipStream_t s);
+void launch_swiglu_bwd(const uint16_t* dact, const uint16_t* gu, int T, int I, uint16_t* dgu, int f16, hipStream_t s);
 void launch_embed(const int32_t* tok, const uint16_t* E, int T, int H, int V, float* h, hipStream_t s);
-void launch_f32_to_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t s);
+// y = 16-bit(x * scale)
+void launch_f32_to_act(const float* x, int64_t n, uint16_t* y, int f16, float scale, hipStream_t s);
 void launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t s);
 // Layer blob wire form -> full form on the device: m32[i] = m16[i] << 16 for
 // the nb block maxima; g1d/g2d = g1s/g2s (H floats each).
@@ -213,6 +218,7 @@ struct AttnArgs {
     uint16_t* dqkv = nullptr;                 // dq written at column 0 (bf16)
     int64_t lddq = 0;
     const float2* rope = nullptr;             // [S, hd/2] (cos, sin): dq rotated back before its store
+    int f16 = 0;                              // 16-bit operands: 0 bf16, 1 fp16
 };
 void launch_flash_fwd(const AttnArgs& a, hipStream_t s);
 void launch_flash_bwd(const AttnArgs& a, hipStream_t s);
@@ -223,18 +229,18 @@ struct LoraSeg {
     int out_p;
 };
 void launch_lora_pack(const LoraSeg* segs, int nseg, int r, int in_f, float scale, uint16_t* Acat,
-                      uint16_t* Bbd, hipStream_t s);
+                      uint16_t* Bbd, int f16, hipStream_t s);
 // Several packs in one launch (one per grid row).
 struct LoraPackJob {
     const LoraSeg* segs;
     int nseg, in_f;
     uint16_t *Acat, *Bbd;
 };
-void launch_lora_pack_jobs(const LoraPackJob* jobs, int njobs, int r, float scale, hipStream_t s);
+void launch_lora_pack_jobs(const LoraPackJob* jobs, int njobs, int r, float scale, int f16, hipStream_t s);
 // rope non-null: each (j, j + hd/2) pair of the sums is rotated back (RoPE
 // transpose, table [S, hd/2]) before the bf16 store.
 void launch_gqa_reduce(const float* dh, int B, int nH, int nKV, int S, int hd, uint16_t* out, int64_t ldo,
-                       int col0, const float* rope, hipStream_t s);
+                       int col0, const float* rope, int f16, hipStream_t s);
 // Cross-entropy pieces over logits [T, V] (fp32).
 // target[t] < 0 marks a row with no loss. lse[t], picked[t] = z[t, target].
 void launch_ce_reduce(const float* pm, const float* ps, int nb, int T, int V, const int32_t* tokens, int seq, int start,

@@ -1,13 +1,29 @@
 """Full-size GPU checks on Llama-3.1-8B-shaped layers (hidden 4096, 32/8
 heads, head_dim 128, SwiGLU 14336, vocab 128256, LoRA r 64 alpha 16):
 
+* the 32-layer model at batch 1 x seq 512 (the pages' configuration): the
+  streamed SFT step against the oracle's, whose loss, gradient norms and a
+  fixed sample of every LoRA gradient's entries are stored in
+  tests/golden/sft8b_32l_b1x512_seed1.npz (written by make_fullsize_golden.py,
+  which calls only the oracle); the streamed DPO step with 2 pairs x 512 and
+  128-token prompts against tests/golden/dpo8b_32l_2x512_p128_seed1.npz;
 * streamed and resident runs of the 32-layer model at batch 4 x seq 512 give
   the same loss and LoRA gradients bit for bit (the pages' "difference 0.0"),
   with 2L-2 layer reads and a loss near its closed form at initialization;
 * at full width with 2 layers (so the oracle finishes in seconds), streamed
   SFT and DPO steps match the oracle, DPO with B = 0 gives exactly ln 2, and
-  the fused and separate reference schedules give identical bits."""
+  the fused and separate reference schedules give identical bits.
+
+Tolerances are the stated ones: |dloss| <= 1e-2 and rel-L2 <= 2e-2 on every
+LoRA gradient. They hold with fp16 activations (the default act_dtype). With
+bf16 activations the 8B-width gradients come out 2.3e-2 (2 layers) and
+8-12e-2 (32 layers) from the fp32 oracle: every bf16 rounding of an
+activation moves the last layers' q/k gradients (measured by replaying the
+oracle with bf16 rounding at the GPU path's points, one at a time); those
+cases are kept at the stated tolerance and marked as expected failures.
+"""
 import dataclasses
+import os
 
 import numpy as np
 import pytest
@@ -16,25 +32,86 @@ import torch
 import oracle
 import synth
 from gpu_helpers import gpu_model, grad_errors, run_dpo, run_sft, same_grads, to_np
-from helpers import lora_list, oracle_model
+from helpers import lora_list, oracle_model, rel_l2
 
 pytestmark = pytest.mark.gpu
 q = pytest.importorskip("qlora_fine_tuning_dequant_amd")
 B_ = q.binding
-# bf16 activations at hidden 4096 cost about 0.6-0.9% rel-L2 per layer (the
-# single-layer 8B test); errors add along the residual stream, so a 2-layer
-# full-width step is held to 3e-2 on every LoRA gradient.
-TOL2 = 3e-2
-# DPO: each summed log-prob (|lp| ~ 600 here) carries the bf16 activation
-# error, measured below 4e-4 relative; Delta combines four of them and the loss
-# moves by beta/2 per unit Delta near Delta = 0, so
-# |dloss| <= beta/2 * 4 * 4e-4 * max|lp|.
-LP_REL = 4e-4
+TOL = 2e-2        # rel-L2 on every LoRA gradient
+TOL_LOSS = 1e-2   # |dloss|
+LP_REL = 1e-3     # each sequence's summed log-prob, relative
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+BF16_XFAIL = pytest.mark.xfail(
+    reason="bf16 activations: the stated 2e-2 does not hold at 8B width (2.3e-2 over 2 layers, 8-12e-2 over 32) "
+           "-- the rounding of the activations themselves, not a kernel; fp16 activations meet it", strict=False)
+ACTS = [pytest.param(B_.QLX_ACT_F16, id="f16"), pytest.param(B_.QLX_ACT_BF16, id="bf16", marks=BF16_XFAIL)]
 
 
-def test_llama8b_32_layers_batch4_streamed_equals_resident():
+def _sample_index(layer, proj, which, size, samples):
+    # the same indices tests/golden/make_fullsize_golden.py kept
+    g = np.random.default_rng([20261203, layer, proj, which])
+    return np.sort(g.choice(size, size=min(samples, size), replace=False))
+
+
+def _vs_golden(grads, gold):
+    """Worst sampled rel-L2 and worst norm ratio error over every LoRA gradient."""
+    worst, worst_norm, where = 0.0, 0.0, ""
+    ns = int(gold["samples"])
+    for l, g in enumerate(grads):
+        for j, p in enumerate(synth.PROJ_NAMES):
+            for w, t in enumerate((g.dA[j], g.dB[j])):
+                key = f"L{l}_{p}_{'dA' if w == 0 else 'dB'}"
+                a = to_np(t).astype(np.float64).ravel()
+                idx = _sample_index(l, j, w, a.size, ns)
+                e = rel_l2(a[idx], gold[key + "_sample"])
+                en = abs(np.linalg.norm(a) - float(gold[key + "_norm"])) / float(gold[key + "_norm"])
+                if e > worst:
+                    worst, where = e, key
+                worst_norm = max(worst_norm, en)
+    return worst, worst_norm, where
+
+
+@pytest.fixture(scope="module")
+def llama32():
+    """The 32-layer 8B-shaped model (seed 1, kaiming LoRA) on the device and in pinned host RAM."""
     d = synth.LLAMA8B
     m, host = gpu_model(q, d, 1, "kaiming")
+    return d, m, host
+
+
+@pytest.mark.parametrize("act", ACTS)
+def test_llama8b_32_layers_b1x512_sft_vs_oracle(llama32, act):
+    d, m, host = llama32
+    gold = np.load(os.path.join(GOLDEN, "sft8b_32l_b1x512_seed1.npz"))
+    toks = synth.tokens(1, 1, 512, d.vocab)
+    loss, g, st = run_sft(q, m.with_blobs(host).with_act(act), toks, B_.QLX_STREAMED)
+    worst, worst_norm, where = _vs_golden(g, gold)
+    print(f"act {act}: loss {loss.item():.6f} oracle {float(gold['loss']):.6f}; worst sampled rel-L2 {worst:.2e} "
+          f"({where}); worst norm error {worst_norm:.2e}", flush=True)
+    assert st["layer_reads"] == 2 * d.n_layers - 2
+    assert abs(loss.item() - float(gold["loss"])) <= TOL_LOSS
+    assert worst <= TOL and worst_norm <= TOL, (worst, where, worst_norm)
+
+
+@pytest.mark.parametrize("act", ACTS)
+def test_llama8b_32_layers_dpo_2x512_prompt128_vs_oracle(llama32, act):
+    d, m, host = llama32
+    gold = np.load(os.path.join(GOLDEN, "dpo8b_32l_2x512_p128_seed1.npz"))
+    ch, rj = synth.dpo_pairs(1, 2, 512, 128, d.vocab)
+    loss, logps, g, st = run_dpo(q, m.with_blobs(host).with_act(act), ch, rj, 128, 0.1, B_.QLX_STREAMED,
+                                 B_.QLX_DPO_REF_FUSED)
+    lp = to_np(logps)
+    worst, worst_norm, where = _vs_golden(g, gold)
+    print(f"act {act}: loss {loss.item():.6f} oracle {float(gold['loss']):.6f}; logps {lp} oracle {gold['logps']}; "
+          f"worst sampled rel-L2 {worst:.2e} ({where}); worst norm error {worst_norm:.2e}", flush=True)
+    assert st["layer_reads"] == 2 * d.n_layers - 2
+    assert abs(loss.item() - float(gold["loss"])) <= TOL_LOSS
+    assert np.all(np.abs(lp - gold["logps"]) <= LP_REL * np.abs(gold["logps"])), (lp, gold["logps"])
+    assert worst <= TOL and worst_norm <= TOL, (worst, where, worst_norm)
+
+
+def test_llama8b_32_layers_batch4_streamed_equals_resident(llama32):
+    d, m, host = llama32
     toks = synth.tokens(1, 4, 512, d.vocab)
     loss_s, g_s, st_s = run_sft(q, m.with_blobs(host), toks, B_.QLX_STREAMED)
     loss_r, g_r, st_r = run_sft(q, m, toks, B_.QLX_RESIDENT)
@@ -53,40 +130,46 @@ def wide2():
     return d, m, host, oracle_model(d, 3), lora_list(d, 3, "kaiming")
 
 
-def test_llama8b_width_sft_step_vs_oracle(wide2):
+@pytest.mark.parametrize("act", ACTS)
+def test_llama8b_width_sft_step_vs_oracle(wide2, act):
     d, m, host, om, ol = wide2
     toks = synth.tokens(3, 1, 64, d.vocab)
-    loss, g, st = run_sft(q, m.with_blobs(host), toks, B_.QLX_STREAMED)
+    loss, g, st = run_sft(q, m.with_blobs(host).with_act(act), toks, B_.QLX_STREAMED)
     ref_loss, ref_g = oracle.sft_step(om, ol, toks, d)
-    assert abs(loss.item() - ref_loss) < 1e-2, (loss.item(), ref_loss)
     errs = grad_errors(g, ref_g)
-    print({k: f"{v:.1e}" for k, v in errs.items()})
-    bad = {k: v for k, v in errs.items() if not v < TOL2}
+    print(act, f"loss {loss.item():.6f} oracle {ref_loss:.6f}", {k: f"{v:.1e}" for k, v in errs.items()}, flush=True)
+    assert abs(loss.item() - ref_loss) <= TOL_LOSS, (loss.item(), ref_loss)
+    bad = {k: v for k, v in errs.items() if not v <= TOL}
     assert not bad, bad
 
 
-def test_llama8b_width_dpo_vs_oracle_and_schedules(wide2):
+@pytest.mark.parametrize("act", ACTS)
+def test_llama8b_width_dpo_vs_oracle_and_schedules(wide2, act):
     d, m, host, om, ol = wide2
     ch, rj = synth.dpo_pairs(3, 2, 64, 16, d.vocab)
-    sm = m.with_blobs(host)
+    sm = m.with_blobs(host).with_act(act)
     l_f, lp_f, g_f, st_f = run_dpo(q, sm, ch, rj, 16, 0.1, B_.QLX_STREAMED, B_.QLX_DPO_REF_FUSED)
     l_s, lp_s, g_s, st_s = run_dpo(q, sm, ch, rj, 16, 0.1, B_.QLX_STREAMED, B_.QLX_DPO_REF_SEPARATE)
     assert torch.equal(l_f, l_s) and torch.equal(lp_f, lp_s) and same_grads(g_f, g_s)
     assert st_f["layer_reads"] == 2 * 2 - 2 and st_s["layer_reads"] == 3 * 2 - 2
     ref_loss, ref_lp, ref_g = oracle.dpo_step(om, ol, ch, rj, 16, 0.1, d)
     lp = to_np(lp_f)
+    errs = grad_errors(g_f, ref_g)
+    print(act, f"loss {l_f.item():.6f} oracle {ref_loss:.6f}; logps {lp} oracle {ref_lp}",
+          {k: f"{v:.1e}" for k, v in errs.items()}, flush=True)
     assert np.all(np.abs(lp - ref_lp) <= LP_REL * np.abs(ref_lp)), (lp, ref_lp)
-    bound = 0.1 / 2 * 4 * LP_REL * np.max(np.abs(ref_lp))
-    assert abs(l_f.item() - ref_loss) <= bound, (l_f.item(), ref_loss, bound)
-    bad = {k: v for k, v in grad_errors(g_f, ref_g).items() if not v < TOL2}
+    assert abs(l_f.item() - ref_loss) <= TOL_LOSS, (l_f.item(), ref_loss)
+    bad = {k: v for k, v in errs.items() if not v <= TOL}
     assert not bad, bad
 
 
-def test_llama8b_width_dpo_zero_adapter_is_exactly_ln2():
+@pytest.mark.parametrize("act", [B_.QLX_ACT_F16, B_.QLX_ACT_BF16], ids=["f16", "bf16"])
+def test_llama8b_width_dpo_zero_adapter_is_exactly_ln2(act):
     d = dataclasses.replace(synth.LLAMA8B, n_layers=2)
     m, host = gpu_model(q, d, 4, "zeroB")
     ch, rj = synth.dpo_pairs(4, 2, 64, 16, d.vocab)
-    loss, logps, _, _ = run_dpo(q, m.with_blobs(host), ch, rj, 16, 0.1, B_.QLX_STREAMED, B_.QLX_DPO_REF_FUSED)
+    loss, logps, _, _ = run_dpo(q, m.with_blobs(host).with_act(act), ch, rj, 16, 0.1, B_.QLX_STREAMED,
+                                B_.QLX_DPO_REF_FUSED)
     lp = to_np(logps)
     assert np.array_equal(lp[:4], lp[4:])
     assert loss.item() == float(np.float32(np.log(2.0)))

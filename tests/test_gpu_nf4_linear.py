@@ -209,3 +209,66 @@ def test_linear_dequant_operand_is_exactly_bf16_of_dequant():
     Wd = oracle.nf4_dequant(p_ref, a_ref, out_f * in_f).reshape(out_f, in_f)
     expect = oracle.bf16_rne_bits(np.stack([Wd[:, i * 31] for i in range(16)]))
     assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), expect)
+
+
+# Every full-tile NF4 kernel shape (QLX_NF4_TILE pins it; by default a cost
+# model picks one) on 8B-width projections at 512 and 1024 tokens, forward and
+# dX with the LoRA slab, against the oracle; and the one-hot check that the
+# weight operand is exactly bf16 of the dequantized value.
+@pytest.mark.parametrize("tile", ["256x128", "512x128", "512x64"])
+@pytest.mark.parametrize("T,in_f,out_f,r", [(512, 4096, 6144, 64), (1024, 14336, 4096, 64), (512, 4096, 28672, 64),
+                                           (1024, 4096, 4096, 64)])
+def test_each_nf4_tile_shape_vs_oracle(monkeypatch, tile, T, in_f, out_f, r):
+    monkeypatch.setenv("QLX_NF4_TILE", tile)
+    seed = T + in_f + out_f + 7
+    wb = _w_bits(out_f, in_f, seed)
+    W = q.NF4Matrix.quantize(bf16_dev(wb))
+    p_ref, a_ref = oracle.nf4_quantize(synth.bf16_bits_to_f32(wb))
+    Wd = oracle.nf4_dequant(p_ref, a_ref, out_f * in_f).reshape(out_f, in_f)
+    xb = synth.activations_bf16(seed, T, in_f, 0)
+    dyb = synth.activations_bf16(seed, T, out_f, 1)
+    g = np.random.default_rng(seed)
+    A = (g.uniform(-1, 1, (r, in_f)) / np.sqrt(in_f)).astype(np.float32)
+    B = (g.standard_normal((out_f, r)) * 0.05).astype(np.float32)
+    s = 16.0 / r
+    x, dy = bf16_dev(xb), bf16_dev(dyb)
+    y = torch.empty(T, out_f, dtype=torch.bfloat16, device=DEV)
+    q.qlora_linear_fwd(x, W, f32_dev(A), f32_dev(B), s, y)
+    y_ref, u_ref = _oracle_linear(xb, Wd, A, B, s)
+    dx = torch.empty(T, in_f, dtype=torch.bfloat16, device=DEV)
+    dA = torch.empty(r, in_f, dtype=torch.float32, device=DEV)
+    dB = torch.empty(out_f, r, dtype=torch.float32, device=DEV)
+    q.qlora_linear_bwd(dy, x, W, f32_dev(A), f32_dev(B), s, dx, dA, dB)
+    dx_ref, _, _ = oracle.qlora_linear_bwd(synth.bf16_bits_to_f32(dyb), synth.bf16_bits_to_f32(xb), u_ref, Wd, A, B, s)
+    print(tile, T, in_f, out_f, "y", rel_l2(to_np(y), y_ref), "dx", rel_l2(to_np(dx), dx_ref), flush=True)
+    assert rel_l2(to_np(y), y_ref) < TOL and rel_l2(to_np(dx), dx_ref) < TOL
+    # B = 0 equals LoRA off bit for bit on this kernel too
+    y0, y_off = torch.empty_like(y), torch.empty_like(y)
+    q.qlora_linear_fwd(x, W, f32_dev(A), torch.zeros(out_f, r, dtype=torch.float32, device=DEV), s, y0)
+    q.qlora_linear_fwd(x, W, None, None, s, y_off)
+    assert torch.equal(y0.view(torch.int16), y_off.view(torch.int16))
+
+
+@pytest.mark.parametrize("tile", ["256x128", "512x128", "512x64"])
+def test_each_nf4_tile_operand_is_bf16_of_dequant(monkeypatch, tile):
+    """One-hot rows at 512 tokens (full-tile kernels): forward y row i =
+    bf16(W'[:, j_i]) exactly, and dX row i = bf16(W'[j_i, :]) exactly."""
+    monkeypatch.setenv("QLX_NF4_TILE", tile)
+    out_f, in_f, T = 1024, 2048, 512
+    wb = _w_bits(out_f, in_f, 11)
+    W = q.NF4Matrix.quantize(bf16_dev(wb))
+    p_ref, a_ref = oracle.nf4_quantize(synth.bf16_bits_to_f32(wb))
+    Wd = oracle.nf4_dequant(p_ref, a_ref, out_f * in_f).reshape(out_f, in_f)
+    jx = (np.arange(T) * 37) % in_f
+    xb = np.zeros((T, in_f), np.float32)
+    xb[np.arange(T), jx] = 1.0
+    y = torch.empty(T, out_f, dtype=torch.bfloat16, device=DEV)
+    q.qlora_linear_fwd(bf16_dev(oracle.bf16_rne_bits(xb)), W, None, None, 1.0, y)
+    assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), oracle.bf16_rne_bits(Wd[:, jx].T))
+    jy = (np.arange(T) * 13) % out_f
+    dyb = np.zeros((T, out_f), np.float32)
+    dyb[np.arange(T), jy] = 1.0
+    dx = torch.empty(T, in_f, dtype=torch.bfloat16, device=DEV)
+    q.qlora_linear_bwd(bf16_dev(oracle.bf16_rne_bits(dyb)), bf16_dev(oracle.bf16_rne_bits(xb)), W, None, None, 1.0,
+                       dx, None, None)
+    assert np.array_equal(dx.view(torch.int16).cpu().numpy().view(np.uint16), oracle.bf16_rne_bits(Wd[jy, :]))
