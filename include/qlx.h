@@ -135,6 +135,22 @@ size_t qlx_linear_workspace_bytes(int64_t T, int64_t in_f, int64_t out_f, int r)
 int qlora_linear_fwd(const uint16_t* x, int64_t T, qlx_nf4 W, const float* A, const float* B,
                      int r, float scale, uint16_t* y, void* ws, size_t ws_bytes, void* stream);
 
+/* The same forward for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * workspace argument; the adapter staging and the split-K partials live in a
+ * static device array of QLX_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends (its device address is looked up
+ * once per device on the first call there). Calls no allocating routine.
+ * Inputs as qlora_linear_fwd; with LoRA on, the staging (2 r (in + out) +
+ * 4 T r bytes, rounded up to 256-byte pieces) must fit the scratch, else
+ * QLX_EINVAL before any launch; what is left of the scratch bounds the
+ * split-K partials (fewer splits, never a different result than the split
+ * count the shapes choose within that room). Calls that overlap on one GPU
+ * share the array and race: serialize them (one stream, or events). */
+#define QLX_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int qlora_linear_fwd_noalloc(const uint16_t* x, int64_t T, qlx_nf4 W, const float* A, const float* B,
+                             int r, float scale, uint16_t* y, void* stream);
+
 /* Backward with W frozen. dy bf16 [T, out], x bf16 [T, in] (the forward input).
  *   du = s dy B;  dx = dy W' + du A (bf16 [T, in], NULL = skip);
  *   dB = s dy^T (x A^T) (fp32 [out, r]);  dA = du^T x (fp32 [r, in]).

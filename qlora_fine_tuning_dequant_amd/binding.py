@@ -49,7 +49,7 @@ EXPORTED = (
     "qlx_layer_file_write", "qlx_layer_file_open", "qlx_layer_file_close", "qlx_layer_file_info",
     "qlx_layer_file_read", "qlx_ctx_set_layer_source", "qlx_stream_source_auto", "qlx_ctx_set_debug",
     "qlx_peak_mfma", "qlx_peak_copy", "qlx_layer_wire_layout", "qlx_layer_blob_to_wire", "qlx_ctx_set_keep_layers",
-    "qlx_ctx_set_adamw", "qlx_ctx_adamw_t",
+    "qlx_ctx_set_adamw", "qlx_ctx_adamw_t", "qlora_linear_fwd_noalloc",
 )
 
 
@@ -141,6 +141,7 @@ def lib() -> C.CDLL:
         "nf4_dequant": (i32, [vp, vp, i64, i64, i32, vp, vp]),
         "qlx_linear_workspace_bytes": (sz, [i64, i64, i64, i32]),
         "qlora_linear_fwd": (i32, [vp, i64, NF4, vp, vp, i32, f32, vp, vp, sz, vp]),
+        "qlora_linear_fwd_noalloc": (i32, [vp, i64, NF4, vp, vp, i32, f32, vp, vp]),
         "qlora_linear_bwd": (i32, [vp, vp, i64, NF4, vp, vp, i32, f32, vp, vp, vp, i32, vp, sz, vp]),
         "qlx_layer_blob_layout": (i32, [C.POINTER(Dims), C.POINTER(C.c_uint64), C.POINTER(C.c_uint64)]),
         "qlx_layer_wire_layout": (i32, [C.POINTER(Dims), C.POINTER(C.c_uint64), C.POINTER(C.c_uint64)]),

@@ -163,6 +163,28 @@ static void linear_fwd(const uint16_t* x, int64_t T, const qlx_nf4& W, const flo
     gemm(p, A_ROW, B_NF4_NT, TE_BF16, w.partial, s);
 }
 
+// Scratch of the allocation-free forward: one copy per GPU the library runs
+// on, held until the process ends. Host code never passes `scratch` itself to
+// a kernel (in host code it names a host-side stand-in): it uses the device
+// address hipGetSymbolAddress returns for the current device.
+constexpr size_t kNoAllocScratchBytes = QLX_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64] = {};
+
+static char* scratch_on_current_device() {
+    int dev = 0;
+    QLX_CHECK_HIP(hipGetDevice(&dev));
+    QLX_REQUIRE(dev >= 0 && dev < 64, QLX_EUNSUPPORTED, "device index out of range");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        QLX_CHECK_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+        QLX_REQUIRE(ptr != nullptr, QLX_EHIP, "scratch: no device address");
+        g_scratch_ptr[dev] = ptr;
+    }
+    return static_cast<char*>(g_scratch_ptr[dev]);
+}
 }  // namespace qlx
 
 extern "C" {
@@ -179,6 +201,38 @@ int qlora_linear_fwd(const uint16_t* x, int64_t T, qlx_nf4 W, const float* A, co
         Carver c(ws);
         const LinearWs w = carve_linear(c, T, W.cols, W.rows, rr);
         linear_fwd(x, T, W, A, B, r, scale, y, w, kGemmPartialFloats, static_cast<hipStream_t>(stream));
+    });
+}
+
+int qlora_linear_fwd_noalloc(const uint16_t* x, int64_t T, qlx_nf4 W, const float* A, const float* B, int r,
+                             float scale, uint16_t* y, void* stream) {
+    return guarded([&] {
+        validate_linear(T, W, A, B, r);
+        if (T == 0) return;
+        REQ_PTR(x, "x");
+        REQ_PTR(y, "y");
+        const int rr = A ? r : 0;
+        // the staging (adapters in bf16, u) first, then whatever is left for split-K partials
+        Carver probe(nullptr);
+        probe.take<uint16_t>(size_t(rr) * W.cols);
+        probe.take<uint16_t>(size_t(W.rows) * rr);
+        probe.take<uint16_t>(size_t(T) * rr);
+        probe.take<uint16_t>(size_t(T) * rr);
+        const size_t staging = probe.size();
+        QLX_REQUIRE(staging <= kNoAllocScratchBytes, QLX_EINVAL,
+                    "qlora_linear_fwd_noalloc: the adapter staging (" + std::to_string(staging) +
+                        " bytes) exceeds the static scratch (" + std::to_string(kNoAllocScratchBytes) + " bytes)");
+        char* base = scratch_on_current_device();
+        Carver c(base);
+        LinearWs w;
+        w.Ab = c.take<uint16_t>(size_t(rr) * W.cols);
+        w.Bb = c.take<uint16_t>(size_t(W.rows) * rr);
+        w.u = c.take<uint16_t>(size_t(T) * rr);
+        w.du = c.take<uint16_t>(size_t(T) * rr);
+        const size_t used = c.size();
+        w.partial = reinterpret_cast<float*>(base + used);
+        linear_fwd(x, T, W, A, B, r, scale, y, w, (kNoAllocScratchBytes - used) / sizeof(float),
+                   static_cast<hipStream_t>(stream));
     });
 }
 
