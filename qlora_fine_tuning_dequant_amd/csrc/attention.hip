@@ -31,6 +31,7 @@
 #include <cmath>
 
 #include "nf4_codes.h"
+#include "partials.h"
 #include "qlx_internal.h"
 
 namespace qlx {
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(256) void k_flash_fwd(const AttnArgs a) {
 // D[b, h, q] = sum_d dO[q, h d] o[q, h d]: hd/8 lanes per (query, head),
 // each with one 16-byte load of dO and of o (consecutive lanes read
 // consecutive bytes of a token row), joined by xor shuffles in a fixed order.
-template <int TE>
+template <int TE, bool PART>
 __global__ __launch_bounds__(256) void k_flash_bwd_dot(const AttnArgs a, int hd) {
     const int L = hd / 8;  // 8 or 16 lanes per (query, head)
     const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -239,7 +240,17 @@ __global__ __launch_bounds__(256) void k_flash_bwd_dot(const AttnArgs a, int hd)
     const int64_t pc = live ? pair : 0;
     const int64_t t = pc / a.nH;
     const int h = int(pc % a.nH);
-    const uint4 u = *reinterpret_cast<const uint4*>(a.dO + t * a.ldo + int64_t(h) * hd + part * 8);
+    uint4 u;
+    if constexpr (PART) {  // dO from the o projection's split-K partials, rounded as its reduce pass would
+        const int64_t i = t * a.qdim + int64_t(h) * hd + part * 8;
+        const float4 x0 = part_sum4(a.dO_part, i, 0), x1 = part_sum4(a.dO_part, i + 4, 0);
+        const bool f = TE == TE_F16;
+        u = make_uint4(f32x2_to_act2(x0.x, x0.y, f), f32x2_to_act2(x0.z, x0.w, f), f32x2_to_act2(x1.x, x1.y, f),
+                       f32x2_to_act2(x1.z, x1.w, f));
+        if (live) *reinterpret_cast<uint4*>(a.dO_out + t * a.ldo + int64_t(h) * hd + part * 8) = u;
+    } else {
+        u = *reinterpret_cast<const uint4*>(a.dO + t * a.ldo + int64_t(h) * hd + part * 8);
+    }
     const uint4 v = *reinterpret_cast<const uint4*>(a.O + t * a.ldo + int64_t(h) * hd + part * 8);
     const uint32_t uw[4] = {u.x, u.y, u.z, u.w}, vw[4] = {v.x, v.y, v.z, v.w};
     float s = 0.f;
@@ -483,10 +494,22 @@ void launch_flash_bwd(const AttnArgs& a, hipStream_t s) {
     check_attn(a);
     const int64_t n = int64_t(a.B) * a.S * a.nH;
     {
-        ProfScope prof("attn_bwd_dot", 2.0 * n * a.hd, double(n) * (a.hd * 4.0 + 4.0), s);
         const int64_t threads = n * (a.hd / 8);
-        if (a.f16) hipLaunchKernelGGL(k_flash_bwd_dot<TE_F16>, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, a, a.hd);
-        else hipLaunchKernelGGL(k_flash_bwd_dot<TE_BF16>, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, a, a.hd);
+        const dim3 g(unsigned((threads + 255) / 256));
+        if (a.dO_part.p) {
+            const Partials& q = a.dO_part;
+            QLX_REQUIRE(a.dO_out && a.dO_out == a.dO && q.splits >= 1 && !q.R && q.mn == int64_t(a.B) * a.S * a.qdim &&
+                            (reinterpret_cast<uintptr_t>(q.p) & 15) == 0,
+                        QLX_EINVAL, "attention backward: bad dO partials");
+            ProfScope prof("reduce_attn_dot", double(n) * a.hd * (q.splits + 2.0),
+                           double(n) * (a.hd * (4.0 * q.splits + 4.0) + 4.0), s);
+            if (a.f16) hipLaunchKernelGGL((k_flash_bwd_dot<TE_F16, true>), g, dim3(256), 0, s, a, a.hd);
+            else hipLaunchKernelGGL((k_flash_bwd_dot<TE_BF16, true>), g, dim3(256), 0, s, a, a.hd);
+        } else {
+            ProfScope prof("attn_bwd_dot", 2.0 * n * a.hd, double(n) * (a.hd * 4.0 + 4.0), s);
+            if (a.f16) hipLaunchKernelGGL((k_flash_bwd_dot<TE_F16, false>), g, dim3(256), 0, s, a, a.hd);
+            else hipLaunchKernelGGL((k_flash_bwd_dot<TE_BF16, false>), g, dim3(256), 0, s, a, a.hd);
+        }
         check_launch("attn_bwd_dot");
     }
     const dim3 grid(unsigned((a.S + QB - 1) / QB), unsigned(a.nH), unsigned(a.B));

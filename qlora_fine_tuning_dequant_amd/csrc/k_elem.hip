@@ -12,6 +12,7 @@
 #include <cmath>
 
 #include "nf4_codes.h"
+#include "partials.h"
 #include "qlx_internal.h"
 
 namespace qlx {
@@ -153,6 +154,74 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd_v(const float* __restrict__
         o[threadIdx.x + 256 * k] = v;
     }
 }
+// The vector kernels above with the input row summed from split-K partials
+// (the GEMM's reduce pass fused in): forward writes the summed row to xout
+// (fp32) too.
+template <int NV>
+__global__ __launch_bounds__(256) void k_rmsnorm_fwd_p(const Partials q, float* __restrict__ xout,
+                                                       const float* __restrict__ g, int H, float eps,
+                                                       void* __restrict__ out, int out_f16, float* __restrict__ rstd) {
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const float4* gr = reinterpret_cast<const float4*>(g);
+    float4* xo = reinterpret_cast<float4*>(xout + row * H);
+    float4 v[NV];
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const int64_t c = 4 * (threadIdx.x + 256 * k);
+        v[k] = part_sum4(q, row * H + c, row * q.ldr + c);
+        xo[threadIdx.x + 256 * k] = v[k];
+        ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
+    }
+    ss = block_sum256(ss, red);
+    const float r = 1.0f / sqrtf(ss / float(H) + eps);
+    if (threadIdx.x == 0 && rstd) rstd[row] = r;
+    uint2* o = reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + row * H);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const float4 gg = gr[threadIdx.x + 256 * k];
+        const float y0 = v[k].x * r * gg.x, y1 = v[k].y * r * gg.y, y2 = v[k].z * r * gg.z, y3 = v[k].w * r * gg.w;
+        o[threadIdx.x + 256 * k] = make_uint2(f32x2_to_act2(y0, y1, out_f16), f32x2_to_act2(y2, y3, out_f16));
+    }
+}
+template <int NV>
+__global__ __launch_bounds__(256) void k_rmsnorm_bwd_p(const Partials q, const float* __restrict__ x,
+                                                       const float* __restrict__ g, const float* __restrict__ rstd,
+                                                       const float* __restrict__ dres, int H, float* __restrict__ dx) {
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const float4* xr = reinterpret_cast<const float4*>(x + row * H);
+    const float4* gr = reinterpret_cast<const float4*>(g);
+    const float r = rstd[row];
+    float4 a[NV], b[NV];  // dy * g, x * r
+    float dot = 0.f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const float4 d = part_sum4(q, row * H + 4 * (threadIdx.x + 256 * k), 0);
+        const float4 xx = xr[threadIdx.x + 256 * k], gg = gr[threadIdx.x + 256 * k];
+        a[k] = make_float4(d.x * gg.x, d.y * gg.y, d.z * gg.z, d.w * gg.w);
+        b[k] = make_float4(xx.x * r, xx.y * r, xx.z * r, xx.w * r);
+        dot += a[k].x * b[k].x + a[k].y * b[k].y + a[k].z * b[k].z + a[k].w * b[k].w;
+    }
+    dot = block_sum256(dot, red) / float(H);
+    float4* o = reinterpret_cast<float4*>(dx + row * H);
+    const float4* dr = dres ? reinterpret_cast<const float4*>(dres + row * H) : nullptr;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        float4 v = make_float4(r * (a[k].x - b[k].x * dot), r * (a[k].y - b[k].y * dot), r * (a[k].z - b[k].z * dot),
+                               r * (a[k].w - b[k].w * dot));
+        if (dr) {
+            const float4 q4 = dr[threadIdx.x + 256 * k];
+            v.x += q4.x;
+            v.y += q4.y;
+            v.z += q4.z;
+            v.w += q4.w;
+        }
+        o[threadIdx.x + 256 * k] = v;
+    }
+}
+
 static bool rms_vec(int H, const void* a, const void* b, const void* c, const void* d) {
     return H % 1024 == 0 && H <= 4096 && al16(a) && al16(b) && al16(c) && (!d || al16(d));
 }
@@ -188,6 +257,44 @@ void launch_rmsnorm_bwd(const float* dy, const float* x, const float* g, const f
         hipLaunchKernelGGL(k_rmsnorm_bwd, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx);
     }
     check_launch("rmsnorm_bwd");
+}
+
+bool rmsnorm_part_ok(int H) { return H % 1024 == 0 && H >= 1024 && H <= 4096; }
+static void check_part(const Partials& q, int64_t mn, const char* what) {
+    QLX_REQUIRE(q.p && q.splits >= 1 && q.mn == mn && al16(q.p) && (!q.R || (al16(q.R) && q.ldr % 4 == 0)),
+                QLX_EINVAL, std::string(what) + ": bad split-K partials");
+}
+void launch_rmsnorm_fwd_part(const Partials& x, float* xout, const float* g, int T, int H, float eps, void* out,
+                             int out_f16, float* rstd, hipStream_t s) {
+    if (T <= 0) return;
+    QLX_REQUIRE(rmsnorm_part_ok(H) && al16(xout) && al16(g) && (reinterpret_cast<uintptr_t>(out) & 7) == 0,
+                QLX_EINVAL, "rmsnorm_fwd (partials): needs H a multiple of 1024 up to 4096 and aligned rows");
+    check_part(x, int64_t(T) * H, "rmsnorm_fwd");
+    ProfScope prof("reduce_rmsnorm_fwd", (x.splits + 4.0) * T * H,
+                   double(T) * H * (4.0 * x.splits + (x.R ? 4 : 0) + 4 + 2) + 4.0 * H, s);
+    switch (H / 1024) {
+        case 1: hipLaunchKernelGGL(k_rmsnorm_fwd_p<1>, dim3(T), dim3(256), 0, s, x, xout, g, H, eps, out, out_f16, rstd); break;
+        case 2: hipLaunchKernelGGL(k_rmsnorm_fwd_p<2>, dim3(T), dim3(256), 0, s, x, xout, g, H, eps, out, out_f16, rstd); break;
+        case 3: hipLaunchKernelGGL(k_rmsnorm_fwd_p<3>, dim3(T), dim3(256), 0, s, x, xout, g, H, eps, out, out_f16, rstd); break;
+        default: hipLaunchKernelGGL(k_rmsnorm_fwd_p<4>, dim3(T), dim3(256), 0, s, x, xout, g, H, eps, out, out_f16, rstd);
+    }
+    check_launch("rmsnorm_fwd (partials)");
+}
+void launch_rmsnorm_bwd_part(const Partials& dy, const float* x, const float* g, const float* rstd, const float* dres,
+                             int T, int H, float* dx, hipStream_t s) {
+    if (T <= 0) return;
+    QLX_REQUIRE(rmsnorm_part_ok(H) && al16(x) && al16(g) && al16(dx) && (!dres || al16(dres)) && !dy.R, QLX_EINVAL,
+                "rmsnorm_bwd (partials): needs H a multiple of 1024 up to 4096 and aligned rows");
+    check_part(dy, int64_t(T) * H, "rmsnorm_bwd");
+    ProfScope prof("reduce_rmsnorm_bwd", (dy.splits + 8.0) * T * H,
+                   double(T) * H * (4.0 * dy.splits + 8.0 + (dres ? 4 : 0)), s);
+    switch (H / 1024) {
+        case 1: hipLaunchKernelGGL(k_rmsnorm_bwd_p<1>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx); break;
+        case 2: hipLaunchKernelGGL(k_rmsnorm_bwd_p<2>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx); break;
+        case 3: hipLaunchKernelGGL(k_rmsnorm_bwd_p<3>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx); break;
+        default: hipLaunchKernelGGL(k_rmsnorm_bwd_p<4>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx);
+    }
+    check_launch("rmsnorm_bwd (partials)");
 }
 
 // 16-bit activations (bf16, or fp16 when f16) x8 <-> fp32 x8 for 16-byte accesses.
@@ -259,6 +366,60 @@ __global__ void k_rope8(uint16_t* __restrict__ buf, int64_t ld, int T, int seq, 
     }
     *reinterpret_cast<uint4*>(p) = pack8(ra, f16);
     *reinterpret_cast<uint4*>(p + half) = pack8(rb, f16);
+}
+
+// The q|k|v projection's split-K partials summed into the 16-bit buffer,
+// heads [0, nrot) rotated as k_rope8 does (eight pairs per thread), heads
+// [nrot, nall) copied; rows of nall * hd.
+__global__ void k_rope8_part(const Partials q, uint16_t* __restrict__ buf, int T, int seq, int nrot, int nall,
+                             int hd, const float2* __restrict__ cs, int f16) {
+    const int half = hd / 2, h8 = half / 8;
+    const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t total = int64_t(T) * nall * h8;
+    if (idx >= total) return;
+    const int j = int(idx % h8) * 8;
+    const int h = int((idx / h8) % nall);
+    const int t = int(idx / (int64_t(h8) * nall));
+    const int64_t i0 = int64_t(t) * nall * hd + h * hd + j;  // flat index of the first half's element j
+    float a[8], b[8];
+    {
+        const float4 a0 = part_sum4(q, i0, 0), a1 = part_sum4(q, i0 + 4, 0);
+        const float4 b0 = part_sum4(q, i0 + half, 0), b1 = part_sum4(q, i0 + half + 4, 0);
+        a[0] = a0.x, a[1] = a0.y, a[2] = a0.z, a[3] = a0.w, a[4] = a1.x, a[5] = a1.y, a[6] = a1.z, a[7] = a1.w;
+        b[0] = b0.x, b[1] = b0.y, b[2] = b0.z, b[3] = b0.w, b[4] = b1.x, b[5] = b1.y, b[6] = b1.z, b[7] = b1.w;
+    }
+    uint16_t* p = buf + i0;
+    if (h < nrot) {
+        const float4* c4 = reinterpret_cast<const float4*>(cs + (t % seq) * half + j);
+        float ra[8], rb[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float4 c = c4[k];  // (cos, sin) of pairs 2k and 2k+1
+            ra[2 * k] = a[2 * k] * c.x - b[2 * k] * c.y;
+            rb[2 * k] = b[2 * k] * c.x + a[2 * k] * c.y;
+            ra[2 * k + 1] = a[2 * k + 1] * c.z - b[2 * k + 1] * c.w;
+            rb[2 * k + 1] = b[2 * k + 1] * c.z + a[2 * k + 1] * c.w;
+        }
+        *reinterpret_cast<uint4*>(p) = pack8(ra, f16);
+        *reinterpret_cast<uint4*>(p + half) = pack8(rb, f16);
+    } else {
+        *reinterpret_cast<uint4*>(p) = pack8(a, f16);
+        *reinterpret_cast<uint4*>(p + half) = pack8(b, f16);
+    }
+}
+bool rope_part_ok(int hd, int nall) { return hd % 16 == 0 && hd >= 16 && nall >= 1; }
+void launch_rope_part(const Partials& src, uint16_t* buf, int T, int seq, int nrot, int nall, int hd, const float* cs,
+                      int f16, hipStream_t s) {
+    const int64_t total = int64_t(T) * nall * (hd / 16);
+    if (total <= 0) return;
+    QLX_REQUIRE(rope_part_ok(hd, nall) && nrot >= 0 && nrot <= nall && al16(buf) && al16(cs) && !src.R, QLX_EINVAL,
+                "rope (partials): needs hd a multiple of 16 and aligned rows");
+    check_part(src, int64_t(T) * nall * hd, "rope");
+    const double n = double(T) * nall * hd;
+    ProfScope prof("reduce_rope", n * (src.splits + 3.0), n * (4.0 * src.splits + 2.0), s);
+    hipLaunchKernelGGL(k_rope8_part, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, src, buf, T, seq, nrot, nall,
+                       hd, reinterpret_cast<const float2*>(cs), f16);
+    check_launch("rope (partials)");
 }
 
 void launch_rope_table(int seq, int hd, float theta, float* cs, hipStream_t s) {

@@ -328,12 +328,15 @@ __device__ inline void mma_chunk(const uint16_t* __restrict__ As, const uint16_t
     }
 }
 
+// SEG = false: the caller guarantees seg_rows == 0 (no indexed access into
+// the parameter block, so a kernel's local copy of it stays in registers)
+template <bool SEG = true>
 __device__ inline void store_out(const GemmParams& p, int bo, int bi, int row, int col, float v) {
     v *= p.alpha;
     if (p.R) v += p.R[int64_t(row) * p.ldr + col];
     void* C = p.C;
     int64_t off;
-    if (p.seg_rows > 0) {
+    if (SEG && p.seg_rows > 0) {
         C = p.Cseg[row / p.seg_rows];
         off = int64_t(row % p.seg_rows) * p.ldc + col;
     } else {
@@ -353,8 +356,9 @@ __device__ inline void store_out(const GemmParams& p, int bo, int bi, int row, i
 // Writes n consecutive outputs of one row starting at col (values already
 // accumulated, alpha not yet applied). Vector path for plain bf16 and fp32
 // (+ residual) rows; store_out element by element otherwise.
+template <bool SEG = true>
 __device__ inline void store_row(const GemmParams& p, int bo, int bi, int row, int col, const float* v, int n) {
-    if (p.seg_rows == 0 && !p.accumulate && col + n <= p.N && (n & 7) == 0) {
+    if ((!SEG || p.seg_rows == 0) && !p.accumulate && col + n <= p.N && (n & 7) == 0) {
         const int64_t off = int64_t(bo) * p.c_so + int64_t(bi) * p.c_si + int64_t(row) * p.ldc + col;
         if ((p.c_type == C_BF16 || p.c_type == C_F16) && (off & 7) == 0 && !p.R) {
             uint16_t* dst = static_cast<uint16_t*>(p.C) + off;
@@ -388,7 +392,7 @@ __device__ inline void store_row(const GemmParams& p, int bo, int bi, int row, i
         }
     }
     for (int c = 0; c < n; ++c)
-        if (col + c < p.N) store_out(p, bo, bi, row, col + c, v[c]);
+        if (col + c < p.N) store_out<SEG>(p, bo, bi, row, col + c, v[c]);
 }
 
 template <int AK, int R, int NT>
@@ -461,8 +465,11 @@ __device__ void ce_epilogue(const GemmParams& p, int row, int col0, const float*
     }
 }
 
-template <int AK, int BKIND, int TE, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm(const GemmParams p) {
+// One output tile of the generic GEMM: tile t (M-tile t % gy of N-tile
+// t / gy), grid row y = batch index * splits + split. GRP: a grouped
+// problem (no segments, batching or split), p a local copy.
+template <int AK, int BKIND, int TE, int BM, int BN, int WM, int WN, bool GRP = false>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, const int t, const int y) {
     constexpr int NT = (BM / WM) * (BN / WN) * 64;
     constexpr bool kNf4 = (BKIND == B_NF4_NT || BKIND == B_NF4_NN);
     __shared__ __align__(16) uint16_t As[2][BM * BKP];
@@ -471,14 +478,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm(const GemmP
     const int tid = threadIdx.x;
     if (kNf4 && tid < 16) lut[tid] = nf4_value(tid);
 
-    // tile order: the gy M-tiles of one N-tile are consecutive within an XCD
-    const int gx = (p.N + BN - 1) / BN, gy = (p.M + BM - 1) / BM;
-    const int ntile = gx * gy;
-    int t = blockIdx.x;
-    if (ntile % 8 == 0) t = (t % 8) * (ntile / 8) + t / 8;
+    const int gy = (p.M + BM - 1) / BM;
     const int m0 = (t % gy) * BM, n0 = (t / gy) * BN;
-    const int split = blockIdx.y % p.splits;
-    const int bz = blockIdx.y / p.splits;
+    const int split = y % p.splits;
+    const int bz = y / p.splits;
     const int bo = bz / p.zdiv, bi = bz % p.zdiv;
     if (p.causal == CAUSAL_SKIP_UPPER && n0 > m0 + BM - 1) return;  // tile strictly above the diagonal
 
@@ -486,7 +489,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm(const GemmP
     const uint16_t* Bd =
         static_cast<const uint16_t*>(p.B) + (kNf4 ? 0 : int64_t(bo) * p.b_so + int64_t(bi / p.b_grp) * p.b_si);
     if constexpr (BKIND == B_DENSE_NN)
-        if (p.seg_rows > 0) Bd += p.bseg[m0 / p.seg_rows];  // the segment's B columns
+        if (!GRP && p.seg_rows > 0) Bd += p.bseg[m0 / p.seg_rows];  // the segment's B columns
     const uint8_t* Bq = static_cast<const uint8_t*>(p.B);
 
     int kbeg = split * p.kchunk, kend = min(p.K, kbeg + p.kchunk);
@@ -586,13 +589,45 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm(const GemmP
                         if (col0 + c < p.N) dst[c] = src[c];
                 }
             } else {
-                store_row(p, bo, bi, row, col0, src, WN / 4);
+                store_row<!GRP>(p, bo, bi, row, col0, src, WN / 4);
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
+}
+
+template <int AK, int BKIND, int TE, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm(const GemmParams p) {
+    // tile order: the gy M-tiles of one N-tile are consecutive within an XCD
+    const int ntile = ((p.N + BN - 1) / BN) * ((p.M + BM - 1) / BM);
+    int t = blockIdx.x;
+    if (ntile % 8 == 0) t = (t % 8) * (ntile / 8) + t / 8;
+    gemm_tile<AK, BKIND, TE, BM, BN, WM, WN>(p, t, blockIdx.y);
+}
+
+// A group of independent products in one launch (no split, no batching):
+// workgroup b runs tile b - prob[i].tile0 of the problem i whose tile range
+// holds b; the problems share everything in base but operands, sizes, output
+// and alpha.
+template <int AK, int BKIND, int TE, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_group(const GemmParams base, const GemmGroup g) {
+    const int b = blockIdx.x;
+    int i = 0;
+    while (i + 1 < g.n && b >= g.prob[i + 1].tile0) ++i;
+    const GemmProb& q = g.prob[i];
+    GemmParams p = base;
+    p.A = q.A;
+    p.lda = q.lda;
+    p.B = q.B;
+    p.ldb = q.ldb;
+    p.C = q.C;
+    p.ldc = q.ldc;
+    p.M = q.M;
+    p.N = q.N;
+    p.alpha = q.alpha;
+    gemm_tile<AK, BKIND, TE, BM, BN, WM, WN, true>(p, b - q.tile0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1566,8 +1601,39 @@ static void dispatch(const GemmParams& p, int akind, int bkind, bool fast_ok, bo
     }
 }
 
-void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStream_t s) {
-    if (p.M <= 0 || p.N <= 0) return;
+void gemm_group_tn(GemmGroup g, int K, int te, const char* tag, hipStream_t s) {
+    QLX_REQUIRE(g.n >= 1 && g.n <= kGemmGroupMax && K >= 1, QLX_EINVAL, "gemm group: 1..16 problems, K >= 1");
+    constexpr int T = 64;  // 64 x 64 tiles on four 32 x 32 wavefronts
+    GemmParams p;
+    p.K = K;
+    p.kchunk = ((K + BK - 1) / BK) * BK;
+    p.splits = 1;
+    p.c_type = C_F32;
+    p.a_vec = p.b_vec = 1;
+    int total = 0;
+    double flops = 0, bytes = 0;
+    for (int i = 0; i < g.n; ++i) {
+        GemmProb& q = g.prob[i];
+        QLX_REQUIRE(q.M >= 1 && q.N >= 1 && q.A && q.B && q.C, QLX_EINVAL, "gemm group: empty problem");
+        p.a_vec &= aligned8(q.A) && q.lda % 4 == 0;
+        p.b_vec &= aligned8(q.B) && q.ldb % 4 == 0;
+        q.tile0 = total;
+        total += ((q.M + T - 1) / T) * ((q.N + T - 1) / T);
+        flops += 2.0 * q.M * q.N * K;
+        bytes += (double(q.M) + q.N) * K * 2 + double(q.M) * q.N * 4;
+    }
+    ProfScope prof(tag, flops, bytes, s);
+    if (te == TE_F16)
+        hipLaunchKernelGGL((k_gemm_group<A_TRANS, B_DENSE_NN, TE_F16, T, T, 32, 32>), dim3(total), dim3(256), 0, s, p,
+                           g);
+    else
+        hipLaunchKernelGGL((k_gemm_group<A_TRANS, B_DENSE_NN, TE_BF16, T, T, 32, 32>), dim3(total), dim3(256), 0, s,
+                           p, g);
+    check_launch("gemm group");
+}
+
+int gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStream_t s) {
+    if (p.M <= 0 || p.N <= 0) return 1;
     const bool nf4 = (bkind == B_NF4_NT || bkind == B_NF4_NN);
     QLX_REQUIRE(!(p.K2 > 0 && !nf4), QLX_EINVAL, "gemm: the LoRA slab rides only on NF4 GEMMs");
     QLX_REQUIRE(!p.ce_mode || (te == TE_F16 && akind == A_ROW && bkind == B_DENSE_NT && p.batch == 1 &&
@@ -1717,13 +1783,14 @@ void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStre
         else dispatch<TE_F16>(p, akind, bkind, fast_ok, dense_fast, shape, tc, tiles, bsz, s, prof);
         check_launch("gemm");
     }
-    if (p.splits > 1) {
+    if (p.splits > 1 && !p.defer_reduce) {
         const int64_t MN = int64_t(p.M) * p.N;
         ProfScope prof("splitk_reduce", double(MN) * p.splits, double(MN) * (4.0 * p.splits + cb + (p.R ? 4 : 0)), s);
         const int64_t threads = (p.N & 3) == 0 ? MN / 4 : MN;
         hipLaunchKernelGGL(k_splitk_reduce, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, p);
         check_launch("gemm splitk reduce");
     }
+    return p.splits;
 }
 
 }  // namespace qlx

@@ -39,7 +39,7 @@ struct LayerWs {
     float* rope_cs;
     bool rope_ready = false;  // host flag: rope_cs holds this geometry's table
     float* partial;
-    uint16_t *dy16, *dact, *dgu, *doattn, *dqkv;
+    uint16_t *dy16, *dy16o, *dact, *dgu, *doattn, *dqkv;  // dy16: down's output gradient, dy16o: o's
     uint16_t *du_d, *du_gu, *du_o, *du_qkv;
     float *dn2, *dh1, *dKh, *dVh, *dn1;
 };

@@ -172,7 +172,8 @@ LayerWs carve_layer(Carver& c, const LayerGeom& g) {
     w.rope_cs = c.take<float>(size_t(g.S) * g.hd);
     w.partial = c.take<float>(kGemmPartialFloats);
     // backward
-    w.dy16 = c.take<uint16_t>(T * std::max(H, size_t(g.qdim)));
+    w.dy16 = c.take<uint16_t>(T * H);
+    w.dy16o = c.take<uint16_t>(T * H);
     w.dact = c.take<uint16_t>(T * g.I);
     w.dgu = c.take<uint16_t>(T * 2 * g.I);
     w.doattn = c.take<uint16_t>(T * g.qdim);
@@ -229,6 +230,19 @@ static void out_f32(GemmParams& p, float* C, int64_t ldc) {
     p.C = C;
     p.ldc = ldc;
     p.c_type = C_F32;
+}
+
+static bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+static Partials partials(const float* p, int splits, int64_t mn, float alpha = 1.f, const float* R = nullptr,
+                         int64_t ldr = 0) {
+    Partials q;
+    q.p = p;
+    q.splits = splits;
+    q.mn = mn;
+    q.alpha = alpha;
+    q.R = R;
+    q.ldr = ldr;
+    return q;
 }
 
 static AttnArgs attn_args(const LayerGeom& g, LayerWs& w) {
@@ -303,9 +317,13 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
             p.slab_alg_k = r;  // block-diagonal: each output column sees one adapter
         }
         out16(p, w.qkv, g.nqkv, g);
-        gemm(p, A_ROW, B_NF4_NT, g.te, w.partial, s);
+        const int nall = g.nH + 2 * g.nKV;  // q and k heads are contiguous, then v
+        p.defer_reduce = rope_part_ok(g.hd, nall);
+        const int sp = gemm(p, A_ROW, B_NF4_NT, g.te, w.partial, s);
+        if (p.defer_reduce && sp > 1) launch_rope_part(partials(w.partial, sp, int64_t(T) * g.nqkv), w.qkv, T, g.S, g.nH + g.nKV, nall, g.hd,
+                                     w.rope_cs, g.f16, s);
+        else launch_rope(w.qkv, g.nqkv, T, g.S, 0, g.nH + g.nKV, g.hd, w.rope_cs, g.f16, s);
     }
-    launch_rope(w.qkv, g.nqkv, T, g.S, 0, g.nH + g.nKV, g.hd, w.rope_cs, g.f16, s);  // q and k heads are contiguous
     launch_flash_fwd(attn_args(g, w), s);
     if (U) {
         GemmParams pu = dense_gemm(T, r, g.qdim, w.oattn, g.qdim, w.A_o, g.qdim);
@@ -313,6 +331,7 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
         pu.tag = "gemm_lora_u";
         gemm(pu, A_ROW, B_DENSE_NT, g.te, w.partial, s);
     }
+    int sp_o;  // > 1: the o projection's partials wait for the norm (deferred)
     {  // h1 = h_in + o_proj(o)
         GemmParams p = nf4_gemm(T, H, g.qdim, w.oattn, g.qdim, wt.packed[3], wt.absmax[3], g.qdim);
         if (L) {
@@ -325,10 +344,16 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
         out_f32(p, w.h1, H);
         p.R = h_in;
         p.ldr = H;
-        gemm(p, A_ROW, B_NF4_NT, g.te, w.partial, s);
+        p.defer_reduce = rmsnorm_part_ok(H) && a16(h_in) && a16(wt.g2);
+        sp_o = gemm(p, A_ROW, B_NF4_NT, g.te, w.partial, s);
+        if (!p.defer_reduce) sp_o = 1;
     }
-    // MLP block
-    launch_rmsnorm_fwd(w.h1, wt.g2, T, H, g.eps, w.n2, g.f16, w.rstd2, s);
+    // MLP block (the o projection's split-K sum, + h_in, written to h1 by the norm when deferred)
+    if (sp_o > 1)
+        launch_rmsnorm_fwd_part(partials(w.partial, sp_o, int64_t(T) * H, 1.f, h_in, H), w.h1, wt.g2, T, H, g.eps, w.n2,
+                                g.f16, w.rstd2, s);
+    else
+        launch_rmsnorm_fwd(w.h1, wt.g2, T, H, g.eps, w.n2, g.f16, w.rstd2, s);
     if (U) {
         GemmParams pu = dense_gemm(T, 2 * r, H, w.n2, H, w.A_gu, H);
         out16(pu, w.u_gu, 2 * r, g);
@@ -371,63 +396,39 @@ void layer_forward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora,
     }
 }
 
-// dB = s * dy^T u  (M = out, N = r, K = T): dy [T, ld_dy] column slice, u [T, ld_u] slice.
-static void grad_B(const LayerGeom& g, const uint16_t* dy, int64_t ld_dy, int out, const uint16_t* u, int64_t ld_u,
-                   float* dB, LayerWs& w, hipStream_t s) {
-    GemmParams p = dense_gemm(out, g.r, g.T, dy, ld_dy, u, ld_u);
-    out_f32(p, dB, g.r);
-    p.alpha = g.s / g.gsc;  // dy holds gsc x the gradient
-    p.tag = "gemm_lora_dB";
-    gemm(p, A_TRANS, B_DENSE_NN, g.te, w.partial, s);
-}
-// dB of projections whose outputs are consecutive column blocks of dy, cut
-// into nseg segments of seg rows, in one product: segment i reads the r
-// columns of u from ucol[i] and writes its rows to dB[i]. Where a segment is
-// not a whole number of 128-row tiles (or there are more than 8), each
-// projection's product runs on its own: proj[j] = {first segment, segments}.
-static void grad_B_group(const LayerGeom& g, const uint16_t* dy, int64_t ld_dy, int seg, int nseg, const uint16_t* u,
-                         int64_t ld_u, const int* ucol, float* const* dB, LayerWs& w, hipStream_t s) {
-    bool one = seg % 128 == 0 && nseg <= 8;
-    for (int i = 0; i < nseg; ++i) one = one && ucol[i] % 4 == 0;
-    if (one) {
-        GemmParams p = dense_gemm(nseg * seg, g.r, g.T, dy, ld_dy, u, ld_u);
-        out_f32(p, dB[0], g.r);
-        p.seg_rows = seg;
-        for (int i = 0; i < nseg; ++i) {
-            p.Cseg[i] = dB[i];
-            p.bseg[i] = ucol[i];
-        }
-        p.alpha = g.s / g.gsc;
-        p.tag = "gemm_lora_dB";
-        gemm(p, A_TRANS, B_DENSE_NN, g.te, w.partial, s);
-        return;
+// The 14 LoRA weight gradients of one layer's backward, gathered while it
+// runs and computed in one launch at its end (each a product over the T
+// tokens: dB = s dy^T u, dA = du^T x, with dy and du holding gsc x the
+// gradient).
+struct LoraGradGroup {
+    GemmGroup g;
+    // dB of the projection whose output gradient is dy (column slice of a
+    // [T, ld_dy] buffer, out columns), u its r columns of a [T, ld_u] buffer
+    void dB(const LayerGeom& L, const uint16_t* dy, int64_t ld_dy, int out, const uint16_t* u, int64_t ld_u,
+            float* C) {
+        GemmProb& q = g.prob[g.n++];
+        q.A = dy, q.lda = ld_dy, q.M = out;
+        q.B = u, q.ldb = ld_u, q.N = L.r;
+        q.C = C, q.ldc = L.r;
+        q.alpha = L.s / L.gsc;
     }
-    for (int i = 0; i < nseg;) {  // runs of segments with the same u columns are one projection
-        int j = i + 1;
-        while (j < nseg && ucol[j] == ucol[i] && dB[j] == dB[j - 1] + int64_t(seg) * g.r) ++j;
-        grad_B(g, dy + int64_t(i) * seg, ld_dy, (j - i) * seg, u + ucol[i], ld_u, dB[i], w, s);
-        i = j;
+    // dA from du (r columns of a [T, ld_du] buffer) and the projection's input x [T, in]
+    void dA(const LayerGeom& L, const uint16_t* du, int64_t ld_du, const uint16_t* x, int in, float* C) {
+        GemmProb& q = g.prob[g.n++];
+        q.A = du, q.lda = ld_du, q.M = L.r;
+        q.B = x, q.ldb = in, q.N = in;
+        q.C = C, q.ldc = in;
+        q.alpha = 1.0f / L.gsc;
     }
-}
-// dA (stacked over nseg segments of r rows) = du^T x  (M = nseg*r, N = in, K = T).
-static void grad_A(const LayerGeom& g, const uint16_t* du, int nseg, const uint16_t* x, int in_f, float* const* dA,
-                   LayerWs& w, hipStream_t s) {
-    GemmParams p = dense_gemm(nseg * g.r, in_f, g.T, du, int64_t(nseg) * g.r, x, in_f);
-    p.c_type = C_F32;
-    p.ldc = in_f;
-    p.seg_rows = g.r;
-    for (int i = 0; i < nseg; ++i) p.Cseg[i] = dA[i];
-    p.C = dA[0];
-    p.alpha = 1.0f / g.gsc;  // du holds gsc x the gradient
-    p.tag = "gemm_lora_dA";
-    gemm(p, A_TRANS, B_DENSE_NN, g.te, w.partial, s);
-}
+};
 
 void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora, const float* h_in,
                     const float* dh_out, float* dh_in, const qlx_lora_grad* grads, LayerWs& w, hipStream_t s,
                     bool recompute, bool u_given) {
     const int T = g.T, H = g.H, r = g.r, S = g.S;
     if (recompute) layer_forward(g, wt, lora, false, h_in, nullptr, w, s, u_given);
+    LoraGradGroup lg;
+    int sp_o = 1;
 
     // ---- down projection: out = h1 + down(act)
     launch_f32_to_act(dh_out, int64_t(T) * H, w.dy16, g.f16, g.gsc, s);  // gradients scaled by gsc from here
@@ -447,11 +448,8 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
         out16(p, w.dact, g.I, g);
         gemm(p, A_ROW, B_NF4_NN, g.te, w.partial, s);
     }
-    grad_B(g, w.dy16, H, H, w.u_d, r, grads->dB[6], w, s);
-    {
-        float* dA[1] = {grads->dA[6]};
-        grad_A(g, w.du_d, 1, w.act, g.I, dA, w, s);
-    }
+    lg.dB(g, w.dy16, H, H, w.u_d, r, grads->dB[6]);
+    lg.dA(g, w.du_d, r, w.act, g.I, grads->dA[6]);
     // ---- SwiGLU and gate/up
     launch_swiglu_bwd(w.dact, w.gu, T, g.I, w.dgu, g.f16, s);
     {
@@ -469,45 +467,50 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
         p.ldb2 = H;
         out_f32(p, w.dn2, H);
         p.alpha = 1.0f / g.gsc;  // back to true gradients on the fp32 residual path
-        gemm(p, A_ROW, B_NF4_NN, g.te, w.partial, s);
+        p.defer_reduce = rmsnorm_part_ok(H) && a16(wt.g2) && a16(dh_out);
+        const int sp = gemm(p, A_ROW, B_NF4_NN, g.te, w.partial, s);
+        if (p.defer_reduce && sp > 1)
+            launch_rmsnorm_bwd_part(partials(w.partial, sp, int64_t(T) * H, p.alpha), w.h1, wt.g2, w.rstd2, dh_out, T, H,
+                                    w.dh1, s);
+        else
+            launch_rmsnorm_bwd(w.dn2, w.h1, wt.g2, w.rstd2, dh_out, T, H, w.dh1, s);
     }
-    {
-        const int ucol[2] = {0, r};
-        float* dB[2] = {grads->dB[4], grads->dB[5]};
-        grad_B_group(g, w.dgu, 2 * g.I, g.I, 2, w.u_gu, 2 * r, ucol, dB, w, s);
+    for (int j = 0; j < 2; ++j) {  // gate, up
+        lg.dB(g, w.dgu + int64_t(j) * g.I, 2 * g.I, g.I, w.u_gu + j * r, 2 * r, grads->dB[4 + j]);
+        lg.dA(g, w.du_gu + j * r, 2 * r, w.n2, H, grads->dA[4 + j]);
     }
-    {
-        float* dA[2] = {grads->dA[4], grads->dA[5]};
-        grad_A(g, w.du_gu, 2, w.n2, H, dA, w, s);
-    }
-    launch_rmsnorm_bwd(w.dn2, w.h1, wt.g2, w.rstd2, dh_out, T, H, w.dh1, s);
 
     // ---- o projection: h1 = h + o(oattn)
-    launch_f32_to_act(w.dh1, int64_t(T) * H, w.dy16, g.f16, g.gsc, s);
+    launch_f32_to_act(w.dh1, int64_t(T) * H, w.dy16o, g.f16, g.gsc, s);
     {
-        GemmParams p = dense_gemm(T, r, H, w.dy16, H, w.B_o, r);
+        GemmParams p = dense_gemm(T, r, H, w.dy16o, H, w.B_o, r);
         out16(p, w.du_o, r, g);
         p.tag = "gemm_lora_du";
         gemm(p, A_ROW, B_DENSE_NN, g.te, w.partial, s);
     }
     {
-        GemmParams p = nf4_gemm(T, g.qdim, H, w.dy16, H, wt.packed[3], wt.absmax[3], g.qdim);
+        GemmParams p = nf4_gemm(T, g.qdim, H, w.dy16o, H, wt.packed[3], wt.absmax[3], g.qdim);
         p.K2 = r;
         p.A2 = w.du_o;
         p.lda2 = r;
         p.B2 = w.A_o;
         p.ldb2 = g.qdim;
         out16(p, w.doattn, g.qdim, g);
-        gemm(p, A_ROW, B_NF4_NN, g.te, w.partial, s);
+        p.defer_reduce = 1;  // summed by the attention backward's first kernel
+        sp_o = gemm(p, A_ROW, B_NF4_NN, g.te, w.partial, s);
     }
-    grad_B(g, w.dy16, H, H, w.u_o, r, grads->dB[3], w, s);
-    {
-        float* dA[1] = {grads->dA[3]};
-        grad_A(g, w.du_o, 1, w.oattn, g.qdim, dA, w, s);
-    }
+    lg.dB(g, w.dy16o, H, H, w.u_o, r, grads->dB[3]);
+    lg.dA(g, w.du_o, r, w.oattn, g.qdim, grads->dA[3]);
 
     // ---- attention: dq into dqkv, per-head fp32 dK, dV summed over each group below
-    launch_flash_bwd(attn_args(g, w), s);
+    {
+        AttnArgs a = attn_args(g, w);
+        if (sp_o > 1) {
+            a.dO_part = partials(w.partial, sp_o, int64_t(T) * g.qdim);
+            a.dO_out = w.doattn;
+        }
+        launch_flash_bwd(a, s);
+    }
     launch_gqa_reduce(w.dKh, g.B, g.nH, g.nKV, S, g.hd, w.dqkv, g.nqkv, g.qdim, w.rope_cs, g.f16, s);  // dk, rotated back
     launch_gqa_reduce(w.dVh, g.B, g.nH, g.nKV, S, g.hd, w.dqkv, g.nqkv, g.qdim + g.kvdim, nullptr, g.f16, s);
 
@@ -527,28 +530,23 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
         p.ldb2 = H;
         out_f32(p, w.dn1, H);
         p.alpha = 1.0f / g.gsc;
-        gemm(p, A_ROW, B_NF4_NN, g.te, w.partial, s);
-        launch_rmsnorm_bwd(w.dn1, h_in, wt.g1, w.rstd1, w.dh1, T, H, dh_in, s);
+        p.defer_reduce = rmsnorm_part_ok(H) && a16(h_in) && a16(wt.g1) && a16(dh_in);
+        const int sp = gemm(p, A_ROW, B_NF4_NN, g.te, w.partial, s);
+        if (p.defer_reduce && sp > 1)
+            launch_rmsnorm_bwd_part(partials(w.partial, sp, int64_t(T) * H, p.alpha), h_in, wt.g1, w.rstd1, w.dh1, T, H,
+                                    dh_in, s);
+        else
+            launch_rmsnorm_bwd(w.dn1, h_in, wt.g1, w.rstd1, w.dh1, T, H, dh_in, s);
     }
-    {  // q as qdim / kvdim segments of kvdim rows, then k and v
-        const int nq = g.qdim / g.kvdim;
-        int ucol[8];
-        float* dB[8];
-        if (g.qdim % g.kvdim == 0 && nq + 2 <= 8) {
-            for (int i = 0; i < nq; ++i) ucol[i] = 0, dB[i] = grads->dB[0] + int64_t(i) * g.kvdim * r;
-            ucol[nq] = r, dB[nq] = grads->dB[1];
-            ucol[nq + 1] = 2 * r, dB[nq + 1] = grads->dB[2];
-            grad_B_group(g, w.dqkv, g.nqkv, g.kvdim, nq + 2, w.u_qkv, 3 * r, ucol, dB, w, s);
-        } else {
-            grad_B(g, w.dqkv, g.nqkv, g.qdim, w.u_qkv, 3 * r, grads->dB[0], w, s);
-            grad_B(g, w.dqkv + g.qdim, g.nqkv, g.kvdim, w.u_qkv + r, 3 * r, grads->dB[1], w, s);
-            grad_B(g, w.dqkv + g.qdim + g.kvdim, g.nqkv, g.kvdim, w.u_qkv + 2 * r, 3 * r, grads->dB[2], w, s);
+    // q, k, v: output columns [0, qdim), [qdim, qdim + kvdim), [qdim + kvdim, nqkv) of dqkv
+    {
+        const int col[3] = {0, g.qdim, g.qdim + g.kvdim}, out[3] = {g.qdim, g.kvdim, g.kvdim};
+        for (int j = 0; j < 3; ++j) {
+            lg.dB(g, w.dqkv + col[j], g.nqkv, out[j], w.u_qkv + j * r, 3 * r, grads->dB[j]);
+            lg.dA(g, w.du_qkv + j * r, 3 * r, w.n1, H, grads->dA[j]);
         }
     }
-    {
-        float* dA[3] = {grads->dA[0], grads->dA[1], grads->dA[2]};
-        grad_A(g, w.du_qkv, 3, w.n1, H, dA, w, s);
-    }
+    gemm_group_tn(lg.g, T, g.te, "gemm_lora_grads", s);
 }
 
 }  // namespace qlx

@@ -135,6 +135,10 @@ struct GemmParams {
     // any offset is non-zero, so no tile straddles two segments)
     int64_t bseg[8] = {};
     int causal = CAUSAL_NONE;
+    // 1: when the launcher splits K, it leaves the fp32 partials for the
+    // caller's next kernel to sum (no reduce pass, C not written); gemm()
+    // returns the split count either way
+    int defer_reduce = 0;
     int slab_alg_k = -1;  // algorithmic K of the slab for flop accounting (-1: K2)
     // LM-head cross-entropy epilogues (fp16 NT products on 64-wide wavefront
     // tiles, no split): ce_mode 1 writes, per row and per 64 columns, the max
@@ -157,7 +161,40 @@ struct GemmParams {
 
 // Floats of split-K scratch the launcher may use for any one GEMM.
 constexpr size_t kGemmPartialFloats = size_t(1024) * 128 * 128;
-void gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStream_t s);
+// Returns the number of K splits it ran (1: C written).
+int gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStream_t s);
+
+// Split-K partial sums left for a consumer kernel (GemmParams::defer_reduce):
+// element (row, col) of an [M, N] product is alpha * (p[0][i] + p[1][i] + ...
+// in split order) [+ R[row * ldr + col]], i = row * N + col, split s at p + s * mn.
+struct Partials {
+    const float* p = nullptr;
+    int splits = 0;
+    int64_t mn = 0;
+    float alpha = 1.f;
+    const float* R = nullptr;
+    int64_t ldr = 0;
+};
+
+// Independent products C_i[M_i, N_i] (fp32) = alpha_i * A_i^T . B_i over one
+// shared K, in one launch without a split: A_i [K][lda_i] and B_i [K][ldb_i]
+// 16-bit (the element type te), each problem's columns read from its own
+// pointers. tile0 is set by the launcher.
+struct GemmProb {
+    const uint16_t* A = nullptr;
+    const uint16_t* B = nullptr;
+    float* C = nullptr;
+    int64_t lda = 0, ldb = 0, ldc = 0;
+    int M = 0, N = 0;
+    float alpha = 1.f;
+    int tile0 = 0;
+};
+constexpr int kGemmGroupMax = 16;
+struct GemmGroup {
+    int n = 0;
+    GemmProb prob[kGemmGroupMax];
+};
+void gemm_group_tn(GemmGroup g, int K, int te, const char* tag, hipStream_t s);
 
 // ---------------------------------------------------------------- AdamW
 struct AdamTensor {
@@ -184,12 +221,26 @@ void launch_rmsnorm_fwd(const float* x, const float* g, int T, int H, float eps,
                         float* rstd, hipStream_t s);
 void launch_rmsnorm_bwd(const float* dy, const float* x, const float* g, const float* rstd, const float* dres,
                         int T, int H, float* dx, hipStream_t s);
+// The same two with the input (forward: x, also written to xout in fp32;
+// backward: dy) summed from split-K partials of an [T, H] product. Only where
+// rmsnorm_part_ok(H) holds (the launchers check it).
+bool rmsnorm_part_ok(int H);
+void launch_rmsnorm_fwd_part(const Partials& x, float* xout, const float* g, int T, int H, float eps, void* out,
+                             int out_f16, float* rstd, hipStream_t s);
+void launch_rmsnorm_bwd_part(const Partials& dy, const float* x, const float* g, const float* rstd, const float* dres,
+                             int T, int H, float* dx, hipStream_t s);
 void launch_rope_table(int seq, int hd, float theta, float* cs, hipStream_t s);
 // Rotates pairs (j, j + hd/2) of nheads heads in columns [col0, col0 + nheads*hd)
 // of a bf16 [T, ld] buffer in place; row t has position t % seq.
 // 16-bit activations below are bf16, or fp16 when f16 != 0.
 void launch_rope(uint16_t* buf, int64_t ld, int T, int seq, int col0, int nheads, int hd, const float* cs, int f16,
                  hipStream_t s);
+// Sums split-K partials of an [T, nall * hd] product into the 16-bit buf
+// (row stride nall * hd), rotating heads [0, nrot) as launch_rope does and
+// copying the rest. Only where rope_part_ok(hd, nall) holds.
+bool rope_part_ok(int hd, int nall);
+void launch_rope_part(const Partials& src, uint16_t* buf, int T, int seq, int nrot, int nall, int hd, const float* cs,
+                      int f16, hipStream_t s);
 void launch_swiglu_fwd(const uint16_t* gu, int T, int I, uint16_t* act, int f16, hipStream_t s);
 void launch_swiglu_bwd(const uint16_t* dact, const uint16_t* gu, int T, int I, uint16_t* dgu, int f16, hipStream_t s);
 void launch_embed(const int32_t* tok, const uint16_t* E, int T, int H, int V, float* h, hipStream_t s);
@@ -219,6 +270,11 @@ struct AttnArgs {
     int64_t lddq = 0;
     const float2* rope = nullptr;             // [S, hd/2] (cos, sin): dq rotated back before its store
     int f16 = 0;                              // 16-bit operands: 0 bf16, 1 fp16
+    // backward: when dO_part.p is set, dO is first formed from these split-K
+    // partials of [B*S, qdim] (rounded to 16 bits, written to dO_out, row
+    // stride ldo) by the kernel that computes Dq
+    Partials dO_part;
+    uint16_t* dO_out = nullptr;
 };
 void launch_flash_fwd(const AttnArgs& a, hipStream_t s);
 void launch_flash_bwd(const AttnArgs& a, hipStream_t s);
