@@ -118,10 +118,16 @@ __global__ __launch_bounds__(256) void k_rmsnorm_fwd_v(const float* __restrict__
                     : make_uint2(f32x2_to_bf16x2(y0, y1), f32x2_to_bf16x2(y2, y3));
     }
 }
+// out16 (optional): also writes 16-bit(dx * sc), 8-byte stores
+__device__ inline void store_act4(uint16_t* out16, int64_t i, const float4& v, float sc, int f16) {
+    *reinterpret_cast<uint2*>(out16 + i) =
+        make_uint2(f32x2_to_act2(v.x * sc, v.y * sc, f16), f32x2_to_act2(v.z * sc, v.w * sc, f16));
+}
 template <int NV>
 __global__ __launch_bounds__(256) void k_rmsnorm_bwd_v(const float* __restrict__ dy, const float* __restrict__ x,
                                                        const float* __restrict__ g, const float* __restrict__ rstd,
-                                                       const float* __restrict__ dres, int H, float* __restrict__ dx) {
+                                                       const float* __restrict__ dres, int H, float* __restrict__ dx,
+                                                       uint16_t* __restrict__ out16, float sc, int f16) {
     __shared__ float red[4];
     const int64_t row = blockIdx.x;
     const float4* dyr = reinterpret_cast<const float4*>(dy + row * H);
@@ -152,6 +158,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd_v(const float* __restrict__
             v.w += q.w;
         }
         o[threadIdx.x + 256 * k] = v;
+        if (out16) store_act4(out16, row * H + 4 * (threadIdx.x + 256 * k), v, sc, f16);
     }
 }
 // The vector kernels above with the input row summed from split-K partials
@@ -188,7 +195,8 @@ __global__ __launch_bounds__(256) void k_rmsnorm_fwd_p(const Partials q, float* 
 template <int NV>
 __global__ __launch_bounds__(256) void k_rmsnorm_bwd_p(const Partials q, const float* __restrict__ x,
                                                        const float* __restrict__ g, const float* __restrict__ rstd,
-                                                       const float* __restrict__ dres, int H, float* __restrict__ dx) {
+                                                       const float* __restrict__ dres, int H, float* __restrict__ dx,
+                                                       uint16_t* __restrict__ out16, float sc, int f16) {
     __shared__ float red[4];
     const int64_t row = blockIdx.x;
     const float4* xr = reinterpret_cast<const float4*>(x + row * H);
@@ -219,6 +227,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd_p(const Partials q, const f
             v.w += q4.w;
         }
         o[threadIdx.x + 256 * k] = v;
+        if (out16) store_act4(out16, row * H + 4 * (threadIdx.x + 256 * k), v, sc, f16);
     }
 }
 
@@ -243,20 +252,25 @@ void launch_rmsnorm_fwd(const float* x, const float* g, int T, int H, float eps,
     check_launch("rmsnorm_fwd");
 }
 void launch_rmsnorm_bwd(const float* dy, const float* x, const float* g, const float* rstd, const float* dres, int T,
-                        int H, float* dx, hipStream_t s) {
+                        int H, float* dx, hipStream_t s, uint16_t* out16, float sc, int f16) {
     if (T <= 0) return;
-    ProfScope prof("rmsnorm_bwd", 8.0 * T * H, double(T) * H * (12.0 + (dres ? 4 : 0)), s);
-    if (rms_vec(H, dy, x, g, dres) && al16(dx)) {
-        switch (H / 1024) {
-            case 1: hipLaunchKernelGGL(k_rmsnorm_bwd_v<1>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx); break;
-            case 2: hipLaunchKernelGGL(k_rmsnorm_bwd_v<2>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx); break;
-            case 3: hipLaunchKernelGGL(k_rmsnorm_bwd_v<3>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx); break;
-            default: hipLaunchKernelGGL(k_rmsnorm_bwd_v<4>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx);
+    const bool vec = rms_vec(H, dy, x, g, dres) && al16(dx) && (!out16 || (reinterpret_cast<uintptr_t>(out16) & 7) == 0);
+    {
+        ProfScope prof("rmsnorm_bwd", 8.0 * T * H, double(T) * H * (12.0 + (dres ? 4 : 0) + (out16 && vec ? 2 : 0)), s);
+        uint16_t* o16 = vec ? out16 : nullptr;
+        if (vec) {
+            switch (H / 1024) {
+                case 1: hipLaunchKernelGGL(k_rmsnorm_bwd_v<1>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx, o16, sc, f16); break;
+                case 2: hipLaunchKernelGGL(k_rmsnorm_bwd_v<2>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx, o16, sc, f16); break;
+                case 3: hipLaunchKernelGGL(k_rmsnorm_bwd_v<3>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx, o16, sc, f16); break;
+                default: hipLaunchKernelGGL(k_rmsnorm_bwd_v<4>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx, o16, sc, f16);
+            }
+        } else {
+            hipLaunchKernelGGL(k_rmsnorm_bwd, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx);
         }
-    } else {
-        hipLaunchKernelGGL(k_rmsnorm_bwd, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx);
+        check_launch("rmsnorm_bwd");
     }
-    check_launch("rmsnorm_bwd");
+    if (out16 && !vec) launch_f32_to_act(dx, int64_t(T) * H, out16, f16, sc, s);
 }
 
 bool rmsnorm_part_ok(int H) { return H % 1024 == 0 && H >= 1024 && H <= 4096; }
@@ -281,18 +295,19 @@ void launch_rmsnorm_fwd_part(const Partials& x, float* xout, const float* g, int
     check_launch("rmsnorm_fwd (partials)");
 }
 void launch_rmsnorm_bwd_part(const Partials& dy, const float* x, const float* g, const float* rstd, const float* dres,
-                             int T, int H, float* dx, hipStream_t s) {
+                             int T, int H, float* dx, hipStream_t s, uint16_t* out16, float sc, int f16) {
     if (T <= 0) return;
-    QLX_REQUIRE(rmsnorm_part_ok(H) && al16(x) && al16(g) && al16(dx) && (!dres || al16(dres)) && !dy.R, QLX_EINVAL,
-                "rmsnorm_bwd (partials): needs H a multiple of 1024 up to 4096 and aligned rows");
+    QLX_REQUIRE(rmsnorm_part_ok(H) && al16(x) && al16(g) && al16(dx) && (!dres || al16(dres)) && !dy.R &&
+                    (reinterpret_cast<uintptr_t>(out16) & 7) == 0,
+                QLX_EINVAL, "rmsnorm_bwd (partials): needs H a multiple of 1024 up to 4096 and aligned rows");
     check_part(dy, int64_t(T) * H, "rmsnorm_bwd");
     ProfScope prof("reduce_rmsnorm_bwd", (dy.splits + 8.0) * T * H,
-                   double(T) * H * (4.0 * dy.splits + 8.0 + (dres ? 4 : 0)), s);
+                   double(T) * H * (4.0 * dy.splits + 8.0 + (dres ? 4 : 0) + (out16 ? 2 : 0)), s);
     switch (H / 1024) {
-        case 1: hipLaunchKernelGGL(k_rmsnorm_bwd_p<1>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx); break;
-        case 2: hipLaunchKernelGGL(k_rmsnorm_bwd_p<2>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx); break;
-        case 3: hipLaunchKernelGGL(k_rmsnorm_bwd_p<3>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx); break;
-        default: hipLaunchKernelGGL(k_rmsnorm_bwd_p<4>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx);
+        case 1: hipLaunchKernelGGL(k_rmsnorm_bwd_p<1>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx, out16, sc, f16); break;
+        case 2: hipLaunchKernelGGL(k_rmsnorm_bwd_p<2>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx, out16, sc, f16); break;
+        case 3: hipLaunchKernelGGL(k_rmsnorm_bwd_p<3>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx, out16, sc, f16); break;
+        default: hipLaunchKernelGGL(k_rmsnorm_bwd_p<4>, dim3(T), dim3(256), 0, s, dy, x, g, rstd, dres, H, dx, out16, sc, f16);
     }
     check_launch("rmsnorm_bwd (partials)");
 }

@@ -738,10 +738,10 @@ struct DmaPlan {
 // Codes of one chunk (LDS) -> bf16 tile [n][k] (LDS). lut2[b] (LDS address
 // 8 b) holds the code values of byte b's high nibble (the even element) and
 // low nibble.
+// t: the thread's slot, 0..511 (a 512-thread workgroup passes threadIdx.x)
 template <int BKIND, int TE>
 __device__ __forceinline__ void dequant(const char* __restrict__ raw, const char* __restrict__ sc,
-                                        const char* __restrict__ lds0, uint16_t* __restrict__ tile) {
-    const int t = threadIdx.x;
+                                        const char* __restrict__ lds0, uint16_t* __restrict__ tile, const int t) {
     const float* s = reinterpret_cast<const float*>(sc);
     auto lut = [&](uint32_t byte) { return *reinterpret_cast<const f2*>(lds0 + OFF_L + (byte << 3)); };
     if constexpr (BKIND == B_NF4_NT) {
@@ -915,14 +915,14 @@ __global__ __launch_bounds__(fast::NTH) void k_nf4_tile(const GemmParams p) {
     a_dma(1, 1);
     code_dma(2, 2);
     stage_sync<2 * NA + 2 * NR>();  // codes 0 (and the table) in LDS
-    dequant<BKIND, TE>(sr(0), ss(0), lds, sb(0));
+    dequant<BKIND, TE>(sr(0), ss(0), lds, sb(0), tid);
     stage_sync<NA + NR>();          // A 0, codes 1, bf16 0
     auto step = [&](int c, auto stage) {
         constexpr int S0 = decltype(stage)::value, S1 = (S0 + 1) % 3, S2 = (S0 + 2) % 3;
         a_dma(c + 2, S2);
         code_dma(c + 3, S0);
         mma<FI, FJ, TE>(reinterpret_cast<const uint16_t*>(sa(S0)), sb(S0), acc, wm * WM, wn * WN, lane);
-        dequant<BKIND, TE>(sr(S1), ss(S1), lds, sb(S1));
+        dequant<BKIND, TE>(sr(S1), ss(S1), lds, sb(S1), tid);
         stage_sync<NA + NR>();      // A c+1, codes c+2, bf16 c+1
     };
     for (int c = 0; c < nch; c += 3) {
@@ -936,6 +936,193 @@ __global__ __launch_bounds__(fast::NTH) void k_nf4_tile(const GemmParams p) {
         slab<BKIND, BM, BN, TE>(p, reinterpret_cast<uint16_t*>(sa(0)), sb(0), acc, m0, n0, wm * WM, wn * WN, lane);
     epilogue<FI, WN>(p, acc, reinterpret_cast<float*>(lds + OFF_A) + wave * (16 * (WN + 4)), m0 + wm * WM,
                      n0 + wn * WN, split, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Warp-specialized full-tile NF4 kernel: the 256 x 128 tile of k_nf4_tile
+// with its two kinds of work on different wavefronts. Eight MFMA wavefronts
+// (4 x 2, 64 x 64 each, two per SIMD) only read fragments and issue MFMAs;
+// four producer wavefronts (one per SIMD) issue every DMA of the tile and
+// dequantize the next chunk's codes into the bf16/fp16 tile. Each SIMD so
+// always has a wavefront with MFMAs ready beside the one doing LDS lookups
+// and conversions, and the MFMA wavefronts never wait on the dequantization
+// chain. One workgroup barrier per 64-wide chunk publishes A (two chunks
+// ahead), the codes (three ahead) and the converted tile (one ahead, two LDS
+// stages). Same operand values, order of MFMAs and epilogue as k_nf4_tile,
+// so the results are bit-identical to it.
+namespace ws {
+constexpr int BM = 256, BN = 128, NMW = 8, NPW = 4, NTH = (NMW + NPW) * 64, WGN = 2, WM = 64, WN = 64;
+constexpr int FI = WM / 16, FJ = WN / 16;
+constexpr int SA = BM * 64 * 2, SB = BN * 64 * 2, SR = BN * 32, SS = 512;
+constexpr int OFF_L = 0, OFF_A = 256 * 8, OFF_B = OFF_A + 3 * SA, OFF_R = OFF_B + 2 * SB, OFF_S = OFF_R + 3 * SR;
+constexpr int LDS_BYTES = OFF_S + 3 * SS;
+static_assert(LDS_BYTES <= 160 * 1024, "warp-specialized NF4 tile exceeds LDS");
+static_assert(OFF_L == fast::OFF_L, "the dequantization reads the table at the fast tile's offset");
+constexpr int NA = BM / 8 / NPW;  // 16-byte A DMAs per producer lane per chunk
+constexpr int NR = 4;             // code (2) + absmax (2) DMAs per producer lane per chunk
+
+// The producers' DMA offsets: the A tile in 1 KB blocks (8 rows x 128 B, the
+// swizzled layout of k_nf4_tile), then the codes in 16-byte slots q (256 per
+// chunk: NT row q >> 1, NN k-row q >> 2) and the maxima in 4-byte slots qs
+// (128 per chunk). pw = producer wavefront 0..3.
+template <int BKIND>
+struct DmaPlanP {
+    uint32_t a[NA];
+    uint32_t code[2], scale[2];
+    int pw;
+    __amdgpu_buffer_rsrc_t ra, rc, rs;
+    __device__ __forceinline__ void init(const void* a0, const void* c0, const void* s0, int64_t lda, int64_t cols,
+                                         int pw_) {
+        const int lane = threadIdx.x & 63;
+        pw = pw_;
+        ra = fast::rsrc(a0);
+        rc = fast::rsrc(c0);
+        rs = fast::rsrc(s0);
+#pragma unroll
+        for (int u = 0; u < NA; ++u) {
+            const int r = (pw * NA + u) * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ ((r >> 1) & 7);
+            a[u] = uint32_t((int64_t(r) * lda + c * 8) * 2);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int q = pw * 64 + j * 32 + (lane & 31), qs = pw * 32 + j * 16 + (lane & 15);
+            if constexpr (BKIND == B_NF4_NN) {
+                code[j] = uint32_t(int64_t(q >> 2) * (cols >> 1) + (q & 3) * 16);
+                scale[j] = uint32_t((int64_t(qs >> 1) * (cols >> 6) + (qs & 1)) * 4);
+            } else {
+                code[j] = uint32_t(int64_t(q >> 1) * (cols >> 1) + (q & 1) * 16);
+                scale[j] = uint32_t(int64_t(qs) * (cols >> 6) * 4);
+            }
+        }
+    }
+    __device__ __forceinline__ void a_dma(uint32_t soff, char* __restrict__ dst) const {
+#pragma unroll
+        for (int u = 0; u < NA; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, fast::as_lds(dst + (pw * NA + u) * 1024), 16, a[u], soff, 0, 0);
+    }
+    __device__ __forceinline__ void code_dma(uint32_t coff, uint32_t soff, char* __restrict__ raw,
+                                             char* __restrict__ sc) const {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (lane < 32)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, fast::as_lds(raw + (pw * 64 + j * 32) * 16), 16, code[j],
+                                                         coff, 0, 0);
+            if (lane < 16)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, fast::as_lds(sc + (pw * 32 + j * 16) * 4), 4, scale[j],
+                                                         soff, 0, 0);
+        }
+    }
+};
+
+// LoRA slab (last split): the MFMA wavefronts stage A2 / B2 and multiply; the
+// producers only keep the barriers.
+template <int BKIND, int TE>
+__device__ __forceinline__ void slab(const GemmParams& p, bool mw, uint16_t* As, uint16_t* Bs,
+                                     f32x4 (&acc)[FI][FJ], int m0, int n0, int rm, int rn, int lane) {
+    for (int k0 = 0; k0 < p.K2; k0 += 64) {
+        if (mw) {
+            RowLoader<BM, NMW * 64, true> la;
+            la.load(p.A2, p.lda2, m0, k0, p.M, p.K2, p.a2_vec);
+            if constexpr (BKIND == B_NF4_NT) {
+                RowLoader<BN, NMW * 64, true> lb;
+                lb.load(p.B2, p.ldb2, n0, k0, p.N, p.K2, p.b2_vec);
+                lb.store(Bs);
+            } else {
+                TransLoader<BN, NMW * 64, true> lb;
+                lb.load(p.B2, p.ldb2, n0, k0, p.N, p.K2, p.b2_vec);
+                lb.store(Bs);
+            }
+            la.store(As);
+        }
+        __syncthreads();
+        if (mw) fast::mma<FI, FJ, TE>(As, Bs, acc, rm, rn, lane);
+        __syncthreads();
+    }
+}
+}  // namespace ws
+
+template <int BKIND, int TE>
+__global__ __launch_bounds__(ws::NTH) void k_nf4_ws(const GemmParams p) {
+    using namespace ws;
+    extern __shared__ __align__(16) char lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool mw = wave < NMW;  // MFMA wavefront (else producer)
+    const int wm = wave / WGN, wn = wave % WGN;
+    if (tid < 256) reinterpret_cast<fast::f2*>(lds + OFF_L)[tid] = fast::f2{nf4_value(tid >> 4), nf4_value(tid & 15)};
+
+    const int gx = p.N / BN, gy = p.M / BM;
+    const int ntile = gx * gy;
+    int t = blockIdx.x;
+    if (ntile % 8 == 0) t = (t % 8) * (ntile / 8) + t / 8;
+    const int m0 = (t / gx) * BM, n0 = (t % gx) * BN;
+    const int split = blockIdx.y;
+    const int kbeg = split * p.kchunk, kend = min(p.K, kbeg + p.kchunk);
+    const int nch = (kend - kbeg) / 64;
+    const int64_t cols = p.nf4_cols;
+
+    const int64_t flat0 = (BKIND == B_NF4_NN) ? int64_t(kbeg) * cols + n0 : int64_t(n0) * cols + kbeg;
+    DmaPlanP<BKIND> plan;
+    if (!mw)
+        plan.init(p.A + int64_t(m0) * p.lda + kbeg, static_cast<const char*>(p.B) + (flat0 >> 1),
+                  p.absmax + (flat0 >> 6), p.lda, cols, wave - NMW);
+    const uint32_t cstep = (BKIND == B_NF4_NN) ? uint32_t(32 * cols) : 32u;
+    const uint32_t sstep = (BKIND == B_NF4_NN) ? uint32_t(4 * cols) : 4u;
+
+    f32x4 acc[FI][FJ];
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto cl = [&](int c) { return min(c, nch - 1); };
+    auto sa = [&](int s) { return lds + OFF_A + s * SA; };
+    auto sb = [&](int s) { return reinterpret_cast<uint16_t*>(lds + OFF_B + s * SB); };
+    auto sr = [&](int s) { return lds + OFF_R + s * SR; };
+    auto ss = [&](int s) { return lds + OFF_S + s * SS; };
+    auto a_dma = [&](int c, int s) { plan.a_dma(uint32_t(cl(c)) * 128u, sa(s)); };
+    auto code_dma = [&](int c, int s) { plan.code_dma(uint32_t(cl(c)) * cstep, uint32_t(cl(c)) * sstep, sr(s), ss(s)); };
+    // the producers' 256 lanes dequantize as the 512 slots of k_nf4_tile, two each
+    const int pt = tid - NMW * 64;
+    auto dq = [&](int rs_, uint16_t* tile) {
+        fast::dequant<BKIND, TE>(sr(rs_), ss(rs_), lds, tile, pt);
+        fast::dequant<BKIND, TE>(sr(rs_), ss(rs_), lds, tile, pt + 256);
+    };
+    if (!mw) {
+        code_dma(0, 0);
+        a_dma(0, 0);
+        code_dma(1, 1);
+        a_dma(1, 1);
+        code_dma(2, 2);
+    }
+    fast::stage_sync<2 * NA + 2 * NR>();  // codes 0 (and the table) in LDS
+    if (!mw) dq(0, sb(0));
+    fast::stage_sync<NA + NR>();          // A 0, codes 1, converted 0
+    auto step = [&](int c, auto stage) {
+        constexpr int S0 = decltype(stage)::value, S1 = (S0 + 1) % 3, S2 = (S0 + 2) % 3;
+        if (mw) {
+            fast::mma<FI, FJ, TE>(reinterpret_cast<const uint16_t*>(sa(S0)), sb(c & 1), acc, wm * WM, wn * WN, lane);
+        } else {
+            a_dma(c + 2, S2);
+            code_dma(c + 3, S0);
+            dq(S1, sb((c + 1) & 1));
+        }
+        fast::stage_sync<NA + NR>();  // A c+1, codes c+2, converted c+1
+    };
+    for (int c = 0; c < nch; c += 3) {
+        step(c, std::integral_constant<int, 0>());
+        if (c + 1 < nch) step(c + 1, std::integral_constant<int, 1>());
+        if (c + 2 < nch) step(c + 2, std::integral_constant<int, 2>());
+    }
+    fast::stage_sync<0>();
+
+    if (p.K2 > 0 && split == p.splits - 1)  // LoRA slab, any K2 (zero-filled tail)
+        ws::slab<BKIND, TE>(p, mw, reinterpret_cast<uint16_t*>(sa(0)), sb(0), acc, m0, n0, wm * WM, wn * WN, lane);
+    if (mw)
+        fast::epilogue<FI, WN>(p, acc, reinterpret_cast<float*>(lds + OFF_A) + wave * (16 * (WN + 4)), m0 + wm * WM,
+                               n0 + wn * WN, split, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1527,6 +1714,13 @@ static void launch_fast(const GemmParams& p, int tiles, hipStream_t s, const Pro
                           prof.stop(), 0, p);
 }
 template <int BKIND, int TE>
+static void launch_ws(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {
+    static std::atomic<bool> allowed[64];
+    allow_lds(allowed, reinterpret_cast<const void*>(&k_nf4_ws<BKIND, TE>), ws::LDS_BYTES);
+    hipExtLaunchKernelGGL(k_nf4_ws<BKIND, TE>, dim3(tiles, p.splits), dim3(ws::NTH), ws::LDS_BYTES, s, prof.start(),
+                          prof.stop(), 0, p);
+}
+template <int BKIND, int TE>
 static void launch_wide(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {
     static std::atomic<bool> allowed[64];
     allow_lds(allowed, reinterpret_cast<const void*>(&k_nf4_wide<BKIND, TE>), wide::LDS_BYTES);
@@ -1556,6 +1750,11 @@ static bool aligned8(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 7
 constexpr double kTallUnit = 1.6;
 // QLX_NF4_TILE = 256x128 | 512x128 | 512x64 pins the full-tile NF4 shape
 // wherever it applies (for measurements); unset: chosen by the cost model.
+// QLX_NF4_WS=1: the 256 x 128 tile runs on the warp-specialized kernel
+static bool nf4_ws() {
+    const char* e = std::getenv("QLX_NF4_WS");
+    return e && e[0] == '1';
+}
 static int nf4_shape_override() {
     const char* e = std::getenv("QLX_NF4_TILE");
     if (!e) return -1;
@@ -1572,6 +1771,7 @@ static void dispatch(const GemmParams& p, int akind, int bkind, bool fast_ok, bo
             if (fast_ok)
                 shape == 2 ? launch_tall<B_NF4_NT, TE>(p, tiles, s, prof)
                 : shape == 1 ? launch_wide<B_NF4_NT, TE>(p, tiles, s, prof)
+                : nf4_ws()   ? launch_ws<B_NF4_NT, TE>(p, tiles, s, prof)
                              : launch_fast<B_NF4_NT, TE>(p, tiles, s, prof);
             else
                 launch_kind<A_ROW, B_NF4_NT, TE>(p, tc, bsz, s);
@@ -1580,6 +1780,7 @@ static void dispatch(const GemmParams& p, int akind, int bkind, bool fast_ok, bo
             if (fast_ok)
                 shape == 2 ? launch_tall<B_NF4_NN, TE>(p, tiles, s, prof)
                 : shape == 1 ? launch_wide<B_NF4_NN, TE>(p, tiles, s, prof)
+                : nf4_ws()   ? launch_ws<B_NF4_NN, TE>(p, tiles, s, prof)
                              : launch_fast<B_NF4_NN, TE>(p, tiles, s, prof);
             else
                 launch_kind<A_ROW, B_NF4_NN, TE>(p, tc, bsz, s);

@@ -38,6 +38,9 @@ struct LayerWs {
     uint16_t *A_qkv, *B_qkv, *A_o, *B_o, *A_gu, *B_gu, *A_d, *B_d;
     float* rope_cs;
     bool rope_ready = false;  // host flag: rope_cs holds this geometry's table
+    // host flag: dy16 already holds 16-bit(gsc x this buffer) (written by the
+    // backward of the layer above, whose input gradient it is)
+    const float* dy16_src = nullptr;
     float* partial;
     uint16_t *dy16, *dy16o, *dact, *dgu, *doattn, *dqkv;  // dy16: down's output gradient, dy16o: o's
     uint16_t *du_d, *du_gu, *du_o, *du_qkv;

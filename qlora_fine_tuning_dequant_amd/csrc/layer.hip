@@ -431,7 +431,9 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
     int sp_o = 1;
 
     // ---- down projection: out = h1 + down(act)
-    launch_f32_to_act(dh_out, int64_t(T) * H, w.dy16, g.f16, g.gsc, s);  // gradients scaled by gsc from here
+    if (w.dy16_src != dh_out)  // gradients scaled by gsc from here
+        launch_f32_to_act(dh_out, int64_t(T) * H, w.dy16, g.f16, g.gsc, s);
+    w.dy16_src = nullptr;
     {
         GemmParams p = dense_gemm(T, r, H, w.dy16, H, w.B_d, r);
         out16(p, w.du_d, r, g);
@@ -469,11 +471,12 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
         p.alpha = 1.0f / g.gsc;  // back to true gradients on the fp32 residual path
         p.defer_reduce = rmsnorm_part_ok(H) && a16(wt.g2) && a16(dh_out);
         const int sp = gemm(p, A_ROW, B_NF4_NN, g.te, w.partial, s);
+        // dh1, and its 16-bit scaled copy: the o projection's output gradient
         if (p.defer_reduce && sp > 1)
             launch_rmsnorm_bwd_part(partials(w.partial, sp, int64_t(T) * H, p.alpha), w.h1, wt.g2, w.rstd2, dh_out, T, H,
-                                    w.dh1, s);
+                                    w.dh1, s, w.dy16o, g.gsc, g.f16);
         else
-            launch_rmsnorm_bwd(w.dn2, w.h1, wt.g2, w.rstd2, dh_out, T, H, w.dh1, s);
+            launch_rmsnorm_bwd(w.dn2, w.h1, wt.g2, w.rstd2, dh_out, T, H, w.dh1, s, w.dy16o, g.gsc, g.f16);
     }
     for (int j = 0; j < 2; ++j) {  // gate, up
         lg.dB(g, w.dgu + int64_t(j) * g.I, 2 * g.I, g.I, w.u_gu + j * r, 2 * r, grads->dB[4 + j]);
@@ -481,7 +484,6 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
     }
 
     // ---- o projection: h1 = h + o(oattn)
-    launch_f32_to_act(w.dh1, int64_t(T) * H, w.dy16o, g.f16, g.gsc, s);
     {
         GemmParams p = dense_gemm(T, r, H, w.dy16o, H, w.B_o, r);
         out16(p, w.du_o, r, g);
@@ -521,6 +523,15 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
         p.tag = "gemm_lora_du";
         gemm(p, A_ROW, B_DENSE_NN, g.te, w.partial, s);
     }
+    // q, k, v: output columns [0, qdim), [qdim, qdim + kvdim), [qdim + kvdim, nqkv) of dqkv
+    {
+        const int col[3] = {0, g.qdim, g.qdim + g.kvdim}, out[3] = {g.qdim, g.kvdim, g.kvdim};
+        for (int j = 0; j < 3; ++j) {
+            lg.dB(g, w.dqkv + col[j], g.nqkv, out[j], w.u_qkv + j * r, 3 * r, grads->dB[j]);
+            lg.dA(g, w.du_qkv + j * r, 3 * r, w.n1, H, grads->dA[j]);
+        }
+    }
+    gemm_group_tn(lg.g, T, g.te, "gemm_lora_grads", s);
     if (dh_in) {
         GemmParams p = nf4_gemm(T, H, g.nqkv, w.dqkv, g.nqkv, wt.packed[0], wt.absmax[0], H);
         p.K2 = 3 * r;
@@ -534,19 +545,11 @@ void layer_backward(const LayerGeom& g, const BlobPtrs& wt, const qlx_lora* lora
         const int sp = gemm(p, A_ROW, B_NF4_NN, g.te, w.partial, s);
         if (p.defer_reduce && sp > 1)
             launch_rmsnorm_bwd_part(partials(w.partial, sp, int64_t(T) * H, p.alpha), h_in, wt.g1, w.rstd1, w.dh1, T, H,
-                                    dh_in, s);
+                                    dh_in, s, w.dy16, g.gsc, g.f16);
         else
-            launch_rmsnorm_bwd(w.dn1, h_in, wt.g1, w.rstd1, w.dh1, T, H, dh_in, s);
+            launch_rmsnorm_bwd(w.dn1, h_in, wt.g1, w.rstd1, w.dh1, T, H, dh_in, s, w.dy16, g.gsc, g.f16);
+        w.dy16_src = dh_in;  // the layer below starts from dy16 as written here
     }
-    // q, k, v: output columns [0, qdim), [qdim, qdim + kvdim), [qdim + kvdim, nqkv) of dqkv
-    {
-        const int col[3] = {0, g.qdim, g.qdim + g.kvdim}, out[3] = {g.qdim, g.kvdim, g.kvdim};
-        for (int j = 0; j < 3; ++j) {
-            lg.dB(g, w.dqkv + col[j], g.nqkv, out[j], w.u_qkv + j * r, 3 * r, grads->dB[j]);
-            lg.dA(g, w.du_qkv + j * r, 3 * r, w.n1, H, grads->dA[j]);
-        }
-    }
-    gemm_group_tn(lg.g, T, g.te, "gemm_lora_grads", s);
 }
 
 }  // namespace qlx

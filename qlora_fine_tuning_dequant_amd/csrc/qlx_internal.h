@@ -219,8 +219,10 @@ void launch_adamw(const AdamTensor* ts, int n, const AdamScalars& c, hipStream_t
 // ---------------------------------------------------------------- elementwise
 void launch_rmsnorm_fwd(const float* x, const float* g, int T, int H, float eps, void* out, int out_f16,
                         float* rstd, hipStream_t s);
+// out16 (optional): also writes the 16-bit activation type (f16) of dx * sc
 void launch_rmsnorm_bwd(const float* dy, const float* x, const float* g, const float* rstd, const float* dres,
-                        int T, int H, float* dx, hipStream_t s);
+                        int T, int H, float* dx, hipStream_t s, uint16_t* out16 = nullptr, float sc = 1.f,
+                        int f16 = 0);
 // The same two with the input (forward: x, also written to xout in fp32;
 // backward: dy) summed from split-K partials of an [T, H] product. Only where
 // rmsnorm_part_ok(H) holds (the launchers check it).
@@ -228,7 +230,8 @@ bool rmsnorm_part_ok(int H);
 void launch_rmsnorm_fwd_part(const Partials& x, float* xout, const float* g, int T, int H, float eps, void* out,
                              int out_f16, float* rstd, hipStream_t s);
 void launch_rmsnorm_bwd_part(const Partials& dy, const float* x, const float* g, const float* rstd, const float* dres,
-                             int T, int H, float* dx, hipStream_t s);
+                             int T, int H, float* dx, hipStream_t s, uint16_t* out16 = nullptr, float sc = 1.f,
+                             int f16 = 0);
 void launch_rope_table(int seq, int hd, float theta, float* cs, hipStream_t s);
 // Rotates pairs (j, j + hd/2) of nheads heads in columns [col0, col0 + nheads*hd)
 // of a bf16 [T, ld] buffer in place; row t has position t % seq.
