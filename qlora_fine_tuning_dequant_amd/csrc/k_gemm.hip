@@ -1750,10 +1750,11 @@ static bool aligned8(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 7
 constexpr double kTallUnit = 1.6;
 // QLX_NF4_TILE = 256x128 | 512x128 | 512x64 pins the full-tile NF4 shape
 // wherever it applies (for measurements); unset: chosen by the cost model.
-// QLX_NF4_WS=1: the 256 x 128 tile runs on the warp-specialized kernel
+// The 256 x 128 tile runs on the warp-specialized kernel (2-3% faster in the
+// 8B-shaped steps, same bits); QLX_NF4_WS=0 selects k_nf4_tile instead
 static bool nf4_ws() {
     const char* e = std::getenv("QLX_NF4_WS");
-    return e && e[0] == '1';
+    return !(e && e[0] == '0');
 }
 static int nf4_shape_override() {
     const char* e = std::getenv("QLX_NF4_TILE");

@@ -272,3 +272,30 @@ def test_each_nf4_tile_operand_is_bf16_of_dequant(monkeypatch, tile):
     q.qlora_linear_bwd(bf16_dev(oracle.bf16_rne_bits(dyb)), bf16_dev(oracle.bf16_rne_bits(xb)), W, None, None, 1.0,
                        dx, None, None)
     assert np.array_equal(dx.view(torch.int16).cpu().numpy().view(np.uint16), oracle.bf16_rne_bits(Wd[jy, :]))
+
+
+# The 256 x 128 tile has two kernels: the warp-specialized one (default) and
+# k_nf4_tile (QLX_NF4_WS=0). Same operand values, MFMA order and epilogue, so
+# forward, dX and the LoRA gradients agree bit for bit, split or not.
+@pytest.mark.parametrize("T,in_f,out_f,r", [(512, 4096, 4096, 64), (2048, 4096, 6144, 64), (512, 14336, 4096, 64)])
+def test_warp_specialized_tile_equals_plain_tile(monkeypatch, T, in_f, out_f, r):
+    monkeypatch.setenv("QLX_NF4_TILE", "256x128")
+    seed = T + in_f + 3 * out_f
+    W = q.NF4Matrix.quantize(bf16_dev(_w_bits(out_f, in_f, seed)))
+    x = bf16_dev(synth.activations_bf16(seed, T, in_f, 0))
+    dy = bf16_dev(synth.activations_bf16(seed, T, out_f, 1))
+    g = np.random.default_rng(seed)
+    A = f32_dev((g.uniform(-1, 1, (r, in_f)) / np.sqrt(in_f)).astype(np.float32))
+    B = f32_dev((g.standard_normal((out_f, r)) * 0.05).astype(np.float32))
+    res = {}
+    for ws in ("1", "0"):
+        monkeypatch.setenv("QLX_NF4_WS", ws)
+        y = torch.empty(T, out_f, dtype=torch.bfloat16, device=DEV)
+        dx = torch.empty(T, in_f, dtype=torch.bfloat16, device=DEV)
+        dA = torch.empty(r, in_f, dtype=torch.float32, device=DEV)
+        dB = torch.empty(out_f, r, dtype=torch.float32, device=DEV)
+        q.qlora_linear_fwd(x, W, A, B, 0.25, y)
+        q.qlora_linear_bwd(dy, x, W, A, B, 0.25, dx, dA, dB)
+        res[ws] = (y, dx, dA, dB)
+    for a, b in zip(res["1"], res["0"]):
+        assert torch.equal(a, b)
