@@ -60,6 +60,10 @@ WORKLOADS = {
                     name="streamed SimPO step, 32-layer Llama-3.1-8B-shaped NF4 base + LoRA r64, 2 pairs x seq 512"),
     "kto8b": dict(kind="kto", batch=2, seq=512, prompt=128,
                   name="streamed KTO step, 32-layer Llama-3.1-8B-shaped NF4 base + LoRA r64, 2 pairs x seq 512"),
+    # one decoder layer alone (layer_fwd, then layer_bwd with its recomputed
+    # forward: the per-layer work of a streamed step), resident on the device
+    "layer8b": dict(kind="layer", batch=1, seq=512,
+                    name="one Llama-3.1-8B-shaped NF4 + LoRA r64 decoder layer, forward then backward, batch 1, seq 512"),
 }
 
 
@@ -426,6 +430,63 @@ def _overlap(a_iv, b_iv):
     return tot
 
 
+def layer_bench(q, args, wl) -> dict:
+    """One 8B-shaped decoder layer: layer_fwd then layer_bwd (which recomputes
+    the forward from h_in), resident, on seeded weights, LoRA and N(0, 1)
+    activations; tokens/s of the pair and the per-kernel table of one more
+    pass with events around every kernel."""
+    import dataclasses
+    import torch
+    import synth
+    B_ = q.binding
+    dev = "cuda:0"
+    act = B_.QLX_ACT_F16 if args.act == "f16" else B_.QLX_ACT_BF16
+    d = dataclasses.replace(synth.LLAMA8B, n_layers=1)
+    m, dev_blobs = build_model(q, d, SEED, want_device_blobs=True, act=act)
+    dims = B_.Dims.of(d, act)
+    batch, seq = wl["batch"], wl["seq"]
+    T = batch * seq
+    g = torch.Generator(device=dev).manual_seed(SEED)
+    h_in = torch.randn(T, d.hidden, device=dev, generator=g)
+    dh_out = torch.randn(T, d.hidden, device=dev, generator=g) / T
+    h_out, dh_in = torch.empty_like(h_in), torch.empty_like(h_in)
+    lora, grads = m.lora[0], q.LoraGrads(m.lora[0])
+    ws = B_.workspace(B_.layer_workspace_bytes(dims, batch, seq))
+
+    def step():
+        q.layer_fwd(dims, dev_blobs[0], lora, h_in, batch, seq, h_out, ws)
+        q.layer_bwd(dims, dev_blobs[0], lora, h_in, dh_out, batch, seq, dh_in, grads, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    B_.profile_begin()
+    step()
+    torch.cuda.synchronize()
+    prof = B_.profile_end()
+    gemm = {k: v for k, v in prof.items() if k.startswith("gemm")}
+    flops = sum(v["flops"] for v in gemm.values())
+    gms = sum(v["ms"] for v in gemm.values())
+    log(f"layer fwd+bwd: {1000 * elapsed / args.steps:.3f} ms, GEMMs {gms:.3f} ms at {flops / gms / 1e9:.0f} TFLOP/s")
+    return {"metric": "train tokens/s through one decoder layer (forward + backward)", "value":
+            round(T * args.steps / elapsed, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(1000 * elapsed / args.steps, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": args.act, "data": "synthetic",
+            "config": {"workload": wl["name"], "global_batch": batch, "seq_len": seq, "mode": "resident",
+                       "activations": args.act, "weight_operand": "bf16 of the NF4 value", "lora_r": d.lora_r},
+            "gpu_time": {"kernels_ms": round(sum(v["ms"] for v in prof.values()), 4), "gemm_ms": round(gms, 4),
+                         "gemm_TFLOP": round(flops / 1e12, 4), "gemm_TFLOPs_avg": round(flops / gms / 1e9, 1)},
+            "kernels": {k: {"launches": v["launches"], "ms": round(v["ms"], 4),
+                            "TFLOP/s": round(v["flops"] / max(v["ms"], 1e-9) / 1e9, 1),
+                            "GB/s": round(v["bytes"] / max(v["ms"], 1e-9) / 1e6, 1)}
+                        for k, v in sorted(prof.items(), key=lambda kv: -kv[1]["ms"])}}
+
+
 def rocpd_summary(path: str, top: int = 25) -> str:
     """Text summary of a rocprofv3 trace database (--kernel-trace and
     --memory-copy-trace): per-kernel dispatch statistics, and the layer
@@ -568,6 +629,9 @@ def main() -> int:
         print(json.dumps({"peaks": measure_peaks(q)}))
         return 0
     wl = WORKLOADS[args.workload]
+    if wl["kind"] == "layer":
+        print(json.dumps(layer_bench(q, args, wl)))
+        return 0
     d = synth.LLAMA8B
     dev = "cuda:0"
     torch.cuda.set_device(0)

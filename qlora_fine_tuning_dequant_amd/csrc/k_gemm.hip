@@ -37,6 +37,16 @@
 #include "nf4_codes.h"
 #include "qlx_internal.h"
 
+// producer wavefronts of the warp-specialized NF4 kernel (4 or 8), forward
+// (NT) and dX (NN): 8 run the forward 4-7% and the dX 3-9% faster than 4 on
+// the 8B shapes
+#ifndef QLX_WS_NPW_NT
+#define QLX_WS_NPW_NT 8
+#endif
+#ifndef QLX_WS_NPW_NN
+#define QLX_WS_NPW_NN 8
+#endif
+
 namespace qlx {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -465,6 +475,23 @@ __device__ void ce_epilogue(const GemmParams& p, int row, int col0, const float*
     }
 }
 
+// Workgroup b of a full-tile NF4 GEMM's 1-D grid of gx * gy * splits
+// workgroups -> (M-tile, N-tile, split): split b / (gx gy), and within a
+// split workgroups go to the 8 XCDs in turn (b % 8) with the gx N-tiles of
+// one M-tile on one XCD, so they share its activation rows in one L2. (An
+// order giving each XCD whole (M-tile, split) groups fetched 40% fewer bytes
+// from memory at 512 tokens but ran 1-3% slower.)
+struct TileIdx {
+    int m, n, split;
+};
+__device__ __forceinline__ TileIdx tile_of(int b, int gx, int gy, int splits) {
+    (void)splits;
+    const int ntile = gx * gy;
+    const int bt = b % ntile, sp = b / ntile;
+    const int t = (ntile % 8 == 0) ? (bt % 8) * (ntile / 8) + bt / 8 : bt;
+    return TileIdx{t / gx, t % gx, sp};
+}
+
 // One output tile of the generic GEMM: tile t (M-tile t % gy of N-tile
 // t / gy), grid row y = batch index * splits + split. GRP: a grouped
 // problem (no segments, batching or split), p a local copy.
@@ -875,12 +902,8 @@ __global__ __launch_bounds__(fast::NTH) void k_nf4_tile(const GemmParams p) {
     const int wm = wave / WGN, wn = wave % WGN;
     if (tid < 256) reinterpret_cast<f2*>(lds + OFF_L)[tid] = f2{nf4_value(tid >> 4), nf4_value(tid & 15)};
 
-    const int gx = p.N / BN, gy = p.M / BM;
-    const int ntile = gx * gy;
-    int t = blockIdx.x;
-    if (ntile % 8 == 0) t = (t % 8) * (ntile / 8) + t / 8;
-    const int m0 = (t / gx) * BM, n0 = (t % gx) * BN;  // the gx N-tiles of one M-tile together
-    const int split = blockIdx.y;
+    const TileIdx ti = tile_of(blockIdx.x, p.N / BN, p.M / BM, p.splits);
+    const int m0 = ti.m * BM, n0 = ti.n * BN, split = ti.split;
     const int kbeg = split * p.kchunk, kend = min(p.K, kbeg + p.kchunk);
     const int nch = (kend - kbeg) / 64;  // >= 1
     const int64_t cols = p.nf4_cols;
@@ -942,33 +965,43 @@ __global__ __launch_bounds__(fast::NTH) void k_nf4_tile(const GemmParams p) {
 // Warp-specialized full-tile NF4 kernel: the 256 x 128 tile of k_nf4_tile
 // with its two kinds of work on different wavefronts. Eight MFMA wavefronts
 // (4 x 2, 64 x 64 each, two per SIMD) only read fragments and issue MFMAs;
-// four producer wavefronts (one per SIMD) issue every DMA of the tile and
-// dequantize the next chunk's codes into the bf16/fp16 tile. Each SIMD so
-// always has a wavefront with MFMAs ready beside the one doing LDS lookups
-// and conversions, and the MFMA wavefronts never wait on the dequantization
-// chain. One workgroup barrier per 64-wide chunk publishes A (two chunks
+// NPW producer wavefronts (4 or 8: one or two per SIMD) issue every DMA of
+// the tile and dequantize the next chunk's codes into the bf16/fp16 tile.
+// Each SIMD so always has a wavefront with MFMAs ready beside one doing LDS
+// lookups and conversions, and the MFMA wavefronts never wait on the
+// dequantization chain. One workgroup barrier per 64-wide chunk publishes A (two chunks
 // ahead), the codes (three ahead) and the converted tile (one ahead, two LDS
 // stages). Same operand values, order of MFMAs and epilogue as k_nf4_tile,
 // so the results are bit-identical to it.
 namespace ws {
-constexpr int BM = 256, BN = 128, NMW = 8, NPW = 4, NTH = (NMW + NPW) * 64, WGN = 2, WM = 64, WN = 64;
+constexpr int BM = 256, BN = 128, NMW = 8, WGN = 2, WM = 64, WN = 64;
 constexpr int FI = WM / 16, FJ = WN / 16;
 constexpr int SA = BM * 64 * 2, SB = BN * 64 * 2, SR = BN * 32, SS = 512;
 constexpr int OFF_L = 0, OFF_A = 256 * 8, OFF_B = OFF_A + 3 * SA, OFF_R = OFF_B + 2 * SB, OFF_S = OFF_R + 3 * SR;
 constexpr int LDS_BYTES = OFF_S + 3 * SS;
 static_assert(LDS_BYTES <= 160 * 1024, "warp-specialized NF4 tile exceeds LDS");
 static_assert(OFF_L == fast::OFF_L, "the dequantization reads the table at the fast tile's offset");
-constexpr int NA = BM / 8 / NPW;  // 16-byte A DMAs per producer lane per chunk
-constexpr int NR = 4;             // code (2) + absmax (2) DMAs per producer lane per chunk
+// NPW producer wavefronts (4 or 8): per chunk each issues NA 16-byte A DMAs
+// and NC code + NC absmax DMAs, and dequantizes 512 / (64 NPW) slots per lane
+template <int NPW>
+struct Prod {
+    static_assert(NPW == 4 || NPW == 8, "4 or 8 producer wavefronts");
+    static constexpr int NTH = (NMW + NPW) * 64;
+    static constexpr int NA = BM / 8 / NPW;
+    static constexpr int NC = 8 / NPW;
+    static constexpr int NR = 2 * NC;
+    static constexpr int NDQ = 512 / (64 * NPW);
+};
 
 // The producers' DMA offsets: the A tile in 1 KB blocks (8 rows x 128 B, the
 // swizzled layout of k_nf4_tile), then the codes in 16-byte slots q (256 per
 // chunk: NT row q >> 1, NN k-row q >> 2) and the maxima in 4-byte slots qs
-// (128 per chunk). pw = producer wavefront 0..3.
-template <int BKIND>
+// (128 per chunk). pw = producer wavefront 0..NPW-1.
+template <int BKIND, int NPW>
 struct DmaPlanP {
+    static constexpr int NA = Prod<NPW>::NA, NC = Prod<NPW>::NC;
     uint32_t a[NA];
-    uint32_t code[2], scale[2];
+    uint32_t code[NC], scale[NC];
     int pw;
     __amdgpu_buffer_rsrc_t ra, rc, rs;
     __device__ __forceinline__ void init(const void* a0, const void* c0, const void* s0, int64_t lda, int64_t cols,
@@ -985,8 +1018,8 @@ struct DmaPlanP {
             a[u] = uint32_t((int64_t(r) * lda + c * 8) * 2);
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int q = pw * 64 + j * 32 + (lane & 31), qs = pw * 32 + j * 16 + (lane & 15);
+        for (int j = 0; j < NC; ++j) {
+            const int q = (pw * NC + j) * 32 + (lane & 31), qs = (pw * NC + j) * 16 + (lane & 15);
             if constexpr (BKIND == B_NF4_NN) {
                 code[j] = uint32_t(int64_t(q >> 2) * (cols >> 1) + (q & 3) * 16);
                 scale[j] = uint32_t((int64_t(qs >> 1) * (cols >> 6) + (qs & 1)) * 4);
@@ -1005,12 +1038,12 @@ struct DmaPlanP {
                                              char* __restrict__ sc) const {
         const int lane = threadIdx.x & 63;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NC; ++j) {
             if (lane < 32)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, fast::as_lds(raw + (pw * 64 + j * 32) * 16), 16, code[j],
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, fast::as_lds(raw + (pw * NC + j) * 32 * 16), 16, code[j],
                                                          coff, 0, 0);
             if (lane < 16)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, fast::as_lds(sc + (pw * 32 + j * 16) * 4), 4, scale[j],
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, fast::as_lds(sc + (pw * NC + j) * 16 * 4), 4, scale[j],
                                                          soff, 0, 0);
         }
     }
@@ -1030,9 +1063,14 @@ __device__ __forceinline__ void slab(const GemmParams& p, bool mw, uint16_t* As,
                 lb.load(p.B2, p.ldb2, n0, k0, p.N, p.K2, p.b2_vec);
                 lb.store(Bs);
             } else {
-                TransLoader<BN, NMW * 64, true> lb;
-                lb.load(p.B2, p.ldb2, n0, k0, p.N, p.K2, p.b2_vec);
-                lb.store(Bs);
+                // B2 is [K2][N]: one element at a time into the swizzled
+                // [n][k] tile (reads along n coalesce; few registers, so the
+                // accumulators need not leave them)
+                for (int e = threadIdx.x; e < BN * 64; e += NMW * 64) {
+                    const int k = e / BN, n = e % BN, gk = k0 + k, gn = n0 + n;
+                    Bs[tile_off<true>(n, k >> 3) + (k & 7)] = (gk < p.K2 && gn < p.N) ? p.B2[int64_t(gk) * p.ldb2 + gn]
+                                                                                      : uint16_t(0);
+                }
             }
             la.store(As);
         }
@@ -1043,9 +1081,10 @@ __device__ __forceinline__ void slab(const GemmParams& p, bool mw, uint16_t* As,
 }
 }  // namespace ws
 
-template <int BKIND, int TE>
-__global__ __launch_bounds__(ws::NTH) void k_nf4_ws(const GemmParams p) {
+template <int BKIND, int TE, int NPW>
+__global__ __launch_bounds__(ws::Prod<NPW>::NTH) void k_nf4_ws(const GemmParams p) {
     using namespace ws;
+    constexpr int NA = Prod<NPW>::NA, NR = Prod<NPW>::NR, NDQ = Prod<NPW>::NDQ;
     extern __shared__ __align__(16) char lds[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1053,76 +1092,86 @@ __global__ __launch_bounds__(ws::NTH) void k_nf4_ws(const GemmParams p) {
     const int wm = wave / WGN, wn = wave % WGN;
     if (tid < 256) reinterpret_cast<fast::f2*>(lds + OFF_L)[tid] = fast::f2{nf4_value(tid >> 4), nf4_value(tid & 15)};
 
-    const int gx = p.N / BN, gy = p.M / BM;
-    const int ntile = gx * gy;
-    int t = blockIdx.x;
-    if (ntile % 8 == 0) t = (t % 8) * (ntile / 8) + t / 8;
-    const int m0 = (t / gx) * BM, n0 = (t % gx) * BN;
-    const int split = blockIdx.y;
+    const TileIdx ti = tile_of(blockIdx.x, p.N / BN, p.M / BM, p.splits);
+    const int m0 = ti.m * BM, n0 = ti.n * BN, split = ti.split;
     const int kbeg = split * p.kchunk, kend = min(p.K, kbeg + p.kchunk);
     const int nch = (kend - kbeg) / 64;
     const int64_t cols = p.nf4_cols;
 
-    const int64_t flat0 = (BKIND == B_NF4_NN) ? int64_t(kbeg) * cols + n0 : int64_t(n0) * cols + kbeg;
-    DmaPlanP<BKIND> plan;
-    if (!mw)
-        plan.init(p.A + int64_t(m0) * p.lda + kbeg, static_cast<const char*>(p.B) + (flat0 >> 1),
-                  p.absmax + (flat0 >> 6), p.lda, cols, wave - NMW);
-    const uint32_t cstep = (BKIND == B_NF4_NN) ? uint32_t(32 * cols) : 32u;
-    const uint32_t sstep = (BKIND == B_NF4_NN) ? uint32_t(4 * cols) : 4u;
-
-    f32x4 acc[FI][FJ];
-#pragma unroll
-    for (int i = 0; i < FI; ++i)
-#pragma unroll
-        for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto cl = [&](int c) { return min(c, nch - 1); };
     auto sa = [&](int s) { return lds + OFF_A + s * SA; };
     auto sb = [&](int s) { return reinterpret_cast<uint16_t*>(lds + OFF_B + s * SB); };
     auto sr = [&](int s) { return lds + OFF_R + s * SR; };
     auto ss = [&](int s) { return lds + OFF_S + s * SS; };
-    auto a_dma = [&](int c, int s) { plan.a_dma(uint32_t(cl(c)) * 128u, sa(s)); };
-    auto code_dma = [&](int c, int s) { plan.code_dma(uint32_t(cl(c)) * cstep, uint32_t(cl(c)) * sstep, sr(s), ss(s)); };
-    // the producers' 256 lanes dequantize as the 512 slots of k_nf4_tile, two each
-    const int pt = tid - NMW * 64;
-    auto dq = [&](int rs_, uint16_t* tile) {
-        fast::dequant<BKIND, TE>(sr(rs_), ss(rs_), lds, tile, pt);
-        fast::dequant<BKIND, TE>(sr(rs_), ss(rs_), lds, tile, pt + 256);
-    };
-    if (!mw) {
+    const bool slab = p.K2 > 0 && split == p.splits - 1;  // LoRA slab, any K2 (zero-filled tail)
+    // The two roles run separate code with the same barriers in the same
+    // order, so neither keeps the other's registers live.
+    if (mw) {
+        f32x4 acc[FI][FJ];
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+#pragma unroll
+            for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        fast::stage_sync<0>();  // codes 0 (and the table) in LDS
+        fast::stage_sync<0>();  // A 0, codes 1, converted 0
+        auto step = [&](int c, auto stage) {
+            constexpr int S0 = decltype(stage)::value;
+            fast::mma<FI, FJ, TE>(reinterpret_cast<const uint16_t*>(sa(S0)), sb(c & 1), acc, wm * WM, wn * WN, lane);
+            fast::stage_sync<0>();  // A c+1, codes c+2, converted c+1
+        };
+        for (int c = 0; c < nch; c += 3) {
+            step(c, std::integral_constant<int, 0>());
+            if (c + 1 < nch) step(c + 1, std::integral_constant<int, 1>());
+            if (c + 2 < nch) step(c + 2, std::integral_constant<int, 2>());
+        }
+        fast::stage_sync<0>();
+        if (slab) ws::slab<BKIND, TE>(p, true, reinterpret_cast<uint16_t*>(sa(0)), sb(0), acc, m0, n0, wm * WM, wn * WN, lane);
+        fast::epilogue<FI, WN>(p, acc, reinterpret_cast<float*>(lds + OFF_A) + wave * (16 * (WN + 4)), m0 + wm * WM,
+                               n0 + wn * WN, split, lane);
+    } else {
+        const int64_t flat0 = (BKIND == B_NF4_NN) ? int64_t(kbeg) * cols + n0 : int64_t(n0) * cols + kbeg;
+        DmaPlanP<BKIND, NPW> plan;
+        plan.init(p.A + int64_t(m0) * p.lda + kbeg, static_cast<const char*>(p.B) + (flat0 >> 1),
+                  p.absmax + (flat0 >> 6), p.lda, cols, wave - NMW);
+        const uint32_t cstep = (BKIND == B_NF4_NN) ? uint32_t(32 * cols) : 32u;
+        const uint32_t sstep = (BKIND == B_NF4_NN) ? uint32_t(4 * cols) : 4u;
+        auto cl = [&](int c) { return min(c, nch - 1); };
+        auto a_dma = [&](int c, int s) { plan.a_dma(uint32_t(cl(c)) * 128u, sa(s)); };
+        auto code_dma = [&](int c, int s) {
+            plan.code_dma(uint32_t(cl(c)) * cstep, uint32_t(cl(c)) * sstep, sr(s), ss(s));
+        };
+        // the producers' lanes dequantize as the 512 slots of k_nf4_tile, NDQ each
+        const int pt = tid - NMW * 64;
+        auto dq = [&](int rs_, uint16_t* tile) {
+#pragma unroll
+            for (int j = 0; j < NDQ; ++j) fast::dequant<BKIND, TE>(sr(rs_), ss(rs_), lds, tile, pt + j * NPW * 64);
+        };
         code_dma(0, 0);
         a_dma(0, 0);
         code_dma(1, 1);
         a_dma(1, 1);
         code_dma(2, 2);
-    }
-    fast::stage_sync<2 * NA + 2 * NR>();  // codes 0 (and the table) in LDS
-    if (!mw) dq(0, sb(0));
-    fast::stage_sync<NA + NR>();          // A 0, codes 1, converted 0
-    auto step = [&](int c, auto stage) {
-        constexpr int S0 = decltype(stage)::value, S1 = (S0 + 1) % 3, S2 = (S0 + 2) % 3;
-        if (mw) {
-            fast::mma<FI, FJ, TE>(reinterpret_cast<const uint16_t*>(sa(S0)), sb(c & 1), acc, wm * WM, wn * WN, lane);
-        } else {
+        fast::stage_sync<2 * NA + 2 * NR>();  // codes 0 (and the table) in LDS
+        dq(0, sb(0));
+        fast::stage_sync<NA + NR>();          // A 0, codes 1, converted 0
+        auto step = [&](int c, auto stage) {
+            constexpr int S0 = decltype(stage)::value, S1 = (S0 + 1) % 3, S2 = (S0 + 2) % 3;
             a_dma(c + 2, S2);
             code_dma(c + 3, S0);
             dq(S1, sb((c + 1) & 1));
+            fast::stage_sync<NA + NR>();  // A c+1, codes c+2, converted c+1
+        };
+        for (int c = 0; c < nch; c += 3) {
+            step(c, std::integral_constant<int, 0>());
+            if (c + 1 < nch) step(c + 1, std::integral_constant<int, 1>());
+            if (c + 2 < nch) step(c + 2, std::integral_constant<int, 2>());
         }
-        fast::stage_sync<NA + NR>();  // A c+1, codes c+2, converted c+1
-    };
-    for (int c = 0; c < nch; c += 3) {
-        step(c, std::integral_constant<int, 0>());
-        if (c + 1 < nch) step(c + 1, std::integral_constant<int, 1>());
-        if (c + 2 < nch) step(c + 2, std::integral_constant<int, 2>());
+        fast::stage_sync<0>();
+        if (slab)  // the producers keep the slab's barriers
+            for (int k0 = 0; k0 < p.K2; k0 += 64) {
+                __syncthreads();
+                __syncthreads();
+            }
     }
-    fast::stage_sync<0>();
-
-    if (p.K2 > 0 && split == p.splits - 1)  // LoRA slab, any K2 (zero-filled tail)
-        ws::slab<BKIND, TE>(p, mw, reinterpret_cast<uint16_t*>(sa(0)), sb(0), acc, m0, n0, wm * WM, wn * WN, lane);
-    if (mw)
-        fast::epilogue<FI, WN>(p, acc, reinterpret_cast<float*>(lds + OFF_A) + wave * (16 * (WN + 4)), m0 + wm * WM,
-                               n0 + wn * WN, split, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1356,12 +1405,8 @@ __global__ __launch_bounds__(wide::NTH) void k_nf4_wide(const GemmParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
     if (tid < 256) reinterpret_cast<f2*>(lds + OFF_L)[tid] = f2{nf4_value(tid >> 4), nf4_value(tid & 15)};
-    const int gx = p.N / BN, gy = p.M / BM;
-    const int ntile = gx * gy;
-    int t = blockIdx.x;
-    if (ntile % 8 == 0) t = (t % 8) * (ntile / 8) + t / 8;
-    const int m0 = (t / gx) * BM, n0 = (t % gx) * BN;  // the gx N-tiles of one M-tile together
-    const int split = blockIdx.y;
+    const TileIdx ti = tile_of(blockIdx.x, p.N / BN, p.M / BM, p.splits);
+    const int m0 = ti.m * BM, n0 = ti.n * BN, split = ti.split;
     const int kbeg = split * p.kchunk, kend = min(p.K, kbeg + p.kchunk);
     const int nch = (kend - kbeg) / BKW;
     const int64_t cols = p.nf4_cols;
@@ -1553,12 +1598,8 @@ __global__ __launch_bounds__(tall::NTH) void k_nf4_tall(const GemmParams p) {
     float* lut = reinterpret_cast<float*>(lds + OFF_L);
     if (tid < 16) lut[tid] = nf4_value(tid);
 
-    const int gx = p.N / BN, gy = p.M / BM;
-    const int ntile = gx * gy;
-    int t = blockIdx.x;
-    if (ntile % 8 == 0) t = (t % 8) * (ntile / 8) + t / 8;
-    const int m0 = (t / gx) * BM, n0 = (t % gx) * BN;  // the gx N-tiles of one M-tile together
-    const int split = blockIdx.y;
+    const TileIdx ti = tile_of(blockIdx.x, p.N / BN, p.M / BM, p.splits);
+    const int m0 = ti.m * BM, n0 = ti.n * BN, split = ti.split;
     const int kbeg = split * p.kchunk, kend = min(p.K, kbeg + p.kchunk);
     const int nch = (kend - kbeg) / 64;  // >= 1
     const int64_t cols = p.nf4_cols;
@@ -1710,28 +1751,37 @@ template <int BKIND, int TE>
 static void launch_fast(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {
     static std::atomic<bool> allowed[64];
     allow_lds(allowed, reinterpret_cast<const void*>(&k_nf4_tile<BKIND, TE>), fast::LDS_BYTES);
-    hipExtLaunchKernelGGL(k_nf4_tile<BKIND, TE>, dim3(tiles, p.splits), dim3(fast::NTH), fast::LDS_BYTES, s, prof.start(),
+    hipExtLaunchKernelGGL(k_nf4_tile<BKIND, TE>, dim3(tiles * p.splits), dim3(fast::NTH), fast::LDS_BYTES, s, prof.start(),
                           prof.stop(), 0, p);
 }
+template <int BKIND>
+struct WsNpw {
+    static constexpr int v = BKIND == B_NF4_NT ? QLX_WS_NPW_NT : QLX_WS_NPW_NN;
+};
+// every (direction, element type) instance, named so both compiler passes emit it
+template __global__ void k_nf4_ws<B_NF4_NT, TE_BF16, WsNpw<B_NF4_NT>::v>(const GemmParams);
+template __global__ void k_nf4_ws<B_NF4_NT, TE_F16, WsNpw<B_NF4_NT>::v>(const GemmParams);
+template __global__ void k_nf4_ws<B_NF4_NN, TE_BF16, WsNpw<B_NF4_NN>::v>(const GemmParams);
+template __global__ void k_nf4_ws<B_NF4_NN, TE_F16, WsNpw<B_NF4_NN>::v>(const GemmParams);
 template <int BKIND, int TE>
 static void launch_ws(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {
     static std::atomic<bool> allowed[64];
-    allow_lds(allowed, reinterpret_cast<const void*>(&k_nf4_ws<BKIND, TE>), ws::LDS_BYTES);
-    hipExtLaunchKernelGGL(k_nf4_ws<BKIND, TE>, dim3(tiles, p.splits), dim3(ws::NTH), ws::LDS_BYTES, s, prof.start(),
-                          prof.stop(), 0, p);
+    allow_lds(allowed, reinterpret_cast<const void*>(&k_nf4_ws<BKIND, TE, WsNpw<BKIND>::v>), ws::LDS_BYTES);
+    hipExtLaunchKernelGGL((k_nf4_ws<BKIND, TE, WsNpw<BKIND>::v>), dim3(tiles * p.splits),
+                          dim3(ws::Prod<WsNpw<BKIND>::v>::NTH), ws::LDS_BYTES, s, prof.start(), prof.stop(), 0, p);
 }
 template <int BKIND, int TE>
 static void launch_wide(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {
     static std::atomic<bool> allowed[64];
     allow_lds(allowed, reinterpret_cast<const void*>(&k_nf4_wide<BKIND, TE>), wide::LDS_BYTES);
-    hipExtLaunchKernelGGL(k_nf4_wide<BKIND, TE>, dim3(tiles, p.splits), dim3(wide::NTH), wide::LDS_BYTES, s, prof.start(),
+    hipExtLaunchKernelGGL(k_nf4_wide<BKIND, TE>, dim3(tiles * p.splits), dim3(wide::NTH), wide::LDS_BYTES, s, prof.start(),
                           prof.stop(), 0, p);
 }
 template <int BKIND, int TE>
 static void launch_tall(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {
     static std::atomic<bool> allowed[64];
     allow_lds(allowed, reinterpret_cast<const void*>(&k_nf4_tall<BKIND, TE>), tall::LDS_BYTES);
-    hipExtLaunchKernelGGL(k_nf4_tall<BKIND, TE>, dim3(tiles, p.splits), dim3(tall::NTH), tall::LDS_BYTES, s, prof.start(),
+    hipExtLaunchKernelGGL(k_nf4_tall<BKIND, TE>, dim3(tiles * p.splits), dim3(tall::NTH), tall::LDS_BYTES, s, prof.start(),
                           prof.stop(), 0, p);
 }
 static void launch_dense(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {
@@ -1788,11 +1838,13 @@ static void dispatch(const GemmParams& p, int akind, int bkind, bool fast_ok, bo
             break;
         case A_ROW * 10 + B_DENSE_NT:
             if (dense_fast && TE == TE_F16) launch_dense(p, tiles, s, prof);
+            else if (tc.bm == 64 && tc.bn == 128) launch_cfg<A_ROW, B_DENSE_NT, TE, 64, 128, 32, 64>(p, bsz, s);
             else if (tc.bm == 64) launch_cfg<A_ROW, B_DENSE_NT, TE, 64, 64, 32, 32>(p, bsz, s);
             else launch_cfg<A_ROW, B_DENSE_NT, TE, 128, 128, 64, 64>(p, bsz, s);
             break;
         case A_ROW * 10 + B_DENSE_NN:
-            if (tc.bm == 64) launch_cfg<A_ROW, B_DENSE_NN, TE, 64, 64, 32, 32>(p, bsz, s);
+            if (tc.bm == 64 && tc.bn == 128) launch_cfg<A_ROW, B_DENSE_NN, TE, 64, 128, 32, 64>(p, bsz, s);
+            else if (tc.bm == 64) launch_cfg<A_ROW, B_DENSE_NN, TE, 64, 64, 32, 32>(p, bsz, s);
             else launch_cfg<A_ROW, B_DENSE_NN, TE, 128, 128, 64, 64>(p, bsz, s);
             break;
         case A_TRANS * 10 + B_DENSE_NN:
@@ -1878,7 +1930,7 @@ int gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStrea
                             int64_t(dense::BN) * p.ldb * 2 + int64_t(p.K) * 2 < (int64_t(1) << 31);
     const TileCfg tc = fast_ok ? TileCfg{fast::BM, fast::BN}
                        : dense_fast ? TileCfg{dense::BM, dense::BN}
-                       : skinny     ? TileCfg{64, 64}
+                       : skinny     ? TileCfg{64, (akind == A_ROW && p.N % 128 == 0) ? 128 : 64}
                                     : pick_tile(p, bkind);
     const int gx = (p.N + tc.bn - 1) / tc.bn, gy = (p.M + tc.bm - 1) / tc.bm;
     // split-K when the grid would leave CUs idle: shapes decide, nothing else
@@ -1928,7 +1980,9 @@ int gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStrea
         if (shape == 2) tiles = (p.M / tall::BM) * (p.N / tall::BN);
         } else if (skinny) {
         // measured on the 8B-shaped LoRA products: at least 512 workgroups
-        // (four fit a CU), at most 2048 of K per split, at least 256
+        // (four fit a CU), at most 2048 of K per split, at least 256; a
+        // product 128 (or a multiple) wide takes 64 x 128 tiles, so its
+        // long operand is read once rather than once per 64 columns
         if (partial_ws) {
             int sp = 1;
             while (sp < 16 && tiles * sp < 512) sp *= 2;

@@ -65,20 +65,30 @@ def oracle_lora(q_lora) -> dict:
     return {p: (to_np(q_lora.A[i]), to_np(q_lora.B[i])) for i, p in enumerate(PROJ_NAMES)}
 
 
-def run_sft(q, m, toks, mode, ctx=None):
-    """One stream_step_sft; returns (loss tensor, grads, stats)."""
+def run_sft(q, m, toks, mode, ctx=None, ws_fill=None):
+    """One stream_step_sft; returns (loss tensor, grads, stats). ws_fill: a
+    byte the workspace and the gradient outputs are filled with first."""
     B_ = q.binding
     d = m.dims
     ctx = ctx or q.Context(0)
     grads = [q.LoraGrads(l) for l in m.lora]
     loss = torch.empty(1, dtype=torch.float32, device=DEV)
     ws = B_.workspace(B_.step_workspace_bytes(d, 0, toks.shape[0], toks.shape[1]))
+    if ws_fill is not None:
+        _fill(ws, grads, ws_fill)
     q.stream_step_sft(ctx, m, torch.from_numpy(toks).to(DEV), mode, loss, grads, ws)
     stats = ctx.sync()
     return loss, grads, stats
 
 
-def run_dpo(q, m, ch, rj, prompt_len, beta, mode, sched, ctx=None):
+def _fill(ws, grads, byte):
+    ws.fill_(byte)
+    for g in grads:
+        for t in g.dA + g.dB:
+            t.view(torch.uint8).fill_(byte)
+
+
+def run_dpo(q, m, ch, rj, prompt_len, beta, mode, sched, ctx=None, ws_fill=None):
     """One stream_step_dpo; returns (loss, logps, grads, stats)."""
     B_ = q.binding
     d = m.dims
@@ -87,6 +97,8 @@ def run_dpo(q, m, ch, rj, prompt_len, beta, mode, sched, ctx=None):
     loss = torch.empty(1, dtype=torch.float32, device=DEV)
     logps = torch.empty(4 * ch.shape[0], dtype=torch.float32, device=DEV)
     ws = B_.workspace(B_.step_workspace_bytes(d, 1, ch.shape[0], ch.shape[1]))
+    if ws_fill is not None:
+        _fill(ws, grads, ws_fill)
     q.stream_step_dpo(ctx, m, torch.from_numpy(ch).to(DEV), torch.from_numpy(rj).to(DEV), prompt_len, beta, mode,
                       sched, loss, logps, grads, ws)
     stats = ctx.sync()
