@@ -1754,21 +1754,34 @@ static void launch_fast(const GemmParams& p, int tiles, hipStream_t s, const Pro
     hipExtLaunchKernelGGL(k_nf4_tile<BKIND, TE>, dim3(tiles * p.splits), dim3(fast::NTH), fast::LDS_BYTES, s, prof.start(),
                           prof.stop(), 0, p);
 }
-template <int BKIND>
-struct WsNpw {
-    static constexpr int v = BKIND == B_NF4_NT ? QLX_WS_NPW_NT : QLX_WS_NPW_NN;
-};
-// every (direction, element type) instance, named so both compiler passes emit it
-template __global__ void k_nf4_ws<B_NF4_NT, TE_BF16, WsNpw<B_NF4_NT>::v>(const GemmParams);
-template __global__ void k_nf4_ws<B_NF4_NT, TE_F16, WsNpw<B_NF4_NT>::v>(const GemmParams);
-template __global__ void k_nf4_ws<B_NF4_NN, TE_BF16, WsNpw<B_NF4_NN>::v>(const GemmParams);
-template __global__ void k_nf4_ws<B_NF4_NN, TE_F16, WsNpw<B_NF4_NN>::v>(const GemmParams);
+// every (direction, element type, producer count) instance, named so both
+// compiler passes emit it
+template __global__ void k_nf4_ws<B_NF4_NT, TE_BF16, 4>(const GemmParams);
+template __global__ void k_nf4_ws<B_NF4_NT, TE_F16, 4>(const GemmParams);
+template __global__ void k_nf4_ws<B_NF4_NN, TE_BF16, 4>(const GemmParams);
+template __global__ void k_nf4_ws<B_NF4_NN, TE_F16, 4>(const GemmParams);
+template __global__ void k_nf4_ws<B_NF4_NT, TE_BF16, 8>(const GemmParams);
+template __global__ void k_nf4_ws<B_NF4_NT, TE_F16, 8>(const GemmParams);
+template __global__ void k_nf4_ws<B_NF4_NN, TE_BF16, 8>(const GemmParams);
+template __global__ void k_nf4_ws<B_NF4_NN, TE_F16, 8>(const GemmParams);
+// QLX_WS_NPW_NT / QLX_WS_NPW_NN (4 or 8) in the environment override the
+// built-in producer counts, read per call
+static int ws_npw(int bkind) {
+    const char* e = std::getenv(bkind == B_NF4_NT ? "QLX_WS_NPW_NT" : "QLX_WS_NPW_NN");
+    if (e && (e[0] == '4' || e[0] == '8') && e[1] == 0) return e[0] - '0';
+    return bkind == B_NF4_NT ? QLX_WS_NPW_NT : QLX_WS_NPW_NN;
+}
+template <int BKIND, int TE, int NPW>
+static void launch_ws_n(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {
+    static std::atomic<bool> allowed[64];
+    allow_lds(allowed, reinterpret_cast<const void*>(&k_nf4_ws<BKIND, TE, NPW>), ws::LDS_BYTES);
+    hipExtLaunchKernelGGL((k_nf4_ws<BKIND, TE, NPW>), dim3(tiles * p.splits), dim3(ws::Prod<NPW>::NTH),
+                          ws::LDS_BYTES, s, prof.start(), prof.stop(), 0, p);
+}
 template <int BKIND, int TE>
 static void launch_ws(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {
-    static std::atomic<bool> allowed[64];
-    allow_lds(allowed, reinterpret_cast<const void*>(&k_nf4_ws<BKIND, TE, WsNpw<BKIND>::v>), ws::LDS_BYTES);
-    hipExtLaunchKernelGGL((k_nf4_ws<BKIND, TE, WsNpw<BKIND>::v>), dim3(tiles * p.splits),
-                          dim3(ws::Prod<WsNpw<BKIND>::v>::NTH), ws::LDS_BYTES, s, prof.start(), prof.stop(), 0, p);
+    if (ws_npw(BKIND) == 8) launch_ws_n<BKIND, TE, 8>(p, tiles, s, prof);
+    else launch_ws_n<BKIND, TE, 4>(p, tiles, s, prof);
 }
 template <int BKIND, int TE>
 static void launch_wide(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {

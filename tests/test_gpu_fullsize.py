@@ -185,3 +185,22 @@ def test_llama8b_width_dpo_zero_adapter_is_exactly_ln2(act):
     lp = to_np(logps)
     assert np.array_equal(lp[:4], lp[4:])
     assert loss.item() == float(np.float32(np.log(2.0)))
+
+
+def test_llama8b_width_steps_do_not_read_stale_workspace(wide2):
+    """SFT at 1 x 512 and DPO at 2 pairs x 512 on the 2-layer 8B-width model
+    (the split-K, fused-consumer and grouped-gradient paths) with the
+    workspace and the gradient outputs first filled with 0x00, then 0xFF
+    (NaN in every fp32 word), then 0x7F: bit-identical results, so no kernel
+    reads workspace it has not written in the same step."""
+    d, m, host, _, _ = wide2
+    toks = synth.tokens(5, 1, 512, d.vocab)
+    ch, rj = synth.dpo_pairs(5, 2, 512, 128, d.vocab)
+    sft = [run_sft(q, m.with_blobs(host), toks, B_.QLX_STREAMED, ws_fill=f) for f in (0x00, 0xFF, 0x7F)]
+    dpo = [run_dpo(q, m.with_blobs(host), ch, rj, 128, 0.1, B_.QLX_STREAMED, B_.QLX_DPO_REF_FUSED, ws_fill=f)
+           for f in (0x00, 0xFF, 0x7F)]
+    for l, g, _ in sft[1:]:
+        assert torch.equal(l, sft[0][0]) and same_grads(g, sft[0][1])
+    for l, lp, g, _ in dpo[1:]:
+        assert torch.equal(l, dpo[0][0]) and torch.equal(lp, dpo[0][1]) and same_grads(g, dpo[0][2])
+    assert torch.isfinite(sft[0][0]).all() and torch.isfinite(dpo[0][0]).all()
