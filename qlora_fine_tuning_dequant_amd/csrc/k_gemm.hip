@@ -810,7 +810,10 @@ __device__ __forceinline__ void dequant(const char* __restrict__ raw, const char
 // One 64-wide chunk of MFMAs for a (16 FI_) x (16 FJ_) wavefront tile. Row
 // (base + i*16 + lr) swizzles with (lr >> 1) & 7 only, so each K half has one
 // per-lane base.
-template <int FI_, int FJ_, int TE_ = TE_BF16>
+// TR: each accumulator holds its 16 x 16 block transposed (the MFMA takes the
+// B fragment as its first operand), so a lane ends with 4 consecutive
+// columns of one row instead of 4 rows of one column.
+template <int FI_, int FJ_, int TE_ = TE_BF16, bool TR = false>
 __device__ __forceinline__ void mma(const uint16_t* __restrict__ As, const uint16_t* __restrict__ Bs,
                                     f32x4 (&acc)[FI_][FJ_], int rm, int rn, int lane) {
     const int lr = lane & 15, lc = lane >> 4, sw = (lr >> 1) & 7;
@@ -827,7 +830,8 @@ __device__ __forceinline__ void mma(const uint16_t* __restrict__ As, const uint1
 #pragma unroll
         for (int i = 0; i < FI_; ++i)
 #pragma unroll
-            for (int j = 0; j < FJ_; ++j) acc[i][j] = mfma16<TE_>(a[i], b[j], acc[i][j]);
+            for (int j = 0; j < FJ_; ++j)
+                acc[i][j] = TR ? mfma16<TE_>(b[j], a[i], acc[i][j]) : mfma16<TE_>(a[i], b[j], acc[i][j]);
     }
 }
 
@@ -1171,6 +1175,355 @@ __global__ __launch_bounds__(ws::Prod<NPW>::NTH) void k_nf4_ws(const GemmParams 
                 __syncthreads();
                 __syncthreads();
             }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent form of k_nf4_ws: the same 256 x 128 tile, roles, LDS stages and
+// one barrier per 64-wide chunk, but one workgroup per CU for the whole
+// launch. Workgroup b takes tiles b, b + G, b + 2G, ... (G, the grid, is a
+// multiple of 8 whenever a workgroup takes more than one tile, so a tile runs
+// on the XCD a one-tile-per-workgroup launch gives it) and runs them as one
+// stream of chunks: a tile's K chunks, then on the last split its LoRA slab
+// chunks, whose A2 rows the producers fetch by DMA like A and whose B2 block
+// they load into the converted-tile stage. The producers' DMAs and
+// dequantization so run on into the next tile while the MFMA wavefronts
+// store the finished one, and the pipeline fills once per launch instead of
+// once per tile (fill, epilogue and workgroup turnover measured ~9 us per
+// tile of 64 chunks, ~12% of the 2048-row projections). The MFMAs accumulate
+// each 16 x 16 block transposed, so a lane holds 4 consecutive columns and
+// the epilogue stores 8 or 16 bytes at a time straight from the accumulators
+// (LDS staging would collide with the stages already filling). Operands,
+// products and output arithmetic are those of k_nf4_ws, and so are the bits. Takes K2 % 64 == 0 with 16-byte
+// aligned A2 and B2 rows, no output segments, residual or accumulation.
+namespace wsp {
+using ws::BM;
+using ws::BN;
+
+// A position in a workgroup's chunk stream. Past the last chunk the cursor
+// stays on it with done set, so clamped DMAs still read valid memory. The
+// tile's operand origins (chunk 0 of A, A2, the codes and the maxima) are
+// set when the cursor enters the tile; a chunk adds a scalar byte offset.
+template <int BKIND>
+struct Cursor {
+    int w, c;  // tile index; chunk in the tile: [0, nch) K chunks, then nsl slab chunks
+    int m0, n0, nch, nsl, split;
+    bool done;
+    const char *a0, *a20, *c0, *s0;
+    __device__ __forceinline__ void load(const GemmParams& p, int w_) {
+        const TileIdx ti = tile_of(w_, p.N / BN, p.M / BM, p.splits);
+        w = w_;
+        c = 0;
+        m0 = ti.m * BM;
+        n0 = ti.n * BN;
+        split = ti.split;
+        const int kbeg = split * p.kchunk;
+        nch = (min(p.K, kbeg + p.kchunk) - kbeg) / 64;
+        nsl = (p.K2 > 0 && split == p.splits - 1) ? p.K2 / 64 : 0;
+        done = false;
+        a0 = reinterpret_cast<const char*>(p.A + int64_t(m0) * p.lda + kbeg);
+        a20 = reinterpret_cast<const char*>(p.A2 + int64_t(m0) * p.lda2);
+        const int64_t flat = (BKIND == B_NF4_NN) ? int64_t(kbeg) * p.nf4_cols + n0 : int64_t(n0) * p.nf4_cols + kbeg;
+        c0 = static_cast<const char*>(p.B) + (flat >> 1);
+        s0 = reinterpret_cast<const char*>(p.absmax + (flat >> 6));
+    }
+    __device__ __forceinline__ void advance(const GemmParams& p, int G, int nitems) {
+        if (c + 1 < nch + nsl) ++c;
+        else if (w + G < nitems) load(p, w + G);
+        else done = true;
+    }
+    __device__ __forceinline__ bool slab() const { return c >= nch; }
+};
+
+// The producers' per-lane DMA offsets (bytes, fixed for the launch): the A
+// tile and the A2 slab rows in 1 KB blocks of the swizzled layout, the codes
+// and maxima as in k_nf4_ws. Each DMA is a buffer resource at the tile's
+// origin, a scalar chunk offset and the per-lane offset.
+template <int BKIND, int NPW>
+struct Plan {
+    static constexpr int NA = ws::Prod<NPW>::NA, NC = ws::Prod<NPW>::NC;
+    uint32_t a[NA], a2[NA];
+    uint32_t code[NC], scale[NC];
+    uint32_t cstep, sstep;  // bytes per K chunk of the codes and the maxima
+    int pw;
+    __device__ __forceinline__ void init(const GemmParams& p, int pw_) {
+        const int lane = threadIdx.x & 63;
+        pw = pw_;
+        const int64_t cols = p.nf4_cols;
+        cstep = (BKIND == B_NF4_NN) ? uint32_t(32 * cols) : 32u;
+        sstep = (BKIND == B_NF4_NN) ? uint32_t(4 * cols) : 4u;
+#pragma unroll
+        for (int u = 0; u < NA; ++u) {
+            const int r = (pw * NA + u) * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ ((r >> 1) & 7);
+            a[u] = uint32_t((int64_t(r) * p.lda + c * 8) * 2);
+            a2[u] = uint32_t((int64_t(r) * p.lda2 + c * 8) * 2);
+        }
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            const int q = (pw * NC + j) * 32 + (lane & 31), qs = (pw * NC + j) * 16 + (lane & 15);
+            if constexpr (BKIND == B_NF4_NN) {
+                code[j] = uint32_t(int64_t(q >> 2) * (cols >> 1) + (q & 3) * 16);
+                scale[j] = uint32_t((int64_t(qs >> 1) * (cols >> 6) + (qs & 1)) * 4);
+            } else {
+                code[j] = uint32_t(int64_t(q >> 1) * (cols >> 1) + (q & 1) * 16);
+                scale[j] = uint32_t(int64_t(qs) * (cols >> 6) * 4);
+            }
+        }
+    }
+    // A rows of the cursor's chunk (A2 rows for a slab chunk) -> A stage
+    __device__ __forceinline__ void a_dma(const Cursor<BKIND>& u, char* __restrict__ dst) const {
+        const bool sl = u.slab();
+        const auto r = fast::rsrc(sl ? u.a20 : u.a0);
+        const uint32_t soff = uint32_t(sl ? u.c - u.nch : u.c) * 128u;
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, fast::as_lds(dst + (pw * NA + i) * 1024), 16, sl ? a2[i] : a[i],
+                                                     soff, 0, 0);
+    }
+    // K chunk c of a tile whose origins the resources hold (the steps whose
+    // three chunks of lookahead stay in one tile)
+    __device__ __forceinline__ void a_dma_k(__amdgpu_buffer_rsrc_t r, int c, char* __restrict__ dst) const {
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, fast::as_lds(dst + (pw * NA + i) * 1024), 16, a[i],
+                                                     uint32_t(c) * 128u, 0, 0);
+    }
+    __device__ __forceinline__ void code_dma_k(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, int c,
+                                               char* __restrict__ raw, char* __restrict__ sc) const {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            if (lane < 32)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, fast::as_lds(raw + (pw * NC + j) * 32 * 16), 16, code[j],
+                                                         uint32_t(c) * cstep, 0, 0);
+            if (lane < 16)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, fast::as_lds(sc + (pw * NC + j) * 16 * 4), 4, scale[j],
+                                                         uint32_t(c) * sstep, 0, 0);
+        }
+    }
+    // codes and maxima of the cursor's K chunk (a slab chunk re-reads the
+    // tile's first K chunk: every step issues the same DMAs)
+    __device__ __forceinline__ void code_dma(const Cursor<BKIND>& u, char* __restrict__ raw,
+                                             char* __restrict__ sc) const {
+        const int lane = threadIdx.x & 63;
+        const uint32_t kc = uint32_t(u.slab() ? 0 : u.c);
+        const auto rc = fast::rsrc(u.c0);
+        const auto rs = fast::rsrc(u.s0);
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            if (lane < 32)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, fast::as_lds(raw + (pw * NC + j) * 32 * 16), 16, code[j],
+                                                         kc * cstep, 0, 0);
+            if (lane < 16)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, fast::as_lds(sc + (pw * NC + j) * 16 * 4), 4, scale[j],
+                                                         kc * sstep, 0, 0);
+        }
+    }
+};
+
+// The B2 block of a slab chunk (128 n x 64 k) for the converted-tile stage:
+// 1024 16-byte loads over the producer lanes. NT: B2 is [N][K2], lane rows
+// along n; NN: B2 is [K2][N], eight n of one k per load, written transposed.
+template <int BKIND, int NPW>
+struct SlabB {
+    static constexpr int NH = 1024 / (NPW * 64);  // 16-byte loads per producer lane
+    uint4 v[NH];
+    __device__ __forceinline__ void load(const GemmParams& p, const Cursor<BKIND>& u, int pt) {
+        const int s = u.c - u.nch;
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            const int idx = pt + h * NPW * 64;
+            if constexpr (BKIND == B_NF4_NT)
+                v[h] = *reinterpret_cast<const uint4*>(p.B2 + int64_t(u.n0 + (idx >> 3)) * p.ldb2 + s * 64 +
+                                                       (idx & 7) * 8);
+            else
+                v[h] = *reinterpret_cast<const uint4*>(p.B2 + int64_t(s * 64 + (idx >> 4)) * p.ldb2 + u.n0 +
+                                                       (idx & 15) * 8);
+        }
+    }
+    __device__ __forceinline__ void store(uint16_t* __restrict__ tile, int pt) const {
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            const int idx = pt + h * NPW * 64;
+            if constexpr (BKIND == B_NF4_NT) {
+                *reinterpret_cast<uint4*>(tile + tile_off<true>(idx >> 3, idx & 7)) = v[h];
+            } else {
+                const int k = idx >> 4, n = (idx & 15) * 8;
+                const uint32_t w[4] = {v[h].x, v[h].y, v[h].z, v[h].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    tile[tile_off<true>(n + e, k >> 3) + (k & 7)] = uint16_t(w[e >> 1] >> (16 * (e & 1)));
+            }
+        }
+    }
+};
+
+// Output of one 64 x 64 wavefront tile straight from transposed accumulators
+// (mma<..., true>): lane (r = lane & 15, q = lane >> 4) holds columns
+// 4q..4q+3 of row r of each 16 x 16 block, stored 16 bytes (fp32) or 8 bytes
+// (16-bit) at a time. The arithmetic is store_row's: fp32 partials as they
+// are; otherwise alpha times the sum, rounded to the output type (no
+// residual: its loads would stall the MFMA wavefronts between tiles).
+template <int FI_, int FJ_>
+__device__ __forceinline__ void epilogue(const GemmParams& p, const f32x4 (&acc)[FI_][FJ_], int row_b, int col_b,
+                                         int split) {
+    if (p.splits > 1 || p.c_type == C_F32) {
+        const bool part = p.splits > 1;
+        float* d = part ? p.partial + (int64_t(split) * p.M + row_b) * p.N + col_b
+                        : static_cast<float*>(p.C) + int64_t(row_b) * p.ldc + col_b;
+        const int64_t ld = part ? int64_t(p.N) : p.ldc;
+        const float al = part ? 1.f : p.alpha;
+#pragma unroll
+        for (int i = 0; i < FI_; ++i)
+#pragma unroll
+            for (int j = 0; j < FJ_; ++j) {
+                const f32x4 v = acc[i][j];
+                *reinterpret_cast<float4*>(d + int64_t(i * 16) * ld + j * 16) =
+                    part ? make_float4(v[0], v[1], v[2], v[3]) : make_float4(v[0] * al, v[1] * al, v[2] * al, v[3] * al);
+            }
+        return;
+    }
+    uint16_t* d = static_cast<uint16_t*>(p.C) + int64_t(row_b) * p.ldc + col_b;
+    const bool h = p.c_type == C_F16;
+    const float al = p.alpha;
+#pragma unroll
+    for (int i = 0; i < FI_; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ_; ++j) {
+            const f32x4 v = acc[i][j];
+            const float x0 = v[0] * al, x1 = v[1] * al, x2 = v[2] * al, x3 = v[3] * al;
+            *reinterpret_cast<uint2*>(d + int64_t(i * 16) * p.ldc + j * 16) =
+                h ? make_uint2(f32x2_to_f16x2(x0, x1), f32x2_to_f16x2(x2, x3))
+                  : make_uint2(f32x2_to_bf16x2(x0, x1), f32x2_to_bf16x2(x2, x3));
+        }
+}
+}  // namespace wsp
+
+template <int BKIND, int TE, int NPW>
+__global__ __launch_bounds__(ws::Prod<NPW>::NTH) void k_nf4_wsp(const GemmParams p, const int nitems) {
+    using namespace ws;
+    constexpr int NA = Prod<NPW>::NA, NR = Prod<NPW>::NR, NDQ = Prod<NPW>::NDQ;
+    extern __shared__ __align__(16) char lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool mw = wave < NMW;  // MFMA wavefront (else producer)
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int G = gridDim.x;
+    if (tid < 256) reinterpret_cast<fast::f2*>(lds + OFF_L)[tid] = fast::f2{nf4_value(tid >> 4), nf4_value(tid & 15)};
+
+    auto sa = [&](int s) { return lds + OFF_A + s * SA; };
+    auto sb = [&](int s) { return reinterpret_cast<uint16_t*>(lds + OFF_B + s * SB); };
+    auto sr = [&](int s) { return lds + OFF_R + s * SR; };
+    auto ss = [&](int s) { return lds + OFF_S + s * SS; };
+    // The two roles run separate code with the same barriers in the same
+    // order: two in the prologue, then one per chunk of the stream.
+    if (mw) {
+        fast::stage_sync<0>();  // codes 0 (and the table) in LDS
+        fast::stage_sync<0>();  // A 0, codes 1, converted 0
+        int s3 = 0, s2 = 0;     // A and converted-tile stages of the current chunk
+        for (int w = blockIdx.x; w < nitems; w += G) {
+            const TileIdx ti = tile_of(w, p.N / BN, p.M / BM, p.splits);
+            const int kbeg = ti.split * p.kchunk;
+            const int n = (min(p.K, kbeg + p.kchunk) - kbeg) / 64 +
+                          ((p.K2 > 0 && ti.split == p.splits - 1) ? p.K2 / 64 : 0);
+            f32x4 acc[FI][FJ];
+#pragma unroll
+            for (int i = 0; i < FI; ++i)
+#pragma unroll
+                for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int c = 0; c < n; ++c) {
+                fast::mma<FI, FJ, TE, true>(reinterpret_cast<const uint16_t*>(sa(s3)), sb(s2), acc, wm * WM, wn * WN,
+                                            lane);
+                // next chunk's A and converted tile; the barrier does not wait
+                // for the previous tile's stores (vmcnt 63: no wait)
+                fast::stage_sync<63>();
+                s3 = s3 == 2 ? 0 : s3 + 1;
+                s2 ^= 1;
+            }
+            wsp::epilogue<FI, FJ>(p, acc, ti.m * BM + wm * WM + (lane & 15), ti.n * BN + wn * WN + (lane >> 4) * 4,
+                                  ti.split);
+        }
+    } else {
+        wsp::Plan<BKIND, NPW> plan;
+        plan.init(p, wave - NMW);
+        const int pt = tid - NMW * 64;
+        // chunk g (this step), g + 1 (converted), g + 2 (A), g + 3 (codes)
+        wsp::Cursor<BKIND> cg, cd, ca, cc;
+        cg.load(p, blockIdx.x);
+        cd = cg;
+        ca = cg;
+        cc = cg;
+        auto adv = [&](wsp::Cursor<BKIND>& u) { u.advance(p, G, nitems); };
+        auto dq = [&](int rs_, uint16_t* tile) {
+#pragma unroll
+            for (int j = 0; j < NDQ; ++j) fast::dequant<BKIND, TE>(sr(rs_), ss(rs_), lds, tile, pt + j * NPW * 64);
+        };
+        plan.code_dma(cc, sr(0), ss(0));
+        adv(cc);
+        plan.a_dma(ca, sa(0));
+        adv(ca);
+        plan.code_dma(cc, sr(1), ss(1));
+        adv(cc);
+        plan.a_dma(ca, sa(1));
+        adv(ca);
+        plan.code_dma(cc, sr(2), ss(2));
+        adv(cc);
+        fast::stage_sync<2 * NA + 2 * NR>();  // codes 0 (and the table) in LDS
+        dq(0, sb(0));                         // chunk 0 is always a K chunk
+        adv(cd);
+        fast::stage_sync<NA + NR>();  // A 0, codes 1, converted 0
+        int s0 = 0;                   // chunk g's A stage (= the codes stage of g + 3)
+        int par = 1;                  // converted-tile stage of chunk g + 1
+        for (;;) {
+            if (cg.c + 3 < cg.nch) {
+                // chunks g + 1..g + 3 are K chunks of g's tile (so are the
+                // other cursors): the plain step, addressed from the tile's
+                // origins, with no cursor work
+                const int last = cg.nch - 3;
+                const auto ra = fast::rsrc(cg.a0), rc = fast::rsrc(cg.c0), rs = fast::rsrc(cg.s0);
+                for (int c = cg.c; c < last; ++c) {
+                    const int s1 = s0 == 2 ? 0 : s0 + 1, s2 = s1 == 2 ? 0 : s1 + 1;
+                    plan.a_dma_k(ra, c + 2, sa(s2));
+                    plan.code_dma_k(rc, rs, c + 3, sr(s0), ss(s0));
+                    dq(s1, sb(par));
+                    fast::stage_sync<NA + NR>();  // A g+1, codes g+2, converted g+1
+                    s0 = s1;
+                    par ^= 1;
+                }
+                cg.c = last;
+                cd.c = last + 1;
+                ca.c = last + 2;
+                cc.c = last + 2;
+                adv(cc);  // to the tile's end: its slab, the next tile or done
+            }
+            const int s1 = s0 == 2 ? 0 : s0 + 1, s2 = s1 == 2 ? 0 : s1 + 1;
+            plan.a_dma(ca, sa(s2));
+            adv(ca);
+            plan.code_dma(cc, sr(s0), ss(s0));
+            adv(cc);
+            uint16_t* const tile = sb(par);
+            if (!cd.done) {
+                if (!cd.slab()) {
+                    dq(s1, tile);
+                } else {
+                    // loaded, waited for and stored within the branch, so no
+                    // load is pending on the registers the K chunks reuse
+                    // (the wait also covers this step's DMAs: a slab chunk
+                    // costs one load latency)
+                    wsp::SlabB<BKIND, NPW> b2;
+                    b2.load(p, cd, pt);
+                    b2.store(tile, pt);
+                }
+            }
+            adv(cd);
+            fast::stage_sync<NA + NR>();  // A g+1, codes g+2, converted g+1
+            adv(cg);
+            if (cg.done) break;
+            s0 = s1;
+            par ^= 1;
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // the clamped DMAs past the stream land before the workgroup ends
     }
 }
 
@@ -1734,6 +2087,7 @@ static void launch_kind(const GemmParams& p, TileCfg tc, int batch_splits, hipSt
 }
 
 static bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; }
+static bool aligned8(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 7) == 0; }
 
 // The full-tile kernels take up to 160 KB of dynamic LDS, which each device
 // has to allow once per kernel before the first launch. The flags are atomic:
@@ -1783,6 +2137,48 @@ static void launch_ws(const GemmParams& p, int tiles, hipStream_t s, const ProfS
     if (ws_npw(BKIND) == 8) launch_ws_n<BKIND, TE, 8>(p, tiles, s, prof);
     else launch_ws_n<BKIND, TE, 4>(p, tiles, s, prof);
 }
+template __global__ void k_nf4_wsp<B_NF4_NT, TE_BF16, 8>(const GemmParams, const int);
+template __global__ void k_nf4_wsp<B_NF4_NT, TE_F16, 8>(const GemmParams, const int);
+template __global__ void k_nf4_wsp<B_NF4_NN, TE_BF16, 8>(const GemmParams, const int);
+template __global__ void k_nf4_wsp<B_NF4_NN, TE_F16, 8>(const GemmParams, const int);
+// compute units of the current device (one persistent workgroup each)
+static int device_cus() {
+    static std::atomic<int> cus[64];
+    int dev = 0;
+    QLX_CHECK_HIP(hipGetDevice(&dev));
+    QLX_REQUIRE(dev >= 0 && dev < 64, QLX_EUNSUPPORTED, "gemm: device index out of range");
+    int n = cus[dev].load(std::memory_order_acquire);
+    if (n == 0) {
+        QLX_CHECK_HIP(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev));
+        QLX_REQUIRE(n > 0, QLX_EUNSUPPORTED, "gemm: device reports no compute units");
+        cus[dev].store(n, std::memory_order_release);
+    }
+    return n;
+}
+// QLX_NF4_PERSIST=0 keeps the one-tile-per-workgroup k_nf4_ws
+static bool nf4_persist() {
+    const char* e = std::getenv("QLX_NF4_PERSIST");
+    return !(e && e[0] == '0');
+}
+// what k_nf4_wsp takes on top of the full-tile conditions (checked on the
+// host: slab rows fetched 16 bytes at a time, plain outputs)
+static bool wsp_ok(const GemmParams& p) {
+    if (p.seg_rows > 0 || p.accumulate || p.R) return false;
+    if (p.splits > 1 ? !aligned16(p.partial)
+                     : !(p.ldc % 4 == 0 && (p.c_type == C_F32 ? aligned16(p.C) : aligned8(p.C))))
+        return false;
+    return p.K2 == 0 || (p.K2 % 64 == 0 && p.a2_vec && aligned16(p.B2) && p.ldb2 % 8 == 0);
+}
+template <int BKIND, int TE>
+static void launch_wsp(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {
+    static std::atomic<bool> allowed[64];
+    allow_lds(allowed, reinterpret_cast<const void*>(&k_nf4_wsp<BKIND, TE, 8>), ws::LDS_BYTES);
+    const int nitems = tiles * p.splits, cus = device_cus();
+    // one workgroup per CU; a multiple of 8 whenever a workgroup takes several tiles
+    const int G = nitems <= cus ? nitems : std::max(8, cus / 8 * 8);
+    hipExtLaunchKernelGGL((k_nf4_wsp<BKIND, TE, 8>), dim3(G), dim3(ws::Prod<8>::NTH), ws::LDS_BYTES, s, prof.start(),
+                          prof.stop(), 0, p, nitems);
+}
 template <int BKIND, int TE>
 static void launch_wide(const GemmParams& p, int tiles, hipStream_t s, const ProfScope& prof) {
     static std::atomic<bool> allowed[64];
@@ -1803,7 +2199,6 @@ static void launch_dense(const GemmParams& p, int tiles, hipStream_t s, const Pr
     hipExtLaunchKernelGGL(k_dense_tile<TE_F16>, dim3(tiles), dim3(dense::NTH), dense::LDS_BYTES, s, prof.start(),
                           prof.stop(), 0, p);
 }
-static bool aligned8(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 7) == 0; }
 
 // Relative cost of one 64-wide chunk of the 512 x 64 NF4 tile against one of
 // the 256 x 128 tile (same work per chunk): measured 1.4-1.8x on the 8B-shaped
@@ -1835,7 +2230,8 @@ static void dispatch(const GemmParams& p, int akind, int bkind, bool fast_ok, bo
             if (fast_ok)
                 shape == 2 ? launch_tall<B_NF4_NT, TE>(p, tiles, s, prof)
                 : shape == 1 ? launch_wide<B_NF4_NT, TE>(p, tiles, s, prof)
-                : nf4_ws()   ? launch_ws<B_NF4_NT, TE>(p, tiles, s, prof)
+                : nf4_ws()   ? (nf4_persist() && wsp_ok(p) ? launch_wsp<B_NF4_NT, TE>(p, tiles, s, prof)
+                                                                : launch_ws<B_NF4_NT, TE>(p, tiles, s, prof))
                              : launch_fast<B_NF4_NT, TE>(p, tiles, s, prof);
             else
                 launch_kind<A_ROW, B_NF4_NT, TE>(p, tc, bsz, s);
@@ -1844,7 +2240,8 @@ static void dispatch(const GemmParams& p, int akind, int bkind, bool fast_ok, bo
             if (fast_ok)
                 shape == 2 ? launch_tall<B_NF4_NN, TE>(p, tiles, s, prof)
                 : shape == 1 ? launch_wide<B_NF4_NN, TE>(p, tiles, s, prof)
-                : nf4_ws()   ? launch_ws<B_NF4_NN, TE>(p, tiles, s, prof)
+                : nf4_ws()   ? (nf4_persist() && wsp_ok(p) ? launch_wsp<B_NF4_NN, TE>(p, tiles, s, prof)
+                                                                : launch_ws<B_NF4_NN, TE>(p, tiles, s, prof))
                              : launch_fast<B_NF4_NN, TE>(p, tiles, s, prof);
             else
                 launch_kind<A_ROW, B_NF4_NN, TE>(p, tc, bsz, s);
@@ -1968,6 +2365,11 @@ int gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStrea
         // tile shape: 0 = 256 x 128, 1 = 512 x 128, 2 = 512 x 64 (each chunk
         // of the 512 x 128 shape is two 256 x 128 chunks of work)
         const int forced = nf4_shape_override();
+        // the 256 x 128 tile on the persistent kernel: the pipeline fills
+        // once per launch, so a tile costs its chunks plus ~half a chunk.
+        // Outputs decide, not which kernel runs: QLX_NF4_WS / QLX_NF4_PERSIST
+        // swap kernels under the same split, so the bits stay comparable.
+        const bool persist = p.seg_rows == 0 && !p.accumulate && !p.R;
         for (int sh = 0; sh < 3; ++sh) {
             if (sh > 0 && p.M % 512 != 0) continue;
             if (forced >= 0 && sh != forced && !(forced > 0 && p.M % 512 != 0 && sh == 0)) continue;
@@ -1977,7 +2379,7 @@ int gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStrea
                 if (sp > 1 && (!partial_ws || size_t(sp) * p.M * p.N > p.partial_cap)) break;
                 const int per = (nch + sp - 1) / sp;
                 const double rounds = double((t * sp + 255) / 256);
-                double cost = rounds * (per + 3.0) * unit;
+                double cost = (sh == 0 && persist) ? rounds * (per + 0.5) + 3.0 : rounds * (per + 3.0) * unit;
                 if (sp > 1) cost += mn * 4.0 * (sp + 1) / 4e12 / 1.35e-6 + 2.0;
                 if (cost < best - 1e-9) best = cost, best_s = sp, shape = sh;
             }

@@ -204,3 +204,26 @@ def test_llama8b_width_steps_do_not_read_stale_workspace(wide2):
     for l, lp, g, _ in dpo[1:]:
         assert torch.equal(l, dpo[0][0]) and torch.equal(lp, dpo[0][1]) and same_grads(g, dpo[0][2])
     assert torch.isfinite(sft[0][0]).all() and torch.isfinite(dpo[0][0]).all()
+
+
+@pytest.mark.parametrize("act", [B_.QLX_ACT_F16, B_.QLX_ACT_BF16], ids=["f16", "bf16"])
+def test_llama8b_width_persistent_nf4_kernel_gives_same_bits(wide2, monkeypatch, act):
+    """SFT at 1 x 512 and DPO at 2 pairs x 512 on the 2-layer 8B-width model
+    with the persistent NF4 kernel (default) and with one tile per workgroup
+    (QLX_NF4_PERSIST=0): the same bits. Covers slabs of r, 2r and 3r columns
+    in both directions, split-K partials, several tiles per workgroup (gate|up:
+    448 tiles) and both activation types."""
+    d, m, host, _, _ = wide2
+    sm = m.with_blobs(host).with_act(act)
+    toks = synth.tokens(6, 1, 512, d.vocab)
+    ch, rj = synth.dpo_pairs(6, 2, 512, 128, d.vocab)
+    out = {}
+    for persist in ("1", "0"):
+        monkeypatch.setenv("QLX_NF4_PERSIST", persist)
+        out[persist] = (run_sft(q, sm, toks, B_.QLX_STREAMED),
+                        run_dpo(q, sm, ch, rj, 128, 0.1, B_.QLX_STREAMED, B_.QLX_DPO_REF_FUSED))
+    (l1, g1, _), (dl1, lp1, dg1, _) = out["1"]
+    (l0, g0, _), (dl0, lp0, dg0, _) = out["0"]
+    assert torch.equal(l1, l0) and same_grads(g1, g0)
+    assert torch.equal(dl1, dl0) and torch.equal(lp1, lp0) and same_grads(dg1, dg0)
+    assert torch.isfinite(l1).all() and torch.isfinite(dl1).all()

@@ -274,9 +274,12 @@ def test_each_nf4_tile_operand_is_bf16_of_dequant(monkeypatch, tile):
     assert np.array_equal(dx.view(torch.int16).cpu().numpy().view(np.uint16), oracle.bf16_rne_bits(Wd[jy, :]))
 
 
-# The 256 x 128 tile has two kernels: the warp-specialized one (default) and
-# k_nf4_tile (QLX_NF4_WS=0). Same operand values, MFMA order and epilogue, so
-# forward, dX and the LoRA gradients agree bit for bit, split or not.
+# The 256 x 128 tile has three kernels: the persistent warp-specialized one
+# (default), the one-tile-per-workgroup warp-specialized one
+# (QLX_NF4_PERSIST=0) and k_nf4_tile (QLX_NF4_WS=0). Same operand values, MFMA
+# order and output arithmetic under the same split, so forward, dX and the
+# LoRA gradients agree bit for bit, split or not, one tile per workgroup or
+# several (2048 x 6144: 384 tiles on 256 workgroups).
 @pytest.mark.parametrize("T,in_f,out_f,r", [(512, 4096, 4096, 64), (2048, 4096, 6144, 64), (512, 14336, 4096, 64)])
 def test_warp_specialized_tile_equals_plain_tile(monkeypatch, T, in_f, out_f, r):
     monkeypatch.setenv("QLX_NF4_TILE", "256x128")
@@ -288,14 +291,16 @@ def test_warp_specialized_tile_equals_plain_tile(monkeypatch, T, in_f, out_f, r)
     A = f32_dev((g.uniform(-1, 1, (r, in_f)) / np.sqrt(in_f)).astype(np.float32))
     B = f32_dev((g.standard_normal((out_f, r)) * 0.05).astype(np.float32))
     res = {}
-    for ws in ("1", "0"):
+    for ws, persist in (("1", "1"), ("1", "0"), ("0", "1")):
         monkeypatch.setenv("QLX_NF4_WS", ws)
+        monkeypatch.setenv("QLX_NF4_PERSIST", persist)
         y = torch.empty(T, out_f, dtype=torch.bfloat16, device=DEV)
         dx = torch.empty(T, in_f, dtype=torch.bfloat16, device=DEV)
         dA = torch.empty(r, in_f, dtype=torch.float32, device=DEV)
         dB = torch.empty(out_f, r, dtype=torch.float32, device=DEV)
         q.qlora_linear_fwd(x, W, A, B, 0.25, y)
         q.qlora_linear_bwd(dy, x, W, A, B, 0.25, dx, dA, dB)
-        res[ws] = (y, dx, dA, dB)
-    for a, b in zip(res["1"], res["0"]):
-        assert torch.equal(a, b)
+        res[ws + persist] = (y, dx, dA, dB)
+    for other in ("10", "01"):
+        for a, b in zip(res["11"], res[other]):
+            assert torch.equal(a, b), other
