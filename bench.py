@@ -68,16 +68,16 @@ WORKLOADS = {
 
 
 # HBM bytes per launch of the NF4 GEMM rows that can come out dominant on the
-# default workload (gemm_nf4_nn; under a short rocprofv3 kernel trace, whose
-# occasional multi-millisecond dispatch stalls land on one kernel, another
-# row can win), from two rocprofv3 --pmc passes
-# (FETCH_SIZE, WRITE_SIZE) over the default workload, each scaled by the same
-# counter on a plain 1 GiB device copy (factors 2.000 and 1.000); valid only
+# default workload (gemm_nf4_nt, the forward and recompute products, or
+# gemm_nf4_nn, the dX products; the two run within a few percent of each
+# other), from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE) over the
+# default workload, each scaled by the same counter on a plain 1 GiB device
+# copy (factors 2.000 and 1.000), weighted over the row's dispatches; valid only
 # for the kernel source they were taken on (SHA-256 prefix of csrc/k_gemm.hip).
-MEASURED_TRAFFIC = {("sft8b_b1", "streamed", "gemm_nf4_nn"): {"bytes": int((114.8 + 28.8) * 1e6),
-                                                              "k_gemm_sha256": "71e152f04402ab69"},
-                    ("sft8b_b1", "streamed", "gemm_nf4_nt_wide"): {"bytes": int((108.5 + 29.4) * 1e6),
-                                                                   "k_gemm_sha256": "71e152f04402ab69"}}
+MEASURED_TRAFFIC = {("sft8b_b1", "streamed", "gemm_nf4_nt"): {"bytes": int((100.4 + 30.0) * 1e6),
+                                                              "k_gemm_sha256": "7f6c7430da2982e0"},
+                    ("sft8b_b1", "streamed", "gemm_nf4_nn"): {"bytes": int((115.3 + 28.9) * 1e6),
+                                                              "k_gemm_sha256": "7f6c7430da2982e0"}}
 
 
 def measured_traffic(workload: str, mode: str, kernel: str):

@@ -2163,7 +2163,8 @@ static bool nf4_persist() {
 // what k_nf4_wsp takes on top of the full-tile conditions (checked on the
 // host: slab rows fetched 16 bytes at a time, plain outputs)
 static bool wsp_ok(const GemmParams& p) {
-    if (p.seg_rows > 0 || p.accumulate || p.R) return false;
+    // (a residual only enters an unsplit output: split-K writes partials)
+    if (p.seg_rows > 0 || p.accumulate || (p.R && p.splits == 1)) return false;
     if (p.splits > 1 ? !aligned16(p.partial)
                      : !(p.ldc % 4 == 0 && (p.c_type == C_F32 ? aligned16(p.C) : aligned8(p.C))))
         return false;
@@ -2369,10 +2370,13 @@ int gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStrea
         // once per launch, so a tile costs its chunks plus ~half a chunk.
         // Outputs decide, not which kernel runs: QLX_NF4_WS / QLX_NF4_PERSIST
         // swap kernels under the same split, so the bits stay comparable.
-        const bool persist = p.seg_rows == 0 && !p.accumulate && !p.R;
+        const bool persist = p.seg_rows == 0 && !p.accumulate;
         for (int sh = 0; sh < 3; ++sh) {
             if (sh > 0 && p.M % 512 != 0) continue;
             if (forced >= 0 && sh != forced && !(forced > 0 && p.M % 512 != 0 && sh == 0)) continue;
+            // the persistent 256 x 128 kernel measured at least as fast as the
+            // 512 x 128 one on every 8B-shaped step (whole steps, one box)
+            if (forced < 0 && sh == 1 && persist) continue;
             const int t = (p.M / (sh ? 512 : 256)) * (p.N / (sh == 2 ? 64 : 128));
             const double unit = sh == 1 ? 1.85 * 1.03 : sh == 2 ? kTallUnit : 1.0;
             for (int sp = 1; sp <= 16 && nch / sp >= 4; ++sp) {
