@@ -98,10 +98,11 @@ def test_llama8b_32_layers_b1x512_sft_vs_oracle(llama32, act):
 # cancel in the margin (the adapter moves every rounded value, so the two
 # passes round independently): measured |dloss| 0.0119 and worst gradient
 # 2.1e-2, just past the stated 1e-2 / 2e-2 (bf16: 0.0103, 1e-1).
-DPO32_XFAIL = pytest.mark.xfail(
-    reason="32 layers x 512 tokens: 16-bit activation rounding in the policy and reference passes does not cancel "
-           "in the DPO margin (|dloss| 0.0119 fp16 / 0.0103 bf16 against 1e-2)", strict=False)
-DPO32_ACTS = [pytest.param(B_.QLX_ACT_F16, id="f16", marks=DPO32_XFAIL), pytest.param(B_.QLX_ACT_BF16, id="bf16", marks=BF16_XFAIL)]
+# fp16 activations meet the stated bar here (|dloss| 0.0061, worst gradient
+# 1.95e-2): the policy and reference passes round independently, so 16-bit
+# rounding over 32 layers x 384 response tokens is what sets the margin's
+# error (0.0119 under an earlier summation order of the split-K partials)
+DPO32_ACTS = [pytest.param(B_.QLX_ACT_F16, id="f16"), pytest.param(B_.QLX_ACT_BF16, id="bf16", marks=BF16_XFAIL)]
 LP_REL32 = 2e-4   # each summed log-prob at 32 layers (|lp| ~ 4800: about 1 nat)
 
 
