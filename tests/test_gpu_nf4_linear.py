@@ -279,8 +279,13 @@ def test_each_nf4_tile_operand_is_bf16_of_dequant(monkeypatch, tile):
 # (QLX_NF4_PERSIST=0) and k_nf4_tile (QLX_NF4_WS=0). Same operand values, MFMA
 # order and output arithmetic under the same split, so forward, dX and the
 # LoRA gradients agree bit for bit, split or not, one tile per workgroup or
-# several (2048 x 6144: 384 tiles on 256 workgroups).
-@pytest.mark.parametrize("T,in_f,out_f,r", [(512, 4096, 4096, 64), (2048, 4096, 6144, 64), (512, 14336, 4096, 64)])
+# several (2048 x 6144: 384 tiles on 256 workgroups). The persistent kernel's
+# edge cases: one K chunk per tile plus its slab chunk (in 64), two K chunks
+# per tile over 512 tiles (only the general per-chunk path runs: the tight
+# loop needs four chunks of lookahead inside a tile), and a rank whose slab
+# is not a whole number of 64-wide chunks (r 16: the one-tile kernel runs).
+@pytest.mark.parametrize("T,in_f,out_f,r", [(512, 4096, 4096, 64), (2048, 4096, 6144, 64), (512, 14336, 4096, 64),
+                                            (256, 64, 8192, 64), (512, 128, 32768, 64), (512, 4096, 4096, 16)])
 def test_warp_specialized_tile_equals_plain_tile(monkeypatch, T, in_f, out_f, r):
     monkeypatch.setenv("QLX_NF4_TILE", "256x128")
     seed = T + in_f + 3 * out_f
