@@ -2399,13 +2399,15 @@ int gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStrea
         if (shape == 2) tiles = (p.M / tall::BM) * (p.N / tall::BN);
         } else if (skinny) {
         // measured on the 8B-shaped LoRA products: at least 512 workgroups
-        // (four fit a CU), at most 2048 of K per split, at least 256; a
-        // product 128 (or a multiple) wide takes 64 x 128 tiles, so its
-        // long operand is read once rather than once per 64 columns
+        // (four fit a CU), at most 2048 of K per split, at least 256, at most
+        // 32 splits (16 left the 512-token products on 128 workgroups: the
+        // step 1.4% slower); a product 128 (or a multiple) wide takes 64 x 128
+        // tiles, so its long operand is read once rather than once per 64
+        // columns
         if (partial_ws) {
             int sp = 1;
-            while (sp < 16 && tiles * sp < 512) sp *= 2;
-            while (sp < 16 && p.K / sp > 2048) sp *= 2;
+            while (sp < 32 && tiles * sp < 512) sp *= 2;
+            while (sp < 32 && p.K / sp > 2048) sp *= 2;
             sp = std::min(sp, std::max(1, p.K / 256));
             while (sp > 1 && size_t(sp) * tiles * tc.bm * tc.bn > p.partial_cap) sp /= 2;
             if (sp > 1) {
