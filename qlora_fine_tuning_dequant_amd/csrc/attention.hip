@@ -11,7 +11,8 @@
 // scores of ONE query (4 keys per 16-key tile): the running max and sum are
 // per-lane scalars shared by the 4 lanes of a query, the rescale of the
 // output is a per-lane multiply, and the probabilities already sit in the
-// layout of the B operand of O^T += V^T P^T (V is staged transposed in LDS).
+// layout of the B operand of O^T += V^T P^T (V^T fragments come from the
+// row-major V tile through the transposing LDS read).
 // P is rounded to the 16-bit operand type for that product; the running sum
 // uses the fp32 values.
 //
@@ -59,37 +60,13 @@ __device__ inline uint32_t pack2(float lo, float hi) {
 }
 
 constexpr int QB = 64;       // queries (or keys) per workgroup block
-constexpr int TP = QB + 8;   // row stride (elements) of a transposed [HD][64] tile
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Stages rows [r0, r0 + 64) x HD of a [T, ld] bf16 matrix (column offset col)
-// into LDS, row-major (stride HD + 8) and/or transposed (stride TP); rows at or
-// past `rows` are zeros. 256 threads: 4 per row, HD/4 columns each.
-template <int HD, bool ROW, bool TRANS>
-__device__ inline void stage(const uint16_t* __restrict__ src, int64_t ld, int64_t base_row, int r0, int rows,
-                             int64_t col, uint16_t* __restrict__ dst_row, uint16_t* __restrict__ dst_t) {
-    const int tid = threadIdx.x, r = tid >> 2, part = tid & 3;
-    const bool ok = r0 + r < rows;
-    const uint16_t* s = src + (base_row + r0 + r) * ld + col + part * (HD / 4);
-#pragma unroll
-    for (int c8 = 0; c8 < HD / 32; ++c8) {
-        const uint4 v = ok ? *reinterpret_cast<const uint4*>(s + c8 * 8) : make_uint4(0, 0, 0, 0);
-        const int c0 = part * (HD / 4) + c8 * 8;
-        if (ROW) *reinterpret_cast<uint4*>(dst_row + r * (HD + 8) + c0) = v;
-        if (TRANS) {
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                dst_t[(c0 + 2 * e) * TP + r] = uint16_t(w[e] & 0xFFFF);
-                dst_t[(c0 + 2 * e + 1) * TP + r] = uint16_t(w[e] >> 16);
-            }
-        }
-    }
-}
-
-// The two halves of stage(), so a block's global loads can be in flight
-// while the previous block computes: load_rows into registers, then
-// store_rows into LDS (same thread-to-element map as stage()).
+// A block's rows in two halves, so its global loads can be in flight while
+// the previous block computes: load_rows takes rows [r0, r0 + 64) x HD of a
+// [T, ld] 16-bit matrix (column offset col) into registers, rows at or past
+// `rows` as zeros; store_rows puts them into LDS row-major (stride HD + 8).
+// 256 threads: 4 per row, HD/4 columns each.
 template <int HD>
 __device__ inline void load_rows(const uint16_t* __restrict__ src, int64_t ld, int64_t base_row, int r0, int rows,
                                  int64_t col, uint4 (&v)[HD / 32]) {
@@ -99,34 +76,37 @@ __device__ inline void load_rows(const uint16_t* __restrict__ src, int64_t ld, i
 #pragma unroll
     for (int c8 = 0; c8 < HD / 32; ++c8) v[c8] = ok ? *reinterpret_cast<const uint4*>(s + c8 * 8) : make_uint4(0, 0, 0, 0);
 }
-template <int HD, bool ROW, bool TRANS>
-__device__ inline void store_rows(const uint4 (&v)[HD / 32], uint16_t* __restrict__ dst_row,
-                                  uint16_t* __restrict__ dst_t) {
+template <int HD>
+__device__ inline void store_rows(const uint4 (&v)[HD / 32], uint16_t* __restrict__ dst_row) {
     const int tid = threadIdx.x, r = tid >> 2, part = tid & 3;
 #pragma unroll
-    for (int c8 = 0; c8 < HD / 32; ++c8) {
-        const int c0 = part * (HD / 4) + c8 * 8;
-        if (ROW) *reinterpret_cast<uint4*>(dst_row + r * (HD + 8) + c0) = v[c8];
-        if (TRANS) {
-            const uint32_t w[4] = {v[c8].x, v[c8].y, v[c8].z, v[c8].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                dst_t[(c0 + 2 * e) * TP + r] = uint16_t(w[e] & 0xFFFF);
-                dst_t[(c0 + 2 * e + 1) * TP + r] = uint16_t(w[e] >> 16);
-            }
-        }
-    }
+    for (int c8 = 0; c8 < HD / 32; ++c8)
+        *reinterpret_cast<uint4*>(dst_row + r * (HD + 8) + part * (HD / 4) + c8 * 8) = v[c8];
 }
 
-// A-operand fragment of a transposed tile for a 32-wide slice js of the
-// 64-row block, in the order the accumulator layout hands out rows: lane
-// (row d = lane & 15 of the 16-row tile dt, group g = lane >> 4) takes block
-// rows 32 js + 4 g + {0..3} and 32 js + 16 + 4 g + {0..3}.
+// A-operand fragment of the transposed block (columns = the 64 block rows)
+// for a 32-wide slice js, in the order the accumulator layout hands out rows:
+// lane (column d = lane & 15 of the 16-column tile dt, group g = lane >> 4)
+// takes block rows 32 js + 4 g + {0..3} and 32 js + 16 + 4 g + {0..3}.
+// It is read from the row-major tile (HD + 8 elements per row) with gfx950's
+// transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane i points at row r0 + i / 4, columns c0 + 4 (i % 4) .. + 3, and lane j
+// receives column c0 + j of rows r0 .. r0 + 3. So no transposed copy of the
+// tile is staged (its 2-byte LDS stores cost more than the products they
+// feed).
+__device__ inline uint2 tr_read(const uint16_t* p) {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4* lds_s4_t;
+    const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<lds_s4_t>(uint32_t(reinterpret_cast<uintptr_t>(p))));
+    return __builtin_bit_cast(uint2, v);
+}
 template <int HD>
-__device__ inline uint4 tfrag(const uint16_t* __restrict__ t, int dt, int js, int lane) {
-    const uint16_t* p = t + (dt * 16 + (lane & 15)) * TP + js * 32 + (lane >> 4) * 4;
-    const uint2 lo = *reinterpret_cast<const uint2*>(p);
-    const uint2 hi = *reinterpret_cast<const uint2*>(p + 16);
+__device__ inline uint4 trfrag(const uint16_t* __restrict__ t, int dt, int js, int lane) {
+    const int i = lane & 15, g = lane >> 4;
+    const uint16_t* p = t + (js * 32 + g * 4 + (i >> 2)) * (HD + 8) + dt * 16 + (i & 3) * 4;
+    const uint2 lo = tr_read(p);
+    const uint2 hi = tr_read(p + 16 * (HD + 8));
     return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
@@ -136,7 +116,7 @@ __device__ inline uint4 tfrag(const uint16_t* __restrict__ t, int dt, int js, in
 template <int HD, int TE>
 __global__ __launch_bounds__(256) void k_flash_fwd(const AttnArgs a) {
     __shared__ __align__(16) uint16_t Ks[QB * (HD + 8)];
-    __shared__ __align__(16) uint16_t Vt[HD * TP];
+    __shared__ __align__(16) uint16_t Vs[QB * (HD + 8)];
     const int nqb = (a.S + QB - 1) / QB;
     const int qb = nqb - 1 - int(blockIdx.x);  // longest (latest) query blocks first
     const int h = blockIdx.y, b = blockIdx.z, kh = h / (a.nH / a.nKV);
@@ -158,8 +138,8 @@ __global__ __launch_bounds__(256) void k_flash_fwd(const AttnArgs a) {
     load_rows<HD>(a.qkv, a.ld, row0, 0, a.S, kcol, kr);
     load_rows<HD>(a.qkv, a.ld, row0, 0, a.S, vcol, vr);
     for (int kb = 0; kb <= qb; ++kb) {
-        store_rows<HD, true, false>(kr, Ks, nullptr);
-        store_rows<HD, false, true>(vr, nullptr, Vt);
+        store_rows<HD>(kr, Ks);
+        store_rows<HD>(vr, Vs);
         __syncthreads();
         if (kb < qb) {
             load_rows<HD>(a.qkv, a.ld, row0, (kb + 1) * QB, a.S, kcol, kr);
@@ -209,7 +189,7 @@ __global__ __launch_bounds__(256) void k_flash_fwd(const AttnArgs a) {
         for (int js = 0; js < 2; ++js) {
             const uint4 pf = make_uint4(pk[2 * js][0], pk[2 * js][1], pk[2 * js + 1][0], pk[2 * js + 1][1]);
 #pragma unroll
-            for (int dt = 0; dt < HD / 16; ++dt) o[dt] = mfma<TE>(tfrag<HD>(Vt, dt, js, lane), pf, o[dt]);
+            for (int dt = 0; dt < HD / 16; ++dt) o[dt] = mfma<TE>(trfrag<HD>(Vs, dt, js, lane), pf, o[dt]);
         }
         __syncthreads();
     }
@@ -275,9 +255,7 @@ __global__ __launch_bounds__(256) void k_flash_bwd_dot(const AttnArgs a, int hd)
 template <int HD, int TE>
 __global__ __launch_bounds__(256) void k_flash_bwd_kv(const AttnArgs a) {
     __shared__ __align__(16) uint16_t Qs[QB * (HD + 8)];
-    __shared__ __align__(16) uint16_t Qt[HD * TP];
-    __shared__ __align__(16) uint16_t Ds[QB * (HD + 8)];  // dO row-major
-    __shared__ __align__(16) uint16_t Dt[HD * TP];        // dO transposed
+    __shared__ __align__(16) uint16_t Ds[QB * (HD + 8)];  // dO
     __shared__ float lse_s[QB], dq_s[QB];
     const int nkb = (a.S + QB - 1) / QB;
     const int kb = int(blockIdx.x);  // early key blocks see the most queries
@@ -304,8 +282,8 @@ __global__ __launch_bounds__(256) void k_flash_bwd_kv(const AttnArgs a) {
     load_rows<HD>(a.qkv, a.ld, row0, kb * QB, a.S, int64_t(h) * HD, qr);
     load_rows<HD>(a.dO, a.ldo, row0, kb * QB, a.S, int64_t(h) * HD, dr);
     for (int qb = kb; qb < nkb; ++qb) {
-        store_rows<HD, true, true>(qr, Qs, Qt);
-        store_rows<HD, true, true>(dr, Ds, Dt);
+        store_rows<HD>(qr, Qs);
+        store_rows<HD>(dr, Ds);
         if (tid < QB) {
             const int qq = qb * QB + tid;
             lse_s[tid] = qq < a.S ? a.lse[zrow + qq] * kLog2e : 0.f;
@@ -353,8 +331,8 @@ __global__ __launch_bounds__(256) void k_flash_bwd_kv(const AttnArgs a) {
             const uint4 sa = make_uint4(sk[2 * js][0], sk[2 * js][1], sk[2 * js + 1][0], sk[2 * js + 1][1]);
 #pragma unroll
             for (int dt = 0; dt < HD / 16; ++dt) {
-                dv[dt] = mfma<TE>(pa, tfrag<HD>(Dt, dt, js, lane), dv[dt]);
-                dk[dt] = mfma<TE>(sa, tfrag<HD>(Qt, dt, js, lane), dk[dt]);
+                dv[dt] = mfma<TE>(pa, trfrag<HD>(Ds, dt, js, lane), dv[dt]);
+                dk[dt] = mfma<TE>(sa, trfrag<HD>(Qs, dt, js, lane), dk[dt]);
             }
         }
         __syncthreads();
@@ -378,7 +356,6 @@ template <int HD, int TE>
 __global__ __launch_bounds__(256) void k_flash_bwd_q(const AttnArgs a) {
     __shared__ __align__(16) uint16_t Ks[QB * (HD + 8)];
     __shared__ __align__(16) uint16_t Vs[QB * (HD + 8)];
-    __shared__ __align__(16) uint16_t Kt[HD * TP];
     const int nqb = (a.S + QB - 1) / QB;
     const int qb = nqb - 1 - int(blockIdx.x);
     const int h = blockIdx.y, b = blockIdx.z, kh = h / (a.nH / a.nKV);
@@ -405,8 +382,8 @@ __global__ __launch_bounds__(256) void k_flash_bwd_q(const AttnArgs a) {
     load_rows<HD>(a.qkv, a.ld, row0, 0, a.S, kcol, kr);
     load_rows<HD>(a.qkv, a.ld, row0, 0, a.S, vcol, vr);
     for (int kb = 0; kb <= qb; ++kb) {
-        store_rows<HD, true, true>(kr, Ks, Kt);
-        store_rows<HD, true, false>(vr, Vs, nullptr);
+        store_rows<HD>(kr, Ks);
+        store_rows<HD>(vr, Vs);
         __syncthreads();
         if (kb < qb) {
             load_rows<HD>(a.qkv, a.ld, row0, (kb + 1) * QB, a.S, kcol, kr);
@@ -438,7 +415,7 @@ __global__ __launch_bounds__(256) void k_flash_bwd_q(const AttnArgs a) {
         for (int js = 0; js < 2; ++js) {
             const uint4 sb = make_uint4(sk[2 * js][0], sk[2 * js][1], sk[2 * js + 1][0], sk[2 * js + 1][1]);
 #pragma unroll
-            for (int dt = 0; dt < HD / 16; ++dt) dq[dt] = mfma<TE>(tfrag<HD>(Kt, dt, js, lane), sb, dq[dt]);
+            for (int dt = 0; dt < HD / 16; ++dt) dq[dt] = mfma<TE>(trfrag<HD>(Ks, dt, js, lane), sb, dq[dt]);
         }
         __syncthreads();
     }
