@@ -168,6 +168,71 @@ struct TransLoader {
     }
 };
 
+// Transposed operand staged as it lies in memory: tile[k][r] =
+// src[(k0 + k) * ld + r0 + r], rows of R + 8 elements, 16-byte loads and
+// stores of 8 consecutive r (zeros past K or past `rows`). The MFMA fragments
+// come out with the transposing LDS read (ktfrag), so no 2-byte transposed
+// stores: the tile holds the same values the row-major layout would.
+template <int R, int NT>
+struct KLoader {
+    static constexpr int RP = R + 8;
+    static constexpr int U = BK * (R / 8) / NT;
+    static_assert(U >= 1 && BK * (R / 8) % NT == 0, "k-major loader shape");
+    static_assert(BK * RP <= R * BKP, "k-major tile must fit the row-major buffer");
+    uint4 v[U];
+    __device__ inline void load(const uint16_t* __restrict__ src, int64_t ld, int r0, int k0, int rows, int K,
+                                int /*vec_ok*/) {
+        const bool v16 = (reinterpret_cast<uintptr_t>(src) & 15) == 0 && (ld & 7) == 0 && (r0 & 7) == 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int idx = threadIdx.x + u * NT;
+            const int k = idx / (R / 8), rg = (idx % (R / 8)) * 8;
+            const int gk = k0 + k, gr = r0 + rg;
+            uint4 val = make_uint4(0, 0, 0, 0);
+            if (gk < K) {
+                const uint16_t* q = src + int64_t(gk) * ld + gr;
+                if (v16 && gr + 8 <= rows) {
+                    val = *reinterpret_cast<const uint4*>(q);
+                } else {
+                    uint32_t e[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) e[j] = (gr + j < rows) ? q[j] : 0u;
+                    val = make_uint4(pack2(e[0], e[1]), pack2(e[2], e[3]), pack2(e[4], e[5]), pack2(e[6], e[7]));
+                }
+            }
+            v[u] = val;
+        }
+    }
+    __device__ inline void store(uint16_t* __restrict__ tile) const {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int idx = threadIdx.x + u * NT;
+            *reinterpret_cast<uint4*>(tile + (idx / (R / 8)) * RP + (idx % (R / 8)) * 8) = v[u];
+        }
+    }
+};
+
+// gfx950's transposing LDS read (ds_read_b64_tr_b16): within each group of
+// 16 lanes, lane i points at row r0 + i / 4, columns c0 + 4 (i % 4) .. + 3
+// of a 16-bit tile, and lane j receives column c0 + j of rows r0 .. r0 + 3.
+__device__ inline uint2 tr_read(const uint16_t* q) {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4* lds_s4_t;
+    const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<lds_s4_t>(uint32_t(reinterpret_cast<uintptr_t>(q))));
+    return __builtin_bit_cast(uint2, v);
+}
+// The MFMA fragment of a k-major tile (rows of RP elements): lane (c = lane &
+// 15, g = lane >> 4) gets column cb + c at k = kk + 8 g .. + 7, the same
+// eight values the row-major layout gives it.
+template <int RP>
+__device__ inline uint4 ktfrag(const uint16_t* __restrict__ tile, int kk, int cb, int lane) {
+    const int i = lane & 15, g = lane >> 4;
+    const uint16_t* q = tile + (kk + 8 * g + (i >> 2)) * RP + cb + 4 * (i & 3);
+    const uint2 lo = tr_read(q), hi = tr_read(q + 4 * RP);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
 // The weight operand is the dequantized value rounded to bf16 (QLoRA's
 // computation type). With fp16 activations (TE_F16) that bf16 value is then
 // converted to fp16, exactly for every |value| in [2^-17, 65504] (fp16 holds
@@ -318,7 +383,9 @@ struct Nf4NnLoader {
 };
 
 // One K chunk of MFMAs for wavefront (wm, wn) owning a WM x WN sub-tile.
-template <int TE, int WM, int WN>
+// AK_ / BK_: the A / B tile is k-major (KLoader, rows of APR / BPR elements)
+// rather than row-major with BKP-element rows.
+template <int TE, int WM, int WN, bool AK_ = false, bool BK_ = false, int APR = 0, int BPR = 0>
 __device__ inline void mma_chunk(const uint16_t* __restrict__ As, const uint16_t* __restrict__ Bs,
                                  f32x4 (&acc)[WM / 16][WN / 16], int wm, int wn, int lane) {
     const int lr = lane & 15, lk = (lane >> 4) * 8;
@@ -327,10 +394,12 @@ __device__ inline void mma_chunk(const uint16_t* __restrict__ As, const uint16_t
         uint4 a[WM / 16], b[WN / 16];
 #pragma unroll
         for (int i = 0; i < WM / 16; ++i)
-            a[i] = *reinterpret_cast<const uint4*>(As + (wm * WM + i * 16 + lr) * BKP + kk + lk);
+            a[i] = AK_ ? ktfrag<APR>(As, kk, wm * WM + i * 16, lane)
+                       : *reinterpret_cast<const uint4*>(As + (wm * WM + i * 16 + lr) * BKP + kk + lk);
 #pragma unroll
         for (int j = 0; j < WN / 16; ++j)
-            b[j] = *reinterpret_cast<const uint4*>(Bs + (wn * WN + j * 16 + lr) * BKP + kk + lk);
+            b[j] = BK_ ? ktfrag<BPR>(Bs, kk, wn * WN + j * 16, lane)
+                       : *reinterpret_cast<const uint4*>(Bs + (wn * WN + j * 16 + lr) * BKP + kk + lk);
 #pragma unroll
         for (int i = 0; i < WM / 16; ++i)
 #pragma unroll
@@ -406,13 +475,13 @@ __device__ inline void store_row(const GemmParams& p, int bo, int bi, int row, i
 }
 
 template <int AK, int R, int NT>
-using ALoader = typename std::conditional<AK == A_ROW, RowLoader<R, NT>, TransLoader<R, NT>>::type;
+using ALoader = typename std::conditional<AK == A_ROW, RowLoader<R, NT>, KLoader<R, NT>>::type;
 template <int BKIND, int R, int NT, int TE>
 using BLoader = typename std::conditional<
     BKIND == B_NF4_NT, Nf4NtLoader<R, NT, TE>,
     typename std::conditional<BKIND == B_NF4_NN, Nf4NnLoader<R, NT, TE>,
                               typename std::conditional<BKIND == B_DENSE_NT, RowLoader<R, NT>,
-                                                        TransLoader<R, NT>>::type>::type>::type;
+                                                        KLoader<R, NT>>::type>::type>::type;
 
 // LM-head cross-entropy epilogues. The lane holds 16 consecutive columns
 // col0.. of one row; the 4 lanes of a row are lanes 4k..4k+3 of the
@@ -556,7 +625,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const int t, cons
                 if constexpr (kNf4) lb.load(Bq, p.absmax, p.nf4_cols, n0, kn, p.N, p.K, p.b_vec);
                 else lb.load(Bd, p.ldb, n0, kn, p.N, p.K, p.b_vec);
             }
-            mma_chunk<TE, WM, WN>(As[buf], Bs[buf], acc, wm, wn, lane);
+            mma_chunk<TE, WM, WN, AK == A_TRANS, BKIND == B_DENSE_NN, BM + 8, BN + 8>(As[buf], Bs[buf], acc, wm, wn,
+                                                                                     lane);
             if (more) {
                 la.store(As[buf ^ 1]);
                 if constexpr (kNf4) lb.store(Bs[buf ^ 1], Bq, p.absmax, p.nf4_cols, n0, kn, p.N, p.K, lut);
