@@ -346,8 +346,9 @@ typedef struct {
 /* Workspace of a step: two device slots of one full-form layer blob each
  * plus room for a wire-form tail (streamed modes), n_layers+1 fp32
  * layer-boundary checkpoints, one layer's workspace, the LM head's per-row
- * partials [T, vocab/64] (max and sum of exponentials, fp32) and one
- * vocabulary chunk of fp16 logit gradients [T, 16384]. kind: 0 = SFT (batch = sequences),
+ * partials [T, vocab/64] (max and sum of exponentials, fp32), the fp32
+ * logits [T, vocab] of the stream being trained (kept for the backward) and
+ * one vocabulary chunk of fp16 logit gradients [T, 16384]. kind: 0 = SFT (batch = sequences),
  * 1 = DPO, ORPO or SimPO, 2 = KTO (batch = pairs; T = 2*pairs*seq; KTO adds
  * the mismatched pairs' tokens, two more fp32 hidden-state streams and
  * their CE statistics). */

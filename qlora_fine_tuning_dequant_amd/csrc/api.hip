@@ -503,6 +503,7 @@ struct StepWs {
     uint16_t* nf;  // fp16 [T, H]
     float* rstd_f;
     float *ce_pm, *ce_ps;  // [T, V/64] LM-head row partials (max, sum exp)
+    float* logits;         // [T, V] the LM head's fp32 logits, kept from the statistics pass for dz
     uint16_t* dzc;         // fp16 [T, kVocabChunk] one vocabulary chunk of dz
     float *lse, *picked, *lse_ref, *pk_ref;
     float* dnf;  // [T, H]
@@ -554,6 +555,7 @@ static StepWs carve_step(Carver& c, const qlx_dims& d, int T, int kind, uint64_t
     w.rstd_f = c.take<float>(Tz);
     w.ce_pm = c.take<float>(Tz * ((V + 63) / 64));
     w.ce_ps = c.take<float>(Tz * ((V + 63) / 64));
+    w.logits = c.take<float>(Tz * V);
     w.dzc = c.take<uint16_t>(Tz * kVocabChunk);
     w.lse = c.take<float>(Tz);
     w.picked = c.take<float>(Tz);
@@ -809,13 +811,15 @@ static void end_step(qlx_ctx* ctx, hipStream_t main) {
 
 // Fused LM head + cross-entropy. Forward: final RMSNorm (fp16 out), then the
 // head GEMM whose epilogue reduces each row's logits to per-64-column (max,
-// sum exp) partials and picks the target's logit; a row reduce gives lse. The
-// [T, V] logits never exist. Backward: per vocabulary chunk of kVocabChunk
-// columns, the head GEMM again with an epilogue writing fp16 dz = (softmax -
-// onehot) * scale, then dnf += dz_chunk . head_chunk (fp32, chunk order), then
-// RMSNorm backward.
+// sum exp) partials, picks the target's logit and, for the stream whose
+// backward follows (logits non-null), stores the fp32 logits; a row reduce
+// gives lse. Backward: per vocabulary chunk of kVocabChunk columns, fp16
+// dz = (softmax - onehot) * scale from the stored logits, then dnf +=
+// dz_chunk . head_chunk (fp32, chunk order), then RMSNorm backward. (Keeping
+// the logits costs 4 T V bytes of workspace and saves a second pass of the
+// head product.)
 static void head_stats(const qlx_model* m, const float* hL, int T, const int32_t* tokens, int seq, int start,
-                       float* lse, float* picked, StepWs& w, float* partial, hipStream_t s) {
+                       float* lse, float* picked, float* logits, StepWs& w, float* partial, hipStream_t s) {
     const qlx_dims& d = m->dims;
     const int nb = (d.vocab + 63) / 64;
     launch_rmsnorm_fwd(hL, m->final_norm, T, d.hidden, d.rms_eps, w.nf, 1, w.rstd_f, s);
@@ -836,6 +840,8 @@ static void head_stats(const qlx_model* m, const float* hL, int T, const int32_t
     p.ce_ps = w.ce_ps;
     p.ce_pld = nb;
     p.ce_picked = picked;
+    p.ce_logits = logits;
+    p.ce_ldl = d.vocab;
     p.tag = "gemm_head";
     gemm(p, A_ROW, B_DENSE_NT, TE_F16, partial, s);
     launch_ce_reduce(w.ce_pm, w.ce_ps, nb, T, d.vocab, tokens, seq, start, lse, picked, s);
@@ -848,27 +854,7 @@ static void head_grad(const qlx_model* m, const float* hL, int T, const int32_t*
     for (int c0 = 0; c0 < d.vocab; c0 += kVocabChunk) {
         const int cw = std::min(kVocabChunk, d.vocab - c0);
         const uint16_t* head = m->lm_head_f16 + size_t(c0) * d.hidden;
-        GemmParams p;
-        p.M = T;
-        p.N = cw;
-        p.K = d.hidden;
-        p.A = w.nf;
-        p.lda = d.hidden;
-        p.B = head;
-        p.ldb = d.hidden;
-        p.C = w.dzc;
-        p.ldc = kVocabChunk;
-        p.c_type = C_F16;
-        p.ce_mode = 2;
-        p.ce_tokens = tokens;
-        p.ce_seq = seq;
-        p.ce_start = start;
-        p.ce_col0 = c0;
-        p.ce_lse = lse;
-        p.ce_sc = sc;
-        p.ce_gseq = gseq;
-        p.tag = "gemm_head_dz";
-        gemm(p, A_ROW, B_DENSE_NT, TE_F16, partial, s);
+        launch_ce_dz(w.logits, d.vocab, T, cw, c0, tokens, seq, start, lse, sc, gseq, w.dzc, kVocabChunk, s);
         GemmParams q;
         q.M = T;
         q.N = d.hidden;
@@ -1182,7 +1168,7 @@ int stream_step_sft(qlx_ctx* ctx, const qlx_model* m, const int32_t* tokens, int
             st.release(i);
         }
         const float* hL = w.ckpt + size_t(L) * TH;
-        head_stats(m, hL, T, tokens, seq, 0, w.lse, w.picked, w, w.lw.partial, s);
+        head_stats(m, hL, T, tokens, seq, 0, w.lse, w.picked, w.logits, w, w.lw.partial, s);
         launch_sft_loss(w.lse, w.picked, T, seq, loss, s);
         const float alpha = 1.0f / (kDzScale * float(batch) * float(seq - 1));
         head_grad(m, hL, T, tokens, seq, 0, w.lse, kDzScale, nullptr, alpha, w, w.dh[0], w.lw.partial, s);
@@ -1289,15 +1275,15 @@ static void pref_step(qlx_ctx* ctx, const qlx_model* m, const qlx_pref_cfg& cfg,
     }
     const int start = prompt_len - 1;
     if (need_ref) {  // reference log-probs
-        head_stats(m, extra[0].cur, T, w.toks, seq, start, w.lse_ref, w.pk_ref, w, w.lw.partial, s);
+        head_stats(m, extra[0].cur, T, w.toks, seq, start, w.lse_ref, w.pk_ref, nullptr, w, w.lw.partial, s);
     }
     if (kto) {  // mismatched pairs: reference, then policy
-        head_stats(m, extra[1].cur, T, w.kl_toks, seq, start, w.kl_lse_r, w.kl_pk_r, w, w.lw.partial, s);
-        head_stats(m, extra[2].cur, T, w.kl_toks, seq, start, w.kl_lse, w.kl_pk, w, w.lw.partial, s);
+        head_stats(m, extra[1].cur, T, w.kl_toks, seq, start, w.kl_lse_r, w.kl_pk_r, nullptr, w, w.lw.partial, s);
+        head_stats(m, extra[2].cur, T, w.kl_toks, seq, start, w.kl_lse, w.kl_pk, nullptr, w, w.lw.partial, s);
     }
     // policy log-probs, loss, and dL/dlp
     const float* hL = w.ckpt + size_t(L) * TH;
-    head_stats(m, hL, T, w.toks, seq, start, w.lse, w.picked, w, w.lw.partial, s);
+    head_stats(m, hL, T, w.toks, seq, start, w.lse, w.picked, w.logits, w, w.lw.partial, s);
     PrefLossArgs la{};
     la.lse_p = w.lse;
     la.pk_p = w.picked;

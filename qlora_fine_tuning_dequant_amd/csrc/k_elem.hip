@@ -881,6 +881,53 @@ void launch_ce_reduce(const float* pm, const float* ps, int nb, int T, int V, co
     check_launch("ce_reduce");
 }
 
+// dz of one vocabulary chunk from the LM head's fp32 logits z (the statistics
+// pass keeps them): dz[t, j] = fp16((exp(z[t, col0 + j] - lse[t]) -
+// [col0 + j == target]) * scale), scale = sc (times gseq[t / seq] when given),
+// 0 on rows without a target. dz = softmax - onehot is the cross-entropy's
+// gradient with respect to the logits; sc carries the loss's 1/N and the
+// fixed power-of-two range factor. One thread: 8 consecutive columns.
+__global__ __launch_bounds__(256) void k_ce_dz(const float* __restrict__ z, int64_t ldz, int T, int cw, int col0,
+                                               const int32_t* __restrict__ tokens, int seq, int start,
+                                               const float* __restrict__ lse, float sc,
+                                               const float* __restrict__ gseq, uint16_t* __restrict__ dz,
+                                               int64_t lddz) {
+    const int groups = (cw + 7) / 8;
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= int64_t(T) * groups) return;
+    const int t = int(i / groups), j0 = int(i % groups) * 8;
+    const int tgt = row_target(tokens, t, seq, start);
+    const float scale = sc * (gseq ? gseq[t / seq] : 1.f);
+    const float l = tgt >= 0 ? lse[t] : 0.f;
+    const float* src = z + int64_t(t) * ldz + col0 + j0;
+    uint16_t* dst = dz + int64_t(t) * lddz + j0;
+    const int v0 = col0 + j0;
+    if (j0 + 8 <= cw && (reinterpret_cast<uintptr_t>(src) & 15) == 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+        const float4 a = reinterpret_cast<const float4*>(src)[0], b = reinterpret_cast<const float4*>(src)[1];
+        const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float v_lo = tgt < 0 ? 0.f : (expf(x[2 * k] - l) - (v0 + 2 * k == tgt ? 1.f : 0.f)) * scale;
+            const float v_hi = tgt < 0 ? 0.f : (expf(x[2 * k + 1] - l) - (v0 + 2 * k + 1 == tgt ? 1.f : 0.f)) * scale;
+            w[k] = uint32_t(f32_to_f16_bits(v_lo)) | (uint32_t(f32_to_f16_bits(v_hi)) << 16);
+        }
+        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+        for (int c = 0; c < 8 && j0 + c < cw; ++c)
+            dst[c] = f32_to_f16_bits(tgt < 0 ? 0.f : (expf(src[c] - l) - (v0 + c == tgt ? 1.f : 0.f)) * scale);
+    }
+}
+void launch_ce_dz(const float* z, int64_t ldz, int T, int cw, int col0, const int32_t* tokens, int seq, int start,
+                  const float* lse, float sc, const float* gseq, uint16_t* dz, int64_t lddz, hipStream_t s) {
+    if (T <= 0 || cw <= 0) return;
+    const int64_t n = int64_t(T) * ((cw + 7) / 8);
+    ProfScope prof("ce_dz", 4.0 * T * cw, 6.0 * T * cw, s);
+    hipLaunchKernelGGL(k_ce_dz, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, z, ldz, T, cw, col0, tokens, seq,
+                       start, lse, sc, gseq, dz, lddz);
+    check_launch("ce_dz");
+}
+
 // SFT loss = sum over target rows of (lse - picked) / (#rows with a target).
 __global__ __launch_bounds__(256) void k_sft_loss(const float* __restrict__ lse, const float* __restrict__ picked,
                                                   int T, int seq, float* __restrict__ loss) {

@@ -483,11 +483,12 @@ using BLoader = typename std::conditional<
                               typename std::conditional<BKIND == B_DENSE_NT, RowLoader<R, NT>,
                                                         KLoader<R, NT>>::type>::type>::type;
 
-// LM-head cross-entropy epilogues. The lane holds 16 consecutive columns
-// col0.. of one row; the 4 lanes of a row are lanes 4k..4k+3 of the
-// wavefront (one 64-column block). Mode 1: the block's max and sum of
-// exp(z - max) (joined over the 4 lanes), and the target's logit. Mode 2: fp16
-// dz = (exp(z - lse) - onehot) * scale.
+// LM-head cross-entropy statistics epilogue. The lane holds 16 consecutive
+// columns col0.. of one row; the 4 lanes of a row are lanes 4k..4k+3 of the
+// wavefront (one 64-column block). It writes the block's max and sum of
+// exp(z - max) (joined over the 4 lanes) and the target's logit, and, when
+// ce_logits is set, the 16 fp32 logits themselves (row stride ce_ldl), from
+// which the backward forms dz without running the product again.
 __device__ inline int ce_target(const GemmParams& p, int t) {
     const int s = t % p.ce_seq;
     if (s < p.ce_start || s >= p.ce_seq - 1) return -1;
@@ -496,51 +497,39 @@ __device__ inline int ce_target(const GemmParams& p, int t) {
 __device__ void ce_epilogue(const GemmParams& p, int row, int col0, const float* src) {
     const bool rok = row < p.M;
     const int tgt = rok ? ce_target(p, row) : -1;
-    const int v0 = p.ce_col0 + col0;  // vocab index of src[0]
-    if (p.ce_mode == 1) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int c = 0; c < 16; ++c)
-            if (col0 + c < p.N) mx = fmaxf(mx, src[c]);
-        float sm = 0.f;
-        if (mx > -INFINITY) {
-#pragma unroll
-            for (int c = 0; c < 16; ++c)
-                if (col0 + c < p.N) sm += expf(src[c] - mx);
-        }
-#pragma unroll
-        for (int off = 1; off <= 2; off <<= 1) {
-            const float om = __shfl_xor(mx, off, 64), os = __shfl_xor(sm, off, 64);
-            const float nm = fmaxf(mx, om);
-            sm = (nm == -INFINITY) ? 0.f : sm * expf(mx - nm) + os * expf(om - nm);
-            mx = nm;
-        }
-        if (rok && (threadIdx.x & 3) == 0 && col0 < p.N) {
-            const int64_t o = int64_t(row) * p.ce_pld + v0 / 64;
-            p.ce_pm[o] = mx;
-            p.ce_ps[o] = sm;
-        }
-        if (rok && tgt >= v0 && tgt < v0 + 16 && tgt - p.ce_col0 < p.N) p.ce_picked[row] = src[tgt - v0];
-        return;
-    }
-    if (!rok) return;
-    const float scale = p.ce_sc * (p.ce_gseq ? p.ce_gseq[row / p.ce_seq] : 1.f);
-    const float lse = tgt >= 0 ? p.ce_lse[row] : 0.f;
-    float v[16];
+    float mx = -INFINITY;
 #pragma unroll
     for (int c = 0; c < 16; ++c)
-        v[c] = tgt < 0 ? 0.f : (expf(src[c] - lse) - (v0 + c == tgt ? 1.f : 0.f)) * scale;
-    uint16_t* dst = static_cast<uint16_t*>(p.C) + int64_t(row) * p.ldc + col0;
-    if (col0 + 16 <= p.N && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-        uint32_t w[8];
+        if (col0 + c < p.N) mx = fmaxf(mx, src[c]);
+    float sm = 0.f;
+    if (mx > -INFINITY) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            w[k] = uint32_t(f32_to_f16_bits(v[2 * k])) | (uint32_t(f32_to_f16_bits(v[2 * k + 1])) << 16);
-        reinterpret_cast<uint4*>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        reinterpret_cast<uint4*>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    } else {
         for (int c = 0; c < 16; ++c)
-            if (col0 + c < p.N) dst[c] = f32_to_f16_bits(v[c]);
+            if (col0 + c < p.N) sm += expf(src[c] - mx);
+    }
+#pragma unroll
+    for (int off = 1; off <= 2; off <<= 1) {
+        const float om = __shfl_xor(mx, off, 64), os = __shfl_xor(sm, off, 64);
+        const float nm = fmaxf(mx, om);
+        sm = (nm == -INFINITY) ? 0.f : sm * expf(mx - nm) + os * expf(om - nm);
+        mx = nm;
+    }
+    if (rok && (threadIdx.x & 3) == 0 && col0 < p.N) {
+        const int64_t o = int64_t(row) * p.ce_pld + col0 / 64;
+        p.ce_pm[o] = mx;
+        p.ce_ps[o] = sm;
+    }
+    if (rok && tgt >= col0 && tgt < col0 + 16 && tgt < p.N) p.ce_picked[row] = src[tgt - col0];
+    if (rok && p.ce_logits && col0 < p.N) {
+        float* dst = p.ce_logits + int64_t(row) * p.ce_ldl + col0;
+        if (col0 + 16 <= p.N && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+#pragma unroll
+            for (int c = 0; c < 16; c += 4)
+                *reinterpret_cast<float4*>(dst + c) = make_float4(src[c], src[c + 1], src[c + 2], src[c + 3]);
+        } else {
+            for (int c = 0; c < 16; ++c)
+                if (col0 + c < p.N) dst[c] = src[c];
+        }
     }
 }
 
@@ -2512,8 +2501,12 @@ int gemm(GemmParams p, int akind, int bkind, int te, float* partial_ws, hipStrea
     const double flops = 2.0 * p.batch * (pairs_k + M * N * k2);
     const double belt = !nf4 ? 2.0 : 0.5 + 4.0 / 64.0;
     const double cb = p.c_type == C_F32 ? 4.0 : 2.0;
-    const double bytes = p.batch * (M * K * 2 + N * K * belt + M * N * cb * (p.accumulate ? 2 : 1) +
-                                    (p.R ? M * N * 4 : 0) + (p.K2 ? (M + N) * p.K2 * 2.0 : 0));
+    // the cross-entropy epilogue writes no C: two floats per row and 64
+    // columns, and the fp32 logits when they are kept
+    const double out_bytes = p.ce_mode ? M * std::ceil(N / 64.0) * 8.0 + (p.ce_logits ? M * N * 4.0 : 0.0)
+                                       : M * N * cb * (p.accumulate ? 2 : 1);
+    const double bytes = p.batch * (M * K * 2 + N * K * belt + out_bytes + (p.R ? M * N * 4 : 0) +
+                                    (p.K2 ? (M + N) * p.K2 * 2.0 : 0));
     static const char* kNames[] = {"gemm_nf4_nt", "gemm_nf4_nn", "gemm_bf16_nt", "gemm_bf16_nn",
                                    "gemm_bf16_tn", "gemm_f16_nt", "gemm_f16_nn", "gemm_other"};
     static const char* kWideNames[] = {"gemm_nf4_nt_wide", "gemm_nf4_nn_wide"};

@@ -140,20 +140,19 @@ struct GemmParams {
     // returns the split count either way
     int defer_reduce = 0;
     int slab_alg_k = -1;  // algorithmic K of the slab for flop accounting (-1: K2)
-    // LM-head cross-entropy epilogues (fp16 NT products on 64-wide wavefront
-    // tiles, no split): ce_mode 1 writes, per row and per 64 columns, the max
-    // and the sum of exp(z - max) (ce_pm, ce_ps, row stride ce_pld) and the
-    // target's logit (ce_picked); ce_mode 2 writes fp16 C = (exp(z - lse) -
-    // [vocab index == target]) * scale, 0 on rows without a target. Column j of
-    // the product is vocab index ce_col0 + j; the target of row t is
-    // ce_tokens[t + 1] when t % ce_seq lies in [ce_start, ce_seq - 1).
+    // LM-head cross-entropy statistics epilogue (fp16 NT products on 64-wide
+    // wavefront tiles, no split; ce_mode 1): per row and per 64 columns, the
+    // max and the sum of exp(z - max) (ce_pm, ce_ps, row stride ce_pld), the
+    // target's logit (ce_picked) and, when ce_logits is non-null, the fp32
+    // logits z (row stride ce_ldl). C is not written. Column j is vocab index
+    // j; the target of row t is ce_tokens[t + 1] when t % ce_seq lies in
+    // [ce_start, ce_seq - 1).
     int ce_mode = 0;
     const int32_t* ce_tokens = nullptr;
-    int ce_seq = 0, ce_start = 0, ce_col0 = 0, ce_pld = 0;
+    int ce_seq = 0, ce_start = 0, ce_pld = 0;
     float *ce_pm = nullptr, *ce_ps = nullptr, *ce_picked = nullptr;
-    const float* ce_lse = nullptr;
-    float ce_sc = 1.f;                  // scale (mode 2)
-    const float* ce_gseq = nullptr;     // non-null: scale also times ce_gseq[t / ce_seq]
+    float* ce_logits = nullptr;
+    int64_t ce_ldl = 0;
     // set by the launcher
     int a_vec = 0, b_vec = 0, a2_vec = 0, b2_vec = 0;
     const char* tag = nullptr;  // profiling label (host side only; default: the operand kinds)
@@ -304,6 +303,10 @@ void launch_gqa_reduce(const float* dh, int B, int nH, int nKV, int S, int hd, u
 // target[t] < 0 marks a row with no loss. lse[t], picked[t] = z[t, target].
 void launch_ce_reduce(const float* pm, const float* ps, int nb, int T, int V, const int32_t* tokens, int seq, int start,
                       float* lse, float* picked, hipStream_t s);
+// fp16 dz = (softmax - onehot) * sc (* gseq[t / seq]) of vocabulary columns
+// col0 .. col0 + cw - 1 from fp32 logits z [T, ldz] into dz [T, lddz].
+void launch_ce_dz(const float* z, int64_t ldz, int T, int cw, int col0, const int32_t* tokens, int seq, int start,
+                  const float* lse, float sc, const float* gseq, uint16_t* dz, int64_t lddz, hipStream_t s);
 void launch_sft_loss(const float* lse, const float* picked, int T, int seq, float* loss, hipStream_t s);
 enum PrefKind { PREF_DPO = 0, PREF_ORPO = 1, PREF_SIMPO = 2, PREF_KTO = 3 };
 struct PrefLossArgs {
