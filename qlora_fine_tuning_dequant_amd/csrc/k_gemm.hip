@@ -237,11 +237,17 @@ __device__ inline uint4 ktfrag(const uint16_t* __restrict__ tile, int kk, int cb
 // computation type). With fp16 activations (TE_F16) that bf16 value is then
 // converted to fp16, exactly for every |value| in [2^-17, 65504] (fp16 holds
 // bf16's 8-bit significands there), so the product sees the same weights.
+// (For fp16, the conversion with a zero low half leaves bf16(x) << 16, the
+// fp32 bits of bf16(x) itself: three instructions per pair instead of four.)
 template <int TE>
 __device__ __forceinline__ uint32_t wpair(float lo, float hi) {
-    const uint32_t b = f32x2_to_bf16x2(lo, hi);
-    if constexpr (TE == TE_BF16) return b;
-    else return bf16x2_to_f16x2(b);
+    if constexpr (TE == TE_BF16) {
+        return f32x2_to_bf16x2(lo, hi);
+    } else {
+        const float l = __builtin_bit_cast(float, f32x2_to_bf16x2(0.f, lo));
+        const float h = __builtin_bit_cast(float, f32x2_to_bf16x2(0.f, hi));
+        return f32x2_to_f16x2(l, h);
+    }
 }
 template <int TE>
 __device__ __forceinline__ uint32_t wone(float v) {
@@ -825,22 +831,53 @@ struct DmaPlan {
 // 8 b) holds the code values of byte b's high nibble (the even element) and
 // low nibble.
 // t: the thread's slot, 0..511 (a 512-thread workgroup passes threadIdx.x)
+// The table entry of byte B of w. The kernels that dequantize through it
+// declare no static LDS, so their dynamic buffer, and the table at its
+// offset 0, start at LDS address 0: the entry's address is the byte times 8,
+// one byte-select shift (SDWA) and no base to add.
+static_assert(OFF_L == 0, "the table lookups address LDS from 0");
+template <int B>
+__device__ __forceinline__ f2 lut_at(uint32_t w) {
+    static_assert(B >= 0 && B < 4, "byte index");
+    uint32_t off;
+    if constexpr (B == 0)
+        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
+            : "=v"(off) : "v"(w));
+    else if constexpr (B == 1)
+        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1"
+            : "=v"(off) : "v"(w));
+    else if constexpr (B == 2)
+        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2"
+            : "=v"(off) : "v"(w));
+    else
+        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+            : "=v"(off) : "v"(w));
+    return *reinterpret_cast<const __attribute__((address_space(3))) f2*>(static_cast<uintptr_t>(off));
+}
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>());
+        static_for<I + 1, N>(f);
+    }
+}
+
 template <int BKIND, int TE>
 __device__ __forceinline__ void dequant(const char* __restrict__ raw, const char* __restrict__ sc,
                                         const char* __restrict__ lds0, uint16_t* __restrict__ tile, const int t) {
     const float* s = reinterpret_cast<const float*>(sc);
-    auto lut = [&](uint32_t byte) { return *reinterpret_cast<const f2*>(lds0 + OFF_L + (byte << 3)); };
+    (void)lds0;  // the table is read at its absolute LDS address (lut_at)
     if constexpr (BKIND == B_NF4_NT) {
         // thread = 16 consecutive k of row t >> 2
         const int r = t >> 2, q4 = t & 3;
         const uint2 w = *reinterpret_cast<const uint2*>(raw + r * 32 + q4 * 8);
         const float a = s[r];
         uint32_t e[8];
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const f2 v = lut(((b < 4 ? w.x : w.y) >> (8 * (b & 3))) & 0xFF);
+        static_for<0, 8>([&](auto bb) {
+            constexpr int b = decltype(bb)::value;
+            const f2 v = lut_at<b & 3>(b < 4 ? w.x : w.y);
             e[b] = wpair<TE>(v.x * a, v.y * a);
-        }
+        });
         *reinterpret_cast<uint4*>(tile + swz(r, 2 * q4)) = make_uint4(e[0], e[1], e[2], e[3]);
         *reinterpret_cast<uint4*>(tile + swz(r, 2 * q4 + 1)) = make_uint4(e[4], e[5], e[6], e[7]);
     } else {
@@ -852,8 +889,8 @@ __device__ __forceinline__ void dequant(const char* __restrict__ raw, const char
         for (int kr = 0; kr < 4; ++kr) {
             const uint32_t two = *reinterpret_cast<const uint16_t*>(raw + (kg + kr) * 64 + (ng >> 1));
             a[kr] = s[(kg + kr) * 2 + (ng >> 6)];
-            v[kr][0] = lut(two & 0xFF);
-            v[kr][1] = lut(two >> 8);
+            v[kr][0] = lut_at<0>(two);
+            v[kr][1] = lut_at<1>(two);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
