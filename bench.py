@@ -74,10 +74,10 @@ WORKLOADS = {
 # default workload, each scaled by the same counter on a plain 1 GiB device
 # copy (factors 2.000 and 1.000), weighted over the row's dispatches; valid only
 # for the kernel source they were taken on (SHA-256 prefix of csrc/k_gemm.hip).
-MEASURED_TRAFFIC = {("sft8b_b1", "streamed", "gemm_nf4_nt"): {"bytes": int((100.4 + 30.0) * 1e6),
-                                                              "k_gemm_sha256": "e7847964bb11bd9f"},
-                    ("sft8b_b1", "streamed", "gemm_nf4_nn"): {"bytes": int((115.3 + 28.9) * 1e6),
-                                                              "k_gemm_sha256": "e7847964bb11bd9f"}}
+MEASURED_TRAFFIC = {("sft8b_b1", "streamed", "gemm_nf4_nt"): {"bytes": int((100.4 + 30.1) * 1e6),
+                                                              "k_gemm_sha256": "9680e68f2874089e"},
+                    ("sft8b_b1", "streamed", "gemm_nf4_nn"): {"bytes": int((115.2 + 28.8) * 1e6),
+                                                              "k_gemm_sha256": "9680e68f2874089e"}}
 
 
 def measured_traffic(workload: str, mode: str, kernel: str):
