@@ -775,7 +775,9 @@ __device__ __forceinline__ void stage_sync() {
 //  block, so it fetches the 16 bytes that belong in that slot of the
 //  swizzled layout.
 //  Codes, in natural order: NT [128 n][32 B] with one absmax per row; NN
-//  [64 k][64 B] with two absmax per row. Every wavefront issues exactly one
+//  [64 k][64 B] with two absmax per row, which land transposed
+//  ([2 blocks][64 k]) so a thread reads its 8 rows' maxima as two 16-byte
+//  vectors. Every wavefront issues exactly one
 //  16-byte DMA (32 lanes) and one 4-byte DMA (16 lanes), so the
 //  per-wavefront vmcnt bookkeeping is the same everywhere.
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -808,7 +810,7 @@ struct DmaPlan {
         const int q = wave * 32 + (lane & 31), qs = wave * 16 + (lane & 15);
         if constexpr (BKIND == B_NF4_NN) {
             code = uint32_t(int64_t(q >> 2) * (cols >> 1) + (q & 3) * 16);
-            scale = uint32_t((int64_t(qs >> 1) * (cols >> 6) + (qs & 1)) * 4);
+            scale = uint32_t((int64_t(qs & 63) * (cols >> 6) + (qs >> 6)) * 4);
         } else {
             code = uint32_t(int64_t(q >> 1) * (cols >> 1) + (q & 1) * 16);
             scale = uint32_t(int64_t(qs) * (cols >> 6) * 4);
@@ -881,25 +883,28 @@ __device__ __forceinline__ void dequant(const char* __restrict__ raw, const char
         *reinterpret_cast<uint4*>(tile + swz(r, 2 * q4)) = make_uint4(e[0], e[1], e[2], e[3]);
         *reinterpret_cast<uint4*>(tile + swz(r, 2 * q4 + 1)) = make_uint4(e[4], e[5], e[6], e[7]);
     } else {
-        // thread = 4 consecutive n x 4 consecutive k; pairs along k convert together
-        const int ng = (t & 31) * 4, kg = (t >> 5) * 4;
-        f2 v[4][2];
-        float a[4];
+        // thread = one code byte column (n = ng, ng + 1) x 8 consecutive k:
+        // per k row one byte, whose high nibble is n = ng; the 8 k of each n
+        // are one 16-byte chunk of the tile. The 64 lanes of a wavefront take
+        // the 64 byte columns, so a row write's lanes cover all 8 swizzled
+        // chunk positions (with 4 n x 4 k per thread they covered 4, in
+        // 8-byte halves: a 4-way LDS bank conflict on every write).
+        const int i = t & 63, ng = 2 * i, kg = (t >> 6) * 8;
+        // maxima of block ng / 64 for rows kg..kg+7 ([block][k] in LDS)
+        const float4 a0 = *reinterpret_cast<const float4*>(s + (i >> 5) * 64 + kg);
+        const float4 a1 = *reinterpret_cast<const float4*>(s + (i >> 5) * 64 + kg + 4);
+        const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        f2 v[8];
 #pragma unroll
-        for (int kr = 0; kr < 4; ++kr) {
-            const uint32_t two = *reinterpret_cast<const uint16_t*>(raw + (kg + kr) * 64 + (ng >> 1));
-            a[kr] = s[(kg + kr) * 2 + (ng >> 6)];
-            v[kr][0] = lut_at<0>(two);
-            v[kr][1] = lut_at<1>(two);
+        for (int kr = 0; kr < 8; ++kr) v[kr] = lut_at<0>(*reinterpret_cast<const uint8_t*>(raw + (kg + kr) * 64 + i));
+        uint32_t e[8], o[8];
+#pragma unroll
+        for (int kr = 0; kr < 8; kr += 2) {
+            e[kr >> 1] = wpair<TE>(v[kr].x * a[kr], v[kr + 1].x * a[kr + 1]);
+            o[kr >> 1] = wpair<TE>(v[kr].y * a[kr], v[kr + 1].y * a[kr + 1]);
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float x[4];
-#pragma unroll
-            for (int kr = 0; kr < 4; ++kr) x[kr] = ((j & 1) ? v[kr][j >> 1].y : v[kr][j >> 1].x) * a[kr];
-            *reinterpret_cast<uint2*>(tile + swz(ng + j, kg >> 3) + (kg & 4)) =
-                make_uint2(wpair<TE>(x[0], x[1]), wpair<TE>(x[2], x[3]));
-        }
+        *reinterpret_cast<uint4*>(tile + swz(ng, kg >> 3)) = make_uint4(e[0], e[1], e[2], e[3]);
+        *reinterpret_cast<uint4*>(tile + swz(ng + 1, kg >> 3)) = make_uint4(o[0], o[1], o[2], o[3]);
     }
 }
 
@@ -1122,7 +1127,7 @@ struct DmaPlanP {
             const int q = (pw * NC + j) * 32 + (lane & 31), qs = (pw * NC + j) * 16 + (lane & 15);
             if constexpr (BKIND == B_NF4_NN) {
                 code[j] = uint32_t(int64_t(q >> 2) * (cols >> 1) + (q & 3) * 16);
-                scale[j] = uint32_t((int64_t(qs >> 1) * (cols >> 6) + (qs & 1)) * 4);
+                scale[j] = uint32_t((int64_t(qs & 63) * (cols >> 6) + (qs >> 6)) * 4);
             } else {
                 code[j] = uint32_t(int64_t(q >> 1) * (cols >> 1) + (q & 1) * 16);
                 scale[j] = uint32_t(int64_t(qs) * (cols >> 6) * 4);
@@ -1360,7 +1365,7 @@ struct Plan {
             const int q = (pw * NC + j) * 32 + (lane & 31), qs = (pw * NC + j) * 16 + (lane & 15);
             if constexpr (BKIND == B_NF4_NN) {
                 code[j] = uint32_t(int64_t(q >> 2) * (cols >> 1) + (q & 3) * 16);
-                scale[j] = uint32_t((int64_t(qs >> 1) * (cols >> 6) + (qs & 1)) * 4);
+                scale[j] = uint32_t((int64_t(qs & 63) * (cols >> 6) + (qs >> 6)) * 4);
             } else {
                 code[j] = uint32_t(int64_t(q >> 1) * (cols >> 1) + (q & 1) * 16);
                 scale[j] = uint32_t(int64_t(qs) * (cols >> 6) * 4);
