@@ -590,7 +590,7 @@ def main() -> int:
                     help="only run a plain device copy of 1 GiB five times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1).",
               file=sys.stderr)
         return 2
 

@@ -54,7 +54,7 @@ extern "C" {
 typedef enum {
     QLX_OK = 0,
     QLX_EINVAL = 1,        /* null pointer, negative size, inconsistent shapes */
-    QLX_EUNSUPPORTED = 2,  /* valid request this build does not handle */
+    QLX_EUNSUPPORTED = 2,  /* valid request the library does not handle */
     QLX_EWORKSPACE = 3,    /* ws_bytes smaller than the reported requirement */
     QLX_ENOTPINNED = 4,    /* a streamed layer blob is not pinned host memory */
     QLX_EHIP = 5,          /* the HIP runtime reported an error */
