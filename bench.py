@@ -75,9 +75,9 @@ WORKLOADS = {
 # copy (factors 2.000 and 1.000), weighted over the row's dispatches; valid only
 # for the kernel source they were taken on (SHA-256 prefix of csrc/k_gemm.hip).
 MEASURED_TRAFFIC = {("sft8b_b1", "streamed", "gemm_nf4_nt"): {"bytes": int((100.4 + 30.2) * 1e6),
-                                                              "k_gemm_sha256": "d196f463a6146176"},
+                                                              "k_gemm_sha256": "3901c14538590722"},
                     ("sft8b_b1", "streamed", "gemm_nf4_nn"): {"bytes": int((115.2 + 28.8) * 1e6),
-                                                              "k_gemm_sha256": "d196f463a6146176"}}
+                                                              "k_gemm_sha256": "3901c14538590722"}}
 
 
 def measured_traffic(workload: str, mode: str, kernel: str):

@@ -829,10 +829,6 @@ struct DmaPlan {
     }
 };
 
-// Codes of one chunk (LDS) -> bf16 tile [n][k] (LDS). lut2[b] (LDS address
-// 8 b) holds the code values of byte b's high nibble (the even element) and
-// low nibble.
-// t: the thread's slot, 0..511 (a 512-thread workgroup passes threadIdx.x)
 // The table entry of byte B of w. The kernels that dequantize through it
 // declare no static LDS, so their dynamic buffer, and the table at its
 // offset 0, start at LDS address 0: the entry's address is the byte times 8,
@@ -864,6 +860,10 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
+// Codes of one chunk (LDS) -> bf16 tile [n][k] (LDS). lut2[b] (LDS address
+// 8 b) holds the code values of byte b's high nibble (the even element) and
+// low nibble.
+// t: the thread's slot, 0..511 (a 512-thread workgroup passes threadIdx.x)
 template <int BKIND, int TE>
 __device__ __forceinline__ void dequant(const char* __restrict__ raw, const char* __restrict__ sc,
                                         const char* __restrict__ lds0, uint16_t* __restrict__ tile, const int t) {

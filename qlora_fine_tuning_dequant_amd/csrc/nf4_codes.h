@@ -29,11 +29,6 @@ __device__ inline uint32_t f32x2_to_f16x2(float lo, float hi) {
     typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2_t){lo, hi}, h2_t));
 }
-// Packed bf16 pair -> packed fp16 pair holding the same two values (exact
-// wherever fp16 can represent them: magnitudes in [2^-17, 65504] or zero).
-__device__ inline uint32_t bf16x2_to_f16x2(uint32_t b) {
-    return f32x2_to_f16x2(__builtin_bit_cast(float, b << 16), __builtin_bit_cast(float, b & 0xFFFF0000u));
-}
 __device__ inline float bf16_bits_to_f32(uint16_t b) { return __builtin_bit_cast(float, uint32_t(b) << 16); }
 __device__ inline float f16_bits_to_f32(uint16_t b) { return float(__builtin_bit_cast(_Float16, b)); }
 // A 16-bit activation (bf16 or fp16 bits, by the format flag) <-> fp32.
