@@ -11,8 +11,10 @@ heads, head_dim 128, SwiGLU 14336, vocab 128256, LoRA r 64 alpha 16):
   the same loss and LoRA gradients bit for bit (the pages' "difference 0.0"),
   with 2L-2 layer reads and a loss near its closed form at initialization;
 * at full width with 2 layers (so the oracle finishes in seconds), streamed
-  SFT and DPO steps match the oracle, DPO with B = 0 gives exactly ln 2, and
-  the fused and separate reference schedules give identical bits.
+  SFT and DPO steps match the oracle (SFT also at 4 x 512 tokens, the
+  batch-4 configuration's sizes inside a layer), DPO with B = 0 gives
+  exactly ln 2, and the fused and separate reference schedules give
+  identical bits.
 
 Tolerances are the stated ones: |dloss| <= 1e-2 and rel-L2 <= 2e-2 on every
 LoRA gradient. They hold with fp16 activations (the default act_dtype). With
@@ -151,6 +153,25 @@ def test_llama8b_width_sft_step_vs_oracle(wide2, act):
     ref_loss, ref_g = oracle.sft_step(om, ol, toks, d)
     errs = grad_errors(g, ref_g)
     print(act, f"loss {loss.item():.6f} oracle {ref_loss:.6f}", {k: f"{v:.1e}" for k, v in errs.items()}, flush=True)
+    assert abs(loss.item() - ref_loss) <= TOL_LOSS, (loss.item(), ref_loss)
+    bad = {k: v for k, v in errs.items() if not v <= TOL}
+    assert not bad, bad
+
+
+def test_llama8b_width_sft_b4x512_vs_oracle(wide2):
+    """2 layers at 8B width with the batch-4 configuration's 2,048 tokens (4 x
+    512): the paths that size takes inside a layer (several tiles per
+    persistent workgroup, the one-tile kernel for outputs that add the
+    residual, attention over 4 sequences of 8 key blocks) against the oracle at
+    the stated tolerances, fp16 activations."""
+    d, m, host, om, ol = wide2
+    toks = synth.tokens(8, 4, 512, d.vocab)
+    loss, g, st = run_sft(q, m.with_blobs(host).with_act(B_.QLX_ACT_F16), toks, B_.QLX_STREAMED)
+    ref_loss, ref_g = oracle.sft_step(om, ol, toks, d)
+    errs = grad_errors(g, ref_g)
+    worst = max(errs, key=errs.get)
+    print(f"loss {loss.item():.6f} oracle {ref_loss:.6f}; worst gradient {errs[worst]:.2e} ({worst})", flush=True)
+    assert st["layer_reads"] == 2 * d.n_layers - 2
     assert abs(loss.item() - ref_loss) <= TOL_LOSS, (loss.item(), ref_loss)
     bad = {k: v for k, v in errs.items() if not v <= TOL}
     assert not bad, bad
