@@ -51,6 +51,33 @@ def test_pref_step_vs_oracle_and_streamed_equals_resident(kind):
     assert not bad, bad
 
 
+@pytest.fixture(scope="module")
+def wide2_pref():
+    d = dataclasses.replace(synth.LLAMA8B, n_layers=2)
+    m, host = gpu_model(q, d, 9, "kaiming")
+    return d, m, host, oracle_model(d, 9), lora_list(d, 9, "kaiming")
+
+
+@pytest.mark.parametrize("kind", ["orpo", "simpo", "kto"])
+def test_pref_step_at_8b_width_2x512_vs_oracle(wide2_pref, kind):
+    """Each objective on 2 layers at 8B width with the bench's preference
+    shape (2 pairs x 512, 128-token prompts), fp16 activations, streamed,
+    against the oracle: |dloss| <= 1e-2, every LoRA gradient within 2e-2, each
+    summed log-prob within 1e-3 of its own size."""
+    d, m, host, om, ol = wide2_pref
+    ch, rj = synth.dpo_pairs(9, 2, 512, 128, d.vocab)
+    l_s, lp_s, g_s, st = run_pref(m.with_blobs(host).with_act(B_.QLX_ACT_F16), kind, ch, rj, 128, B_.QLX_STREAMED)
+    ref_loss, ref_lp, ref_g = oracle.pref_step(kind, om, ol, ch, rj, 128, d, **HP[kind])
+    errs = grad_errors(g_s, ref_g)
+    worst = max(errs, key=errs.get)
+    print(f"{kind}: loss {l_s.item():.6f} oracle {ref_loss:.6f}; worst gradient {errs[worst]:.2e} ({worst})", flush=True)
+    assert st["layer_reads"] == 2 * d.n_layers - 2
+    assert abs(l_s.item() - ref_loss) <= 1e-2, (l_s.item(), ref_loss)
+    assert np.all(np.abs(to_np(lp_s) - ref_lp) <= 1e-3 * np.abs(ref_lp)), (to_np(lp_s), ref_lp)
+    bad = {k: v for k, v in errs.items() if not v <= TOL}
+    assert not bad, bad
+
+
 def test_layer_reads_and_kto_schedules_on_four_layers():
     d = dataclasses.replace(synth.TINY, n_layers=4)
     m, host = gpu_model(q, d, 1, "normal")
